@@ -1,0 +1,198 @@
+/*
+ * coli_moe.h -- C ABI of the routed-expert MoE layer library (libcoli_moe.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the one the colibrì pages describe for GLM-5.2 (colibrì README,
+ * JustVugg/colibri, sections "思路" (Idea) and "已实现的功能" (Implemented
+ * features)):
+ *   - a DeepSeek-V3-like sigmoid router with the aux-loss-free ("noaux_tc")
+ *     selection bias, group-limited top-k and routed_scaling_factor;
+ *   - one always-on shared expert;
+ *   - SwiGLU expert FFNs whose weights are int8, packed int4 or packed int2
+ *     with one fp32 scale per row, dequantised on use against Q8_0-style
+ *     int8 activations (integer dot products);
+ *   - a batch-union dispatch: in a multi-token batch (prefill, MTP verify)
+ *     each unique expert is read once and applied to every token routed to it.
+ *
+ * Memory: every data pointer is a DEVICE pointer on the current HIP device
+ * unless marked "host".  The caller allocates and owns every buffer and keeps
+ * it alive until the stream work that uses it has finished; the library
+ * allocates nothing and keeps no per-call state, so calls on different
+ * streams may run concurrently when their buffers are disjoint.
+ *
+ * Streams: `stream` is a hipStream_t passed as a plain pointer (NULL = the
+ * null stream).  Every call only enqueues work on it and returns; outputs are
+ * valid when that stream work completes.  Outputs are fully overwritten.
+ *
+ * Errors: all argument checks run before anything is enqueued; on a failed
+ * check the call returns a code and enqueues nothing.  A failed launch (or no
+ * usable gfx950 device) returns COLI_ERR_DEVICE.  Faults during execution
+ * surface, as with any HIP work, at the caller's next synchronisation.  No
+ * C++ exception crosses this interface.
+ *
+ * Layouts (the container reading; the pages give only "per-row scale"):
+ *   - quantised weights: row-major [rows][cols*b/8] bytes, b = 8, 4 or 2;
+ *     codes are two's complement, lowest bits first: int4 byte j holds
+ *     element 2j in bits 0-3 and 2j+1 in bits 4-7; int2 byte j holds element
+ *     4j+m in bits 2m..2m+1.  Scales are fp32 [rows].  Codes lie in
+ *     [-qmax, qmax] with qmax = 127, 7, 1 (int2 is ternary).
+ *   - Q8_0 activations: blocks of 32 consecutive values, int8 codes and one
+ *     fp32 scale per block.
+ */
+#ifndef COLI_MOE_H
+#define COLI_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define COLI_ABI_VERSION 1
+
+typedef enum {
+  COLI_OK = 0,
+  COLI_ERR_INVALID_ARG = 1, /* a pointer, size or configuration check failed */
+  COLI_ERR_UNSUPPORTED = 2, /* valid request outside this build's limits */
+  COLI_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
+  COLI_ERR_DEVICE = 4       /* no gfx950 device, or a launch failed */
+} coli_status;
+
+typedef enum { COLI_Q8 = 8, COLI_Q4 = 4, COLI_Q2 = 2 } coli_qtype; /* bits */
+
+/* Router configuration (host struct).  Limits: n_experts <= 1024,
+ * n_experts % n_group == 0, 1 <= topk_group <= n_group <= 64,
+ * 1 <= top_k <= min(32, topk_group * n_experts / n_group). */
+typedef struct {
+  int32_t n_experts;           /* E: 256 for GLM-5.2 */
+  int32_t top_k;               /* k: 8 */
+  int32_t n_group;             /* contiguous groups of E/n_group experts: 8 */
+  int32_t topk_group;          /* groups kept: 4 */
+  int32_t norm_topk_prob;      /* 1: selected weights normalised to sum 1 */
+  float routed_scaling_factor; /* 2.5 */
+  float expert_top_p;          /* adaptive expert top-p; off unless 0<p<1 */
+  int32_t top_p_renorm;        /* 1: renormalise the kept weights */
+} coli_router_cfg;
+
+/* One layer's weights (host struct of device pointers).
+ * Routed experts are stacked: w_gate/w_up [E][I][H*b/8], s_gate/s_up [E][I],
+ * w_down [E][H][I*b/8], s_down [E][H].  The shared expert has the same
+ * per-expert layouts (E = 1).  Every weight row must start 16-byte aligned
+ * (holds for any 16-byte aligned base since H*b/8 and I*b/8 are multiples of
+ * 16).  H and I are multiples of 64 (int2: of 128 so a row is whole 16-byte
+ * chunks), at most 16384.  mfma_min_tokens: a unique expert receiving at least
+ * this many tokens of a batch runs on the int8 matrix cores, fewer on the
+ * integer dot-product GEMV; 0 selects the library default. */
+typedef struct {
+  int32_t hidden;   /* H: 6144 */
+  int32_t inter;    /* I: 2048 */
+  int32_t qtype;    /* coli_qtype */
+  coli_router_cfg router;
+  const float *gate_w;    /* [E][H] fp32; may be NULL if logits are supplied */
+  const float *gate_bias; /* [E] fp32 selection bias; NULL = zero */
+  const uint8_t *w_gate;
+  const uint8_t *w_up;
+  const uint8_t *w_down;
+  const float *s_gate;
+  const float *s_up;
+  const float *s_down;
+  const uint8_t *sh_gate;
+  const uint8_t *sh_up;
+  const uint8_t *sh_down;
+  const float *sh_s_gate;
+  const float *sh_s_up;
+  const float *sh_s_down;
+  int32_t mfma_min_tokens;
+} coli_moe_layer;
+
+/* ABI version (COLI_ABI_VERSION) and a static message for a status. */
+int coli_abi_version(void);
+const char *coli_status_str(coli_status s);
+
+/* Weight quantisation and packing (colibrì README, "Implemented features":
+ * int8 / packed int4 / packed int2 containers, one scale per row; the
+ * "convert" tool requantises a checkpoint into this container).
+ * Per row r of w [rows][cols] fp32: amax = max|w|; s = amax/qmax (fp32,
+ * correctly rounded); q = clamp(round_half_even(w/s), -qmax, qmax); s = 0
+ * gives q = 0.  Writes q_out [rows][cols*qtype/8] bytes (layout above) and
+ * scale_out [rows].  cols must be a positive multiple of 32; rows >= 0. */
+coli_status coli_quant_pack(int32_t qtype, const float *w, int64_t rows,
+                            int64_t cols, uint8_t *q_out, float *scale_out,
+                            void *stream);
+
+/* Q8_0-style activation quantisation (colibrì README, "Implemented
+ * features": integer dot products against Q8_0-style int8 activations).
+ * x [T][n] fp32 -> q [T][n] int8 (natural order) and d [T][n/32] fp32:
+ * d = amax/127 per block of 32; q = clamp(round_half_even(x/d), -127, 127);
+ * d = 0 gives q = 0.  n a positive multiple of 32; T >= 0. */
+coli_status coli_quant_act_q8_0(const float *x, int32_t T, int32_t n,
+                                int8_t *q, float *d, void *stream);
+
+/* Router logits: logits [T][E] = x [T][H] . gate_w[E][H]^T, accumulated in
+ * fp64 and rounded once to fp32.  H a positive multiple of 32. */
+coli_status coli_moe_logits(const float *x, const float *gate_w, int32_t T,
+                            int32_t E, int32_t H, float *logits, void *stream);
+
+/* Routing (colibrì README, "Implemented features": sigmoid router,
+ * noaux_tc, routed_scaling_factor; "Quick start": expert top-p).
+ * For each of T tokens: sigma = fl32(1/(1+exp(-l))) evaluated in fp64;
+ * c = sigma + bias (selection only); group score = sum of the two largest c
+ * of the group; keep topk_group groups, then the top_k largest c of their
+ * experts (ties: lower index first) -- the rank order of the outputs;
+ * w = sigma/S * rsf with S the fp32 sum of the chosen sigma in rank order
+ * (sigma * rsf when norm_topk_prob is 0).  With expert top-p the slots
+ * outside the smallest weight-descending prefix whose normalised sum reaches
+ * p get idx -1 and w 0 (kept weights renormalised if top_p_renorm).
+ * logits [T][E] fp32, bias [E] or NULL; writes topk_idx [T][k] int32 and
+ * topk_w [T][k] fp32. */
+coli_status coli_moe_route(const coli_router_cfg *cfg, const float *logits,
+                           const float *bias, int32_t T, int32_t *topk_idx,
+                           float *topk_w, void *stream);
+
+/* Batch-union tables (colibrì README, "Implemented features": batch-union
+ * MoE).  From topk_idx [T][k] (entries -1 skipped): counts [E], offs [E+1]
+ * (exclusive scan of counts), perm [T*k] = t*k+j of the routed pairs listed
+ * by expert id, then token, then slot (entries past offs[E] are undefined),
+ * uniq [E] = experts with nonzero count in increasing order (entries past
+ * n_uniq undefined), n_uniq [1].  Bit-exact and deterministic.  The forward
+ * call builds the same tables inside its workspace. */
+coli_status coli_moe_dispatch(const int32_t *topk_idx, int32_t T, int32_t k,
+                              int32_t E, int32_t *counts, int32_t *offs,
+                              int32_t *perm, int32_t *uniq, int32_t *n_uniq,
+                              void *stream);
+
+/* Workspace bytes coli_moe_forward needs for up to max_tokens tokens with
+ * this layer's shapes (0 if the descriptor is invalid).  The workspace is a
+ * device buffer, 256-byte aligned, needing no initialisation. */
+size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int32_t max_tokens);
+
+/* The layer on T tokens: y [T][H] fp32 = shared(x_t) + sum_j w_tj *
+ * expert_{idx_tj}(x_t), the sum over kept slots in rank order, where
+ * expert(x) = down( silu(gate . q(x)) * (up . q(x)) ) with both expert inputs
+ * Q8_0-quantised and all three products integer dot products rescaled by the
+ * row scale and the block scale.  No residual and no normalisation.
+ * x [T][H] fp32.  logits_in [T][E] or NULL (then logits = x . gate_w^T).
+ * Optional outputs (NULL to skip): idx_out [T][k], w_out [T][k],
+ * logits_out [T][E].  T = 1 runs the decode path; T >= 2 groups the batch by
+ * expert (each unique expert's weights are read once).  T = 0 is a no-op.
+ * workspace must hold coli_moe_workspace_bytes(L, T) bytes. */
+coli_status coli_moe_forward(const coli_moe_layer *L, const float *x,
+                             int32_t T, const float *logits_in, float *y,
+                             int32_t *idx_out, float *w_out, float *logits_out,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Test export of the integer products, same device code as the forward:
+ * acc_out [T][rows][cols/32] int32 = per-block sums of weight codes times
+ * Q8_0 codes, exact.  Wq [rows][cols*qtype/8], xq [T][cols] int8 (natural
+ * order).  cols a multiple of 64 (int2: 128), T <= 8. */
+coli_status coli_debug_qgemv_blocks(int32_t qtype, const uint8_t *Wq,
+                                    int32_t rows, int32_t cols,
+                                    const int8_t *xq, int32_t T,
+                                    int32_t *acc_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COLI_MOE_H */

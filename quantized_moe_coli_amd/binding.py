@@ -1,0 +1,271 @@
+"""Thin Python binding over ``libcoli_moe.so`` (include/coli_moe.h).
+
+Argument marshalling only: every function checks tensor dtypes, devices and
+shapes, passes raw device pointers and the current HIP stream to the C ABI of
+the same name, and raises ``ColiError`` on a non-OK status.  All computation
+happens in the library's gfx950 kernels; there is no fallback.  PyTorch is
+used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcoli_moe.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "coli_moe.h")
+
+COLI_OK, COLI_ERR_INVALID_ARG, COLI_ERR_UNSUPPORTED, COLI_ERR_WORKSPACE, COLI_ERR_DEVICE = range(5)
+COLI_Q8, COLI_Q4, COLI_Q2 = 8, 4, 2
+
+
+class ColiError(RuntimeError):
+    def __init__(self, name: str, status: int, msg: str):
+        super().__init__(f"{name}: status {status} ({msg})")
+        self.status = status
+
+
+class RouterCfg(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+                ("norm_topk_prob", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
+                ("expert_top_p", ctypes.c_float), ("top_p_renorm", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+
+
+class MoeLayerC(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("qtype", ctypes.c_int32),
+                ("router", RouterCfg),
+                ("gate_w", _P), ("gate_bias", _P),
+                ("w_gate", _P), ("w_up", _P), ("w_down", _P),
+                ("s_gate", _P), ("s_up", _P), ("s_down", _P),
+                ("sh_gate", _P), ("sh_up", _P), ("sh_down", _P),
+                ("sh_s_gate", _P), ("sh_s_up", _P), ("sh_s_down", _P),
+                ("mfma_min_tokens", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(python -m quantized_moe_coli_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        sig = {
+            "coli_abi_version": ([], ctypes.c_int),
+            "coli_status_str": ([ctypes.c_int], ctypes.c_char_p),
+            "coli_quant_pack": ([i32, _P, i64, i64, _P, _P, _P], ctypes.c_int),
+            "coli_quant_act_q8_0": ([_P, i32, i32, _P, _P, _P], ctypes.c_int),
+            "coli_moe_logits": ([_P, _P, i32, i32, i32, _P, _P], ctypes.c_int),
+            "coli_moe_route": ([ctypes.POINTER(RouterCfg), _P, _P, i32, _P, _P, _P], ctypes.c_int),
+            "coli_moe_dispatch": ([_P, i32, i32, i32, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+            "coli_moe_workspace_bytes": ([ctypes.POINTER(MoeLayerC), i32], sz),
+            "coli_moe_forward": ([ctypes.POINTER(MoeLayerC), _P, i32, _P, _P, _P, _P, _P, _P, sz,
+                                  _P], ctypes.c_int),
+            "coli_debug_qgemv_blocks": ([i32, _P, i32, i32, _P, i32, _P, _P], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def declared_symbols() -> list[str]:
+    """Function names declared in include/coli_moe.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(coli_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(name: str, status: int) -> None:
+    if status != COLI_OK:
+        raise ColiError(name, status, lib().coli_status_str(status).decode())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t: torch.Tensor | None, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def router_cfg(n_experts, top_k, n_group=1, topk_group=1, norm_topk_prob=1,
+               routed_scaling_factor=2.5, expert_top_p=0.0, top_p_renorm=1) -> RouterCfg:
+    return RouterCfg(n_experts, top_k, n_group, topk_group, norm_topk_prob,
+                     routed_scaling_factor, expert_top_p, top_p_renorm)
+
+
+def coli_abi_version() -> int:
+    return lib().coli_abi_version()
+
+
+def coli_quant_pack(qtype: int, w: torch.Tensor, q_out: torch.Tensor, scale_out: torch.Tensor,
+                    stream=None) -> None:
+    """w fp32 [rows, cols] -> q_out uint8 [rows, cols*qtype/8], scale_out fp32 [rows]."""
+    rows, cols = w.shape
+    if q_out.numel() != rows * cols * qtype // 8 or scale_out.numel() != rows:
+        raise ValueError("output sizes do not match")
+    _check("coli_quant_pack", lib().coli_quant_pack(
+        qtype, _ptr(w, torch.float32, "w"), rows, cols, _ptr(q_out, torch.uint8, "q_out"),
+        _ptr(scale_out, torch.float32, "scale_out"), _stream(stream)))
+
+
+def coli_quant_act_q8_0(x: torch.Tensor, q: torch.Tensor, d: torch.Tensor, stream=None) -> None:
+    """x fp32 [T, n] -> q int8 [T, n] (natural order), d fp32 [T, n/32]."""
+    T, n = x.shape
+    if q.numel() != T * n or d.numel() != T * (n // 32):
+        raise ValueError("output sizes do not match")
+    _check("coli_quant_act_q8_0", lib().coli_quant_act_q8_0(
+        _ptr(x, torch.float32, "x"), T, n, _ptr(q, torch.int8, "q"), _ptr(d, torch.float32, "d"),
+        _stream(stream)))
+
+
+def coli_moe_logits(x: torch.Tensor, gate_w: torch.Tensor, logits: torch.Tensor, stream=None) -> None:
+    T, H = x.shape
+    E = gate_w.shape[0]
+    if gate_w.shape[1] != H or logits.numel() != T * E:
+        raise ValueError("shape mismatch")
+    _check("coli_moe_logits", lib().coli_moe_logits(
+        _ptr(x, torch.float32, "x"), _ptr(gate_w, torch.float32, "gate_w"), T, E, H,
+        _ptr(logits, torch.float32, "logits"), _stream(stream)))
+
+
+def coli_moe_route(cfg: RouterCfg, logits: torch.Tensor, bias: torch.Tensor | None,
+                   idx: torch.Tensor, w: torch.Tensor, stream=None) -> None:
+    T = logits.shape[0]
+    if logits.shape[1] != cfg.n_experts or idx.numel() != T * cfg.top_k or w.numel() != T * cfg.top_k:
+        raise ValueError("shape mismatch")
+    _check("coli_moe_route", lib().coli_moe_route(
+        ctypes.byref(cfg), _ptr(logits, torch.float32, "logits"),
+        _ptr(bias, torch.float32, "bias"), T, _ptr(idx, torch.int32, "idx"),
+        _ptr(w, torch.float32, "w"), _stream(stream)))
+
+
+def coli_moe_dispatch(idx: torch.Tensor, E: int, counts, offs, perm, uniq, n_uniq,
+                      stream=None) -> None:
+    T, k = idx.shape
+    _check("coli_moe_dispatch", lib().coli_moe_dispatch(
+        _ptr(idx, torch.int32, "idx"), T, k, E, _ptr(counts, torch.int32, "counts"),
+        _ptr(offs, torch.int32, "offs"), _ptr(perm, torch.int32, "perm"),
+        _ptr(uniq, torch.int32, "uniq"), _ptr(n_uniq, torch.int32, "n_uniq"), _stream(stream)))
+
+
+class MoeLayer:
+    """A layer's device tensors plus the C descriptor that points at them.
+
+    Routed tensors are stacked: w_gate/w_up uint8 [E, I, H*b/8], s_gate/s_up
+    fp32 [E, I], w_down uint8 [E, H, I*b/8], s_down fp32 [E, H]; the shared
+    expert's tensors have no leading E.  The object keeps the tensors alive.
+    """
+
+    def __init__(self, hidden, inter, qtype, cfg: RouterCfg, gate_w, gate_bias,
+                 w_gate, s_gate, w_up, s_up, w_down, s_down,
+                 sh_gate, sh_s_gate, sh_up, sh_s_up, sh_down, sh_s_down, mfma_min_tokens=0):
+        self.hidden, self.inter, self.qtype, self.cfg = hidden, inter, qtype, cfg
+        self.gate_w, self.gate_bias = gate_w, gate_bias
+        self.w_gate, self.s_gate, self.w_up, self.s_up = w_gate, s_gate, w_up, s_up
+        self.w_down, self.s_down = w_down, s_down
+        self.sh_gate, self.sh_s_gate, self.sh_up, self.sh_s_up = sh_gate, sh_s_gate, sh_up, sh_s_up
+        self.sh_down, self.sh_s_down = sh_down, sh_s_down
+        self.mfma_min_tokens = mfma_min_tokens
+
+    def c_struct(self) -> MoeLayerC:
+        u8, f32 = torch.uint8, torch.float32
+        return MoeLayerC(self.hidden, self.inter, self.qtype, self.cfg,
+                         _ptr(self.gate_w, f32, "gate_w"), _ptr(self.gate_bias, f32, "gate_bias"),
+                         _ptr(self.w_gate, u8, "w_gate"), _ptr(self.w_up, u8, "w_up"),
+                         _ptr(self.w_down, u8, "w_down"),
+                         _ptr(self.s_gate, f32, "s_gate"), _ptr(self.s_up, f32, "s_up"),
+                         _ptr(self.s_down, f32, "s_down"),
+                         _ptr(self.sh_gate, u8, "sh_gate"), _ptr(self.sh_up, u8, "sh_up"),
+                         _ptr(self.sh_down, u8, "sh_down"),
+                         _ptr(self.sh_s_gate, f32, "sh_s_gate"), _ptr(self.sh_s_up, f32, "sh_s_up"),
+                         _ptr(self.sh_s_down, f32, "sh_s_down"), self.mfma_min_tokens)
+
+    @staticmethod
+    def empty(hidden, inter, qtype, cfg: RouterCfg, device="cuda", gate=True) -> "MoeLayer":
+        """Uninitialised device storage for a layer (filled by coli_quant_pack)."""
+        E, H, I = cfg.n_experts, hidden, inter
+        gb, db = H * qtype // 8, I * qtype // 8
+        u8, f32 = torch.uint8, torch.float32
+        z = lambda *s, dt: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
+        return MoeLayer(H, I, qtype, cfg,
+                        z(E, H, dt=f32) if gate else None, z(E, dt=f32),
+                        z(E, I, gb, dt=u8), z(E, I, dt=f32), z(E, I, gb, dt=u8), z(E, I, dt=f32),
+                        z(E, H, db, dt=u8), z(E, H, dt=f32),
+                        z(I, gb, dt=u8), z(I, dt=f32), z(I, gb, dt=u8), z(I, dt=f32),
+                        z(H, db, dt=u8), z(H, dt=f32))
+
+    def pack_expert(self, e: int, gate: torch.Tensor, up: torch.Tensor, down: torch.Tensor,
+                    stream=None) -> None:
+        """Quantise fp32 gate [I, H], up [I, H], down [H, I] of routed expert e
+        (e == n_experts: the shared expert) into this layer's storage."""
+        if e == self.cfg.n_experts:
+            dst = ((self.sh_gate, self.sh_s_gate), (self.sh_up, self.sh_s_up),
+                   (self.sh_down, self.sh_s_down))
+        else:
+            dst = ((self.w_gate[e], self.s_gate[e]), (self.w_up[e], self.s_up[e]),
+                   (self.w_down[e], self.s_down[e]))
+        for src, (q, s) in zip((gate, up, down), dst):
+            coli_quant_pack(self.qtype, src, q, s, stream)
+
+
+def coli_moe_workspace_bytes(layer: MoeLayer, max_tokens: int) -> int:
+    c = layer.c_struct()
+    return lib().coli_moe_workspace_bytes(ctypes.byref(c), max_tokens)
+
+
+def workspace(layer: MoeLayer, max_tokens: int, device="cuda") -> torch.Tensor:
+    """A device workspace big enough for ``max_tokens`` (256-byte aligned)."""
+    n = coli_moe_workspace_bytes(layer, max_tokens)
+    if n == 0:
+        raise ValueError("invalid layer descriptor")
+    buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + n]
+
+
+def coli_moe_forward(layer: MoeLayer, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor,
+                     logits_in=None, idx_out=None, w_out=None, logits_out=None,
+                     stream=None, c_layer: MoeLayerC | None = None) -> None:
+    """y [T, H] = the layer on x [T, H]; optional routing outputs."""
+    T = x.shape[0]
+    c = c_layer if c_layer is not None else layer.c_struct()
+    _check("coli_moe_forward", lib().coli_moe_forward(
+        ctypes.byref(c), _ptr(x, torch.float32, "x"), T,
+        _ptr(logits_in, torch.float32, "logits_in"), _ptr(y, torch.float32, "y"),
+        _ptr(idx_out, torch.int32, "idx_out"), _ptr(w_out, torch.float32, "w_out"),
+        _ptr(logits_out, torch.float32, "logits_out"), ctypes.c_void_p(ws.data_ptr()),
+        ws.numel(), _stream(stream)))
+
+
+def coli_debug_qgemv_blocks(qtype: int, Wq: torch.Tensor, cols: int, xq: torch.Tensor,
+                            acc_out: torch.Tensor, stream=None) -> None:
+    rows = Wq.shape[0]
+    T = xq.shape[0]
+    _check("coli_debug_qgemv_blocks", lib().coli_debug_qgemv_blocks(
+        qtype, _ptr(Wq, torch.uint8, "Wq"), rows, cols, _ptr(xq, torch.int8, "xq"), T,
+        _ptr(acc_out, torch.int32, "acc_out"), _stream(stream)))

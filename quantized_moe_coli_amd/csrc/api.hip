@@ -1,0 +1,300 @@
+// api.hip -- the C ABI declared in include/coli_moe.h: argument validation,
+// workspace layout and the kernel sequence of each call.  Nothing here
+// allocates device memory or synchronises the stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "coli_moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+
+constexpr int kMaxDim = 8192;
+constexpr int kMaxTokens = 1 << 20;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Device check, cached per device: 0 unknown, 1 usable gfx950, 2 not usable.
+std::atomic<int> g_dev_state[64];
+
+coli_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return COLI_ERR_DEVICE;
+  }
+  if (dev >= 64) return COLI_ERR_DEVICE;
+  int st = g_dev_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    st = 2;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+        std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
+      st = 1;
+    (void)hipGetLastError();
+    g_dev_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? COLI_OK : COLI_ERR_DEVICE;
+}
+
+coli_status from_hip(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_ERR_DEVICE; }
+
+bool qtype_ok(int q) { return q == COLI_Q8 || q == COLI_Q4 || q == COLI_Q2; }
+
+bool router_ok(const coli_router_cfg *c) {
+  if (!c) return false;
+  const int E = c->n_experts, G = c->n_group;
+  if (E < 1 || E > 1024 || G < 1 || G > 64 || E % G) return false;
+  if (c->topk_group < 1 || c->topk_group > G) return false;
+  if (c->top_k < 1 || c->top_k > 32 || c->top_k > c->topk_group * (E / G)) return false;
+  return true;
+}
+
+bool layer_ok(const coli_moe_layer *L) {
+  if (!L || !qtype_ok(L->qtype) || !router_ok(&L->router)) return false;
+  const int H = L->hidden, I = L->inter;
+  if (H < 64 || I < 64 || H > kMaxDim || I > kMaxDim || H % 64 || I % 64) return false;
+  const void *w[] = {L->w_gate, L->w_up, L->w_down, L->sh_gate, L->sh_up, L->sh_down};
+  for (const void *p : w)
+    if (!p || !aligned(p, 16)) return false;
+  const void *s[] = {L->s_gate, L->s_up, L->s_down, L->sh_s_gate, L->sh_s_up, L->sh_s_down};
+  for (const void *p : s)
+    if (!p || !aligned(p, 4)) return false;
+  if (L->gate_w && !aligned(L->gate_w, 16)) return false;
+  if (L->gate_bias && !aligned(L->gate_bias, 4)) return false;
+  if (L->mfma_min_tokens < 0) return false;
+  return true;
+}
+
+coli::RouterCfg to_cfg(const coli_router_cfg &c) {
+  return coli::RouterCfg{c.n_experts, c.top_k, c.n_group, c.topk_group, c.norm_topk_prob,
+                         c.routed_scaling_factor, c.expert_top_p, c.top_p_renorm};
+}
+
+struct WsLayout {
+  size_t xq, xd, logits, idx, w, counts, offs, perm, uniq, nuniq, hq, hd, obuf, total;
+};
+
+WsLayout ws_layout(const coli_moe_layer *L, int Tmax) {
+  const size_t H = L->hidden, I = L->inter, E = L->router.n_experts, k = L->router.top_k;
+  const size_t T = Tmax < 1 ? 1 : Tmax;
+  WsLayout w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + (bytes ? bytes : 1), 256);
+    return o;
+  };
+  w.xq = take(T * H);
+  w.xd = take(T * (H / 32) * 4);
+  w.logits = take(T * E * 4);
+  w.idx = take(T * k * 4);
+  w.w = take(T * k * 4);
+  w.counts = take(E * 4);
+  w.offs = take((E + 1) * 4);
+  w.perm = take(T * k * 4);
+  w.uniq = take(E * 4);
+  w.nuniq = take(4);
+  w.hq = take((T * k + T) * I);
+  w.hd = take((T * k + T) * (I / 32) * 4);
+  w.obuf = take(Tmax >= 2 ? T * (k + 1) * H * 4 : 0);
+  w.total = off;
+  return w;
+}
+
+template <typename F>
+coli_status guarded(F &&f) {
+  try {
+    return f();
+  } catch (...) {
+    return COLI_ERR_DEVICE;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int coli_abi_version(void) { return COLI_ABI_VERSION; }
+
+const char *coli_status_str(coli_status s) {
+  switch (s) {
+    case COLI_OK: return "ok";
+    case COLI_ERR_INVALID_ARG: return "invalid argument";
+    case COLI_ERR_UNSUPPORTED: return "unsupported configuration";
+    case COLI_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case COLI_ERR_DEVICE: return "no usable gfx950 device, or a launch failed";
+  }
+  return "unknown status";
+}
+
+coli_status coli_quant_pack(int32_t qtype, const float *w, int64_t rows, int64_t cols,
+                            uint8_t *q_out, float *scale_out, void *stream) {
+  return guarded([&] {
+    if (!qtype_ok(qtype) || rows < 0 || cols <= 0 || cols % 32 || !w || !q_out || !scale_out)
+      return COLI_ERR_INVALID_ARG;
+    if (!aligned(w, 4) || !aligned(q_out, 4) || !aligned(scale_out, 4)) return COLI_ERR_INVALID_ARG;
+    if (rows > (int64_t)1 << 34) return COLI_ERR_UNSUPPORTED;
+    const coli_status d = check_device();
+    if (d != COLI_OK) return d;
+    return from_hip(coli::launch_quant_pack(qtype, w, rows, cols, q_out, scale_out,
+                                            static_cast<hipStream_t>(stream)));
+  });
+}
+
+coli_status coli_quant_act_q8_0(const float *x, int32_t T, int32_t n, int8_t *q, float *d,
+                                void *stream) {
+  return guarded([&] {
+    if (T < 0 || n <= 0 || n % 32 || !x || !q || !d) return COLI_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(d, 4)) return COLI_ERR_INVALID_ARG;
+    const coli_status st = check_device();
+    if (st != COLI_OK) return st;
+    return from_hip(coli::launch_act_quant(8, x, T, n, q, d, static_cast<hipStream_t>(stream)));
+  });
+}
+
+coli_status coli_moe_logits(const float *x, const float *gate_w, int32_t T, int32_t E, int32_t H,
+                            float *logits, void *stream) {
+  return guarded([&] {
+    if (T < 0 || E < 1 || H < 32 || H % 32 || !x || !gate_w || !logits) return COLI_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(gate_w, 16) || !aligned(logits, 4)) return COLI_ERR_INVALID_ARG;
+    const coli_status st = check_device();
+    if (st != COLI_OK) return st;
+    return from_hip(coli::launch_logits(x, gate_w, T, E, H, logits, static_cast<hipStream_t>(stream)));
+  });
+}
+
+coli_status coli_moe_route(const coli_router_cfg *cfg, const float *logits, const float *bias,
+                           int32_t T, int32_t *topk_idx, float *topk_w, void *stream) {
+  return guarded([&] {
+    if (!router_ok(cfg) || T < 0 || T > kMaxTokens || !logits || !topk_idx || !topk_w)
+      return COLI_ERR_INVALID_ARG;
+    const coli_status st = check_device();
+    if (st != COLI_OK) return st;
+    return from_hip(coli::launch_route(to_cfg(*cfg), logits, bias, T, topk_idx, topk_w, nullptr,
+                                       nullptr, static_cast<hipStream_t>(stream)));
+  });
+}
+
+coli_status coli_moe_dispatch(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E,
+                              int32_t *counts, int32_t *offs, int32_t *perm, int32_t *uniq,
+                              int32_t *n_uniq, void *stream) {
+  return guarded([&] {
+    if (T < 0 || T > kMaxTokens || k < 1 || k > 32 || E < 1 || E > 1024 || !topk_idx || !counts ||
+        !offs || !perm || !uniq || !n_uniq)
+      return COLI_ERR_INVALID_ARG;
+    const coli_status st = check_device();
+    if (st != COLI_OK) return st;
+    return from_hip(coli::launch_dispatch(topk_idx, T, k, E, counts, offs, perm, uniq, n_uniq,
+                                          static_cast<hipStream_t>(stream)));
+  });
+}
+
+size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int32_t max_tokens) {
+  if (!layer_ok(L) || max_tokens < 0 || max_tokens > kMaxTokens) return 0;
+  return ws_layout(L, max_tokens).total;
+}
+
+coli_status coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
+                             const float *logits_in, float *y, int32_t *idx_out, float *w_out,
+                             float *logits_out, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  return guarded([&] {
+    if (!layer_ok(L) || T < 0 || T > kMaxTokens) return COLI_ERR_INVALID_ARG;
+    if (T == 0) return COLI_OK;
+    if (!x || !y) return COLI_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16)) return COLI_ERR_INVALID_ARG;
+    if (!logits_in && !L->gate_w) return COLI_ERR_INVALID_ARG;
+    if (logits_in && !aligned(logits_in, 4)) return COLI_ERR_INVALID_ARG;
+    if ((idx_out && !aligned(idx_out, 4)) || (w_out && !aligned(w_out, 4)) ||
+        (logits_out && !aligned(logits_out, 4)))
+      return COLI_ERR_INVALID_ARG;
+    const WsLayout ws = ws_layout(L, T);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < ws.total)
+      return COLI_ERR_WORKSPACE;
+    const coli_status st = check_device();
+    if (st != COLI_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *base = static_cast<char *>(workspace);
+    const int H = L->hidden, I = L->inter, E = L->router.n_experts, k = L->router.top_k;
+    int8_t *xq = reinterpret_cast<int8_t *>(base + ws.xq);
+    float *xd = reinterpret_cast<float *>(base + ws.xd);
+    int32_t *idx = reinterpret_cast<int32_t *>(base + ws.idx);
+    float *wts = reinterpret_cast<float *>(base + ws.w);
+
+    hipError_t e = coli::launch_act_quant(L->qtype, x, T, H, xq, xd, s);
+    if (e != hipSuccess) return COLI_ERR_DEVICE;
+
+    const float *lp = logits_in;
+    if (logits_in) {
+      if (logits_out) {
+        e = hipMemcpyAsync(logits_out, logits_in, (size_t)T * E * sizeof(float),
+                           hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return COLI_ERR_DEVICE;
+      }
+    } else {
+      float *dst = logits_out ? logits_out : reinterpret_cast<float *>(base + ws.logits);
+      e = coli::launch_logits(x, L->gate_w, T, E, H, dst, s);
+      if (e != hipSuccess) return COLI_ERR_DEVICE;
+      lp = dst;
+    }
+    e = coli::launch_route(to_cfg(L->router), lp, L->gate_bias, T, idx, wts, idx_out, w_out, s);
+    if (e != hipSuccess) return COLI_ERR_DEVICE;
+
+    coli::FfnArgs fa{};
+    fa.L = coli::LayerPtrs{H, I, L->qtype, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up,
+                           L->s_down, L->sh_gate, L->sh_up, L->sh_down, L->sh_s_gate,
+                           L->sh_s_up, L->sh_s_down};
+    fa.T = T;
+    fa.k = k;
+    fa.E = E;
+    fa.xq = xq;
+    fa.xd = xd;
+    fa.idx = idx;
+    fa.w = wts;
+    fa.hq = reinterpret_cast<int8_t *>(base + ws.hq);
+    fa.hd = reinterpret_cast<float *>(base + ws.hd);
+    fa.obuf = reinterpret_cast<float *>(base + ws.obuf);
+    fa.y = y;
+    const int mfma_min = L->mfma_min_tokens;
+    if (T == 1) {
+      e = coli::launch_gateup(fa, false, mfma_min, s);
+      if (e == hipSuccess) e = coli::launch_down(fa, false, mfma_min, s);
+      return from_hip(e);
+    }
+    int32_t *counts = reinterpret_cast<int32_t *>(base + ws.counts);
+    int32_t *offs = reinterpret_cast<int32_t *>(base + ws.offs);
+    int32_t *perm = reinterpret_cast<int32_t *>(base + ws.perm);
+    int32_t *uniq = reinterpret_cast<int32_t *>(base + ws.uniq);
+    int32_t *nuniq = reinterpret_cast<int32_t *>(base + ws.nuniq);
+    e = coli::launch_dispatch(idx, T, k, E, counts, offs, perm, uniq, nuniq, s);
+    if (e != hipSuccess) return COLI_ERR_DEVICE;
+    fa.disp = coli::Dispatch{counts, offs, perm, uniq, nuniq};
+    e = coli::launch_gateup(fa, true, mfma_min, s);
+    if (e == hipSuccess) e = coli::launch_down(fa, true, mfma_min, s);
+    if (e == hipSuccess) e = coli::launch_combine(fa, s);
+    return from_hip(e);
+  });
+}
+
+coli_status coli_debug_qgemv_blocks(int32_t qtype, const uint8_t *Wq, int32_t rows, int32_t cols,
+                                    const int8_t *xq, int32_t T, int32_t *acc_out, void *stream) {
+  return guarded([&] {
+    if (!qtype_ok(qtype) || rows < 0 || cols < 64 || cols % 64 || T < 0 || T > 8 || !Wq || !xq ||
+        !acc_out)
+      return COLI_ERR_INVALID_ARG;
+    if (!aligned(Wq, 16) || !aligned(xq, 4) || !aligned(acc_out, 4)) return COLI_ERR_INVALID_ARG;
+    const coli_status st = check_device();
+    if (st != COLI_OK) return st;
+    return from_hip(coli::launch_debug_blocks(qtype, Wq, rows, cols, xq, T, acc_out,
+                                              static_cast<hipStream_t>(stream)));
+  });
+}
+
+}  // extern "C"

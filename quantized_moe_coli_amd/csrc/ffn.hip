@@ -1,0 +1,557 @@
+// ffn.hip -- the expert FFNs of the routed-MoE layer on the integer
+// dot-product path (gfx950 v_dot4_i32_i8), decode and batch-union modes.
+//
+// colibrì README, "Implemented features": expert weights are int8 / packed
+// int4 / packed int2 with one scale per row, dequantised on use against
+// Q8_0-style int8 activations; the MoE is DeepSeek-V3-like (SwiGLU experts
+// plus a shared expert); in a batch each unique expert is read once and
+// applied to every position routed to it.
+//
+// Work split.  A "chunk" is 16 bytes of packed weights (device.hpp).  LPR
+// lanes share a weight row, lane c of the group loading chunks c, c+LPR, ...
+// (CPL chunks at most), so every wave-wide load is a run of contiguous
+// 16-byte pieces; the fp32 partial sums of a row are reduced across its LPR
+// lanes with DPP.  Each block partial is scaled by its Q8_0 scale d in fp32
+// and the row sum by the row scale s.
+//
+// Gate/up: a workgroup owns 32 consecutive intermediate rows of one expert
+// (exactly one Q8_0 block of h), computes g and u for every token of the
+// expert, h = silu(g) * u, and quantises the 32 values of h per token to
+// one Q8_0 block -- so the down projection's input never leaves int8.
+//
+// Down: decode mode spreads the k+1 slots of the token over the waves of a
+// workgroup and combines w_j * o_j in a fixed slot order through LDS; union
+// mode runs one expert over its tokens and writes o into a per-(token, slot)
+// buffer that a combine kernel reduces in the same fixed order.  No
+// floating-point atomics: results are bit-reproducible.
+#include "kernels.hpp"
+
+namespace coli {
+
+template <int BITS>
+struct Act {
+  static constexpr int kInts = Q<BITS>::kElems / 4;
+  static constexpr int kD = Q<BITS>::kBlocks;
+  int a[kInts];
+  float d[kD];
+};
+
+// Activation codes/scales for chunk c of a row (codes in BITS ordering).
+template <int BITS>
+__device__ __forceinline__ void load_act(Act<BITS> &ac, const int8_t *q, const float *d, int c) {
+  const uint4 *p = reinterpret_cast<const uint4 *>(q + (size_t)c * Q<BITS>::kElems);
+#pragma unroll
+  for (int m = 0; m < Act<BITS>::kInts / 4; ++m) {
+    const uint4 v = p[m];
+    ac.a[4 * m] = (int)v.x;
+    ac.a[4 * m + 1] = (int)v.y;
+    ac.a[4 * m + 2] = (int)v.z;
+    ac.a[4 * m + 3] = (int)v.w;
+  }
+  if constexpr (BITS == 8) ac.d[0] = d[c >> 1];
+  else if constexpr (BITS == 4) ac.d[0] = d[c];
+  else { ac.d[0] = d[2 * c]; ac.d[1] = d[2 * c + 1]; }
+}
+
+template <int BITS>
+__device__ __forceinline__ void zero_act(Act<BITS> &ac) {
+#pragma unroll
+  for (int m = 0; m < Act<BITS>::kInts; ++m) ac.a[m] = 0;
+#pragma unroll
+  for (int m = 0; m < Act<BITS>::kD; ++m) ac.d[m] = 0.f;
+}
+
+template <int BITS>
+__device__ __forceinline__ float chunk_part(const uint4 w, const Act<BITS> &ac) {
+  if constexpr (BITS == 8) return ac.d[0] * (float)chunk_dot_q8(w, ac.a);
+  else if constexpr (BITS == 4) return ac.d[0] * (float)chunk_dot_q4(w, ac.a);
+  else {
+    int b0, b1;
+    chunk_dot_q2(w, ac.a, b0, b1);
+    return ac.d[0] * (float)b0 + ac.d[1] * (float)b1;
+  }
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.f + expf(-g)); }
+
+// Resolve an item's expert: returns false if the slot has no work.
+struct SlotInfo {
+  const uint8_t *wg, *wu, *wd;
+  const float *sg, *su, *sd;
+  int n_tok;    // tokens of this slot
+  int p0;       // union: first perm position (routed) / -1 shared
+  int slot;     // decode: slot index
+  bool shared;
+};
+
+__device__ __forceinline__ bool resolve_slot(const FfnArgs &a, bool union_mode, int u,
+                                             SlotInfo &s) {
+  const LayerPtrs &L = a.L;
+  const size_t gu_stride = (size_t)L.I * (L.H * L.bits / 8);
+  const size_t d_stride = (size_t)L.H * (L.I * L.bits / 8);
+  int e;
+  if (!union_mode) {
+    if (u > a.k) return false;
+    s.slot = u;
+    s.shared = (u == a.k);
+    s.n_tok = 1;
+    s.p0 = 0;
+    e = s.shared ? -1 : a.idx[u];
+    if (!s.shared && e < 0) return false;
+  } else {
+    const int nu = *a.disp.n_uniq;
+    if (u > nu) return false;
+    s.slot = -1;
+    s.shared = (u == nu);
+    if (s.shared) {
+      e = -1;
+      s.n_tok = a.T;
+      s.p0 = -1;
+    } else {
+      e = a.disp.uniq[u];
+      s.p0 = a.disp.offs[e];
+      s.n_tok = a.disp.offs[e + 1] - s.p0;
+    }
+  }
+  if (s.shared) {
+    s.wg = L.sh_gate; s.wu = L.sh_up; s.wd = L.sh_down;
+    s.sg = L.sh_s_gate; s.su = L.sh_s_up; s.sd = L.sh_s_down;
+  } else {
+    s.wg = L.w_gate + (size_t)e * gu_stride;
+    s.wu = L.w_up + (size_t)e * gu_stride;
+    s.wd = L.w_down + (size_t)e * d_stride;
+    s.sg = L.s_gate + (size_t)e * L.I;
+    s.su = L.s_up + (size_t)e * L.I;
+    s.sd = L.s_down + (size_t)e * L.H;
+  }
+  return true;
+}
+
+// Token n (0-based) of a slot -> (token t, activation/h row, slot j).
+__device__ __forceinline__ void slot_token(const FfnArgs &a, bool union_mode, const SlotInfo &s,
+                                           int n, int &t, int &hrow, int &j) {
+  if (!union_mode) {
+    t = 0;
+    hrow = s.slot;
+    j = s.slot;
+  } else if (s.shared) {
+    t = n;
+    hrow = a.disp.offs[a.E] + n;
+    j = a.k;
+  } else {
+    const int p = a.disp.perm[s.p0 + n];
+    t = p / a.k;
+    j = p % a.k;
+    hrow = s.p0 + n;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up + SwiGLU + Q8_0(h).  grid.x = slots * (I/32); block = 256.
+// ---------------------------------------------------------------------------
+template <int BITS, int LPR, int CPL, int NT>
+__global__ __launch_bounds__(256) void k_gateup(FfnArgs a, int union_mode) {
+  constexpr int RPP = 64 / LPR;  // rows per pass of a wave
+  constexpr int ROWS_PER_WAVE = 8;
+  constexpr int PASSES = ROWS_PER_WAVE / RPP;
+  __shared__ float hs[NT][32];
+  const int n_rb = a.L.I / 32;
+  const int u = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
+  SlotInfo s;
+  if (!resolve_slot(a, union_mode != 0, u, s)) return;
+
+  const int H = a.L.H, I = a.L.I;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gl = lane % LPR;           // lane in its row group
+  const int rsub = lane / LPR;         // row within the pass
+  const int nchunks = H * BITS / 128;  // 16-byte chunks per row
+  const size_t row_bytes = (size_t)H * BITS / 8;
+  const int xblocks = H / 32;
+
+  for (int t0 = 0; t0 < s.n_tok; t0 += NT) {
+    Act<BITS> act[CPL][NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      int t = 0, hrow = 0, j = 0;
+      const bool tv = t0 + tt < s.n_tok;
+      if (tv) slot_token(a, union_mode != 0, s, t0 + tt, t, hrow, j);
+      const int8_t *xq = a.xq + (size_t)t * H;
+      const float *xd = a.xd + (size_t)t * xblocks;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = gl + LPR * i;
+        if (tv && c < nchunks) load_act<BITS>(act[i][tt], xq, xd, c);
+        else zero_act<BITS>(act[i][tt]);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int rl = wave * ROWS_PER_WAVE + p * RPP + rsub;  // row within the 32-row block
+      const int row = rb * 32 + rl;
+      const uint4 *gp = reinterpret_cast<const uint4 *>(s.wg + (size_t)row * row_bytes);
+      const uint4 *up = reinterpret_cast<const uint4 *>(s.wu + (size_t)row * row_bytes);
+      uint4 wg[CPL], wu[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = gl + LPR * i;
+        if (c < nchunks) {
+          wg[i] = ld_nt(gp + c);
+          wu[i] = ld_nt(up + c);
+        } else {
+          wg[i] = make_uint4(0, 0, 0, 0);
+          wu[i] = make_uint4(0, 0, 0, 0);
+        }
+      }
+      float pg[NT], pu[NT];
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        pg[tt] = 0.f;
+        pu[tt] = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          pg[tt] += chunk_part<BITS>(wg[i], act[i][tt]);
+          pu[tt] += chunk_part<BITS>(wu[i], act[i][tt]);
+        }
+        pg[tt] = group_sum<LPR>(pg[tt]);
+        pu[tt] = group_sum<LPR>(pu[tt]);
+      }
+      if (lane == group_sum_lane<LPR>(lane)) {
+        const float sg = s.sg[row], su = s.su[row];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          const float g = pg[tt] * sg, uu = pu[tt] * su;
+          hs[tt][rl] = silu_f32(g) * uu;
+        }
+      }
+    }
+    __syncthreads();
+    // Q8_0 of each token's 32 h values: thread -> (token tt, element i)
+    {
+      const int tt = threadIdx.x >> 5, i = threadIdx.x & 31;
+      if (tt < NT) {
+        const float h = hs[tt][i];
+        float amax = group_max<32>(fabsf(h));
+        amax = __shfl(amax, (lane & 32) | 31, 64);
+        if (t0 + tt < s.n_tok) {
+          int t, hrow, j;
+          slot_token(a, union_mode != 0, s, t0 + tt, t, hrow, j);
+          const float db = amax / 127.f;
+          float c = 0.f;
+          if (db != 0.f) c = fminf(fmaxf(rintf(h / db), -127.f), 127.f);
+          a.hq[(size_t)hrow * I + rb * 32 + perm_dst<BITS>(i)] = (int8_t)c;
+          if (i == 0) a.hd[(size_t)hrow * (I / 32) + rb] = db;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Down, decode mode (T == 1).  grid.x = H / ROWS; block = 256 (4 waves).
+// Wave w handles slots w, w+4, ... of [routed 0..k-1, shared k]; each writes
+// w_j * o_j (o for the shared slot) per row into LDS; then the rows are
+// summed in the order shared, 0, 1, ..., k-1.
+// ---------------------------------------------------------------------------
+template <int BITS, int LPR, int CPL, int ROWS>
+__global__ __launch_bounds__(256) void k_down_decode(FfnArgs a) {
+  constexpr int RPP = 64 / LPR;
+  constexpr int PASSES = ROWS / RPP;
+  constexpr int kMaxSlots = 33;
+  __shared__ float part[kMaxSlots][ROWS];
+  const int I = a.L.I;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gl = lane % LPR, rsub = lane / LPR;
+  const int nchunks = I * BITS / 128;
+  const size_t row_bytes = (size_t)I * BITS / 8;
+  const int r0 = blockIdx.x * ROWS;
+  const int nslots = a.k + 1;
+
+  for (int sl = wave; sl < nslots; sl += 4) {
+    SlotInfo s;
+    const bool live = resolve_slot(a, false, sl, s);
+    if (!live) {
+      for (int r = lane; r < ROWS; r += 64) part[sl][r] = 0.f;
+      continue;
+    }
+    const float wgt = s.shared ? 1.f : a.w[sl];
+    Act<BITS> act[CPL];
+    const int8_t *hq = a.hq + (size_t)sl * I;
+    const float *hd = a.hd + (size_t)sl * (I / 32);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = gl + LPR * i;
+      if (c < nchunks) load_act<BITS>(act[i], hq, hd, c);
+      else zero_act<BITS>(act[i]);
+    }
+    uint4 wv[PASSES][CPL];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = r0 + p * RPP + rsub;
+      const uint4 *wp = reinterpret_cast<const uint4 *>(s.wd + (size_t)row * row_bytes);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = gl + LPR * i;
+        wv[p][i] = c < nchunks ? ld_nt(wp + c) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) acc += chunk_part<BITS>(wv[p][i], act[i]);
+      acc = group_sum<LPR>(acc);
+      const int rl = p * RPP + rsub;
+      if (lane == group_sum_lane<LPR>(lane)) {
+        const float o = acc * s.sd[r0 + rl];
+        part[sl][rl] = s.shared ? o : wgt * o;
+      }
+    }
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < ROWS; r += 256) {
+    float y = part[a.k][r];
+    for (int j = 0; j < a.k; ++j) y += part[j][r];
+    a.y[r0 + r] = y;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Down, union mode.  grid.x = slots * (H / (4*ROWS)); each wave owns ROWS
+// rows of one expert and runs every token of the expert on them (NT at a
+// time), writing o to obuf[t][j][row].
+// ---------------------------------------------------------------------------
+template <int BITS, int LPR, int CPL, int NT, int ROWS>
+__global__ __launch_bounds__(256) void k_down_union(FfnArgs a) {
+  constexpr int RPP = 64 / LPR;
+  constexpr int PASSES = ROWS / RPP;
+  const int H = a.L.H, I = a.L.I;
+  const int n_rb = H / (4 * ROWS);
+  const int u = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
+  SlotInfo s;
+  if (!resolve_slot(a, true, u, s)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gl = lane % LPR, rsub = lane / LPR;
+  const int nchunks = I * BITS / 128;
+  const size_t row_bytes = (size_t)I * BITS / 8;
+  const int r0 = rb * 4 * ROWS + wave * ROWS;
+
+  uint4 wv[PASSES][CPL];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = r0 + p * RPP + rsub;
+    const uint4 *wp = reinterpret_cast<const uint4 *>(s.wd + (size_t)row * row_bytes);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = gl + LPR * i;
+      wv[p][i] = c < nchunks ? ld_nt(wp + c) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  for (int t0 = 0; t0 < s.n_tok; t0 += NT) {
+    Act<BITS> act[CPL][NT];
+    int tok[NT], slot[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      int t = 0, hrow = 0, j = 0;
+      const bool tv = t0 + tt < s.n_tok;
+      if (tv) slot_token(a, true, s, t0 + tt, t, hrow, j);
+      tok[tt] = tv ? t : -1;
+      slot[tt] = j;
+      const int8_t *hq = a.hq + (size_t)hrow * I;
+      const float *hd = a.hd + (size_t)hrow * (I / 32);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = gl + LPR * i;
+        if (tv && c < nchunks) load_act<BITS>(act[i][tt], hq, hd, c);
+        else zero_act<BITS>(act[i][tt]);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = r0 + p * RPP + rsub;
+      float acc[NT];
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        acc[tt] = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) acc[tt] += chunk_part<BITS>(wv[p][i], act[i][tt]);
+        acc[tt] = group_sum<LPR>(acc[tt]);
+      }
+      if (lane == group_sum_lane<LPR>(lane)) {
+        const float sd = s.sd[row];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          if (tok[tt] >= 0)
+            a.obuf[((size_t)tok[tt] * (a.k + 1) + slot[tt]) * H + row] = acc[tt] * sd;
+      }
+    }
+  }
+}
+
+// y[t][r] = o_shared + sum over kept slots j (in order) of w_tj * o_tj.
+__global__ __launch_bounds__(256) void k_combine(FfnArgs a) {
+  const int H = a.L.H, k = a.k;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
+  if (i >= (int64_t)a.T * (H / 4)) return;
+  const int t = (int)(i / (H / 4)), r4 = (int)(i % (H / 4));
+  const float4 *ob = reinterpret_cast<const float4 *>(a.obuf + (size_t)t * (k + 1) * H);
+  float4 y = ob[(size_t)k * (H / 4) + r4];
+  for (int j = 0; j < k; ++j) {
+    if (a.idx[(size_t)t * k + j] < 0) continue;
+    const float w = a.w[(size_t)t * k + j];
+    const float4 o = ob[(size_t)j * (H / 4) + r4];
+    y.x += w * o.x;
+    y.y += w * o.y;
+    y.z += w * o.z;
+    y.w += w * o.w;
+  }
+  reinterpret_cast<float4 *>(a.y + (size_t)t * H)[r4] = y;
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers.  LPR is 32 when a row has an odd multiple of 32 chunks,
+// else 64; CPL is the chunk count per lane rounded up to 1, 2, 4 or 8.
+// ---------------------------------------------------------------------------
+static int pick_lpr(int nchunks) { return (nchunks % 64 != 0 && nchunks % 32 == 0) ? 32 : 64; }
+
+static int pick_cpl(int nchunks, int lpr) {
+  const int c = (nchunks + lpr - 1) / lpr;
+  return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : c <= 8 ? 8 : -1;
+}
+
+#define COLI_CPL_SWITCH(CPLV, ...)                        \
+  switch (CPLV) {                                         \
+    case 1: { constexpr int CPL = 1; __VA_ARGS__; } break; \
+    case 2: { constexpr int CPL = 2; __VA_ARGS__; } break; \
+    case 4: { constexpr int CPL = 4; __VA_ARGS__; } break; \
+    case 8: { constexpr int CPL = 8; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;                 \
+  }
+
+#define COLI_LPR_SWITCH(LPRV, ...)                          \
+  if ((LPRV) == 32) { constexpr int LPR = 32; __VA_ARGS__; } \
+  else { constexpr int LPR = 64; __VA_ARGS__; }
+
+#define COLI_BITS_SWITCH(BV, ...)                          \
+  switch (BV) {                                            \
+    case 8: { constexpr int BITS = 8; __VA_ARGS__; } break; \
+    case 4: { constexpr int BITS = 4; __VA_ARGS__; } break; \
+    case 2: { constexpr int BITS = 2; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;                  \
+  }
+
+static int union_slots(const FfnArgs &a) {
+  const long routed = (long)a.T * a.k;
+  return (int)((routed < a.E ? routed : a.E) + 1);
+}
+
+hipError_t launch_gateup(const FfnArgs &a, bool union_mode, int /*mfma_min*/, hipStream_t st) {
+  const int nch = a.L.H * a.L.bits / 128;
+  const int lpr = pick_lpr(nch), cpl = pick_cpl(nch, lpr);
+  const int slots = union_mode ? union_slots(a) : a.k + 1;
+  const dim3 grid((unsigned)(slots * (a.L.I / 32))), block(256);
+  COLI_BITS_SWITCH(a.L.bits, COLI_LPR_SWITCH(lpr, COLI_CPL_SWITCH(cpl, {
+    if (union_mode)
+      hipLaunchKernelGGL((k_gateup<BITS, LPR, CPL, 4>), grid, block, 0, st, a, 1);
+    else
+      hipLaunchKernelGGL((k_gateup<BITS, LPR, CPL, 1>), grid, block, 0, st, a, 0);
+  })));
+  return hipGetLastError();
+}
+
+hipError_t launch_down(const FfnArgs &a, bool union_mode, int /*mfma_min*/, hipStream_t st) {
+  const int nch = a.L.I * a.L.bits / 128;
+  const int lpr = pick_lpr(nch), cpl = pick_cpl(nch, lpr);
+  if (!union_mode) {
+    constexpr int ROWS = 16;
+    const dim3 grid((unsigned)(a.L.H / ROWS)), block(256);
+    COLI_BITS_SWITCH(a.L.bits, COLI_LPR_SWITCH(lpr, COLI_CPL_SWITCH(cpl, {
+      hipLaunchKernelGGL((k_down_decode<BITS, LPR, CPL, ROWS>), grid, block, 0, st, a);
+    })));
+  } else {
+    constexpr int ROWS = 8;
+    const int slots = union_slots(a);
+    const dim3 grid((unsigned)(slots * (a.L.H / (4 * ROWS)))), block(256);
+    COLI_BITS_SWITCH(a.L.bits, COLI_LPR_SWITCH(lpr, COLI_CPL_SWITCH(cpl, {
+      hipLaunchKernelGGL((k_down_union<BITS, LPR, CPL, 4, ROWS>), grid, block, 0, st, a);
+    })));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const FfnArgs &a, hipStream_t st) {
+  const int64_t n = (int64_t)a.T * (a.L.H / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Test export: exact int32 block sums through the same chunk products.
+// xq is in natural order; the kernel reorders each chunk's codes into the
+// container's ordering before the product.  Thread per (t, row, chunk).
+// ---------------------------------------------------------------------------
+template <int BITS>
+__global__ __launch_bounds__(256) void k_debug_blocks(const uint8_t *__restrict__ Wq, int rows,
+                                                      int cols, const int8_t *__restrict__ xq,
+                                                      int T, int32_t *__restrict__ acc) {
+  const int nch = cols * BITS / 128;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)T * rows * nch) return;
+  const int c = (int)(i % nch);
+  const int r = (int)((i / nch) % rows);
+  const int t = (int)(i / ((int64_t)nch * rows));
+  const uint4 w = reinterpret_cast<const uint4 *>(Wq + (size_t)r * cols * BITS / 8)[c];
+  constexpr int E = Q<BITS>::kElems;
+  int words[E / 4];
+  const int8_t *xs = xq + (size_t)t * cols + (size_t)c * E;
+#pragma unroll
+  for (int m = 0; m < E / 4; ++m) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v |= (uint32_t)(uint8_t)xs[perm_src<BITS>(4 * m + b)] << (8 * b);
+    words[m] = (int)v;
+  }
+  const int nb = cols / 32;
+  int32_t *out = acc + ((size_t)t * rows + r) * nb;
+  if constexpr (BITS == 8) {
+    // two chunks per block: the even chunk writes, the odd one adds later --
+    // instead each thread owns one half and the block sum is formed by the
+    // even-chunk thread reading its partner's codes.
+    if ((c & 1) == 0) {
+      const uint4 w2 = reinterpret_cast<const uint4 *>(Wq + (size_t)r * cols)[c + 1];
+      int words2[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) v |= (uint32_t)(uint8_t)xs[16 + 4 * m + b] << (8 * b);
+        words2[m] = (int)v;
+      }
+      out[c >> 1] = chunk_dot_q8(w, words) + chunk_dot_q8(w2, words2);
+    }
+  } else if constexpr (BITS == 4) {
+    out[c] = chunk_dot_q4(w, words);
+  } else {
+    int b0, b1;
+    chunk_dot_q2(w, words, b0, b1);
+    out[2 * c] = b0;
+    out[2 * c + 1] = b1;
+  }
+}
+
+hipError_t launch_debug_blocks(int bits, const uint8_t *Wq, int rows, int cols, const int8_t *xq,
+                               int T, int32_t *acc, hipStream_t st) {
+  const int64_t n = (int64_t)T * rows * (cols * bits / 128);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  switch (bits) {
+    case 8: hipLaunchKernelGGL(k_debug_blocks<8>, grid, block, 0, st, Wq, rows, cols, xq, T, acc); break;
+    case 4: hipLaunchKernelGGL(k_debug_blocks<4>, grid, block, 0, st, Wq, rows, cols, xq, T, acc); break;
+    case 2: hipLaunchKernelGGL(k_debug_blocks<2>, grid, block, 0, st, Wq, rows, cols, xq, T, acc); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace coli

@@ -1,0 +1,78 @@
+// kernels.hpp -- host-side launchers of the library's gfx950 kernels.  Each
+// launcher enqueues on `st` and returns the launch status; shapes have been
+// validated by the C-ABI layer (api.hip) before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "device.hpp"
+
+namespace coli {
+
+// Router configuration as the kernels see it (a copy of the ABI struct).
+struct RouterCfg {
+  int E, k, n_group, topk_group, norm;
+  float rsf, top_p;
+  int renorm;
+};
+
+// Pointers of one layer's weights (device), stacked routed experts plus the
+// shared expert.
+struct LayerPtrs {
+  int H, I, bits;
+  const uint8_t *w_gate, *w_up, *w_down;
+  const float *s_gate, *s_up, *s_down;
+  const uint8_t *sh_gate, *sh_up, *sh_down;
+  const float *sh_s_gate, *sh_s_up, *sh_s_down;
+};
+
+// Union bookkeeping living in the workspace.
+struct Dispatch {
+  const int32_t *counts;  // [E]
+  const int32_t *offs;    // [E+1]
+  const int32_t *perm;    // [T*k] entries t*k+j ordered by (expert, t, j)
+  const int32_t *uniq;    // [E]
+  const int32_t *n_uniq;  // [1]
+};
+
+hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t cols, uint8_t *q,
+                             float *scale, hipStream_t st);
+hipError_t launch_act_quant(int layout_bits, const float *x, int64_t T, int64_t n, int8_t *q,
+                            float *d, hipStream_t st);
+
+hipError_t launch_logits(const float *x, const float *gate_w, int T, int E, int H, float *logits,
+                         hipStream_t st);
+hipError_t launch_route(const RouterCfg &cfg, const float *logits, const float *bias, int T,
+                        int32_t *idx, float *w, int32_t *idx_copy, float *w_copy, hipStream_t st);
+hipError_t launch_dispatch(const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offs,
+                           int32_t *perm, int32_t *uniq, int32_t *n_uniq, hipStream_t st);
+
+// Expert FFN stages.  Slot lists: decode mode (T == 1) runs the k routed
+// slots of token 0 (idx[0..k-1], -1 skipped) plus the shared expert as slot
+// k; union mode runs every unique expert of the batch on its tokens plus the
+// shared expert on all T tokens.  hq/hd rows: decode -> slot; union -> the
+// pair's position in perm for routed pairs, n_routed + t for the shared one.
+struct FfnArgs {
+  LayerPtrs L;
+  int T, k, E;
+  const int8_t *xq;     // [T][H], ordering of L.bits
+  const float *xd;      // [T][H/32]
+  const int32_t *idx;   // [T][k]
+  const float *w;       // [T][k]
+  Dispatch disp;        // union mode only
+  int8_t *hq;           // [rows][I], ordering of L.bits
+  float *hd;            // [rows][I/32]
+  float *obuf;          // union: [T][k+1][H]
+  float *y;             // [T][H]
+};
+
+hipError_t launch_gateup(const FfnArgs &a, bool union_mode, int mfma_min, hipStream_t st);
+hipError_t launch_down(const FfnArgs &a, bool union_mode, int mfma_min, hipStream_t st);
+hipError_t launch_combine(const FfnArgs &a, hipStream_t st);
+
+hipError_t launch_debug_blocks(int bits, const uint8_t *Wq, int rows, int cols, const int8_t *xq_perm,
+                               int T, int32_t *acc, hipStream_t st);
+
+}  // namespace coli

@@ -1,0 +1,333 @@
+"""GPU parity: every step of the layer on gfx950 through the C ABI, against
+the CPU oracle on the same seeded inputs.
+
+Bar: bit-exact for packed codes, scales, Q8_0 codes, int32 block
+accumulators, routing indices and weights (when both sides take the same
+fp32 logits) and the union tables; router logits within 1 ulp (binary64
+accumulation in a different order, rounded once); layer outputs within
+1e-3 of the token's largest |y| (the GPU accumulates in fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (LayerPair, assert_close_layer, gpu_cfg, orc_cfg, to_dev, ulp_diff)
+from quantized_moe_coli_amd import binding as B
+from quantized_moe_coli_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "needs a GPU"
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    assert name.startswith("gfx950"), name
+
+
+def _special_rows(rng, R, C):
+    w = rng.normal(0, 0.02, size=(R, C)).astype(F32)
+    w[0] = 0.0                                     # zero row
+    w[1] = rng.integers(-7, 8, size=C) * F32(2.0 ** -6)  # grid row
+    w[1, 0] = 7 * 2.0 ** -6
+    w[2] *= F32(1e-30)                             # tiny values
+    w[3] *= F32(1e30)                              # huge values
+    w[4, :] = 0.0
+    w[4, 5] = -3.0                                 # single negative spike
+    return w
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("R,C", [(37, 96), (64, 256), (8, 6144)])
+def test_quant_pack_bit_exact(orc, bits, R, C):
+    rng = np.random.default_rng(R * C + bits)
+    w = _special_rows(rng, R, C)
+    q_ref, s_ref = orc.quant_pack(bits, w)
+    q = torch.empty(R, C * bits // 8, dtype=torch.uint8, device="cuda")
+    s = torch.empty(R, device="cuda")
+    B.coli_quant_pack(bits, to_dev(w), q, s)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("bits", [4, 8, 2])
+def test_quant_pack_full_expert(orc, bits):
+    """A GLM-5.2-shaped expert matrix, 2048 x 6144, drawn on the device."""
+    w = inputs.normal((2048, 6144), 0.02, "cuda", 77, bits)
+    q = torch.empty(2048, 6144 * bits // 8, dtype=torch.uint8, device="cuda")
+    s = torch.empty(2048, device="cuda")
+    B.coli_quant_pack(bits, w, q, s)
+    q_ref, s_ref = orc.quant_pack(bits, w.cpu().numpy())
+    np.testing.assert_array_equal(s.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("T,n", [(1, 32), (3, 256), (17, 6144), (512, 2048)])
+def test_act_quant_bit_exact(orc, T, n):
+    rng = np.random.default_rng(T + n)
+    x = rng.normal(0, 1, size=(T, n)).astype(F32)
+    x[0, :32] = 0.0
+    if n >= 64:
+        x[0, 32:64] = rng.integers(-127, 128, size=32) * F32(2.0 ** -9)
+        x[0, 32] = 127 * 2.0 ** -9
+    q_ref, d_ref = orc.q8_0(x)
+    q = torch.empty(T, n, dtype=torch.int8, device="cuda")
+    d = torch.empty(T, n // 32, device="cuda")
+    B.coli_quant_act_q8_0(to_dev(x), q, d)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d.cpu().numpy(), d_ref)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("R,C,T", [(16, 128, 1), (40, 6144, 3), (6144, 2048, 1), (7, 256, 8)])
+def test_int32_block_accumulators_exact(orc, bits, R, C, T):
+    rng = np.random.default_rng(bits * 1000 + R + C + T)
+    # arbitrary bytes: every field value, including -8 (int4) and -2 (int2)
+    packed = rng.integers(0, 256, size=(R, C * bits // 8), dtype=np.uint8)
+    xq = rng.integers(-128, 128, size=(T, C)).astype(np.int8)
+    xd = np.ones((T, C // 32), F32)
+    acc_ref, _ = orc.qdot(bits, packed, np.ones(R, F32), C, xq, xd)
+    acc = torch.empty(T, R, C // 32, dtype=torch.int32, device="cuda")
+    B.coli_debug_qgemv_blocks(bits, to_dev(packed), C, to_dev(xq), acc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_container_identity_on_gpu(orc, bits):
+    """int4 (int2) codes in the int8 container and in the packed container
+    give identical int32 block sums through the GPU kernels."""
+    rng = np.random.default_rng(90 + bits)
+    R, C, T = 64, 6144, 2
+    w = rng.normal(0, 0.02, size=(R, C)).astype(F32)
+    codes, _ = orc.quant_rows(bits, w)
+    packed, cont8 = orc.pack(bits, codes), orc.pack(8, codes)
+    xq = rng.integers(-127, 128, size=(T, C)).astype(np.int8)
+    a_p = torch.empty(T, R, C // 32, dtype=torch.int32, device="cuda")
+    a_8 = torch.empty_like(a_p)
+    B.coli_debug_qgemv_blocks(bits, to_dev(packed), C, to_dev(xq), a_p)
+    B.coli_debug_qgemv_blocks(8, to_dev(cont8), C, to_dev(xq), a_8)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(a_p.cpu().numpy(), a_8.cpu().numpy())
+    acc_ref, _ = orc.qdot(bits, packed, np.ones(R, F32), C, xq, np.ones((T, C // 32), F32))
+    np.testing.assert_array_equal(a_p.cpu().numpy(), acc_ref)
+
+
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 37, 512])
+def test_logits_within_one_ulp(orc, T):
+    s = inputs.GLM
+    gw = inputs.gate_weight(s, 0)
+    x = inputs.tokens(s, 0, T, T)
+    ref = orc.logits(x.numpy(), gw.numpy())
+    out = torch.empty(T, s.n_experts, device="cuda")
+    B.coli_moe_logits(x.cuda(), gw.cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert ulp_diff(got, ref).max() <= 1
+    assert (got == ref).mean() > 0.99
+
+
+ROUTERS = {
+    "tiny": dict(E=16, k=2, G=1, TG=1, bias=0.0, top_p=0.0),
+    "grouped": dict(E=16, k=4, G=4, TG=2, bias=0.05, top_p=0.0),
+    "glm": dict(E=256, k=8, G=8, TG=4, bias=0.01, top_p=0.0),
+    "glm_top_p": dict(E=256, k=8, G=8, TG=4, bias=0.01, top_p=0.7),
+    "glm_top_p_norenorm": dict(E=256, k=8, G=8, TG=4, bias=0.01, top_p=0.7, renorm=0),
+    "glm_nonorm": dict(E=256, k=8, G=8, TG=4, bias=0.01, top_p=0.0, norm=0),
+    "wide": dict(E=1024, k=32, G=64, TG=8, bias=0.01, top_p=0.0),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTERS))
+@pytest.mark.parametrize("T,rho", [(1, 0.0), (3, 0.0), (512, 0.9)])
+def test_route_bit_exact(orc, name, T, rho):
+    r = ROUTERS[name]
+    norm, renorm = r.get("norm", 1), r.get("renorm", 1)
+    lg = inputs.correlated_logits(5, T, r["E"], rho).numpy()
+    rng = np.random.default_rng(T)
+    bias = (rng.normal(0, r["bias"], size=r["E"]) if r["bias"] else np.zeros(r["E"])).astype(F32)
+    if T > 1:
+        lg[1, :] = lg[0, :]  # duplicate token
+        lg[-1, : r["E"] // 2] = 0.0  # many exact ties
+    oc = oracle.make_cfg(r["E"], r["k"], r["G"], r["TG"], norm, 2.5, r["top_p"], renorm)
+    idx_ref, w_ref = orc.route(oc, lg, bias)
+    gc = B.router_cfg(r["E"], r["k"], r["G"], r["TG"], norm, 2.5, r["top_p"], renorm)
+    idx = torch.empty(T, r["k"], dtype=torch.int32, device="cuda")
+    w = torch.empty(T, r["k"], device="cuda")
+    B.coli_moe_route(gc, to_dev(lg), to_dev(bias), idx, w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_ref)
+    np.testing.assert_array_equal(w.cpu().numpy(), w_ref)
+
+
+@pytest.mark.parametrize("T,k,E,drop,dup", [(1, 8, 256, 0.0, False), (3, 8, 256, 0.0, False),
+                                            (512, 8, 256, 0.0, False), (77, 4, 16, 0.3, False),
+                                            (300, 8, 1024, 0.1, True), (2, 32, 64, 0.0, False)])
+def test_dispatch_tables_bit_exact(orc, T, k, E, drop, dup):
+    rng = np.random.default_rng(T * 31 + E)
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    if dup:
+        idx[::5, 1] = idx[::5, 0]  # a token naming an expert twice
+    if drop:
+        idx[rng.random(idx.shape) < drop] = -1
+    counts_r, offs_r, perm_r, uniq_r = orc.union_tables(idx, E)
+    dev = lambda n: torch.full((n,), -7, dtype=torch.int32, device="cuda")  # noqa: E731
+    counts, offs, perm, uniq, nu = dev(E), dev(E + 1), dev(T * k), dev(E), dev(1)
+    B.coli_moe_dispatch(to_dev(idx), E, counts, offs, perm, uniq, nu)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(counts.cpu().numpy(), counts_r)
+    np.testing.assert_array_equal(offs.cpu().numpy(), offs_r)
+    n = int(offs_r[-1])
+    np.testing.assert_array_equal(perm.cpu().numpy()[:n], perm_r)
+    assert int(nu.item()) == len(uniq_r)
+    np.testing.assert_array_equal(uniq.cpu().numpy()[: len(uniq_r)], uniq_r)
+
+
+# ------------------------------------------------------------------ layer --
+TINY_VARIANTS = {
+    "tiny_int8": inputs.TINY,                                              # the small layer, int8
+    "tiny_int4": inputs.TINY.with_(bits=4),
+    "tiny_int2": inputs.TINY.with_(bits=2),
+    "tiny_grouped": inputs.TINY.with_(n_group=4, topk_group=2, top_k=4, bias_std=0.05, bits=4),
+    "tiny_top_p": inputs.TINY.with_(n_group=4, topk_group=2, top_k=4, top_p=0.5, bits=4),
+    "tiny_rsf1": inputs.TINY.with_(rsf=1.0),
+}
+
+
+@pytest.fixture(scope="module")
+def tiny_pairs():
+    return {}
+
+
+def _pair(cache, name):
+    if name not in cache:
+        cache[name] = LayerPair(TINY_VARIANTS[name], seed=0)
+    return cache[name]
+
+
+@pytest.mark.parametrize("name", list(TINY_VARIANTS))
+@pytest.mark.parametrize("T", [1, 4, 5, 33])
+def test_layer_tiny(tiny_pairs, name, T):
+    p = _pair(tiny_pairs, name)
+    x = inputs.tokens(p.s, 0, 100 + T, T)
+    y_r, idx_r, w_r, lg_r = p.oracle_forward(x.numpy())
+    y, idx, w, lg = p.gpu_forward(x.cuda())
+    assert ulp_diff(lg, lg_r).max() <= 1
+    np.testing.assert_array_equal(idx, idx_r)
+    np.testing.assert_array_equal(w, w_r)
+    assert_close_layer(y, y_r)
+
+
+def test_layer_tiny_supplied_logits(tiny_pairs):
+    p = _pair(tiny_pairs, "tiny_grouped")
+    T = 9
+    x = inputs.tokens(p.s, 0, 7, T)
+    lg = inputs.correlated_logits(3, T, p.s.n_experts, 0.5).numpy()
+    y_r, idx_r, w_r, _ = p.oracle_forward(x.numpy(), lg)
+    y, idx, w, lg_out = p.gpu_forward(x.cuda(), to_dev(lg))
+    np.testing.assert_array_equal(lg_out, lg)
+    np.testing.assert_array_equal(idx, idx_r)
+    np.testing.assert_array_equal(w, w_r)
+    assert_close_layer(y, y_r)
+
+
+def test_layer_zero_input_and_zero_rsf(tiny_pairs):
+    p = _pair(tiny_pairs, "tiny_int8")
+    y, _, _, _ = p.gpu_forward(torch.zeros(3, p.s.hidden, device="cuda"))
+    assert (y == 0).all()
+    s0 = inputs.TINY.with_(rsf=0.0)
+    p0 = LayerPair(s0, seed=0)
+    x = inputs.tokens(s0, 0, 3, 5)
+    y, _, w, _ = p0.gpu_forward(x.cuda())
+    assert (w == 0).all()
+    # with zero weights the layer is the shared expert alone
+    y_sh = oracle.expert_ffn(s0.bits, s0.hidden, s0.inter, p0.orc_expert(s0.n_experts), x.numpy())
+    assert_close_layer(y, y_sh)
+
+
+def test_layer_empty_batch(tiny_pairs):
+    p = _pair(tiny_pairs, "tiny_int8")
+    y = torch.full((1, p.s.hidden), 5.0, device="cuda")
+    ws = B.workspace(p.gpu, 1)
+    B.coli_moe_forward(p.gpu, torch.empty(0, p.s.hidden, device="cuda"), y[:0], ws)
+    torch.cuda.synchronize()
+    assert (y == 5.0).all()
+
+
+def test_union_equals_per_token(tiny_pairs):
+    """A batch grouped by expert gives each token what it gets alone."""
+    p = _pair(tiny_pairs, "tiny_int4")
+    T = 12
+    x = inputs.tokens(p.s, 0, 55, T).cuda()
+    yb, idxb, wb, _ = p.gpu_forward(x)
+    for t in range(T):
+        y1, idx1, w1, _ = p.gpu_forward(x[t:t + 1].contiguous())
+        np.testing.assert_array_equal(idx1[0], idxb[t])
+        np.testing.assert_array_equal(w1[0], wb[t])
+        assert_close_layer(y1, yb[t:t + 1], tol=1e-5)
+
+
+def test_determinism(tiny_pairs):
+    p = _pair(tiny_pairs, "tiny_grouped")
+    x = inputs.tokens(p.s, 0, 9, 17).cuda()
+    a = p.gpu_forward(x)
+    b = p.gpu_forward(x)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+# ------------------------------------------------ GLM-5.2-shaped layer --
+@pytest.fixture(scope="module")
+def glm():
+    return LayerPair(inputs.GLM, seed=0, device_gen=True)
+
+
+@pytest.mark.slow
+def test_glm_decode(glm):
+    """Batch-1 decode of the full-size layer (computed logits), 4 tokens."""
+    errs = []
+    for step in range(4):
+        x = inputs.tokens(glm.s, 0, step, 1, "cuda")
+        y, idx, w, lg = glm.gpu_forward(x)
+        y_r, idx_r, w_r, lg_r = glm.oracle_forward(x.cpu().numpy())
+        assert ulp_diff(lg, lg_r).max() <= 1
+        np.testing.assert_array_equal(idx, idx_r)
+        np.testing.assert_array_equal(w, w_r)
+        errs.append(assert_close_layer(y, y_r))
+    print("glm decode max rel err", max(errs))
+
+
+@pytest.mark.slow
+def test_glm_mtp_verify_union(glm):
+    """The 3-token verify batch with supplied logits, every token checked."""
+    T = 3
+    x = inputs.tokens(glm.s, 0, 1000, T, "cuda")
+    lg = inputs.correlated_logits(11, T, glm.s.n_experts, 0.0)
+    y, idx, w, _ = glm.gpu_forward(x, lg.cuda())
+    y_r, idx_r, w_r, _ = glm.oracle_forward(x.cpu().numpy(), lg.numpy())
+    np.testing.assert_array_equal(idx, idx_r)
+    np.testing.assert_array_equal(w, w_r)
+    assert_close_layer(y, y_r)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("T", [8, 64])
+def test_glm_union_sampled(glm, T):
+    """Computed logits; a union batch of T tokens, 3 sampled tokens checked
+    against the oracle, the routing of all tokens checked."""
+    x = inputs.tokens(glm.s, 0, 2000 + T, T, "cuda")
+    y, idx, w, lg = glm.gpu_forward(x)
+    xh = x.cpu().numpy()
+    lg_r = oracle.logits(xh, glm.gate_w)
+    assert ulp_diff(lg, lg_r).max() <= 1
+    idx_r, w_r = oracle.route(orc_cfg(glm.s), lg_r, glm.gate_bias)
+    np.testing.assert_array_equal(idx, idx_r)
+    np.testing.assert_array_equal(w, w_r)
+    for t in (0, T // 2, T - 1):
+        y_r, _, _, _ = glm.oracle_forward(xh[t:t + 1])
+        assert_close_layer(y[t:t + 1], y_r)
