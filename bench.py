@@ -1,0 +1,351 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+Default workload: batch-1 decode through the GLM-5.2-shaped layer (H 6144,
+I 2048, 256 routed experts top-8 with 8 groups keeping 4, rsf 2.5, router
+bias N(0, 0.01), one shared expert; packed int4 weights with per-row fp32
+scales; Q8_0 activations; logits computed from the fp32 gate).  Eight
+independent layer instances (8 x 4.87 GB) are resident and step s uses
+instance s mod 8 with its own token, so no step re-reads another step's
+weights out of the 256 MB Infinity Cache.
+
+A "step" is one full layer forward on one token.  The K timed steps are
+captured into one HIP graph (launch overhead out of the way) and replayed
+once between two synchronisations.  The same K steps are then launched
+eagerly on the current stream through coli_moe_forward_profiled, whose
+front, gate/up and down kernel launches each record a start and a stop
+hipEvent (hipExtLaunchKernelGGL); those give each kernel's average
+execution time, including that of the dominant gate/up kernel used for the
+roofline figure.  Prints ONE JSON
+line on stdout; details go to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--workload decode|verify3|prefill512]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _hip():
+    """The HIP runtime torch loaded (shared with libcoli_moe.so)."""
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+    L = ctypes.CDLL(path or "libamdhip64.so.7")
+    L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    L.hipGetLastError.argtypes = []
+    return L
+
+
+WORKLOADS = {
+    # name: (tokens per step, logits supplied?, correlation of supplied logits)
+    "decode": (1, False, 0.0),
+    "verify3": (3, True, 0.0),
+    "prefill512": (512, True, 0.0),
+}
+
+
+def expert_bytes(s) -> dict:
+    """Algorithmic bytes of one expert (packed codes + fp32 row scales)."""
+    H, I, b = s.hidden, s.inter, s.bits
+    gate_up = 2 * (I * H * b // 8 + I * 4)
+    down = H * I * b // 8 + H * 4
+    return {"gate_up": gate_up, "down": down, "total": gate_up + down}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--instances", type=int, default=8)
+    ap.add_argument("--workload", choices=list(WORKLOADS), default="decode")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the oracle's timed CPU sample (0 disables it)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this "
+              "build runs the layer on a single MI355X; multi-GPU sharding is a design "
+              "note, not a measured path.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from quantized_moe_coli_amd import binding as B
+    from quantized_moe_coli_amd import inputs
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    s = inputs.GLM
+    T, supplied, rho = WORKLOADS[args.workload]
+    K, W, NI = args.steps, args.warmup, args.instances
+    cfg = B.router_cfg(s.n_experts, s.top_k, s.n_group, s.topk_group, 1, s.rsf, 0.0, 1)
+
+    t0 = time.time()
+    layers = []
+    for li in range(NI):
+        L = B.MoeLayer.empty(s.hidden, s.inter, s.bits, cfg, dev)
+        L.gate_w.copy_(inputs.gate_weight(s, li, dev))
+        L.gate_bias.copy_(inputs.gate_bias(s, li, dev))
+        for e in range(s.n_experts + 1):
+            g, u, d = inputs.expert_weights(s, li, e, dev)
+            L.pack_expert(e, g, u, d)
+            del g, u, d
+        layers.append(L)
+        torch.cuda.synchronize()
+    log(f"[bench] {NI} layer instances packed in {time.time() - t0:.1f}s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB resident)")
+
+    n_x = max(K, W)
+    xs = torch.stack([inputs.tokens(s, 1, st, T, dev) for st in range(n_x)])  # [n_x, T, H]
+    lgs = None
+    if supplied:
+        lgs = torch.stack([inputs.correlated_logits(1000 + st, T, s.n_experts, rho, device=dev)
+                           for st in range(n_x)])
+    ys = torch.empty(n_x, T, s.hidden, device=dev)
+    ws = B.workspace(layers[0], T)
+    cls = [L.c_struct() for L in layers]
+
+    def step(st, stream_events=None):
+        li = st % NI
+        lin = lgs[st] if lgs is not None else None
+        if stream_events is None:
+            B.coli_moe_forward(layers[li], xs[st], ys[st], ws, logits_in=lin, c_layer=cls[li])
+        else:
+            B.coli_moe_forward_profiled(layers[li], xs[st], ys[st], ws, stream_events,
+                                        logits_in=lin, c_layer=cls[li])
+
+    # warm-up (eager, untimed)
+    for st in range(W):
+        step(st)
+    torch.cuda.synchronize()
+
+    # headline: the K timed steps captured into one HIP graph, replayed once
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for st in range(K):
+                step(st)
+    torch.cuda.synchronize()
+    g.replay()  # one untimed replay of the captured steps
+    torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    del g
+
+    # kernel durations: the same K steps launched eagerly on the current
+    # stream; each launch of the front, gate/up and down kernels records a
+    # start and a stop hipEvent itself (hipExtLaunchKernelGGL)
+    hip = _hip()
+    n_ev = 6
+    evs = []
+    for _ in range(K * n_ev):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        evs.append(e.value)
+    torch.cuda.synchronize()
+    e0 = time.perf_counter()
+    for st in range(K):
+        step(st, evs[st * n_ev:(st + 1) * n_ev])
+    torch.cuda.synchronize()
+    eager_wall = time.perf_counter() - e0
+
+    def el(a, b):
+        v = ctypes.c_float()
+        rc = hip.hipEventElapsedTime(ctypes.byref(v), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            hip.hipGetLastError()
+            return float("nan")
+        return v.value
+
+    stage = np.array([[el(evs[st * n_ev + 2 * i], evs[st * n_ev + 2 * i + 1]) for i in range(3)]
+                      for st in range(K)])  # ms: front, gate/up, down kernels
+    span = np.array([el(evs[st * n_ev], evs[st * n_ev + 5]) for st in range(K)])
+    eager_ms = el(evs[0], evs[K * n_ev - 1])
+    for e in evs:
+        hip.hipEventDestroy(ctypes.c_void_p(e))
+    hip.hipGetLastError()
+
+    ms_per_step = total_ms / K
+    tokens_per_s = T * K / (total_ms / 1e3)
+    eb = expert_bytes(s)
+    gate_bytes = 0 if supplied else s.n_experts * s.hidden * 4
+
+    # algorithmic bytes: the unique experts each step reads (+ the shared one)
+    if T == 1:
+        uniq = np.full(K, s.top_k, dtype=np.float64)
+    else:
+        uniq = []
+        for st in range(K):
+            idx = torch.empty(T, s.top_k, dtype=torch.int32, device=dev)
+            B.coli_moe_route(cfg, lgs[st], layers[st % NI].gate_bias, idx,
+                             torch.empty(T, s.top_k, device=dev))
+            uniq.append(len(torch.unique(idx[idx >= 0])))
+        uniq = np.array(uniq, dtype=np.float64)
+    act_bytes = T * s.hidden * 4 * 2  # x in, y out
+    layer_bytes = (uniq + 1) * eb["total"] + gate_bytes + act_bytes
+    gu_bytes = (uniq + 1) * eb["gate_up"]
+    down_bytes = (uniq + 1) * eb["down"]
+    avg = stage.mean(axis=0)
+    gu_ms = float(np.mean(stage[:, 1]))
+    gu_gbps = float(np.mean(gu_bytes)) / (gu_ms * 1e-3) / 1e9
+    layer_gbps = float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] {args.workload}: {K} steps in {total_ms:.3f} ms (wall {wall * 1e3:.1f} ms): "
+        f"{ms_per_step * 1e3:.2f} us/step, {tokens_per_s:.0f} tokens/s")
+    log(f"[bench] eager pass with kernel events: {eager_ms / K * 1e3:.2f} us/step (host wall "
+        f"{eager_wall / K * 1e6:.2f} us/step), first-kernel start to last-kernel end "
+        f"{np.mean(span) * 1e3:.2f} us")
+    log(f"[bench] kernel means (us): front (act quant + logits) {avg[0] * 1e3:.2f}, gate/up "
+        f"{avg[1] * 1e3:.2f}, down {avg[2] * 1e3:.2f}")
+    log(f"[bench] unique experts/step {uniq.mean():.1f}; layer bytes/step "
+        f"{np.mean(layer_bytes) / 1e6:.2f} MB -> {layer_gbps:.0f} GB/s "
+        f"({100 * layer_gbps / HBM_PEAK_GBPS:.1f}% of HBM peak); gate/up "
+        f"{gu_gbps:.0f} GB/s; down {float(np.mean(down_bytes)) / (avg[2] * 1e-3) / 1e9:.0f} GB/s")
+
+    result = {
+        "metric": "MoE-layer tokens/s (int4 top-8/256 decode)" if T == 1 else
+                  f"MoE-layer tokens/s ({args.workload})",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4xint8->int32,fp32-scale",
+        "data": "synthetic",
+        "config": {
+            "workload": ("GLM-5.2 routed-MoE layer" + (" batch-1 decode" if T == 1 else
+                         f" {T}-token union batch") + ": H 6144, I 2048, 256 experts top-8 "
+                         "(8 groups keep 4, rsf 2.5) + 1 shared, packed int4 per-row fp32 "
+                         "scale, Q8_0 activations" + (", logits from the fp32 gate" if not supplied
+                                                       else ", logits supplied")),
+            "tokens_per_step": T,
+            "layer_instances": NI,
+            "launch": "one HIP graph of the K timed steps",
+            "kernel_us": {"front": round(float(avg[0]) * 1e3, 3),
+                          "gate_up": round(float(avg[1]) * 1e3, 3),
+                          "down": round(float(avg[2]) * 1e3, 3)},
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_gateup (gate/up GEMV + SwiGLU + Q8_0 of h)",
+            "achieved": round(gu_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(gu_ms * 1e3, 3),
+            "bytes_per_launch": int(np.mean(gu_bytes)),
+        },
+        "layer_roofline": {
+            "bound": "hbm",
+            "achieved": round(layer_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(layer_gbps / HBM_PEAK_GBPS, 4),
+            "bytes_per_step": int(np.mean(layer_bytes)),
+        },
+    }
+
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(s, layers[0], xs, lgs, ys, NI, args.cpu_seconds, T)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(s, layer0, xs, lgs, ys, NI, budget_s, T):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    steps that use layer instance 0, timed one forward call at a time until
+    the budget is spent.  The oracle packs the experts it needs from the same
+    fp32 draws with its own code (untimed)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from quantized_moe_coli_amd import inputs
+
+    li = 0
+    ocfg = oracle.make_cfg(s.n_experts, s.top_k, s.n_group, s.topk_group, 1, s.rsf, 0.0, 1)
+    gate_w = inputs.gate_weight(s, li, "cuda").cpu().numpy()
+    bias = inputs.gate_bias(s, li, "cuda").cpu().numpy()
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            g, u, d = (t.cpu().numpy() for t in inputs.expert_weights(s, li, e, "cuda"))
+            cache[e] = oracle.Expert.from_float(s.bits, g, u, d)
+        return cache[e]
+
+    done, spent, max_err = 0, 0.0, 0.0
+    steps = list(range(0, xs.shape[0], NI))
+    for st in steps:
+        x = xs[st].cpu().numpy()
+        lin = lgs[st].cpu().numpy() if lgs is not None else None
+        lg = oracle.logits(x, gate_w) if lin is None else lin
+        idx, _ = oracle.route(ocfg, lg, bias)
+        exps = [None] * s.n_experts
+        for e in set(idx.ravel().tolist()):
+            if e >= 0:
+                exps[e] = expert(e)
+        L = oracle.Layer(s.hidden, s.inter, s.bits, ocfg, exps, expert(s.n_experts), gate_w, bias)
+        t0 = time.perf_counter()
+        y_r, _, _, _ = oracle.moe_forward(L, x, lin)
+        spent += time.perf_counter() - t0
+        done += 1
+        y = ys[st].cpu().numpy().astype(np.float64)
+        err = np.abs(y - y_r).max(axis=1) / np.maximum(np.abs(y_r).max(axis=1), 1e-30)
+        max_err = max(max_err, float(err.max()))
+        if spent >= budget_s:
+            break
+    log(f"[bench] oracle: {done} steps x {T} tokens in {spent:.2f}s on {oracle.num_threads()} "
+        f"threads; GPU outputs of those steps within {max_err:.2e} (rel. to max |y|) of it")
+    return {
+        "value": round(done * T / spent, 4),
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{done} timed forward calls of {T} token(s) on layer instance 0 "
+                  f"(steps 0, {NI}, {2 * NI}, ...), {spent:.1f} s of CPU time; GPU outputs "
+                  f"of the same steps agree to {max_err:.1e}",
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

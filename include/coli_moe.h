@@ -80,8 +80,7 @@ typedef struct {
  * w_down [E][H][I*b/8], s_down [E][H].  The shared expert has the same
  * per-expert layouts (E = 1).  Every weight row must start 16-byte aligned
  * (holds for any 16-byte aligned base since H*b/8 and I*b/8 are multiples of
- * 16).  H and I are multiples of 64 (int2: of 128 so a row is whole 16-byte
- * chunks), at most 16384.  mfma_min_tokens: a unique expert receiving at least
+ * 16).  H and I are multiples of 64, at most 8192.  mfma_min_tokens: a unique expert receiving at least
  * this many tokens of a batch runs on the int8 matrix cores, fewer on the
  * integer dot-product GEMV; 0 selects the library default. */
 typedef struct {
@@ -183,10 +182,26 @@ coli_status coli_moe_forward(const coli_moe_layer *L, const float *x,
                              void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* Profiling variant of coli_moe_forward (same work, same results) for the
+ * benchmark.  stage_events holds n_stage_events caller-created hipEvent_t
+ * handles (NULL entries skipped): [2i] and [2i+1] are recorded by the launch
+ * of kernel i itself at its start and end (so their interval is that
+ * kernel's execution time), for i = 0 the front kernel (activation
+ * quantisation + router logits), 1 the gate/up kernel (for T = 1 including
+ * the expert selection), 2 the down-projection kernel.  Works inside a
+ * stream capture only if the runtime supports these event launches there. */
+coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x,
+                                      int32_t T, const float *logits_in,
+                                      float *y, int32_t *idx_out, float *w_out,
+                                      float *logits_out, void *workspace,
+                                      size_t workspace_bytes, void *stream,
+                                      void *const *stage_events,
+                                      int32_t n_stage_events);
+
 /* Test export of the integer products, same device code as the forward:
  * acc_out [T][rows][cols/32] int32 = per-block sums of weight codes times
  * Q8_0 codes, exact.  Wq [rows][cols*qtype/8], xq [T][cols] int8 (natural
- * order).  cols a multiple of 64 (int2: 128), T <= 8. */
+ * order).  cols a positive multiple of 64, T <= 8. */
 coli_status coli_debug_qgemv_blocks(int32_t qtype, const uint8_t *Wq,
                                     int32_t rows, int32_t cols,
                                     const int8_t *xq, int32_t T,

@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
             "coli_moe_workspace_bytes": ([ctypes.POINTER(MoeLayerC), i32], sz),
             "coli_moe_forward": ([ctypes.POINTER(MoeLayerC), _P, i32, _P, _P, _P, _P, _P, _P, sz,
                                   _P], ctypes.c_int),
+            "coli_moe_forward_profiled": ([ctypes.POINTER(MoeLayerC), _P, i32, _P, _P, _P, _P, _P,
+                                           _P, sz, _P, ctypes.POINTER(_P), i32], ctypes.c_int),
             "coli_debug_qgemv_blocks": ([i32, _P, i32, i32, _P, i32, _P, _P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
@@ -260,6 +262,21 @@ def coli_moe_forward(layer: MoeLayer, x: torch.Tensor, y: torch.Tensor, ws: torc
         _ptr(idx_out, torch.int32, "idx_out"), _ptr(w_out, torch.float32, "w_out"),
         _ptr(logits_out, torch.float32, "logits_out"), ctypes.c_void_p(ws.data_ptr()),
         ws.numel(), _stream(stream)))
+
+
+def coli_moe_forward_profiled(layer: MoeLayer, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor,
+                              events, logits_in=None, stream=None,
+                              c_layer: MoeLayerC | None = None) -> None:
+    """coli_moe_forward recording the hipEvent_t handles ``events`` (ints)
+    at its stage boundaries."""
+    T = x.shape[0]
+    c = c_layer if c_layer is not None else layer.c_struct()
+    ev = (_P * len(events))(*events)
+    _check("coli_moe_forward_profiled", lib().coli_moe_forward_profiled(
+        ctypes.byref(c), _ptr(x, torch.float32, "x"), T,
+        _ptr(logits_in, torch.float32, "logits_in"), _ptr(y, torch.float32, "y"),
+        None, None, None, ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream),
+        ev, len(events)))
 
 
 def coli_debug_qgemv_blocks(qtype: int, Wq: torch.Tensor, cols: int, xq: torch.Tensor,

@@ -1,0 +1,41 @@
+// actq.hpp -- Q8_0-style quantisation of one block of 32 activations
+// (colibrì README, "Implemented features": integer dot products against
+// Q8_0-style int8 activations).  d = amax/127 (IEEE binary32 division);
+// q = clamp(round_half_even(x/d), -127, 127); d = 0 gives q = 0.  The 32 codes
+// are stored in the ordering the weight container BITS consumes (perm_src).
+#pragma once
+
+#include "device.hpp"
+
+namespace coli {
+
+template <int BITS>
+__device__ __forceinline__ void act_quant_block(const float *__restrict__ xb, int8_t *__restrict__ qb,
+                                                float *__restrict__ db) {
+  const float4 *x4 = reinterpret_cast<const float4 *>(xb);
+  float v[32];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const float4 f = x4[m];
+    v[4 * m] = f.x; v[4 * m + 1] = f.y; v[4 * m + 2] = f.z; v[4 * m + 3] = f.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int m = 0; m < 32; ++m) amax = fmaxf(amax, fabsf(v[m]));
+  const float d = amax / 127.f;
+  *db = d;
+  uint32_t words[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) words[m] = 0;
+#pragma unroll
+  for (int s = 0; s < 32; ++s) {
+    float c = 0.f;
+    if (d != 0.f) c = fminf(fmaxf(rintf(v[perm_src<BITS>(s)] / d), -127.f), 127.f);
+    words[s >> 2] |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * (s & 3));
+  }
+  uint4 *out = reinterpret_cast<uint4 *>(qb);
+  out[0] = make_uint4(words[0], words[1], words[2], words[3]);
+  out[1] = make_uint4(words[4], words[5], words[6], words[7]);
+}
+
+}  // namespace coli

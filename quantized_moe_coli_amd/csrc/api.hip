@@ -204,7 +204,17 @@ coli_status coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
                              const float *logits_in, float *y, int32_t *idx_out, float *w_out,
                              float *logits_out, void *workspace, size_t workspace_bytes,
                              void *stream) {
+  return coli_moe_forward_profiled(L, x, T, logits_in, y, idx_out, w_out, logits_out, workspace,
+                                   workspace_bytes, stream, nullptr, 0);
+}
+
+coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int32_t T,
+                                      const float *logits_in, float *y, int32_t *idx_out,
+                                      float *w_out, float *logits_out, void *workspace,
+                                      size_t workspace_bytes, void *stream,
+                                      void *const *stage_events, int32_t n_stage_events) {
   return guarded([&] {
+    if (n_stage_events < 0 || (n_stage_events > 0 && !stage_events)) return COLI_ERR_INVALID_ARG;
     if (!layer_ok(L) || T < 0 || T > kMaxTokens) return COLI_ERR_INVALID_ARG;
     if (T == 0) return COLI_OK;
     if (!x || !y) return COLI_ERR_INVALID_ARG;
@@ -228,24 +238,26 @@ coli_status coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
     int32_t *idx = reinterpret_cast<int32_t *>(base + ws.idx);
     float *wts = reinterpret_cast<float *>(base + ws.w);
 
-    hipError_t e = coli::launch_act_quant(L->qtype, x, T, H, xq, xd, s);
+    // kernel i in (front, gate/up, down) gets events [2i] and [2i+1]
+    auto kev = [&](int i) {
+      coli::KEvents ev;
+      if (2 * i < n_stage_events) ev.start = static_cast<hipEvent_t>(stage_events[2 * i]);
+      if (2 * i + 1 < n_stage_events) ev.stop = static_cast<hipEvent_t>(stage_events[2 * i + 1]);
+      return ev;
+    };
+    hipError_t e = hipSuccess;
+    // activations -> Q8_0 codes, and the router logits unless supplied
+    float *lp_dst = logits_out ? logits_out : reinterpret_cast<float *>(base + ws.logits);
+    if (e == hipSuccess)
+      e = coli::launch_front(L->qtype, x, logits_in ? nullptr : L->gate_w, T, E, H, lp_dst, xq, xd,
+                             s, kev(0));
     if (e != hipSuccess) return COLI_ERR_DEVICE;
-
-    const float *lp = logits_in;
-    if (logits_in) {
-      if (logits_out) {
-        e = hipMemcpyAsync(logits_out, logits_in, (size_t)T * E * sizeof(float),
-                           hipMemcpyDeviceToDevice, s);
-        if (e != hipSuccess) return COLI_ERR_DEVICE;
-      }
-    } else {
-      float *dst = logits_out ? logits_out : reinterpret_cast<float *>(base + ws.logits);
-      e = coli::launch_logits(x, L->gate_w, T, E, H, dst, s);
+    const float *lp = logits_in ? logits_in : lp_dst;
+    if (logits_in && logits_out) {
+      e = hipMemcpyAsync(logits_out, logits_in, (size_t)T * E * sizeof(float),
+                         hipMemcpyDeviceToDevice, s);
       if (e != hipSuccess) return COLI_ERR_DEVICE;
-      lp = dst;
     }
-    e = coli::launch_route(to_cfg(L->router), lp, L->gate_bias, T, idx, wts, idx_out, w_out, s);
-    if (e != hipSuccess) return COLI_ERR_DEVICE;
 
     coli::FfnArgs fa{};
     fa.L = coli::LayerPtrs{H, I, L->qtype, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up,
@@ -258,16 +270,24 @@ coli_status coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
     fa.xd = xd;
     fa.idx = idx;
     fa.w = wts;
+    fa.cfg = to_cfg(L->router);
+    fa.logits = lp;
+    fa.bias = L->gate_bias;
+    fa.idx_user = idx_out;
+    fa.w_user = w_out;
     fa.hq = reinterpret_cast<int8_t *>(base + ws.hq);
     fa.hd = reinterpret_cast<float *>(base + ws.hd);
     fa.obuf = reinterpret_cast<float *>(base + ws.obuf);
     fa.y = y;
     const int mfma_min = L->mfma_min_tokens;
     if (T == 1) {
-      e = coli::launch_gateup(fa, false, mfma_min, s);
-      if (e == hipSuccess) e = coli::launch_down(fa, false, mfma_min, s);
+      // decode: the gate/up kernel selects the token's experts itself
+      e = coli::launch_gateup(fa, false, mfma_min, s, kev(1));
+      if (e == hipSuccess) e = coli::launch_down(fa, false, mfma_min, s, kev(2));
       return from_hip(e);
     }
+    e = coli::launch_route(to_cfg(L->router), lp, L->gate_bias, T, idx, wts, idx_out, w_out, s);
+    if (e != hipSuccess) return COLI_ERR_DEVICE;
     int32_t *counts = reinterpret_cast<int32_t *>(base + ws.counts);
     int32_t *offs = reinterpret_cast<int32_t *>(base + ws.offs);
     int32_t *perm = reinterpret_cast<int32_t *>(base + ws.perm);
@@ -276,8 +296,8 @@ coli_status coli_moe_forward(const coli_moe_layer *L, const float *x, int32_t T,
     e = coli::launch_dispatch(idx, T, k, E, counts, offs, perm, uniq, nuniq, s);
     if (e != hipSuccess) return COLI_ERR_DEVICE;
     fa.disp = coli::Dispatch{counts, offs, perm, uniq, nuniq};
-    e = coli::launch_gateup(fa, true, mfma_min, s);
-    if (e == hipSuccess) e = coli::launch_down(fa, true, mfma_min, s);
+    e = coli::launch_gateup(fa, true, mfma_min, s, kev(1));
+    if (e == hipSuccess) e = coli::launch_down(fa, true, mfma_min, s, kev(2));
     if (e == hipSuccess) e = coli::launch_combine(fa, s);
     return from_hip(e);
   });

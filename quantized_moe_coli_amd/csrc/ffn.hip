@@ -25,6 +25,7 @@
 // buffer that a combine kernel reduces in the same fixed order.  No
 // floating-point atomics: results are bit-reproducible.
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace coli {
 
@@ -74,62 +75,53 @@ __device__ __forceinline__ float chunk_part(const uint4 w, const Act<BITS> &ac) 
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.f + expf(-g)); }
 
-// Resolve an item's expert: returns false if the slot has no work.
-struct SlotInfo {
+__device__ __forceinline__ float bcast(float v, int lane_idx) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane_idx));
+}
+
+// Row scale of row (p * RPP + rsub) of a wave whose lane i holds the scale of
+// its i-th row (p is a compile-time pass index after unrolling).
+template <int RPP>
+__device__ __forceinline__ float row_scale(float sv, int p, int rsub) {
+  if constexpr (RPP == 1) return bcast(sv, p);
+  else return rsub ? bcast(sv, RPP * p + 1) : bcast(sv, RPP * p);
+}
+
+// Pointers of one expert (e = -1: the shared expert).
+struct ExpertPtrs {
   const uint8_t *wg, *wu, *wd;
   const float *sg, *su, *sd;
-  int n_tok;    // tokens of this slot
-  int p0;       // union: first perm position (routed) / -1 shared
-  int slot;     // decode: slot index
+};
+
+__device__ __forceinline__ ExpertPtrs expert_ptrs(const LayerPtrs &L, int e) {
+  ExpertPtrs p;
+  if (e < 0) {
+    p.wg = L.sh_gate; p.wu = L.sh_up; p.wd = L.sh_down;
+    p.sg = L.sh_s_gate; p.su = L.sh_s_up; p.sd = L.sh_s_down;
+  } else {
+    const size_t gu_stride = (size_t)L.I * (L.H * L.bits / 8);
+    const size_t d_stride = (size_t)L.H * (L.I * L.bits / 8);
+    p.wg = L.w_gate + (size_t)e * gu_stride;
+    p.wu = L.w_up + (size_t)e * gu_stride;
+    p.wd = L.w_down + (size_t)e * d_stride;
+    p.sg = L.s_gate + (size_t)e * L.I;
+    p.su = L.s_up + (size_t)e * L.I;
+    p.sd = L.s_down + (size_t)e * L.H;
+  }
+  return p;
+}
+
+// The tokens of one work item: decode -> token 0 at h row `slot`; union ->
+// the expert's perm range (routed) or every token (shared).
+struct TokList {
+  int n_tok;
+  int p0;      // union routed: first perm position; -1 otherwise
+  int slot;    // decode: slot index
   bool shared;
 };
 
-__device__ __forceinline__ bool resolve_slot(const FfnArgs &a, bool union_mode, int u,
-                                             SlotInfo &s) {
-  const LayerPtrs &L = a.L;
-  const size_t gu_stride = (size_t)L.I * (L.H * L.bits / 8);
-  const size_t d_stride = (size_t)L.H * (L.I * L.bits / 8);
-  int e;
-  if (!union_mode) {
-    if (u > a.k) return false;
-    s.slot = u;
-    s.shared = (u == a.k);
-    s.n_tok = 1;
-    s.p0 = 0;
-    e = s.shared ? -1 : a.idx[u];
-    if (!s.shared && e < 0) return false;
-  } else {
-    const int nu = *a.disp.n_uniq;
-    if (u > nu) return false;
-    s.slot = -1;
-    s.shared = (u == nu);
-    if (s.shared) {
-      e = -1;
-      s.n_tok = a.T;
-      s.p0 = -1;
-    } else {
-      e = a.disp.uniq[u];
-      s.p0 = a.disp.offs[e];
-      s.n_tok = a.disp.offs[e + 1] - s.p0;
-    }
-  }
-  if (s.shared) {
-    s.wg = L.sh_gate; s.wu = L.sh_up; s.wd = L.sh_down;
-    s.sg = L.sh_s_gate; s.su = L.sh_s_up; s.sd = L.sh_s_down;
-  } else {
-    s.wg = L.w_gate + (size_t)e * gu_stride;
-    s.wu = L.w_up + (size_t)e * gu_stride;
-    s.wd = L.w_down + (size_t)e * d_stride;
-    s.sg = L.s_gate + (size_t)e * L.I;
-    s.su = L.s_up + (size_t)e * L.I;
-    s.sd = L.s_down + (size_t)e * L.H;
-  }
-  return true;
-}
-
-// Token n (0-based) of a slot -> (token t, activation/h row, slot j).
-__device__ __forceinline__ void slot_token(const FfnArgs &a, bool union_mode, const SlotInfo &s,
-                                           int n, int &t, int &hrow, int &j) {
+__device__ __forceinline__ void tok_at(const FfnArgs &a, bool union_mode, const TokList &s, int n,
+                                       int &t, int &hrow, int &j) {
   if (!union_mode) {
     t = 0;
     hrow = s.slot;
@@ -146,20 +138,35 @@ __device__ __forceinline__ void slot_token(const FfnArgs &a, bool union_mode, co
   }
 }
 
+// Union item u -> expert and token list; false past the last unique expert.
+__device__ __forceinline__ bool union_item(const FfnArgs &a, int u, int &e, TokList &s) {
+  const int nu = *a.disp.n_uniq;
+  if (u > nu) return false;
+  s.slot = -1;
+  s.shared = (u == nu);
+  if (s.shared) {
+    e = -1;
+    s.n_tok = a.T;
+    s.p0 = -1;
+  } else {
+    e = a.disp.uniq[u];
+    s.p0 = a.disp.offs[e];
+    s.n_tok = a.disp.offs[e + 1] - s.p0;
+  }
+  return true;
+}
+
 // ---------------------------------------------------------------------------
-// Gate/up + SwiGLU + Q8_0(h).  grid.x = slots * (I/32); block = 256.
+// Gate/up + SwiGLU + Q8_0(h) for 32 rows (row block rb) of one expert over
+// its tokens.  Each wave owns 8 rows; the loads of the next row pass are in
+// flight while the current one is reduced.
 // ---------------------------------------------------------------------------
 template <int BITS, int LPR, int CPL, int NT>
-__global__ __launch_bounds__(256) void k_gateup(FfnArgs a, int union_mode) {
+__device__ __forceinline__ void gateup_body(const FfnArgs &a, bool union_mode, const ExpertPtrs &ep,
+                                            const TokList &s, int rb, float (*hs)[32]) {
   constexpr int RPP = 64 / LPR;  // rows per pass of a wave
   constexpr int ROWS_PER_WAVE = 8;
   constexpr int PASSES = ROWS_PER_WAVE / RPP;
-  __shared__ float hs[NT][32];
-  const int n_rb = a.L.I / 32;
-  const int u = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
-  SlotInfo s;
-  if (!resolve_slot(a, union_mode != 0, u, s)) return;
-
   const int H = a.L.H, I = a.L.I;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gl = lane % LPR;           // lane in its row group
@@ -168,13 +175,16 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs a, int union_mode) {
   const size_t row_bytes = (size_t)H * BITS / 8;
   const int xblocks = H / 32;
 
+  // lane i < 8 holds the gate/up scales of the wave's i-th row
+  const int srow = rb * 32 + wave * ROWS_PER_WAVE + min(lane, ROWS_PER_WAVE - 1);
+  const float sgv = ep.sg[srow], suv = ep.su[srow];
   for (int t0 = 0; t0 < s.n_tok; t0 += NT) {
     Act<BITS> act[CPL][NT];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       int t = 0, hrow = 0, j = 0;
       const bool tv = t0 + tt < s.n_tok;
-      if (tv) slot_token(a, union_mode != 0, s, t0 + tt, t, hrow, j);
+      if (tv) tok_at(a, union_mode, s, t0 + tt, t, hrow, j);
       const int8_t *xq = a.xq + (size_t)t * H;
       const float *xd = a.xd + (size_t)t * xblocks;
 #pragma unroll
@@ -184,24 +194,26 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs a, int union_mode) {
         else zero_act<BITS>(act[i][tt]);
       }
     }
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int rl = wave * ROWS_PER_WAVE + p * RPP + rsub;  // row within the 32-row block
-      const int row = rb * 32 + rl;
-      const uint4 *gp = reinterpret_cast<const uint4 *>(s.wg + (size_t)row * row_bytes);
-      const uint4 *up = reinterpret_cast<const uint4 *>(s.wu + (size_t)row * row_bytes);
-      uint4 wg[CPL], wu[CPL];
+    uint4 wg[2][CPL], wu[2][CPL];
+    // chunks past the row end reload the last chunk; their activations are
+    // zero, so they add exactly 0 -- no branch around the loads
+    auto load_rows = [&](int p, int buf) {
+      const int row = rb * 32 + wave * ROWS_PER_WAVE + p * RPP + rsub;
+      const uint4 *gp = reinterpret_cast<const uint4 *>(ep.wg + (size_t)row * row_bytes);
+      const uint4 *up = reinterpret_cast<const uint4 *>(ep.wu + (size_t)row * row_bytes);
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
-        const int c = gl + LPR * i;
-        if (c < nchunks) {
-          wg[i] = ld_nt(gp + c);
-          wu[i] = ld_nt(up + c);
-        } else {
-          wg[i] = make_uint4(0, 0, 0, 0);
-          wu[i] = make_uint4(0, 0, 0, 0);
-        }
+        const int c = min(gl + LPR * i, nchunks - 1);
+        wg[buf][i] = ld_nt(gp + c);
+        wu[buf][i] = ld_nt(up + c);
       }
+    };
+    load_rows(0, 0);
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      if (p + 1 < PASSES) load_rows(p + 1, (p + 1) & 1);
+      const int buf = p & 1;
+      const int rl = wave * ROWS_PER_WAVE + p * RPP + rsub;  // row within the 32-row block
       float pg[NT], pu[NT];
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
@@ -209,19 +221,16 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs a, int union_mode) {
         pu[tt] = 0.f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-          pg[tt] += chunk_part<BITS>(wg[i], act[i][tt]);
-          pu[tt] += chunk_part<BITS>(wu[i], act[i][tt]);
+          pg[tt] += chunk_part<BITS>(wg[buf][i], act[i][tt]);
+          pu[tt] += chunk_part<BITS>(wu[buf][i], act[i][tt]);
         }
         pg[tt] = group_sum<LPR>(pg[tt]);
         pu[tt] = group_sum<LPR>(pu[tt]);
       }
+      const float sg = row_scale<RPP>(sgv, p, rsub), su = row_scale<RPP>(suv, p, rsub);
       if (lane == group_sum_lane<LPR>(lane)) {
-        const float sg = s.sg[row], su = s.su[row];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          const float g = pg[tt] * sg, uu = pu[tt] * su;
-          hs[tt][rl] = silu_f32(g) * uu;
-        }
+        for (int tt = 0; tt < NT; ++tt) hs[tt][rl] = silu_f32(pg[tt] * sg) * (pu[tt] * su);
       }
     }
     __syncthreads();
@@ -234,7 +243,7 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs a, int union_mode) {
         amax = __shfl(amax, (lane & 32) | 31, 64);
         if (t0 + tt < s.n_tok) {
           int t, hrow, j;
-          slot_token(a, union_mode != 0, s, t0 + tt, t, hrow, j);
+          tok_at(a, union_mode, s, t0 + tt, t, hrow, j);
           const float db = amax / 127.f;
           float c = 0.f;
           if (db != 0.f) c = fminf(fmaxf(rintf(h / db), -127.f), 127.f);
@@ -247,34 +256,93 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs a, int union_mode) {
   }
 }
 
+// Decode (T == 1): grid.x = (k+1) * (I/32).  Slot u < k is the u-th routed
+// expert of the token, which every routed workgroup selects itself from the
+// logits (one wave, select.hpp) -- no separate routing launch; workgroup
+// (0, 0) also stores the routing for the down kernel and the caller.  Slot k
+// is the shared expert, which needs no routing and starts at once.
+template <int BITS, int LPR, int CPL>
+__global__ __launch_bounds__(256) void k_gateup_decode(FfnArgs a) {
+  __shared__ float hs[1][32];
+  __shared__ SelScratch sc;
+  __shared__ int32_t sidx[kSelMaxK];
+  __shared__ float sw[kSelMaxK];
+  const int n_rb = a.L.I / 32;
+  const int u = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
+  int e = -1;
+  if (u < a.k) {
+    if (threadIdx.x < 64) select_token(a.cfg, a.logits, a.bias, sc, sidx, sw);
+    __syncthreads();
+    if (u == 0 && rb == 0 && (int)threadIdx.x < a.k) {
+      const int j = threadIdx.x;
+      a.idx[j] = sidx[j];
+      a.w[j] = sw[j];
+      if (a.idx_user) a.idx_user[j] = sidx[j];
+      if (a.w_user) a.w_user[j] = sw[j];
+    }
+    e = sidx[u];
+    if (e < 0) return;  // dropped by expert top-p
+  }
+  TokList s;
+  s.n_tok = 1;
+  s.p0 = -1;
+  s.slot = u;
+  s.shared = (u == a.k);
+  gateup_body<BITS, LPR, CPL, 1>(a, false, expert_ptrs(a.L, e), s, rb, hs);
+}
+
+// Union (T >= 2): grid.x = (max unique experts + 1) * (I/32).
+template <int BITS, int LPR, int CPL, int NT>
+__global__ __launch_bounds__(256) void k_gateup_union(FfnArgs a) {
+  __shared__ float hs[NT][32];
+  const int n_rb = a.L.I / 32;
+  const int u = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
+  int e;
+  TokList s;
+  if (!union_item(a, u, e, s)) return;
+  gateup_body<BITS, LPR, CPL, NT>(a, true, expert_ptrs(a.L, e), s, rb, hs);
+}
+
 // ---------------------------------------------------------------------------
-// Down, decode mode (T == 1).  grid.x = H / ROWS; block = 256 (4 waves).
-// Wave w handles slots w, w+4, ... of [routed 0..k-1, shared k]; each writes
-// w_j * o_j (o for the shared slot) per row into LDS; then the rows are
-// summed in the order shared, 0, 1, ..., k-1.
+// Down, decode mode (T == 1).  grid.x = H / ROWS; block = 64 * NW waves with
+// NW = min(k+1, 12).  Wave w handles slots w, w+NW, ... of [routed 0..k-1,
+// shared k]: ROWS rows of w_j * o_j (o for the shared slot) into LDS, all
+// ROWS row loads in flight at once; then the rows are summed in the order
+// shared, 0, 1, ..., k-1.
 // ---------------------------------------------------------------------------
-template <int BITS, int LPR, int CPL, int ROWS>
-__global__ __launch_bounds__(256) void k_down_decode(FfnArgs a) {
+template <int BITS, int LPR, int CPL>
+__global__ __launch_bounds__(768) void k_down_decode(FfnArgs a) {
   constexpr int RPP = 64 / LPR;
-  constexpr int PASSES = ROWS / RPP;
-  constexpr int kMaxSlots = 33;
+  constexpr int PASSES = CPL == 1 ? 16 : CPL == 2 ? 8 : CPL <= 4 ? 4 : 2;  // ~16 loads in flight
+  constexpr int ROWS = PASSES * RPP;
+  constexpr int kMaxSlots = kSelMaxK + 1;
   __shared__ float part[kMaxSlots][ROWS];
   const int I = a.L.I;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int gl = lane % LPR, rsub = lane / LPR;
   const int nchunks = I * BITS / 128;
   const size_t row_bytes = (size_t)I * BITS / 8;
   const int r0 = blockIdx.x * ROWS;
   const int nslots = a.k + 1;
 
-  for (int sl = wave; sl < nslots; sl += 4) {
-    SlotInfo s;
-    const bool live = resolve_slot(a, false, sl, s);
-    if (!live) {
+  for (int sl = wave; sl < nslots; sl += nw) {
+    const bool shared = (sl == a.k);
+    const int e = shared ? -1 : a.idx[sl];
+    if (!shared && e < 0) {
       for (int r = lane; r < ROWS; r += 64) part[sl][r] = 0.f;
       continue;
     }
-    const float wgt = s.shared ? 1.f : a.w[sl];
+    const ExpertPtrs ep = expert_ptrs(a.L, e);
+    const float wgt = shared ? 1.f : a.w[sl];
+    uint4 wv[PASSES][CPL];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = r0 + p * RPP + rsub;
+      const uint4 *wp = reinterpret_cast<const uint4 *>(ep.wd + (size_t)row * row_bytes);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) wv[p][i] = ld_nt(wp + min(gl + LPR * i, nchunks - 1));
+    }
+    const float sdv = ep.sd[r0 + min(lane, ROWS - 1)];  // lane i: scale of row r0 + i
     Act<BITS> act[CPL];
     const int8_t *hq = a.hq + (size_t)sl * I;
     const float *hd = a.hd + (size_t)sl * (I / 32);
@@ -284,17 +352,6 @@ __global__ __launch_bounds__(256) void k_down_decode(FfnArgs a) {
       if (c < nchunks) load_act<BITS>(act[i], hq, hd, c);
       else zero_act<BITS>(act[i]);
     }
-    uint4 wv[PASSES][CPL];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = r0 + p * RPP + rsub;
-      const uint4 *wp = reinterpret_cast<const uint4 *>(s.wd + (size_t)row * row_bytes);
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = gl + LPR * i;
-        wv[p][i] = c < nchunks ? ld_nt(wp + c) : make_uint4(0, 0, 0, 0);
-      }
-    }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       float acc = 0.f;
@@ -302,14 +359,15 @@ __global__ __launch_bounds__(256) void k_down_decode(FfnArgs a) {
       for (int i = 0; i < CPL; ++i) acc += chunk_part<BITS>(wv[p][i], act[i]);
       acc = group_sum<LPR>(acc);
       const int rl = p * RPP + rsub;
+      const float sd = row_scale<RPP>(sdv, p, rsub);
       if (lane == group_sum_lane<LPR>(lane)) {
-        const float o = acc * s.sd[r0 + rl];
-        part[sl][rl] = s.shared ? o : wgt * o;
+        const float o = acc * sd;
+        part[sl][rl] = shared ? o : wgt * o;
       }
     }
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < ROWS; r += 256) {
+  for (int r = threadIdx.x; r < ROWS; r += blockDim.x) {
     float y = part[a.k][r];
     for (int j = 0; j < a.k; ++j) y += part[j][r];
     a.y[r0 + r] = y;
@@ -328,8 +386,10 @@ __global__ __launch_bounds__(256) void k_down_union(FfnArgs a) {
   const int H = a.L.H, I = a.L.I;
   const int n_rb = H / (4 * ROWS);
   const int u = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
-  SlotInfo s;
-  if (!resolve_slot(a, true, u, s)) return;
+  int e;
+  TokList s;
+  if (!union_item(a, u, e, s)) return;
+  const ExpertPtrs ep = expert_ptrs(a.L, e);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gl = lane % LPR, rsub = lane / LPR;
   const int nchunks = I * BITS / 128;
@@ -340,13 +400,11 @@ __global__ __launch_bounds__(256) void k_down_union(FfnArgs a) {
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = r0 + p * RPP + rsub;
-    const uint4 *wp = reinterpret_cast<const uint4 *>(s.wd + (size_t)row * row_bytes);
+    const uint4 *wp = reinterpret_cast<const uint4 *>(ep.wd + (size_t)row * row_bytes);
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = gl + LPR * i;
-      wv[p][i] = c < nchunks ? ld_nt(wp + c) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < CPL; ++i) wv[p][i] = ld_nt(wp + min(gl + LPR * i, nchunks - 1));
   }
+  const float sdv = ep.sd[r0 + min(lane, ROWS - 1)];  // lane i: scale of row r0 + i
   for (int t0 = 0; t0 < s.n_tok; t0 += NT) {
     Act<BITS> act[CPL][NT];
     int tok[NT], slot[NT];
@@ -354,7 +412,7 @@ __global__ __launch_bounds__(256) void k_down_union(FfnArgs a) {
     for (int tt = 0; tt < NT; ++tt) {
       int t = 0, hrow = 0, j = 0;
       const bool tv = t0 + tt < s.n_tok;
-      if (tv) slot_token(a, true, s, t0 + tt, t, hrow, j);
+      if (tv) tok_at(a, true, s, t0 + tt, t, hrow, j);
       tok[tt] = tv ? t : -1;
       slot[tt] = j;
       const int8_t *hq = a.hq + (size_t)hrow * I;
@@ -377,8 +435,8 @@ __global__ __launch_bounds__(256) void k_down_union(FfnArgs a) {
         for (int i = 0; i < CPL; ++i) acc[tt] += chunk_part<BITS>(wv[p][i], act[i][tt]);
         acc[tt] = group_sum<LPR>(acc[tt]);
       }
+      const float sd = row_scale<RPP>(sdv, p, rsub);
       if (lane == group_sum_lane<LPR>(lane)) {
-        const float sd = s.sd[row];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
           if (tok[tt] >= 0)
@@ -416,14 +474,16 @@ static int pick_lpr(int nchunks) { return (nchunks % 64 != 0 && nchunks % 32 == 
 
 static int pick_cpl(int nchunks, int lpr) {
   const int c = (nchunks + lpr - 1) / lpr;
-  return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : c <= 8 ? 8 : -1;
+  return c <= 1 ? 1 : c <= 2 ? 2 : c <= 3 ? 3 : c <= 4 ? 4 : c <= 6 ? 6 : c <= 8 ? 8 : -1;
 }
 
 #define COLI_CPL_SWITCH(CPLV, ...)                        \
   switch (CPLV) {                                         \
     case 1: { constexpr int CPL = 1; __VA_ARGS__; } break; \
     case 2: { constexpr int CPL = 2; __VA_ARGS__; } break; \
+    case 3: { constexpr int CPL = 3; __VA_ARGS__; } break; \
     case 4: { constexpr int CPL = 4; __VA_ARGS__; } break; \
+    case 6: { constexpr int CPL = 6; __VA_ARGS__; } break; \
     case 8: { constexpr int CPL = 8; __VA_ARGS__; } break; \
     default: return hipErrorInvalidValue;                 \
   }
@@ -445,35 +505,39 @@ static int union_slots(const FfnArgs &a) {
   return (int)((routed < a.E ? routed : a.E) + 1);
 }
 
-hipError_t launch_gateup(const FfnArgs &a, bool union_mode, int /*mfma_min*/, hipStream_t st) {
+hipError_t launch_gateup(const FfnArgs &a, bool union_mode, int /*mfma_min*/, hipStream_t st,
+                         KEvents ev) {
   const int nch = a.L.H * a.L.bits / 128;
   const int lpr = pick_lpr(nch), cpl = pick_cpl(nch, lpr);
   const int slots = union_mode ? union_slots(a) : a.k + 1;
   const dim3 grid((unsigned)(slots * (a.L.I / 32))), block(256);
   COLI_BITS_SWITCH(a.L.bits, COLI_LPR_SWITCH(lpr, COLI_CPL_SWITCH(cpl, {
     if (union_mode)
-      hipLaunchKernelGGL((k_gateup<BITS, LPR, CPL, 4>), grid, block, 0, st, a, 1);
+      COLI_LAUNCH(ev, (k_gateup_union<BITS, LPR, CPL, 4>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((k_gateup<BITS, LPR, CPL, 1>), grid, block, 0, st, a, 0);
+      COLI_LAUNCH(ev, (k_gateup_decode<BITS, LPR, CPL>), grid, block, 0, st, a);
   })));
   return hipGetLastError();
 }
 
-hipError_t launch_down(const FfnArgs &a, bool union_mode, int /*mfma_min*/, hipStream_t st) {
+hipError_t launch_down(const FfnArgs &a, bool union_mode, int /*mfma_min*/, hipStream_t st,
+                       KEvents ev) {
   const int nch = a.L.I * a.L.bits / 128;
   const int lpr = pick_lpr(nch), cpl = pick_cpl(nch, lpr);
   if (!union_mode) {
-    constexpr int ROWS = 16;
-    const dim3 grid((unsigned)(a.L.H / ROWS)), block(256);
+    const int nw = a.k + 1 < 12 ? a.k + 1 : 12;
+    const int passes = cpl == 1 ? 16 : cpl == 2 ? 8 : cpl <= 4 ? 4 : 2;
+    const int rows = passes * (64 / lpr);
+    const dim3 grid((unsigned)(a.L.H / rows)), block(64 * nw);
     COLI_BITS_SWITCH(a.L.bits, COLI_LPR_SWITCH(lpr, COLI_CPL_SWITCH(cpl, {
-      hipLaunchKernelGGL((k_down_decode<BITS, LPR, CPL, ROWS>), grid, block, 0, st, a);
+      COLI_LAUNCH(ev, (k_down_decode<BITS, LPR, CPL>), grid, block, 0, st, a);
     })));
   } else {
     constexpr int ROWS = 8;
     const int slots = union_slots(a);
     const dim3 grid((unsigned)(slots * (a.L.H / (4 * ROWS)))), block(256);
     COLI_BITS_SWITCH(a.L.bits, COLI_LPR_SWITCH(lpr, COLI_CPL_SWITCH(cpl, {
-      hipLaunchKernelGGL((k_down_union<BITS, LPR, CPL, 4, ROWS>), grid, block, 0, st, a);
+      COLI_LAUNCH(ev, (k_down_union<BITS, LPR, CPL, 4, ROWS>), grid, block, 0, st, a);
     })));
   }
   return hipGetLastError();

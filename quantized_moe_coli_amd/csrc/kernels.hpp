@@ -7,9 +7,27 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_ext.h>
+
 #include "device.hpp"
 
 namespace coli {
+
+// Optional per-kernel timing: events recorded by the launch itself at the
+// kernel's start and end (hipExtLaunchKernelGGL), so their interval is the
+// kernel's execution, as a kernel-trace profiler reports it.
+struct KEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+#define COLI_LAUNCH(EV, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                  \
+  do {                                                                                           \
+    if ((EV).start || (EV).stop)                                                                 \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, (EV).start, (EV).stop, 0,        \
+                            __VA_ARGS__);                                                        \
+    else                                                                                         \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                       \
+  } while (0)
 
 // Router configuration as the kernels see it (a copy of the ABI struct).
 struct RouterCfg {
@@ -44,6 +62,10 @@ hipError_t launch_act_quant(int layout_bits, const float *x, int64_t T, int64_t 
 
 hipError_t launch_logits(const float *x, const float *gate_w, int T, int E, int H, float *logits,
                          hipStream_t st);
+// Router logits (if gate_w) and Q8_0 activations in container BITS ordering
+// (if xq), in as few launches as the batch allows.
+hipError_t launch_front(int bits, const float *x, const float *gate_w, int T, int E, int H,
+                        float *logits, int8_t *xq, float *xd, hipStream_t st, KEvents ev = {});
 hipError_t launch_route(const RouterCfg &cfg, const float *logits, const float *bias, int T,
                         int32_t *idx, float *w, int32_t *idx_copy, float *w_copy, hipStream_t st);
 hipError_t launch_dispatch(const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offs,
@@ -59,8 +81,14 @@ struct FfnArgs {
   int T, k, E;
   const int8_t *xq;     // [T][H], ordering of L.bits
   const float *xd;      // [T][H/32]
-  const int32_t *idx;   // [T][k]
-  const float *w;       // [T][k]
+  int32_t *idx;         // [T][k] (decode: written by the gate/up kernel)
+  float *w;             // [T][k]
+  // decode mode: the gate/up kernel selects the experts itself
+  RouterCfg cfg;
+  const float *logits;  // [1][E]
+  const float *bias;    // [E] or null
+  int32_t *idx_user;    // optional copies for the caller
+  float *w_user;
   Dispatch disp;        // union mode only
   int8_t *hq;           // [rows][I], ordering of L.bits
   float *hd;            // [rows][I/32]
@@ -68,8 +96,10 @@ struct FfnArgs {
   float *y;             // [T][H]
 };
 
-hipError_t launch_gateup(const FfnArgs &a, bool union_mode, int mfma_min, hipStream_t st);
-hipError_t launch_down(const FfnArgs &a, bool union_mode, int mfma_min, hipStream_t st);
+hipError_t launch_gateup(const FfnArgs &a, bool union_mode, int mfma_min, hipStream_t st,
+                         KEvents ev = {});
+hipError_t launch_down(const FfnArgs &a, bool union_mode, int mfma_min, hipStream_t st,
+                       KEvents ev = {});
 hipError_t launch_combine(const FfnArgs &a, hipStream_t st);
 
 hipError_t launch_debug_blocks(int bits, const uint8_t *Wq, int rows, int cols, const int8_t *xq_perm,

@@ -8,6 +8,7 @@
 // symmetric-absmax reading with a correctly rounded binary32 division and
 // round-half-even, so the codes and scales are bit-identical to any IEEE
 // implementation of the same rule.
+#include "actq.hpp"
 #include "kernels.hpp"
 
 namespace coli {
@@ -46,9 +47,7 @@ __global__ __launch_bounds__(256) void k_quant_pack(const float *__restrict__ w,
   }
 }
 
-// One thread per Q8_0 block of 32 values.  The codes are stored in the
-// ordering the weight container BITS consumes (see perm_src in device.hpp);
-// BITS = 8 is the natural order.
+// One thread per Q8_0 block of 32 values (act_quant_block, actq.hpp).
 template <int BITS>
 __global__ __launch_bounds__(256) void k_act_quant(const float *__restrict__ x, int64_t T,
                                                    int64_t n, int8_t *__restrict__ q,
@@ -57,30 +56,7 @@ __global__ __launch_bounds__(256) void k_act_quant(const float *__restrict__ x, 
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * nb) return;
   const int64_t t = i / nb, b = i % nb;
-  const float4 *xb = reinterpret_cast<const float4 *>(x + t * n + b * 32);
-  float v[32];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const float4 f = xb[m];
-    v[4 * m] = f.x; v[4 * m + 1] = f.y; v[4 * m + 2] = f.z; v[4 * m + 3] = f.w;
-  }
-  float amax = 0.f;
-#pragma unroll
-  for (int m = 0; m < 32; ++m) amax = fmaxf(amax, fabsf(v[m]));
-  const float db = amax / 127.f;
-  d[i] = db;
-  uint32_t words[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) words[m] = 0;
-#pragma unroll
-  for (int s = 0; s < 32; ++s) {
-    float c = 0.f;
-    if (db != 0.f) c = fminf(fmaxf(rintf(v[perm_src<BITS>(s)] / db), -127.f), 127.f);
-    words[s >> 2] |= ((uint32_t)(int32_t)c & 0xFFu) << (8 * (s & 3));
-  }
-  uint4 *out = reinterpret_cast<uint4 *>(q + t * n + b * 32);
-  out[0] = make_uint4(words[0], words[1], words[2], words[3]);
-  out[1] = make_uint4(words[4], words[5], words[6], words[7]);
+  act_quant_block<BITS>(x + t * n + b * 32, q + t * n + b * 32, d + i);
 }
 
 hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t cols, uint8_t *q,

@@ -12,48 +12,83 @@
 // order as the definition (no contraction), so indices and weights are
 // reproducible bit for bit; the sigmoid is evaluated in binary64 and rounded
 // once.
+#include "actq.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 #pragma clang fp contract(off)
 
 namespace coli {
 
 // ---------------------------------------------------------------------------
-// Logits, small batches: one wave per expert row, the row read once and
-// applied to every token; binary64 accumulation (each fp32 product is exact
-// in binary64), rounded once to binary32.
+// Front of the layer for small batches (T <= 4), one launch:
+//   blocks [0, nlog): router logits of expert row b.  The 4 waves split the
+//     row in quarters; binary64 accumulation (each fp32 product is exact in
+//     binary64), partials added in a fixed order, rounded once to binary32.
+//   blocks [nlog, nlog + naq): Q8_0 quantisation of the activations, one
+//     thread per block of 32 (codes in the ordering of container BITS).
 // ---------------------------------------------------------------------------
-template <int MAXT>
-__global__ __launch_bounds__(256) void k_logits_gemv(const float *__restrict__ x,
+template <int BITS, int MAXT>
+__global__ __launch_bounds__(256) void k_front_small(const float *__restrict__ x,
                                                      const float *__restrict__ gw, int T, int E,
-                                                     int H, float *__restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
-  const float4 *wr = reinterpret_cast<const float4 *>(gw + (size_t)e * H);
+                                                     int H, float *__restrict__ out, int nlog,
+                                                     int8_t *__restrict__ xq,
+                                                     float *__restrict__ xd) {
+  __shared__ double red[4][MAXT];
+  const int b = blockIdx.x;
+  if (b >= nlog) {
+    const int64_t nb = H / 32;
+    const int64_t i = (int64_t)(b - nlog) * 256 + threadIdx.x;
+    if (i >= (int64_t)T * nb) return;
+    const int64_t t = i / nb, blk = i % nb;
+    act_quant_block<BITS>(x + t * H + blk * 32, xq + t * H + blk * 32, xd + i);
+    return;
+  }
+  const int e = b;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q4 = H / 16;  // float4 per quarter row (<= 128 for H <= 8192)
+  constexpr int kPer = 2;  // float4 per lane per step
+  const float4 *wr = reinterpret_cast<const float4 *>(gw + (size_t)e * H) + wave * q4;
   double acc[MAXT];
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) acc[t] = 0.0;
-  const int n4 = H / 4;
-  for (int c = lane; c < n4; c += 64) {
-    const float4 wv = wr[c];
+  for (int c0 = 0; c0 < q4; c0 += 64 * kPer) {
+    float4 wv[kPer];
+    bool ok[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = c0 + lane + 64 * i;
+      ok[i] = c < q4;
+      wv[i] = wr[min(c, q4 - 1)];
+    }
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) {
       if (t < T) {
-        const float4 xv = reinterpret_cast<const float4 *>(x + (size_t)t * H)[c];
-        acc[t] = fma((double)xv.x, (double)wv.x, acc[t]);
-        acc[t] = fma((double)xv.y, (double)wv.y, acc[t]);
-        acc[t] = fma((double)xv.z, (double)wv.z, acc[t]);
-        acc[t] = fma((double)xv.w, (double)wv.w, acc[t]);
+        const float4 *xr = reinterpret_cast<const float4 *>(x + (size_t)t * H) + wave * q4;
+        float4 xv[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) xv[i] = xr[min(c0 + lane + 64 * i, q4 - 1)];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          if (!ok[i]) continue;
+          acc[t] = fma((double)xv[i].x, (double)wv[i].x, acc[t]);
+          acc[t] = fma((double)xv[i].y, (double)wv[i].y, acc[t]);
+          acc[t] = fma((double)xv[i].z, (double)wv[i].z, acc[t]);
+          acc[t] = fma((double)xv[i].w, (double)wv[i].w, acc[t]);
+        }
       }
     }
   }
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) {
-    if (t < T) {
-      const double s = wave_sum_f64(acc[t]);
-      if (lane == 0) out[(size_t)t * E + e] = (float)s;
-    }
+    const double s = wave_sum_f64(acc[t]);
+    if (lane == 0) red[wave][t] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < MAXT && (int)threadIdx.x < T) {
+    const int t = threadIdx.x;
+    const double s = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
+    out[(size_t)t * E + e] = (float)s;
   }
 }
 
@@ -63,7 +98,8 @@ __global__ __launch_bounds__(256) void k_logits_gemv(const float *__restrict__ x
 // 16x16x4: lane l supplies row (l % 16) and reduction index (l / 16); the
 // reduction order inside a tile does not matter, so for a step of 16 inputs
 // lane l loads the float4 at offset 4*(l/16) and feeds component j to the
-// j-th MFMA.  Result: lane l holds rows 4*(l/16)+i, column l % 16.
+// j-th MFMA.  Result (binary64 layout): register i of lane l holds row
+// (l / 16) + 4*i, column l % 16.
 // ---------------------------------------------------------------------------
 typedef double d4 __attribute__((ext_vector_type(4)));
 
@@ -110,164 +146,78 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const float *__restrict__ x
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * a + 4 * g + i;
+        const int t = t0 + 16 * a + g + 4 * i;
         const int e = e0 + 16 * b + r;
         if (t < T && e < E) out[(size_t)t * E + e] = (float)acc[a][b][i];
       }
 }
 
+template <int BITS>
+static void front_small(const float *x, const float *gate_w, int T, int E, int H, float *logits,
+                        int8_t *xq, float *xd, hipStream_t st, KEvents ev) {
+  const int nlog = gate_w ? E : 0;
+  const int naq = xq ? (int)(((int64_t)T * (H / 32) + 255) / 256) : 0;
+  COLI_LAUNCH(ev, (k_front_small<BITS, 4>), dim3(nlog + naq), dim3(256), 0, st, x, gate_w, T, E,
+              H, logits, nlog, xq, xd);
+}
+
+hipError_t launch_front(int bits, const float *x, const float *gate_w, int T, int E, int H,
+                        float *logits, int8_t *xq, float *xd, hipStream_t st, KEvents ev) {
+  if (T == 0 || (!gate_w && !xq)) return hipSuccess;
+  if (T <= 4) {
+    switch (bits) {
+      case 8: front_small<8>(x, gate_w, T, E, H, logits, xq, xd, st, ev); break;
+      case 4: front_small<4>(x, gate_w, T, E, H, logits, xq, xd, st, ev); break;
+      case 2: front_small<2>(x, gate_w, T, E, H, logits, xq, xd, st, ev); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  if (gate_w) {
+    const dim3 grid((E + 127) / 128, (T + 31) / 32), block(256);
+    COLI_LAUNCH(ev, k_logits_mfma, grid, block, 0, st, x, gate_w, T, E, H, logits);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (xq) return launch_act_quant(bits, x, T, H, xq, xd, st);
+  return hipSuccess;
+}
+
 hipError_t launch_logits(const float *x, const float *gate_w, int T, int E, int H, float *logits,
                          hipStream_t st) {
-  if (T == 0) return hipSuccess;
-  if (T <= 4) {
-    const dim3 grid((E + 3) / 4), block(256);
-    hipLaunchKernelGGL(k_logits_gemv<4>, grid, block, 0, st, x, gate_w, T, E, H, logits);
-  } else {
-    const dim3 grid((E + 127) / 128, (T + 31) / 32), block(256);
-    hipLaunchKernelGGL(k_logits_mfma, grid, block, 0, st, x, gate_w, T, E, H, logits);
-  }
-  return hipGetLastError();
+  return launch_front(8, x, gate_w, T, E, H, logits, nullptr, nullptr, st);
 }
 
 // ---------------------------------------------------------------------------
-// Selection: one wave per token.
+// Selection: one wave per token (select.hpp), four tokens per workgroup.
 // ---------------------------------------------------------------------------
-struct Cand {
-  float v;
-  int i;  // index; -1 = no candidate
-};
-
-__device__ __forceinline__ bool better(const Cand &a, const Cand &b) {
-  if (a.i < 0) return false;
-  if (b.i < 0) return true;
-  return a.v > b.v || (a.v == b.v && a.i < b.i);
-}
-
-__device__ __forceinline__ Cand wave_best(Cand c) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    Cand o;
-    o.v = __shfl_xor(c.v, m, 64);
-    o.i = __shfl_xor(c.i, m, 64);
-    if (better(o, c)) c = o;
-  }
-  return c;
-}
-
-constexpr int kMaxE = 1024, kMaxK = 32;
-
-__global__ __launch_bounds__(64) void k_route(RouterCfg cfg, const float *__restrict__ logits,
-                                              const float *__restrict__ bias, int T,
-                                              int32_t *__restrict__ idx, float *__restrict__ wout,
-                                              int32_t *__restrict__ idx2, float *__restrict__ w2) {
-  __shared__ float sig[kMaxE];
-  __shared__ float cs[kMaxE];
-  __shared__ int rank[kMaxK];
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int E = cfg.E, k = cfg.k, G = cfg.n_group, per = E / G;
-  for (int e = lane; e < E; e += 64) {
-    const float l = logits[(size_t)t * E + e];
-    const float s = (float)(1.0 / (1.0 + exp(-(double)l)));
-    sig[e] = s;
-    cs[e] = s + (bias ? bias[e] : 0.f);
-  }
-  __syncthreads();
-
-  // group scores: sum of the two best biased scores of each group
-  Cand gc;
-  gc.i = -1;
-  gc.v = 0.f;
-  if (lane < G) {
-    int b1 = -1, b2 = -1;
-    for (int e = lane * per; e < (lane + 1) * per; ++e) {
-      if (b1 < 0 || cs[e] > cs[b1]) { b2 = b1; b1 = e; }
-      else if (b2 < 0 || cs[e] > cs[b2]) { b2 = e; }
-    }
-    gc.v = per >= 2 ? cs[b1] + cs[b2] : cs[b1];
-    gc.i = lane;
-  }
-  bool gkeep = false;
-  for (int n = 0; n < cfg.topk_group; ++n) {
-    Cand probe = gc;
-    if (gkeep) probe.i = -1;
-    const Cand best = wave_best(probe);
-    if (lane == best.i) gkeep = true;
-  }
-  const uint64_t keepmask = __ballot(gkeep);
-
-  // experts: lane owns e = lane + 64*m
-  uint32_t taken = 0;
-  for (int j = 0; j < k; ++j) {
-    Cand c;
-    c.i = -1;
-    c.v = 0.f;
-    for (int m = 0, e = lane; e < E; ++m, e += 64) {
-      if (((keepmask >> (e / per)) & 1ull) == 0 || ((taken >> m) & 1u)) continue;
-      Cand o{cs[e], e};
-      if (better(o, c)) c = o;
-    }
-    const Cand best = wave_best(c);
-    if (best.i >= 0 && (best.i & 63) == lane) taken |= 1u << (best.i >> 6);
-    if (lane == 0) rank[j] = best.i;
-  }
-  __syncthreads();
-
-  if (lane == 0) {
-    // a slot with no candidate cannot occur for a validated configuration;
-    // it is dropped rather than read out of range
-    float S = 0.f;
-    for (int j = 0; j < k; ++j)
-      if (rank[j] >= 0) S += sig[rank[j]];
-    float wv[kMaxK];
-    int iv[kMaxK];
-    for (int j = 0; j < k; ++j) {
-      iv[j] = rank[j];
-      if (rank[j] < 0) { wv[j] = 0.f; continue; }
-      const float s = sig[rank[j]];
-      if (cfg.norm) wv[j] = (S != 0.f) ? (s / S) * cfg.rsf : 0.f;
-      else wv[j] = s * cfg.rsf;
-    }
-    if (cfg.top_p > 0.f && cfg.top_p < 1.f) {
-      float pn[kMaxK];
-      bool keep[kMaxK], seen[kMaxK];
-      for (int j = 0; j < k; ++j) {
-        pn[j] = (S != 0.f && iv[j] >= 0) ? sig[iv[j]] / S : 0.f;
-        keep[j] = false;
-        seen[j] = false;
-      }
-      float cum = 0.f;
-      for (int n = 0; n < k; ++n) {
-        int best = -1;
-        for (int j = 0; j < k; ++j)
-          if (!seen[j] && (best < 0 || pn[j] > pn[best])) best = j;
-        seen[best] = true;
-        keep[best] = true;
-        cum += pn[best];
-        if (cum >= cfg.top_p) break;
-      }
-      float Sk = 0.f;
-      for (int j = 0; j < k; ++j)
-        if (keep[j] && iv[j] >= 0) Sk += sig[iv[j]];
-      for (int j = 0; j < k; ++j) {
-        if (!keep[j] || iv[j] < 0) { iv[j] = -1; wv[j] = 0.f; continue; }
-        if (cfg.renorm) wv[j] = (Sk != 0.f) ? (sig[iv[j]] / Sk) * cfg.rsf : 0.f;
-      }
-    }
-    for (int j = 0; j < k; ++j) {
-      idx[(size_t)t * k + j] = iv[j];
-      wout[(size_t)t * k + j] = wv[j];
-      if (idx2) idx2[(size_t)t * k + j] = iv[j];
-      if (w2) w2[(size_t)t * k + j] = wv[j];
-    }
+__global__ __launch_bounds__(256) void k_route(RouterCfg cfg, const float *__restrict__ logits,
+                                               const float *__restrict__ bias, int T,
+                                               int32_t *__restrict__ idx, float *__restrict__ wout,
+                                               int32_t *__restrict__ idx2, float *__restrict__ w2) {
+  __shared__ SelScratch sc[4];
+  __shared__ int32_t li[4][kSelMaxK];
+  __shared__ float lw[4][kSelMaxK];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const int k = cfg.k;
+  select_token(cfg, logits + (size_t)t * cfg.E, bias, sc[wave], li[wave], lw[wave]);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = li[wave][lane];
+    wout[(size_t)t * k + lane] = lw[wave][lane];
+    if (idx2) idx2[(size_t)t * k + lane] = li[wave][lane];
+    if (w2) w2[(size_t)t * k + lane] = lw[wave][lane];
   }
 }
 
 hipError_t launch_route(const RouterCfg &cfg, const float *logits, const float *bias, int T,
                         int32_t *idx, float *w, int32_t *idx_copy, float *w_copy, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_route, dim3(T), dim3(64), 0, st, cfg, logits, bias, T, idx, w, idx_copy,
-                     w_copy);
+  hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, st, cfg, logits, bias, T, idx, w,
+                     idx_copy, w_copy);
   return hipGetLastError();
 }
 
@@ -289,10 +239,10 @@ __global__ __launch_bounds__(kDispThreads) void k_dispatch(const int32_t *__rest
                                                            int32_t *__restrict__ perm,
                                                            int32_t *__restrict__ uniq,
                                                            int32_t *__restrict__ n_uniq) {
-  __shared__ int cnt[kMaxE];
-  __shared__ int scan_a[kMaxE];
-  __shared__ int scan_b[kMaxE];
-  __shared__ int base[kMaxE];
+  __shared__ int cnt[kSelMaxE];
+  __shared__ int scan_a[kSelMaxE];
+  __shared__ int scan_b[kSelMaxE];
+  __shared__ int base[kSelMaxE];
   __shared__ uint32_t mask[kDispWords];
   __shared__ int pref[kDispWords];
   const int tid = threadIdx.x;
@@ -313,7 +263,7 @@ __global__ __launch_bounds__(kDispThreads) void k_dispatch(const int32_t *__rest
   }
   __syncthreads();
   for (int d = 1; d < E; d <<= 1) {
-    int va[(kMaxE + kDispThreads - 1) / kDispThreads], vb[(kMaxE + kDispThreads - 1) / kDispThreads];
+    int va[(kSelMaxE + kDispThreads - 1) / kDispThreads], vb[(kSelMaxE + kDispThreads - 1) / kDispThreads];
     int q = 0;
     for (int e = tid; e < E; e += kDispThreads, ++q) {
       va[q] = scan_a[e] + (e >= d ? scan_a[e - d] : 0);
