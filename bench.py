@@ -13,10 +13,10 @@ A "step" is one full layer forward on one token.  The K timed steps are
 captured into one HIP graph (launch overhead out of the way) and replayed
 once between two synchronisations.  The same K steps are then launched
 eagerly on the current stream through coli_moe_forward_profiled, whose
-front, gate/up and down kernel launches each record a start and a stop
-hipEvent (hipExtLaunchKernelGGL); those give each kernel's average
-execution time, including that of the dominant gate/up kernel used for the
-roofline figure.  Prints ONE JSON
+kernel launches each record a start and a stop hipEvent
+(hipExtLaunchKernelGGL); those give each kernel's average execution time,
+including that of the dominant kernel used for the roofline figure (decode:
+the single fused kernel; union batches: the gate/up kernel).  Prints ONE JSON
 line on stdout; details go to stderr.
 
   python bench.py [--steps K] [--warmup W] [--workload decode|verify3|prefill512]
@@ -192,10 +192,11 @@ def main() -> int:
             return float("nan")
         return v.value
 
-    stage = np.array([[el(evs[st * n_ev + 2 * i], evs[st * n_ev + 2 * i + 1]) for i in range(3)]
-                      for st in range(K)])  # ms: front, gate/up, down kernels
-    span = np.array([el(evs[st * n_ev], evs[st * n_ev + 5]) for st in range(K)])
-    eager_ms = el(evs[0], evs[K * n_ev - 1])
+    n_k = 1 if T == 1 else 3  # decode: one fused kernel; union: front, gate/up, down
+    stage = np.array([[el(evs[st * n_ev + 2 * i], evs[st * n_ev + 2 * i + 1]) for i in range(n_k)]
+                      for st in range(K)])  # ms
+    span = np.array([el(evs[st * n_ev], evs[st * n_ev + 2 * n_k - 1]) for st in range(K)])
+    eager_ms = el(evs[0], evs[(K - 1) * n_ev + 2 * n_k - 1])
     for e in evs:
         hip.hipEventDestroy(ctypes.c_void_p(e))
     hip.hipGetLastError()
@@ -221,20 +222,31 @@ def main() -> int:
     gu_bytes = (uniq + 1) * eb["gate_up"]
     down_bytes = (uniq + 1) * eb["down"]
     avg = stage.mean(axis=0)
-    gu_ms = float(np.mean(stage[:, 1]))
-    gu_gbps = float(np.mean(gu_bytes)) / (gu_ms * 1e-3) / 1e9
     layer_gbps = float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9
+    if T == 1:  # the dominant (only) kernel is the fused decode kernel
+        dom_name = "k_decode_fused (the whole layer for one token)"
+        dom_ms = float(avg[0])
+        dom_bytes = float(np.mean(layer_bytes))
+    else:
+        dom_name = "k_gateup_union (gate/up GEMV + SwiGLU + Q8_0 of h)"
+        dom_ms = float(avg[1])
+        dom_bytes = float(np.mean(gu_bytes))
+    dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
     log(f"[bench] {args.workload}: {K} steps in {total_ms:.3f} ms (wall {wall * 1e3:.1f} ms): "
         f"{ms_per_step * 1e3:.2f} us/step, {tokens_per_s:.0f} tokens/s")
     log(f"[bench] eager pass with kernel events: {eager_ms / K * 1e3:.2f} us/step (host wall "
         f"{eager_wall / K * 1e6:.2f} us/step), first-kernel start to last-kernel end "
         f"{np.mean(span) * 1e3:.2f} us")
-    log(f"[bench] kernel means (us): front (act quant + logits) {avg[0] * 1e3:.2f}, gate/up "
-        f"{avg[1] * 1e3:.2f}, down {avg[2] * 1e3:.2f}")
+    if T == 1:
+        log(f"[bench] kernel mean (us): k_decode_fused {avg[0] * 1e3:.2f}")
+    else:
+        log(f"[bench] kernel means (us): front (act quant + logits) {avg[0] * 1e3:.2f}, gate/up "
+            f"{avg[1] * 1e3:.2f} ({float(np.mean(gu_bytes)) / (avg[1] * 1e-3) / 1e9:.0f} GB/s), down "
+            f"{avg[2] * 1e3:.2f} ({float(np.mean(down_bytes)) / (avg[2] * 1e-3) / 1e9:.0f} GB/s)")
     log(f"[bench] unique experts/step {uniq.mean():.1f}; layer bytes/step "
         f"{np.mean(layer_bytes) / 1e6:.2f} MB -> {layer_gbps:.0f} GB/s "
-        f"({100 * layer_gbps / HBM_PEAK_GBPS:.1f}% of HBM peak); gate/up "
-        f"{gu_gbps:.0f} GB/s; down {float(np.mean(down_bytes)) / (avg[2] * 1e-3) / 1e9:.0f} GB/s")
+        f"({100 * layer_gbps / HBM_PEAK_GBPS:.1f}% of HBM peak); dominant kernel "
+        f"{dom_gbps:.0f} GB/s")
 
     result = {
         "metric": "MoE-layer tokens/s (int4 top-8/256 decode)" if T == 1 else
@@ -259,20 +271,21 @@ def main() -> int:
             "tokens_per_step": T,
             "layer_instances": NI,
             "launch": "one HIP graph of the K timed steps",
-            "kernel_us": {"front": round(float(avg[0]) * 1e3, 3),
-                          "gate_up": round(float(avg[1]) * 1e3, 3),
-                          "down": round(float(avg[2]) * 1e3, 3)},
+            "kernel_us": ({"k_decode_fused": round(float(avg[0]) * 1e3, 3)} if T == 1 else
+                          {"front": round(float(avg[0]) * 1e3, 3),
+                           "gate_up": round(float(avg[1]) * 1e3, 3),
+                           "down": round(float(avg[2]) * 1e3, 3)}),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_gateup (gate/up GEMV + SwiGLU + Q8_0 of h)",
-            "achieved": round(gu_gbps, 1),
+            "kernel": dom_name,
+            "achieved": round(dom_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
+            "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
             "traffic": None,
-            "avg_launch_us": round(gu_ms * 1e3, 3),
-            "bytes_per_launch": int(np.mean(gu_bytes)),
+            "avg_launch_us": round(dom_ms * 1e3, 3),
+            "bytes_per_launch": int(dom_bytes),
         },
         "layer_roofline": {
             "bound": "hbm",

@@ -163,7 +163,14 @@ coli_status coli_moe_dispatch(const int32_t *topk_idx, int32_t T, int32_t k,
 
 /* Workspace bytes coli_moe_forward needs for up to max_tokens tokens with
  * this layer's shapes (0 if the descriptor is invalid).  The workspace is a
- * device buffer, 256-byte aligned, needing no initialisation. */
+ * device buffer, 256-byte aligned.  Its first COLI_WORKSPACE_COUNTER_BYTES
+ * bytes hold the counters of the single-kernel decode path: they must be
+ * zero before the workspace is first used (allocate it zeroed), and every
+ * call leaves them zero.  If they are not, a decode call cannot hang or read
+ * outside the layer, but its outputs are undefined.  One workspace serves one
+ * call at a time. */
+#define COLI_WORKSPACE_COUNTER_BYTES 20480
+
 size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int32_t max_tokens);
 
 /* The layer on T tokens: y [T][H] fp32 = shared(x_t) + sum_j w_tj *
@@ -173,9 +180,9 @@ size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int32_t max_tokens);
  * row scale and the block scale.  No residual and no normalisation.
  * x [T][H] fp32.  logits_in [T][E] or NULL (then logits = x . gate_w^T).
  * Optional outputs (NULL to skip): idx_out [T][k], w_out [T][k],
- * logits_out [T][E].  T = 1 runs the decode path; T >= 2 groups the batch by
- * expert (each unique expert's weights are read once).  T = 0 is a no-op.
- * workspace must hold coli_moe_workspace_bytes(L, T) bytes. */
+ * logits_out [T][E].  T = 1 runs the decode path (one kernel); T >= 2 groups
+ * the batch by expert (each unique expert's weights are read once).  T = 0
+ * is a no-op.  workspace must hold coli_moe_workspace_bytes(L, T) bytes. */
 coli_status coli_moe_forward(const coli_moe_layer *L, const float *x,
                              int32_t T, const float *logits_in, float *y,
                              int32_t *idx_out, float *w_out, float *logits_out,
@@ -186,10 +193,9 @@ coli_status coli_moe_forward(const coli_moe_layer *L, const float *x,
  * benchmark.  stage_events holds n_stage_events caller-created hipEvent_t
  * handles (NULL entries skipped): [2i] and [2i+1] are recorded by the launch
  * of kernel i itself at its start and end (so their interval is that
- * kernel's execution time), for i = 0 the front kernel (activation
- * quantisation + router logits), 1 the gate/up kernel (for T = 1 including
- * the expert selection), 2 the down-projection kernel.  Works inside a
- * stream capture only if the runtime supports these event launches there. */
+ * kernel's execution time).  T = 1: kernel 0 is the single decode kernel.
+ * T >= 2: kernel 0 the front kernel (activation quantisation + logits), 1
+ * the gate/up kernel, 2 the down-projection kernel. */
 coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x,
                                       int32_t T, const float *logits_in,
                                       float *y, int32_t *idx_out, float *w_out,

@@ -240,12 +240,18 @@ def coli_moe_workspace_bytes(layer: MoeLayer, max_tokens: int) -> int:
     return lib().coli_moe_workspace_bytes(ctypes.byref(c), max_tokens)
 
 
+# Leading workspace bytes holding the decode kernel's counters
+# (COLI_WORKSPACE_COUNTER_BYTES in include/coli_moe.h).
+WORKSPACE_COUNTER_BYTES = 20480
+
+
 def workspace(layer: MoeLayer, max_tokens: int, device="cuda") -> torch.Tensor:
-    """A device workspace big enough for ``max_tokens`` (256-byte aligned)."""
+    """A zeroed device workspace big enough for ``max_tokens`` (256-byte
+    aligned; its counter header must start at zero)."""
     n = coli_moe_workspace_bytes(layer, max_tokens)
     if n == 0:
         raise ValueError("invalid layer descriptor")
-    buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    buf = torch.zeros(n + 256, dtype=torch.uint8, device=device)
     off = (-buf.data_ptr()) % 256
     return buf[off:off + n]
 

@@ -77,7 +77,7 @@ coli::RouterCfg to_cfg(const coli_router_cfg &c) {
 }
 
 struct WsLayout {
-  size_t xq, xd, logits, idx, w, counts, offs, perm, uniq, nuniq, hq, hd, obuf, total;
+  size_t ctr, xq, xd, logits, idx, w, counts, offs, perm, uniq, nuniq, hq, hd, obuf, total;
 };
 
 WsLayout ws_layout(const coli_moe_layer *L, int Tmax) {
@@ -90,6 +90,7 @@ WsLayout ws_layout(const coli_moe_layer *L, int Tmax) {
     off = align_up(off + (bytes ? bytes : 1), 256);
     return o;
   };
+  w.ctr = take(COLI_WORKSPACE_COUNTER_BYTES);  // decode counters: zero before first use, left zero
   w.xq = take(T * H);
   w.xd = take(T * (H / 32) * 4);
   w.logits = take(T * E * 4);
@@ -246,18 +247,13 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
       return ev;
     };
     hipError_t e = hipSuccess;
-    // activations -> Q8_0 codes, and the router logits unless supplied
     float *lp_dst = logits_out ? logits_out : reinterpret_cast<float *>(base + ws.logits);
-    if (e == hipSuccess)
-      e = coli::launch_front(L->qtype, x, logits_in ? nullptr : L->gate_w, T, E, H, lp_dst, xq, xd,
-                             s, kev(0));
-    if (e != hipSuccess) return COLI_ERR_DEVICE;
-    const float *lp = logits_in ? logits_in : lp_dst;
     if (logits_in && logits_out) {
       e = hipMemcpyAsync(logits_out, logits_in, (size_t)T * E * sizeof(float),
                          hipMemcpyDeviceToDevice, s);
       if (e != hipSuccess) return COLI_ERR_DEVICE;
     }
+    const float *lp = logits_in ? logits_in : lp_dst;
 
     coli::FfnArgs fa{};
     fa.L = coli::LayerPtrs{H, I, L->qtype, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up,
@@ -281,7 +277,18 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
     fa.y = y;
     const int mfma_min = L->mfma_min_tokens;
     if (T == 1) {
-      // decode: the gate/up kernel selects the token's experts itself
+      // decode: the whole layer in one kernel where that kernel is built for
+      // the layer's row shapes
+      e = coli::launch_decode_fused(fa, x, logits_in ? nullptr : L->gate_w, logits_in, logits_out,
+                                    reinterpret_cast<uint32_t *>(base + ws.ctr), s, kev(0));
+      if (e != hipErrorNotSupported) return from_hip(e);
+    }
+    // activations -> Q8_0 codes, and the router logits unless supplied
+    e = coli::launch_front(L->qtype, x, logits_in ? nullptr : L->gate_w, T, E, H, lp_dst, xq, xd, s,
+                           kev(0));
+    if (e != hipSuccess) return COLI_ERR_DEVICE;
+    if (T == 1) {
+      // decode on other shapes: each gate/up workgroup selects the experts itself
       e = coli::launch_gateup(fa, false, mfma_min, s, kev(1));
       if (e == hipSuccess) e = coli::launch_down(fa, false, mfma_min, s, kev(2));
       return from_hip(e);

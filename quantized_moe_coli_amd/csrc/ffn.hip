@@ -24,237 +24,11 @@
 // mode runs one expert over its tokens and writes o into a per-(token, slot)
 // buffer that a combine kernel reduces in the same fixed order.  No
 // floating-point atomics: results are bit-reproducible.
+#include "ffn_common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
 
 namespace coli {
-
-template <int BITS>
-struct Act {
-  static constexpr int kInts = Q<BITS>::kElems / 4;
-  static constexpr int kD = Q<BITS>::kBlocks;
-  int a[kInts];
-  float d[kD];
-};
-
-// Activation codes/scales for chunk c of a row (codes in BITS ordering).
-template <int BITS>
-__device__ __forceinline__ void load_act(Act<BITS> &ac, const int8_t *q, const float *d, int c) {
-  const uint4 *p = reinterpret_cast<const uint4 *>(q + (size_t)c * Q<BITS>::kElems);
-#pragma unroll
-  for (int m = 0; m < Act<BITS>::kInts / 4; ++m) {
-    const uint4 v = p[m];
-    ac.a[4 * m] = (int)v.x;
-    ac.a[4 * m + 1] = (int)v.y;
-    ac.a[4 * m + 2] = (int)v.z;
-    ac.a[4 * m + 3] = (int)v.w;
-  }
-  if constexpr (BITS == 8) ac.d[0] = d[c >> 1];
-  else if constexpr (BITS == 4) ac.d[0] = d[c];
-  else { ac.d[0] = d[2 * c]; ac.d[1] = d[2 * c + 1]; }
-}
-
-template <int BITS>
-__device__ __forceinline__ void zero_act(Act<BITS> &ac) {
-#pragma unroll
-  for (int m = 0; m < Act<BITS>::kInts; ++m) ac.a[m] = 0;
-#pragma unroll
-  for (int m = 0; m < Act<BITS>::kD; ++m) ac.d[m] = 0.f;
-}
-
-template <int BITS>
-__device__ __forceinline__ float chunk_part(const uint4 w, const Act<BITS> &ac) {
-  if constexpr (BITS == 8) return ac.d[0] * (float)chunk_dot_q8(w, ac.a);
-  else if constexpr (BITS == 4) return ac.d[0] * (float)chunk_dot_q4(w, ac.a);
-  else {
-    int b0, b1;
-    chunk_dot_q2(w, ac.a, b0, b1);
-    return ac.d[0] * (float)b0 + ac.d[1] * (float)b1;
-  }
-}
-
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.f + expf(-g)); }
-
-__device__ __forceinline__ float bcast(float v, int lane_idx) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane_idx));
-}
-
-// Row scale of row (p * RPP + rsub) of a wave whose lane i holds the scale of
-// its i-th row (p is a compile-time pass index after unrolling).
-template <int RPP>
-__device__ __forceinline__ float row_scale(float sv, int p, int rsub) {
-  if constexpr (RPP == 1) return bcast(sv, p);
-  else return rsub ? bcast(sv, RPP * p + 1) : bcast(sv, RPP * p);
-}
-
-// Pointers of one expert (e = -1: the shared expert).
-struct ExpertPtrs {
-  const uint8_t *wg, *wu, *wd;
-  const float *sg, *su, *sd;
-};
-
-__device__ __forceinline__ ExpertPtrs expert_ptrs(const LayerPtrs &L, int e) {
-  ExpertPtrs p;
-  if (e < 0) {
-    p.wg = L.sh_gate; p.wu = L.sh_up; p.wd = L.sh_down;
-    p.sg = L.sh_s_gate; p.su = L.sh_s_up; p.sd = L.sh_s_down;
-  } else {
-    const size_t gu_stride = (size_t)L.I * (L.H * L.bits / 8);
-    const size_t d_stride = (size_t)L.H * (L.I * L.bits / 8);
-    p.wg = L.w_gate + (size_t)e * gu_stride;
-    p.wu = L.w_up + (size_t)e * gu_stride;
-    p.wd = L.w_down + (size_t)e * d_stride;
-    p.sg = L.s_gate + (size_t)e * L.I;
-    p.su = L.s_up + (size_t)e * L.I;
-    p.sd = L.s_down + (size_t)e * L.H;
-  }
-  return p;
-}
-
-// The tokens of one work item: decode -> token 0 at h row `slot`; union ->
-// the expert's perm range (routed) or every token (shared).
-struct TokList {
-  int n_tok;
-  int p0;      // union routed: first perm position; -1 otherwise
-  int slot;    // decode: slot index
-  bool shared;
-};
-
-__device__ __forceinline__ void tok_at(const FfnArgs &a, bool union_mode, const TokList &s, int n,
-                                       int &t, int &hrow, int &j) {
-  if (!union_mode) {
-    t = 0;
-    hrow = s.slot;
-    j = s.slot;
-  } else if (s.shared) {
-    t = n;
-    hrow = a.disp.offs[a.E] + n;
-    j = a.k;
-  } else {
-    const int p = a.disp.perm[s.p0 + n];
-    t = p / a.k;
-    j = p % a.k;
-    hrow = s.p0 + n;
-  }
-}
-
-// Union item u -> expert and token list; false past the last unique expert.
-__device__ __forceinline__ bool union_item(const FfnArgs &a, int u, int &e, TokList &s) {
-  const int nu = *a.disp.n_uniq;
-  if (u > nu) return false;
-  s.slot = -1;
-  s.shared = (u == nu);
-  if (s.shared) {
-    e = -1;
-    s.n_tok = a.T;
-    s.p0 = -1;
-  } else {
-    e = a.disp.uniq[u];
-    s.p0 = a.disp.offs[e];
-    s.n_tok = a.disp.offs[e + 1] - s.p0;
-  }
-  return true;
-}
-
-// ---------------------------------------------------------------------------
-// Gate/up + SwiGLU + Q8_0(h) for 32 rows (row block rb) of one expert over
-// its tokens.  Each wave owns 8 rows; the loads of the next row pass are in
-// flight while the current one is reduced.
-// ---------------------------------------------------------------------------
-template <int BITS, int LPR, int CPL, int NT>
-__device__ __forceinline__ void gateup_body(const FfnArgs &a, bool union_mode, const ExpertPtrs &ep,
-                                            const TokList &s, int rb, float (*hs)[32]) {
-  constexpr int RPP = 64 / LPR;  // rows per pass of a wave
-  constexpr int ROWS_PER_WAVE = 8;
-  constexpr int PASSES = ROWS_PER_WAVE / RPP;
-  const int H = a.L.H, I = a.L.I;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int gl = lane % LPR;           // lane in its row group
-  const int rsub = lane / LPR;         // row within the pass
-  const int nchunks = H * BITS / 128;  // 16-byte chunks per row
-  const size_t row_bytes = (size_t)H * BITS / 8;
-  const int xblocks = H / 32;
-
-  // lane i < 8 holds the gate/up scales of the wave's i-th row
-  const int srow = rb * 32 + wave * ROWS_PER_WAVE + min(lane, ROWS_PER_WAVE - 1);
-  const float sgv = ep.sg[srow], suv = ep.su[srow];
-  for (int t0 = 0; t0 < s.n_tok; t0 += NT) {
-    Act<BITS> act[CPL][NT];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      int t = 0, hrow = 0, j = 0;
-      const bool tv = t0 + tt < s.n_tok;
-      if (tv) tok_at(a, union_mode, s, t0 + tt, t, hrow, j);
-      const int8_t *xq = a.xq + (size_t)t * H;
-      const float *xd = a.xd + (size_t)t * xblocks;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = gl + LPR * i;
-        if (tv && c < nchunks) load_act<BITS>(act[i][tt], xq, xd, c);
-        else zero_act<BITS>(act[i][tt]);
-      }
-    }
-    uint4 wg[2][CPL], wu[2][CPL];
-    // chunks past the row end reload the last chunk; their activations are
-    // zero, so they add exactly 0 -- no branch around the loads
-    auto load_rows = [&](int p, int buf) {
-      const int row = rb * 32 + wave * ROWS_PER_WAVE + p * RPP + rsub;
-      const uint4 *gp = reinterpret_cast<const uint4 *>(ep.wg + (size_t)row * row_bytes);
-      const uint4 *up = reinterpret_cast<const uint4 *>(ep.wu + (size_t)row * row_bytes);
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = min(gl + LPR * i, nchunks - 1);
-        wg[buf][i] = ld_nt(gp + c);
-        wu[buf][i] = ld_nt(up + c);
-      }
-    };
-    load_rows(0, 0);
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      if (p + 1 < PASSES) load_rows(p + 1, (p + 1) & 1);
-      const int buf = p & 1;
-      const int rl = wave * ROWS_PER_WAVE + p * RPP + rsub;  // row within the 32-row block
-      float pg[NT], pu[NT];
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        pg[tt] = 0.f;
-        pu[tt] = 0.f;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          pg[tt] += chunk_part<BITS>(wg[buf][i], act[i][tt]);
-          pu[tt] += chunk_part<BITS>(wu[buf][i], act[i][tt]);
-        }
-        pg[tt] = group_sum<LPR>(pg[tt]);
-        pu[tt] = group_sum<LPR>(pu[tt]);
-      }
-      const float sg = row_scale<RPP>(sgv, p, rsub), su = row_scale<RPP>(suv, p, rsub);
-      if (lane == group_sum_lane<LPR>(lane)) {
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) hs[tt][rl] = silu_f32(pg[tt] * sg) * (pu[tt] * su);
-      }
-    }
-    __syncthreads();
-    // Q8_0 of each token's 32 h values: thread -> (token tt, element i)
-    {
-      const int tt = threadIdx.x >> 5, i = threadIdx.x & 31;
-      if (tt < NT) {
-        const float h = hs[tt][i];
-        float amax = group_max<32>(fabsf(h));
-        amax = __shfl(amax, (lane & 32) | 31, 64);
-        if (t0 + tt < s.n_tok) {
-          int t, hrow, j;
-          tok_at(a, union_mode, s, t0 + tt, t, hrow, j);
-          const float db = amax / 127.f;
-          float c = 0.f;
-          if (db != 0.f) c = fminf(fmaxf(rintf(h / db), -127.f), 127.f);
-          a.hq[(size_t)hrow * I + rb * 32 + perm_dst<BITS>(i)] = (int8_t)c;
-          if (i == 0) a.hd[(size_t)hrow * (I / 32) + rb] = db;
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
 
 // Decode (T == 1): grid.x = (k+1) * (I/32).  Slot u < k is the u-th routed
 // expert of the token, which every routed workgroup selects itself from the
@@ -288,7 +62,7 @@ __global__ __launch_bounds__(256) void k_gateup_decode(FfnArgs a) {
   s.p0 = -1;
   s.slot = u;
   s.shared = (u == a.k);
-  gateup_body<BITS, LPR, CPL, 1>(a, false, expert_ptrs(a.L, e), s, rb, hs);
+  gateup_body<BITS, LPR, CPL, 1>(a, false, expert_ptrs(a.L, e), s, rb, hs, a.xq, a.xd);
 }
 
 // Union (T >= 2): grid.x = (max unique experts + 1) * (I/32).
@@ -300,7 +74,7 @@ __global__ __launch_bounds__(256) void k_gateup_union(FfnArgs a) {
   int e;
   TokList s;
   if (!union_item(a, u, e, s)) return;
-  gateup_body<BITS, LPR, CPL, NT>(a, true, expert_ptrs(a.L, e), s, rb, hs);
+  gateup_body<BITS, LPR, CPL, NT>(a, true, expert_ptrs(a.L, e), s, rb, hs, a.xq, a.xd);
 }
 
 // ---------------------------------------------------------------------------
@@ -500,6 +274,16 @@ static int pick_cpl(int nchunks, int lpr) {
     default: return hipErrorInvalidValue;                  \
   }
 
+// Tokens per register batch of the union kernels: every lane keeps the
+// activations of NT tokens for its CPL chunks in registers, so NT shrinks as
+// a chunk's activation (Act<BITS>) grows, keeping that set within ~100
+// registers (the kernels then need no spill registers).
+template <int BITS, int CPL>
+constexpr int union_nt() {
+  constexpr int regs = CPL * (Act<BITS>::kInts + Act<BITS>::kD);
+  return regs * 4 <= 100 ? 4 : regs * 2 <= 100 ? 2 : 1;
+}
+
 static int union_slots(const FfnArgs &a) {
   const long routed = (long)a.T * a.k;
   return (int)((routed < a.E ? routed : a.E) + 1);
@@ -513,7 +297,7 @@ hipError_t launch_gateup(const FfnArgs &a, bool union_mode, int /*mfma_min*/, hi
   const dim3 grid((unsigned)(slots * (a.L.I / 32))), block(256);
   COLI_BITS_SWITCH(a.L.bits, COLI_LPR_SWITCH(lpr, COLI_CPL_SWITCH(cpl, {
     if (union_mode)
-      COLI_LAUNCH(ev, (k_gateup_union<BITS, LPR, CPL, 4>), grid, block, 0, st, a);
+      COLI_LAUNCH(ev, (k_gateup_union<BITS, LPR, CPL, union_nt<BITS, CPL>()>), grid, block, 0, st, a);
     else
       COLI_LAUNCH(ev, (k_gateup_decode<BITS, LPR, CPL>), grid, block, 0, st, a);
   })));
@@ -537,7 +321,7 @@ hipError_t launch_down(const FfnArgs &a, bool union_mode, int /*mfma_min*/, hipS
     const int slots = union_slots(a);
     const dim3 grid((unsigned)(slots * (a.L.H / (4 * ROWS)))), block(256);
     COLI_BITS_SWITCH(a.L.bits, COLI_LPR_SWITCH(lpr, COLI_CPL_SWITCH(cpl, {
-      COLI_LAUNCH(ev, (k_down_union<BITS, LPR, CPL, 4, ROWS>), grid, block, 0, st, a);
+      COLI_LAUNCH(ev, (k_down_union<BITS, LPR, CPL, union_nt<BITS, CPL>(), ROWS>), grid, block, 0, st, a);
     })));
   }
   return hipGetLastError();

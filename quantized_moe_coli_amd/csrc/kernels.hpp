@@ -9,9 +9,14 @@
 
 #include <hip/hip_ext.h>
 
+#include "coli_moe.h"
 #include "device.hpp"
 
 namespace coli {
+
+// Bytes at the start of the forward workspace that hold the single-kernel
+// decode's counters (zero before first use, left zero by every call).
+constexpr int kDecodeCounterBytes = COLI_WORKSPACE_COUNTER_BYTES;
 
 // Optional per-kernel timing: events recorded by the launch itself at the
 // kernel's start and end (hipExtLaunchKernelGGL), so their interval is the
@@ -101,6 +106,15 @@ hipError_t launch_gateup(const FfnArgs &a, bool union_mode, int mfma_min, hipStr
 hipError_t launch_down(const FfnArgs &a, bool union_mode, int mfma_min, hipStream_t st,
                        KEvents ev = {});
 hipError_t launch_combine(const FfnArgs &a, hipStream_t st);
+
+// The whole layer for one token in one kernel (decode.hip).  `ctr` is the
+// workspace's state header (zero before the call; left zero after it).
+// gate_w null: logits_in holds the supplied logits; else the computed logits
+// are also written to logits_out when it is not null.  Returns
+// hipErrorNotSupported for row shapes the kernel is not built for.
+hipError_t launch_decode_fused(const FfnArgs &f, const float *x, const float *gate_w,
+                               const float *logits_in, float *logits_out, uint32_t *ctr,
+                               hipStream_t st, KEvents ev = {});
 
 hipError_t launch_debug_blocks(int bits, const uint8_t *Wq, int rows, int cols, const int8_t *xq_perm,
                                int T, int32_t *acc, hipStream_t st);

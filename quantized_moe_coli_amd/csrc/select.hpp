@@ -24,6 +24,14 @@ namespace coli {
 
 constexpr int kSelMaxE = 1024, kSelMaxK = 32, kSelEPL = kSelMaxE / 64;
 
+// sigma(l) evaluated in binary64, rounded once to binary32.
+__device__ __forceinline__ float sigmoid_f64(float l) {
+  return (float)(1.0 / (1.0 + exp(-(double)l)));
+}
+
+// A value every lane of the wave holds, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int uniform_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 template <int L>
 __device__ __forceinline__ int group_min_i32(int v) {
   if constexpr (L >= 2) v = min(v, dpp_i32<0xB1>(v));
@@ -100,7 +108,7 @@ __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *
     const int e = lane + 64 * m;
     c[m] = 0.f;
     if (m < epl) {
-      const float s = (float)(1.0 / (1.0 + exp(-(double)lv[m])));
+      const float s = sigmoid_f64(lv[m]);
       if (e < E) sc.sig[e] = s;
       c[m] = s + bv[m];
     }
@@ -246,6 +254,354 @@ __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+}  // namespace coli
+
+namespace coli {
+
+// ---------------------------------------------------------------------------
+// The same selection computed by a whole workgroup of NT threads, for the
+// latency-critical single-token path.  Instead of k rounds of wave arg-max it
+// counts, for every candidate of the kept groups, how many candidates beat it
+// (value desc, index asc): that count is the candidate's rank, a total order
+// identical to repeated arg-max, so the chosen experts, their slot order and
+// the weights are bit-identical to select_token.
+// ---------------------------------------------------------------------------
+// A token's router scores: sigma = fl32(sigmoid(logit)) and the biased
+// score c = sigma + bias, per expert.
+struct SelInput {
+  float c[kSelMaxE];
+  float sg[kSelMaxE];
+};
+
+struct SelWgScratch {
+  float candv[kSelMaxE];  // biased scores of the kept groups' experts
+  int cande[kSelMaxE];    // their expert ids
+  float gtop[64][2];      // two largest biased scores of each group
+  float gs[64];
+  int gkeep[64];          // kept group ids, in rank order
+  int slot[kSelMaxK];     // expert of each rank
+  float ssig[kSelMaxK];   // its sigmoid score
+  float pn[kSelMaxK];
+  int keep[kSelMaxK];
+  float sum;
+};
+
+// (v2, e2) beats (v, e): larger value, or equal value and lower index.
+__device__ __forceinline__ int beats(float v2, int e2, float v, int e) {
+  return (v2 > v || (v2 == v && e2 < e)) ? 1 : 0;
+}
+
+// `in`: the token's scores (typically in LDS).
+template <int NT>
+__device__ __forceinline__ void select_wg(const RouterCfg &cfg, const SelInput &in,
+                                          SelWgScratch &sc, int32_t *idx_out, float *w_out) {
+  const int tid = threadIdx.x;
+  const int E = cfg.E, k = cfg.k, G = cfg.n_group, per = E / G;
+  const float *cval = in.c, *sig = in.sg;
+  if (tid < kSelMaxK) sc.slot[tid] = -1;
+  if (tid < 64) sc.gkeep[tid] = tid < G ? tid : 0;  // valid ids even if NaN scores tie every rank
+  __syncthreads();
+
+  // groups: score = sum of the two largest biased scores (rank 0 and 1 of
+  // the group); keep the topk_group best groups
+  const bool all_groups = cfg.topk_group >= G;
+  if (!all_groups) {
+    for (int e = tid; e < E; e += NT) {
+      const int g = e / per, base = g * per;
+      const float v = cval[e];
+      int r = 0;
+      for (int q = base; q < base + per; ++q) r += beats(cval[q], q, v, e);
+      if (r < 2) sc.gtop[g][r] = v;
+    }
+    __syncthreads();
+    for (int g = tid; g < G; g += NT) sc.gs[g] = per >= 2 ? sc.gtop[g][0] + sc.gtop[g][1] : sc.gtop[g][0];
+    __syncthreads();
+    for (int g = tid; g < G; g += NT) {
+      const float v = sc.gs[g];
+      int r = 0;
+      for (int g2 = 0; g2 < G; ++g2) r += beats(sc.gs[g2], g2, v, g);
+      if (r < cfg.topk_group) sc.gkeep[r] = g;
+    }
+    __syncthreads();
+  }
+  const int ng = all_groups ? G : cfg.topk_group;
+
+  // the kept groups' experts, compacted
+  const int M = ng * per;
+  for (int m = tid; m < M; m += NT) {
+    const int gi = m / per;
+    const int e = (all_groups ? gi : sc.gkeep[gi]) * per + (m - gi * per);
+    sc.candv[m] = cval[e];
+    sc.cande[m] = e;
+  }
+  __syncthreads();
+
+  // rank of each candidate = number of candidates that beat it; P lanes of a
+  // wave share a candidate (P a power of two, P * candidates <= NT)
+  int P = 1;
+  while (P < 64 && 2 * P * M <= NT) P *= 2;
+  const int per_pass = NT / P;
+  for (int m0 = 0; m0 < M; m0 += per_pass) {
+    const int m = m0 + tid / P, part = tid % P;
+    const bool valid = m < M;
+    const float v = valid ? sc.candv[m] : 0.f;
+    const int e = valid ? sc.cande[m] : 0;
+    int r = 0;
+    if (valid)
+      for (int q = part; q < M; q += P) r += beats(sc.candv[q], sc.cande[q], v, e);
+    for (int o = 1; o < P; o *= 2) r += __shfl_xor(r, o, 64);
+    if (valid && part == 0 && r < k) {
+      sc.slot[r] = e;
+      sc.ssig[r] = sig[e];
+    }
+  }
+  __syncthreads();
+
+  // weights: the sums run in rank order (one thread), slot j by thread j
+  if (tid == 0) {
+    float S = 0.f;
+    for (int j = 0; j < k; ++j)
+      if (sc.slot[j] >= 0) S += sc.ssig[j];
+    sc.sum = S;
+  }
+  __syncthreads();
+  const float S = sc.sum;
+  int my_i = -1;
+  float my_w = 0.f, my_s = 0.f;
+  if (tid < k) {
+    my_i = sc.slot[tid];
+    if (my_i >= 0) {
+      my_s = sc.ssig[tid];
+      if (cfg.norm) my_w = (S != 0.f) ? (my_s / S) * cfg.rsf : 0.f;
+      else my_w = my_s * cfg.rsf;
+    }
+  }
+  if (cfg.top_p > 0.f && cfg.top_p < 1.f) {
+    if (tid < k) {
+      sc.pn[tid] = (S != 0.f && my_i >= 0) ? my_s / S : 0.f;
+      sc.keep[tid] = 0;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t seen = 0;
+      float cum = 0.f;
+      for (int n = 0; n < k; ++n) {
+        int best = -1;
+        for (int j = 0; j < k; ++j)
+          if (!((seen >> j) & 1u) && (best < 0 || sc.pn[j] > sc.pn[best])) best = j;
+        seen |= 1u << best;
+        sc.keep[best] = 1;
+        cum += sc.pn[best];
+        if (cum >= cfg.top_p) break;
+      }
+      float Sk = 0.f;
+      for (int j = 0; j < k; ++j)
+        if (sc.keep[j] && sc.slot[j] >= 0) Sk += sc.ssig[j];
+      sc.sum = Sk;
+    }
+    __syncthreads();
+    if (tid < k) {
+      const float Sk = sc.sum;
+      if (!sc.keep[tid] || my_i < 0) {
+        my_i = -1;
+        my_w = 0.f;
+      } else if (cfg.renorm) {
+        my_w = (Sk != 0.f) ? (my_s / Sk) * cfg.rsf : 0.f;
+      }
+    }
+  }
+  if (tid < k) {
+    idx_out[tid] = my_i;
+    w_out[tid] = my_w;
+  }
+  __syncthreads();
+}
+
+
+// ---------------------------------------------------------------------------
+// Fast form of the workgroup selection, for E <= NT experts in groups of
+// `per` that tile a wavefront (per divides 64) with at most 64 experts left
+// after the group step -- the GLM-5.2 router.  Only an expert ranked below
+// k inside its own group can be among the token's k (the top k of a union
+// of groups lie in the groups' own top k).  Thread e owns expert e: it
+// counts the members of its group that beat it (reading the group's scores
+// from LDS as broadcasts), every wave ranks the groups itself from their
+// DPP-reduced scores, the kept groups' top min(k, per) experts are ranked
+// by wave 0 the same way, and wave 0 computes the weights.  Same total order
+// (value desc, index asc) and the same binary32 operations in the same
+// order as select_token: bit-identical.
+// ---------------------------------------------------------------------------
+struct SelFastScratch {
+  __align__(16) float candv[64];  // biased scores of the candidates
+  __align__(16) int cande[64];    // their expert ids
+  float cands[64];                // their sigmoid scores
+  __align__(16) float gs[64];
+  __align__(16) int slot[kSelMaxK];
+  __align__(16) float ssig[kSelMaxK];
+};
+
+__host__ __device__ __forceinline__ bool select_fast_ok(int E, int G, int topk_group, int k,
+                                                        int nt) {
+  const int per = E / G;
+  const int ng = topk_group < G ? topk_group : G;
+  return E <= nt && per <= 64 && 64 % per == 0 && ng * (k < per ? k : per) <= 64;
+}
+
+__device__ __forceinline__ float rdlane(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Number of entries of v[0, N) (16-byte aligned, LDS) that beat (x, xi),
+// entry j carrying index base + j.  All loads are issued before the first
+// comparison.
+template <int N>
+__device__ __forceinline__ int count_beating(const float *v, int base, float x, int xi) {
+  int r = 0;
+  if constexpr (N >= 4) {
+    float4 q[N / 4];
+    const float4 *v4 = reinterpret_cast<const float4 *>(v);
+#pragma unroll
+    for (int j = 0; j < N / 4; ++j) q[j] = v4[j];
+#pragma unroll
+    for (int j = 0; j < N / 4; ++j) {
+      const int b = base + 4 * j;
+      r += (q[j].x > x || (q[j].x == x && b < xi)) ? 1 : 0;
+      r += (q[j].y > x || (q[j].y == x && b + 1 < xi)) ? 1 : 0;
+      r += (q[j].z > x || (q[j].z == x && b + 2 < xi)) ? 1 : 0;
+      r += (q[j].w > x || (q[j].w == x && b + 3 < xi)) ? 1 : 0;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) r += (v[j] > x || (v[j] == x && base + j < xi)) ? 1 : 0;
+  }
+  return r;
+}
+
+template <int NT, int PER>
+__device__ __forceinline__ void select_fast_t(const RouterCfg &cfg, const SelInput &in,
+                                              SelFastScratch &sc, int32_t *idx_out, float *w_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = cfg.E, k = cfg.k, G = cfg.n_group;
+  const int kk = k < PER ? k : PER;  // candidates per kept group
+  const bool valid = tid < E;
+  const int g = tid / PER;
+  const float c = valid ? in.c[tid] : -INFINITY;
+
+  // rank inside the group, and the group scores
+  const int rin = valid ? count_beating<PER>(in.c + g * PER, g * PER, c, tid) : 0;
+  unsigned long long gmask = G >= 64 ? ~0ull : ((1ull << G) - 1ull);
+  if (cfg.topk_group < G) {
+    float gsum;
+    if constexpr (PER == 1) gsum = c;
+    else gsum = seg_top2_sum<PER>(c);
+    if (valid && tid % PER == 0) sc.gs[g] = gsum;
+    __syncthreads();
+    // every wave ranks the groups (lane g2 < G holds group g2)
+    const float gv = lane < G ? sc.gs[lane] : 0.f;
+    int r = 0;
+#pragma unroll 8
+    for (int g2 = 0; g2 < G; ++g2) {
+      const float v2 = sc.gs[g2];  // broadcast read
+      r += (v2 > gv || (v2 == gv && g2 < lane)) ? 1 : 0;
+    }
+    gmask = __ballot(lane < G && r < cfg.topk_group);
+  }
+
+  // the kept groups' top kk experts, by group id then rank inside the group
+  if (valid && rin < kk && ((gmask >> g) & 1ull)) {
+    const int pos = __popcll(gmask & ((1ull << g) - 1ull)) * kk + rin;
+    sc.candv[pos] = c;
+    sc.cande[pos] = tid;
+    sc.cands[pos] = in.sg[tid];
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    // lane m < M holds candidate m; its rank among all candidates comes from
+    // wave-uniform lane reads (no memory round trips)
+    const int M = __popcll(gmask) * kk;
+    const bool cand = lane < M;
+    const float v = cand ? sc.candv[lane] : 0.f;
+    const int e = cand ? sc.cande[lane] : 0;
+    const float sgv = cand ? sc.cands[lane] : 0.f;
+    int r = 0;
+    for (int j = 0; j < M; ++j) {
+      const float v2 = rdlane(v, j);
+      const int e2 = __builtin_amdgcn_readlane(e, j);
+      r += (v2 > v || (v2 == v && e2 < e)) ? 1 : 0;
+    }
+    const bool win = cand && r < k;
+    // S = sum of the winners' sigma in rank (slot) order
+    float S = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const unsigned long long who = __ballot(win && r == j);
+      if (who) S += rdlane(sgv, __ffsll((long long)who) - 1);
+    }
+    float my_w;
+    if (cfg.norm) my_w = (S != 0.f) ? (sgv / S) * cfg.rsf : 0.f;
+    else my_w = sgv * cfg.rsf;
+    if (cfg.top_p > 0.f && cfg.top_p < 1.f) {
+      // slots by normalised weight (desc, slot order on ties) while the
+      // running binary32 sum is below p
+      const float pn = (S != 0.f && win) ? sgv / S : 0.f;
+      int rk = 0;
+      for (int j = 0; j < M; ++j) {
+        const bool wj = __builtin_amdgcn_readlane((int)win, j) != 0;
+        const float pj = rdlane(pn, j);
+        const int rj = __builtin_amdgcn_readlane(r, j);
+        rk += (wj && (pj > pn || (pj == pn && rj < r))) ? 1 : 0;
+      }
+      float cum = 0.f;
+      bool kept = false;
+      for (int q = 0; q < k; ++q) {
+        if (cum >= cfg.top_p) break;
+        const unsigned long long who = __ballot(win && rk == q);
+        if (!who) break;
+        const int src = __ffsll((long long)who) - 1;
+        if (lane == src) kept = true;
+        cum += rdlane(pn, src);
+      }
+      float Sk = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const unsigned long long who = __ballot(win && kept && r == j);
+        if (who) Sk += rdlane(sgv, __ffsll((long long)who) - 1);
+      }
+      if (win) {
+        if (!kept) {
+          idx_out[r] = -1;
+          w_out[r] = 0.f;
+        } else {
+          idx_out[r] = e;
+          w_out[r] = cfg.renorm ? ((Sk != 0.f) ? (sgv / Sk) * cfg.rsf : 0.f) : my_w;
+        }
+      }
+    } else if (win) {
+      idx_out[r] = e;
+      w_out[r] = my_w;
+    }
+  }
+  __syncthreads();
+}
+
+template <int NT>
+__device__ __forceinline__ void select_fast(const RouterCfg &cfg, const SelInput &in,
+                                            SelFastScratch &sc, int32_t *idx_out, float *w_out) {
+  // slots no candidate reaches (only with NaN scores) stay empty
+  if ((int)threadIdx.x < cfg.k) {
+    idx_out[threadIdx.x] = -1;
+    w_out[threadIdx.x] = 0.f;
+  }
+  switch (cfg.E / cfg.n_group) {
+    case 1: select_fast_t<NT, 1>(cfg, in, sc, idx_out, w_out); break;
+    case 2: select_fast_t<NT, 2>(cfg, in, sc, idx_out, w_out); break;
+    case 4: select_fast_t<NT, 4>(cfg, in, sc, idx_out, w_out); break;
+    case 8: select_fast_t<NT, 8>(cfg, in, sc, idx_out, w_out); break;
+    case 16: select_fast_t<NT, 16>(cfg, in, sc, idx_out, w_out); break;
+    case 32: select_fast_t<NT, 32>(cfg, in, sc, idx_out, w_out); break;
+    default: select_fast_t<NT, 64>(cfg, in, sc, idx_out, w_out); break;
+  }
 }
 
 }  // namespace coli

@@ -100,6 +100,16 @@ def test_forward_argument_checks():
                               _fake(0x300000), ws, None) == B.COLI_ERR_INVALID_ARG
 
 
+def test_counter_header_size_matches_c_header():
+    import pathlib
+    import re
+    h = (pathlib.Path(__file__).resolve().parents[1] / "include" / "coli_moe.h").read_text()
+    m = re.search(r"#define COLI_WORKSPACE_COUNTER_BYTES (\d+)", h)
+    assert m and int(m.group(1)) == B.WORKSPACE_COUNTER_BYTES
+    s = _layer_struct()
+    assert B.lib().coli_moe_workspace_bytes(ctypes.byref(s), 1) > B.WORKSPACE_COUNTER_BYTES
+
+
 def test_workspace_grows_with_tokens():
     L = B.lib()
     s = _layer_struct()

@@ -196,6 +196,12 @@ TINY_VARIANTS = {
     "tiny_grouped": inputs.TINY.with_(n_group=4, topk_group=2, top_k=4, bias_std=0.05, bits=4),
     "tiny_top_p": inputs.TINY.with_(n_group=4, topk_group=2, top_k=4, top_p=0.5, bits=4),
     "tiny_rsf1": inputs.TINY.with_(rsf=1.0),
+    # groups of 3 experts: the selection's general group path
+    "tiny_odd_groups": inputs.TINY.with_(n_experts=24, n_group=8, topk_group=3, top_k=5,
+                                         bias_std=0.05, bits=4),
+    # more experts than the decode workgroup has threads
+    "tiny_wide": inputs.TINY.with_(n_experts=640, n_group=10, topk_group=4, top_k=6,
+                                   bias_std=0.05, bits=2),
 }
 
 
@@ -223,9 +229,9 @@ def test_layer_tiny(tiny_pairs, name, T):
     assert_close_layer(y, y_r)
 
 
-def test_layer_tiny_supplied_logits(tiny_pairs):
+@pytest.mark.parametrize("T", [1, 9])
+def test_layer_tiny_supplied_logits(tiny_pairs, T):
     p = _pair(tiny_pairs, "tiny_grouped")
-    T = 9
     x = inputs.tokens(p.s, 0, 7, T)
     lg = inputs.correlated_logits(3, T, p.s.n_experts, 0.5).numpy()
     y_r, idx_r, w_r, _ = p.oracle_forward(x.numpy(), lg)
@@ -281,6 +287,46 @@ def test_determinism(tiny_pairs):
         np.testing.assert_array_equal(u, v)
 
 
+def test_decode_workspace_reuse(tiny_pairs):
+    """Many single-token calls on one workspace (the decode kernel's counters
+    must return to zero after every call) match calls on fresh workspaces."""
+    p = _pair(tiny_pairs, "tiny_grouped")
+    ws = B.workspace(p.gpu, 1)
+    x = inputs.tokens(p.s, 0, 77, 40).cuda()
+    for t in range(40):
+        a = p.gpu_forward(x[t:t + 1].contiguous(), ws=ws)
+        b = p.gpu_forward(x[t:t + 1].contiguous())
+        for u, v in zip(a, b):
+            np.testing.assert_array_equal(u, v)
+    hdr = ws[:B.WORKSPACE_COUNTER_BYTES].cpu().numpy()
+    assert (hdr == 0).all()
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_graph_replay_matches_eager(tiny_pairs, T):
+    """The forward captured in a HIP graph and replayed several times, with
+    eager work between replays, gives the eager result every time."""
+    p = _pair(tiny_pairs, "tiny_int4")
+    s = p.s
+    x = inputs.tokens(s, 0, 88 + T, T).cuda()
+    ref = p.gpu_forward(x)[0]
+    ws = B.workspace(p.gpu, T)
+    y = torch.empty(T, s.hidden, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            B.coli_moe_forward(p.gpu, x, y, ws)
+    torch.cuda.synchronize()
+    for rep in range(5):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), ref, err_msg=f"replay {rep}")
+        p.gpu_forward(inputs.tokens(s, 0, 500 + rep, 2).cuda())  # eager work in between
+
+
 # ------------------------------------------------ GLM-5.2-shaped layer --
 @pytest.fixture(scope="module")
 def glm():
@@ -331,3 +377,28 @@ def test_glm_union_sampled(glm, T):
     for t in (0, T // 2, T - 1):
         y_r, _, _, _ = glm.oracle_forward(xh[t:t + 1])
         assert_close_layer(y[t:t + 1], y_r)
+
+
+# GLM-5.2 row shapes (H 6144, I 2048) in the int8 and int2 containers, with
+# 16 experts so the layer packs quickly: the decode kernel's other row
+# layouts and the union path at full row length.
+@pytest.fixture(scope="module")
+def glm_rows():
+    return {}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("bits", [8, 2])
+@pytest.mark.parametrize("T", [1, 3])
+def test_glm_rows_other_containers(glm_rows, bits, T):
+    if bits not in glm_rows:
+        s = inputs.GLM.with_(n_experts=16, top_k=4, n_group=4, topk_group=2, bits=bits)
+        glm_rows[bits] = LayerPair(s, seed=3, device_gen=True)
+    p = glm_rows[bits]
+    x = inputs.tokens(p.s, 0, 40 + T, T, "cuda")
+    y, idx, w, lg = p.gpu_forward(x)
+    y_r, idx_r, w_r, lg_r = p.oracle_forward(x.cpu().numpy())
+    assert ulp_diff(lg, lg_r).max() <= 1
+    np.testing.assert_array_equal(idx, idx_r)
+    np.testing.assert_array_equal(w, w_r)
+    assert_close_layer(y, y_r)
