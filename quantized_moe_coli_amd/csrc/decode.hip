@@ -67,7 +67,7 @@ constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr uint32_t kSpinLimit = 1u << 19;  // ~100 ms of polling
 constexpr int kLogRows = 2;                // logit rows per L item (four waves each)
-constexpr int kGuRows = 64;                // gate/up rows per GS/GR item
+constexpr int kGuRows = 32;                // gate/up rows per GS/GR item
 
 struct DecodeArgs {
   FfnArgs f;
@@ -239,16 +239,35 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
       wait_ge(d.ctr + kCtrSlot0 + sl * kCtrStride, (uint32_t)(I / kGuRows));
     }
     {
-      const int wq = I / 4, wd = I / 32;  // code words and scales per slot
-      for (int i = threadIdx.x; i < gn * (wq + wd); i += kDecThreads) {
-        const int q = i / (wq + wd), r = i - q * (wq + wd);
-        const int sl = g0 + q == 0 ? k : g0 + q - 1;
-        if (r < wq)
-          reinterpret_cast<uint32_t *>(lds_q + (size_t)q * I)[r] =
-              ld_dev(reinterpret_cast<const uint32_t *>(a.hq + (size_t)sl * I) + r);
-        else
-          lds_d[q * wd + (r - wq)] =
-              __uint_as_float(ld_dev(reinterpret_cast<const uint32_t *>(a.hd) + (size_t)sl * wd + (r - wq)));
+      // 64-bit device-scope loads, kStage per thread issued before any is
+      // written to LDS
+      constexpr int kStage = 2;
+      const int wq = I / 8, wd = I / 64;  // 8-byte words of codes and scales per slot
+      const int n = gn * (wq + wd);
+      for (int i0 = 0; i0 < n; i0 += kStage * kDecThreads) {
+        uint64_t v[kStage];
+#pragma unroll
+        for (int j = 0; j < kStage; ++j) {
+          const int i = i0 + j * kDecThreads + threadIdx.x;
+          v[j] = 0;
+          if (i < n) {
+            const int q = i / (wq + wd), r = i - q * (wq + wd);
+            const int sl = g0 + q == 0 ? k : g0 + q - 1;
+            const uint64_t *src = r < wq ? reinterpret_cast<const uint64_t *>(a.hq + (size_t)sl * I) + r
+                                         : reinterpret_cast<const uint64_t *>(a.hd + (size_t)sl * (I / 32)) + (r - wq);
+            v[j] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kStage; ++j) {
+          const int i = i0 + j * kDecThreads + threadIdx.x;
+          if (i < n) {
+            const int q = i / (wq + wd), r = i - q * (wq + wd);
+            uint64_t *dst = r < wq ? reinterpret_cast<uint64_t *>(lds_q + (size_t)q * I) + r
+                                   : reinterpret_cast<uint64_t *>(lds_d + q * (I / 32)) + (r - wq);
+            *dst = v[j];
+          }
+        }
       }
     }
     __syncthreads();
