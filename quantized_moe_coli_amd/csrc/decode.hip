@@ -234,10 +234,17 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
     }
     // once every gate/up item of the group's slots is done, stage their h
     // codes and scales in LDS (device-scope loads, all in flight together)
-    for (int q = 0; q < gn; ++q) {
+    if ((int)threadIdx.x < gn) {
+      const int q = threadIdx.x;
       const int sl = g0 + q == 0 ? k : g0 + q - 1;
-      wait_ge(d.ctr + kCtrSlot0 + sl * kCtrStride, (uint32_t)(I / kGuRows));
+      const uint32_t *c = d.ctr + kCtrSlot0 + sl * kCtrStride;
+      uint32_t it = 0;
+      while (ld_ctr(c) < (uint32_t)(I / kGuRows) && it < kSpinLimit) {
+        __builtin_amdgcn_s_sleep(64);
+        ++it;
+      }
     }
+    __syncthreads();
     {
       // 64-bit device-scope loads, kStage per thread issued before any is
       // written to LDS
