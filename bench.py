@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+MFMA_MIN_DEFAULT = 8  # the library's default mfma_min_tokens
 INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, published
 
 
@@ -170,7 +171,7 @@ def main() -> int:
     # stream; each launch of the front, gate/up and down kernels records a
     # start and a stop hipEvent itself (hipExtLaunchKernelGGL)
     hip = _hip()
-    n_ev = 6
+    n_ev = 10
     evs = []
     for _ in range(K * n_ev):
         e = ctypes.c_void_p()
@@ -192,11 +193,16 @@ def main() -> int:
             return float("nan")
         return v.value
 
-    n_k = 1 if T == 1 else 3  # decode: one fused kernel; union: front, gate/up, down
+    # decode: one fused kernel; union: front, gate/up and down on the
+    # dot-product path, gate/up and down on the matrix cores
+    n_k = 1 if T == 1 else 5
     stage = np.array([[el(evs[st * n_ev + 2 * i], evs[st * n_ev + 2 * i + 1]) for i in range(n_k)]
                       for st in range(K)])  # ms
-    span = np.array([el(evs[st * n_ev], evs[st * n_ev + 2 * n_k - 1]) for st in range(K)])
-    eager_ms = el(evs[0], evs[(K - 1) * n_ev + 2 * n_k - 1])
+    # the last kernel that ran (the matrix-core kernels are skipped for
+    # batches below mfma_min tokens)
+    last = n_k - 1 if np.isfinite(stage[:, n_k - 1]).all() else min(n_k - 1, 2)
+    span = np.array([el(evs[st * n_ev], evs[st * n_ev + 2 * last + 1]) for st in range(K)])
+    eager_ms = el(evs[0], evs[(K - 1) * n_ev + 2 * last + 1])
     for e in evs:
         hip.hipEventDestroy(ctypes.c_void_p(e))
     hip.hipGetLastError()
@@ -206,21 +212,26 @@ def main() -> int:
     eb = expert_bytes(s)
     gate_bytes = 0 if supplied else s.n_experts * s.hidden * 4
 
-    # algorithmic bytes: the unique experts each step reads (+ the shared one)
+    # algorithmic bytes: the unique experts each step reads (+ the shared
+    # one); in a union batch, experts with at least mfma_min tokens (and the
+    # shared expert when T >= mfma_min) run on the matrix cores
+    mfma_min = layers[0].mfma_min_tokens or MFMA_MIN_DEFAULT
     if T == 1:
         uniq = np.full(K, s.top_k, dtype=np.float64)
+        n_mfma = np.zeros(K)
     else:
-        uniq = []
+        uniq, n_mfma = [], []
         for st in range(K):
             idx = torch.empty(T, s.top_k, dtype=torch.int32, device=dev)
             B.coli_moe_route(cfg, lgs[st], layers[st % NI].gate_bias, idx,
                              torch.empty(T, s.top_k, device=dev))
-            uniq.append(len(torch.unique(idx[idx >= 0])))
+            cnt = torch.bincount(idx[idx >= 0].long(), minlength=s.n_experts)
+            uniq.append(int((cnt > 0).sum()))
+            n_mfma.append(int((cnt >= mfma_min).sum()) + (1 if T >= mfma_min else 0))
         uniq = np.array(uniq, dtype=np.float64)
+        n_mfma = np.array(n_mfma, dtype=np.float64)
     act_bytes = T * s.hidden * 4 * 2  # x in, y out
     layer_bytes = (uniq + 1) * eb["total"] + gate_bytes + act_bytes
-    gu_bytes = (uniq + 1) * eb["gate_up"]
-    down_bytes = (uniq + 1) * eb["down"]
     avg = stage.mean(axis=0)
     layer_gbps = float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9
     if T == 1:  # the dominant (only) kernel is the fused decode kernel
@@ -228,9 +239,19 @@ def main() -> int:
         dom_ms = float(avg[0])
         dom_bytes = float(np.mean(layer_bytes))
     else:
-        dom_name = "k_gateup_union (gate/up GEMV + SwiGLU + Q8_0 of h)"
-        dom_ms = float(avg[1])
-        dom_bytes = float(np.mean(gu_bytes))
+        # each kernel's bytes: the expert weights of the slots it runs
+        n_dot = uniq + 1 - n_mfma
+        kbytes = {1: n_dot * eb["gate_up"], 2: n_dot * eb["down"],
+                  3: n_mfma * eb["gate_up"], 4: n_mfma * eb["down"]}
+        knames = {1: "k_gateup_union (gate/up dot-product GEMV + SwiGLU + Q8_0 of h)",
+                  2: "k_down_union (down dot-product GEMV)",
+                  3: "k_gateup_mfma (gate/up on the int8 matrix cores + SwiGLU + Q8_0 of h)",
+                  4: "k_down_mfma (down on the int8 matrix cores)"}
+        dom = max((1, 2, 3, 4), key=lambda i: np.nan_to_num(avg[i]))
+        avg = np.nan_to_num(avg)
+        dom_name = knames[dom]
+        dom_ms = float(avg[dom])
+        dom_bytes = float(np.mean(kbytes[dom]))
     dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
     log(f"[bench] {args.workload}: {K} steps in {total_ms:.3f} ms (wall {wall * 1e3:.1f} ms): "
         f"{ms_per_step * 1e3:.2f} us/step, {tokens_per_s:.0f} tokens/s")
@@ -240,9 +261,11 @@ def main() -> int:
     if T == 1:
         log(f"[bench] kernel mean (us): k_decode_fused {avg[0] * 1e3:.2f}")
     else:
-        log(f"[bench] kernel means (us): front (act quant + logits) {avg[0] * 1e3:.2f}, gate/up "
-            f"{avg[1] * 1e3:.2f} ({float(np.mean(gu_bytes)) / (avg[1] * 1e-3) / 1e9:.0f} GB/s), down "
-            f"{avg[2] * 1e3:.2f} ({float(np.mean(down_bytes)) / (avg[2] * 1e-3) / 1e9:.0f} GB/s)")
+        gbs = {i: float(np.mean(kbytes[i])) / (avg[i] * 1e-3) / 1e9 for i in (1, 2, 3, 4)}
+        log(f"[bench] kernel means (us): front {avg[0] * 1e3:.2f}; dot-product path gate/up "
+            f"{avg[1] * 1e3:.2f} ({gbs[1]:.0f} GB/s), down {avg[2] * 1e3:.2f} ({gbs[2]:.0f} GB/s); "
+            f"matrix cores gate/up {avg[3] * 1e3:.2f} ({gbs[3]:.0f} GB/s), down {avg[4] * 1e3:.2f} "
+            f"({gbs[4]:.0f} GB/s); experts on the matrix cores/step {n_mfma.mean():.1f}")
     log(f"[bench] unique experts/step {uniq.mean():.1f}; layer bytes/step "
         f"{np.mean(layer_bytes) / 1e6:.2f} MB -> {layer_gbps:.0f} GB/s "
         f"({100 * layer_gbps / HBM_PEAK_GBPS:.1f}% of HBM peak); dominant kernel "
@@ -273,8 +296,10 @@ def main() -> int:
             "launch": "one HIP graph of the K timed steps",
             "kernel_us": ({"k_decode_fused": round(float(avg[0]) * 1e3, 3)} if T == 1 else
                           {"front": round(float(avg[0]) * 1e3, 3),
-                           "gate_up": round(float(avg[1]) * 1e3, 3),
-                           "down": round(float(avg[2]) * 1e3, 3)}),
+                           "gate_up_dot": round(float(avg[1]) * 1e3, 3),
+                           "down_dot": round(float(avg[2]) * 1e3, 3),
+                           "gate_up_mfma": round(float(avg[3]) * 1e3, 3),
+                           "down_mfma": round(float(avg[4]) * 1e3, 3)}),
         },
         "roofline": {
             "bound": "hbm",

@@ -80,9 +80,11 @@ typedef struct {
  * w_down [E][H][I*b/8], s_down [E][H].  The shared expert has the same
  * per-expert layouts (E = 1).  Every weight row must start 16-byte aligned
  * (holds for any 16-byte aligned base since H*b/8 and I*b/8 are multiples of
- * 16).  H and I are multiples of 64, at most 8192.  mfma_min_tokens: a unique expert receiving at least
- * this many tokens of a batch runs on the int8 matrix cores, fewer on the
- * integer dot-product GEMV; 0 selects the library default. */
+ * 16).  H and I are multiples of 64, at most 8192.  mfma_min_tokens: in a
+ * batch of T >= 2 tokens, a unique expert (or the shared expert) receiving at
+ * least this many tokens runs on the int8 matrix cores, one with fewer on the
+ * integer dot-product GEMV; 0 selects the library default (8).  Both give
+ * the same results up to fp32 summation order. */
 typedef struct {
   int32_t hidden;   /* H: 6144 */
   int32_t inter;    /* I: 2048 */
@@ -193,9 +195,14 @@ coli_status coli_moe_forward(const coli_moe_layer *L, const float *x,
  * benchmark.  stage_events holds n_stage_events caller-created hipEvent_t
  * handles (NULL entries skipped): [2i] and [2i+1] are recorded by the launch
  * of kernel i itself at its start and end (so their interval is that
- * kernel's execution time).  T = 1: kernel 0 is the single decode kernel.
- * T >= 2: kernel 0 the front kernel (activation quantisation + logits), 1
- * the gate/up kernel, 2 the down-projection kernel. */
+ * kernel's execution time).  T = 1: kernel 0 is the single decode kernel
+ * (for row shapes it is not built for: as below, kernels 0-2).  T >= 2:
+ * kernel 0 the front kernel (activation quantisation + logits), 1 the
+ * gate/up and 2 the down-projection kernel of the dot-product path, 3 the
+ * gate/up and 4 the down-projection kernel of the matrix-core path (a
+ * kernel with no work records an empty interval; the matrix-core kernels
+ * are not launched, and their events not recorded, when T is below the
+ * layer's mfma_min_tokens). */
 coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x,
                                       int32_t T, const float *logits_in,
                                       float *y, int32_t *idx_out, float *w_out,

@@ -77,7 +77,7 @@ coli::RouterCfg to_cfg(const coli_router_cfg &c) {
 }
 
 struct WsLayout {
-  size_t ctr, xq, xd, logits, idx, w, counts, offs, perm, uniq, nuniq, hq, hd, obuf, total;
+  size_t ctr, xq, xd, logits, idx, w, counts, offs, perm, uniq, nuniq, mgofs, hq, hd, obuf, total;
 };
 
 WsLayout ws_layout(const coli_moe_layer *L, int Tmax) {
@@ -101,6 +101,7 @@ WsLayout ws_layout(const coli_moe_layer *L, int Tmax) {
   w.perm = take(T * k * 4);
   w.uniq = take(E * 4);
   w.nuniq = take(4);
+  w.mgofs = take((E + 2) * 4);
   w.hq = take((T * k + T) * I);
   w.hd = take((T * k + T) * (I / 32) * 4);
   w.obuf = take(Tmax >= 2 ? T * (k + 1) * H * 4 : 0);
@@ -302,9 +303,16 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
     int32_t *nuniq = reinterpret_cast<int32_t *>(base + ws.nuniq);
     e = coli::launch_dispatch(idx, T, k, E, counts, offs, perm, uniq, nuniq, s);
     if (e != hipSuccess) return COLI_ERR_DEVICE;
-    fa.disp = coli::Dispatch{counts, offs, perm, uniq, nuniq};
-    e = coli::launch_gateup(fa, true, mfma_min, s, kev(1));
+    int32_t *mgofs = reinterpret_cast<int32_t *>(base + ws.mgofs);
+    fa.disp = coli::Dispatch{counts, offs, perm, uniq, nuniq, mgofs};
+    fa.mfma_min = mfma_min > 0 ? mfma_min : coli::kMfmaMinDefault;
+    // no slot of a batch smaller than mfma_min tokens can reach the matrix cores
+    const bool mfma = T >= fa.mfma_min;
+    if (mfma) e = coli::launch_mfma_items(fa, mgofs, s);
+    if (e == hipSuccess) e = coli::launch_gateup(fa, true, mfma_min, s, kev(1));
+    if (e == hipSuccess && mfma) e = coli::launch_gateup_mfma(fa, s, kev(3));
     if (e == hipSuccess) e = coli::launch_down(fa, true, mfma_min, s, kev(2));
+    if (e == hipSuccess && mfma) e = coli::launch_down_mfma(fa, s, kev(4));
     if (e == hipSuccess) e = coli::launch_combine(fa, s);
     return from_hip(e);
   });

@@ -24,6 +24,8 @@
 // mode runs one expert over its tokens and writes o into a per-(token, slot)
 // buffer that a combine kernel reduces in the same fixed order.  No
 // floating-point atomics: results are bit-reproducible.
+#include <algorithm>
+
 #include "ffn_common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
@@ -65,16 +67,20 @@ __global__ __launch_bounds__(256) void k_gateup_decode(FfnArgs a) {
   gateup_body<BITS, LPR, CPL, 1>(a, false, expert_ptrs(a.L, e), s, rb, hs, a.xq, a.xd);
 }
 
-// Union (T >= 2): grid.x = (max unique experts + 1) * (I/32).
+// Union (T >= 2): items (union slot u, 32-row block rb) for u up to the
+// largest possible slot count, grid-strided (slots the matrix-core kernels
+// take, or past the last unique expert, are skipped).
 template <int BITS, int LPR, int CPL, int NT>
-__global__ __launch_bounds__(256) void k_gateup_union(FfnArgs a) {
+__global__ __launch_bounds__(256) void k_gateup_union(FfnArgs a, int n_items) {
   __shared__ float hs[NT][32];
   const int n_rb = a.L.I / 32;
-  const int u = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
-  int e;
-  TokList s;
-  if (!union_item(a, u, e, s)) return;
-  gateup_body<BITS, LPR, CPL, NT>(a, true, expert_ptrs(a.L, e), s, rb, hs, a.xq, a.xd);
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int u = item / n_rb, rb = item % n_rb;
+    int e;
+    TokList s;
+    if (!union_item(a, u, e, s)) continue;
+    gateup_body<BITS, LPR, CPL, NT>(a, true, expert_ptrs(a.L, e), s, rb, hs, a.xq, a.xd);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -149,17 +155,17 @@ __global__ __launch_bounds__(768) void k_down_decode(FfnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Down, union mode.  grid.x = slots * (H / (4*ROWS)); each wave owns ROWS
-// rows of one expert and runs every token of the expert on them (NT at a
-// time), writing o to obuf[t][j][row].
+// Down, union mode.  Items (slot, block of 4*ROWS rows), grid-strided; each
+// wave owns ROWS rows of one expert and runs every token of the expert on
+// them (NT at a time), writing o to obuf[t][j][row].
 // ---------------------------------------------------------------------------
 template <int BITS, int LPR, int CPL, int NT, int ROWS>
-__global__ __launch_bounds__(256) void k_down_union(FfnArgs a) {
+__device__ __forceinline__ void down_union_item(const FfnArgs &a, int item) {
   constexpr int RPP = 64 / LPR;
   constexpr int PASSES = ROWS / RPP;
   const int H = a.L.H, I = a.L.I;
   const int n_rb = H / (4 * ROWS);
-  const int u = blockIdx.x / n_rb, rb = blockIdx.x % n_rb;
+  const int u = item / n_rb, rb = item % n_rb;
   int e;
   TokList s;
   if (!union_item(a, u, e, s)) return;
@@ -218,6 +224,12 @@ __global__ __launch_bounds__(256) void k_down_union(FfnArgs a) {
       }
     }
   }
+}
+
+template <int BITS, int LPR, int CPL, int NT, int ROWS>
+__global__ __launch_bounds__(256) void k_down_union(FfnArgs a, int n_items) {
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x)
+    down_union_item<BITS, LPR, CPL, NT, ROWS>(a, item);
 }
 
 // y[t][r] = o_shared + sum over kept slots j (in order) of w_tj * o_tj.
@@ -284,6 +296,9 @@ constexpr int union_nt() {
   return regs * 4 <= 100 ? 4 : regs * 2 <= 100 ? 2 : 1;
 }
 
+// Workgroups of a union GEMV launch (8 per CU); more items are strided.
+constexpr int kUnionGrid = 2048;
+
 static int union_slots(const FfnArgs &a) {
   const long routed = (long)a.T * a.k;
   return (int)((routed < a.E ? routed : a.E) + 1);
@@ -294,10 +309,12 @@ hipError_t launch_gateup(const FfnArgs &a, bool union_mode, int /*mfma_min*/, hi
   const int nch = a.L.H * a.L.bits / 128;
   const int lpr = pick_lpr(nch), cpl = pick_cpl(nch, lpr);
   const int slots = union_mode ? union_slots(a) : a.k + 1;
-  const dim3 grid((unsigned)(slots * (a.L.I / 32))), block(256);
+  const int n_items = slots * (a.L.I / 32);
+  const dim3 grid((unsigned)(union_mode ? std::min(n_items, kUnionGrid) : n_items)), block(256);
   COLI_BITS_SWITCH(a.L.bits, COLI_LPR_SWITCH(lpr, COLI_CPL_SWITCH(cpl, {
     if (union_mode)
-      COLI_LAUNCH(ev, (k_gateup_union<BITS, LPR, CPL, union_nt<BITS, CPL>()>), grid, block, 0, st, a);
+      COLI_LAUNCH(ev, (k_gateup_union<BITS, LPR, CPL, union_nt<BITS, CPL>()>), grid, block, 0, st, a,
+                  n_items);
     else
       COLI_LAUNCH(ev, (k_gateup_decode<BITS, LPR, CPL>), grid, block, 0, st, a);
   })));
@@ -319,9 +336,11 @@ hipError_t launch_down(const FfnArgs &a, bool union_mode, int /*mfma_min*/, hipS
   } else {
     constexpr int ROWS = 8;
     const int slots = union_slots(a);
-    const dim3 grid((unsigned)(slots * (a.L.H / (4 * ROWS)))), block(256);
+    const int n_items = slots * (a.L.H / (4 * ROWS));
+    const dim3 grid((unsigned)std::min(n_items, kUnionGrid)), block(256);
     COLI_BITS_SWITCH(a.L.bits, COLI_LPR_SWITCH(lpr, COLI_CPL_SWITCH(cpl, {
-      COLI_LAUNCH(ev, (k_down_union<BITS, LPR, CPL, union_nt<BITS, CPL>(), ROWS>), grid, block, 0, st, a);
+      COLI_LAUNCH(ev, (k_down_union<BITS, LPR, CPL, union_nt<BITS, CPL>(), ROWS>), grid, block, 0, st, a,
+                  n_items);
     })));
   }
   return hipGetLastError();

@@ -117,7 +117,8 @@ __device__ __forceinline__ void tok_at(const FfnArgs &a, bool union_mode, const 
   }
 }
 
-// Union item u -> expert and token list; false past the last unique expert.
+// Union item u -> expert and token list; false past the last unique expert
+// and for slots the matrix-core kernels take.
 __device__ __forceinline__ bool union_item(const FfnArgs &a, int u, int &e, TokList &s) {
   const int nu = *a.disp.n_uniq;
   if (u > nu) return false;
@@ -132,7 +133,7 @@ __device__ __forceinline__ bool union_item(const FfnArgs &a, int u, int &e, TokL
     s.p0 = a.disp.offs[e];
     s.n_tok = a.disp.offs[e + 1] - s.p0;
   }
-  return true;
+  return s.n_tok < a.mfma_min;
 }
 
 // ---------------------------------------------------------------------------

@@ -58,12 +58,13 @@ struct Dispatch {
   const int32_t *perm;    // [T*k] entries t*k+j ordered by (expert, t, j)
   const int32_t *uniq;    // [E]
   const int32_t *n_uniq;  // [1]
+  const int32_t *mgofs;   // [n_uniq+2] first matrix-core token group of each union slot
 };
 
 hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t cols, uint8_t *q,
                              float *scale, hipStream_t st);
 hipError_t launch_act_quant(int layout_bits, const float *x, int64_t T, int64_t n, int8_t *q,
-                            float *d, hipStream_t st);
+                            float *d, hipStream_t st, KEvents ev = {});
 
 hipError_t launch_logits(const float *x, const float *gate_w, int T, int E, int H, float *logits,
                          hipStream_t st);
@@ -99,13 +100,24 @@ struct FfnArgs {
   float *hd;            // [rows][I/32]
   float *obuf;          // union: [T][k+1][H]
   float *y;             // [T][H]
+  int mfma_min;         // union: slots with at least this many tokens run on the matrix cores
 };
+
+constexpr int kMfmaTokens = 64;  // tokens per matrix-core work item
+constexpr int kMfmaMinDefault = 8;  // default token count from which an expert runs on MFMA
 
 hipError_t launch_gateup(const FfnArgs &a, bool union_mode, int mfma_min, hipStream_t st,
                          KEvents ev = {});
 hipError_t launch_down(const FfnArgs &a, bool union_mode, int mfma_min, hipStream_t st,
                        KEvents ev = {});
 hipError_t launch_combine(const FfnArgs &a, hipStream_t st);
+
+// Union slots with at least a.mfma_min tokens run on the int8 matrix cores
+// (mfma.hip): the item table after the dispatch tables, then gate/up and
+// down; the dot-product kernels skip those slots.
+hipError_t launch_mfma_items(const FfnArgs &a, int32_t *mgofs, hipStream_t st);
+hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t st, KEvents ev = {});
+hipError_t launch_down_mfma(const FfnArgs &a, hipStream_t st, KEvents ev = {});
 
 // The whole layer for one token in one kernel (decode.hip).  `ctr` is the
 // workspace's state header (zero before the call; left zero after it).

@@ -74,14 +74,14 @@ hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t col
 }
 
 hipError_t launch_act_quant(int layout_bits, const float *x, int64_t T, int64_t n, int8_t *q,
-                            float *d, hipStream_t st) {
+                            float *d, hipStream_t st, KEvents ev) {
   const int64_t blocks = T * (n / 32);
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)((blocks + 255) / 256)), block(256);
   switch (layout_bits) {
-    case 8: hipLaunchKernelGGL(k_act_quant<8>, grid, block, 0, st, x, T, n, q, d); break;
-    case 4: hipLaunchKernelGGL(k_act_quant<4>, grid, block, 0, st, x, T, n, q, d); break;
-    case 2: hipLaunchKernelGGL(k_act_quant<2>, grid, block, 0, st, x, T, n, q, d); break;
+    case 8: COLI_LAUNCH(ev, k_act_quant<8>, grid, block, 0, st, x, T, n, q, d); break;
+    case 4: COLI_LAUNCH(ev, k_act_quant<4>, grid, block, 0, st, x, T, n, q, d); break;
+    case 2: COLI_LAUNCH(ev, k_act_quant<2>, grid, block, 0, st, x, T, n, q, d); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

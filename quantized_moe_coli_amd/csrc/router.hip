@@ -173,13 +173,15 @@ hipError_t launch_front(int bits, const float *x, const float *gate_w, int T, in
     }
     return hipGetLastError();
   }
+  // the kernel events time the logits kernel, or the activation
+  // quantisation when the logits are supplied
   if (gate_w) {
     const dim3 grid((E + 127) / 128, (T + 31) / 32), block(256);
     COLI_LAUNCH(ev, k_logits_mfma, grid, block, 0, st, x, gate_w, T, E, H, logits);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (xq) return launch_act_quant(bits, x, T, H, xq, xd, st);
+  if (xq) return launch_act_quant(bits, x, T, H, xq, xd, st, gate_w ? KEvents{} : ev);
   return hipSuccess;
 }
 

@@ -402,3 +402,54 @@ def test_glm_rows_other_containers(glm_rows, bits, T):
     np.testing.assert_array_equal(idx, idx_r)
     np.testing.assert_array_equal(w, w_r)
     assert_close_layer(y, y_r)
+
+
+# The matrix-core union path (experts with at least mfma_min_tokens tokens
+# run on v_mfma_i32_16x16x32_i8) against the oracle, with every slot forced
+# onto it (min 1), with none on it (min large), and at the library default.
+@pytest.fixture(scope="module")
+def mfma_pairs():
+    return {}
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("mfma_min", [1, 0, 1 << 30])
+@pytest.mark.parametrize("T", [2, 33, 130])
+def test_union_matrix_cores(mfma_pairs, bits, mfma_min, T):
+    key = (bits, mfma_min)
+    if key not in mfma_pairs:
+        s = inputs.TINY.with_(n_experts=16, top_k=4, n_group=4, topk_group=2, bias_std=0.05,
+                              bits=bits)
+        mfma_pairs[key] = LayerPair(s, seed=5, mfma_min_tokens=mfma_min)
+    p = mfma_pairs[key]
+    x = inputs.tokens(p.s, 0, 300 + T, T)
+    y_r, idx_r, w_r, _ = p.oracle_forward(x.numpy())
+    y, idx, w, _ = p.gpu_forward(x.cuda())
+    np.testing.assert_array_equal(idx, idx_r)
+    np.testing.assert_array_equal(w, w_r)
+    assert_close_layer(y, y_r)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("bits", [4, 2])
+def test_glm_rows_matrix_cores(glm_rows, bits):
+    """GLM-5.2 row lengths on the matrix cores: 96 tokens over 16 experts
+    (about 24 per expert, shared expert 96) with every slot on MFMA."""
+    if bits not in glm_rows:
+        s = inputs.GLM.with_(n_experts=16, top_k=4, n_group=4, topk_group=2, bits=bits)
+        glm_rows[bits] = LayerPair(s, seed=3, device_gen=True)
+    p = glm_rows[bits]
+    p.gpu.mfma_min_tokens = 1
+    try:
+        T = 96
+        x = inputs.tokens(p.s, 0, 900, T, "cuda")
+        y, idx, w, lg = p.gpu_forward(x)
+        xh = x.cpu().numpy()
+        lg_r = oracle.logits(xh, p.gate_w)
+        idx_r, w_r = oracle.route(orc_cfg(p.s), lg_r, p.gate_bias)
+        np.testing.assert_array_equal(idx, idx_r)
+        for t in (0, 47, 95):
+            y_r, _, _, _ = p.oracle_forward(xh[t:t + 1])
+            assert_close_layer(y[t:t + 1], y_r)
+    finally:
+        p.gpu.mfma_min_tokens = 0
