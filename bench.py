@@ -75,6 +75,37 @@ def expert_bytes(s) -> dict:
     return {"gate_up": gate_up, "down": down, "total": gate_up + down}
 
 
+def kernel_sources_sha256() -> str:
+    """Hash of the library's kernel sources and ABI header: a stored counter
+    measurement applies only to the kernels it was taken on."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(root, "quantized_moe_coli_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
+    files.append(os.path.join(root, "include", "coli_moe.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs (profiles/traffic_<workload>.json, scaled by a copy of
+    known size), or None if absent or taken on other kernel sources."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("sources_sha256") != kernel_sources_sha256() or not kernel.startswith(rec.get("kernel", "?")):
+        return None
+    return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +113,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--instances", type=int, default=8)
     ap.add_argument("--workload", choices=list(WORKLOADS), default="decode")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one untimed device-to-device copy of this many MiB after the "
+                         "warm-up (the known-size reference for hardware byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's timed CPU sample (0 disables it)")
     args = ap.parse_args()
@@ -143,6 +177,13 @@ def main() -> int:
     for st in range(W):
         step(st)
     torch.cuda.synchronize()
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # headline: the K timed steps captured into one HIP graph, replayed once
     g = torch.cuda.CUDAGraph()
@@ -308,7 +349,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload, dom_name),
             "avg_launch_us": round(dom_ms * 1e3, 3),
             "bytes_per_launch": int(dom_bytes),
         },
