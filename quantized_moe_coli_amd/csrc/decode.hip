@@ -193,8 +193,11 @@ __device__ __forceinline__ void select_local(const DecodeArgs &d, unsigned char 
 }
 
 // D item: output rows [r0, r0 + down_rows).  Wave w owns rows
-// r0 + w*PR .. r0 + w*PR + PR-1 (PR = NPASS * RPP) for every slot, so it can
-// combine y = o_shared + sum_j w_j * o_j in the fixed slot order itself.
+// r0 + w*PR .. r0 + w*PR + PR-1 (PR = NPASS * RPP) for every slot, so it
+// combines y = o_shared + sum_j w_j * o_j itself: each lane accumulates its
+// chunks' share of every slot (shared first, then slots 0 .. k-1), and the
+// lanes of a row are summed once at the end -- a fixed order, so the result
+// is reproducible.
 template <int BITS, int LPR, int CPL, int NPASS, int SG>
 __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *lds_q, float *lds_d,
                                           const int32_t *sidx, const float *sw) {
@@ -296,17 +299,19 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
           float acc = 0.f;
 #pragma unroll
           for (int i = 0; i < CPL; ++i) acc += chunk_part<BITS>(wv[q][p][i], act[i]);
-          acc = group_sum<LPR>(acc);
-          const float o = acc * sdv[q][p];
-          y[p] = shared ? o : y[p] + wgt * o;
+          // each lane's share of w_j * s_j * o_j; the lanes of a row are
+          // summed once, after the last slot
+          y[p] += (shared ? sdv[q][p] : wgt * sdv[q][p]) * acc;
         }
       }
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int p = 0; p < NPASS; ++p)
-    if (lane == group_sum_lane<LPR>(lane)) a.y[wrow0 + p * RPP + rsub] = y[p];
+  for (int p = 0; p < NPASS; ++p) {
+    const float yr = group_sum<LPR>(y[p]);
+    if (lane == group_sum_lane<LPR>(lane)) a.y[wrow0 + p * RPP + rsub] = yr;
+  }
 }
 
 // Persistent: the grid is at most the workgroups the GPU holds at once;
