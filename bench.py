@@ -20,6 +20,11 @@ the single fused kernel; union batches: the gate/up kernel).  Prints ONE JSON
 line on stdout; details go to stderr.
 
   python bench.py [--steps K] [--warmup W] [--workload decode|verify3|prefill512]
+
+``--workload stack`` measures instead a 40-layer stack of such layers resident
+in HBM (40 x 257 int4 experts, ~195 GB) decoded one token at a time, with a
+Zipf-like expert popularity per layer and expert top-p 0.7; its bytes per
+step are those of the experts the routing actually kept.
 """
 from __future__ import annotations
 
@@ -112,7 +117,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--instances", type=int, default=8)
-    ap.add_argument("--workload", choices=list(WORKLOADS), default="decode")
+    ap.add_argument("--workload", choices=list(WORKLOADS) + ["stack"], default="decode")
+    ap.add_argument("--layers", type=int, default=40, help="stack workload: layers resident")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one untimed device-to-device copy of this many MiB after the "
                          "warm-up (the known-size reference for hardware byte counters)")
@@ -133,6 +139,8 @@ def main() -> int:
     from quantized_moe_coli_amd import inputs
 
     torch.cuda.set_device(0)
+    if args.workload == "stack":
+        return stack_main(args)
     dev = "cuda"
     s = inputs.GLM
     T, supplied, rho = WORKLOADS[args.workload]
@@ -423,6 +431,234 @@ def cpu_baseline(s, layer0, xs, lgs, ys, NI, budget_s, T):
         "sample": f"{done} timed forward calls of {T} token(s) on layer instance 0 "
                   f"(steps 0, {NI}, {2 * NI}, ...), {spent:.1f} s of CPU time; GPU outputs "
                   f"of the same steps agree to {max_err:.1e}",
+    }
+
+
+def _kernel_events(hip, n):
+    evs = []
+    for _ in range(n):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        evs.append(e.value)
+    return evs
+
+
+def stack_main(args) -> int:
+    """The multi-layer decode: every step feeds a fresh token through all
+    resident layers (h <- h + MoE_l(rmsnorm(h))), one HIP graph per step
+    replayed on the token."""
+    import numpy as np
+    import torch
+
+    from quantized_moe_coli_amd import binding as B
+    from quantized_moe_coli_amd import inputs, stack
+
+    dev = "cuda"
+    K, W, NL = args.steps, args.warmup, args.layers
+    t0 = time.time()
+    stk = stack.build(NL)
+    s = stk.s
+    log(f"[bench] stack: {NL} layers packed in {time.time() - t0:.1f}s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB resident)")
+    n_x = max(K, W, 1)
+    xs = torch.stack([inputs.tokens(s, stack.token_seed(), t, 1, dev) for t in range(n_x)])
+    ws = B.workspace(stk.layers[0], 1)
+    h = torch.empty(1, s.hidden, device=dev)
+    y = torch.empty(1, s.hidden, device=dev)
+    idx_g = torch.empty(NL, 1, s.top_k, dtype=torch.int32, device=dev)
+    w_g = torch.empty(NL, 1, s.top_k, device=dev)
+    for t in range(W):
+        h.copy_(xs[t])
+        stack.step(stk, h, ws, y, idx_g, w_g)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            stack.step(stk, h, ws, y, idx_g, w_g)
+    torch.cuda.synchronize()
+    idx_all = torch.empty(K, NL, s.top_k, dtype=torch.int32, device=dev)
+
+    def run_steps():
+        for t in range(K):
+            h.copy_(xs[t])
+            g.replay()
+            idx_all[t].copy_(idx_g[:, 0])
+
+    run_steps()  # one untimed pass
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record()
+    run_steps()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    del g
+
+    # the decode kernel's own duration: an eager pass over the first steps,
+    # every layer's launch recording a start and a stop event
+    hip = _hip()
+    KP = min(K, 32)
+    evs = _kernel_events(hip, KP * NL * 2)
+    torch.cuda.synchronize()
+    for t in range(KP):
+        h.copy_(xs[t])
+        for li, L in enumerate(stk.layers):
+            e = evs[(t * NL + li) * 2:(t * NL + li) * 2 + 2]
+            B.coli_moe_forward_profiled(L, stack.rmsnorm(h), y, ws, e, c_layer=stk.c_layers[li])
+            h.add_(y)
+    torch.cuda.synchronize()
+    kms = []
+    for i in range(KP * NL):
+        v = ctypes.c_float()
+        rc = hip.hipEventElapsedTime(ctypes.byref(v), ctypes.c_void_p(evs[2 * i]),
+                                     ctypes.c_void_p(evs[2 * i + 1]))
+        kms.append(v.value if rc == 0 else float("nan"))
+    for e in evs:
+        hip.hipEventDestroy(ctypes.c_void_p(e))
+    hip.hipGetLastError()
+    kms = np.array(kms).reshape(KP, NL)
+
+    idx = idx_all.cpu().numpy()
+    kept = (idx >= 0).sum(axis=2)  # [K, NL]
+    eb = expert_bytes(s)["total"]
+    gate_bytes = s.n_experts * s.hidden * 4
+    act_bytes = s.hidden * 4 * 2
+    launch_bytes = (kept + 1) * eb + gate_bytes + act_bytes  # per layer launch
+    step_bytes = launch_bytes.sum(axis=1)
+    ms_per_step = total_ms / K
+    tokens_per_s = K / (total_ms / 1e3)
+    gbps = float(step_bytes.mean()) / (ms_per_step * 1e-3) / 1e9
+    k_avg_ms = float(np.nanmean(kms))
+    k_bytes = float(launch_bytes[:KP].mean())
+    k_gbps = k_bytes / (k_avg_ms * 1e-3) / 1e9
+    log(f"[bench] stack: {K} steps in {total_ms:.2f} ms (wall {wall * 1e3:.1f} ms): "
+        f"{ms_per_step * 1e3:.1f} us/step, {tokens_per_s:.1f} tokens/s; kept experts/layer "
+        f"{kept.mean():.2f}; bytes/step {step_bytes.mean() / 1e9:.3f} GB -> {gbps:.0f} GB/s")
+    log(f"[bench] decode kernel: {k_avg_ms * 1e3:.2f} us avg over {KP * NL} launches, "
+        f"{k_bytes / 1e6:.1f} MB each -> {k_gbps:.0f} GB/s")
+
+    result = {
+        "metric": f"MoE-stack tokens/s ({NL} int4 layers, Zipf popularity, expert top-p 0.7)",
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4xint8->int32,fp32-scale",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{NL} GLM-5.2-shaped routed-MoE layers resident (H 6144, I 2048, 256 "
+                        "experts top-8, 8 groups keep 4, rsf 2.5, + 1 shared; packed int4), "
+                        "per-layer logit offsets -1.1 ln(rank+1) over a random expert ranking, "
+                        "expert top-p 0.7 renormalised; batch-1 decode, h <- h + "
+                        "MoE(rmsnorm(h)) between layers",
+            "tokens_per_step": 1,
+            "layers": NL,
+            "launch": "one HIP graph per step (all layers), replayed on each token",
+            "kept_experts_per_layer": round(float(kept.mean()), 3),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_decode_fused (one layer for one token)",
+            "achieved": round(k_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(k_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(k_avg_ms * 1e3, 3),
+            "bytes_per_launch": int(k_bytes),
+        },
+        "layer_roofline": {
+            "bound": "hbm",
+            "achieved": round(gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "bytes_per_step": int(step_bytes.mean()),
+        },
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = stack_cpu_baseline(stk, xs, ws, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def stack_cpu_baseline(stk, xs, ws, budget_s):
+    """The oracle's own chain for step 0: layer after layer on its own hidden
+    state (its logits plus the layer's offsets, its routing, its experts
+    packed from the same fp32 draws, untimed; the glue in numpy), until the
+    budget is spent; the per-layer time is extrapolated to the whole stack.
+    The GPU's hidden state after each of those layers is compared with it."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from quantized_moe_coli_amd import binding as B
+    from quantized_moe_coli_amd import inputs, stack
+
+    s = stk.s
+    ocfg = oracle.make_cfg(s.n_experts, s.top_k, s.n_group, s.topk_group, 1, s.rsf, s.top_p, 1)
+    # the GPU chain for step 0, keeping h after every layer
+    h = xs[0].clone()
+    y = torch.empty_like(h)
+    h_gpu = []
+    for li, L in enumerate(stk.layers):
+        B.coli_moe_forward(L, stack.rmsnorm(h), y, ws, c_layer=stk.c_layers[li])
+        h.add_(y)
+        h_gpu.append(h.cpu().numpy())
+    hc = xs[0].cpu().numpy().astype(np.float32)
+    spent, done, max_err = 0.0, 0, 0.0
+    for li, L in enumerate(stk.layers):
+        gate_w = L.gate_w.cpu().numpy()
+        bias = L.gate_bias.cpu().numpy()
+        off = stk.offsets[li].cpu().numpy()
+        hd = hc.astype(np.float64)
+        hn = (hd / np.sqrt((hd * hd).mean(axis=1, keepdims=True) + stack.RMS_EPS)).astype(np.float32)
+        lg = (oracle.logits(hn, gate_w) + off[None, :]).astype(np.float32)
+        idx, _ = oracle.route(ocfg, lg, bias)
+
+        def ex(e):
+            g, u, d = (t.cpu().numpy() for t in
+                       inputs.expert_weights(s, stack.layer_seed(li), e, "cuda"))
+            return oracle.Expert.from_float(s.bits, g, u, d)
+
+        exps = [None] * s.n_experts
+        for e in set(idx.ravel().tolist()):
+            if e >= 0:
+                exps[e] = ex(e)
+        layer = oracle.Layer(s.hidden, s.inter, s.bits, ocfg, exps, ex(s.n_experts), gate_w, bias)
+        t0 = time.perf_counter()
+        y_r, _, _, _ = oracle.moe_forward(layer, hn, lg)
+        spent += time.perf_counter() - t0
+        hc = (hc + y_r).astype(np.float32)
+        done += 1
+        d = np.abs(h_gpu[li].astype(np.float64) - hc).max() / np.abs(hc).max()
+        max_err = max(max_err, float(d))
+        if spent >= budget_s:
+            break
+    per_layer = spent / done
+    tok_s = 1.0 / (per_layer * stk.n_layers)
+    log(f"[bench] oracle chain, step 0: {done} layers in {spent:.2f}s on {oracle.num_threads()} "
+        f"threads -> {tok_s:.3f} tokens/s extrapolated to {stk.n_layers} layers; GPU hidden "
+        f"state within {max_err:.2e} (rel. to max |h|) of the oracle's over those layers")
+    return {
+        "value": round(tok_s, 5),
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"step 0 through layers 0..{done - 1} of the oracle's own chain "
+                  f"({spent:.1f} s of timed forward calls), extrapolated to {stk.n_layers} "
+                  f"layers; GPU hidden state agrees to {max_err:.1e}",
     }
 
 

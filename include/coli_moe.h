@@ -84,7 +84,11 @@ typedef struct {
  * batch of T >= 2 tokens, a unique expert (or the shared expert) receiving at
  * least this many tokens runs on the int8 matrix cores, one with fewer on the
  * integer dot-product GEMV; 0 selects the library default (8).  Both give
- * the same results up to fp32 summation order. */
+ * the same results up to fp32 summation order.  gate_offset: optional [E]
+ * fp32 per-expert terms added (one binary32 addition) to the logits computed
+ * from gate_w, before selection and weighting; it models a skewed expert
+ * popularity on synthetic gates.  NULL = none; ignored when logits are
+ * supplied, which already include any offset. */
 typedef struct {
   int32_t hidden;   /* H: 6144 */
   int32_t inter;    /* I: 2048 */
@@ -105,6 +109,7 @@ typedef struct {
   const float *sh_s_up;
   const float *sh_s_down;
   int32_t mfma_min_tokens;
+  const float *gate_offset; /* [E] fp32 or NULL */
 } coli_moe_layer;
 
 /* ABI version (COLI_ABI_VERSION) and a static message for a status. */

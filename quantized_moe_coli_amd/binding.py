@@ -46,7 +46,7 @@ class MoeLayerC(ctypes.Structure):
                 ("s_gate", _P), ("s_up", _P), ("s_down", _P),
                 ("sh_gate", _P), ("sh_up", _P), ("sh_down", _P),
                 ("sh_s_gate", _P), ("sh_s_up", _P), ("sh_s_down", _P),
-                ("mfma_min_tokens", ctypes.c_int32)]
+                ("mfma_min_tokens", ctypes.c_int32), ("gate_offset", _P)]
 
 
 _lib = None
@@ -185,7 +185,8 @@ class MoeLayer:
 
     def __init__(self, hidden, inter, qtype, cfg: RouterCfg, gate_w, gate_bias,
                  w_gate, s_gate, w_up, s_up, w_down, s_down,
-                 sh_gate, sh_s_gate, sh_up, sh_s_up, sh_down, sh_s_down, mfma_min_tokens=0):
+                 sh_gate, sh_s_gate, sh_up, sh_s_up, sh_down, sh_s_down, mfma_min_tokens=0,
+                 gate_offset=None):
         self.hidden, self.inter, self.qtype, self.cfg = hidden, inter, qtype, cfg
         self.gate_w, self.gate_bias = gate_w, gate_bias
         self.w_gate, self.s_gate, self.w_up, self.s_up = w_gate, s_gate, w_up, s_up
@@ -193,6 +194,7 @@ class MoeLayer:
         self.sh_gate, self.sh_s_gate, self.sh_up, self.sh_s_up = sh_gate, sh_s_gate, sh_up, sh_s_up
         self.sh_down, self.sh_s_down = sh_down, sh_s_down
         self.mfma_min_tokens = mfma_min_tokens
+        self.gate_offset = gate_offset  # optional fp32 [E] added to computed logits
 
     def c_struct(self) -> MoeLayerC:
         u8, f32 = torch.uint8, torch.float32
@@ -205,7 +207,8 @@ class MoeLayer:
                          _ptr(self.sh_gate, u8, "sh_gate"), _ptr(self.sh_up, u8, "sh_up"),
                          _ptr(self.sh_down, u8, "sh_down"),
                          _ptr(self.sh_s_gate, f32, "sh_s_gate"), _ptr(self.sh_s_up, f32, "sh_s_up"),
-                         _ptr(self.sh_s_down, f32, "sh_s_down"), self.mfma_min_tokens)
+                         _ptr(self.sh_s_down, f32, "sh_s_down"), self.mfma_min_tokens,
+                         _ptr(self.gate_offset, f32, "gate_offset"))
 
     @staticmethod
     def empty(hidden, inter, qtype, cfg: RouterCfg, device="cuda", gate=True) -> "MoeLayer":

@@ -67,6 +67,7 @@ bool layer_ok(const coli_moe_layer *L) {
     if (!p || !aligned(p, 4)) return false;
   if (L->gate_w && !aligned(L->gate_w, 16)) return false;
   if (L->gate_bias && !aligned(L->gate_bias, 4)) return false;
+  if (L->gate_offset && !aligned(L->gate_offset, 4)) return false;
   if (L->mfma_min_tokens < 0) return false;
   return true;
 }
@@ -270,6 +271,7 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
     fa.cfg = to_cfg(L->router);
     fa.logits = lp;
     fa.bias = L->gate_bias;
+    fa.loff = logits_in ? nullptr : L->gate_offset;
     fa.idx_user = idx_out;
     fa.w_user = w_out;
     fa.hq = reinterpret_cast<int8_t *>(base + ws.hq);
@@ -285,8 +287,8 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
       if (e != hipErrorNotSupported) return from_hip(e);
     }
     // activations -> Q8_0 codes, and the router logits unless supplied
-    e = coli::launch_front(L->qtype, x, logits_in ? nullptr : L->gate_w, T, E, H, lp_dst, xq, xd, s,
-                           kev(0));
+    e = coli::launch_front(L->qtype, x, logits_in ? nullptr : L->gate_w, fa.loff, T, E, H, lp_dst,
+                           xq, xd, s, kev(0));
     if (e != hipSuccess) return COLI_ERR_DEVICE;
     if (T == 1) {
       // decode on other shapes: each gate/up workgroup selects the experts itself

@@ -144,7 +144,8 @@ __device__ __forceinline__ void logits_rows(const DecodeArgs &d, int e0, double 
   if ((int)threadIdx.x < kLogRows && e0 + (int)threadIdx.x < d.f.E) {
     const int e = e0 + threadIdx.x;
     const double *p = part + 4 * threadIdx.x;
-    const float l = (float)(((p[0] + p[1]) + p[2]) + p[3]);
+    float l = (float)(((p[0] + p[1]) + p[2]) + p[3]);
+    if (d.f.loff) l += d.f.loff[e];
     const float sg = sigmoid_f64(l);
     const float c = sg + (d.f.bias ? d.f.bias[e] : 0.f);
     const uint64_t w = ((uint64_t)__float_as_uint(sg) << 32) | (uint64_t)(~__float_as_uint(c));

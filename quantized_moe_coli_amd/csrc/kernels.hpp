@@ -70,8 +70,10 @@ hipError_t launch_logits(const float *x, const float *gate_w, int T, int E, int 
                          hipStream_t st);
 // Router logits (if gate_w) and Q8_0 activations in container BITS ordering
 // (if xq), in as few launches as the batch allows.
-hipError_t launch_front(int bits, const float *x, const float *gate_w, int T, int E, int H,
-                        float *logits, int8_t *xq, float *xd, hipStream_t st, KEvents ev = {});
+// loff: optional [E] terms added to each computed logit.
+hipError_t launch_front(int bits, const float *x, const float *gate_w, const float *loff, int T,
+                        int E, int H, float *logits, int8_t *xq, float *xd, hipStream_t st,
+                        KEvents ev = {});
 hipError_t launch_route(const RouterCfg &cfg, const float *logits, const float *bias, int T,
                         int32_t *idx, float *w, int32_t *idx_copy, float *w_copy, hipStream_t st);
 hipError_t launch_dispatch(const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offs,
@@ -93,6 +95,7 @@ struct FfnArgs {
   RouterCfg cfg;
   const float *logits;  // [1][E]
   const float *bias;    // [E] or null
+  const float *loff;    // [E] terms added to computed logits, or null
   int32_t *idx_user;    // optional copies for the caller
   float *w_user;
   Dispatch disp;        // union mode only

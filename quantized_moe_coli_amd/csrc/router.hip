@@ -30,7 +30,8 @@ namespace coli {
 // ---------------------------------------------------------------------------
 template <int BITS, int MAXT>
 __global__ __launch_bounds__(256) void k_front_small(const float *__restrict__ x,
-                                                     const float *__restrict__ gw, int T, int E,
+                                                     const float *__restrict__ gw,
+                                                     const float *__restrict__ loff, int T, int E,
                                                      int H, float *__restrict__ out, int nlog,
                                                      int8_t *__restrict__ xq,
                                                      float *__restrict__ xd) {
@@ -88,7 +89,9 @@ __global__ __launch_bounds__(256) void k_front_small(const float *__restrict__ x
   if (threadIdx.x < MAXT && (int)threadIdx.x < T) {
     const int t = threadIdx.x;
     const double s = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
-    out[(size_t)t * E + e] = (float)s;
+    float l = (float)s;
+    if (loff) l += loff[e];
+    out[(size_t)t * E + e] = l;
   }
 }
 
@@ -104,7 +107,8 @@ __global__ __launch_bounds__(256) void k_front_small(const float *__restrict__ x
 typedef double d4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void k_logits_mfma(const float *__restrict__ x,
-                                                     const float *__restrict__ gw, int T, int E,
+                                                     const float *__restrict__ gw,
+                                                     const float *__restrict__ loff, int T, int E,
                                                      int H, float *__restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -148,27 +152,32 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const float *__restrict__ x
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 16 * a + g + 4 * i;
         const int e = e0 + 16 * b + r;
-        if (t < T && e < E) out[(size_t)t * E + e] = (float)acc[a][b][i];
+        if (t < T && e < E) {
+          float l = (float)acc[a][b][i];
+          if (loff) l += loff[e];
+          out[(size_t)t * E + e] = l;
+        }
       }
 }
 
 template <int BITS>
-static void front_small(const float *x, const float *gate_w, int T, int E, int H, float *logits,
-                        int8_t *xq, float *xd, hipStream_t st, KEvents ev) {
+static void front_small(const float *x, const float *gate_w, const float *loff, int T, int E,
+                        int H, float *logits, int8_t *xq, float *xd, hipStream_t st, KEvents ev) {
   const int nlog = gate_w ? E : 0;
   const int naq = xq ? (int)(((int64_t)T * (H / 32) + 255) / 256) : 0;
-  COLI_LAUNCH(ev, (k_front_small<BITS, 4>), dim3(nlog + naq), dim3(256), 0, st, x, gate_w, T, E,
-              H, logits, nlog, xq, xd);
+  COLI_LAUNCH(ev, (k_front_small<BITS, 4>), dim3(nlog + naq), dim3(256), 0, st, x, gate_w, loff, T,
+              E, H, logits, nlog, xq, xd);
 }
 
-hipError_t launch_front(int bits, const float *x, const float *gate_w, int T, int E, int H,
-                        float *logits, int8_t *xq, float *xd, hipStream_t st, KEvents ev) {
+hipError_t launch_front(int bits, const float *x, const float *gate_w, const float *loff, int T,
+                        int E, int H, float *logits, int8_t *xq, float *xd, hipStream_t st,
+                        KEvents ev) {
   if (T == 0 || (!gate_w && !xq)) return hipSuccess;
   if (T <= 4) {
     switch (bits) {
-      case 8: front_small<8>(x, gate_w, T, E, H, logits, xq, xd, st, ev); break;
-      case 4: front_small<4>(x, gate_w, T, E, H, logits, xq, xd, st, ev); break;
-      case 2: front_small<2>(x, gate_w, T, E, H, logits, xq, xd, st, ev); break;
+      case 8: front_small<8>(x, gate_w, loff, T, E, H, logits, xq, xd, st, ev); break;
+      case 4: front_small<4>(x, gate_w, loff, T, E, H, logits, xq, xd, st, ev); break;
+      case 2: front_small<2>(x, gate_w, loff, T, E, H, logits, xq, xd, st, ev); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -177,7 +186,7 @@ hipError_t launch_front(int bits, const float *x, const float *gate_w, int T, in
   // quantisation when the logits are supplied
   if (gate_w) {
     const dim3 grid((E + 127) / 128, (T + 31) / 32), block(256);
-    COLI_LAUNCH(ev, k_logits_mfma, grid, block, 0, st, x, gate_w, T, E, H, logits);
+    COLI_LAUNCH(ev, k_logits_mfma, grid, block, 0, st, x, gate_w, loff, T, E, H, logits);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -187,7 +196,7 @@ hipError_t launch_front(int bits, const float *x, const float *gate_w, int T, in
 
 hipError_t launch_logits(const float *x, const float *gate_w, int T, int E, int H, float *logits,
                          hipStream_t st) {
-  return launch_front(8, x, gate_w, T, E, H, logits, nullptr, nullptr, st);
+  return launch_front(8, x, gate_w, nullptr, T, E, H, logits, nullptr, nullptr, st);
 }
 
 // ---------------------------------------------------------------------------

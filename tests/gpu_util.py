@@ -31,11 +31,14 @@ class LayerPair:
     the oracle needs; otherwise they are drawn on the CPU."""
 
     def __init__(self, s: inputs.Shape, seed: int = 0, device_gen: bool = False,
-                 mfma_min_tokens: int = 0):
+                 mfma_min_tokens: int = 0, gate_offset: np.ndarray | None = None):
         self.s, self.seed, self.device_gen = s, seed, device_gen
+        self.gate_offset = gate_offset
         gdev = "cuda" if device_gen else "cpu"
         self.gpu = B.MoeLayer.empty(s.hidden, s.inter, s.bits, gpu_cfg(s))
         self.gpu.mfma_min_tokens = mfma_min_tokens
+        if gate_offset is not None:
+            self.gpu.gate_offset = to_dev(gate_offset.astype(np.float32))
         gw = inputs.gate_weight(s, seed, gdev)
         gb = inputs.gate_bias(s, seed, gdev)
         self.gpu.gate_w.copy_(gw)
@@ -69,7 +72,12 @@ class LayerPair:
                             self.orc_expert(E), self.gate_w, self.gate_bias)
 
     def oracle_forward(self, x: np.ndarray, logits_in: np.ndarray | None = None):
-        """The oracle on x, supplying only the experts its own routing picks."""
+        """The oracle on x, supplying only the experts its own routing picks.
+        With per-expert logit offsets, the oracle's logits from the gate plus
+        the offsets (one binary32 addition) are handed to it as supplied."""
+        if logits_in is None and self.gate_offset is not None:
+            logits_in = (oracle.logits(x, self.gate_w) +
+                         self.gate_offset.astype(np.float32)[None, :]).astype(np.float32)
         lg = oracle.logits(x, self.gate_w) if logits_in is None else logits_in
         idx, _ = oracle.route(orc_cfg(self.s), lg, self.gate_bias)
         return oracle.moe_forward(self.orc_layer(set(idx.ravel().tolist())), x, logits_in)

@@ -242,6 +242,25 @@ def test_layer_tiny_supplied_logits(tiny_pairs, T):
     assert_close_layer(y, y_r)
 
 
+@pytest.mark.parametrize("T", [1, 5, 40])
+def test_layer_gate_offsets(T):
+    """Per-expert logit offsets (a Zipf-like popularity over a random expert
+    ranking) added to the computed logits, with expert top-p: batch 1 (the
+    decode kernel), 5 and 40 (the two logits kernels of the union path)."""
+    s = inputs.TINY.with_(n_experts=64, top_k=6, n_group=4, topk_group=2, bias_std=0.05,
+                          bits=4, top_p=0.7)
+    off = inputs.zipf_logit_offsets(0, 7, s.n_experts).numpy()
+    p = LayerPair(s, seed=9, gate_offset=off)
+    x = inputs.tokens(s, 0, 700 + T, T)
+    y_r, idx_r, w_r, lg_r = p.oracle_forward(x.numpy())
+    y, idx, w, lg = p.gpu_forward(x.cuda())
+    l_raw = oracle.logits(x.numpy(), p.gate_w)
+    assert (np.abs(lg - lg_r) <= 2.0 ** -23 * np.maximum(np.abs(l_raw), np.abs(off))).all()
+    np.testing.assert_array_equal(idx, idx_r)
+    np.testing.assert_array_equal(w, w_r)
+    assert_close_layer(y, y_r)
+
+
 def test_layer_zero_input_and_zero_rsf(tiny_pairs):
     p = _pair(tiny_pairs, "tiny_int8")
     y, _, _, _ = p.gpu_forward(torch.zeros(3, p.s.hidden, device="cuda"))
@@ -376,6 +395,36 @@ def test_glm_union_sampled(glm, T):
     np.testing.assert_array_equal(w, w_r)
     for t in (0, T // 2, T - 1):
         y_r, _, _, _ = glm.oracle_forward(xh[t:t + 1])
+        assert_close_layer(y[t:t + 1], y_r)
+
+
+# The full-size layer (256 experts, computed logits) in the int8 and int2
+# containers at batch 1, 8 and 64 (the int4 container is covered above): the
+# precision-by-batch grid.  Routing of every token is checked; outputs for
+# every token at T = 1 and for three sampled tokens of larger batches.
+@pytest.fixture(scope="module")
+def glm_containers():
+    return {}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("bits", [8, 2])
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_glm_full_containers(glm_containers, bits, T):
+    if bits not in glm_containers:
+        glm_containers.clear()  # one full-size layer resident at a time
+        glm_containers[bits] = LayerPair(inputs.GLM.with_(bits=bits), seed=4, device_gen=True)
+    p = glm_containers[bits]
+    x = inputs.tokens(p.s, 0, 3000 + T, T, "cuda")
+    y, idx, w, lg = p.gpu_forward(x)
+    xh = x.cpu().numpy()
+    lg_r = oracle.logits(xh, p.gate_w)
+    assert ulp_diff(lg, lg_r).max() <= 1
+    idx_r, w_r = oracle.route(orc_cfg(p.s), lg_r, p.gate_bias)
+    np.testing.assert_array_equal(idx, idx_r)
+    np.testing.assert_array_equal(w, w_r)
+    for t in sorted({0, T // 2, T - 1}):
+        y_r, _, _, _ = p.oracle_forward(xh[t:t + 1])
         assert_close_layer(y[t:t + 1], y_r)
 
 
