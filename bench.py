@@ -111,7 +111,54 @@ def measured_traffic(workload: str, kernel: str):
     return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
 
+def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, calib_mib: int,
+                       commands: list) -> dict:
+    """Traffic record of `kernel` from two rocprofv3 counter CSVs (FETCH_SIZE,
+    then WRITE_SIZE; KiB per dispatch): the kernel's mean per dispatch, each
+    scaled by what the same counter reads for the largest device-to-device
+    copy in the run (the calibration copy of calib_mib MiB, which must read
+    and write calib_mib * 1024 KiB)."""
+    import csv
+
+    def per_kernel(path):
+        vals, copy = [], 0.0
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+                v = float(r.get("Counter_Value") or r.get("Counter-Value") or 0.0)
+                if kernel in name:
+                    vals.append(v)
+                elif "copyBuffer" in name:
+                    copy = max(copy, v)
+        if not vals or copy <= 0:
+            raise SystemExit(f"{path}: no {kernel} dispatches or no calibration copy")
+        return sum(vals) / len(vals), copy, len(vals)
+
+    known_kib = calib_mib * 1024.0
+    f_mean, f_copy, n_f = per_kernel(fetch_csv)
+    w_mean, w_copy, n_w = per_kernel(write_csv)
+    f_scale, w_scale = known_kib / f_copy, known_kib / w_copy
+    return {
+        "kernel": kernel,
+        "sources_sha256": kernel_sources_sha256(),
+        "fetch_bytes_per_launch": int(round(f_mean * 1024 * f_scale)),
+        "write_bytes_per_launch": int(round(w_mean * 1024 * w_scale)),
+        "fetch_kib_mean": round(f_mean, 1), "write_kib_mean": round(w_mean, 1),
+        "copy_fetch_kib": round(f_copy, 1), "copy_write_kib": round(w_copy, 1),
+        "fetch_scale": round(f_scale, 5),
+        "write_scale": round(w_scale, 5),
+        "dispatches": [n_f, n_w],
+        "commands": commands,
+    }
+
+
 def main() -> int:
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        # bench.py --summarize-counters FETCH.csv WRITE.csv KERNEL CALIB_MIB "cmd1" "cmd2"
+        rec = summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]),
+                                 sys.argv[6:])
+        print(json.dumps(rec, indent=1))
+        return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)

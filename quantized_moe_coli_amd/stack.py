@@ -1,9 +1,9 @@
 """A stack of routed-MoE layers resident in HBM, decoded one token at a time.
 
 The colibrì pages run GLM-5.2 by streaming each layer's selected experts for
-every generated token, with a skewed (learned, pinned) expert popularity and
-an adaptive expert top-p (README "Quick start" knobs; the pages' measurement
-of resident expert sets).  On one MI355X a 40-layer int4 stack
+every generated token, with a learned cache that pins the most-used experts
+(README "Quick start"; CSDN feature, "冷启动与热缓存的辩证法") and an
+adaptive expert top-p (README "Quick start").  On one MI355X a 40-layer int4 stack
 (40 x 257 experts, ~195 GB) fits in HBM, so this driver measures the routed
 layers back to back at the popularity skew and top-p of that workload.
 
