@@ -78,7 +78,7 @@ def build(n_layers: int = 40, s: inputs.Shape = STACK_SHAPE, device="cuda") -> S
 
 
 def rmsnorm(h: torch.Tensor) -> torch.Tensor:
-    return h * torch.rsqrt(h.square().mean(dim=-1, keepdim=True) + RMS_EPS)
+    return torch.nn.functional.rms_norm(h, (h.shape[-1],), eps=RMS_EPS)
 
 
 def step(st: Stack, h: torch.Tensor, ws: torch.Tensor, y: torch.Tensor,
