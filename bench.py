@@ -40,7 +40,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
-MFMA_MIN_DEFAULT = 8  # the library's default mfma_min_tokens
+MFMA_MIN_DEFAULT = 8  # the library's default mfma_min_tokens (routed experts)
+MFMA_MIN_SHARED_DEFAULT = 64  # and for the shared expert
 INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, published
 
 
@@ -69,6 +70,8 @@ WORKLOADS = {
     "decode": (1, False, 0.0),
     "verify3": (3, True, 0.0),
     "prefill512": (512, True, 0.0),
+    # the small layer (H 256, I 128, 16 int8 experts top-2): latency only
+    "tiny": (4, False, 0.0),
 }
 
 
@@ -166,6 +169,13 @@ def main() -> int:
     ap.add_argument("--instances", type=int, default=8)
     ap.add_argument("--workload", choices=list(WORKLOADS) + ["stack"], default="decode")
     ap.add_argument("--layers", type=int, default=40, help="stack workload: layers resident")
+    ap.add_argument("--bits", type=int, choices=(8, 4, 2), default=None,
+                    help="weight container of the GLM-5.2-shaped layer (default int4)")
+    ap.add_argument("--mfma-min", type=int, default=0,
+                    help="layer's mfma_min_tokens (0: the library default)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="tokens per step with logits computed from the gate (overrides the "
+                         "workload's batch; 1 = decode)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one untimed device-to-device copy of this many MiB after the "
                          "warm-up (the known-size reference for hardware byte counters)")
@@ -189,8 +199,16 @@ def main() -> int:
     if args.workload == "stack":
         return stack_main(args)
     dev = "cuda"
-    s = inputs.GLM
+    s = inputs.TINY if args.workload == "tiny" else inputs.GLM
+    if args.bits is not None:
+        s = s.with_(bits=args.bits)
     T, supplied, rho = WORKLOADS[args.workload]
+    if args.tokens > 0:
+        T, supplied, rho = args.tokens, False, 0.0
+    default_run = (args.bits in (None, 4) and args.tokens == 0 and args.workload != "tiny"
+                   and args.mfma_min == 0)
+    label = args.workload if default_run else (f"{args.workload}_int{s.bits}_T{T}" +
+                                               (f"_mfma{args.mfma_min}" if args.mfma_min else ""))
     K, W, NI = args.steps, args.warmup, args.instances
     cfg = B.router_cfg(s.n_experts, s.top_k, s.n_group, s.topk_group, 1, s.rsf, 0.0, 1)
 
@@ -204,6 +222,7 @@ def main() -> int:
             g, u, d = inputs.expert_weights(s, li, e, dev)
             L.pack_expert(e, g, u, d)
             del g, u, d
+        L.mfma_min_tokens = args.mfma_min
         layers.append(L)
         torch.cuda.synchronize()
     log(f"[bench] {NI} layer instances packed in {time.time() - t0:.1f}s "
@@ -312,6 +331,7 @@ def main() -> int:
     # one); in a union batch, experts with at least mfma_min tokens (and the
     # shared expert when T >= mfma_min) run on the matrix cores
     mfma_min = layers[0].mfma_min_tokens or MFMA_MIN_DEFAULT
+    shared_min = layers[0].mfma_min_tokens or MFMA_MIN_SHARED_DEFAULT
     if T == 1:
         uniq = np.full(K, s.top_k, dtype=np.float64)
         n_mfma = np.zeros(K)
@@ -319,11 +339,15 @@ def main() -> int:
         uniq, n_mfma = [], []
         for st in range(K):
             idx = torch.empty(T, s.top_k, dtype=torch.int32, device=dev)
-            B.coli_moe_route(cfg, lgs[st], layers[st % NI].gate_bias, idx,
-                             torch.empty(T, s.top_k, device=dev))
+            if lgs is not None:
+                B.coli_moe_route(cfg, lgs[st], layers[st % NI].gate_bias, idx,
+                                 torch.empty(T, s.top_k, device=dev))
+            else:  # computed logits: the layer's own routing of this step
+                B.coli_moe_forward(layers[st % NI], xs[st], torch.empty_like(ys[st]), ws,
+                                   idx_out=idx, c_layer=cls[st % NI])
             cnt = torch.bincount(idx[idx >= 0].long(), minlength=s.n_experts)
             uniq.append(int((cnt > 0).sum()))
-            n_mfma.append(int((cnt >= mfma_min).sum()) + (1 if T >= mfma_min else 0))
+            n_mfma.append(int((cnt >= mfma_min).sum()) + (1 if T >= shared_min else 0))
         uniq = np.array(uniq, dtype=np.float64)
         n_mfma = np.array(n_mfma, dtype=np.float64)
     act_bytes = T * s.hidden * 4 * 2  # x in, y out
@@ -349,7 +373,7 @@ def main() -> int:
         dom_ms = float(avg[dom])
         dom_bytes = float(np.mean(kbytes[dom]))
     dom_gbps = dom_bytes / (dom_ms * 1e-3) / 1e9
-    log(f"[bench] {args.workload}: {K} steps in {total_ms:.3f} ms (wall {wall * 1e3:.1f} ms): "
+    log(f"[bench] {label}: {K} steps in {total_ms:.3f} ms (wall {wall * 1e3:.1f} ms): "
         f"{ms_per_step * 1e3:.2f} us/step, {tokens_per_s:.0f} tokens/s")
     log(f"[bench] eager pass with kernel events: {eager_ms / K * 1e3:.2f} us/step (host wall "
         f"{eager_wall / K * 1e6:.2f} us/step), first-kernel start to last-kernel end "
@@ -368,8 +392,8 @@ def main() -> int:
         f"{dom_gbps:.0f} GB/s")
 
     result = {
-        "metric": "MoE-layer tokens/s (int4 top-8/256 decode)" if T == 1 else
-                  f"MoE-layer tokens/s ({args.workload})",
+        "metric": "MoE-layer tokens/s (int4 top-8/256 decode)" if (T == 1 and default_run) else
+                  f"MoE-layer tokens/s ({label})",
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -379,12 +403,16 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4xint8->int32,fp32-scale",
+        "dtype": f"int{s.bits}xint8->int32,fp32-scale",
         "data": "synthetic",
         "config": {
-            "workload": ("GLM-5.2 routed-MoE layer" + (" batch-1 decode" if T == 1 else
-                         f" {T}-token union batch") + ": H 6144, I 2048, 256 experts top-8 "
-                         "(8 groups keep 4, rsf 2.5) + 1 shared, packed int4 per-row fp32 "
+            "workload": (("GLM-5.2 routed-MoE layer" if s is not inputs.TINY and args.workload != "tiny"
+                          else "small routed-MoE layer") +
+                         (" batch-1 decode" if T == 1 else f" {T}-token union batch") +
+                         f": H {s.hidden}, I {s.inter}, {s.n_experts} experts top-{s.top_k} "
+                         + (f"({s.n_group} groups keep {s.topk_group}, rsf {s.rsf}) " if s.n_group > 1
+                            else f"(rsf {s.rsf}) ")
+                         + f"+ 1 shared, {'packed ' if s.bits < 8 else ''}int{s.bits} per-row fp32 "
                          "scale, Q8_0 activations" + (", logits from the fp32 gate" if not supplied
                                                        else ", logits supplied")),
             "tokens_per_step": T,
@@ -404,7 +432,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(args.workload, dom_name),
+            "traffic": measured_traffic(label, dom_name),
             "avg_launch_us": round(dom_ms * 1e3, 3),
             "bytes_per_launch": int(dom_bytes),
         },

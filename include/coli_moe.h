@@ -83,8 +83,9 @@ typedef struct {
  * 16).  H and I are multiples of 64, at most 8192.  mfma_min_tokens: in a
  * batch of T >= 2 tokens, a unique expert (or the shared expert) receiving at
  * least this many tokens runs on the int8 matrix cores, one with fewer on the
- * integer dot-product GEMV; 0 selects the library default (8).  Both give
- * the same results up to fp32 summation order.  gate_offset: optional [E]
+ * integer dot-product GEMV; 0 selects the library defaults (8 tokens for a
+ * routed expert, 64 for the shared expert, which receives the whole batch).
+ * Both give the same results up to fp32 summation order.  gate_offset: optional [E]
  * fp32 per-expert terms added (one binary32 addition) to the logits computed
  * from gate_w, before selection and weighting; it models a skewed expert
  * popularity on synthetic gates.  NULL = none; ignored when logits are

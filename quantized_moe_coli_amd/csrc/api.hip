@@ -308,6 +308,7 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
     int32_t *mgofs = reinterpret_cast<int32_t *>(base + ws.mgofs);
     fa.disp = coli::Dispatch{counts, offs, perm, uniq, nuniq, mgofs};
     fa.mfma_min = mfma_min > 0 ? mfma_min : coli::kMfmaMinDefault;
+    fa.mfma_min_shared = mfma_min > 0 ? mfma_min : coli::kMfmaMinSharedDefault;
     // no slot of a batch smaller than mfma_min tokens can reach the matrix cores
     const bool mfma = T >= fa.mfma_min;
     if (mfma) e = coli::launch_mfma_items(fa, mgofs, s);

@@ -133,7 +133,7 @@ __device__ __forceinline__ bool union_item(const FfnArgs &a, int u, int &e, TokL
     s.p0 = a.disp.offs[e];
     s.n_tok = a.disp.offs[e + 1] - s.p0;
   }
-  return s.n_tok < a.mfma_min;
+  return s.n_tok < (e < 0 ? a.mfma_min_shared : a.mfma_min);
 }
 
 // ---------------------------------------------------------------------------

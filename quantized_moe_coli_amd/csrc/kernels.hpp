@@ -103,11 +103,16 @@ struct FfnArgs {
   float *hd;            // [rows][I/32]
   float *obuf;          // union: [T][k+1][H]
   float *y;             // [T][H]
-  int mfma_min;         // union: slots with at least this many tokens run on the matrix cores
+  int mfma_min;         // union: routed slots with at least this many tokens run on the matrix cores
+  int mfma_min_shared;  // union: the same for the shared expert (its tokens: the whole batch)
 };
 
 constexpr int kMfmaTokens = 64;  // tokens per matrix-core work item
 constexpr int kMfmaMinDefault = 8;  // default token count from which an expert runs on MFMA
+// default for the shared expert, which receives the whole batch: one full
+// 64-token group.  With fewer tokens it usually runs alone on the matrix
+// cores (I/64 + H/64 workgroups), slower than on the dot-product path.
+constexpr int kMfmaMinSharedDefault = 64;
 
 hipError_t launch_gateup(const FfnArgs &a, bool union_mode, int mfma_min, hipStream_t st,
                          KEvents ev = {});

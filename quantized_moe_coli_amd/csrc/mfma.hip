@@ -54,11 +54,13 @@ __global__ __launch_bounds__(1024) void k_mfma_items(FfnArgs a, int32_t *__restr
   int g0 = 0, g1 = 0;
   if (2 * tid < slots) {
     const int u = 2 * tid;
-    g0 = mfma_groups(u < nu ? a.disp.counts[a.disp.uniq[u]] : a.T, a.mfma_min);
+    g0 = u < nu ? mfma_groups(a.disp.counts[a.disp.uniq[u]], a.mfma_min)
+               : mfma_groups(a.T, a.mfma_min_shared);
   }
   if (2 * tid + 1 < slots) {
     const int u = 2 * tid + 1;
-    g1 = mfma_groups(u < nu ? a.disp.counts[a.disp.uniq[u]] : a.T, a.mfma_min);
+    g1 = u < nu ? mfma_groups(a.disp.counts[a.disp.uniq[u]], a.mfma_min)
+               : mfma_groups(a.T, a.mfma_min_shared);
   }
   int cur = 0;
   sc[0][tid] = g0 + g1;
@@ -392,12 +394,15 @@ __global__ __launch_bounds__(256) void k_down_mfma(FfnArgs a) {
 }
 
 // Upper bound of the token groups a batch can send here: routed pairs in
-// groups of 64 plus one partial group per unique expert, plus the shared
-// expert's groups.
+// groups of 64 plus one partial group per unique expert that can reach
+// mfma_min tokens (at most pairs / mfma_min of them), plus the shared
+// expert's groups when the batch reaches its threshold.
 static int mfma_group_bound(const FfnArgs &a) {
   const long pairs = (long)a.T * a.k;
-  const long uniq = pairs < a.E ? pairs : a.E;
-  return (int)((pairs + kMfmaTokens - 1) / kMfmaTokens + uniq + (a.T + kMfmaTokens - 1) / kMfmaTokens);
+  long cap = pairs < a.E ? pairs : a.E;
+  if (pairs / a.mfma_min < cap) cap = pairs / a.mfma_min;
+  const long shared = a.T >= a.mfma_min_shared ? (a.T + kMfmaTokens - 1) / kMfmaTokens : 0;
+  return (int)((pairs + kMfmaTokens - 1) / kMfmaTokens + cap + shared);
 }
 
 hipError_t launch_mfma_items(const FfnArgs &a, int32_t *mgofs, hipStream_t st) {

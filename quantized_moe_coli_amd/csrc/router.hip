@@ -96,68 +96,68 @@ __global__ __launch_bounds__(256) void k_front_small(const float *__restrict__ x
 }
 
 // ---------------------------------------------------------------------------
-// Logits, larger batches: binary64 matrix cores.  A wave owns a 32-token x
-// 32-expert tile as 2x2 v_mfma_f64_16x16x4 blocks.  Operand lane layout for
-// 16x16x4: lane l supplies row (l % 16) and reduction index (l / 16); the
-// reduction order inside a tile does not matter, so for a step of 16 inputs
-// lane l loads the float4 at offset 4*(l/16) and feeds component j to the
-// j-th MFMA.  Result (binary64 layout): register i of lane l holds row
-// (l / 16) + 4*i, column l % 16.
+// Logits, larger batches: binary64 matrix cores.  A workgroup owns a
+// 16-token x 16-expert tile; its 8 waves take the reduction steps of 16
+// inputs round-robin, each into its own v_mfma_f64_16x16x4 accumulator, and
+// the 8 partial tiles are added in wave order through LDS and rounded once.
+// Operand lane layout for 16x16x4: lane l supplies row (l % 16) and
+// reduction index (l / 16); for a step of 16 inputs lane l loads the float4
+// at offset 4*(l/16) and feeds component j to the j-th MFMA.  Result
+// (binary64 layout): register i of lane l holds row (l / 16) + 4*i, column
+// l % 16.  Small tiles keep every batch size spread over many workgroups
+// (16 experts x 16 tokens each).
 // ---------------------------------------------------------------------------
 typedef double d4 __attribute__((ext_vector_type(4)));
+constexpr int kLogWaves = 8;
 
-__global__ __launch_bounds__(256) void k_logits_mfma(const float *__restrict__ x,
-                                                     const float *__restrict__ gw,
-                                                     const float *__restrict__ loff, int T, int E,
-                                                     int H, float *__restrict__ out) {
+__global__ __launch_bounds__(64 * kLogWaves) void k_logits_mfma(const float *__restrict__ x,
+                                                                const float *__restrict__ gw,
+                                                                const float *__restrict__ loff,
+                                                                int T, int E, int H,
+                                                                float *__restrict__ out) {
+  __shared__ double part[kLogWaves][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.y * 32;
-  const int e0 = (blockIdx.x * 4 + wave) * 32;
-  if (e0 >= E) return;
+  const int t0 = blockIdx.y * 16;
+  const int e0 = blockIdx.x * 16;
   const int r = lane & 15, g = lane >> 4;
-  const float *xr[2], *wr[2];
+  const float *xr = x + (size_t)min(t0 + r, T - 1) * H + 4 * g;
+  const float *wr = gw + (size_t)min(e0 + r, E - 1) * H + 4 * g;
+  d4 acc = {0.0, 0.0, 0.0, 0.0};
+  constexpr int kBatch = 4;  // steps whose loads are issued together
+  for (int k0 = 16 * wave; k0 < H; k0 += 16 * kLogWaves * kBatch) {
+    float4 xv[kBatch], wv[kBatch];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    xr[a] = x + (size_t)min(t0 + 16 * a + r, T - 1) * H + 4 * g;
-    wr[a] = gw + (size_t)min(e0 + 16 * a + r, E - 1) * H + 4 * g;
-  }
-  d4 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = d4{0.0, 0.0, 0.0, 0.0};
-  for (int k0 = 0; k0 < H; k0 += 16) {
-    float4 xv[2], wv[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      xv[a] = *reinterpret_cast<const float4 *>(xr[a] + k0);
-      wv[a] = *reinterpret_cast<const float4 *>(wr[a] + k0);
+    for (int j = 0; j < kBatch; ++j) {
+      const int k = min(k0 + 16 * kLogWaves * j, H - 16);  // clamped: valid, unused
+      xv[j] = *reinterpret_cast<const float4 *>(xr + k);
+      wv[j] = *reinterpret_cast<const float4 *>(wr + k);
     }
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[a].x, (double)wv[b].x, acc[a][b], 0, 0, 0);
-        acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[a].y, (double)wv[b].y, acc[a][b], 0, 0, 0);
-        acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[a].z, (double)wv[b].z, acc[a][b], 0, 0, 0);
-        acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[a].w, (double)wv[b].w, acc[a][b], 0, 0, 0);
+    for (int j = 0; j < kBatch; ++j) {
+      if (k0 + 16 * kLogWaves * j < H) {
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[j].x, (double)wv[j].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[j].y, (double)wv[j].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[j].z, (double)wv[j].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[j].w, (double)wv[j].w, acc, 0, 0, 0);
       }
+    }
   }
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int i = 0; i < 4; ++i) part[wave][i][lane] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int i = threadIdx.x >> 6;
+    double sum = part[0][i][lane];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * a + g + 4 * i;
-        const int e = e0 + 16 * b + r;
-        if (t < T && e < E) {
-          float l = (float)acc[a][b][i];
-          if (loff) l += loff[e];
-          out[(size_t)t * E + e] = l;
-        }
-      }
+    for (int w = 1; w < kLogWaves; ++w) sum += part[w][i][lane];
+    const int t = t0 + g + 4 * i, e = e0 + r;
+    if (t < T && e < E) {
+      float l = (float)sum;
+      if (loff) l += loff[e];
+      out[(size_t)t * E + e] = l;
+    }
+  }
 }
 
 template <int BITS>
@@ -185,7 +185,7 @@ hipError_t launch_front(int bits, const float *x, const float *gate_w, const flo
   // the kernel events time the logits kernel, or the activation
   // quantisation when the logits are supplied
   if (gate_w) {
-    const dim3 grid((E + 127) / 128, (T + 31) / 32), block(256);
+    const dim3 grid((E + 15) / 16, (T + 15) / 16), block(64 * kLogWaves);
     COLI_LAUNCH(ev, k_logits_mfma, grid, block, 0, st, x, gate_w, loff, T, E, H, logits);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
