@@ -99,11 +99,14 @@ def _declare(L: ctypes.CDLL) -> None:
         "orc_moe_forward": [ctypes.POINTER(_Layer), _P, _I64, _P, _P, _P, _P, _P],
         "orc_union_tables": [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P],
         "orc_num_threads": [],
+        "orc_dequant_fp8_block": [_P, _P, _I64, _I64, _P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+    L.orc_e4m3_value.restype = ctypes.c_float
 
 
 def _ptr(a):
@@ -201,6 +204,30 @@ def logits(x: np.ndarray, gate_w: np.ndarray) -> np.ndarray:
     out = np.empty((T, E), np.float32)
     _check(lib().orc_logits(_ptr(x), _ptr(gate_w), T, E, H, _ptr(out)), "logits")
     return out
+
+
+def e4m3_value(code: int) -> float:
+    """O11: the value of one OCP FP8 E4M3 (e4m3fn) code."""
+    return float(lib().orc_e4m3_value(code & 0xFF))
+
+
+def dequant_fp8_block(w8: np.ndarray, block_scale: np.ndarray) -> np.ndarray:
+    """O11: uint8 codes [rows, cols] and fp32 scales [ceil(rows/128),
+    ceil(cols/128)] -> fp32 [rows, cols]."""
+    w8 = _c(w8, np.uint8)
+    rows, cols = w8.shape
+    bs = _c(block_scale, np.float32)
+    if bs.shape != ((rows + 127) // 128, (cols + 127) // 128):
+        raise ValueError(f"block scales {bs.shape} do not tile {w8.shape} in 128x128 blocks")
+    out = np.empty((rows, cols), np.float32)
+    _check(lib().orc_dequant_fp8_block(_ptr(w8), _ptr(bs), rows, cols, _ptr(out)), "dequant_fp8_block")
+    return out
+
+
+def requant_fp8_block(bits: int, w8: np.ndarray, block_scale: np.ndarray):
+    """O11 then O1 + O2: the converter's FP8 -> container step; returns
+    (packed codes, row scales)."""
+    return quant_pack(bits, dequant_fp8_block(w8, block_scale))
 
 
 def make_cfg(n_experts, top_k, n_group=1, topk_group=1, norm_topk_prob=1,

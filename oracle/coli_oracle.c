@@ -150,6 +150,43 @@ int orc_quant_pack(int bits, const float *w, int64_t rows, int64_t cols,
 }
 
 /*
+ * O11 -- FP8 checkpoint dequantisation (colibrì README, "Implemented
+ * features": the offline FP8 -> int4 converter dequantises the checkpoint's
+ * 128x128 block-scaled FP8 weights and requantises them into the engine's
+ * container; with O1 + O2 that is the converter's arithmetic).
+ * Reading: the FP8 format is OCP E4M3 with no infinities ("e4m3fn"): bit 7
+ * the sign, bits 6..3 the exponent field e (bias 7), bits 2..0 the mantissa
+ * field m.  e = 0: the subnormal m/8 * 2^-6; e = 15 with m = 7: NaN;
+ * otherwise (1 + m/8) * 2^(e-7).  A block's scale multiplies every value of
+ * its 128x128 tile (blocks start at row 0 and column 0; edge blocks are
+ * partial).  The binary64 product of two binary32 numbers is exact, so
+ * rounding it once gives the binary32 product.
+ */
+float orc_e4m3_value(uint8_t code) {
+  const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m / 8.0, -6);
+  else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return (float)(sign ? -v : v);
+}
+
+int orc_dequant_fp8_block(const uint8_t *w8, const float *block_scale, int64_t rows,
+                          int64_t cols, float *out) {
+  if (rows < 0 || cols <= 0 || !w8 || !block_scale || !out) return ORC_EINVAL;
+  const int64_t nbc = (cols + 127) / 128;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t c = 0; c < cols; ++c) {
+      const double v = (double)orc_e4m3_value(w8[r * cols + c]);
+      const double s = (double)block_scale[(r / 128) * nbc + c / 128];
+      out[r * cols + c] = (float)(v * s);
+    }
+  }
+  return ORC_OK;
+}
+
+/*
  * O3 -- Q8_0-style activation quantisation (colibrì README, "Implemented
  * features", integer dot-product kernels).
  * Reading: blocks of 32 consecutive values along the row starting at column

@@ -117,6 +117,14 @@ int orc_moe_forward(const orc_layer *L, const float *x, int64_t T,
                     const float *logits_in, float *y, int32_t *idx_out,
                     float *w_out, float *logits_out);
 
+/* O11 FP8 checkpoint dequantisation: w8 [rows][cols] OCP FP8 E4M3 ("e4m3fn")
+ * codes, block_scale [ceil(rows/128)][ceil(cols/128)] fp32; out[r][c] =
+ * e4m3(w8[r][c]) * block_scale[r/128][c/128] rounded once to binary32.  The
+ * two NaN codes give NaN.  orc_e4m3_value decodes one code. */
+float orc_e4m3_value(uint8_t code);
+int orc_dequant_fp8_block(const uint8_t *w8, const float *block_scale, int64_t rows,
+                          int64_t cols, float *out);
+
 /* O10 batch-union tables from idx [T][k] (entries -1 are skipped):
  * counts[E], offs[E+1] (exclusive scan), perm[] = t*k+j of each routed pair
  * ordered by (expert, t, j), uniq[] = experts with a nonzero count in
