@@ -21,6 +21,11 @@ line on stdout; details go to stderr.
 
   python bench.py [--steps K] [--warmup W] [--workload decode|verify3|prefill512]
 
+``--workload fp8convert`` measures the checkpoint converter's step on the
+device: one GLM-5.2 expert (gate and up 2048 x 6144, down 6144 x 2048) of
+128x128 block-scaled FP8 E4M3 codes requantised into the packed container
+(int4 unless --bits says otherwise) per step, over 16 resident experts.
+
 ``--workload stack`` measures instead a 40-layer stack of such layers resident
 in HBM (40 x 257 int4 experts, ~195 GB) decoded one token at a time, with a
 Zipf-like expert popularity per layer and expert top-p 0.7; its bytes per
@@ -167,7 +172,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--instances", type=int, default=8)
-    ap.add_argument("--workload", choices=list(WORKLOADS) + ["stack"], default="decode")
+    ap.add_argument("--workload", choices=list(WORKLOADS) + ["stack", "fp8convert"],
+                    default="decode")
     ap.add_argument("--layers", type=int, default=40, help="stack workload: layers resident")
     ap.add_argument("--bits", type=int, choices=(8, 4, 2), default=None,
                     help="weight container of the GLM-5.2-shaped layer (default int4)")
@@ -198,6 +204,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.workload == "stack":
         return stack_main(args)
+    if args.workload == "fp8convert":
+        return fp8_main(args)
     dev = "cuda"
     s = inputs.TINY if args.workload == "tiny" else inputs.GLM
     if args.bits is not None:
@@ -664,6 +672,121 @@ def stack_main(args) -> int:
     }
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = stack_cpu_baseline(stk, xs, ws, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def fp8_main(args) -> int:
+    """FP8 -> container requantisation of GLM-5.2 expert matrices: each step
+    converts one expert's three matrices (three launches of the FP8 kernel),
+    cycling over resident experts so that no step's codes are still cached."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from quantized_moe_coli_amd import binding as B
+    from quantized_moe_coli_amd import inputs
+
+    dev = "cuda"
+    s = inputs.GLM if args.bits is None else inputs.GLM.with_(bits=args.bits)
+    H, I, b = s.hidden, s.inter, s.bits
+    K, W, NE = args.steps, args.warmup, 16
+    shapes = [(I, H), (I, H), (H, I)]  # gate, up, down
+    src = [[inputs.fp8_checkpoint(r, c, 100 + e * 3 + m, dev) for m, (r, c) in enumerate(shapes)]
+           for e in range(NE)]
+    outs = [(torch.empty(r, c * b // 8, dtype=torch.uint8, device=dev),
+             torch.empty(r, device=dev)) for (r, c) in shapes]
+    torch.cuda.synchronize()
+
+    def convert(e):
+        for m in range(3):
+            codes, bs = src[e][m]
+            B.coli_quant_pack_fp8(b, codes, bs, outs[m][0], outs[m][1])
+
+    for t in range(W):
+        convert(t % NE)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for t in range(K):
+        convert(t % NE)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    # each launch's own duration, from events around it on the launch stream
+    KP = min(K, 64)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(KP * 3)]
+    for t in range(KP):
+        for m in range(3):
+            codes, bs = src[t % NE][m]
+            evs[t * 3 + m][0].record()
+            B.coli_quant_pack_fp8(b, codes, bs, outs[m][0], outs[m][1])
+            evs[t * 3 + m][1].record()
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(z) for a, z in evs]))
+
+    code_bytes = 3 * H * I
+    bscale_bytes = sum(((r + 127) // 128) * ((c + 127) // 128) * 4 for r, c in shapes)
+    out_bytes = 3 * H * I * b // 8 + (2 * I + H) * 4
+    step_bytes = code_bytes + bscale_bytes + out_bytes
+    launch_bytes = step_bytes / 3
+    ms_per_step = total_ms / K
+    experts_per_s = K / (total_ms / 1e3)
+    gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    k_gbps = launch_bytes / (k_ms * 1e-3) / 1e9
+    log(f"[bench] fp8convert: {ms_per_step * 1e3:.2f} us/expert, {experts_per_s:.0f} experts/s, "
+        f"{step_bytes / 1e6:.2f} MB/expert -> {gbps:.0f} GB/s; kernel {k_ms * 1e3:.2f} us avg "
+        f"-> {k_gbps:.0f} GB/s")
+
+    result = {
+        "metric": f"FP8 -> int{b} expert requantisation (GLM-5.2 expert, 128x128 block scales)",
+        "value": round(experts_per_s, 1),
+        "unit": "experts/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3->fp32->int%d" % b,
+        "data": "synthetic",
+        "config": {
+            "workload": f"one GLM-5.2 expert per step (gate, up 2048 x 6144; down 6144 x 2048) "
+                        f"of FP8 E4M3 codes with 128x128 fp32 block scales -> packed int{b} "
+                        f"with per-row fp32 scales; {NE} experts resident",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"k_quant_pack_fp8<{b}> (one expert matrix)",
+            "achieved": round(k_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(k_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(k_ms * 1e3, 3),
+            "bytes_per_launch": int(launch_bytes),
+        },
+    }
+    if args.cpu_seconds > 0:
+        B.coli_quant_pack_fp8(b, src[0][0][0], src[0][0][1], outs[0][0], outs[0][1])
+        torch.cuda.synchronize()
+        codes, bs = (t.cpu().numpy() for t in src[0][0])
+        t0 = time.perf_counter()
+        q_ref, s_ref = oracle.requant_fp8_block(b, codes, bs)
+        spent = time.perf_counter() - t0
+        same = (np.array_equal(q_ref, outs[0][0].cpu().numpy())
+                and np.array_equal(s_ref, outs[0][1].cpu().numpy()))
+        result["cpu_baseline"] = {
+            "value": round(1.0 / (3 * spent), 3),
+            "unit": "experts/s",
+            "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the oracle's dequantisation + requantisation of one 2048 x 6144 gate "
+                      f"matrix ({spent:.2f} s), times three for the expert",
+        }
+        result["cpu_baseline"]["gpu_bytes_equal"] = bool(same)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -128,6 +128,24 @@ coli_status coli_quant_pack(int32_t qtype, const float *w, int64_t rows,
                             int64_t cols, uint8_t *q_out, float *scale_out,
                             void *stream);
 
+/* FP8 checkpoint requantisation (colibrì README, "Implemented features": the
+ * offline FP8 -> int4 converter dequantises the 128x128 block-scaled FP8
+ * checkpoint and requantises it into the engine's container).
+ * w8 [rows][cols] OCP FP8 E4M3 codes without infinities (sign, 4-bit
+ * exponent of bias 7, 3-bit mantissa; exponent 0 subnormal), block_scale
+ * [ceil(rows/128)][ceil(cols/128)] fp32, the scale of each 128x128 tile
+ * counted from row 0 and column 0 (edge tiles partial).  Each weight is
+ * fl32(e4m3(code) * block_scale), and the rows are then quantised and packed
+ * exactly as coli_quant_pack does, into q_out [rows][cols*qtype/8] and
+ * scale_out [rows].  The result is bit-identical to coli_quant_pack of the
+ * dequantised fp32 matrix.  cols a positive multiple of 32, rows >= 0;
+ * w8 and q_out 16-byte aligned.  The two NaN codes (0x7F, 0xFF) are not
+ * weights: a row holding one gets unspecified codes and scale. */
+coli_status coli_quant_pack_fp8(int32_t qtype, const uint8_t *w8,
+                                const float *block_scale, int64_t rows,
+                                int64_t cols, uint8_t *q_out, float *scale_out,
+                                void *stream);
+
 /* Q8_0-style activation quantisation (colibrì README, "Implemented
  * features": integer dot products against Q8_0-style int8 activations).
  * x [T][n] fp32 -> q [T][n] int8 (natural order) and d [T][n/32] fp32:

@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "coli_abi_version": ([], ctypes.c_int),
             "coli_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "coli_quant_pack": ([i32, _P, i64, i64, _P, _P, _P], ctypes.c_int),
+            "coli_quant_pack_fp8": ([i32, _P, _P, i64, i64, _P, _P, _P], ctypes.c_int),
             "coli_quant_act_q8_0": ([_P, i32, i32, _P, _P, _P], ctypes.c_int),
             "coli_moe_logits": ([_P, _P, i32, i32, i32, _P, _P], ctypes.c_int),
             "coli_moe_route": ([ctypes.POINTER(RouterCfg), _P, _P, i32, _P, _P, _P], ctypes.c_int),
@@ -132,6 +133,21 @@ def coli_quant_pack(qtype: int, w: torch.Tensor, q_out: torch.Tensor, scale_out:
         raise ValueError("output sizes do not match")
     _check("coli_quant_pack", lib().coli_quant_pack(
         qtype, _ptr(w, torch.float32, "w"), rows, cols, _ptr(q_out, torch.uint8, "q_out"),
+        _ptr(scale_out, torch.float32, "scale_out"), _stream(stream)))
+
+
+def coli_quant_pack_fp8(qtype: int, w8: torch.Tensor, block_scale: torch.Tensor,
+                        q_out: torch.Tensor, scale_out: torch.Tensor, stream=None) -> None:
+    """w8 uint8 FP8 E4M3 codes [rows, cols], block_scale fp32 [ceil(rows/128),
+    ceil(cols/128)] -> q_out uint8 [rows, cols*qtype/8], scale_out fp32 [rows]."""
+    rows, cols = w8.shape
+    if tuple(block_scale.shape) != ((rows + 127) // 128, (cols + 127) // 128):
+        raise ValueError("block scales do not tile the matrix in 128x128 blocks")
+    if q_out.numel() != rows * cols * qtype // 8 or scale_out.numel() != rows:
+        raise ValueError("output sizes do not match")
+    _check("coli_quant_pack_fp8", lib().coli_quant_pack_fp8(
+        qtype, _ptr(w8, torch.uint8, "w8"), _ptr(block_scale, torch.float32, "block_scale"),
+        rows, cols, _ptr(q_out, torch.uint8, "q_out"),
         _ptr(scale_out, torch.float32, "scale_out"), _stream(stream)))
 
 

@@ -150,6 +150,24 @@ coli_status coli_quant_pack(int32_t qtype, const float *w, int64_t rows, int64_t
   });
 }
 
+coli_status coli_quant_pack_fp8(int32_t qtype, const uint8_t *w8, const float *block_scale,
+                                int64_t rows, int64_t cols, uint8_t *q_out, float *scale_out,
+                                void *stream) {
+  return guarded([&] {
+    if (!qtype_ok(qtype) || rows < 0 || cols <= 0 || cols % 32 || !w8 || !block_scale || !q_out ||
+        !scale_out)
+      return COLI_ERR_INVALID_ARG;
+    if (!aligned(w8, 16) || !aligned(q_out, 16) || !aligned(block_scale, 4) ||
+        !aligned(scale_out, 4))
+      return COLI_ERR_INVALID_ARG;
+    if (rows > (int64_t)1 << 34 || cols > (int64_t)1 << 30) return COLI_ERR_UNSUPPORTED;
+    const coli_status d = check_device();
+    if (d != COLI_OK) return d;
+    return from_hip(coli::launch_quant_pack_fp8(qtype, w8, block_scale, rows, cols, q_out,
+                                                scale_out, static_cast<hipStream_t>(stream)));
+  });
+}
+
 coli_status coli_quant_act_q8_0(const float *x, int32_t T, int32_t n, int8_t *q, float *d,
                                 void *stream) {
   return guarded([&] {

@@ -47,6 +47,83 @@ __global__ __launch_bounds__(256) void k_quant_pack(const float *__restrict__ w,
   }
 }
 
+// FP8 checkpoint requantisation (colibrì README, "Implemented features": the
+// offline FP8 -> int4 converter dequantises the checkpoint's 128x128
+// block-scaled FP8 weights and requantises them into the engine's
+// container).  The FP8 format is OCP E4M3 without infinities: bit 7 sign,
+// bits 6..3 exponent (bias 7), bits 2..0 mantissa; exponent 0 is subnormal
+// (m * 2^-9), exponent 15 with mantissa 7 is NaN.  Decoded here by placing
+// the fields into a binary32 word, which is exact for every code.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  if (e == 15u && m == 7u) v = __uint_as_float(0x7fc00000u);
+  return __uint_as_float(__float_as_uint(v) | ((c & 0x80u) << 24));
+}
+
+// The 16 dequantised values of one 16-byte chunk of codes: each code's value
+// times its block's scale, one correctly rounded binary32 product.
+__device__ __forceinline__ void fp8_chunk(const uint4 c, float s, float (&v)[16]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = e4m3_value((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * s;
+}
+
+// One wave per row; a lane handles 16-byte chunks of 16 codes, chunk j
+// lying in block column j/8.  The first pass finds the row's absmax, the
+// second re-reads the row (now in cache), quantises with the same rule as
+// k_quant_pack and stores the chunk's 16 codes as one 4-, 8- or 16-byte word
+// group, so consecutive lanes write consecutive bytes.
+template <int BITS>
+__global__ __launch_bounds__(256) void k_quant_pack_fp8(const uint8_t *__restrict__ w8,
+                                                        const float *__restrict__ bscale,
+                                                        int64_t rows, int64_t cols,
+                                                        uint8_t *__restrict__ q,
+                                                        float *__restrict__ scale) {
+  constexpr float kQmax = BITS == 8 ? 127.f : (BITS == 4 ? 7.f : 1.f);
+  constexpr int kPer = 32 / BITS;  // codes per 32-bit output word
+  constexpr int kWords = 16 / kPer;
+  constexpr uint32_t kMask = (1u << BITS) - 1u;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t chunks = cols / 16;
+  const uint4 *src = reinterpret_cast<const uint4 *>(w8 + row * cols);
+  const float *bs = bscale + (row / 128) * ((cols + 127) / 128);
+
+  float amax = 0.f;
+  for (int64_t j = lane; j < chunks; j += 64) {
+    float v[16];
+    fp8_chunk(src[j], bs[j >> 3], v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+  amax = wave_max(amax);
+  const float s = amax / kQmax;  // IEEE binary32 division
+  if (lane == 0) scale[row] = s;
+
+  uint32_t *dst = reinterpret_cast<uint32_t *>(q + row * (cols * BITS / 8));
+  for (int64_t j = lane; j < chunks; j += 64) {
+    float v[16];
+    fp8_chunk(src[j], bs[j >> 3], v);
+    uint32_t word[kWords];
+#pragma unroll
+    for (int k = 0; k < kWords; ++k) word[k] = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float c = 0.f;
+      if (s != 0.f) c = fminf(fmaxf(rintf(v[i] / s), -kQmax), kQmax);
+      word[i / kPer] |= ((uint32_t)(int32_t)c & kMask) << (BITS * (i % kPer));
+    }
+    if constexpr (kWords == 4)
+      reinterpret_cast<uint4 *>(dst)[j] = make_uint4(word[0], word[1], word[2], word[3]);
+    else if constexpr (kWords == 2)
+      reinterpret_cast<uint2 *>(dst)[j] = make_uint2(word[0], word[1]);
+    else
+      dst[j] = word[0];
+  }
+}
+
 // One thread per Q8_0 block of 32 values (act_quant_block, actq.hpp).
 template <int BITS>
 __global__ __launch_bounds__(256) void k_act_quant(const float *__restrict__ x, int64_t T,
@@ -68,6 +145,19 @@ hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t col
     case 8: hipLaunchKernelGGL(k_quant_pack<8>, grid, block, 0, st, w, rows, cols, qw, scale); break;
     case 4: hipLaunchKernelGGL(k_quant_pack<4>, grid, block, 0, st, w, rows, cols, qw, scale); break;
     case 2: hipLaunchKernelGGL(k_quant_pack<2>, grid, block, 0, st, w, rows, cols, qw, scale); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_pack_fp8(int bits, const uint8_t *w8, const float *bscale, int64_t rows,
+                                 int64_t cols, uint8_t *q, float *scale, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  switch (bits) {
+    case 8: hipLaunchKernelGGL(k_quant_pack_fp8<8>, grid, block, 0, st, w8, bscale, rows, cols, q, scale); break;
+    case 4: hipLaunchKernelGGL(k_quant_pack_fp8<4>, grid, block, 0, st, w8, bscale, rows, cols, q, scale); break;
+    case 2: hipLaunchKernelGGL(k_quant_pack_fp8<2>, grid, block, 0, st, w8, bscale, rows, cols, q, scale); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

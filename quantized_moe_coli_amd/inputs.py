@@ -28,7 +28,7 @@ import torch
 
 # roles: distinct streams for each kind of tensor
 _ROLE = {"gate_w": 1, "bias": 2, "w_gate": 3, "w_up": 4, "w_down": 5,
-         "x": 6, "logit_z": 7, "logit_eps": 8, "zipf": 9}
+         "x": 6, "logit_z": 7, "logit_eps": 8, "zipf": 9, "fp8_codes": 10, "fp8_scale": 11}
 
 
 @dataclass(frozen=True)
@@ -122,3 +122,22 @@ def zipf_logit_offsets(seed: int, layer: int, E: int, s_exp: float = 1.1,
     g = _gen("cpu", seed, _ROLE["zipf"], layer)
     rank = torch.randperm(E, generator=g)
     return (-s_exp * torch.log(rank.double() + 1.0)).float().to(device)
+
+
+def fp8_checkpoint(rows: int, cols: int, seed: int, device="cpu"):
+    """A synthetic FP8 checkpoint matrix as a block-scaled FP8 checkpoint
+    stores it: uint8 OCP E4M3 codes [rows, cols] and fp32 scales
+    [ceil(rows/128), ceil(cols/128)].  The codes are torch's float8_e4m3fn
+    storage of N(0, 100^2) draws clipped to the format's +-448 (so they span
+    the format's normal and subnormal codes and both zeros); the block scales
+    are uniform in [1e-4, 4e-4], which puts the weights at the N(0, 0.02)
+    scale of the layer's other weights.  No NaN code is produced."""
+    g = _gen(device, seed, _ROLE["fp8_codes"], rows, cols)
+    v = torch.randn((rows, cols), generator=g, device=device, dtype=torch.float32)
+    v.mul_(100.0).clamp_(-448.0, 448.0)
+    codes = v.to(torch.float8_e4m3fn).view(torch.uint8)
+    g = _gen(device, seed, _ROLE["fp8_scale"], rows, cols)
+    bs = torch.rand(((rows + 127) // 128, (cols + 127) // 128), generator=g, device=device,
+                    dtype=torch.float32)
+    bs.mul_(3e-4).add_(1e-4)
+    return codes.contiguous(), bs

@@ -49,6 +49,14 @@ def test_invalid_arguments_rejected_before_device():
     assert L.coli_quant_pack(4, None, 4, 32, _fake(16), _fake(16), None) == B.COLI_ERR_INVALID_ARG
     assert L.coli_quant_pack(4, _fake(16), 4, 48, _fake(16), _fake(16), None) == B.COLI_ERR_INVALID_ARG
     assert L.coli_quant_act_q8_0(_fake(16), 1, 33, _fake(16), _fake(16), None) == B.COLI_ERR_INVALID_ARG
+    # FP8 requantisation: bad qtype, null scales, ragged columns, misaligned codes or output
+    f = _fake
+    assert L.coli_quant_pack_fp8(5, f(16), f(16), 4, 32, f(16), f(16), None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_quant_pack_fp8(4, f(16), None, 4, 32, f(16), f(16), None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_quant_pack_fp8(4, f(16), f(16), 4, 40, f(16), f(16), None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_quant_pack_fp8(4, f(8), f(16), 4, 32, f(16), f(16), None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_quant_pack_fp8(4, f(16), f(16), 4, 32, f(8), f(16), None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_quant_pack_fp8(4, f(16), f(16), -1, 32, f(16), f(16), None) == B.COLI_ERR_INVALID_ARG
     assert L.coli_quant_act_q8_0(_fake(8), 1, 32, _fake(16), _fake(16), None) == B.COLI_ERR_INVALID_ARG
     assert L.coli_moe_logits(_fake(16), _fake(16), 1, 0, 64, _fake(16), None) == B.COLI_ERR_INVALID_ARG
     bad = B.router_cfg(256, 8, 7, 4)  # 256 % 7 != 0
@@ -129,6 +137,8 @@ def test_no_device_reports_device_error():
     assert L.coli_moe_forward(ctypes.byref(good), _fake(0x100000), 1, None, _fake(0x200000),
                               None, None, None, _fake(0x300000), ws, None) == B.COLI_ERR_DEVICE
     assert L.coli_quant_pack(4, _fake(16), 4, 32, _fake(16), _fake(16), None) == B.COLI_ERR_DEVICE
+    assert L.coli_quant_pack_fp8(4, _fake(16), _fake(16), 4, 32, _fake(16), _fake(16), None) \
+        == B.COLI_ERR_DEVICE
     cfg = B.router_cfg(16, 2)
     assert L.coli_moe_route(ctypes.byref(cfg), _fake(16), None, 1, _fake(16), _fake(16), None) \
         == B.COLI_ERR_DEVICE

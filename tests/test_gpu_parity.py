@@ -66,6 +66,62 @@ def test_quant_pack_full_expert(orc, bits):
     np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
 
 
+def _fp8_requant_gpu(bits, codes, bs):
+    R, C = codes.shape
+    q = torch.empty(R, C * bits // 8, dtype=torch.uint8, device="cuda")
+    s = torch.empty(R, device="cuda")
+    B.coli_quant_pack_fp8(bits, codes.cuda(), bs.cuda(), q, s)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("bits", [4, 8, 2])
+@pytest.mark.parametrize("R,C", [(1, 32), (200, 96), (130, 288), (256, 1024)])
+def test_fp8_requant_bit_exact(orc, bits, R, C):
+    """FP8 block-scaled codes -> container on the GPU equals the oracle's
+    dequantisation followed by its quantisation and packing.  The shapes put
+    rows and columns across ragged 128x128 tiles; special rows hold zeros of
+    both signs only (scale 0), the format's extreme codes, and subnormals."""
+    codes, bs = inputs.fp8_checkpoint(R, C, 5, "cpu")
+    c = codes.numpy().copy()
+    if R >= 4:
+        c[0] = 0x80                                  # -0.0 everywhere: zero row
+        c[1, :] = 0x00
+        c[1, 3] = 0x7E                               # +448 spike
+        c[2] = np.resize(np.array([0x01, 0x81, 0x07, 0x87, 0x08], np.uint8), C)  # subnormals
+        c[3, ::2] = 0xFE                             # -448 and random codes
+    codes = torch.from_numpy(c)
+    q, s = _fp8_requant_gpu(bits, codes, bs)
+    q_ref, s_ref = orc.requant_fp8_block(bits, c, bs.numpy())
+    np.testing.assert_array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(q, q_ref)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("R,C", [(2048, 6144), (6144, 2048)])
+def test_fp8_requant_full_expert(orc, bits, R, C):
+    """GLM-5.2-shaped expert matrices (gate/up 2048 x 6144, down 6144 x 2048)."""
+    codes, bs = inputs.fp8_checkpoint(R, C, 6, "cpu")
+    q, s = _fp8_requant_gpu(bits, codes, bs)
+    q_ref, s_ref = orc.requant_fp8_block(bits, codes.numpy(), bs.numpy())
+    np.testing.assert_array_equal(s, s_ref)
+    np.testing.assert_array_equal(q, q_ref)
+
+
+def test_fp8_requant_equals_fp32_pack_on_device(orc):
+    """Through the oracle's dequantised fp32 matrix, the FP8 entry point and
+    coli_quant_pack write the same bytes and scales."""
+    codes, bs = inputs.fp8_checkpoint(384, 640, 7, "cpu")
+    q, s = _fp8_requant_gpu(4, codes, bs)
+    w = to_dev(orc.dequant_fp8_block(codes.numpy(), bs.numpy()))
+    q2 = torch.empty(384, 320, dtype=torch.uint8, device="cuda")
+    s2 = torch.empty(384, device="cuda")
+    B.coli_quant_pack(4, w, q2, s2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q, q2.cpu().numpy())
+    np.testing.assert_array_equal(s.view(np.uint32), s2.cpu().numpy().view(np.uint32))
+
+
 @pytest.mark.parametrize("T,n", [(1, 32), (3, 256), (17, 6144), (512, 2048)])
 def test_act_quant_bit_exact(orc, T, n):
     rng = np.random.default_rng(T + n)
