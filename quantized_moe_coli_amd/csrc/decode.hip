@@ -68,6 +68,9 @@ constexpr int kDecThreads = 64 * kDecWaves;
 constexpr uint32_t kSpinLimit = 1u << 19;  // ~100 ms of polling
 constexpr int kLogRows = 2;                // logit rows per L item (four waves each)
 constexpr int kGuRows = 32;                // gate/up rows per GS/GR item
+// cache-policy bits of global_load_lds giving sc1, the policy of the relaxed
+// device-scope loads, so staged data is as coherent across XCDs as theirs
+constexpr int kLoadSc1 = 16;
 
 struct DecodeArgs {
   FfnArgs f;
@@ -243,13 +246,37 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
       const int sl = g0 + q == 0 ? k : g0 + q - 1;
       const uint32_t *c = d.ctr + kCtrSlot0 + sl * kCtrStride;
       uint32_t it = 0;
-      while (ld_ctr(c) < (uint32_t)(I / kGuRows) && it < kSpinLimit) {
-        __builtin_amdgcn_s_sleep(64);
+      while (ld_ctr(c) < (uint32_t)(I / kGuRows) && it < kSpinLimit * 8) {
+        __builtin_amdgcn_s_sleep(8);
         ++it;
       }
     }
     __syncthreads();
-    {
+    if (I % 128 == 0) {
+      // straight into LDS: 16-byte loads with the cache policy of the
+      // device-scope loads (sc1), all in flight at once and no registers.
+      // One wave instruction fills 64 consecutive 16-byte LDS chunks.
+      const int cq = I / 16, cd = I / 128;  // chunks of codes / of scales per slot
+      const int nA = gn * cq, nB = gn * cd;
+      const int nwA = (nA + 63) / 64, nwB = (nB + 63) / 64;
+      for (int ii = wave; ii < nwA + nwB; ii += kDecWaves) {
+        const bool codes = ii < nwA;
+        const int base = (codes ? ii : ii - nwA) * 64;
+        const int c = base + lane, per = codes ? cq : cd;
+        unsigned char *dst = (codes ? reinterpret_cast<unsigned char *>(lds_q)
+                                    : reinterpret_cast<unsigned char *>(lds_d)) + (size_t)base * 16;
+        if (c < (codes ? nA : nB)) {
+          const int q = c / per, r = c - q * per;
+          const int sl = g0 + q == 0 ? k : g0 + q - 1;
+          const unsigned char *src =
+              codes ? reinterpret_cast<const unsigned char *>(a.hq) + (size_t)sl * I + r * 16
+                    : reinterpret_cast<const unsigned char *>(a.hd) + (size_t)sl * (I / 8) + r * 16;
+          __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0,
+                                           kLoadSc1);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
       // 64-bit device-scope loads, kStage per thread issued before any is
       // written to LDS
       constexpr int kStage = 2;
@@ -321,7 +348,8 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
 // (tickets only increase, so a workgroup never returns to gate/up work
 // after a D item, whose staging overwrites x's codes).
 template <int BITS, int GLPR, int GCPL, int DLPR, int DCPL>
-__global__ __launch_bounds__(kDecThreads) void k_decode_fused(DecodeArgs d) {
+__global__ __launch_bounds__(kDecThreads)
+__attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(DecodeArgs d) {
   constexpr int DNPASS = DCPL == 1 ? 2 : 1;
   constexpr int DSG = DCPL == 1 ? 9 : 3;
   constexpr int BLK = kGuRows / 32;
@@ -346,17 +374,21 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_fused(DecodeArgs d) {
   // Work queue q = b % 8 holds items q, q + 8, ...; consecutive workgroups
   // go to consecutive XCDs, so each XCD streams an equal share of every
   // kind of item.  Within a queue the items keep their global order.
+  // A workgroup's first item is its own index (queue q's nq workgroups take
+  // its first nq items in order), which saves the first atomic round trip;
+  // later tickets come from the queue's counter, offset by nq.
   const int q = blockIdx.x % kQueues;
+  const int nq = ((int)gridDim.x - q + kQueues - 1) / kQueues;
   auto next_ticket = [&]() -> int {
     if (threadIdx.x == 0)
       s_ticket = (int)__hip_atomic_fetch_add(d.ctr + kCtrTicket + q * kCtrStride, 1u,
                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const int t = q + kQueues * uniform_i32(s_ticket);
+    const int t = q + kQueues * (nq + uniform_i32(s_ticket));
     __syncthreads();
     return t;
   };
-  int t = next_ticket();
+  int t = (int)blockIdx.x;
 
   // L: two logit rows per item
   for (; t < b_gsh; t = next_ticket()) {

@@ -69,58 +69,103 @@ __device__ __forceinline__ void fp8_chunk(const uint4 c, float s, float (&v)[16]
   for (int i = 0; i < 16; ++i) v[i] = e4m3_value((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * s;
 }
 
-// One wave per row; a lane handles 16-byte chunks of 16 codes, chunk j
-// lying in block column j/8.  The first pass finds the row's absmax, the
-// second re-reads the row (now in cache), quantises with the same rule as
-// k_quant_pack and stores the chunk's 16 codes as one 4-, 8- or 16-byte word
-// group, so consecutive lanes write consecutive bytes.
+// Quantises and packs the 16 values of one chunk (same rule as
+// k_quant_pack) and stores them as one 4-, 8- or 16-byte group, so that
+// consecutive lanes write consecutive bytes.
 template <int BITS>
+__device__ __forceinline__ void fp8_store_chunk(const float (&v)[16], float s, uint32_t *dst,
+                                                int64_t j) {
+  constexpr float kQmax = BITS == 8 ? 127.f : (BITS == 4 ? 7.f : 1.f);
+  constexpr int kPer = 32 / BITS;  // codes per 32-bit output word
+  constexpr int kWords = 16 / kPer;
+  constexpr uint32_t kMask = (1u << BITS) - 1u;
+  uint32_t word[kWords];
+#pragma unroll
+  for (int k = 0; k < kWords; ++k) word[k] = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float c = 0.f;
+    if (s != 0.f) c = fminf(fmaxf(rintf(v[i] / s), -kQmax), kQmax);
+    word[i / kPer] |= ((uint32_t)(int32_t)c & kMask) << (BITS * (i % kPer));
+  }
+  if constexpr (kWords == 4)
+    reinterpret_cast<uint4 *>(dst)[j] = make_uint4(word[0], word[1], word[2], word[3]);
+  else if constexpr (kWords == 2)
+    reinterpret_cast<uint2 *>(dst)[j] = make_uint2(word[0], word[1]);
+  else
+    dst[j] = word[0];
+}
+
+// One wave per row; a lane handles 16-byte chunks of 16 codes, chunk j
+// lying in block column j/8.  NC > 0: the row has at most 64*NC chunks, and
+// each lane loads all of its chunks at once and keeps them in registers
+// (one read of the row, every load in flight together); the absmax and the
+// codes are then computed from the registers.  NC = 0: longer rows, read
+// twice (the second time from cache).
+template <int BITS, int NC>
 __global__ __launch_bounds__(256) void k_quant_pack_fp8(const uint8_t *__restrict__ w8,
                                                         const float *__restrict__ bscale,
                                                         int64_t rows, int64_t cols,
                                                         uint8_t *__restrict__ q,
                                                         float *__restrict__ scale) {
   constexpr float kQmax = BITS == 8 ? 127.f : (BITS == 4 ? 7.f : 1.f);
-  constexpr int kPer = 32 / BITS;  // codes per 32-bit output word
-  constexpr int kWords = 16 / kPer;
-  constexpr uint32_t kMask = (1u << BITS) - 1u;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int64_t chunks = cols / 16;
   const uint4 *src = reinterpret_cast<const uint4 *>(w8 + row * cols);
   const float *bs = bscale + (row / 128) * ((cols + 127) / 128);
-
-  float amax = 0.f;
-  for (int64_t j = lane; j < chunks; j += 64) {
-    float v[16];
-    fp8_chunk(src[j], bs[j >> 3], v);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  }
-  amax = wave_max(amax);
-  const float s = amax / kQmax;  // IEEE binary32 division
-  if (lane == 0) scale[row] = s;
-
   uint32_t *dst = reinterpret_cast<uint32_t *>(q + row * (cols * BITS / 8));
-  for (int64_t j = lane; j < chunks; j += 64) {
-    float v[16];
-    fp8_chunk(src[j], bs[j >> 3], v);
-    uint32_t word[kWords];
+
+  if constexpr (NC > 0) {
+    uint4 c[NC];
+    float sc[NC];
 #pragma unroll
-    for (int k = 0; k < kWords; ++k) word[k] = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float c = 0.f;
-      if (s != 0.f) c = fminf(fmaxf(rintf(v[i] / s), -kQmax), kQmax);
-      word[i / kPer] |= ((uint32_t)(int32_t)c & kMask) << (BITS * (i % kPer));
+    for (int i = 0; i < NC; ++i) {
+      const int64_t j = lane + 64 * i;
+      c[i] = j < chunks ? src[j] : make_uint4(0, 0, 0, 0);
+      sc[i] = j < chunks ? bs[j >> 3] : 0.f;
     }
-    if constexpr (kWords == 4)
-      reinterpret_cast<uint4 *>(dst)[j] = make_uint4(word[0], word[1], word[2], word[3]);
-    else if constexpr (kWords == 2)
-      reinterpret_cast<uint2 *>(dst)[j] = make_uint2(word[0], word[1]);
-    else
-      dst[j] = word[0];
+    // E4M3 magnitudes grow with the low seven bits of the code and binary32
+    // rounding is monotonic, so a chunk's largest |value * scale| is that of
+    // its largest seven-bit magnitude: one decode per chunk
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const uint32_t w[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
+      uint32_t m = 0;
+#pragma unroll
+      for (int b = 0; b < 16; ++b) m = max(m, (w[b >> 2] >> (8 * (b & 3))) & 0x7Fu);
+      amax = fmaxf(amax, fabsf(e4m3_value(m) * sc[i]));
+    }
+    amax = wave_max(amax);
+    const float s = amax / kQmax;  // IEEE binary32 division
+    if (lane == 0) scale[row] = s;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int64_t j = lane + 64 * i;
+      if (j < chunks) {
+        float v[16];
+        fp8_chunk(c[i], sc[i], v);
+        fp8_store_chunk<BITS>(v, s, dst, j);
+      }
+    }
+  } else {
+    float amax = 0.f;
+    for (int64_t j = lane; j < chunks; j += 64) {
+      float v[16];
+      fp8_chunk(src[j], bs[j >> 3], v);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) amax = fmaxf(amax, fabsf(v[m]));
+    }
+    amax = wave_max(amax);
+    const float s = amax / kQmax;
+    if (lane == 0) scale[row] = s;
+    for (int64_t j = lane; j < chunks; j += 64) {
+      float v[16];
+      fp8_chunk(src[j], bs[j >> 3], v);
+      fp8_store_chunk<BITS>(v, s, dst, j);
+    }
   }
 }
 
@@ -150,17 +195,33 @@ hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t col
   return hipGetLastError();
 }
 
+template <int BITS>
+static hipError_t launch_fp8_bits(const uint8_t *w8, const float *bscale, int64_t rows,
+                                  int64_t cols, uint8_t *q, float *scale, hipStream_t st) {
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const int64_t per_lane = (cols / 16 + 63) / 64;  // chunks per lane
+  if (per_lane <= 1)
+    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, 1>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
+  else if (per_lane <= 2)
+    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, 2>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
+  else if (per_lane <= 4)
+    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, 4>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
+  else if (per_lane <= 8)
+    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, 8>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
+  else
+    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, 0>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_pack_fp8(int bits, const uint8_t *w8, const float *bscale, int64_t rows,
                                  int64_t cols, uint8_t *q, float *scale, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   switch (bits) {
-    case 8: hipLaunchKernelGGL(k_quant_pack_fp8<8>, grid, block, 0, st, w8, bscale, rows, cols, q, scale); break;
-    case 4: hipLaunchKernelGGL(k_quant_pack_fp8<4>, grid, block, 0, st, w8, bscale, rows, cols, q, scale); break;
-    case 2: hipLaunchKernelGGL(k_quant_pack_fp8<2>, grid, block, 0, st, w8, bscale, rows, cols, q, scale); break;
+    case 8: return launch_fp8_bits<8>(w8, bscale, rows, cols, q, scale, st);
+    case 4: return launch_fp8_bits<4>(w8, bscale, rows, cols, q, scale, st);
+    case 2: return launch_fp8_bits<2>(w8, bscale, rows, cols, q, scale, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_act_quant(int layout_bits, const float *x, int64_t T, int64_t n, int8_t *q,

@@ -293,12 +293,106 @@ __device__ __forceinline__ int beats(float v2, int e2, float v, int e) {
   return (v2 > v || (v2 == v && e2 < e)) ? 1 : 0;
 }
 
+// The last step of a selection: ranks M candidates (biased scores candv,
+// expert ids cande; sig_of(m, e) gives candidate m's sigmoid score) by
+// (value desc, index asc), keeps the k best in rank order and writes their
+// weights -- normalised by the binary32 sum of the kept sigmoids in rank
+// order, times rsf -- with expert top-p applied if configured.  P threads
+// share a candidate, so the ranking is spread over the whole workgroup.
+// slot[0..k) must hold -1 on entry (visible to every thread).
+template <int NT, typename SigOf>
+__device__ __forceinline__ void rank_and_weigh(const RouterCfg &cfg, int M, const float *candv,
+                                               const int *cande, SigOf sig_of, int *slot,
+                                               float *ssig, float *pn, int *keep, float &sum,
+                                               int32_t *idx_out, float *w_out) {
+  const int tid = threadIdx.x, k = cfg.k;
+  // rank of each candidate = number of candidates that beat it; P lanes of a
+  // wave share a candidate (P a power of two, P * candidates <= NT)
+  int P = 1;
+  while (P < 64 && 2 * P * M <= NT) P *= 2;
+  const int per_pass = NT / P;
+  for (int m0 = 0; m0 < M; m0 += per_pass) {
+    const int m = m0 + tid / P, part = tid % P;
+    const bool valid = m < M;
+    const float v = valid ? candv[m] : 0.f;
+    const int e = valid ? cande[m] : 0;
+    int r = 0;
+    if (valid)
+      for (int q = part; q < M; q += P) r += beats(candv[q], cande[q], v, e);
+    for (int o = 1; o < P; o *= 2) r += __shfl_xor(r, o, 64);
+    if (valid && part == 0 && r < k) {
+      slot[r] = e;
+      ssig[r] = sig_of(m, e);
+    }
+  }
+  __syncthreads();
+
+  // weights: the sums run in rank order (one thread), slot j by thread j
+  if (tid == 0) {
+    float S = 0.f;
+    for (int j = 0; j < k; ++j)
+      if (slot[j] >= 0) S += ssig[j];
+    sum = S;
+  }
+  __syncthreads();
+  const float S = sum;
+  int my_i = -1;
+  float my_w = 0.f, my_s = 0.f;
+  if (tid < k) {
+    my_i = slot[tid];
+    if (my_i >= 0) {
+      my_s = ssig[tid];
+      if (cfg.norm) my_w = (S != 0.f) ? (my_s / S) * cfg.rsf : 0.f;
+      else my_w = my_s * cfg.rsf;
+    }
+  }
+  if (cfg.top_p > 0.f && cfg.top_p < 1.f) {
+    if (tid < k) {
+      pn[tid] = (S != 0.f && my_i >= 0) ? my_s / S : 0.f;
+      keep[tid] = 0;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t seen = 0;
+      float cum = 0.f;
+      for (int n = 0; n < k; ++n) {
+        int best = -1;
+        for (int j = 0; j < k; ++j)
+          if (!((seen >> j) & 1u) && (best < 0 || pn[j] > pn[best])) best = j;
+        seen |= 1u << best;
+        keep[best] = 1;
+        cum += pn[best];
+        if (cum >= cfg.top_p) break;
+      }
+      float Sk = 0.f;
+      for (int j = 0; j < k; ++j)
+        if (keep[j] && slot[j] >= 0) Sk += ssig[j];
+      sum = Sk;
+    }
+    __syncthreads();
+    if (tid < k) {
+      const float Sk = sum;
+      if (!keep[tid] || my_i < 0) {
+        my_i = -1;
+        my_w = 0.f;
+      } else if (cfg.renorm) {
+        my_w = (Sk != 0.f) ? (my_s / Sk) * cfg.rsf : 0.f;
+      }
+    }
+  }
+  if (tid < k) {
+    idx_out[tid] = my_i;
+    w_out[tid] = my_w;
+  }
+  __syncthreads();
+}
+
 // `in`: the token's scores (typically in LDS).
 template <int NT>
 __device__ __forceinline__ void select_wg(const RouterCfg &cfg, const SelInput &in,
                                           SelWgScratch &sc, int32_t *idx_out, float *w_out) {
   const int tid = threadIdx.x;
-  const int E = cfg.E, k = cfg.k, G = cfg.n_group, per = E / G;
+  const int E = cfg.E, G = cfg.n_group, per = E / G;
   const float *cval = in.c, *sig = in.sg;
   if (tid < kSelMaxK) sc.slot[tid] = -1;
   if (tid < 64) sc.gkeep[tid] = tid < G ? tid : 0;  // valid ids even if NaN scores tie every rank
@@ -338,85 +432,8 @@ __device__ __forceinline__ void select_wg(const RouterCfg &cfg, const SelInput &
   }
   __syncthreads();
 
-  // rank of each candidate = number of candidates that beat it; P lanes of a
-  // wave share a candidate (P a power of two, P * candidates <= NT)
-  int P = 1;
-  while (P < 64 && 2 * P * M <= NT) P *= 2;
-  const int per_pass = NT / P;
-  for (int m0 = 0; m0 < M; m0 += per_pass) {
-    const int m = m0 + tid / P, part = tid % P;
-    const bool valid = m < M;
-    const float v = valid ? sc.candv[m] : 0.f;
-    const int e = valid ? sc.cande[m] : 0;
-    int r = 0;
-    if (valid)
-      for (int q = part; q < M; q += P) r += beats(sc.candv[q], sc.cande[q], v, e);
-    for (int o = 1; o < P; o *= 2) r += __shfl_xor(r, o, 64);
-    if (valid && part == 0 && r < k) {
-      sc.slot[r] = e;
-      sc.ssig[r] = sig[e];
-    }
-  }
-  __syncthreads();
-
-  // weights: the sums run in rank order (one thread), slot j by thread j
-  if (tid == 0) {
-    float S = 0.f;
-    for (int j = 0; j < k; ++j)
-      if (sc.slot[j] >= 0) S += sc.ssig[j];
-    sc.sum = S;
-  }
-  __syncthreads();
-  const float S = sc.sum;
-  int my_i = -1;
-  float my_w = 0.f, my_s = 0.f;
-  if (tid < k) {
-    my_i = sc.slot[tid];
-    if (my_i >= 0) {
-      my_s = sc.ssig[tid];
-      if (cfg.norm) my_w = (S != 0.f) ? (my_s / S) * cfg.rsf : 0.f;
-      else my_w = my_s * cfg.rsf;
-    }
-  }
-  if (cfg.top_p > 0.f && cfg.top_p < 1.f) {
-    if (tid < k) {
-      sc.pn[tid] = (S != 0.f && my_i >= 0) ? my_s / S : 0.f;
-      sc.keep[tid] = 0;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t seen = 0;
-      float cum = 0.f;
-      for (int n = 0; n < k; ++n) {
-        int best = -1;
-        for (int j = 0; j < k; ++j)
-          if (!((seen >> j) & 1u) && (best < 0 || sc.pn[j] > sc.pn[best])) best = j;
-        seen |= 1u << best;
-        sc.keep[best] = 1;
-        cum += sc.pn[best];
-        if (cum >= cfg.top_p) break;
-      }
-      float Sk = 0.f;
-      for (int j = 0; j < k; ++j)
-        if (sc.keep[j] && sc.slot[j] >= 0) Sk += sc.ssig[j];
-      sc.sum = Sk;
-    }
-    __syncthreads();
-    if (tid < k) {
-      const float Sk = sc.sum;
-      if (!sc.keep[tid] || my_i < 0) {
-        my_i = -1;
-        my_w = 0.f;
-      } else if (cfg.renorm) {
-        my_w = (Sk != 0.f) ? (my_s / Sk) * cfg.rsf : 0.f;
-      }
-    }
-  }
-  if (tid < k) {
-    idx_out[tid] = my_i;
-    w_out[tid] = my_w;
-  }
-  __syncthreads();
+  rank_and_weigh<NT>(cfg, M, sc.candv, sc.cande, [&](int, int e) { return sig[e]; }, sc.slot, sc.ssig,
+                     sc.pn, sc.keep, sc.sum, idx_out, w_out);
 }
 
 
@@ -440,6 +457,9 @@ struct SelFastScratch {
   __align__(16) float gs[64];
   __align__(16) int slot[kSelMaxK];
   __align__(16) float ssig[kSelMaxK];
+  float pn[kSelMaxK];
+  int keep[kSelMaxK];
+  float sum;
 };
 
 __host__ __device__ __forceinline__ bool select_fast_ok(int E, int G, int topk_group, int k,
@@ -482,7 +502,7 @@ __device__ __forceinline__ int count_beating(const float *v, int base, float x, 
 template <int NT, int PER>
 __device__ __forceinline__ void select_fast_t(const RouterCfg &cfg, const SelInput &in,
                                               SelFastScratch &sc, int32_t *idx_out, float *w_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int E = cfg.E, k = cfg.k, G = cfg.n_group;
   const int kk = k < PER ? k : PER;  // candidates per kept group
   const bool valid = tid < E;
@@ -518,46 +538,55 @@ __device__ __forceinline__ void select_fast_t(const RouterCfg &cfg, const SelInp
   }
   __syncthreads();
 
-  if (wave == 0) {
-    // lane m < M holds candidate m; its rank among all candidates comes from
-    // wave-uniform lane reads (no memory round trips)
-    const int M = __popcll(gmask) * kk;
-    const bool cand = lane < M;
-    const float v = cand ? sc.candv[lane] : 0.f;
-    const int e = cand ? sc.cande[lane] : 0;
-    const float sgv = cand ? sc.cands[lane] : 0.f;
-    int r = 0;
-    for (int j = 0; j < M; ++j) {
-      const float v2 = rdlane(v, j);
-      const int e2 = __builtin_amdgcn_readlane(e, j);
-      r += (v2 > v || (v2 == v && e2 < e)) ? 1 : 0;
+  // rank of each candidate among the M <= 64: P = NT/64 consecutive lanes
+  // share candidate m, each comparing it with every P-th candidate; the
+  // partial counts are summed with DPP (exact: counts are small integers)
+  constexpr int P = NT / 64;
+  static_assert(P >= 1 && P <= 16 && (P & (P - 1)) == 0, "P lanes per candidate");
+  const int M = __popcll(gmask) * kk;
+  {
+    const int m = tid / P, part = tid % P;
+    const bool valid = m < M;
+    const float v = valid ? sc.candv[m] : 0.f;
+    const int e = valid ? sc.cande[m] : 0;
+    float r = 0.f;
+    if (valid)
+      for (int q2 = part; q2 < M; q2 += P) r += (float)beats(sc.candv[q2], sc.cande[q2], v, e);
+    r = group_sum<P>(r);
+    if (valid && part == 0 && (int)r < k) {
+      sc.slot[(int)r] = e;
+      sc.ssig[(int)r] = sc.cands[m];
     }
-    const bool win = cand && r < k;
-    // S = sum of the winners' sigma in rank (slot) order
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // wave 0, lane j < k: slot j.  S = the kept sigmoids summed in slot
+    // order, read across lanes (no memory round trips)
+    const int my_i = lane < k ? sc.slot[lane] : -1;
+    const bool win = my_i >= 0;
+    const float sgv = win ? sc.ssig[lane] : 0.f;
     float S = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const unsigned long long who = __ballot(win && r == j);
-      if (who) S += rdlane(sgv, __ffsll((long long)who) - 1);
-    }
+    for (int j = 0; j < k; ++j)
+      if (__builtin_amdgcn_readlane(my_i, j) >= 0) S += rdlane(sgv, j);
     float my_w;
     if (cfg.norm) my_w = (S != 0.f) ? (sgv / S) * cfg.rsf : 0.f;
     else my_w = sgv * cfg.rsf;
+    bool kept = win;
     if (cfg.top_p > 0.f && cfg.top_p < 1.f) {
       // slots by normalised weight (desc, slot order on ties) while the
       // running binary32 sum is below p
       const float pn = (S != 0.f && win) ? sgv / S : 0.f;
       int rk = 0;
-      for (int j = 0; j < M; ++j) {
-        const bool wj = __builtin_amdgcn_readlane((int)win, j) != 0;
+      for (int j = 0; j < k; ++j) {
+        const bool wj = __builtin_amdgcn_readlane(my_i, j) >= 0;
         const float pj = rdlane(pn, j);
-        const int rj = __builtin_amdgcn_readlane(r, j);
-        rk += (wj && (pj > pn || (pj == pn && rj < r))) ? 1 : 0;
+        rk += (wj && (pj > pn || (pj == pn && j < lane))) ? 1 : 0;
       }
       float cum = 0.f;
-      bool kept = false;
-      for (int q = 0; q < k; ++q) {
+      kept = false;
+      for (int q2 = 0; q2 < k; ++q2) {
         if (cum >= cfg.top_p) break;
-        const unsigned long long who = __ballot(win && rk == q);
+        const unsigned long long who = __ballot(win && rk == q2);
         if (!who) break;
         const int src = __ffsll((long long)who) - 1;
         if (lane == src) kept = true;
@@ -565,21 +594,14 @@ __device__ __forceinline__ void select_fast_t(const RouterCfg &cfg, const SelInp
       }
       float Sk = 0.f;
       for (int j = 0; j < k; ++j) {
-        const unsigned long long who = __ballot(win && kept && r == j);
-        if (who) Sk += rdlane(sgv, __ffsll((long long)who) - 1);
+        const int kj = __builtin_amdgcn_readlane((int)(win && kept), j);
+        if (kj) Sk += rdlane(sgv, j);
       }
-      if (win) {
-        if (!kept) {
-          idx_out[r] = -1;
-          w_out[r] = 0.f;
-        } else {
-          idx_out[r] = e;
-          w_out[r] = cfg.renorm ? ((Sk != 0.f) ? (sgv / Sk) * cfg.rsf : 0.f) : my_w;
-        }
-      }
-    } else if (win) {
-      idx_out[r] = e;
-      w_out[r] = my_w;
+      if (kept && cfg.renorm) my_w = (Sk != 0.f) ? (sgv / Sk) * cfg.rsf : 0.f;
+    }
+    if (lane < k) {
+      idx_out[lane] = kept ? my_i : -1;
+      w_out[lane] = kept ? my_w : 0.f;
     }
   }
   __syncthreads();
@@ -589,10 +611,7 @@ template <int NT>
 __device__ __forceinline__ void select_fast(const RouterCfg &cfg, const SelInput &in,
                                             SelFastScratch &sc, int32_t *idx_out, float *w_out) {
   // slots no candidate reaches (only with NaN scores) stay empty
-  if ((int)threadIdx.x < cfg.k) {
-    idx_out[threadIdx.x] = -1;
-    w_out[threadIdx.x] = 0.f;
-  }
+  if ((int)threadIdx.x < kSelMaxK) sc.slot[threadIdx.x] = -1;
   switch (cfg.E / cfg.n_group) {
     case 1: select_fast_t<NT, 1>(cfg, in, sc, idx_out, w_out); break;
     case 2: select_fast_t<NT, 2>(cfg, in, sc, idx_out, w_out); break;
