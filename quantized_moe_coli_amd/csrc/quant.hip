@@ -61,32 +61,63 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return __uint_as_float(__float_as_uint(v) | ((c & 0x80u) << 24));
 }
 
+// The same value for the 127 magnitudes that are not NaN, in two
+// operations: the code's seven magnitude bits placed at the top of a
+// binary32 mantissa/exponent give (1 + m/8) * 2^(e-127) (or the subnormal
+// m/8 * 2^-126 for e = 0), which the exact product with 2^120 turns into
+// the code's value; the sign bit is copied.  The NaN codes give 480.
+__device__ __forceinline__ float e4m3_fast(uint32_t c) {
+  return __uint_as_float(((c & 0x7Fu) << 20) | ((c & 0x80u) << 24)) * 0x1p120f;
+}
+
 // The 16 dequantised values of one 16-byte chunk of codes: each code's value
 // times its block's scale, one correctly rounded binary32 product.
 __device__ __forceinline__ void fp8_chunk(const uint4 c, float s, float (&v)[16]) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = e4m3_value((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * s;
+  for (int i = 0; i < 16; ++i) v[i] = e4m3_fast((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * s;
 }
 
 // Quantises and packs the 16 values of one chunk (same rule as
-// k_quant_pack) and stores them as one 4-, 8- or 16-byte group, so that
-// consecutive lanes write consecutive bytes.
+// k_quant_pack; s != 0, r = fl32(1/s)) and stores them as one 4-, 8- or
+// 16-byte group, so that consecutive lanes write consecutive bytes.
+// round_half_even(fl32(v / s)) comes from a multiplication by r:
+// y = fl32(v * r) is within 3 * 2^-24 * |v/s| of fl32(v/s) (one rounding in
+// r, one in y; |v/s| <= qmax + 1, so within 2^-15), so wherever y lies more
+// than 2^-15 from every half-integer both round to the same integer.  A
+// chunk with a value closer than that (or a non-finite y) in any lane of the
+// wave is redone with the correctly rounded division, in a branch the whole
+// wave takes together.  The codes equal k_quant_pack's.
 template <int BITS>
-__device__ __forceinline__ void fp8_store_chunk(const float (&v)[16], float s, uint32_t *dst,
+__device__ __forceinline__ void fp8_store_chunk(const float (&v)[16], float s, float r, uint32_t *dst,
                                                 int64_t j) {
   constexpr float kQmax = BITS == 8 ? 127.f : (BITS == 4 ? 7.f : 1.f);
   constexpr int kPer = 32 / BITS;  // codes per 32-bit output word
   constexpr int kWords = 16 / kPer;
   constexpr uint32_t kMask = (1u << BITS) - 1u;
+  float c[16];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float y = v[i] * r;
+    near |= !(fabsf(y - (floorf(y) + 0.5f)) > 0x1p-15f);
+    c[i] = rintf(y);
+  }
+  if (__ballot(near)) {
+    if (near) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = rintf(v[i] / s);
+    }
+  }
   uint32_t word[kWords];
 #pragma unroll
   for (int k = 0; k < kWords; ++k) word[k] = 0;
+  if (s != 0.f) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float c = 0.f;
-    if (s != 0.f) c = fminf(fmaxf(rintf(v[i] / s), -kQmax), kQmax);
-    word[i / kPer] |= ((uint32_t)(int32_t)c & kMask) << (BITS * (i % kPer));
+    for (int i = 0; i < 16; ++i) {
+      const float q = __builtin_amdgcn_fmed3f(c[i], -kQmax, kQmax);
+      word[i / kPer] |= ((uint32_t)(int32_t)q & kMask) << (BITS * (i % kPer));
+    }
   }
   if constexpr (kWords == 4)
     reinterpret_cast<uint4 *>(dst)[j] = make_uint4(word[0], word[1], word[2], word[3]);
@@ -96,35 +127,53 @@ __device__ __forceinline__ void fp8_store_chunk(const float (&v)[16], float s, u
     dst[j] = word[0];
 }
 
-// One wave per row; a lane handles 16-byte chunks of 16 codes, chunk j
-// lying in block column j/8.  NC > 0: the row has at most 64*NC chunks, and
-// each lane loads all of its chunks at once and keeps them in registers
-// (one read of the row, every load in flight together); the absmax and the
-// codes are then computed from the registers.  NC = 0: longer rows, read
-// twice (the second time from cache).
-template <int BITS, int NC>
+// TPR threads (one to four waves) per row, 256 / TPR rows per workgroup; a
+// thread handles 16-byte chunks of 16 codes, chunk j lying in block column
+// j/8.  NC > 0: the row has at most TPR*NC chunks, and each thread loads
+// all of its chunks at once and keeps them in registers (one read of the
+// row, every load in flight together); the row's absmax (wave DPP maxima,
+// then across the row's waves in LDS) and the codes are computed from the
+// registers.  NC = 0: longer rows, read twice (the second time from cache).
+template <int BITS, int TPR, int NC>
 __global__ __launch_bounds__(256) void k_quant_pack_fp8(const uint8_t *__restrict__ w8,
                                                         const float *__restrict__ bscale,
                                                         int64_t rows, int64_t cols,
                                                         uint8_t *__restrict__ q,
                                                         float *__restrict__ scale) {
   constexpr float kQmax = BITS == 8 ? 127.f : (BITS == 4 ? 7.f : 1.f);
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  constexpr int kWpr = TPR / 64;  // waves per row
+  __shared__ float wmax[4];
+  const int tr = threadIdx.x % TPR, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const bool active = row < rows;  // uniform per wave
   const int64_t chunks = cols / 16;
-  const uint4 *src = reinterpret_cast<const uint4 *>(w8 + row * cols);
-  const float *bs = bscale + (row / 128) * ((cols + 127) / 128);
-  uint32_t *dst = reinterpret_cast<uint32_t *>(q + row * (cols * BITS / 8));
+  const int64_t rr = active ? row : 0;
+  const uint4 *src = reinterpret_cast<const uint4 *>(w8 + rr * cols);
+  const float *bs = bscale + (rr / 128) * ((cols + 127) / 128);
+  uint32_t *dst = reinterpret_cast<uint32_t *>(q + rr * (cols * BITS / 8));
+
+  // the row's absmax: each wave's maximum, then the row's waves' maxima
+  auto row_max = [&](float m) {
+    m = wave_max(m);
+    if constexpr (kWpr > 1) {
+      if (lane == 0) wmax[wave] = m;
+      __syncthreads();
+      const int w0 = wave - wave % kWpr;
+#pragma unroll
+      for (int i = 0; i < kWpr; ++i) m = fmaxf(m, wmax[w0 + i]);
+    }
+    return m;
+  };
 
   if constexpr (NC > 0) {
     uint4 c[NC];
     float sc[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const int64_t j = lane + 64 * i;
-      c[i] = j < chunks ? src[j] : make_uint4(0, 0, 0, 0);
-      sc[i] = j < chunks ? bs[j >> 3] : 0.f;
+      const int64_t j = tr + (int64_t)TPR * i;
+      const bool ok = active && j < chunks;
+      c[i] = ok ? src[j] : make_uint4(0, 0, 0, 0);
+      sc[i] = ok ? bs[j >> 3] : 0.f;
     }
     // E4M3 magnitudes grow with the low seven bits of the code and binary32
     // rounding is monotonic, so a chunk's largest |value * scale| is that of
@@ -138,33 +187,37 @@ __global__ __launch_bounds__(256) void k_quant_pack_fp8(const uint8_t *__restric
       for (int b = 0; b < 16; ++b) m = max(m, (w[b >> 2] >> (8 * (b & 3))) & 0x7Fu);
       amax = fmaxf(amax, fabsf(e4m3_value(m) * sc[i]));
     }
-    amax = wave_max(amax);
+    amax = row_max(amax);
+    if (!active) return;
     const float s = amax / kQmax;  // IEEE binary32 division
-    if (lane == 0) scale[row] = s;
+    const float r = 1.f / s;
+    if (tr == 0) scale[row] = s;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const int64_t j = lane + 64 * i;
+      const int64_t j = tr + (int64_t)TPR * i;
       if (j < chunks) {
         float v[16];
         fp8_chunk(c[i], sc[i], v);
-        fp8_store_chunk<BITS>(v, s, dst, j);
+        fp8_store_chunk<BITS>(v, s, r, dst, j);
       }
     }
   } else {
     float amax = 0.f;
-    for (int64_t j = lane; j < chunks; j += 64) {
+    for (int64_t j = tr; active && j < chunks; j += TPR) {
       float v[16];
       fp8_chunk(src[j], bs[j >> 3], v);
 #pragma unroll
       for (int m = 0; m < 16; ++m) amax = fmaxf(amax, fabsf(v[m]));
     }
-    amax = wave_max(amax);
+    amax = row_max(amax);
+    if (!active) return;
     const float s = amax / kQmax;
-    if (lane == 0) scale[row] = s;
-    for (int64_t j = lane; j < chunks; j += 64) {
+    const float r = 1.f / s;
+    if (tr == 0) scale[row] = s;
+    for (int64_t j = tr; j < chunks; j += TPR) {
       float v[16];
       fp8_chunk(src[j], bs[j >> 3], v);
-      fp8_store_chunk<BITS>(v, s, dst, j);
+      fp8_store_chunk<BITS>(v, s, r, dst, j);
     }
   }
 }
@@ -195,22 +248,33 @@ hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t col
   return hipGetLastError();
 }
 
+// Threads per row: as many of 64, 128, 256 as the row has chunks for (at
+// least 64), so a matrix of a few thousand rows still gives every SIMD
+// several waves.
+template <int BITS, int TPR>
+static hipError_t launch_fp8_tpr(const uint8_t *w8, const float *bscale, int64_t rows,
+                                 int64_t cols, uint8_t *q, float *scale, hipStream_t st) {
+  constexpr int RPW = 256 / TPR;
+  const dim3 grid((unsigned)((rows + RPW - 1) / RPW)), block(256);
+  const int64_t per = (cols / 16 + TPR - 1) / TPR;  // chunks per thread
+  if (per <= 1)
+    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, TPR, 1>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
+  else if (per <= 2)
+    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, TPR, 2>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
+  else if (per <= 4)
+    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, TPR, 4>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
+  else
+    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, TPR, 0>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
+  return hipGetLastError();
+}
+
 template <int BITS>
 static hipError_t launch_fp8_bits(const uint8_t *w8, const float *bscale, int64_t rows,
                                   int64_t cols, uint8_t *q, float *scale, hipStream_t st) {
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-  const int64_t per_lane = (cols / 16 + 63) / 64;  // chunks per lane
-  if (per_lane <= 1)
-    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, 1>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
-  else if (per_lane <= 2)
-    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, 2>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
-  else if (per_lane <= 4)
-    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, 4>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
-  else if (per_lane <= 8)
-    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, 8>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
-  else
-    hipLaunchKernelGGL((k_quant_pack_fp8<BITS, 0>), grid, block, 0, st, w8, bscale, rows, cols, q, scale);
-  return hipGetLastError();
+  const int64_t chunks = cols / 16;
+  if (chunks > 128) return launch_fp8_tpr<BITS, 256>(w8, bscale, rows, cols, q, scale, st);
+  if (chunks > 64) return launch_fp8_tpr<BITS, 128>(w8, bscale, rows, cols, q, scale, st);
+  return launch_fp8_tpr<BITS, 64>(w8, bscale, rows, cols, q, scale, st);
 }
 
 hipError_t launch_quant_pack_fp8(int bits, const uint8_t *w8, const float *bscale, int64_t rows,

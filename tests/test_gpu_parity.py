@@ -76,7 +76,8 @@ def _fp8_requant_gpu(bits, codes, bs):
 
 
 @pytest.mark.parametrize("bits", [4, 8, 2])
-@pytest.mark.parametrize("R,C", [(1, 32), (200, 96), (130, 288), (256, 1024), (40, 4096), (5, 8224)])
+@pytest.mark.parametrize("R,C", [(1, 32), (200, 96), (130, 288), (256, 1024), (40, 4096), (5, 8224),
+                                 (3, 16416), (129, 2080)])
 def test_fp8_requant_bit_exact(orc, bits, R, C):
     """FP8 block-scaled codes -> container on the GPU equals the oracle's
     dequantisation followed by its quantisation and packing.  The shapes put
