@@ -88,13 +88,24 @@ def expert_bytes(s) -> dict:
     return {"gate_up": gate_up, "down": down, "total": gate_up + down}
 
 
-def kernel_sources_sha256() -> str:
-    """Hash of the library's kernel sources and ABI header: a stored counter
-    measurement applies only to the kernels it was taken on."""
+# sources each counted kernel is built from (its .hip file and the headers
+# it includes)
+KERNEL_SOURCES = {
+    "k_decode_fused": ["decode.hip", "actq.hpp", "device.hpp", "ffn_common.hpp", "kernels.hpp",
+                       "select.hpp"],
+}
+
+
+def kernel_sources_sha256(kernel: str = "k_decode_fused") -> str:
+    """Hash of the sources a kernel is built from and of the ABI header: a
+    stored counter measurement applies only to the kernel it was taken on."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(root, "quantized_moe_coli_amd", "csrc")
-    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
+    names = KERNEL_SOURCES.get(kernel)
+    if names is None:
+        names = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
+    files = [os.path.join(csrc, f) for f in sorted(names)]
     files.append(os.path.join(root, "include", "coli_moe.h"))
     h = hashlib.sha256()
     for f in files:
@@ -114,7 +125,8 @@ def measured_traffic(workload: str, kernel: str):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("sources_sha256") != kernel_sources_sha256() or not kernel.startswith(rec.get("kernel", "?")):
+    if (not kernel.startswith(rec.get("kernel", "?"))
+            or rec.get("sources_sha256") != kernel_sources_sha256(rec["kernel"])):
         return None
     return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
@@ -148,7 +160,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, kernel: str, calib_mib: i
     f_scale, w_scale = known_kib / f_copy, known_kib / w_copy
     return {
         "kernel": kernel,
-        "sources_sha256": kernel_sources_sha256(),
+        "sources_sha256": kernel_sources_sha256(kernel),
         "fetch_bytes_per_launch": int(round(f_mean * 1024 * f_scale)),
         "write_bytes_per_launch": int(round(w_mean * 1024 * w_scale)),
         "fetch_kib_mean": round(f_mean, 1), "write_kib_mean": round(w_mean, 1),
