@@ -725,10 +725,15 @@ def fp8_main(args) -> int:
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    # each launch's own duration, from events around it on the launch stream
+    # each launch's own duration, from events around it on the launch stream;
+    # the launches queue behind a short spin on the GPU so that they run
+    # back to back (no host launch gap inside an interval)
     KP = min(K, 64)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(KP * 3)]
+    torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(50_000_000)
     for t in range(KP):
         for m in range(3):
             codes, bs = src[t % NE][m]
