@@ -13,9 +13,8 @@
 // Work items, in ticket order (each workgroup takes the next ticket from a
 // device-wide counter, so a workgroup only ever waits for items with lower
 // tickets, which are already running -- progress is guaranteed):
-//   L   router logits, 2 expert rows per item (four waves per row, each
-//       summing a quarter of the row in binary64; skipped if logits are
-//       given)
+//   L   router logits, four expert rows per item (two waves per row, each
+//       summing half of the row in binary64; skipped if logits are given)
 //   GS  shared-expert gate/up + SwiGLU + Q8_0(h), 64 rows per item
 //   GR  routed-expert gate/up, one (slot, 64-row block) per item
 //   D   down projection + combine for a block of output rows, slot by slot
@@ -66,7 +65,7 @@ static_assert((kScoreWords + 2 * kSelMaxE) * 4 <= kDecodeCounterBytes,
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr uint32_t kSpinLimit = 1u << 19;  // ~100 ms of polling
-constexpr int kLogRows = 2;                // logit rows per L item (four waves each)
+constexpr int kLogRows = 4;                // logit rows per L item (two waves each)
 constexpr int kGuRows = 32;                // gate/up rows per GS/GR item
 // cache-policy bits of global_load_lds giving sc1, the policy of the relaxed
 // device-scope loads, so staged data is as coherent across XCDs as theirs
@@ -110,17 +109,18 @@ __device__ __forceinline__ void wait_ge(const uint32_t *c, uint32_t target) {
   __syncthreads();
 }
 
-// L item: logits of experts e0, e0+1.  Waves 4r .. 4r+3 sum the quarters of
-// row e0+r in binary64; the quarters are added in order and the result
-// rounded once to binary32.
+// L item: logits of experts e0 .. e0 + kLogRows - 1.  The kWpr waves of a
+// row each sum one 1/kWpr part of it in binary64; the parts are added in
+// order and the result rounded once to binary32.
 __device__ __forceinline__ void logits_rows(const DecodeArgs &d, int e0, double *part) {
+  constexpr int kWpr = kDecWaves / kLogRows;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = wave >> 2, qtr = wave & 3;
+  const int r = wave / kWpr, seg = wave % kWpr;
   const int e = min(e0 + r, d.f.E - 1);  // a row past E recomputes the last row, unused
   const int H = d.f.L.H;
-  const int q4 = H / 16;  // float4 per quarter row (H % 64 == 0)
-  const float4 *wr = reinterpret_cast<const float4 *>(d.gate_w + (size_t)e * H) + qtr * q4;
-  const float4 *xr = reinterpret_cast<const float4 *>(d.x) + qtr * q4;
+  const int q4 = H / (4 * kWpr);  // float4 per part (H % 32 == 0)
+  const float4 *wr = reinterpret_cast<const float4 *>(d.gate_w + (size_t)e * H) + seg * q4;
+  const float4 *xr = reinterpret_cast<const float4 *>(d.x) + seg * q4;
   constexpr int kPer = 6;
   double acc = 0.0;
   for (int c0 = 0; c0 < q4; c0 += 64 * kPer) {
@@ -146,8 +146,11 @@ __device__ __forceinline__ void logits_rows(const DecodeArgs &d, int e0, double 
   __syncthreads();
   if ((int)threadIdx.x < kLogRows && e0 + (int)threadIdx.x < d.f.E) {
     const int e = e0 + threadIdx.x;
-    const double *p = part + 4 * threadIdx.x;
-    float l = (float)(((p[0] + p[1]) + p[2]) + p[3]);
+    const double *p = part + kWpr * threadIdx.x;
+    double sum = p[0];
+#pragma unroll
+    for (int i = 1; i < kWpr; ++i) sum += p[i];
+    float l = (float)sum;
     if (d.f.loff) l += d.f.loff[e];
     const float sg = sigmoid_f64(l);
     const float c = sg + (d.f.bias ? d.f.bias[e] : 0.f);
@@ -390,7 +393,7 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
   };
   int t = (int)blockIdx.x;
 
-  // L: two logit rows per item
+  // L: four logit rows per item
   for (; t < b_gsh; t = next_ticket()) {
     logits_rows(d, t * kLogRows, lpart);
     __syncthreads();
