@@ -193,7 +193,8 @@ def main() -> int:
                     help="layer's mfma_min_tokens (0: the library default)")
     ap.add_argument("--tokens", type=int, default=0,
                     help="tokens per step with logits computed from the gate (overrides the "
-                         "workload's batch; 1 = decode)")
+                         "workload's batch; 1 = decode; with --workload stack: tokens per "
+                         "step through the stack, e.g. 3 for MTP verify batches)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one untimed device-to-device copy of this many MiB after the "
                          "warm-up (the known-size reference for hardware byte counters)")
@@ -542,7 +543,9 @@ def _kernel_events(hip, n):
 def stack_main(args) -> int:
     """The multi-layer decode: every step feeds a fresh token through all
     resident layers (h <- h + MoE_l(rmsnorm(h))), one HIP graph per step
-    replayed on the token."""
+    replayed on the token.  With --tokens T > 1 every step is instead a
+    T-token batch (an MTP verify: the current token and T - 1 drafts) that
+    each layer runs as one batch union."""
     import numpy as np
     import torch
 
@@ -551,18 +554,19 @@ def stack_main(args) -> int:
 
     dev = "cuda"
     K, W, NL = args.steps, args.warmup, args.layers
+    T = max(1, args.tokens)
     t0 = time.time()
     stk = stack.build(NL)
     s = stk.s
     log(f"[bench] stack: {NL} layers packed in {time.time() - t0:.1f}s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB resident)")
     n_x = max(K, W, 1)
-    xs = torch.stack([inputs.tokens(s, stack.token_seed(), t, 1, dev) for t in range(n_x)])
-    ws = B.workspace(stk.layers[0], 1)
-    h = torch.empty(1, s.hidden, device=dev)
-    y = torch.empty(1, s.hidden, device=dev)
-    idx_g = torch.empty(NL, 1, s.top_k, dtype=torch.int32, device=dev)
-    w_g = torch.empty(NL, 1, s.top_k, device=dev)
+    xs = torch.stack([inputs.tokens(s, stack.token_seed(), t, T, dev) for t in range(n_x)])
+    ws = B.workspace(stk.layers[0], T)
+    h = torch.empty(T, s.hidden, device=dev)
+    y = torch.empty(T, s.hidden, device=dev)
+    idx_g = torch.empty(NL, T, s.top_k, dtype=torch.int32, device=dev)
+    w_g = torch.empty(NL, T, s.top_k, device=dev)
     for t in range(W):
         h.copy_(xs[t])
         stack.step(stk, h, ws, y, idx_g, w_g)
@@ -575,13 +579,13 @@ def stack_main(args) -> int:
         with torch.cuda.graph(g, stream=cap):
             stack.step(stk, h, ws, y, idx_g, w_g)
     torch.cuda.synchronize()
-    idx_all = torch.empty(K, NL, s.top_k, dtype=torch.int32, device=dev)
+    idx_all = torch.empty(K, NL, T, s.top_k, dtype=torch.int32, device=dev)
 
     def run_steps():
         for t in range(K):
             h.copy_(xs[t])
             g.replay()
-            idx_all[t].copy_(idx_g[:, 0])
+            idx_all[t].copy_(idx_g)
 
     run_steps()  # one untimed pass
     torch.cuda.synchronize()
@@ -595,51 +599,67 @@ def stack_main(args) -> int:
     total_ms = start.elapsed_time(stop)
     del g
 
-    # the decode kernel's own duration: an eager pass over the first steps,
-    # every layer's launch recording a start and a stop event
+    # kernel durations: an eager pass over the first steps, every layer's
+    # launches recording start and stop events (T = 1: the fused decode
+    # kernel; T > 1: front, gate/up and down on the dot-product path, gate/up
+    # and down on the matrix cores)
     hip = _hip()
     KP = min(K, 32)
-    evs = _kernel_events(hip, KP * NL * 2)
+    n_ev = 2 if T == 1 else 10
+    evs = _kernel_events(hip, KP * NL * n_ev)
     torch.cuda.synchronize()
     for t in range(KP):
         h.copy_(xs[t])
         for li, L in enumerate(stk.layers):
-            e = evs[(t * NL + li) * 2:(t * NL + li) * 2 + 2]
+            e = evs[(t * NL + li) * n_ev:(t * NL + li + 1) * n_ev]
             B.coli_moe_forward_profiled(L, stack.rmsnorm(h), y, ws, e, c_layer=stk.c_layers[li])
             h.add_(y)
     torch.cuda.synchronize()
     kms = []
+    dom_k = 0 if T == 1 else 1  # the fused kernel / the dot-product gate/up kernel
     for i in range(KP * NL):
         v = ctypes.c_float()
-        rc = hip.hipEventElapsedTime(ctypes.byref(v), ctypes.c_void_p(evs[2 * i]),
-                                     ctypes.c_void_p(evs[2 * i + 1]))
+        rc = hip.hipEventElapsedTime(ctypes.byref(v), ctypes.c_void_p(evs[i * n_ev + 2 * dom_k]),
+                                     ctypes.c_void_p(evs[i * n_ev + 2 * dom_k + 1]))
         kms.append(v.value if rc == 0 else float("nan"))
     for e in evs:
         hip.hipEventDestroy(ctypes.c_void_p(e))
     hip.hipGetLastError()
     kms = np.array(kms).reshape(KP, NL)
 
-    idx = idx_all.cpu().numpy()
-    kept = (idx >= 0).sum(axis=2)  # [K, NL]
-    eb = expert_bytes(s)["total"]
+    idx = idx_all.cpu().numpy()  # [K, NL, T, k]
+    kept = (idx >= 0).sum(axis=3)  # [K, NL, T] experts each token keeps
+    uniq = np.array([[len(set(idx[t, li][idx[t, li] >= 0].tolist())) for li in range(NL)]
+                     for t in range(K)])  # [K, NL] unique experts a layer reads for the batch
+    ebd = expert_bytes(s)
+    eb = ebd["total"]
     gate_bytes = s.n_experts * s.hidden * 4
-    act_bytes = s.hidden * 4 * 2
-    launch_bytes = (kept + 1) * eb + gate_bytes + act_bytes  # per layer launch
+    act_bytes = T * s.hidden * 4 * 2
+    launch_bytes = (uniq + 1) * eb + gate_bytes + act_bytes  # per layer launch
     step_bytes = launch_bytes.sum(axis=1)
     ms_per_step = total_ms / K
-    tokens_per_s = K / (total_ms / 1e3)
+    tokens_per_s = T * K / (total_ms / 1e3)
     gbps = float(step_bytes.mean()) / (ms_per_step * 1e-3) / 1e9
     k_avg_ms = float(np.nanmean(kms))
-    k_bytes = float(launch_bytes[:KP].mean())
+    if T == 1:
+        k_bytes = float(launch_bytes[:KP].mean())
+        k_name = "k_decode_fused (one layer for one token)"
+    else:  # T < 8: every slot on the dot-product path
+        k_bytes = float(((uniq[:KP] + 1) * ebd["gate_up"]).mean())
+        k_name = "k_gateup_union (one layer's gate/up for the batch union)"
     k_gbps = k_bytes / (k_avg_ms * 1e-3) / 1e9
-    log(f"[bench] stack: {K} steps in {total_ms:.2f} ms (wall {wall * 1e3:.1f} ms): "
-        f"{ms_per_step * 1e3:.1f} us/step, {tokens_per_s:.1f} tokens/s; kept experts/layer "
-        f"{kept.mean():.2f}; bytes/step {step_bytes.mean() / 1e9:.3f} GB -> {gbps:.0f} GB/s")
-    log(f"[bench] decode kernel: {k_avg_ms * 1e3:.2f} us avg over {KP * NL} launches, "
+    log(f"[bench] stack: {K} steps of {T} token(s) in {total_ms:.2f} ms (wall {wall * 1e3:.1f} "
+        f"ms): {ms_per_step * 1e3:.1f} us/step, {tokens_per_s:.1f} tokens/s; kept experts per "
+        f"token and layer {kept.mean():.2f}, unique per layer {uniq.mean():.2f}; bytes/step "
+        f"{step_bytes.mean() / 1e9:.3f} GB -> {gbps:.0f} GB/s")
+    log(f"[bench] {k_name.split()[0]}: {k_avg_ms * 1e3:.2f} us avg over {KP * NL} launches, "
         f"{k_bytes / 1e6:.1f} MB each -> {k_gbps:.0f} GB/s")
 
     result = {
-        "metric": f"MoE-stack tokens/s ({NL} int4 layers, Zipf popularity, expert top-p 0.7)",
+        "metric": (f"MoE-stack tokens/s ({NL} int4 layers, Zipf popularity, expert top-p 0.7)"
+                   if T == 1 else
+                   f"MoE-stack MTP-verify tokens/s ({T}-token batches through {NL} int4 layers, "
+                   "Zipf popularity, expert top-p 0.7)"),
         "value": round(tokens_per_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -655,16 +675,22 @@ def stack_main(args) -> int:
             "workload": f"{NL} GLM-5.2-shaped routed-MoE layers resident (H 6144, I 2048, 256 "
                         "experts top-8, 8 groups keep 4, rsf 2.5, + 1 shared; packed int4), "
                         "per-layer logit offsets -1.1 ln(rank+1) over a random expert ranking, "
-                        "expert top-p 0.7 renormalised; batch-1 decode, h <- h + "
-                        "MoE(rmsnorm(h)) between layers",
-            "tokens_per_step": 1,
+                        "expert top-p 0.7 renormalised; "
+                        + ("batch-1 decode" if T == 1 else
+                           f"{T}-token MTP verify batches (the current token and {T - 1} "
+                           "drafts) run as one batch union per layer")
+                        + ", h <- h + MoE(rmsnorm(h)) between layers",
+            "tokens_per_step": T,
             "layers": NL,
             "launch": "one HIP graph per step (all layers), replayed on each token",
             "kept_experts_per_layer": round(float(kept.mean()), 3),
+            "unique_experts_per_layer": round(float(uniq.mean()), 3),
+            # expert reads of a verify batch against T decode steps of the same tokens
+            "expert_reads_vs_per_token": round(float((uniq + 1).sum() / (kept + 1).sum()), 4),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_decode_fused (one layer for one token)",
+            "kernel": k_name,
             "achieved": round(k_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -862,7 +888,7 @@ def stack_cpu_baseline(stk, xs, ws, budget_s):
         if spent >= budget_s:
             break
     per_layer = spent / done
-    tok_s = 1.0 / (per_layer * stk.n_layers)
+    tok_s = xs.shape[1] / (per_layer * stk.n_layers)
     log(f"[bench] oracle chain, step 0: {done} layers in {spent:.2f}s on {oracle.num_threads()} "
         f"threads -> {tok_s:.3f} tokens/s extrapolated to {stk.n_layers} layers; GPU hidden "
         f"state within {max_err:.2e} (rel. to max |h|) of the oracle's over those layers")
@@ -871,9 +897,13 @@ def stack_cpu_baseline(stk, xs, ws, budget_s):
         "unit": "tokens/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"step 0 through layers 0..{done - 1} of the oracle's own chain "
-                  f"({spent:.1f} s of timed forward calls), extrapolated to {stk.n_layers} "
-                  f"layers; GPU hidden state agrees to {max_err:.1e}",
+        "sample": f"step 0 ({xs.shape[1]} token(s)) through layers 0..{done - 1} of the "
+                  f"oracle's own chain ({spent:.1f} s of timed forward calls), extrapolated to "
+                  f"{stk.n_layers} layers; the GPU's chained hidden state is within "
+                  f"{max_err:.1e} of max |h| of the oracle's (each side chains its own "
+                  f"outputs, so a near-tied routing decision can flip an expert and the "
+                  f"chains drift; single layers are checked bit-exact in routing by the "
+                  f"tests)",
     }
 
 

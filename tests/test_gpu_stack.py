@@ -89,6 +89,32 @@ def test_stack_layer_parity(stk, li):
         assert 1 <= kept <= s.top_k
 
 
+
+@pytest.mark.parametrize("li", [0, 39])
+def test_stack_verify_batch_parity(stk, li):
+    """An MTP verify batch (the current token and two drafts, drawn as the
+    stack's 3-token step inputs) through layer li as one batch union, against
+    the oracle, which computes each token on its own."""
+    s = stk.s
+    ws = B.workspace(stk.layers[li], 3)
+    for step in (0, N_STEPS - 1):
+        x = inputs.tokens(s, stack.token_seed(), step, 3, "cuda")
+        y = torch.empty(3, s.hidden, device="cuda")
+        idx = torch.empty(3, s.top_k, dtype=torch.int32, device="cuda")
+        w = torch.empty(3, s.top_k, device="cuda")
+        lg = torch.empty(3, s.n_experts, device="cuda")
+        B.coli_moe_forward(stk.layers[li], x, y, ws, idx_out=idx, w_out=w, logits_out=lg)
+        torch.cuda.synchronize()
+        y_r, idx_r, w_r, lg_r = _oracle_layer(stk, li, x.cpu().numpy())
+        l_raw = oracle.logits(x.cpu().numpy(), stk.layers[li].gate_w.cpu().numpy())
+        bound = 2.0 ** -23 * np.maximum(np.abs(l_raw), np.abs(stk.offsets[li].cpu().numpy())[None, :])
+        assert (np.abs(lg.cpu().numpy() - lg_r) <= bound).all()
+        np.testing.assert_array_equal(idx.cpu().numpy(), idx_r)
+        np.testing.assert_array_equal(w.cpu().numpy(), w_r)
+        assert_close_layer(y.cpu().numpy(), y_r)
+        kept = (idx_r >= 0).sum(axis=1)
+        assert ((kept >= 1) & (kept <= s.top_k)).all()
+
 def _chain_eager(st, x, ws, y, idx_rec, w_rec):
     h = x.clone()
     stack.step(st, h, ws, y, idx_rec, w_rec)
