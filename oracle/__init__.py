@@ -100,6 +100,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "orc_union_tables": [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P],
         "orc_num_threads": [],
         "orc_dequant_fp8_block": [_P, _P, _I64, _I64, _P],
+        "orc_qdot_f32act": [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, _P],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -193,6 +194,20 @@ def qdot(bits: int, w_packed: np.ndarray, w_scale: np.ndarray, cols: int,
     _check(lib().orc_qdot(bits, _ptr(w_packed), _ptr(w_scale), R, cols, _ptr(xq),
                           _ptr(xd), T, _ptr(acc), _ptr(y)), "qdot")
     return acc, y
+
+
+def qdot_f32act(bits: int, w_packed: np.ndarray, w_scale: np.ndarray, cols: int,
+                x: np.ndarray) -> np.ndarray:
+    """O12: packed codes [R, cols*bits/8], row scales [R], fp32 x [T, cols]
+    -> fp32 y [T, R]."""
+    w_packed = _c(w_packed, np.uint8)
+    w_scale = _c(w_scale, np.float32)
+    x = _c(x, np.float32)
+    R, T = w_packed.shape[0], x.shape[0]
+    y = np.empty((T, R), np.float32)
+    _check(lib().orc_qdot_f32act(bits, _ptr(w_packed), _ptr(w_scale), R, cols, _ptr(x), T,
+                                 _ptr(y)), "qdot_f32act")
+    return y
 
 
 def logits(x: np.ndarray, gate_w: np.ndarray) -> np.ndarray:

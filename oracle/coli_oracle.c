@@ -187,6 +187,37 @@ int orc_dequant_fp8_block(const uint8_t *w8, const float *block_scale, int64_t r
 }
 
 /*
+ * O12 -- the f32-activation variant of the quantised product (colibrì
+ * README, "Implemented features": for a single row the int4 kernel keeps
+ * its activations in f32, measured faster there than the integer path).
+ * Reading: the weight row is dequantised on use (code times the row scale)
+ * against unquantised binary32 activations: y = fl32( s_r * sum_c code*x ),
+ * the sum over c in increasing order and the product with s_r in binary64,
+ * rounded to binary32 once.
+ */
+int orc_qdot_f32act(int bits, const uint8_t *w_packed, const float *w_scale,
+                    int64_t rows, int64_t cols, const float *x, int64_t T, float *y) {
+  if (orc_qmax(bits) < 0 || rows < 0 || cols <= 0 || (cols * bits) % 8 || T < 0 ||
+      !w_packed || !w_scale || !x || !y)
+    return ORC_EINVAL;
+  const int64_t stride = cols * bits / 8;
+  int rc = ORC_OK;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    int8_t *wrow = (int8_t *)malloc((size_t)cols);
+    if (!wrow) { rc = ORC_EINVAL; continue; }
+    orc_unpack(bits, w_packed + r * stride, 1, cols, wrow);
+    for (int64_t t = 0; t < T; ++t) {
+      double sum = 0.0;
+      for (int64_t c = 0; c < cols; ++c) sum += (double)wrow[c] * (double)x[t * cols + c];
+      y[t * rows + r] = (float)((double)w_scale[r] * sum);
+    }
+    free(wrow);
+  }
+  return rc;
+}
+
+/*
  * O3 -- Q8_0-style activation quantisation (colibrì README, "Implemented
  * features", integer dot-product kernels).
  * Reading: blocks of 32 consecutive values along the row starting at column

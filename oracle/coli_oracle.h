@@ -65,6 +65,11 @@ int orc_qdot(int bits, const uint8_t *w_packed, const float *w_scale,
              int64_t rows, int64_t cols, const int8_t *xq, const float *xd,
              int64_t T, int32_t *acc, float *y);
 
+/* O12 the f32-activation variant of O4: y[t][r] = fl32(s_r * sum_c
+ * code[r][c] * x[t][c]) with the sum and the product in fp64. */
+int orc_qdot_f32act(int bits, const uint8_t *w_packed, const float *w_scale,
+                    int64_t rows, int64_t cols, const float *x, int64_t T, float *y);
+
 /* O5 router logits: l[t][e] = fl32(sum_i x[t][i]*Wg[e][i]) in fp64. */
 int orc_logits(const float *x, const float *gate_w, int64_t T, int64_t E,
                int64_t H, float *logits);
