@@ -26,6 +26,10 @@ device: one GLM-5.2 expert (gate and up 2048 x 6144, down 6144 x 2048) of
 128x128 block-scaled FP8 E4M3 codes requantised into the packed container
 (int4 unless --bits says otherwise) per step, over 16 resident experts.
 
+``--workload gemvf32`` measures the f32-activation variant of the expert
+GEMV (codes times row scale against binary32 activations, one token) on
+GLM-5.2 gate-shaped (2048 x 6144) and down-shaped (6144 x 2048) matrices.
+
 ``--workload stack`` measures instead a 40-layer stack of such layers resident
 in HBM (40 x 257 int4 experts, ~195 GB) decoded one token at a time, with a
 Zipf-like expert popularity per layer and expert top-p 0.7; its bytes per
@@ -184,7 +188,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--instances", type=int, default=8)
-    ap.add_argument("--workload", choices=list(WORKLOADS) + ["stack", "fp8convert"],
+    ap.add_argument("--workload", choices=list(WORKLOADS) + ["stack", "fp8convert", "gemvf32"],
                     default="decode")
     ap.add_argument("--layers", type=int, default=40, help="stack workload: layers resident")
     ap.add_argument("--bits", type=int, choices=(8, 4, 2), default=None,
@@ -219,6 +223,8 @@ def main() -> int:
         return stack_main(args)
     if args.workload == "fp8convert":
         return fp8_main(args)
+    if args.workload == "gemvf32":
+        return gemv_f32_main(args)
     dev = "cuda"
     s = inputs.TINY if args.workload == "tiny" else inputs.GLM
     if args.bits is not None:
@@ -830,6 +836,122 @@ def fp8_main(args) -> int:
                       f"matrix ({spent:.2f} s), times three for the expert",
         }
         result["cpu_baseline"]["gpu_bytes_equal"] = bool(same)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def gemv_f32_main(args) -> int:
+    """The f32-activation expert GEMV for one token: each step runs it on one
+    gate-shaped and one down-shaped matrix of a GLM-5.2 expert, cycling over
+    16 resident experts so no step's weights are still cached."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from quantized_moe_coli_amd import binding as B
+    from quantized_moe_coli_amd import inputs
+
+    dev = "cuda"
+    s = inputs.GLM if args.bits is None else inputs.GLM.with_(bits=args.bits)
+    H, I, b = s.hidden, s.inter, s.bits
+    K, W, NE = args.steps, args.warmup, 16
+    shapes = [(I, H), (H, I)]
+    mats = []
+    for e in range(NE):
+        row = []
+        for m, (r, c) in enumerate(shapes):
+            w = inputs.normal((r, c), 0.02, dev, 200 + e, m)
+            q = torch.empty(r, c * b // 8, dtype=torch.uint8, device=dev)
+            sc = torch.empty(r, device=dev)
+            B.coli_quant_pack(b, w, q, sc)
+            row.append((q, sc))
+            del w
+        mats.append(row)
+    xs = [inputs.normal((c,), 1.0, dev, 300, m) for m, (r, c) in enumerate(shapes)]
+    ys = [torch.empty(r, device=dev) for (r, c) in shapes]
+    torch.cuda.synchronize()
+
+    def step(e):
+        for m in range(2):
+            B.coli_gemv_f32act(b, mats[e][m][0], mats[e][m][1], xs[m], ys[m])
+
+    for t in range(W):
+        step(t % NE)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for t in range(K):
+        step(t % NE)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    KP = min(K, 64)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(2)] for _ in range(KP)]
+    torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(50_000_000)
+    for t in range(KP):
+        for m in range(2):
+            evs[t][m][0].record()
+            B.coli_gemv_f32act(b, mats[t % NE][m][0], mats[t % NE][m][1], xs[m], ys[m])
+            evs[t][m][1].record()
+    torch.cuda.synchronize()
+    k_ms = [float(np.mean([evs[t][m][0].elapsed_time(evs[t][m][1]) for t in range(KP)]))
+            for m in range(2)]
+    mbytes = [r * c * b // 8 + r * 4 + c * 4 + r * 4 for (r, c) in shapes]  # codes, scales, x, y
+    gbps = [mbytes[m] / (k_ms[m] * 1e-3) / 1e9 for m in range(2)]
+    ms_per_step = total_ms / K
+    step_gbps = sum(mbytes) / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] gemvf32 int{b}: {ms_per_step * 1e3:.2f} us per gate + down pair "
+        f"({step_gbps:.0f} GB/s); gate-shaped {k_ms[0] * 1e3:.2f} us ({gbps[0]:.0f} GB/s), "
+        f"down-shaped {k_ms[1] * 1e3:.2f} us ({gbps[1]:.0f} GB/s)")
+    result = {
+        "metric": f"f32-activation int{b} expert GEMV, one token (GLM-5.2 gate + down matrices)",
+        "value": round(K / (total_ms / 1e3), 1),
+        "unit": "matrix pairs/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"int{b}xf32->f32",
+        "data": "synthetic",
+        "config": {"workload": f"one token through a GLM-5.2 expert's gate-shaped (2048 x 6144) "
+                               f"and down-shaped (6144 x 2048) int{b} matrices with per-row "
+                               f"fp32 scales, binary32 activations; {NE} experts resident"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"k_gemv_f32act<{b}> (gate-shaped matrix)",
+            "achieved": round(gbps[0], 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps[0] / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(k_ms[0] * 1e3, 3),
+            "bytes_per_launch": int(mbytes[0]),
+            "down_shaped_us": round(k_ms[1] * 1e3, 3),
+        },
+    }
+    if args.cpu_seconds > 0:
+        q, sc = (t.cpu().numpy() for t in mats[0][0])
+        x0 = xs[0].cpu().numpy()[None, :]
+        step(0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        y_ref = oracle.qdot_f32act(b, q, sc, H, x0)[0]
+        spent = time.perf_counter() - t0
+        err = float(np.abs(ys[0].cpu().numpy().astype(np.float64) - y_ref).max() / np.abs(y_ref).max())
+        result["cpu_baseline"] = {
+            "value": round(1.0 / (2 * spent), 2),
+            "unit": "matrix pairs/s",
+            "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the oracle's product on one gate-shaped matrix ({spent * 1e3:.1f} ms), "
+                      f"twice for the pair; GPU output within {err:.1e} of max |y| of it",
+        }
     print(json.dumps(result), flush=True)
     return 0
 

@@ -146,6 +146,19 @@ coli_status coli_quant_pack_fp8(int32_t qtype, const uint8_t *w8,
                                 int64_t cols, uint8_t *q_out, float *scale_out,
                                 void *stream);
 
+/* f32-activation variant of the quantised product, for one token
+ * (colibrì README, "Implemented features": for a single row the int4 kernel
+ * keeps its activations in f32, which measured faster there than the
+ * integer Q8_0 path).  y[r] = s_r * sum_c code[r][c] * x[c] with the codes
+ * of w [rows][cols*qtype/8] (layout above, 16-byte aligned rows), scale
+ * [rows], x [cols] fp32 (16-byte aligned), y [rows] fp32; sums in fp32.
+ * cols*qtype must be a multiple of 128 (one 16-byte chunk) and at most
+ * 65536, with cols <= 16384 (int8 8192, int4 and int2 16384 columns);
+ * rows >= 0. */
+coli_status coli_gemv_f32act(int32_t qtype, const uint8_t *w, const float *scale,
+                             int64_t rows, int64_t cols, const float *x, float *y,
+                             void *stream);
+
 /* Q8_0-style activation quantisation (colibrì README, "Implemented
  * features": integer dot products against Q8_0-style int8 activations).
  * x [T][n] fp32 -> q [T][n] int8 (natural order) and d [T][n/32] fp32:

@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
             "coli_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "coli_quant_pack": ([i32, _P, i64, i64, _P, _P, _P], ctypes.c_int),
             "coli_quant_pack_fp8": ([i32, _P, _P, i64, i64, _P, _P, _P], ctypes.c_int),
+            "coli_gemv_f32act": ([i32, _P, _P, i64, i64, _P, _P, _P], ctypes.c_int),
             "coli_quant_act_q8_0": ([_P, i32, i32, _P, _P, _P], ctypes.c_int),
             "coli_moe_logits": ([_P, _P, i32, i32, i32, _P, _P], ctypes.c_int),
             "coli_moe_route": ([ctypes.POINTER(RouterCfg), _P, _P, i32, _P, _P, _P], ctypes.c_int),
@@ -149,6 +150,19 @@ def coli_quant_pack_fp8(qtype: int, w8: torch.Tensor, block_scale: torch.Tensor,
         qtype, _ptr(w8, torch.uint8, "w8"), _ptr(block_scale, torch.float32, "block_scale"),
         rows, cols, _ptr(q_out, torch.uint8, "q_out"),
         _ptr(scale_out, torch.float32, "scale_out"), _stream(stream)))
+
+
+def coli_gemv_f32act(qtype: int, w: torch.Tensor, scale: torch.Tensor, x: torch.Tensor,
+                     y: torch.Tensor, stream=None) -> None:
+    """w uint8 [rows, cols*qtype/8] packed codes, scale fp32 [rows], x fp32
+    [cols] -> y fp32 [rows] = scale * (codes @ x)."""
+    rows = w.shape[0]
+    cols = x.numel()
+    if w.shape[1] * 8 != cols * qtype or scale.numel() != rows or y.numel() != rows:
+        raise ValueError("shapes do not match")
+    _check("coli_gemv_f32act", lib().coli_gemv_f32act(
+        qtype, _ptr(w, torch.uint8, "w"), _ptr(scale, torch.float32, "scale"), rows, cols,
+        _ptr(x, torch.float32, "x"), _ptr(y, torch.float32, "y"), _stream(stream)))
 
 
 def coli_quant_act_q8_0(x: torch.Tensor, q: torch.Tensor, d: torch.Tensor, stream=None) -> None:

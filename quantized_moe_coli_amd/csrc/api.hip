@@ -168,6 +168,23 @@ coli_status coli_quant_pack_fp8(int32_t qtype, const uint8_t *w8, const float *b
   });
 }
 
+coli_status coli_gemv_f32act(int32_t qtype, const uint8_t *w, const float *scale, int64_t rows,
+                             int64_t cols, const float *x, float *y, void *stream) {
+  return guarded([&] {
+    if (!qtype_ok(qtype) || rows < 0 || cols <= 0 || (cols * qtype) % 128 || !w || !scale || !x ||
+        !y)
+      return COLI_ERR_INVALID_ARG;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(scale, 4) || !aligned(y, 4))
+      return COLI_ERR_INVALID_ARG;
+    if (rows > (int64_t)1 << 34 || (cols * qtype / 128 + 63) / 64 > 8 || cols > 16384)
+      return COLI_ERR_UNSUPPORTED;
+    const coli_status d = check_device();
+    if (d != COLI_OK) return d;
+    return from_hip(coli::launch_gemv_f32act(qtype, w, scale, rows, cols, x, y,
+                                             static_cast<hipStream_t>(stream)));
+  });
+}
+
 coli_status coli_quant_act_q8_0(const float *x, int32_t T, int32_t n, int8_t *q, float *d,
                                 void *stream) {
   return guarded([&] {

@@ -65,6 +65,8 @@ hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t col
                              float *scale, hipStream_t st);
 hipError_t launch_quant_pack_fp8(int bits, const uint8_t *w8, const float *bscale, int64_t rows,
                                  int64_t cols, uint8_t *q, float *scale, hipStream_t st);
+hipError_t launch_gemv_f32act(int bits, const uint8_t *W, const float *scale, int64_t rows,
+                              int64_t cols, const float *x, float *y, hipStream_t st);
 hipError_t launch_act_quant(int layout_bits, const float *x, int64_t T, int64_t n, int8_t *q,
                             float *d, hipStream_t st, KEvents ev = {});
 

@@ -248,6 +248,112 @@ hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t col
   return hipGetLastError();
 }
 
+// f32-activation variant of the quantised product (colibrì README,
+// "Implemented features": for a single row the int4 kernel keeps its
+// activations in f32, measured faster than the integer path there):
+// y[r] = s_r * sum_c code[r][c] * x[c] for one token, the codes
+// sign-extended in registers and multiplied with the binary32 activations.
+// x is staged in LDS once per workgroup; the four float4 groups of a
+// 16-byte weight chunk's activations are stored rotated by the chunk index,
+// so the lanes of a wave (one chunk each) read different banks.  A wave owns
+// RW rows; a lane takes chunks lane, lane + 64, ... of each, all loaded at
+// once, and reuses each chunk's activations for its RW rows.  fp32 sums,
+// wave-reduced with DPP.
+template <int BITS, int CPL, int RW>
+__global__ __launch_bounds__(256) void k_gemv_f32act(const uint8_t *__restrict__ W,
+                                                     const float *__restrict__ scale, int64_t rows,
+                                                     int64_t cols, const float *__restrict__ x,
+                                                     float *__restrict__ y) {
+  constexpr int kElems = 128 / BITS, kPerWord = 32 / BITS, kN4 = kElems / 4;
+  extern __shared__ __align__(16) float xs[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nchunks = cols * BITS / 128;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RW;
+  const size_t row_bytes = (size_t)cols * BITS / 8;
+  uint4 wv[RW][CPL];
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr) {
+    const int64_t row = min(row0 + rr, rows - 1);
+    const uint4 *wr = reinterpret_cast<const uint4 *>(W + row * row_bytes);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int64_t c = lane + 64 * i;
+      wv[rr][i] = c < nchunks ? ld_nt(wr + c) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // float4 group m of chunk c at position c*kN4 + (m + c) % kN4
+  for (int64_t q = threadIdx.x; q < nchunks * kN4; q += 256) {
+    const int64_t c = q / kN4;
+    const int m = (int)(q - c * kN4);
+    reinterpret_cast<float4 *>(xs)[c * kN4 + (m + c) % kN4] = reinterpret_cast<const float4 *>(x)[q];
+  }
+  __syncthreads();
+  float acc[RW];
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr) acc[rr] = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int64_t c = lane + 64 * i;
+    if (c < nchunks) {
+      const float4 *xc = reinterpret_cast<const float4 *>(xs) + c * kN4;
+#pragma unroll
+      for (int m = 0; m < kN4; ++m) {
+        const float4 v = xc[(m + c) % kN4];
+        const float xv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+          const uint32_t ws[4] = {wv[rr][i].x, wv[rr][i].y, wv[rr][i].z, wv[rr][i].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int k = 4 * m + j;
+            const int sh = 32 - BITS * (k % kPerWord + 1);
+            const int code = (int)(ws[k / kPerWord] << sh) >> (32 - BITS);  // sign-extended field
+            acc[rr] = fmaf((float)code, xv[j], acc[rr]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr) {
+    const float sum = wave_sum(acc[rr]);
+    if (lane == 0 && row0 + rr < rows) y[row0 + rr] = scale[row0 + rr] * sum;
+  }
+}
+
+template <int BITS, int CPL, int RW>
+static hipError_t launch_gemv_f32act_t(const uint8_t *W, const float *scale, int64_t rows,
+                                       int64_t cols, const float *x, float *y, hipStream_t st) {
+  const dim3 grid((unsigned)((rows + 4 * RW - 1) / (4 * RW))), block(256);
+  hipLaunchKernelGGL((k_gemv_f32act<BITS, CPL, RW>), grid, block, (size_t)cols * 4, st, W, scale,
+                     rows, cols, x, y);
+  return hipGetLastError();
+}
+
+template <int BITS>
+static hipError_t launch_gemv_f32act_bits(const uint8_t *W, const float *scale, int64_t rows,
+                                          int64_t cols, const float *x, float *y, hipStream_t st) {
+  const int64_t per = (cols * BITS / 128 + 63) / 64;  // chunks per lane
+  if (per <= 1) return launch_gemv_f32act_t<BITS, 1, 4>(W, scale, rows, cols, x, y, st);
+  if (per <= 2) return launch_gemv_f32act_t<BITS, 2, 4>(W, scale, rows, cols, x, y, st);
+  if (per <= 3) return launch_gemv_f32act_t<BITS, 3, 2>(W, scale, rows, cols, x, y, st);
+  if (per <= 4) return launch_gemv_f32act_t<BITS, 4, 2>(W, scale, rows, cols, x, y, st);
+  if (per <= 6) return launch_gemv_f32act_t<BITS, 6, 1>(W, scale, rows, cols, x, y, st);
+  if (per <= 8) return launch_gemv_f32act_t<BITS, 8, 1>(W, scale, rows, cols, x, y, st);
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_gemv_f32act(int bits, const uint8_t *W, const float *scale, int64_t rows,
+                              int64_t cols, const float *x, float *y, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  switch (bits) {
+    case 8: return launch_gemv_f32act_bits<8>(W, scale, rows, cols, x, y, st);
+    case 4: return launch_gemv_f32act_bits<4>(W, scale, rows, cols, x, y, st);
+    case 2: return launch_gemv_f32act_bits<2>(W, scale, rows, cols, x, y, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // Threads per row: as many of 64, 128, 256 as the row has chunks for (at
 // least 64), so a matrix of a few thousand rows still gives every SIMD
 // several waves.

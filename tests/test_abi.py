@@ -49,6 +49,16 @@ def test_invalid_arguments_rejected_before_device():
     assert L.coli_quant_pack(4, None, 4, 32, _fake(16), _fake(16), None) == B.COLI_ERR_INVALID_ARG
     assert L.coli_quant_pack(4, _fake(16), 4, 48, _fake(16), _fake(16), None) == B.COLI_ERR_INVALID_ARG
     assert L.coli_quant_act_q8_0(_fake(16), 1, 33, _fake(16), _fake(16), None) == B.COLI_ERR_INVALID_ARG
+    f = _fake
+    # f32-activation GEMV: bad qtype, ragged columns, misaligned x, rows too long
+    assert L.coli_gemv_f32act(3, f(16), f(16), 4, 64, f(16), f(16), None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_gemv_f32act(2, f(16), f(16), 4, 32, f(16), f(16), None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_gemv_f32act(4, f(16), f(16), 4, 64, f(8), f(16), None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_gemv_f32act(4, f(16), None, 4, 64, f(16), f(16), None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_gemv_f32act(4, f(16), f(16), 4, 16384 + 32, f(16), f(16), None) \
+        == B.COLI_ERR_UNSUPPORTED
+    assert L.coli_gemv_f32act(8, f(16), f(16), 4, 8192 + 32, f(16), f(16), None) \
+        == B.COLI_ERR_UNSUPPORTED
     # FP8 requantisation: bad qtype, null scales, ragged columns, misaligned codes or output
     f = _fake
     assert L.coli_quant_pack_fp8(5, f(16), f(16), 4, 32, f(16), f(16), None) == B.COLI_ERR_INVALID_ARG
@@ -138,6 +148,8 @@ def test_no_device_reports_device_error():
                               None, None, None, _fake(0x300000), ws, None) == B.COLI_ERR_DEVICE
     assert L.coli_quant_pack(4, _fake(16), 4, 32, _fake(16), _fake(16), None) == B.COLI_ERR_DEVICE
     assert L.coli_quant_pack_fp8(4, _fake(16), _fake(16), 4, 32, _fake(16), _fake(16), None) \
+        == B.COLI_ERR_DEVICE
+    assert L.coli_gemv_f32act(4, _fake(16), _fake(16), 4, 64, _fake(16), _fake(16), None) \
         == B.COLI_ERR_DEVICE
     cfg = B.router_cfg(16, 2)
     assert L.coli_moe_route(ctypes.byref(cfg), _fake(16), None, 1, _fake(16), _fake(16), None) \

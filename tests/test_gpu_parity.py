@@ -123,6 +123,44 @@ def test_fp8_requant_equals_fp32_pack_on_device(orc):
     np.testing.assert_array_equal(s.view(np.uint32), s2.cpu().numpy().view(np.uint32))
 
 
+def _gemv_f32_case(orc, bits, R, C, seed, integer_x):
+    rng = np.random.default_rng(seed)
+    if integer_x:
+        # power-of-two scales and integer activations: every fp32 summation
+        # order is exact, so the GPU must match the oracle bit for bit
+        q = {8: 127, 4: 7, 2: 1}[bits]
+        codes = rng.integers(-q, q + 1, size=(R, C)).astype(np.float32)
+        codes[:, 0] = q
+        w = codes * F32(2.0 ** -7)
+        x = rng.integers(-8, 9, size=C).astype(np.float32)
+    else:
+        w = rng.normal(0, 0.02, size=(R, C)).astype(F32)
+        x = rng.normal(0, 1, size=C).astype(F32)
+    packed, scale = orc.quant_pack(bits, w)
+    y_ref = orc.qdot_f32act(bits, packed, scale, C, x[None, :])[0]
+    y = torch.empty(R, device="cuda")
+    B.coli_gemv_f32act(bits, to_dev(packed), to_dev(scale), to_dev(x), y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), y_ref
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("R,C", [(1, 64), (37, 128), (130, 1088), (21, 4096)])
+def test_gemv_f32act_exact_on_integer_activations(orc, bits, R, C):
+    y, y_ref = _gemv_f32_case(orc, bits, R, C, R + C + bits, True)
+    np.testing.assert_array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("bits,R,C", [(4, 2048, 6144), (4, 6144, 2048), (2, 2048, 6144),
+                                      (8, 2048, 6144), (8, 9, 8192), (2, 5, 16384),
+                                      (4, 19, 16384), (8, 131, 3072)])
+def test_gemv_f32act_glm_rows(orc, bits, R, C):
+    """GLM-5.2 expert rows and the longest rows of each container: fp32 sums
+    within 1e-4 of the row block's largest |y| (the oracle sums in binary64)."""
+    y, y_ref = _gemv_f32_case(orc, bits, R, C, 7 * bits + R, False)
+    assert np.abs(y.astype(np.float64) - y_ref).max() <= 1e-4 * np.abs(y_ref).max()
+
+
 @pytest.mark.parametrize("T,n", [(1, 32), (3, 256), (17, 6144), (512, 2048)])
 def test_act_quant_bit_exact(orc, T, n):
     rng = np.random.default_rng(T + n)
