@@ -100,8 +100,12 @@ __device__ __forceinline__ void fp8_store_chunk(const float (&v)[16], float s, f
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float y = v[i] * r;
-    near |= !(fabsf(y - (floorf(y) + 0.5f)) > 0x1p-15f);
     c[i] = rintf(y);
+    // more than 2^-15 from every half-integer <=> within 0.5 - 2^-15 of the
+    // nearest integer (y - rint(y) is exact: the operands are within a
+    // factor of two of each other, or rint(y) is zero); NaN and infinities
+    // fail the test
+    near |= !(fabsf(y - c[i]) < 0.5f - 0x1p-15f);
   }
   if (__ballot(near)) {
     if (near) {
@@ -354,9 +358,9 @@ hipError_t launch_gemv_f32act(int bits, const uint8_t *W, const float *scale, in
   }
 }
 
-// Threads per row: as many of 64, 128, 256 as the row has chunks for (at
-// least 64), so a matrix of a few thousand rows still gives every SIMD
-// several waves.
+// Threads per row: one wave for rows of up to 256 chunks (4096 columns),
+// four waves for longer rows, so a matrix of a few thousand rows still gives
+// every SIMD several waves while short rows skip the cross-wave reduction.
 template <int BITS, int TPR>
 static hipError_t launch_fp8_tpr(const uint8_t *w8, const float *bscale, int64_t rows,
                                  int64_t cols, uint8_t *q, float *scale, hipStream_t st) {
@@ -378,8 +382,7 @@ template <int BITS>
 static hipError_t launch_fp8_bits(const uint8_t *w8, const float *bscale, int64_t rows,
                                   int64_t cols, uint8_t *q, float *scale, hipStream_t st) {
   const int64_t chunks = cols / 16;
-  if (chunks > 128) return launch_fp8_tpr<BITS, 256>(w8, bscale, rows, cols, q, scale, st);
-  if (chunks > 64) return launch_fp8_tpr<BITS, 128>(w8, bscale, rows, cols, q, scale, st);
+  if (chunks > 256) return launch_fp8_tpr<BITS, 256>(w8, bscale, rows, cols, q, scale, st);
   return launch_fp8_tpr<BITS, 64>(w8, bscale, rows, cols, q, scale, st);
 }
 
