@@ -199,6 +199,9 @@ def main() -> int:
                     help="tokens per step with logits computed from the gate (overrides the "
                          "workload's batch; 1 = decode; with --workload stack: tokens per "
                          "step through the stack, e.g. 3 for MTP verify batches)")
+    ap.add_argument("--rho", type=float, default=None,
+                    help="verify3/prefill512: correlation of the supplied logits across the "
+                         "batch (0: independent tokens; near 1: few unique experts)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one untimed device-to-device copy of this many MiB after the "
                          "warm-up (the known-size reference for hardware byte counters)")
@@ -232,10 +235,14 @@ def main() -> int:
     T, supplied, rho = WORKLOADS[args.workload]
     if args.tokens > 0:
         T, supplied, rho = args.tokens, False, 0.0
+    if args.rho is not None and supplied:
+        rho = args.rho
     default_run = (args.bits in (None, 4) and args.tokens == 0 and args.workload != "tiny"
                    and args.mfma_min == 0)
     label = args.workload if default_run else (f"{args.workload}_int{s.bits}_T{T}" +
                                                (f"_mfma{args.mfma_min}" if args.mfma_min else ""))
+    if supplied and rho != 0.0:
+        label += f"_rho{rho:g}"
     K, W, NI = args.steps, args.warmup, args.instances
     cfg = B.router_cfg(s.n_experts, s.top_k, s.n_group, s.topk_group, 1, s.rsf, 0.0, 1)
 
@@ -441,9 +448,12 @@ def main() -> int:
                             else f"(rsf {s.rsf}) ")
                          + f"+ 1 shared, {'packed ' if s.bits < 8 else ''}int{s.bits} per-row fp32 "
                          "scale, Q8_0 activations" + (", logits from the fp32 gate" if not supplied
-                                                       else ", logits supplied")),
+                                                       else f", logits supplied (correlation "
+                                                            f"{rho:g} across the batch)")),
             "tokens_per_step": T,
             "layer_instances": NI,
+            "unique_experts_per_step": {"mean": round(float(uniq.mean()), 2),
+                                        "min": int(uniq.min()), "max": int(uniq.max())},
             "launch": "one HIP graph of the K timed steps",
             "kernel_us": ({"k_decode_fused": round(float(avg[0]) * 1e3, 3)} if T == 1 else
                           {"front": round(float(avg[0]) * 1e3, 3),

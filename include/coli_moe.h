@@ -75,21 +75,29 @@ typedef struct {
   int32_t top_p_renorm;        /* 1: renormalise the kept weights */
 } coli_router_cfg;
 
-/* One layer's weights (host struct of device pointers).
+/* One layer's weights (host struct of device pointers): the routed experts,
+ * the shared expert and the router gate of one MoE layer (colibrì README,
+ * "Implemented features": shared expert, sigmoid router; "Idea": 256 routed
+ * experts of ~19 MB each at int4).
  * Routed experts are stacked: w_gate/w_up [E][I][H*b/8], s_gate/s_up [E][I],
  * w_down [E][H][I*b/8], s_down [E][H].  The shared expert has the same
  * per-expert layouts (E = 1).  Every weight row must start 16-byte aligned
  * (holds for any 16-byte aligned base since H*b/8 and I*b/8 are multiples of
- * 16).  H and I are multiples of 64, at most 8192.  mfma_min_tokens: in a
+ * 16).  H and I are multiples of 64 (one 16-byte chunk of an int2 row, and
+ * a whole number of 32-row blocks in every kernel), at most 8192.
+ * mfma_min_tokens: in a
  * batch of T >= 2 tokens, a unique expert (or the shared expert) receiving at
  * least this many tokens runs on the int8 matrix cores, one with fewer on the
  * integer dot-product GEMV; 0 selects the library defaults (8 tokens for a
  * routed expert, 64 for the shared expert, which receives the whole batch).
- * Both give the same results up to fp32 summation order.  gate_offset: optional [E]
- * fp32 per-expert terms added (one binary32 addition) to the logits computed
- * from gate_w, before selection and weighting; it models a skewed expert
- * popularity on synthetic gates.  NULL = none; ignored when logits are
- * supplied, which already include any offset. */
+ * Both give the same results up to fp32 summation order.
+ * gate_offset: NOT a step of the pages' layer -- an extension for synthetic
+ * workloads.  Optional [E] fp32 per-expert terms added (one binary32
+ * addition) to the logits computed from gate_w, before selection and
+ * weighting; a synthetic gate uses it to give each layer a skewed (Zipf-like)
+ * expert popularity, the regime in which the pages' learned expert cache
+ * pays.  NULL = none (the layer as the pages define it); ignored when logits
+ * are supplied, which already include any offset. */
 typedef struct {
   int32_t hidden;   /* H: 6144 */
   int32_t inter;    /* I: 2048 */
@@ -113,7 +121,8 @@ typedef struct {
   const float *gate_offset; /* [E] fp32 or NULL */
 } coli_moe_layer;
 
-/* ABI version (COLI_ABI_VERSION) and a static message for a status. */
+/* ABI version (COLI_ABI_VERSION) and a static message for a status.  Library
+ * plumbing, not a step of the pages' layer. */
 int coli_abi_version(void);
 const char *coli_status_str(coli_status s);
 
@@ -167,8 +176,12 @@ coli_status coli_gemv_f32act(int32_t qtype, const uint8_t *w, const float *scale
 coli_status coli_quant_act_q8_0(const float *x, int32_t T, int32_t n,
                                 int8_t *q, float *d, void *stream);
 
-/* Router logits: logits [T][E] = x [T][H] . gate_w[E][H]^T, accumulated in
- * fp64 and rounded once to fp32.  H a positive multiple of 32. */
+/* Router logits (colibrì README, "Implemented features": the
+ * DeepSeek-V3-like router scores every routed expert from the token's hidden
+ * state; its gate is the one fp32 weight of the layer).
+ * logits [T][E] = x [T][H] . gate_w[E][H]^T, accumulated in fp64 and rounded
+ * once to fp32.  x, gate_w 16-byte aligned; H a positive multiple of 32;
+ * T >= 0 (0: no-op).  Writes logits [T][E]; reads nothing else. */
 coli_status coli_moe_logits(const float *x, const float *gate_w, int32_t T,
                             int32_t E, int32_t H, float *logits, void *stream);
 
@@ -201,18 +214,49 @@ coli_status coli_moe_dispatch(const int32_t *topk_idx, int32_t T, int32_t k,
                               void *stream);
 
 /* Workspace bytes coli_moe_forward needs for up to max_tokens tokens with
- * this layer's shapes (0 if the descriptor is invalid).  The workspace is a
- * device buffer, 256-byte aligned.  Its first COLI_WORKSPACE_COUNTER_BYTES
- * bytes hold the counters of the single-kernel decode path: they must be
- * zero before the workspace is first used (allocate it zeroed), and every
- * call leaves them zero.  If they are not, a decode call cannot hang or read
- * outside the layer, but its outputs are undefined.  One workspace serves one
- * call at a time. */
+ * this layer's shapes (0 if the descriptor is invalid).  The workspace holds
+ * what the layer passes between its steps: the Q8_0 codes of x and h, the
+ * routing, the batch-union tables (colibrì README, "Implemented features":
+ * batch-union MoE, each unique expert read once per batch) and, for T >= 2,
+ * one fp32 output row per (token, slot) that the combine sums in slot order.
+ * It is a caller-owned device buffer, 256-byte aligned.  Its first
+ * COLI_WORKSPACE_COUNTER_BYTES bytes are the state header of the
+ * single-kernel decode path: they must be zero before the workspace is first
+ * used (allocate it zeroed), and every call leaves them as it found them,
+ * except the status word below.  One workspace serves one call at a time.
+ *
+ * Status word (uint32 at byte offset COLI_WORKSPACE_STATUS_OFFSET; sticky):
+ * the decode kernel's waits for data other workgroups produce are bounded.
+ * They assume the kernel's workgroups (no more than the GPU holds at once)
+ * become resident together, which holds when it has the GPU to itself.  If
+ * other work holds part of the GPU and a wait runs out of polling rounds,
+ * the kernel ORs COLI_WAIT_SCORES (router scores) or COLI_WAIT_SLOTS (expert
+ * gate/up results) into the word, and that call's y and routing outputs are
+ * undefined.  The library never clears it; read and clear it with
+ * coli_moe_workspace_status.  A header holding stale nonzero counters can
+ * likewise only give undefined outputs, a set status bit, or both -- never a
+ * hang or an access outside the buffers.
+ *
+ * Polling bound (uint32 at COLI_WORKSPACE_SPIN_LIMIT_OFFSET): a test hook.
+ * If it is nonzero when a decode call starts, it replaces the default bound
+ * on each wait's polling rounds (capped at the default) for that call, which
+ * clears it.  Failure-handling tests set it to 1 so that waits give up while
+ * every workgroup still exits normally. */
 #define COLI_WORKSPACE_COUNTER_BYTES 20480
+#define COLI_WORKSPACE_STATUS_OFFSET 10752
+#define COLI_WORKSPACE_SPIN_LIMIT_OFFSET 11008
+#define COLI_WAIT_SCORES 1u
+#define COLI_WAIT_SLOTS 2u
 
 size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int32_t max_tokens);
 
-/* The layer on T tokens: y [T][H] fp32 = shared(x_t) + sum_j w_tj *
+/* The routed-expert MoE layer on T tokens (colibrì README, "Implemented
+ * features": the DeepSeek-V3-like sigmoid router with noaux_tc and
+ * routed_scaling_factor, the shared expert, int8 / packed int4 / packed int2
+ * experts with per-row scales against Q8_0-style int8 activations, and the
+ * batch-union MoE in which each unique expert of a batch is read once and
+ * applied to every token routed to it; "Quick start": expert top-p).
+ * y [T][H] fp32 = shared(x_t) + sum_j w_tj *
  * expert_{idx_tj}(x_t), the sum over kept slots in rank order, where
  * expert(x) = down( silu(gate . q(x)) * (up . q(x)) ) with both expert inputs
  * Q8_0-quantised and all three products integer dot products rescaled by the
@@ -221,15 +265,21 @@ size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int32_t max_tokens);
  * Optional outputs (NULL to skip): idx_out [T][k], w_out [T][k],
  * logits_out [T][E].  T = 1 runs the decode path (one kernel); T >= 2 groups
  * the batch by expert (each unique expert's weights are read once).  T = 0
- * is a no-op.  workspace must hold coli_moe_workspace_bytes(L, T) bytes. */
+ * is a no-op.  x and y 16-byte aligned.  workspace must hold
+ * coli_moe_workspace_bytes(L, T) bytes (see there for its header and status
+ * word).  Errors: COLI_ERR_INVALID_ARG for a bad descriptor, pointer or T
+ * (T < 0 or > 2^20), COLI_ERR_WORKSPACE for a missing, misaligned or short
+ * workspace, COLI_ERR_DEVICE for no gfx950 device or a failed launch; on any
+ * error nothing is enqueued. */
 coli_status coli_moe_forward(const coli_moe_layer *L, const float *x,
                              int32_t T, const float *logits_in, float *y,
                              int32_t *idx_out, float *w_out, float *logits_out,
                              void *workspace, size_t workspace_bytes,
                              void *stream);
 
-/* Profiling variant of coli_moe_forward (same work, same results) for the
- * benchmark.  stage_events holds n_stage_events caller-created hipEvent_t
+/* Profiling variant of coli_moe_forward: the same layer (colibrì README,
+ * "Implemented features"; see coli_moe_forward), same work, same results,
+ * for the benchmark.  stage_events holds n_stage_events caller-created hipEvent_t
  * handles (NULL entries skipped): [2i] and [2i+1] are recorded by the launch
  * of kernel i itself at its start and end (so their interval is that
  * kernel's execution time).  T = 1: kernel 0 is the single decode kernel
@@ -248,7 +298,18 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x,
                                       void *const *stage_events,
                                       int32_t n_stage_events);
 
-/* Test export of the integer products, same device code as the forward:
+/* Status of the decode path's bounded waits (library plumbing, not a step
+ * of the pages' layer; it reports when the outputs of coli_moe_forward are
+ * undefined).  The workspace's status word (see coli_moe_workspace_bytes) copied to
+ * status_out[0] (device int32) on the stream, then set to zero if clear is
+ * nonzero.  0 means every bounded wait of every decode call since the last
+ * clear completed.  workspace 256-byte aligned, status_out 4-byte aligned. */
+coli_status coli_moe_workspace_status(void *workspace, int32_t *status_out,
+                                      int32_t clear, void *stream);
+
+/* Test export of the integer products (colibrì README, "Implemented
+ * features": integer dot products of the int8 / packed int4 / packed int2
+ * weights against Q8_0-style int8 activations), same device code as the forward:
  * acc_out [T][rows][cols/32] int32 = per-block sums of weight codes times
  * Q8_0 codes, exact.  Wq [rows][cols*qtype/8], xq [T][cols] int8 (natural
  * order).  cols a positive multiple of 64, T <= 8. */

@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "coli_moe_forward_profiled": ([ctypes.POINTER(MoeLayerC), _P, i32, _P, _P, _P, _P, _P,
                                            _P, sz, _P, ctypes.POINTER(_P), i32], ctypes.c_int),
             "coli_debug_qgemv_blocks": ([i32, _P, i32, i32, _P, i32, _P, _P], ctypes.c_int),
+            "coli_moe_workspace_status": ([_P, _P, i32, _P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -273,9 +274,13 @@ def coli_moe_workspace_bytes(layer: MoeLayer, max_tokens: int) -> int:
     return lib().coli_moe_workspace_bytes(ctypes.byref(c), max_tokens)
 
 
-# Leading workspace bytes holding the decode kernel's counters
-# (COLI_WORKSPACE_COUNTER_BYTES in include/coli_moe.h).
+# Leading workspace bytes holding the decode kernel's counters, and the byte
+# offsets of its sticky status word and polling-bound test hook
+# (COLI_WORKSPACE_* in include/coli_moe.h), with the status bits.
 WORKSPACE_COUNTER_BYTES = 20480
+WORKSPACE_STATUS_OFFSET = 10752
+WORKSPACE_SPIN_LIMIT_OFFSET = 11008
+WAIT_SCORES, WAIT_SLOTS = 1, 2
 
 
 def workspace(layer: MoeLayer, max_tokens: int, device="cuda") -> torch.Tensor:
@@ -316,6 +321,17 @@ def coli_moe_forward_profiled(layer: MoeLayer, x: torch.Tensor, y: torch.Tensor,
         _ptr(logits_in, torch.float32, "logits_in"), _ptr(y, torch.float32, "y"),
         None, None, None, ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream),
         ev, len(events)))
+
+
+def coli_moe_workspace_status(ws: torch.Tensor, status_out: torch.Tensor, clear: bool = False,
+                              stream=None) -> None:
+    """status_out int32 [1] (device) <- the workspace's status word; cleared
+    afterwards when ``clear``."""
+    if status_out.numel() != 1:
+        raise ValueError("status_out must hold one int32")
+    _check("coli_moe_workspace_status", lib().coli_moe_workspace_status(
+        ctypes.c_void_p(ws.data_ptr()), _ptr(status_out, torch.int32, "status_out"),
+        1 if clear else 0, _stream(stream)))
 
 
 def coli_debug_qgemv_blocks(qtype: int, Wq: torch.Tensor, cols: int, xq: torch.Tensor,

@@ -356,6 +356,18 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
   });
 }
 
+coli_status coli_moe_workspace_status(void *workspace, int32_t *status_out, int32_t clear,
+                                      void *stream) {
+  return guarded([&] {
+    if (!workspace || !aligned(workspace, 256) || !status_out || !aligned(status_out, 4))
+      return COLI_ERR_INVALID_ARG;
+    const coli_status st = check_device();
+    if (st != COLI_OK) return st;
+    return from_hip(coli::launch_workspace_status(static_cast<uint32_t *>(workspace), status_out,
+                                                  clear ? 1 : 0, static_cast<hipStream_t>(stream)));
+  });
+}
+
 coli_status coli_debug_qgemv_blocks(int32_t qtype, const uint8_t *Wq, int32_t rows, int32_t cols,
                                     const int8_t *xq, int32_t T, int32_t *acc_out, void *stream) {
   return guarded([&] {

@@ -10,30 +10,37 @@
 // down phases each pay a launch, ramp-up and drain that one streaming kernel
 // pays once.
 //
-// Work items, in ticket order (each workgroup takes the next ticket from a
-// device-wide counter, so a workgroup only ever waits for items with lower
-// tickets, which are already running -- progress is guaranteed):
+// Work items, in ticket order:
 //   L   router logits, four expert rows per item (two waves per row, each
 //       summing half of the row in binary64; skipped if logits are given)
-//   GS  shared-expert gate/up + SwiGLU + Q8_0(h), 64 rows per item
-//   GR  routed-expert gate/up, one (slot, 64-row block) per item
-//   D   down projection + combine for a block of output rows, slot by slot
-//       in the combine order (shared, then routed 0 .. k-1), each slot as
-//       soon as all of its gate/up items are done.
-// GR and D items wait for the logits and then each selects the token's
-// experts itself with its whole workgroup (select.hpp): a few microseconds
-// of arithmetic, but no further round trip through memory before the expert
-// weights stream.  Every gate/up item quantises x into its own LDS (x is an
-// input, so no item has to publish it).  Data passed between workgroups
-// (logits, h codes and scales) is written and read with relaxed device-scope
-// 32-bit atomics, coherent across XCDs per access; a producer waits for its
-// stores to complete, then bumps a counter (relaxed atomic add).  No
-// cache-wide write-back or invalidation is needed -- such fences, issued by
-// every workgroup, cost far more than the whole layer.  Consumers spin on
-// the counter (bounded: a corrupted counter can never hang the GPU).  The
-// last workgroup to finish resets the counters, so they are zero for the
-// next call; the counters live in the first bytes of the workspace, which
-// must be zero before its first use.
+//   GS  shared-expert gate/up + SwiGLU + Q8_0(h), kGuRows rows per item
+//   GR  routed-expert gate/up, one (slot, kGuRows-row block) per item
+//   D   down projection + combine for a block of output rows, all slots in
+//       the combine order (shared, then routed 0 .. k-1).
+// Item i sits in work queue i % 8; workgroup b serves queue b % 8, taking
+// its first item statically (its own index) and later ones from the
+// queue's counter, so within a queue items start in ticket order.  GR and D
+// items wait for the router scores, D items for the gate/up items of every
+// slot.  These waits assume that the grid, sized to what the GPU holds at
+// once, becomes resident together, which holds when the kernel has the GPU
+// to itself.  If other work holds part of the GPU, a waiting workgroup can
+// occupy a slot that the producer of its data needs; then the wait gives up
+// after a bounded number of polling rounds (~0.1 s for the scores, ~0.8 s
+// for the slots), the call's outputs are undefined, and the give-up is
+// recorded in a sticky status word of the workspace header that the caller
+// reads (coli_moe_workspace_status).  No wait can hang the GPU.
+// GR and D items select the token's experts themselves with their whole
+// workgroup (select.hpp): a few microseconds of arithmetic, but no further
+// round trip through memory before the expert weights stream.  Every gate/up
+// item quantises x into its own LDS (x is an input, so no item has to
+// publish it).  Data passed between workgroups (scores, h codes and scales)
+// is written and read with relaxed device-scope atomics, coherent across
+// XCDs per access; a producer waits for its stores to complete, then bumps
+// a counter (relaxed atomic add).  No cache-wide write-back or invalidation
+// is needed -- such fences, issued by every workgroup, cost far more than
+// the whole layer.  The last workgroup to finish resets the counters, so
+// they are zero for the next call; the counters live in the first bytes of
+// the workspace, which must be zero before its first use.
 #include <algorithm>
 
 #include "actq.hpp"
@@ -43,11 +50,15 @@
 
 namespace coli {
 
-// Workspace header (uint32 words, zero between calls):
+// Workspace header (uint32 words, zero between calls except the status):
 //   counters, each on its own 256-byte line so polls and atomic adds on one
 //   do not contend with the others: one ticket per work queue, the finished
 //   workgroups, and per slot (routed 0 .. k-1, shared k) the finished
 //   gate/up items;
+//   the status word (sticky: give-ups of bounded waits, never cleared by the
+//   kernel) and the polling bound override (test hook: if nonzero at the
+//   start of a call, the bound on every wait's polling rounds; cleared by
+//   the call);
 //   then one 64-bit word per expert from the router: the complemented bits of
 //   the biased score c = sigma + bias (low half) and sigma (high half).  Zero
 //   means "not written yet", so consumers poll the scores themselves.
@@ -57,11 +68,15 @@ enum : int {
   kCtrTicket = 0,
   kCtrExit = kQueues * kCtrStride,
   kCtrSlot0 = kCtrExit + kCtrStride,
+  kCtrStatus = kCtrSlot0 + (kSelMaxK + 1) * kCtrStride,
+  kCtrSpin = kCtrStatus + kCtrStride,
   kScoreWords = 3072
 };
-static_assert(kCtrSlot0 + (kSelMaxK + 1) * kCtrStride <= kScoreWords, "counters overlap scores");
+static_assert(kCtrSpin + kCtrStride <= kScoreWords, "counters overlap scores");
 static_assert((kScoreWords + 2 * kSelMaxE) * 4 <= kDecodeCounterBytes,
               "decode state exceeds the workspace header");
+static_assert(kCtrStatus * 4 == COLI_WORKSPACE_STATUS_OFFSET, "status word offset");
+static_assert(kCtrSpin * 4 == COLI_WORKSPACE_SPIN_LIMIT_OFFSET, "polling bound offset");
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr uint32_t kSpinLimit = 1u << 19;  // ~100 ms of polling
@@ -96,17 +111,17 @@ __device__ __forceinline__ void publish(uint32_t *c, uint32_t v) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait until *c >= target (bounded).  Data behind the counter is then read
-// with device-scope loads, issued after this returns.
-__device__ __forceinline__ void wait_ge(const uint32_t *c, uint32_t target) {
-  if (threadIdx.x == 0) {
-    uint32_t it = 0;
-    while (ld_ctr(c) < target && it < kSpinLimit) {
-      __builtin_amdgcn_s_sleep(8);
-      ++it;
-    }
-  }
-  __syncthreads();
+// Polling rounds of a wait: the header's override when it is nonzero (at
+// most the default), else `dflt`.
+__device__ __forceinline__ uint32_t spin_bound(const DecodeArgs &d, uint32_t dflt) {
+  const uint32_t v = ld_ctr(d.ctr + kCtrSpin);
+  return v ? min(v, dflt) : dflt;
+}
+
+// A bounded wait that ran out of polling rounds: record it (the call's
+// outputs are undefined).
+__device__ __forceinline__ void gave_up(const DecodeArgs &d, uint32_t what) {
+  __hip_atomic_fetch_or(d.ctr + kCtrStatus, what, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // L item: logits of experts e0 .. e0 + kLogRows - 1.  The kWpr waves of a
@@ -179,12 +194,14 @@ __device__ __forceinline__ void select_local(const DecodeArgs &d, unsigned char 
     } else {
       const uint64_t *w = reinterpret_cast<const uint64_t *>(d.ctr + kScoreWords) + e;
       uint64_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t spin = spin_bound(d, kSpinLimit);
       uint32_t it = 0;
-      while ((uint32_t)v == 0u && it < kSpinLimit) {
+      while ((uint32_t)v == 0u && it < spin) {
         __builtin_amdgcn_s_sleep(2);
         v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ++it;
       }
+      if ((uint32_t)v == 0u) gave_up(d, COLI_WAIT_SCORES);
       in.c[e] = __uint_as_float(~(uint32_t)v);
       in.sg[e] = __uint_as_float((uint32_t)(v >> 32));
     }
@@ -248,11 +265,13 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
       const int q = threadIdx.x;
       const int sl = g0 + q == 0 ? k : g0 + q - 1;
       const uint32_t *c = d.ctr + kCtrSlot0 + sl * kCtrStride;
-      uint32_t it = 0;
-      while (ld_ctr(c) < (uint32_t)(I / kGuRows) && it < kSpinLimit * 8) {
+      const uint32_t spin = spin_bound(d, 8u * kSpinLimit);
+      uint32_t it = 0, v;
+      while ((v = ld_ctr(c)) < (uint32_t)(I / kGuRows) && it < spin) {
         __builtin_amdgcn_s_sleep(8);
         ++it;
       }
+      if (v < (uint32_t)(I / kGuRows)) gave_up(d, COLI_WAIT_SLOTS);
     }
     __syncthreads();
     if (I % 128 == 0) {
@@ -404,7 +423,7 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
       act_quant_block<BITS>(d.x + i * 32, xq_lds + i * 32, xd_lds + i);
     __syncthreads();
   }
-  // GS: shared expert, rows [64 (t - b_gsh), +64)
+  // GS: shared expert, rows [kGuRows (t - b_gsh), +kGuRows)
   for (; t < b_gr; t = next_ticket()) {
     TokList s{1, -1, k, true};
     gateup_body<BITS, GLPR, GCPL, 1, kDecWaves, true, BLK>(a, false, expert_ptrs(a.L, -1), s,
@@ -413,7 +432,7 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
   }
   // routed gate/up and down items: the token's experts, once
   if (t < d.total) select_local(d, dyn, sidx, sw);
-  // GR: routed slot u, rows [64 rb, +64)
+  // GR: routed slot u, rows [kGuRows rb, +kGuRows)
   for (; t < b_down; t = next_ticket()) {
     const int u = (t - b_gr) / n_rb, rb = (t - b_gr) % n_rb;
     if (u == 0 && rb == 0) {
@@ -447,6 +466,8 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
     const int nc = kCtrSlot0 / kCtrStride + k + 1;
     for (int i = threadIdx.x; i < nc; i += kDecThreads)
       __hip_atomic_store(d.ctr + i * kCtrStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(d.ctr + kCtrSpin, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d.n_log > 0)
       for (int e = threadIdx.x; e < a.E; e += kDecThreads)
         __hip_atomic_store(reinterpret_cast<uint64_t *>(d.ctr + kScoreWords) + e, (uint64_t)0,
@@ -514,6 +535,21 @@ static hipError_t launch_fused_bits(DecodeArgs d, hipStream_t st, KEvents ev) {
   if constexpr (BITS == 2) { COLI_DEC_CASE(32, 3, 32, 1) }
 #undef COLI_DEC_CASE
   return hipErrorNotSupported;
+}
+
+// The header's status word into *out, cleared afterwards when `clear`.
+__global__ void k_workspace_status(uint32_t *ctr, int32_t *out, int clear) {
+  if (threadIdx.x == 0) {
+    const uint32_t v = clear ? __hip_atomic_exchange(ctr + kCtrStatus, 0u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                             : ld_ctr(ctr + kCtrStatus);
+    *out = (int32_t)v;
+  }
+}
+
+hipError_t launch_workspace_status(uint32_t *ctr, int32_t *out, int clear, hipStream_t st) {
+  hipLaunchKernelGGL(k_workspace_status, dim3(1), dim3(64), 0, st, ctr, out, clear);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_fused(const FfnArgs &f, const float *x, const float *gate_w,

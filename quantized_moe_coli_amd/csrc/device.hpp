@@ -72,9 +72,35 @@ __device__ __forceinline__ float wave_max(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+// DPP move of a binary64 value (both 32-bit halves take the same pattern).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xFFFFFFFFll), CTRL, ROW_MASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROW_MASK, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
+// group_sum<L> in binary64: the same lanes hold the result, same fixed
+// pattern (lanes outside a row mask read +0, which adds exactly nothing).
+template <int L>
+__device__ __forceinline__ double group_sum_f64(double v) {
+  if constexpr (L >= 2) v += dpp_f64<0xB1>(v);
+  if constexpr (L >= 4) v += dpp_f64<0x4E>(v);
+  if constexpr (L >= 8) v += dpp_f64<0x141>(v);
+  if constexpr (L >= 16) v += dpp_f64<0x140>(v);
+  if constexpr (L >= 32) v += dpp_f64<0x142, 0xA>(v);
+  if constexpr (L >= 64) v += dpp_f64<0x143, 0xC>(v);
   return v;
+}
+
+// Sum over the wave in binary64 (DPP steps, then lane 63 broadcast).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = group_sum_f64<64>(v);
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), 63);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
 }
 
 // ---------------------------------------------------------------------------

@@ -52,7 +52,32 @@ __device__ __forceinline__ float chunk_part(const uint4 w, const Act<BITS> &ac) 
   }
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.f + expf(-g)); }
+// The chunk's block sums times their activation scales, in binary64: every
+// product of a binary32 scale and an exact int32 block sum is exact there,
+// so only the additions of a row's partial sums round (at the 2^-53 level).
+template <int BITS>
+__device__ __forceinline__ double chunk_part_f64(const uint4 w, const Act<BITS> &ac) {
+  if constexpr (BITS == 8) return (double)ac.d[0] * (double)chunk_dot_q8(w, ac.a);
+  else if constexpr (BITS == 4) return (double)ac.d[0] * (double)chunk_dot_q4(w, ac.a);
+  else {
+    int b0, b1;
+    chunk_dot_q2(w, ac.a, b0, b1);
+    return fma((double)ac.d[0], (double)b0, (double)ac.d[1] * (double)b1);
+  }
+}
+
+// h = fl32(silu(g) * u) from the binary32 g and u, with silu(z) =
+// z / (1 + exp(-z)) and the product evaluated in binary64 and rounded once
+// (the expert definition: g and u are the rescaled integer products
+// rounded to binary32, the SwiGLU step is exact up to that one rounding).
+__device__ __forceinline__ float swiglu_h(float g, float u) {
+  const double z = (double)g;
+  return (float)((z / (1.0 + exp(-z))) * (double)u);
+}
+
+// A row's rescaled product: fl32(s * sum), the sum of its block partials
+// taken in binary64.
+__device__ __forceinline__ float row_out(double sum, float s) { return (float)(sum * (double)s); }
 
 __device__ __forceinline__ float bcast(float v, int lane_idx) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane_idx));
@@ -211,23 +236,25 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, bool union_mode, c
       if (p + 1 < PASSES) load_rows(p + 1, (p + 1) & 1);
       const int buf = p & 1;
       const int rl = wave * ROWS_PER_WAVE + p * RPP + rsub;  // row within the item
-      float pg[NT], pu[NT];
+      // g and u of the row: block partials in binary64, summed across the
+      // row's lanes in binary64, times the row scale, rounded once
+      double pg[NT], pu[NT];
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
-        pg[tt] = 0.f;
-        pu[tt] = 0.f;
+        pg[tt] = 0.0;
+        pu[tt] = 0.0;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-          pg[tt] += chunk_part<BITS>(wg[buf][i], act[i][tt]);
-          pu[tt] += chunk_part<BITS>(wu[buf][i], act[i][tt]);
+          pg[tt] += chunk_part_f64<BITS>(wg[buf][i], act[i][tt]);
+          pu[tt] += chunk_part_f64<BITS>(wu[buf][i], act[i][tt]);
         }
-        pg[tt] = group_sum<LPR>(pg[tt]);
-        pu[tt] = group_sum<LPR>(pu[tt]);
+        pg[tt] = group_sum_f64<LPR>(pg[tt]);
+        pu[tt] = group_sum_f64<LPR>(pu[tt]);
       }
       const float sg = row_scale<RPP>(sgv, p, rsub), su = row_scale<RPP>(suv, p, rsub);
       if (lane == group_sum_lane<LPR>(lane)) {
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) hs[tt][rl] = silu_f32(pg[tt] * sg) * (pu[tt] * su);
+        for (int tt = 0; tt < NT; ++tt) hs[tt][rl] = swiglu_h(row_out(pg[tt], sg), row_out(pu[tt], su));
       }
     }
     __syncthreads();

@@ -140,6 +140,10 @@ hipError_t launch_decode_fused(const FfnArgs &f, const float *x, const float *ga
                                const float *logits_in, float *logits_out, uint32_t *ctr,
                                hipStream_t st, KEvents ev = {});
 
+// Copy the workspace header's sticky status word to out[0] (device), and
+// clear it when `clear` is nonzero.
+hipError_t launch_workspace_status(uint32_t *ctr, int32_t *out, int clear, hipStream_t st);
+
 hipError_t launch_debug_blocks(int bits, const uint8_t *Wq, int rows, int cols, const int8_t *xq_perm,
                                int T, int32_t *acc, hipStream_t st);
 

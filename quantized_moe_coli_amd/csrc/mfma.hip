@@ -182,10 +182,10 @@ struct MfmaLds {
   int trow[kMfmaTokens];              // activation row of each token
 };
 
-template <int BITS, int NMAT>
+template <int BITS, int NMAT, typename Acc>
 __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, size_t row_bytes,
                                           const int8_t *act, const float *actd, int K, int nt,
-                                          MfmaLds<BITS, NMAT> &L, float (*acc)[kMfmaTiles][4]) {
+                                          MfmaLds<BITS, NMAT> &L, Acc (*acc)[kMfmaTiles][4]) {
   using G = MfmaGeo<BITS>;
   constexpr int SH = wshift<BITS>();
   constexpr int PPR = G::RBC / 16;             // 16-byte pieces per weight row
@@ -262,12 +262,14 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, size_t ro
       for (int tt = 0; tt < kMfmaTiles; ++tt) {
         if (tt < ntt) {
           const long bx = *reinterpret_cast<const long *>(L.xs + (16 * tt + li) * G::XST + 32 * b + 8 * g);
-          const float dj = L.ds[16 * tt + li][b];
+          const Acc dj = (Acc)L.ds[16 * tt + li][b];
 #pragma unroll
           for (int m = 0; m < NMAT; ++m) {
             const v4i cm = __builtin_amdgcn_mfma_i32_16x16x32_i8(aw[m], bx, zero, 0, 0, 0);
+            // the block's exact int32 sum times the token's block scale
+            // (exact in binary64; one rounding per step in binary32)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[m][tt][r] += (float)(cm[r] >> SH) * dj;
+            for (int r = 0; r < 4; ++r) acc[m][tt][r] += (Acc)(cm[r] >> SH) * dj;
           }
         }
       }
@@ -298,13 +300,15 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(FfnArgs a) {
   }
   __syncthreads();
   const uint8_t *wb[2] = {ep.wg + (size_t)row0 * row_bytes, ep.wu + (size_t)row0 * row_bytes};
-  float acc[2][kMfmaTiles][4];
+  // g and u accumulate in binary64 (the expert definition's sum, rounded
+  // once), so h -- and its Q8_0 codes -- are those of that definition
+  double acc[2][kMfmaTiles][4];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int tt = 0; tt < kMfmaTiles; ++tt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[m][tt][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[m][tt][r] = 0.0;
   mfma_core<BITS, 2>(wb, row_bytes, a.xq, a.xd, H, it.nt, L, acc);
 
   // h = silu(g) * u for rows 4 g + r of the wave, token 16 tt + li, staged
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(256) void k_gateup_mfma(FfnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         hs[16 * tt + li][wave * 16 + 4 * g + r] =
-            silu_f32(acc[0][tt][r] * sg[r]) * (acc[1][tt][r] * su[r]);
+            swiglu_h(row_out(acc[0][tt][r], sg[r]), row_out(acc[1][tt][r], su[r]));
   __syncthreads();
   // Q8_0 of each token's two 32-row blocks of h: 32 threads per block
   for (int q = threadIdx.x; q < it.nt * kMfmaRows; q += 256) {

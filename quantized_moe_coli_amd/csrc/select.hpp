@@ -527,6 +527,10 @@ __device__ __forceinline__ void select_fast_t(const RouterCfg &cfg, const SelInp
       r += (v2 > gv || (v2 == gv && g2 < lane)) ? 1 : 0;
     }
     gmask = __ballot(lane < G && r < cfg.topk_group);
+    // finite scores rank the groups as a permutation, so exactly topk_group
+    // bits are set; NaN scores (a wait that gave up) can tie ranks, and the
+    // highest extra bits are dropped so the candidate slots stay in range
+    while (__popcll(gmask) > cfg.topk_group) gmask &= ~(1ull << (63 - __clzll(gmask)));
   }
 
   // the kept groups' top kk experts, by group id then rank inside the group

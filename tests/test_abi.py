@@ -124,8 +124,26 @@ def test_counter_header_size_matches_c_header():
     h = (pathlib.Path(__file__).resolve().parents[1] / "include" / "coli_moe.h").read_text()
     m = re.search(r"#define COLI_WORKSPACE_COUNTER_BYTES (\d+)", h)
     assert m and int(m.group(1)) == B.WORKSPACE_COUNTER_BYTES
+    for name, val in (("COLI_WORKSPACE_STATUS_OFFSET", B.WORKSPACE_STATUS_OFFSET),
+                      ("COLI_WORKSPACE_SPIN_LIMIT_OFFSET", B.WORKSPACE_SPIN_LIMIT_OFFSET)):
+        m = re.search(rf"#define {name} (\d+)", h)
+        assert m and int(m.group(1)) == val, name
+        assert val % 256 == 0 and val < B.WORKSPACE_COUNTER_BYTES  # own 256-byte line
+    for name, val in (("COLI_WAIT_SCORES", B.WAIT_SCORES), ("COLI_WAIT_SLOTS", B.WAIT_SLOTS)):
+        m = re.search(rf"#define {name} (\d+)u", h)
+        assert m and int(m.group(1)) == val, name
     s = _layer_struct()
     assert B.lib().coli_moe_workspace_bytes(ctypes.byref(s), 1) > B.WORKSPACE_COUNTER_BYTES
+
+
+def test_workspace_status_rejects_bad_arguments():
+    L = B.lib()
+    assert L.coli_moe_workspace_status(None, _fake(16), 0, None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_moe_workspace_status(_fake(0x300010), _fake(16), 0, None) \
+        == B.COLI_ERR_INVALID_ARG  # not 256-byte aligned
+    assert L.coli_moe_workspace_status(_fake(0x300000), None, 1, None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_moe_workspace_status(_fake(0x300000), _fake(0x10002), 1, None) \
+        == B.COLI_ERR_INVALID_ARG
 
 
 def test_workspace_grows_with_tokens():

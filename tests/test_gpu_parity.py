@@ -413,7 +413,7 @@ def test_decode_workspace_reuse(tiny_pairs):
         for u, v in zip(a, b):
             np.testing.assert_array_equal(u, v)
     hdr = ws[:B.WORKSPACE_COUNTER_BYTES].cpu().numpy()
-    assert (hdr == 0).all()
+    assert (hdr == 0).all()  # the status word too: no wait gave up
 
 
 @pytest.mark.parametrize("T", [1, 3])
@@ -491,6 +491,45 @@ def test_glm_union_sampled(glm, T):
     for t in (0, T // 2, T - 1):
         y_r, _, _, _ = glm.oracle_forward(xh[t:t + 1])
         assert_close_layer(y[t:t + 1], y_r)
+
+
+def _ws_status(ws, clear=False) -> int:
+    st = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    B.coli_moe_workspace_status(ws, st, clear=clear)
+    torch.cuda.synchronize()
+    return int(st.item())
+
+
+@pytest.mark.slow
+def test_decode_wait_giveup_is_reported(glm):
+    """Failure handling of the decode kernel's bounded waits, forced from the
+    host: a polling bound of one round (the workspace's test hook) makes the
+    down items give up on gate/up results that are still streaming.  The call
+    completes (every workgroup exits), the sticky status word records the
+    give-up, the call clears the hook, and after the status is cleared the
+    next call on the same workspace is bit-identical to one on a fresh
+    workspace."""
+    x = inputs.tokens(glm.s, 0, 6, 1, "cuda")
+    ref = glm.gpu_forward(x)
+    ws = B.workspace(glm.gpu, 1)
+    assert _ws_status(ws) == 0
+    a = glm.gpu_forward(x, ws=ws)
+    for u, v in zip(a, ref):
+        np.testing.assert_array_equal(u, v)
+    assert _ws_status(ws) == 0
+    off = B.WORKSPACE_SPIN_LIMIT_OFFSET
+    ws[off:off + 4].copy_(torch.tensor([1, 0, 0, 0], dtype=torch.uint8))
+    glm.gpu_forward(x, ws=ws)  # outputs undefined
+    st = _ws_status(ws, clear=True)
+    assert st & B.WAIT_SLOTS, st
+    assert st & ~(B.WAIT_SCORES | B.WAIT_SLOTS) == 0, st
+    assert _ws_status(ws) == 0
+    hdr = ws[:B.WORKSPACE_COUNTER_BYTES].cpu().numpy()
+    assert (hdr == 0).all()  # counters, scores and the hook cleared by the call
+    b = glm.gpu_forward(x, ws=ws)
+    for u, v in zip(b, ref):
+        np.testing.assert_array_equal(u, v)
+    assert _ws_status(ws) == 0
 
 
 # The full-size layer (256 experts, computed logits) in the int8 and int2
@@ -597,3 +636,72 @@ def test_glm_rows_matrix_cores(glm_rows, bits):
             assert_close_layer(y[t:t + 1], y_r)
     finally:
         p.gpu.mfma_min_tokens = 0
+
+
+# Matrix-core work items cover up to 64 tokens of one expert; an expert with
+# more runs as several token groups (first token n0 = 0, 64, 128, ...).
+@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("mfma_min", [1, 0])
+def test_union_matrix_cores_long_groups(bits, mfma_min):
+    """4 experts top-2 over 300 tokens: every routed expert receives 139-165
+    tokens, so each runs as three 64-token groups on the matrix cores, and
+    the shared expert (300 tokens) as five."""
+    s = inputs.TINY.with_(n_experts=4, top_k=2, n_group=1, topk_group=1, bits=bits)
+    p = LayerPair(s, seed=5, mfma_min_tokens=mfma_min)
+    T = 300
+    x = inputs.tokens(s, 0, 301, T)
+    y_r, idx_r, w_r, _ = p.oracle_forward(x.numpy())
+    counts = np.bincount(idx_r.ravel(), minlength=s.n_experts)
+    assert counts.min() > 128, counts  # the case this test is for
+    y, idx, w, _ = p.gpu_forward(x.cuda())
+    np.testing.assert_array_equal(idx, idx_r)
+    np.testing.assert_array_equal(w, w_r)
+    assert_close_layer(y, y_r)
+
+
+def _prefill_picks(idx: np.ndarray, E: int, T: int, n_experts_checked: int = 3) -> list[int]:
+    """Tokens to check against the oracle in a long batch: every 73rd token
+    (spread over the batch and over the shared expert's 64-token groups),
+    the last one, and in the batch's most loaded experts the tokens at
+    union positions 64, 130 and the last (past the first and second 64-token
+    group of that expert's matrix-core work)."""
+    counts = np.bincount(idx[idx >= 0], minlength=E)
+    picks = set(range(0, T, 73)) | {T - 1}
+    for e in np.argsort(-counts, kind="stable")[:n_experts_checked]:
+        toks = np.nonzero((idx == e).any(axis=1))[0]
+        for pos in (64, 130, len(toks) - 1):
+            if pos < len(toks):
+                picks.add(int(toks[pos]))
+    return sorted(picks)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("rho", [0.0, 0.99])
+def test_glm_prefill512(glm, rho):
+    """The 512-token prefill batch at full GLM-5.2 shape (256 int4 experts,
+    logits supplied with correlation rho across the batch): routing of every
+    token bit-exact, and the outputs of sampled tokens within the layer
+    tolerance.  rho = 0 gives ~256 unique experts of ~16 tokens each; rho =
+    0.99 gives ~20-30 unique experts, the busiest with up to 512 tokens, so
+    routed experts run as several 64-token matrix-core groups."""
+    T = 512
+    E = glm.s.n_experts
+    x = inputs.tokens(glm.s, 0, 4000, T, "cuda")
+    lg = inputs.correlated_logits(21, T, E, rho)
+    y, idx, w, _ = glm.gpu_forward(x, lg.cuda())
+    lgh = lg.numpy()
+    idx_r, w_r = oracle.route(orc_cfg(glm.s), lgh, glm.gate_bias)
+    np.testing.assert_array_equal(idx, idx_r)
+    np.testing.assert_array_equal(w, w_r)
+    counts = np.bincount(idx_r[idx_r >= 0], minlength=E)
+    if rho > 0.9:
+        assert counts.max() > 128, counts.max()  # routed multi-group items run
+    picks = _prefill_picks(idx_r, E, T)
+    assert len(picks) >= 8, picks
+    xh = x.cpu().numpy()
+    errs = []
+    for t in picks:
+        y_r, _, _, _ = glm.oracle_forward(xh[t:t + 1], lgh[t:t + 1])
+        errs.append(assert_close_layer(y[t:t + 1], y_r))
+    print(f"prefill512 rho {rho}: U {int((counts > 0).sum())}, max tokens/expert "
+          f"{counts.max()}, {len(picks)} tokens checked, max rel err {max(errs):.2e}")
