@@ -298,6 +298,28 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x,
                                       void *const *stage_events,
                                       int32_t n_stage_events);
 
+/* coli_moe_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same layer, kernels and results, with the workspace
+ * replaced by the library's own static device scratch of
+ * COLI_NOALLOC_SCRATCH_BYTES per GPU (allocated when the library's code is
+ * loaded on that GPU and held until the process ends).  The call allocates
+ * nothing.  The caller still passes x, y and the optional outputs, as for
+ * coli_moe_forward.  T whose workspace (coli_moe_workspace_bytes) exceeds
+ * the scratch returns COLI_ERR_UNSUPPORTED and enqueues nothing (about 128
+ * tokens at the GLM-5.2 shape; 1 token always fits).  wait_status_out:
+ * optional device int32 that receives the scratch's status word after the
+ * call (0 = every bounded wait completed), which is then cleared.  Every call
+ * on one GPU shares that GPU's scratch and keeps its contents until the next
+ * call: calls that overlap on one GPU (other streams, other threads) race and
+ * give undefined results; serialise them. */
+#define COLI_NOALLOC_SCRATCH_BYTES (32u << 20)
+coli_status coli_moe_forward_noalloc(const coli_moe_layer *L, const float *x,
+                                     int32_t T, const float *logits_in,
+                                     float *y, int32_t *idx_out, float *w_out,
+                                     float *logits_out,
+                                     int32_t *wait_status_out, void *stream);
+
 /* Status of the decode path's bounded waits (library plumbing, not a step
  * of the pages' layer; it reports when the outputs of coli_moe_forward are
  * undefined).  The workspace's status word (see coli_moe_workspace_bytes) copied to

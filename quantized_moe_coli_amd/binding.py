@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
                                            _P, sz, _P, ctypes.POINTER(_P), i32], ctypes.c_int),
             "coli_debug_qgemv_blocks": ([i32, _P, i32, i32, _P, i32, _P, _P], ctypes.c_int),
             "coli_moe_workspace_status": ([_P, _P, i32, _P], ctypes.c_int),
+            "coli_moe_forward_noalloc": ([ctypes.POINTER(MoeLayerC), _P, i32, _P, _P, _P, _P, _P,
+                                          _P, _P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -306,6 +308,27 @@ def coli_moe_forward(layer: MoeLayer, x: torch.Tensor, y: torch.Tensor, ws: torc
         _ptr(idx_out, torch.int32, "idx_out"), _ptr(w_out, torch.float32, "w_out"),
         _ptr(logits_out, torch.float32, "logits_out"), ctypes.c_void_p(ws.data_ptr()),
         ws.numel(), _stream(stream)))
+
+
+# Bytes of the library's static per-GPU scratch behind coli_moe_forward_noalloc
+# (COLI_NOALLOC_SCRATCH_BYTES in include/coli_moe.h).
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def coli_moe_forward_noalloc(layer: MoeLayer, x: torch.Tensor, y: torch.Tensor, logits_in=None,
+                             idx_out=None, w_out=None, logits_out=None, wait_status_out=None,
+                             stream=None, c_layer: MoeLayerC | None = None) -> None:
+    """coli_moe_forward without a workspace argument: the library's static
+    per-GPU scratch serves as the workspace (calls on one GPU must not
+    overlap); optional ``wait_status_out`` int32 [1] receives the status word."""
+    T = x.shape[0]
+    c = c_layer if c_layer is not None else layer.c_struct()
+    _check("coli_moe_forward_noalloc", lib().coli_moe_forward_noalloc(
+        ctypes.byref(c), _ptr(x, torch.float32, "x"), T,
+        _ptr(logits_in, torch.float32, "logits_in"), _ptr(y, torch.float32, "y"),
+        _ptr(idx_out, torch.int32, "idx_out"), _ptr(w_out, torch.float32, "w_out"),
+        _ptr(logits_out, torch.float32, "logits_out"),
+        _ptr(wait_status_out, torch.int32, "wait_status_out"), _stream(stream)))
 
 
 def coli_moe_forward_profiled(layer: MoeLayer, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor,

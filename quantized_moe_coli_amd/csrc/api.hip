@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "coli_moe.h"
 #include "kernels.hpp"
@@ -108,6 +109,39 @@ WsLayout ws_layout(const coli_moe_layer *L, int Tmax) {
   w.obuf = take(Tmax >= 2 ? T * (k + 1) * H * 4 : 0);
   w.total = off;
   return w;
+}
+
+// Scratch of coli_moe_forward_noalloc: the forward's workspace as a
+// file-scope device array, one copy per GPU the library runs on, held until
+// the process ends.  Host code never names it except to look up each
+// device's address (the name is a host-side stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[COLI_NOALLOC_SCRATCH_BYTES];
+
+// Per device: its copy's address, found once with that device current.
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];
+
+__global__ void k_zero_words(uint32_t *p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The current device's scratch address (nullptr on failure).  The first call
+// on a device also clears the decode header at the start of the scratch with
+// a kernel on `st` (a fill kernel, not a memset node, so it may be captured).
+void *scratch_ptr(int dev, hipStream_t st) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    hipLaunchKernelGGL(k_zero_words, dim3(COLI_WORKSPACE_COUNTER_BYTES / 4 / 256), dim3(256), 0, st,
+                       static_cast<uint32_t *>(p), COLI_WORKSPACE_COUNTER_BYTES / 4);
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 template <typename F>
@@ -353,6 +387,30 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
     if (e == hipSuccess && mfma) e = coli::launch_down_mfma(fa, s, kev(4));
     if (e == hipSuccess) e = coli::launch_combine(fa, s);
     return from_hip(e);
+  });
+}
+
+coli_status coli_moe_forward_noalloc(const coli_moe_layer *L, const float *x, int32_t T,
+                                     const float *logits_in, float *y, int32_t *idx_out,
+                                     float *w_out, float *logits_out, int32_t *wait_status_out,
+                                     void *stream) {
+  return guarded([&] {
+    if (!layer_ok(L) || T < 0 || T > kMaxTokens) return COLI_ERR_INVALID_ARG;
+    if (wait_status_out && !aligned(wait_status_out, 4)) return COLI_ERR_INVALID_ARG;
+    if (T == 0) return COLI_OK;
+    if (ws_layout(L, T).total > (size_t)COLI_NOALLOC_SCRATCH_BYTES) return COLI_ERR_UNSUPPORTED;
+    const coli_status st = check_device();
+    if (st != COLI_OK) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return COLI_ERR_DEVICE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *ws = scratch_ptr(dev, s);
+    if (!ws) return COLI_ERR_DEVICE;
+    const coli_status r = coli_moe_forward_profiled(L, x, T, logits_in, y, idx_out, w_out,
+                                                    logits_out, ws, COLI_NOALLOC_SCRATCH_BYTES,
+                                                    stream, nullptr, 0);
+    if (r != COLI_OK || !wait_status_out) return r;
+    return from_hip(coli::launch_workspace_status(static_cast<uint32_t *>(ws), wait_status_out, 1, s));
   });
 }
 
