@@ -188,7 +188,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--instances", type=int, default=8)
-    ap.add_argument("--workload", choices=list(WORKLOADS) + ["stack", "fp8convert", "gemvf32"],
+    ap.add_argument("--workload", choices=list(WORKLOADS) + ["stack", "fp8convert", "gemvf32",
+                                                          "timeline"],
                     default="decode")
     ap.add_argument("--layers", type=int, default=40, help="stack workload: layers resident")
     ap.add_argument("--bits", type=int, choices=(8, 4, 2), default=None,
@@ -228,6 +229,8 @@ def main() -> int:
         return fp8_main(args)
     if args.workload == "gemvf32":
         return gemv_f32_main(args)
+    if args.workload == "timeline":
+        return timeline_main(args)
     dev = "cuda"
     s = inputs.TINY if args.workload == "tiny" else inputs.GLM
     if args.bits is not None:
@@ -544,6 +547,128 @@ def cpu_baseline(s, layer0, xs, lgs, ys, NI, budget_s, T):
                   f"(steps 0, {NI}, {2 * NI}, ...), {spent:.1f} s of CPU time; GPU outputs "
                   f"of the same steps agree to {max_err:.1e}",
     }
+
+
+TRACE_NAMES = {1: "entry", 2: "logit slices done", 3: "x quantised", 4: "shared gate/up item done",
+               5: "selection begins", 6: "scores read", 7: "selection done",
+               8: "routed gate/up item done", 9: "down item begins", 10: "down item h ready",
+               11: "down item done", 12: "exit"}
+
+
+def timeline_main(args) -> int:
+    """Where the single-kernel decode's time goes: the timeline build of the
+    library records every workgroup's phase and item boundaries
+    (s_memrealtime, 10 ns ticks) on the default decode workload; each step's
+    times are taken from its first workgroup's entry, and the medians over
+    the steps of each phase's first / median / last workgroup are reported.
+    Beside it, the plain streaming read of as many bytes (the practical HBM
+    ceiling for a kernel with no routing and no dependencies) over 8
+    distinct buffers, timed with hip events."""
+    import numpy as np
+    import torch
+
+    from quantized_moe_coli_amd import binding as B
+    from quantized_moe_coli_amd import inputs
+
+    dev = "cuda"
+    s = inputs.GLM if args.bits is None else inputs.GLM.with_(bits=args.bits)
+    NI, K = args.instances, max(8, min(args.steps, 64))
+    cfg = B.router_cfg(s.n_experts, s.top_k, s.n_group, s.topk_group, 1, s.rsf, 0.0, 1)
+    layers = []
+    for li in range(NI):
+        L = B.MoeLayer.empty(s.hidden, s.inter, s.bits, cfg, dev)
+        L.gate_w.copy_(inputs.gate_weight(s, li, dev))
+        L.gate_bias.copy_(inputs.gate_bias(s, li, dev))
+        for e in range(s.n_experts + 1):
+            g, u, d = inputs.expert_weights(s, li, e, dev)
+            L.pack_expert(e, g, u, d)
+            del g, u, d
+        layers.append(L)
+    torch.cuda.synchronize()
+    cls = [L.c_struct() for L in layers]
+    xs = [inputs.tokens(s, 1, st, 1, dev) for st in range(K + 8)]
+    y = torch.empty(1, s.hidden, device=dev)
+    ws = B.workspace(layers[0], 1)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    trace = torch.zeros(8 * n_cu, B.TRACE_RECORDS, 2, dtype=torch.int64, device=dev)
+    for st in range(8):  # warm-up
+        B.coli_debug_decode_trace(layers[st % NI], xs[st], y, ws, trace, c_layer=cls[st % NI])
+    torch.cuda.synchronize()
+    rows = {}  # name -> list over steps of (first, median, last) in us
+    kern = []
+    for st in range(K):
+        trace.zero_()
+        li = (8 + st) % NI
+        grid = B.coli_debug_decode_trace(layers[li], xs[8 + st], y, ws, trace, c_layer=cls[li])
+        torch.cuda.synchronize()
+        r = trace[:grid].cpu().numpy()
+        code = (r[:, :, 0] >> 48) & 0xFFFF
+        tm = r[:, :, 1].astype(np.float64)
+        t0 = tm[code == 1].min()
+        rel = (tm - t0) / 100.0  # 100 MHz ticks -> us
+        kern.append(rel[code == 12].max())
+        for c, nm in TRACE_NAMES.items():
+            v = rel[code == c]
+            if v.size:
+                rows.setdefault(nm, []).append((v.min(), np.median(v), v.max(), v.size))
+    table = {nm: {"first": round(float(np.median([x[0] for x in v])), 2),
+                  "median": round(float(np.median([x[1] for x in v])), 2),
+                  "last": round(float(np.median([x[2] for x in v])), 2),
+                  "records": int(np.median([x[3] for x in v]))}
+             for nm, v in rows.items()}
+    log(f"[bench] timeline of the single-kernel decode (int{s.bits}, grid {grid}, medians over {K} "
+        f"steps; us from the first workgroup's entry)")
+    for nm in TRACE_NAMES.values():
+        if nm in table:
+            t = table[nm]
+            log(f"[bench]   {nm:26s} first {t['first']:6.2f}  median {t['median']:6.2f}  "
+                f"last {t['last']:6.2f}  ({t['records']} records)")
+    eb = expert_bytes(s)
+    step_bytes = 9 * eb["total"] + s.n_experts * s.hidden * 4 + 2 * s.hidden * 4
+    # plain streaming read of the same bytes, 8 distinct buffers
+    nbytes = (step_bytes + 15) // 16 * 16
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(8)]
+    for b in bufs:
+        b.fill_(1)
+    out = torch.empty(8 * n_cu, dtype=torch.int32, device=dev)
+    for b in bufs:
+        B.coli_debug_stream_read(b, out)
+    torch.cuda.synchronize()
+    reps = 200
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(reps):
+        B.coli_debug_stream_read(bufs[i % 8], out)
+    stop.record()
+    torch.cuda.synchronize()
+    stream_us = start.elapsed_time(stop) / reps * 1e3
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    big.fill_(1)
+    B.coli_debug_stream_read(big, out)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(20):
+        B.coli_debug_stream_read(big, out)
+    stop.record()
+    torch.cuda.synchronize()
+    big_us = start.elapsed_time(stop) / 20 * 1e3
+    kernel_us = float(np.median(kern))
+    log(f"[bench] decode kernel (trace build, median over steps) {kernel_us:.2f} us for "
+        f"{step_bytes / 1e6:.2f} MB")
+    log(f"[bench] plain streaming read of {nbytes / 1e6:.2f} MB: {stream_us:.2f} us "
+        f"({nbytes / stream_us / 1e3:.0f} GB/s); of 1 GiB: {big_us:.1f} us "
+        f"({(1 << 30) / big_us / 1e3:.0f} GB/s)")
+    print(json.dumps({
+        "metric": "single-kernel decode timeline (us from the first workgroup's entry)",
+        "workload": f"GLM-5.2 layer batch-1 decode, int{s.bits}, {NI} layer instances",
+        "grid": grid, "steps": K, "phases": table,
+        "kernel_us": round(kernel_us, 2),
+        "stream_ceiling": {"bytes": nbytes, "us": round(stream_us, 2),
+                           "GBps": round(nbytes / stream_us / 1e3, 1),
+                           "GiB_us": round(big_us, 1),
+                           "GiB_GBps": round((1 << 30) / big_us / 1e3, 1)},
+    }), flush=True)
+    return 0
 
 
 def _kernel_events(hip, n):

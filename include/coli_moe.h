@@ -238,10 +238,12 @@ coli_status coli_moe_dispatch(const int32_t *topk_idx, int32_t T, int32_t k,
  * hang or an access outside the buffers.
  *
  * Polling bound (uint32 at COLI_WORKSPACE_SPIN_LIMIT_OFFSET): a test hook.
- * If it is nonzero when a decode call starts, it replaces the default bound
- * on each wait's polling rounds (capped at the default) for that call, which
- * clears it.  Failure-handling tests set it to 1 so that waits give up while
- * every workgroup still exits normally. */
+ * If it is nonzero when a decode call starts, its bits 0-30 replace the
+ * default bound on each wait's polling rounds (capped at the default) for
+ * that call, which clears it; with bit 31 set every wait of the call also
+ * treats its data as absent, runs the bound out and gives up.
+ * Failure-handling tests set it to 0x80000001 so that waits give up
+ * deterministically while every workgroup still exits normally. */
 #define COLI_WORKSPACE_COUNTER_BYTES 20480
 #define COLI_WORKSPACE_STATUS_OFFSET 10752
 #define COLI_WORKSPACE_SPIN_LIMIT_OFFSET 11008
@@ -339,6 +341,39 @@ coli_status coli_debug_qgemv_blocks(int32_t qtype, const uint8_t *Wq,
                                     int32_t rows, int32_t cols,
                                     const int8_t *xq, int32_t T,
                                     int32_t *acc_out, void *stream);
+
+/* Diagnostics (library plumbing, not steps of the pages' layer).
+ *
+ * coli_debug_decode_trace: coli_moe_forward for one token with logits
+ * computed from the gate, on the single-kernel decode path only
+ * (COLI_ERR_UNSUPPORTED for row shapes it is not built for, and always in
+ * libcoli_moe.so: only the timeline build of the library, libcoli_moe_trace.so,
+ * compiles the records in), recording a timeline: trace [trace_wgs][COLI_TRACE_RECORDS][2] uint64 (device), for
+ * workgroups below trace_wgs, record n = (code << 48 | value, s_memrealtime
+ * ticks at 100 MHz) at phase and item boundaries (codes: 1 entry, 2 logit
+ * slices done, 3 x quantised, 4 shared gate/up item done, 5 selection
+ * begins, 6 router scores all read, 7 selection done, 8 routed gate/up item
+ * done, 9 down item begins, 10 its h is ready, 11 down item done, 12 exit;
+ * the value is the item's ticket).  Unused records keep their contents: zero
+ * the buffer first.  *grid_out (host) receives the grid size.  Same results
+ * as coli_moe_forward.
+ *
+ * coli_debug_stream_read: reads `bytes` (a positive multiple of 16) of the
+ * 16-byte aligned device buffer `buf` with the plain streaming access
+ * pattern of a bandwidth-bound kernel (16-byte non-temporal loads, eight in
+ * flight per lane, grid-strided over as many workgroups as keep the GPU
+ * full) and writes one xor word per workgroup to out [*grid_out] (device;
+ * must hold 8 words per compute unit).  Its duration is the practical HBM
+ * ceiling for that many bytes. */
+#define COLI_TRACE_RECORDS 64
+coli_status coli_debug_decode_trace(const coli_moe_layer *L, const float *x,
+                                    float *y, void *workspace,
+                                    size_t workspace_bytes, uint64_t *trace,
+                                    int32_t trace_wgs, int32_t *grid_out,
+                                    void *stream);
+coli_status coli_debug_stream_read(const void *buf, size_t bytes,
+                                   uint32_t *out, int32_t *grid_out,
+                                   void *stream);
 
 #ifdef __cplusplus
 }

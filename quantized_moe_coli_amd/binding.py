@@ -49,44 +49,64 @@ class MoeLayerC(ctypes.Structure):
                 ("mfma_min_tokens", ctypes.c_int32), ("gate_offset", _P)]
 
 
+# The timeline build (decode kernel with timeline records compiled in), for
+# coli_debug_decode_trace only.
+TRACE_LIB_PATH = os.path.join(_PKG, "libcoli_moe_trace.so")
+
 _lib = None
+_trace_lib = None
 
 
 def lib() -> ctypes.CDLL:
     """Load the library (built in-tree by ``__graft_entry__.build()``)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                               "(python -m quantized_moe_coli_amd.build)")
-        L = ctypes.CDLL(LIB_PATH)
-        i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-        sig = {
-            "coli_abi_version": ([], ctypes.c_int),
-            "coli_status_str": ([ctypes.c_int], ctypes.c_char_p),
-            "coli_quant_pack": ([i32, _P, i64, i64, _P, _P, _P], ctypes.c_int),
-            "coli_quant_pack_fp8": ([i32, _P, _P, i64, i64, _P, _P, _P], ctypes.c_int),
-            "coli_gemv_f32act": ([i32, _P, _P, i64, i64, _P, _P, _P], ctypes.c_int),
-            "coli_quant_act_q8_0": ([_P, i32, i32, _P, _P, _P], ctypes.c_int),
-            "coli_moe_logits": ([_P, _P, i32, i32, i32, _P, _P], ctypes.c_int),
-            "coli_moe_route": ([ctypes.POINTER(RouterCfg), _P, _P, i32, _P, _P, _P], ctypes.c_int),
-            "coli_moe_dispatch": ([_P, i32, i32, i32, _P, _P, _P, _P, _P, _P], ctypes.c_int),
-            "coli_moe_workspace_bytes": ([ctypes.POINTER(MoeLayerC), i32], sz),
-            "coli_moe_forward": ([ctypes.POINTER(MoeLayerC), _P, i32, _P, _P, _P, _P, _P, _P, sz,
-                                  _P], ctypes.c_int),
-            "coli_moe_forward_profiled": ([ctypes.POINTER(MoeLayerC), _P, i32, _P, _P, _P, _P, _P,
-                                           _P, sz, _P, ctypes.POINTER(_P), i32], ctypes.c_int),
-            "coli_debug_qgemv_blocks": ([i32, _P, i32, i32, _P, i32, _P, _P], ctypes.c_int),
-            "coli_moe_workspace_status": ([_P, _P, i32, _P], ctypes.c_int),
-            "coli_moe_forward_noalloc": ([ctypes.POINTER(MoeLayerC), _P, i32, _P, _P, _P, _P, _P,
-                                          _P, _P], ctypes.c_int),
-        }
-        for name, (args, res) in sig.items():
-            fn = getattr(L, name)
-            fn.argtypes = args
-            fn.restype = res
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def trace_lib() -> ctypes.CDLL:
+    """Load the timeline build of the library."""
+    global _trace_lib
+    if _trace_lib is None:
+        _trace_lib = _load(TRACE_LIB_PATH)
+    return _trace_lib
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
+                           "(python -m quantized_moe_coli_amd.build)")
+    L = ctypes.CDLL(path)
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "coli_abi_version": ([], ctypes.c_int),
+        "coli_status_str": ([ctypes.c_int], ctypes.c_char_p),
+        "coli_quant_pack": ([i32, _P, i64, i64, _P, _P, _P], ctypes.c_int),
+        "coli_quant_pack_fp8": ([i32, _P, _P, i64, i64, _P, _P, _P], ctypes.c_int),
+        "coli_gemv_f32act": ([i32, _P, _P, i64, i64, _P, _P, _P], ctypes.c_int),
+        "coli_quant_act_q8_0": ([_P, i32, i32, _P, _P, _P], ctypes.c_int),
+        "coli_moe_logits": ([_P, _P, i32, i32, i32, _P, _P], ctypes.c_int),
+        "coli_moe_route": ([ctypes.POINTER(RouterCfg), _P, _P, i32, _P, _P, _P], ctypes.c_int),
+        "coli_moe_dispatch": ([_P, i32, i32, i32, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+        "coli_moe_workspace_bytes": ([ctypes.POINTER(MoeLayerC), i32], sz),
+        "coli_moe_forward": ([ctypes.POINTER(MoeLayerC), _P, i32, _P, _P, _P, _P, _P, _P, sz,
+                              _P], ctypes.c_int),
+        "coli_moe_forward_profiled": ([ctypes.POINTER(MoeLayerC), _P, i32, _P, _P, _P, _P, _P,
+                                       _P, sz, _P, ctypes.POINTER(_P), i32], ctypes.c_int),
+        "coli_debug_qgemv_blocks": ([i32, _P, i32, i32, _P, i32, _P, _P], ctypes.c_int),
+        "coli_moe_workspace_status": ([_P, _P, i32, _P], ctypes.c_int),
+        "coli_debug_decode_trace": ([ctypes.POINTER(MoeLayerC), _P, _P, _P, sz, _P, i32,
+                                     ctypes.POINTER(i32), _P], ctypes.c_int),
+        "coli_debug_stream_read": ([_P, sz, _P, ctypes.POINTER(i32), _P], ctypes.c_int),
+        "coli_moe_forward_noalloc": ([ctypes.POINTER(MoeLayerC), _P, i32, _P, _P, _P, _P, _P,
+                                      _P, _P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
 
 
 def declared_symbols() -> list[str]:
@@ -355,6 +375,33 @@ def coli_moe_workspace_status(ws: torch.Tensor, status_out: torch.Tensor, clear:
     _check("coli_moe_workspace_status", lib().coli_moe_workspace_status(
         ctypes.c_void_p(ws.data_ptr()), _ptr(status_out, torch.int32, "status_out"),
         1 if clear else 0, _stream(stream)))
+
+
+TRACE_RECORDS = 64  # COLI_TRACE_RECORDS in include/coli_moe.h
+
+
+def coli_debug_decode_trace(layer: MoeLayer, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor,
+                            trace: torch.Tensor, stream=None, c_layer: MoeLayerC | None = None) -> int:
+    """One-token decode recording its timeline into ``trace`` (int64
+    [wgs, TRACE_RECORDS, 2], zeroed by the caller); returns the grid size."""
+    c = c_layer if c_layer is not None else layer.c_struct()
+    if trace.dim() != 3 or trace.shape[1:] != (TRACE_RECORDS, 2):
+        raise ValueError("trace must be [wgs, TRACE_RECORDS, 2]")
+    grid = ctypes.c_int32(0)
+    _check("coli_debug_decode_trace", trace_lib().coli_debug_decode_trace(
+        ctypes.byref(c), _ptr(x, torch.float32, "x"), _ptr(y, torch.float32, "y"),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _ptr(trace, torch.int64, "trace"),
+        trace.shape[0], ctypes.byref(grid), _stream(stream)))
+    return grid.value
+
+
+def coli_debug_stream_read(buf: torch.Tensor, out: torch.Tensor, stream=None) -> int:
+    """Streaming read of every byte of ``buf``; returns the grid size."""
+    grid = ctypes.c_int32(0)
+    _check("coli_debug_stream_read", lib().coli_debug_stream_read(
+        ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+        _ptr(out, torch.int32, "out"), ctypes.byref(grid), _stream(stream)))
+    return grid.value
 
 
 def coli_debug_qgemv_blocks(qtype: int, Wq: torch.Tensor, cols: int, xq: torch.Tensor,

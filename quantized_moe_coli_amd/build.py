@@ -35,9 +35,9 @@ def _headers():
     return sorted(glob.glob(os.path.join(CSRC, "*.hpp")) + glob.glob(os.path.join(INCLUDE, "*.h")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, extra=(), suffix=".o") -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + suffix)
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -54,19 +54,36 @@ def stale() -> bool:
     return any(os.path.getmtime(p) > t for p in sources() + _headers())
 
 
-def build(jobs: int | None = None) -> str:
-    """Compile and link the library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(8, len(srcs))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+# The timeline build: the same library with the decode kernel's timeline
+# records compiled in (only these sources differ).
+TRACE_LIB_PATH = os.path.join(PKG, "libcoli_moe_trace.so")
+TRACE_SOURCES = ("decode.hip", "api.hip")
+TRACE_FLAGS = ["-DCOLI_DECODE_TRACE"]
+
+
+def _link(objs, path):
+    tmp = path + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(jobs: int | None = None) -> str:
+    """Compile and link the library and its timeline build; returns the
+    library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    traced = [s for s in srcs if os.path.basename(s) in TRACE_SOURCES]
+    jobs = jobs or min(8, len(srcs) + len(traced))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        futs = [ex.submit(_compile, s) for s in srcs]
+        tfuts = {os.path.basename(s): ex.submit(_compile, s, TRACE_FLAGS, ".trace.o") for s in traced}
+        objs = [f.result() for f in futs]
+        tobj = {k: f.result() for k, f in tfuts.items()}
+    _link(objs, LIB_PATH)
+    _link([tobj.get(os.path.basename(s), o) for s, o in zip(srcs, objs)], TRACE_LIB_PATH)
     return LIB_PATH
 
 

@@ -38,4 +38,48 @@ __device__ __forceinline__ void act_quant_block(const float *__restrict__ xb, in
   out[1] = make_uint4(words[4], words[5], words[6], words[7]);
 }
 
+// The same quantisation of a whole row of n values (n % 32 == 0, at most
+// 8192) by the first NT threads of a workgroup, eight lanes per block of 32
+// (four values each, one 16-byte load), writing the codes in the container
+// ordering and one scale per block.  load() issues every load of the thread; quantize() then uses
+// them, so other loads can be issued in between.  The block's amax is a max
+// over its lanes (exact in any order), so codes and scales equal
+// act_quant_block's.
+template <int BITS, int NT>
+struct ActRow {
+  static constexpr int kPasses = 2048 / NT;  // blocks per group of eight threads, at most
+  float4 v[kPasses];
+
+  __device__ __forceinline__ void load(const float *__restrict__ x, int n) {
+    const int tid = threadIdx.x, part = tid & 7, nb = n / 32;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int blk = p * (NT / 8) + tid / 8;
+      v[p] = blk < nb ? reinterpret_cast<const float4 *>(x + (size_t)blk * 32)[part]
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __device__ __forceinline__ void quantize(int n, int8_t *__restrict__ q, float *__restrict__ d) {
+    const int tid = threadIdx.x, part = tid & 7, nb = n / 32;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int blk = p * (NT / 8) + tid / 8;
+      if (p * (NT / 8) >= nb) break;  // uniform
+      float m = fmaxf(fmaxf(fabsf(v[p].x), fabsf(v[p].y)), fmaxf(fabsf(v[p].z), fabsf(v[p].w)));
+      m = group_max<8>(m);  // every lane of the eight holds the block's amax
+      const float dd = m / 127.f;
+      if (blk < nb) {
+        if (part == 0) d[blk] = dd;
+        const float e[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float c = 0.f;
+          if (dd != 0.f) c = fminf(fmaxf(rintf(e[j] / dd), -127.f), 127.f);
+          q[(size_t)blk * 32 + perm_dst<BITS>(4 * part + j)] = (int8_t)c;
+        }
+      }
+    }
+  }
+};
+
 }  // namespace coli

@@ -79,7 +79,8 @@ coli::RouterCfg to_cfg(const coli_router_cfg &c) {
 }
 
 struct WsLayout {
-  size_t ctr, xq, xd, logits, idx, w, counts, offs, perm, uniq, nuniq, mgofs, hq, hd, obuf, total;
+  size_t ctr, xq, xd, logits, idx, w, counts, offs, perm, uniq, nuniq, mgofs, hq, hd, hsh, obuf,
+      total;
 };
 
 WsLayout ws_layout(const coli_moe_layer *L, int Tmax) {
@@ -106,6 +107,7 @@ WsLayout ws_layout(const coli_moe_layer *L, int Tmax) {
   w.mgofs = take((E + 2) * 4);
   w.hq = take((T * k + T) * I);
   w.hd = take((T * k + T) * (I / 32) * 4);
+  w.hsh = take(I * 4);  // decode: the shared expert's h in binary32
   w.obuf = take(Tmax >= 2 ? T * (k + 1) * H * 4 : 0);
   w.total = off;
   return w;
@@ -352,7 +354,8 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
       // decode: the whole layer in one kernel where that kernel is built for
       // the layer's row shapes
       e = coli::launch_decode_fused(fa, x, logits_in ? nullptr : L->gate_w, logits_in, logits_out,
-                                    reinterpret_cast<uint32_t *>(base + ws.ctr), s, kev(0));
+                                    reinterpret_cast<uint32_t *>(base + ws.ctr),
+                                    reinterpret_cast<float *>(base + ws.hsh), s, kev(0));
       if (e != hipErrorNotSupported) return from_hip(e);
     }
     // activations -> Q8_0 codes, and the router logits unless supplied
@@ -423,6 +426,68 @@ coli_status coli_moe_workspace_status(void *workspace, int32_t *status_out, int3
     if (st != COLI_OK) return st;
     return from_hip(coli::launch_workspace_status(static_cast<uint32_t *>(workspace), status_out,
                                                   clear ? 1 : 0, static_cast<hipStream_t>(stream)));
+  });
+}
+
+coli_status coli_debug_decode_trace(const coli_moe_layer *L, const float *x, float *y,
+                                    void *workspace, size_t workspace_bytes, uint64_t *trace,
+                                    int32_t trace_wgs, int32_t *grid_out, void *stream) {
+  return guarded([&] {
+    if (!layer_ok(L) || !L->gate_w || !x || !y || !trace || trace_wgs < 1 || !grid_out)
+      return COLI_ERR_INVALID_ARG;
+#ifndef COLI_DECODE_TRACE
+    // the ordinary build records nothing: libcoli_moe_trace.so does
+    return COLI_ERR_UNSUPPORTED;
+#endif
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(trace, 8)) return COLI_ERR_INVALID_ARG;
+    const WsLayout ws = ws_layout(L, 1);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < ws.total)
+      return COLI_ERR_WORKSPACE;
+    const coli_status st = check_device();
+    if (st != COLI_OK) return st;
+    char *base = static_cast<char *>(workspace);
+    coli::FfnArgs fa{};
+    fa.L = coli::LayerPtrs{L->hidden, L->inter, L->qtype, L->w_gate, L->w_up, L->w_down,
+                           L->s_gate, L->s_up, L->s_down, L->sh_gate, L->sh_up, L->sh_down,
+                           L->sh_s_gate, L->sh_s_up, L->sh_s_down};
+    fa.T = 1;
+    fa.k = L->router.top_k;
+    fa.E = L->router.n_experts;
+    fa.xq = reinterpret_cast<int8_t *>(base + ws.xq);
+    fa.xd = reinterpret_cast<float *>(base + ws.xd);
+    fa.idx = reinterpret_cast<int32_t *>(base + ws.idx);
+    fa.w = reinterpret_cast<float *>(base + ws.w);
+    fa.cfg = to_cfg(L->router);
+    fa.logits = reinterpret_cast<float *>(base + ws.logits);
+    fa.bias = L->gate_bias;
+    fa.loff = L->gate_offset;
+    fa.hq = reinterpret_cast<int8_t *>(base + ws.hq);
+    fa.hd = reinterpret_cast<float *>(base + ws.hd);
+    fa.y = y;
+    int grid = 0;
+    const hipError_t e = coli::launch_decode_fused(
+        fa, x, L->gate_w, nullptr, nullptr, reinterpret_cast<uint32_t *>(base + ws.ctr),
+        reinterpret_cast<float *>(base + ws.hsh), static_cast<hipStream_t>(stream), {}, trace,
+        trace_wgs, &grid);
+    if (e == hipErrorNotSupported) return COLI_ERR_UNSUPPORTED;
+    *grid_out = grid;
+    return from_hip(e);
+  });
+}
+
+coli_status coli_debug_stream_read(const void *buf, size_t bytes, uint32_t *out,
+                                   int32_t *grid_out, void *stream) {
+  return guarded([&] {
+    if (!buf || !out || !grid_out || bytes == 0 || bytes % 16 || !aligned(buf, 16) ||
+        !aligned(out, 4))
+      return COLI_ERR_INVALID_ARG;
+    const coli_status st = check_device();
+    if (st != COLI_OK) return st;
+    int grid = 0;
+    const hipError_t e = coli::launch_stream_read(buf, bytes, out, &grid,
+                                                  static_cast<hipStream_t>(stream));
+    *grid_out = grid;
+    return from_hip(e);
   });
 }
 

@@ -59,9 +59,12 @@ namespace coli {
 //   kernel) and the polling bound override (test hook: if nonzero at the
 //   start of a call, the bound on every wait's polling rounds; cleared by
 //   the call);
-//   then one 64-bit word per expert from the router: the complemented bits of
-//   the biased score c = sigma + bias (low half) and sigma (high half).  Zero
-//   means "not written yet", so consumers poll the scores themselves.
+//   one word per 32-row block of the shared expert: its rows done so far;
+//   then up to 1024 64-bit words of router logit partials: slice s = e * P + p
+//   holds the complemented bits of the binary64 sum of x . gate_w[e] over the
+//   p-th of P equal column ranges.  Zero means "not written yet" (no finite
+//   binary64 value has all bits set), so consumers poll the words
+//   themselves.
 constexpr int kCtrStride = 64;  // uint32 words
 constexpr int kQueues = 8;      // one work queue per XCD (workgroup b serves queue b % 8)
 enum : int {
@@ -70,18 +73,24 @@ enum : int {
   kCtrSlot0 = kCtrExit + kCtrStride,
   kCtrStatus = kCtrSlot0 + (kSelMaxK + 1) * kCtrStride,
   kCtrSpin = kCtrStatus + kCtrStride,
+  kCtrShBlk = kCtrSpin + kCtrStride,  // one word per 32-row block of the shared expert
   kScoreWords = 3072
 };
-static_assert(kCtrSpin + kCtrStride <= kScoreWords, "counters overlap scores");
-static_assert((kScoreWords + 2 * kSelMaxE) * 4 <= kDecodeCounterBytes,
+static_assert(kCtrShBlk + 8192 / 32 <= kScoreWords, "counters overlap scores");
+constexpr int kMaxSlices = 1024;  // logit partial words in the header
+static_assert((kScoreWords + 2 * kMaxSlices) * 4 <= kDecodeCounterBytes,
               "decode state exceeds the workspace header");
 static_assert(kCtrStatus * 4 == COLI_WORKSPACE_STATUS_OFFSET, "status word offset");
 static_assert(kCtrSpin * 4 == COLI_WORKSPACE_SPIN_LIMIT_OFFSET, "polling bound offset");
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr uint32_t kSpinLimit = 1u << 19;  // ~100 ms of polling
-constexpr int kLogRows = 4;                // logit rows per L item (two waves each)
+constexpr int kMaxPartsPerRow = 4;         // logit slices per gate row at most
 constexpr int kGuRows = 32;                // gate/up rows per GS/GR item
+#ifndef COLI_DECODE_GU_PIPE
+#define COLI_DECODE_GU_PIPE 1
+#endif
+constexpr int kGuPipe = COLI_DECODE_GU_PIPE;  // gate/up row passes in flight per wave
 // cache-policy bits of global_load_lds giving sc1, the policy of the relaxed
 // device-scope loads, so staged data is as coherent across XCDs as theirs
 constexpr int kLoadSc1 = 16;
@@ -93,11 +102,40 @@ struct DecodeArgs {
   const float *logits_in;  // [E] supplied logits, or null
   float *logits_out;       // [E] copy of the computed logits for the caller, or null
   uint32_t *ctr;         // workspace header
-  int n_log, n_gsh, n_gr, n_down, total;
+  int n_slice, n_part;   // logit slices (E * n_part, 0 with supplied logits) and parts per row
+  float *hsh;            // [I] the shared expert's h in binary32 (workspace)
+  int sh_rows;           // shared-expert gate/up rows of each workgroup
+  int n_gr, n_down, total;  // items: GR, then D; total
   int down_rows;         // output rows per D item
   int slot_group;        // slots staged in LDS at a time by a D item
-  int lds_main;          // byte offset of the per-role region in dynamic LDS
+  int lds_x;             // byte offset of x's Q8_0 codes and scales in dynamic LDS
+  int lds_l;             // byte offset of the token's logits kept for logits_out (-1: none)
+  uint64_t *trace;       // optional timeline records [grid][COLI_TRACE_RECORDS][2], else null
+  int trace_wgs;         // workgroups the trace buffer holds
+  int *grid_out;         // host: receives the grid size when not null
 };
+
+// Timeline records (only when d.trace is set, by thread 0 of each
+// workgroup): (code << 48 | value, s_memrealtime) at the boundaries of the
+// kernel's phases and items; `n` counts the workgroup's records.
+enum TraceCode : int {
+  kTrEntry = 1, kTrSlices = 2, kTrXq = 3, kTrShDone = 4, kTrSelBegin = 5, kTrPollDone = 6,
+  kTrSelEnd = 7, kTrGrEnd = 8, kTrDBegin = 9, kTrDReady = 10, kTrDEnd = 11, kTrExit = 12
+};
+// Compiled in only for the timeline build (COLI_DECODE_TRACE defined): in
+// the library's ordinary build the records cost nothing.
+__device__ __forceinline__ void trace_rec(const DecodeArgs &d, int &n, int code, int val) {
+#ifdef COLI_DECODE_TRACE
+  if (d.trace && threadIdx.x == 0 && n < COLI_TRACE_RECORDS && (int)blockIdx.x < d.trace_wgs) {
+    uint64_t *p = d.trace + ((size_t)blockIdx.x * COLI_TRACE_RECORDS + n) * 2;
+    p[0] = ((uint64_t)code << 48) | (uint32_t)val;
+    p[1] = __builtin_amdgcn_s_memrealtime();
+  }
+  ++n;
+#else
+  (void)d, (void)n, (void)code, (void)val;
+#endif
+}
 
 __device__ __forceinline__ uint32_t ld_ctr(const uint32_t *c) {
   return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -111,12 +149,17 @@ __device__ __forceinline__ void publish(uint32_t *c, uint32_t v) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Polling rounds of a wait: the header's override when it is nonzero (at
-// most the default), else `dflt`.
+// Polling rounds of a wait: the header's test-hook word, when nonzero, sets
+// them (bits 0-30, at most the default `dflt`); with bit 31 set every wait
+// of the call also treats its data as absent, so it runs the bound out and
+// gives up (a failure forced from the host).  The result's bit 31 carries
+// that flag.
 __device__ __forceinline__ uint32_t spin_bound(const DecodeArgs &d, uint32_t dflt) {
   const uint32_t v = ld_ctr(d.ctr + kCtrSpin);
-  return v ? min(v, dflt) : dflt;
+  if (v == 0u) return dflt;
+  return min(v & 0x7FFFFFFFu, dflt & 0x7FFFFFFFu) | (v & 0x80000000u);
 }
+constexpr uint32_t kSpinForced = 0x80000000u;
 
 // A bounded wait that ran out of polling rounds: record it (the call's
 // outputs are undefined).
@@ -124,96 +167,235 @@ __device__ __forceinline__ void gave_up(const DecodeArgs &d, uint32_t what) {
   __hip_atomic_fetch_or(d.ctr + kCtrStatus, what, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// L item: logits of experts e0 .. e0 + kLogRows - 1.  The kWpr waves of a
-// row each sum one 1/kWpr part of it in binary64; the parts are added in
-// order and the result rounded once to binary32.
-__device__ __forceinline__ void logits_rows(const DecodeArgs &d, int e0, double *part) {
-  constexpr int kWpr = kDecWaves / kLogRows;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = wave / kWpr, seg = wave % kWpr;
-  const int e = min(e0 + r, d.f.E - 1);  // a row past E recomputes the last row, unused
-  const int H = d.f.L.H;
-  const int q4 = H / (4 * kWpr);  // float4 per part (H % 32 == 0)
-  const float4 *wr = reinterpret_cast<const float4 *>(d.gate_w + (size_t)e * H) + seg * q4;
-  const float4 *xr = reinterpret_cast<const float4 *>(d.x) + seg * q4;
-  constexpr int kPer = 6;
-  double acc = 0.0;
-  for (int c0 = 0; c0 < q4; c0 += 64 * kPer) {
-    float4 wv[kPer], xv[kPer];
+// Logit slice s = e * P + p: the binary64 sum of x[c] * gate_w[e][c] over
+// the p-th of P equal column ranges, split over the waves (each lane's
+// products summed in binary64, then the wave's lanes, then the waves in
+// order), published as one 64-bit device-scope store.  issue() requests the
+// slice's gate and x values; finish() sums and publishes.
+struct SliceGate {
+  static constexpr int kMaxPer = 4;  // float4 per lane: H / (P * 4 * waves * 64) <= 4 for H <= 8192
+  float4 wv[kMaxPer], xv[kMaxPer];
+
+  __device__ __forceinline__ void range(const DecodeArgs &d, int s, int &c0, int &cn) const {
+    const int wave = threadIdx.x >> 6;
+    const int P = d.n_part, pp = s % P;
+    const int q4 = d.f.L.H / (4 * P);                  // float4 in the slice
+    const int qw = (q4 + kDecWaves - 1) / kDecWaves;   // float4 per wave
+    c0 = pp * q4 + wave * qw;
+    cn = min(qw, q4 - wave * qw);                      // this wave's float4 (may be <= 0)
+  }
+  __device__ __forceinline__ void issue(const DecodeArgs &d, int s) {
+    const int lane = threadIdx.x & 63;
+    int c0, cn;
+    range(d, s, c0, cn);
+    const float4 *wr = reinterpret_cast<const float4 *>(d.gate_w + (size_t)(s / d.n_part) * d.f.L.H);
+    const float4 *xr = reinterpret_cast<const float4 *>(d.x);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = min(c0 + lane + 64 * i, q4 - 1);
-      wv[i] = wr[c];
-      xv[i] = xr[c];
+    for (int i = 0; i < kMaxPer; ++i) {
+      if (lane + 64 * i < cn) {
+        wv[i] = wr[c0 + lane + 64 * i];
+        xv[i] = xr[c0 + lane + 64 * i];
+      }
     }
+  }
+  __device__ __forceinline__ void finish(const DecodeArgs &d, int s, double *part) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int c0, cn;
+    range(d, s, c0, cn);
+    double acc = 0.0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if (c0 + lane + 64 * i < q4) {
+    for (int i = 0; i < kMaxPer; ++i) {
+      if (lane + 64 * i < cn) {
         acc = fma((double)xv[i].x, (double)wv[i].x, acc);
         acc = fma((double)xv[i].y, (double)wv[i].y, acc);
         acc = fma((double)xv[i].z, (double)wv[i].z, acc);
         acc = fma((double)xv[i].w, (double)wv[i].w, acc);
       }
     }
-  }
-  const double s = wave_sum_f64(acc);
-  if (lane == 0) part[wave] = s;
-  __syncthreads();
-  if ((int)threadIdx.x < kLogRows && e0 + (int)threadIdx.x < d.f.E) {
-    const int e = e0 + threadIdx.x;
-    const double *p = part + kWpr * threadIdx.x;
-    double sum = p[0];
+    const double ws = wave_sum_f64(acc);
+    if (lane == 0) part[wave] = ws;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double sum = part[0];
 #pragma unroll
-    for (int i = 1; i < kWpr; ++i) sum += p[i];
-    float l = (float)sum;
-    if (d.f.loff) l += d.f.loff[e];
-    const float sg = sigmoid_f64(l);
-    const float c = sg + (d.f.bias ? d.f.bias[e] : 0.f);
-    const uint64_t w = ((uint64_t)__float_as_uint(sg) << 32) | (uint64_t)(~__float_as_uint(c));
-    __hip_atomic_store(reinterpret_cast<uint64_t *>(d.ctr + kScoreWords) + e, w, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    if (d.logits_out) d.logits_out[e] = l;
+      for (int w = 1; w < kDecWaves; ++w) sum += part[w];
+      __hip_atomic_store(reinterpret_cast<uint64_t *>(d.ctr + kScoreWords) + s,
+                         ~(uint64_t)__double_as_longlong(sum), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
   }
-}
+};
 
-// The token's experts and weights into LDS (sidx, sw), from the router's
-// scores: polled in the header until every expert's word has been written
-// (bounded: a lost word leaves garbage, never a hang), or computed here from
-// supplied logits.  `scratch` holds a SelInput followed by the selection's
-// own scratch.
-__device__ __forceinline__ void select_local(const DecodeArgs &d, unsigned char *scratch,
-                                             int32_t *sidx, float *sw) {
-  const RouterCfg &cfg = d.f.cfg;
-  SelInput &in = *reinterpret_cast<SelInput *>(scratch);
-  unsigned char *sel = scratch + sizeof(SelInput);
-  for (int e = threadIdx.x; e < cfg.E; e += kDecThreads) {
-    if (d.logits_in) {
-      const float sg = sigmoid_f64(d.logits_in[e]);
+// The token's router scores into LDS: the logits from the slices' partials
+// polled in the header until every one has been written (bounded: a lost
+// word leaves garbage, never a hang), added in column order in binary64 and
+// rounded once (plus the layer's offset, if any), or the supplied logits;
+// then sigma (binary64, rounded once) and c = sigma + bias.  issue()
+// requests every partial of the thread's expert once (threads that call
+// it); finish() requests the rest, polls what was absent, computes the
+// scores, and ends with a barrier.  `lsave` (or null) keeps the logits for
+// the caller.  Threads cover experts e, e + NT, ....
+struct ScorePoll {
+  uint64_t v[kMaxPartsPerRow];
+
+  bool have = false;  // the first round's words were requested by issue()
+
+  __device__ __forceinline__ void issue(const DecodeArgs &d) {
+    const int e = threadIdx.x, P = d.n_part;
+    if (d.logits_in || e >= d.f.cfg.E) return;
+    have = true;
+    const uint64_t *w = reinterpret_cast<const uint64_t *>(d.ctr + kScoreWords) + e * P;
+#pragma unroll
+    for (int p = 0; p < kMaxPartsPerRow; ++p)
+      if (p < P) v[p] = __hip_atomic_load(w + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ void finish(const DecodeArgs &d, SelInput &in, float *lsave) {
+    const RouterCfg &cfg = d.f.cfg;
+    const int P = d.n_part;
+    for (int e = threadIdx.x; e < cfg.E; e += kDecThreads) {
+      float l;
+      if (d.logits_in) {
+        l = d.logits_in[e];
+      } else {
+        const uint64_t *w = reinterpret_cast<const uint64_t *>(d.ctr + kScoreWords) + e * P;
+        if (e >= kDecThreads || !have) {  // words not requested by issue(): requested now
+#pragma unroll
+          for (int p = 0; p < kMaxPartsPerRow; ++p)
+            if (p < P) v[p] = __hip_atomic_load(w + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const uint32_t sb = spin_bound(d, kSpinLimit);
+        const uint32_t spin = sb & ~kSpinForced;
+        const bool forced = (sb & kSpinForced) != 0u;
+        double sum = 0.0;
+#pragma unroll
+        for (int p = 0; p < kMaxPartsPerRow; ++p) {
+          if (p < P) {
+            uint32_t it = 0;
+            while ((v[p] == 0ull || forced) && it < spin) {
+              __builtin_amdgcn_s_sleep(2);
+              v[p] = __hip_atomic_load(w + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              ++it;
+            }
+            if (v[p] == 0ull || forced) gave_up(d, COLI_WAIT_SCORES);
+            const double part = __longlong_as_double((long long)~v[p]);
+            sum = p == 0 ? part : sum + part;
+          }
+        }
+        l = (float)sum;
+        if (d.f.loff) l += d.f.loff[e];
+      }
+      if (lsave) lsave[e] = l;
+      const float sg = sigmoid_f64(l);
       in.sg[e] = sg;
       in.c[e] = sg + (d.f.bias ? d.f.bias[e] : 0.f);
-    } else {
-      const uint64_t *w = reinterpret_cast<const uint64_t *>(d.ctr + kScoreWords) + e;
-      uint64_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t spin = spin_bound(d, kSpinLimit);
-      uint32_t it = 0;
-      while ((uint32_t)v == 0u && it < spin) {
-        __builtin_amdgcn_s_sleep(2);
-        v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ++it;
-      }
-      if ((uint32_t)v == 0u) gave_up(d, COLI_WAIT_SCORES);
-      in.c[e] = __uint_as_float(~(uint32_t)v);
-      in.sg[e] = __uint_as_float((uint32_t)(v >> 32));
     }
+    __syncthreads();
   }
-  __syncthreads();
+};
+
+// The token's experts and weights into LDS (sidx, sw) from the scores in
+// `in`, by the whole workgroup (select_fast, else select_wg: the same total
+// order and binary32 operations as select_token); slots that are not valid
+// expert ids become -1.
+__device__ __forceinline__ void select_local(const DecodeArgs &d, const SelInput &in,
+                                             unsigned char *sel, int32_t *sidx, float *sw) {
+  const RouterCfg &cfg = d.f.cfg;
   if (select_fast_ok(cfg.E, cfg.n_group, cfg.topk_group, cfg.k, kDecThreads))
     select_fast<kDecThreads>(cfg, in, *reinterpret_cast<SelFastScratch *>(sel), sidx, sw);
   else
     select_wg<kDecThreads>(cfg, in, *reinterpret_cast<SelWgScratch *>(sel), sidx, sw);
   for (int j = threadIdx.x; j < d.f.k; j += kDecThreads)
-    if ((unsigned)sidx[j] >= (unsigned)d.f.E) sidx[j] = -1;  // never index outside the experts
+    if ((unsigned)sidx[j] >= (unsigned)cfg.E) sidx[j] = -1;  // never index outside the experts
   __syncthreads();
+}
+
+// The shared expert's gate/up rows [r0, r0 + nr) of this workgroup, in
+// passes of RPP rows per wave: g and u summed in binary64 and rounded once,
+// h = SwiGLU, stored in binary32 to hsh with device-scope stores.  Every
+// 32-row block then counts the rows it received; the workgroup whose rows
+// complete a block quantises it to Q8_0 (codes in the container ordering,
+// into the shared slot's h row; its scale) and bumps the shared slot's
+// counter.  The shared expert needs no routing, so this runs while the
+// router's scores are still on their way, spread over every workgroup.
+template <int BITS, int LPR, int CPL>
+__device__ __forceinline__ void shared_rows(const DecodeArgs &d, int r0, int nr, const int8_t *xq,
+                                            const float *xd, int *s_last) {
+  constexpr int RPP = 64 / LPR;
+  const FfnArgs &a = d.f;
+  const int H = a.L.H, I = a.L.I, k = a.k;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gl = lane % LPR, rsub = lane / LPR;
+  const int nchunks = H * BITS / 128;
+  const size_t row_bytes = (size_t)H * BITS / 8;
+  const ExpertPtrs ep = expert_ptrs(a.L, -1);
+  Act<BITS> act[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = gl + LPR * i;
+    if (c < nchunks) load_act<BITS>(act[i], xq, xd, c);
+    else zero_act<BITS>(act[i]);
+  }
+  for (int rp = wave * RPP; rp < nr; rp += kDecWaves * RPP) {
+    const int row = min(r0 + rp + rsub, I - 1);  // a row past the range recomputes the last, unused
+    const uint4 *gp = reinterpret_cast<const uint4 *>(ep.wg + (size_t)row * row_bytes);
+    const uint4 *up = reinterpret_cast<const uint4 *>(ep.wu + (size_t)row * row_bytes);
+    uint4 wg[CPL], wu[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = min(gl + LPR * i, nchunks - 1);
+      wg[i] = ld_nt(gp + c);
+      wu[i] = ld_nt(up + c);
+    }
+    double pg = 0.0, pu = 0.0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      pg += chunk_part_f64<BITS>(wg[i], act[i]);
+      pu += chunk_part_f64<BITS>(wu[i], act[i]);
+    }
+    pg = group_sum_f64<LPR>(pg);
+    pu = group_sum_f64<LPR>(pu);
+    if (lane == group_sum_lane<LPR>(lane) && rp + rsub < nr) {
+      const float h = swiglu_h(row_out(pg, ep.sg[row]), row_out(pu, ep.su[row]));
+      st_dev(reinterpret_cast<uint32_t *>(d.hsh) + row, __float_as_uint(h));
+    }
+  }
+  // the rows' stores complete before any block counts them
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int b_lo = r0 / 32, b_hi = (r0 + nr - 1) / 32;
+  for (int b = b_lo; b <= b_hi; ++b) {
+    if (threadIdx.x == 0) {
+      const int n_in = min(r0 + nr, 32 * b + 32) - max(r0, 32 * b);
+      const uint32_t old = __hip_atomic_fetch_add(d.ctr + kCtrShBlk + b, (uint32_t)n_in,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_last = (int)(old + (uint32_t)n_in) == 32;
+    }
+    __syncthreads();
+    if (*s_last) {
+      // this workgroup completed block b: Q8_0 of its 32 values of h
+      if (threadIdx.x < 32) {
+        const int i = threadIdx.x;
+        const float h = __uint_as_float(ld_dev(reinterpret_cast<const uint32_t *>(d.hsh) + 32 * b + i));
+        const float amax = __shfl(group_max<32>(fabsf(h)), 31, 64);
+        const float db = amax / 127.f;
+        float c = 0.f;
+        if (db != 0.f) c = fminf(fmaxf(rintf(h / db), -127.f), 127.f);
+        // lane j < 8 gathers bytes 4j .. 4j+3 of the block in the container
+        // ordering (byte s holds element perm_src(s))
+        const int code = (int)c & 0xFF;
+        uint32_t word = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          word |= ((uint32_t)__shfl(code, perm_src<BITS>((4 * i + m) & 31), 64) & 0xFFu) << (8 * m);
+        if (i < 8) st_dev(reinterpret_cast<uint32_t *>(a.hq + (size_t)k * I + 32 * b) + i, word);
+        if (i == 0)
+          st_dev(reinterpret_cast<uint32_t *>(a.hd) + (size_t)k * (I / 32) + b, __float_as_uint(db));
+      }
+      publish(d.ctr + kCtrSlot0 + k * kCtrStride, 1u);
+    }
+    __syncthreads();
+  }
 }
 
 // D item: output rows [r0, r0 + down_rows).  Wave w owns rows
@@ -224,7 +406,7 @@ __device__ __forceinline__ void select_local(const DecodeArgs &d, unsigned char 
 // is reproducible.
 template <int BITS, int LPR, int CPL, int NPASS, int SG>
 __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *lds_q, float *lds_d,
-                                          const int32_t *sidx, const float *sw) {
+                                          const int32_t *sidx, const float *sw, int &trn) {
   constexpr int RPP = 64 / LPR;
   const FfnArgs &a = d.f;
   const int I = a.L.I, k = a.k;
@@ -265,15 +447,19 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
       const int q = threadIdx.x;
       const int sl = g0 + q == 0 ? k : g0 + q - 1;
       const uint32_t *c = d.ctr + kCtrSlot0 + sl * kCtrStride;
-      const uint32_t spin = spin_bound(d, 8u * kSpinLimit);
+      const uint32_t target = (uint32_t)(I / kGuRows);
+      const uint32_t sb = spin_bound(d, 8u * kSpinLimit);
+      const uint32_t spin = sb & ~kSpinForced;
+      const bool forced = (sb & kSpinForced) != 0u;
       uint32_t it = 0, v;
-      while ((v = ld_ctr(c)) < (uint32_t)(I / kGuRows) && it < spin) {
+      while (((v = ld_ctr(c)) < target || forced) && it < spin) {
         __builtin_amdgcn_s_sleep(8);
         ++it;
       }
-      if (v < (uint32_t)(I / kGuRows)) gave_up(d, COLI_WAIT_SLOTS);
+      if (v < target || forced) gave_up(d, COLI_WAIT_SLOTS);
     }
     __syncthreads();
+    if (g0 == 0) trace_rec(d, trn, kTrDReady, r0);
     if (I % 128 == 0) {
       // straight into LDS: 16-byte loads with the cache policy of the
       // device-scope loads (sc1), all in flight at once and no registers.
@@ -364,11 +550,12 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
   }
 }
 
-// Persistent: the grid is at most the workgroups the GPU holds at once;
-// each workgroup takes tickets until none are left.  x's Q8_0 codes and the
-// selection are computed once per workgroup and reused by its later items
-// (tickets only increase, so a workgroup never returns to gate/up work
-// after a D item, whose staging overwrites x's codes).
+// Persistent: the grid is at most the workgroups the GPU holds at once.
+// Every workgroup first computes its logit slices, quantises x into its LDS
+// and computes its share of the shared expert's gate/up rows (none of which
+// needs the routing), then selects the token's experts itself and takes
+// tickets: GR items (with a full grid, exactly one per workgroup), then D
+// items.  A D item stages h in the region the selection scratch used.
 template <int BITS, int GLPR, int GCPL, int DLPR, int DCPL>
 __global__ __launch_bounds__(kDecThreads)
 __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(DecodeArgs d) {
@@ -380,19 +567,17 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
   __shared__ float hs[1][kGuRows];
   __shared__ double lpart[kDecWaves];
   __shared__ int s_ticket;
-  // dynamic LDS: [selection scratch | x's Q8_0 codes and scales]; a D item's
-  // staged h overlays both once the selection is done
+  // dynamic LDS: [selection scratch, later a D item's staged h | x's Q8_0
+  // codes and scales | the logits kept for the caller]
   extern __shared__ __align__(16) unsigned char dyn[];
-  unsigned char *lds_x = dyn + d.lds_main;
   const FfnArgs &a = d.f;
   const int k = a.k, I = a.L.I, H = a.L.H;
   const int n_rb = I / kGuRows;
-  const int b_gsh = d.n_log, b_gr = b_gsh + d.n_gsh, b_down = b_gr + d.n_gr;
-  int8_t *xq_lds = reinterpret_cast<int8_t *>(lds_x);
-  float *xd_lds = reinterpret_cast<float *>(lds_x + H);
+  const int b_d = d.n_gr;
+  int8_t *xq_lds = reinterpret_cast<int8_t *>(dyn + d.lds_x);
+  float *xd_lds = reinterpret_cast<float *>(dyn + d.lds_x + H);
+  float *lsave = d.lds_l >= 0 ? reinterpret_cast<float *>(dyn + d.lds_l) : nullptr;
 
-  // Tickets only increase, so the items of each kind form one loop of their
-  // own (this keeps each kind's registers apart).
   // Work queue q = b % 8 holds items q, q + 8, ...; consecutive workgroups
   // go to consecutive XCDs, so each XCD streams an equal share of every
   // kind of item.  Within a queue the items keep their global order.
@@ -410,51 +595,77 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
     __syncthreads();
     return t;
   };
-  int t = (int)blockIdx.x;
 
-  // L: four logit rows per item
-  for (; t < b_gsh; t = next_ticket()) {
-    logits_rows(d, t * kLogRows, lpart);
-    __syncthreads();
+  int trn = 0;
+  trace_rec(d, trn, kTrEntry, 0);
+  // router logits first: this workgroup's slices
+  {
+    SliceGate sg;
+    for (int sl = (int)blockIdx.x; sl < d.n_slice; sl += gridDim.x) {
+      sg.issue(d, sl);
+      sg.finish(d, sl, lpart);
+    }
   }
-  if (t < b_down) {
-    // gate/up items: x's Q8_0 codes, once
-    for (int i = threadIdx.x; i < H / 32; i += kDecThreads)
-      act_quant_block<BITS>(d.x + i * 32, xq_lds + i * 32, xd_lds + i);
-    __syncthreads();
+  trace_rec(d, trn, kTrSlices, 0);
+  // then x's Q8_0 codes into LDS, this workgroup's rows of the shared expert
+  // (which needs no routing), the router's scores and the token's experts,
+  // by the whole workgroup
+  SelInput &in = *reinterpret_cast<SelInput *>(dyn);
+  {
+    ActRow<BITS, kDecThreads> xr;
+    xr.load(d.x, H);
+    xr.quantize(H, xq_lds, xd_lds);
   }
-  // GS: shared expert, rows [kGuRows (t - b_gsh), +kGuRows)
-  for (; t < b_gr; t = next_ticket()) {
-    TokList s{1, -1, k, true};
-    gateup_body<BITS, GLPR, GCPL, 1, kDecWaves, true, BLK>(a, false, expert_ptrs(a.L, -1), s,
-                                                          BLK * (t - b_gsh), hs, xq_lds, xd_lds);
-    publish(d.ctr + kCtrSlot0 + k * kCtrStride, 1u);
+  __syncthreads();
+  trace_rec(d, trn, kTrXq, 0);
+  {
+    const int r0 = (int)blockIdx.x * d.sh_rows;
+    const int nr = min(d.sh_rows, I - r0);
+    if (nr > 0) shared_rows<BITS, GLPR, GCPL>(d, r0, nr, xq_lds, xd_lds, &s_ticket);
   }
-  // routed gate/up and down items: the token's experts, once
-  if (t < d.total) select_local(d, dyn, sidx, sw);
+  trace_rec(d, trn, kTrShDone, 0);
+  trace_rec(d, trn, kTrSelBegin, 0);
+  {
+    ScorePoll sp;
+    sp.issue(d);
+    sp.finish(d, in, lsave);
+  }
+  trace_rec(d, trn, kTrPollDone, 0);
+  select_local(d, in, dyn + sizeof(SelInput), sidx, sw);
+  trace_rec(d, trn, kTrSelEnd, 0);
+
+  int t = (int)blockIdx.x;
   // GR: routed slot u, rows [kGuRows rb, +kGuRows)
-  for (; t < b_down; t = next_ticket()) {
-    const int u = (t - b_gr) / n_rb, rb = (t - b_gr) % n_rb;
+  for (; t < b_d; t = next_ticket()) {
+    const int u = t / n_rb, rb = t % n_rb;
     if (u == 0 && rb == 0) {
       for (int j = threadIdx.x; j < k; j += kDecThreads) {
         if (a.idx_user) a.idx_user[j] = sidx[j];
         if (a.w_user) a.w_user[j] = sw[j];
       }
+      if (lsave && d.logits_out)
+        for (int e = threadIdx.x; e < a.E; e += kDecThreads) d.logits_out[e] = lsave[e];
     }
     const int e = uniform_i32(sidx[u]);
     if (e >= 0) {
       TokList s{1, -1, u, false};
-      gateup_body<BITS, GLPR, GCPL, 1, kDecWaves, true, BLK>(a, false, expert_ptrs(a.L, e), s,
-                                                            BLK * rb, hs, xq_lds, xd_lds);
+      gateup_body<BITS, GLPR, GCPL, 1, kDecWaves, true, BLK, kGuPipe>(a, false, expert_ptrs(a.L, e), s,
+                                                                     BLK * rb, hs, xq_lds, xd_lds);
     }
     publish(d.ctr + kCtrSlot0 + u * kCtrStride, 1u);
+    trace_rec(d, trn, kTrGrEnd, t);
   }
-  // D: output rows; the staged h overwrites x's codes
+  // D: output rows of D item t - b_d; the staged h overlays the selection
+  // scratch, which is no longer needed by then
+  int8_t *lds_q = reinterpret_cast<int8_t *>(dyn);
+  float *lds_d = reinterpret_cast<float *>(dyn + (size_t)d.slot_group * I);
   for (; t < d.total; t = next_ticket()) {
-    int8_t *lds_q = reinterpret_cast<int8_t *>(dyn);
-    float *lds_d = reinterpret_cast<float *>(dyn + (size_t)d.slot_group * I);
-    down_rows<BITS, DLPR, DCPL, DNPASS, DSG>(d, (t - b_down) * d.down_rows, lds_q, lds_d, sidx, sw);
+    trace_rec(d, trn, kTrDBegin, t);
+    down_rows<BITS, DLPR, DCPL, DNPASS, DSG>(d, (t - b_d) * d.down_rows, lds_q, lds_d, sidx, sw,
+                                            trn);
+    trace_rec(d, trn, kTrDEnd, t);
   }
+  trace_rec(d, trn, kTrExit, 0);
 
   // the last workgroup out clears the header for the next call
   __syncthreads();
@@ -468,10 +679,11 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
       __hip_atomic_store(d.ctr + i * kCtrStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x == 0)
       __hip_atomic_store(d.ctr + kCtrSpin, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d.n_log > 0)
-      for (int e = threadIdx.x; e < a.E; e += kDecThreads)
-        __hip_atomic_store(reinterpret_cast<uint64_t *>(d.ctr + kScoreWords) + e, (uint64_t)0,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int sl = threadIdx.x; sl < d.n_slice; sl += kDecThreads)
+      __hip_atomic_store(reinterpret_cast<uint64_t *>(d.ctr + kScoreWords) + sl, (uint64_t)0,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int b = threadIdx.x; b < I / 32; b += kDecThreads)
+      __hip_atomic_store(d.ctr + kCtrShBlk + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -486,21 +698,23 @@ template <int BITS, int GLPR, int GCPL, int DLPR, int DCPL>
 static hipError_t launch_fused_t(DecodeArgs d, hipStream_t st, KEvents ev) {
   constexpr int DNPASS = DCPL == 1 ? 2 : 1;
   constexpr int DSG = DCPL == 1 ? 9 : 3;
-  const int I = d.f.L.I;
+  const int I = d.f.L.I, H = d.f.L.H, E = d.f.E;
   d.down_rows = kDecWaves * DNPASS * (64 / DLPR);
-  if (d.f.L.H % d.down_rows) return hipErrorNotSupported;
-  d.n_down = d.f.L.H / d.down_rows;
-  // dynamic LDS: the selection scratch, then the larger of x's Q8_0 codes
-  // and scales and the D items' staged h (I code bytes + I/32 scales a slot)
+  if (H % d.down_rows) return hipErrorNotSupported;
+  d.n_down = H / d.down_rows;
+  // dynamic LDS: [max(selection scratch, staged h: I code bytes + I/32
+  // scales a slot) | x's codes and scales | the logits kept for the caller]
   const int per_slot = I + (I / 32) * 4;
   d.slot_group = DSG;
   while (d.slot_group > 1 && d.slot_group * per_slot > 24 * 1024) --d.slot_group;
-  d.total = d.n_log + d.n_gsh + d.n_gr + d.n_down;
-  d.lds_main =
-      (int)((sizeof(SelInput) + std::max(sizeof(SelWgScratch), sizeof(SelFastScratch)) + 15) / 16 * 16);
-  const size_t shmem = std::max((size_t)d.slot_group * per_slot,
-                                (size_t)d.lds_main + (size_t)d.f.L.H + (size_t)(d.f.L.H / 32) * 4);
-  // as many workgroups as the GPU holds at once (never more than the items)
+  const size_t sel =
+      (sizeof(SelInput) + std::max(sizeof(SelWgScratch), sizeof(SelFastScratch)) + 15) / 16 * 16;
+  const size_t reg_a = (std::max(sel, (size_t)d.slot_group * per_slot) + 15) / 16 * 16;
+  d.lds_x = (int)reg_a;
+  const size_t reg_x = ((size_t)H + (size_t)(H / 32) * 4 + 15) / 16 * 16;
+  d.lds_l = d.logits_out ? (int)(reg_a + reg_x) : -1;
+  const size_t shmem = reg_a + reg_x + (d.logits_out ? (size_t)E * 4 : 0);
+  // as many workgroups as the GPU holds at once
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &per_cu, reinterpret_cast<const void *>(&k_decode_fused<BITS, GLPR, GCPL, DLPR, DCPL>),
@@ -512,8 +726,26 @@ static hipError_t launch_fused_t(DecodeArgs d, hipStream_t st, KEvents ev) {
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       n_cu <= 0)
     n_cu = 256;
+  const int cap = std::max(per_cu * n_cu, kQueues);
+  d.total = d.n_gr + d.n_down;
   // every queue that holds an item has a workgroup (grid >= min(total, 8))
-  const int grid = std::min(d.total, std::max(per_cu * n_cu, kQueues));
+  const int grid = std::min(d.total, cap);
+  // the shared expert's gate/up rows, spread evenly over the grid
+  d.sh_rows = (I + grid - 1) / grid;
+  // logit slices: P parts per gate row, as many as fit the grid and the
+  // header's partial words (the columns of a part a whole number of float4)
+  if (d.gate_w) {
+    int P = 1;
+    while (P * 2 <= kMaxPartsPerRow && E * P * 2 <= std::min(grid, kMaxSlices) && (H / (P * 2)) % 4 == 0)
+      P *= 2;
+    if (E * P > kMaxSlices) return hipErrorNotSupported;
+    d.n_part = P;
+    d.n_slice = E * P;
+  } else {
+    d.n_part = 1;
+    d.n_slice = 0;
+  }
+  if (d.grid_out) *d.grid_out = grid;
   COLI_LAUNCH(ev, (k_decode_fused<BITS, GLPR, GCPL, DLPR, DCPL>), dim3(grid), dim3(kDecThreads),
               shmem, st, d);
   return hipGetLastError();
@@ -554,16 +786,19 @@ hipError_t launch_workspace_status(uint32_t *ctr, int32_t *out, int clear, hipSt
 
 hipError_t launch_decode_fused(const FfnArgs &f, const float *x, const float *gate_w,
                                const float *logits_in, float *logits_out, uint32_t *ctr,
-                               hipStream_t st, KEvents ev) {
+                               float *hsh, hipStream_t st, KEvents ev, uint64_t *trace,
+                               int trace_wgs, int *grid_out) {
   DecodeArgs d{};
+  d.trace = trace;
+  d.trace_wgs = trace_wgs;
+  d.grid_out = grid_out;
   d.f = f;
   d.x = x;
   d.gate_w = gate_w;
   d.logits_in = gate_w ? nullptr : logits_in;
   d.logits_out = gate_w ? logits_out : nullptr;
   d.ctr = ctr;
-  d.n_log = gate_w ? (f.E + kLogRows - 1) / kLogRows : 0;
-  d.n_gsh = f.L.I / kGuRows;
+  d.hsh = hsh;
   d.n_gr = f.k * (f.L.I / kGuRows);
   if (f.L.I % kGuRows) return hipErrorNotSupported;
   switch (f.L.bits) {

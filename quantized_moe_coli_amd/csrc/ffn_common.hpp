@@ -180,12 +180,19 @@ __device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
 // xq_all/xd_all: the tokens' Q8_0 codes [T][H] and scales [T][H/32] (global
 // memory or LDS).  COHERENT_OUT: h codes and scales are written with
 // device-scope stores (read by other workgroups of the same kernel).
+// PIPE = 2: the loads of the next row pass are issued before the current
+// pass's products (two passes of weights in registers); PIPE = 1: after them,
+// reusing their registers (the reduction of the current pass overlaps the
+// loads), for kernels held to few registers.  hs receives g, and u goes to
+// LDS of its own; SwiGLU is evaluated in the Q8_0 step, one lane per row.
 template <int BITS, int LPR, int CPL, int NT, int WAVES = 4, bool COHERENT_OUT = false,
-          int BLK = 1>
+          int BLK = 1, int PIPE = 2>
 __device__ __forceinline__ void gateup_body(const FfnArgs &a, bool union_mode, const ExpertPtrs &ep,
                                             const TokList &s, int rb, float (*hs)[32 * BLK],
                                             const int8_t *xq_all, const float *xd_all) {
+  static_assert(PIPE == 1 || PIPE == 2, "row passes in flight");
   __shared__ __align__(16) int8_t hcode[NT][32 * BLK];
+  __shared__ float hu[NT][32 * BLK];
   constexpr int RPP = 64 / LPR;  // rows per pass of a wave
   constexpr int ROWS_PER_WAVE = 32 * BLK / WAVES;
   constexpr int PASSES = ROWS_PER_WAVE / RPP;
@@ -216,7 +223,7 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, bool union_mode, c
         else zero_act<BITS>(act[i][tt]);
       }
     }
-    uint4 wg[2][CPL], wu[2][CPL];
+    uint4 wg[PIPE][CPL], wu[PIPE][CPL];
     // chunks past the row end reload the last chunk; their activations are
     // zero, so they add exactly 0 -- no branch around the loads
     auto load_rows = [&](int p, int buf) {
@@ -233,8 +240,8 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, bool union_mode, c
     load_rows(0, 0);
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      if (p + 1 < PASSES) load_rows(p + 1, (p + 1) & 1);
-      const int buf = p & 1;
+      if (PIPE == 2 && p + 1 < PASSES) load_rows(p + 1, (p + 1) & 1);
+      const int buf = PIPE == 2 ? (p & 1) : 0;
       const int rl = wave * ROWS_PER_WAVE + p * RPP + rsub;  // row within the item
       // g and u of the row: block partials in binary64, summed across the
       // row's lanes in binary64, times the row scale, rounded once
@@ -248,20 +255,28 @@ __device__ __forceinline__ void gateup_body(const FfnArgs &a, bool union_mode, c
           pg[tt] += chunk_part_f64<BITS>(wg[buf][i], act[i][tt]);
           pu[tt] += chunk_part_f64<BITS>(wu[buf][i], act[i][tt]);
         }
+      }
+      if (PIPE == 1 && p + 1 < PASSES) load_rows(p + 1, 0);
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
         pg[tt] = group_sum_f64<LPR>(pg[tt]);
         pu[tt] = group_sum_f64<LPR>(pu[tt]);
       }
       const float sg = row_scale<RPP>(sgv, p, rsub), su = row_scale<RPP>(suv, p, rsub);
       if (lane == group_sum_lane<LPR>(lane)) {
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) hs[tt][rl] = swiglu_h(row_out(pg[tt], sg), row_out(pu[tt], su));
+        for (int tt = 0; tt < NT; ++tt) {
+          hs[tt][rl] = row_out(pg[tt], sg);
+          hu[tt][rl] = row_out(pu[tt], su);
+        }
       }
     }
     __syncthreads();
-    // Q8_0 of each token's h blocks: thread -> (token tt, block b, element i)
+    // SwiGLU and Q8_0 of each token's h blocks: thread -> (token tt, block b,
+    // element i)
     const int tt = threadIdx.x / (32 * BLK), b = (threadIdx.x >> 5) % BLK, i = threadIdx.x & 31;
     if (tt < NT) {
-      const float h = hs[tt][b * 32 + i];
+      const float h = swiglu_h(hs[tt][b * 32 + i], hu[tt][b * 32 + i]);
       float amax = group_max<32>(fabsf(h));
       amax = __shfl(amax, (lane & 32) | 31, 64);
       if (t0 + tt < s.n_tok) {

@@ -136,9 +136,20 @@ hipError_t launch_down_mfma(const FfnArgs &a, hipStream_t st, KEvents ev = {});
 // gate_w null: logits_in holds the supplied logits; else the computed logits
 // are also written to logits_out when it is not null.  Returns
 // hipErrorNotSupported for row shapes the kernel is not built for.
+// trace: optional timeline records (coli_debug_decode_trace); grid_out
+// (host) receives the grid size.
+// hsh: [I] binary32 workspace for the shared expert's h.
 hipError_t launch_decode_fused(const FfnArgs &f, const float *x, const float *gate_w,
                                const float *logits_in, float *logits_out, uint32_t *ctr,
-                               hipStream_t st, KEvents ev = {});
+                               float *hsh, hipStream_t st, KEvents ev = {},
+                               uint64_t *trace = nullptr, int trace_wgs = 0,
+                               int *grid_out = nullptr);
+
+// Plain streaming read of `bytes` (a multiple of 16, 16-byte aligned) with
+// 16-byte non-temporal loads, one sum word per workgroup into out[grid]
+// (keeps the loads live); *grid_out receives the grid size.
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *out, int *grid_out,
+                              hipStream_t st, KEvents ev = {});
 
 // Copy the workspace header's sticky status word to out[0] (device), and
 // clear it when `clear` is nonzero.

@@ -85,6 +85,11 @@ struct SelScratch {  // LDS scratch of one wave
   float sum;
 };
 
+template <int EPL = kSelEPL>
+__device__ __forceinline__ void select_core(const RouterCfg &cfg, const float *c,
+                                            const float *__restrict__ sig, SelScratch &sc,
+                                            int32_t *idx_out, float *w_out);
+
 // Selects a token's experts.  Lane j < k writes slot j of `idx_out`/`w_out`
 // (any address space).
 __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *__restrict__ lrow,
@@ -114,17 +119,32 @@ __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *
     }
   }
 
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  select_core(cfg, c, sc.sig, sc, idx_out, w_out);
+}
+
+// The selection itself from the biased scores c[m] of experts lane + 64 m
+// (every lane, c[m] = 0 past E; EPL >= E / 64 of them) and the sigmoid
+// scores sig[e] (any address space, visible to the whole wave): groups,
+// experts in rank order, weights and expert top-p, by one wave.
+template <int EPL>
+__device__ __forceinline__ void select_core(const RouterCfg &cfg, const float *c,
+                                            const float *__restrict__ sig, SelScratch &sc,
+                                            int32_t *idx_out, float *w_out) {
+  const int lane = threadIdx.x & 63;
+  const int E = cfg.E, k = cfg.k, G = cfg.n_group, per = E / G;
   // groups
   uint32_t allowed = 0;  // bit m: candidate lane + 64 m is in a kept group
   if (cfg.topk_group >= G) {
 #pragma unroll
-    for (int m = 0; m < kSelEPL; ++m)
+    for (int m = 0; m < EPL; ++m)
       if (lane + 64 * m < E) allowed |= 1u << m;
   } else {
     const bool aligned = per <= 64 && (64 % per) == 0;
     if (aligned) {
 #pragma unroll
-      for (int m = 0; m < kSelEPL; ++m) {
+      for (int m = 0; m < EPL; ++m) {
         if (64 * m >= E) break;
         float gsum;
         switch (per) {
@@ -144,7 +164,7 @@ __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *
       // the same two values, so the score is identical)
       float *cstage = sc.cst;
 #pragma unroll
-      for (int m = 0; m < kSelEPL; ++m)
+      for (int m = 0; m < EPL; ++m)
         if (lane + 64 * m < E) cstage[lane + 64 * m] = c[m];
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -166,7 +186,7 @@ __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *
       if (gb >= 0) keep |= 1ull << gb;
     }
 #pragma unroll
-    for (int m = 0; m < kSelEPL; ++m) {
+    for (int m = 0; m < EPL; ++m) {
       const int e = lane + 64 * m;
       if (e < E && ((keep >> (e / per)) & 1ull)) allowed |= 1u << m;
     }
@@ -178,7 +198,7 @@ __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *
     int bi = 0x7fffffff;
     bool have = false;
 #pragma unroll
-    for (int m = 0; m < kSelEPL; ++m) {
+    for (int m = 0; m < EPL; ++m) {
       if ((allowed >> m) & 1u) {
         if (!have || c[m] > bv) { bv = c[m]; bi = lane + 64 * m; have = true; }
       }
@@ -194,7 +214,7 @@ __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *
   if (lane == 0) {
     float S = 0.f;
     for (int j = 0; j < k; ++j)
-      if (sc.rank[j] >= 0) S += sc.sig[sc.rank[j]];
+      if (sc.rank[j] >= 0) S += sig[sc.rank[j]];
     sc.sum = S;
   }
   __builtin_amdgcn_wave_barrier();
@@ -205,7 +225,7 @@ __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *
   if (lane < k) {
     my_i = sc.rank[lane];
     if (my_i >= 0) {
-      my_s = sc.sig[my_i];
+      my_s = sig[my_i];
       if (cfg.norm) my_w = (S != 0.f) ? (my_s / S) * cfg.rsf : 0.f;
       else my_w = my_s * cfg.rsf;
     }
@@ -233,7 +253,7 @@ __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *
       }
       float Sk = 0.f;
       for (int j = 0; j < k; ++j)
-        if (sc.keep[j] && sc.rank[j] >= 0) Sk += sc.sig[sc.rank[j]];
+        if (sc.keep[j] && sc.rank[j] >= 0) Sk += sig[sc.rank[j]];
       sc.sum = Sk;
     }
     __builtin_amdgcn_wave_barrier();
