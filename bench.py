@@ -549,7 +549,7 @@ def cpu_baseline(s, layer0, xs, lgs, ys, NI, budget_s, T):
     }
 
 
-TRACE_NAMES = {1: "entry", 2: "logit slices done", 3: "x quantised", 4: "shared gate/up item done",
+TRACE_NAMES = {1: "entry", 2: "logit slices done", 3: "x quantised", 4: "shared rows done",
                5: "selection begins", 6: "scores read", 7: "selection done",
                8: "routed gate/up item done", 9: "down item begins", 10: "down item h ready",
                11: "down item done", 12: "exit"}

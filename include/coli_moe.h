@@ -351,7 +351,7 @@ coli_status coli_debug_qgemv_blocks(int32_t qtype, const uint8_t *Wq,
  * compiles the records in), recording a timeline: trace [trace_wgs][COLI_TRACE_RECORDS][2] uint64 (device), for
  * workgroups below trace_wgs, record n = (code << 48 | value, s_memrealtime
  * ticks at 100 MHz) at phase and item boundaries (codes: 1 entry, 2 logit
- * slices done, 3 x quantised, 4 shared gate/up item done, 5 selection
+ * slices done, 3 x quantised, 4 the workgroup's shared-expert rows done, 5 selection
  * begins, 6 router scores all read, 7 selection done, 8 routed gate/up item
  * done, 9 down item begins, 10 its h is ready, 11 down item done, 12 exit;
  * the value is the item's ticket).  Unused records keep their contents: zero
