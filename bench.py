@@ -492,13 +492,46 @@ def main() -> int:
     return 0
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def timed_samples(run_one, budget_s, n_samples=3):
+    """Rates of `n_samples` back-to-back samples that share `budget_s`: each
+    sample calls `run_one()` (which returns its own timed seconds and units
+    done) until its share is spent, at least once.  Returns the per-sample
+    (units, seconds)."""
+    out = []
+    for _ in range(n_samples):
+        units, spent = 0, 0.0
+        while True:
+            dt, du = run_one()
+            spent += dt
+            units += du
+            if spent >= budget_s / n_samples:
+                break
+        out.append((units, spent))
+    return out
+
+
 def cpu_baseline(s, layer0, xs, lgs, ys, NI, budget_s, T):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    steps that use layer instance 0, timed one forward call at a time until
-    the budget is spent.  The oracle packs the experts it needs from the same
-    fp32 draws with its own code (untimed)."""
+    steps that use layer instance 0, one forward call at a time, first on one
+    thread and then on every thread the oracle's OpenMP runtime starts by
+    default (the host's share of cores), half the budget each, as three
+    samples per thread count whose median rate is reported.  The oracle packs
+    the experts it needs from the same fp32 draws with its own code (untimed,
+    once per step) and each thread count gets one untimed warm call."""
     import numpy as np
-    import torch
 
     import oracle
     from quantized_moe_coli_amd import inputs
@@ -507,7 +540,7 @@ def cpu_baseline(s, layer0, xs, lgs, ys, NI, budget_s, T):
     ocfg = oracle.make_cfg(s.n_experts, s.top_k, s.n_group, s.topk_group, 1, s.rsf, 0.0, 1)
     gate_w = inputs.gate_weight(s, li, "cuda").cpu().numpy()
     bias = inputs.gate_bias(s, li, "cuda").cpu().numpy()
-    cache = {}
+    cache, prepared = {}, {}
 
     def expert(e):
         if e not in cache:
@@ -515,37 +548,65 @@ def cpu_baseline(s, layer0, xs, lgs, ys, NI, budget_s, T):
             cache[e] = oracle.Expert.from_float(s.bits, g, u, d)
         return cache[e]
 
-    done, spent, max_err = 0, 0.0, 0.0
+    def prepare(st):
+        if st not in prepared:
+            x = xs[st].cpu().numpy()
+            lin = lgs[st].cpu().numpy() if lgs is not None else None
+            lg = oracle.logits(x, gate_w) if lin is None else lin
+            idx, _ = oracle.route(ocfg, lg, bias)
+            exps = [None] * s.n_experts
+            for e in set(idx.ravel().tolist()):
+                if e >= 0:
+                    exps[e] = expert(e)
+            L = oracle.Layer(s.hidden, s.inter, s.bits, ocfg, exps, expert(s.n_experts), gate_w, bias)
+            prepared[st] = (L, x, lin, ys[st].cpu().numpy().astype(np.float64))
+        return prepared[st]
+
     steps = list(range(0, xs.shape[0], NI))
-    for st in steps:
-        x = xs[st].cpu().numpy()
-        lin = lgs[st].cpu().numpy() if lgs is not None else None
-        lg = oracle.logits(x, gate_w) if lin is None else lin
-        idx, _ = oracle.route(ocfg, lg, bias)
-        exps = [None] * s.n_experts
-        for e in set(idx.ravel().tolist()):
-            if e >= 0:
-                exps[e] = expert(e)
-        L = oracle.Layer(s.hidden, s.inter, s.bits, ocfg, exps, expert(s.n_experts), gate_w, bias)
+    state = {"i": 0, "err": 0.0}
+
+    def run_one():
+        st = steps[state["i"] % len(steps)]
+        state["i"] += 1
+        L, x, lin, y = prepare(st)
         t0 = time.perf_counter()
         y_r, _, _, _ = oracle.moe_forward(L, x, lin)
-        spent += time.perf_counter() - t0
-        done += 1
-        y = ys[st].cpu().numpy().astype(np.float64)
+        dt = time.perf_counter() - t0
         err = np.abs(y - y_r).max(axis=1) / np.maximum(np.abs(y_r).max(axis=1), 1e-30)
-        max_err = max(max_err, float(err.max()))
-        if spent >= budget_s:
-            break
-    log(f"[bench] oracle: {done} steps x {T} tokens in {spent:.2f}s on {oracle.num_threads()} "
-        f"threads; GPU outputs of those steps within {max_err:.2e} (rel. to max |y|) of it")
+        state["err"] = max(state["err"], float(err.max()))
+        return dt, T
+
+    n_all = oracle.num_threads()
+    legs = {}
+    for n in (1, n_all):
+        if n in legs:
+            continue
+        oracle.set_num_threads(n)
+        L, x, lin, _ = prepare(steps[0])
+        oracle.moe_forward(L, x, lin)  # untimed warm call
+        samples = timed_samples(run_one, budget_s / 2)
+        rates = sorted(u / t for u, t in samples)
+        legs[n] = {"threads": n, "value": round(float(np.median(rates)), 4),
+                   "samples": [round(r, 4) for r in rates],
+                   "calls": int(sum(u for u, _ in samples) // T),
+                   "seconds": round(sum(t for _, t in samples), 2)}
+        log(f"[bench] oracle on {n} thread(s): median {legs[n]['value']} tokens/s over "
+            f"samples {legs[n]['samples']} ({legs[n]['calls']} calls)")
+    oracle.set_num_threads(n_all)
+    log(f"[bench] GPU outputs of the timed steps within {state['err']:.2e} (rel. to max |y|) "
+        f"of the oracle")
     return {
-        "value": round(done * T / spent, 4),
+        "value": legs[n_all]["value"],
         "unit": "tokens/s",
-        "cores": oracle.num_threads(),
+        "cores": n_all,
         "kind": "oracle",
-        "sample": f"{done} timed forward calls of {T} token(s) on layer instance 0 "
-                  f"(steps 0, {NI}, {2 * NI}, ...), {spent:.1f} s of CPU time; GPU outputs "
-                  f"of the same steps agree to {max_err:.1e}",
+        "cpu": cpu_model(),
+        "single_thread": legs[1],
+        "all_threads": legs[n_all],
+        "sample": f"forward calls of {T} token(s) on layer instance 0 (steps 0, {NI}, "
+                  f"{2 * NI}, ... in turn), on 1 thread and on {n_all}; per thread count "
+                  f"three back-to-back samples of ~{budget_s / 6:.1f} s of timed calls, "
+                  f"median rate; GPU outputs of the same steps agree to {state['err']:.1e}",
     }
 
 
@@ -967,6 +1028,7 @@ def fp8_main(args) -> int:
             "unit": "experts/s",
             "cores": oracle.num_threads(),
             "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"the oracle's dequantisation + requantisation of one 2048 x 6144 gate "
                       f"matrix ({spent:.2f} s), times three for the expert",
         }
@@ -1084,6 +1146,7 @@ def gemv_f32_main(args) -> int:
             "unit": "matrix pairs/s",
             "cores": oracle.num_threads(),
             "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"the oracle's product on one gate-shaped matrix ({spent * 1e3:.1f} ms), "
                       f"twice for the pair; GPU output within {err:.1e} of max |y| of it",
         }
@@ -1116,6 +1179,8 @@ def stack_cpu_baseline(stk, xs, ws, budget_s):
         h_gpu.append(h.cpu().numpy())
     hc = xs[0].cpu().numpy().astype(np.float32)
     spent, done, max_err = 0.0, 0, 0.0
+    times, first = [], None
+    n_all = oracle.num_threads()
     for li, L in enumerate(stk.layers):
         gate_w = L.gate_w.cpu().numpy()
         bias = L.gate_bias.cpu().numpy()
@@ -1135,28 +1200,51 @@ def stack_cpu_baseline(stk, xs, ws, budget_s):
             if e >= 0:
                 exps[e] = ex(e)
         layer = oracle.Layer(s.hidden, s.inter, s.bits, ocfg, exps, ex(s.n_experts), gate_w, bias)
+        if first is None:
+            first = (layer, hn, lg)
         t0 = time.perf_counter()
         y_r, _, _, _ = oracle.moe_forward(layer, hn, lg)
-        spent += time.perf_counter() - t0
+        times.append(time.perf_counter() - t0)
+        spent += times[-1]
         hc = (hc + y_r).astype(np.float32)
         done += 1
         d = np.abs(h_gpu[li].astype(np.float64) - hc).max() / np.abs(hc).max()
         max_err = max(max_err, float(d))
-        if spent >= budget_s:
+        if spent >= budget_s * 2 / 3 and done >= 3:
             break
-    per_layer = spent / done
-    tok_s = xs.shape[1] / (per_layer * stk.n_layers)
-    log(f"[bench] oracle chain, step 0: {done} layers in {spent:.2f}s on {oracle.num_threads()} "
-        f"threads -> {tok_s:.3f} tokens/s extrapolated to {stk.n_layers} layers; GPU hidden "
-        f"state within {max_err:.2e} (rel. to max |h|) of the oracle's over those layers")
+    T = xs.shape[1]
+    tok_s = T / (float(np.median(times)) * stk.n_layers)
+    # the same first layer on one thread: three samples, median rate
+    oracle.set_num_threads(1)
+    layer, hn, lg = first
+    oracle.moe_forward(layer, hn, lg)  # untimed warm call
+
+    def run_one():
+        t0 = time.perf_counter()
+        oracle.moe_forward(layer, hn, lg)
+        return time.perf_counter() - t0, 1
+
+    one = sorted(c / t for c, t in timed_samples(run_one, budget_s / 3))
+    oracle.set_num_threads(n_all)
+    tok_s_1 = T * float(np.median(one)) / stk.n_layers
+    log(f"[bench] oracle chain, step 0: {done} layers in {spent:.2f}s on {n_all} threads -> "
+        f"{tok_s:.3f} tokens/s (median layer) extrapolated to {stk.n_layers} layers, "
+        f"{tok_s_1:.4f} on 1 thread; GPU hidden state within {max_err:.2e} (rel. to max |h|) "
+        f"of the oracle's over those layers")
     return {
         "value": round(tok_s, 5),
         "unit": "tokens/s",
-        "cores": oracle.num_threads(),
+        "cores": n_all,
         "kind": "oracle",
-        "sample": f"step 0 ({xs.shape[1]} token(s)) through layers 0..{done - 1} of the "
-                  f"oracle's own chain ({spent:.1f} s of timed forward calls), extrapolated to "
-                  f"{stk.n_layers} layers; the GPU's chained hidden state is within "
+        "cpu": cpu_model(),
+        "single_thread": {"threads": 1, "value": round(tok_s_1, 5),
+                          "samples_layers_per_s": [round(r, 4) for r in one]},
+        "all_threads": {"threads": n_all, "value": round(tok_s, 5),
+                        "layer_seconds": [round(t, 4) for t in times]},
+        "sample": f"step 0 ({T} token(s)) through layers 0..{done - 1} of the oracle's own "
+                  f"chain on {n_all} threads ({spent:.1f} s of timed forward calls, the median "
+                  f"layer time extrapolated to {stk.n_layers} layers); layer 0 again on one "
+                  f"thread, three samples, median; the GPU's chained hidden state is within "
                   f"{max_err:.1e} of max |h| of the oracle's (each side chains its own "
                   f"outputs, so a near-tied routing decision can flip an expert and the "
                   f"chains drift; single layers are checked bit-exact in routing by the "

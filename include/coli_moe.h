@@ -122,9 +122,10 @@ typedef struct {
 } coli_moe_layer;
 
 /* ABI version (COLI_ABI_VERSION) and a static message for a status.  Library
- * plumbing, not a step of the pages' layer. */
+ * plumbing, not a step of the pages' layer.  coli_status_str takes any int32
+ * (a coli_status value or not: unknown codes give "unknown status"). */
 int coli_abi_version(void);
-const char *coli_status_str(coli_status s);
+const char *coli_status_str(int32_t s);
 
 /* Weight quantisation and packing (colibrì README, "Implemented features":
  * int8 / packed int4 / packed int2 containers, one scale per row; the

@@ -99,6 +99,7 @@ def _declare(L: ctypes.CDLL) -> None:
         "orc_moe_forward": [ctypes.POINTER(_Layer), _P, _I64, _P, _P, _P, _P, _P],
         "orc_union_tables": [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P],
         "orc_num_threads": [],
+        "orc_set_num_threads": [ctypes.c_int],
         "orc_dequant_fp8_block": [_P, _P, _I64, _I64, _P],
         "orc_qdot_f32act": [ctypes.c_int, _P, _P, _I64, _I64, _P, _I64, _P],
     }
@@ -106,6 +107,7 @@ def _declare(L: ctypes.CDLL) -> None:
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    L.orc_set_num_threads.restype = None
     L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
     L.orc_e4m3_value.restype = ctypes.c_float
 
@@ -130,6 +132,11 @@ def qmax(bits: int) -> int:
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of later oracle calls; results do not depend on it."""
+    lib().orc_set_num_threads(int(n))
 
 
 def quant_rows(bits: int, w: np.ndarray):

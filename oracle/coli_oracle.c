@@ -38,6 +38,16 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Every parallel loop of the oracle splits independent rows or experts, so
+ * the thread count changes its speed, never its results. */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int orc_qmax(int bits) {
   switch (bits) {
     case 8: return 127;

@@ -142,6 +142,10 @@ int orc_union_tables(const int32_t *idx, int64_t T, int32_t k, int32_t E,
 /* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
 int orc_num_threads(void);
 
+/* Sets the OpenMP thread count of later oracle calls (n <= 0: no change).
+ * Results do not depend on it. */
+void orc_set_num_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -161,7 +161,7 @@ extern "C" {
 
 int coli_abi_version(void) { return COLI_ABI_VERSION; }
 
-const char *coli_status_str(coli_status s) {
+const char *coli_status_str(int32_t s) {
   switch (s) {
     case COLI_OK: return "ok";
     case COLI_ERR_INVALID_ARG: return "invalid argument";
@@ -226,6 +226,8 @@ coli_status coli_quant_act_q8_0(const float *x, int32_t T, int32_t n, int8_t *q,
   return guarded([&] {
     if (T < 0 || n <= 0 || n % 32 || !x || !q || !d) return COLI_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(d, 4)) return COLI_ERR_INVALID_ARG;
+    // one thread per 32-value block; the launch's thread count is 32-bit
+    if ((int64_t)T * (n / 32) > (int64_t)UINT32_MAX - 255) return COLI_ERR_UNSUPPORTED;
     const coli_status st = check_device();
     if (st != COLI_OK) return st;
     return from_hip(coli::launch_act_quant(8, x, T, n, q, d, static_cast<hipStream_t>(stream)));

@@ -96,7 +96,7 @@ __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *
                                              const float *__restrict__ bias, SelScratch &sc,
                                              int32_t *idx_out, float *w_out) {
   const int lane = threadIdx.x & 63;
-  const int E = cfg.E, k = cfg.k, G = cfg.n_group, per = E / G;
+  const int E = cfg.E;
   const int epl = (E + 63) / 64;  // candidates per lane (uniform)
   float c[kSelEPL], lv[kSelEPL], bv[kSelEPL];
   // all loads first (clamped addresses), so they are in flight together
