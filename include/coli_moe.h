@@ -323,6 +323,104 @@ coli_status coli_moe_forward_noalloc(const coli_moe_layer *L, const float *x,
                                      float *logits_out,
                                      int32_t *wait_status_out, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Tiered expert residency.  The pages treat device memory, host memory and
+ * disk as one hierarchy and stream the routed experts a token needs from the
+ * slower tier (CSDN feature, "把内存、显存和磁盘当成同一块蛋糕"), behind a
+ * per-layer LRU cache of experts plus an optional pinned store of the hot
+ * ones (colibrì README, "Idea"), where the pinned set is learned from the
+ * experts actually used and can be re-chosen in session (labhub post,
+ * "让它变得可以忍受的那些装置": the usage profile and --repin; CSDN
+ * feature, "冷启动与热缓存的辩证法").  Here the cache is HBM and the slower
+ * tier is pinned host memory read by the GPU over the host link.
+ *
+ * One layer's cache: S HBM slots for routed experts.  The layer descriptor's
+ * routed arrays (w_gate, s_gate, w_up, s_up, w_down, s_down) are stacked over
+ * the S slots instead of the E experts; the host tier holds every routed
+ * expert, stacked over E in the same per-expert layouts.  Every forward
+ * through the cache first routes the batch, then one workgroup updates the
+ * cache state and lists the misses, then a copy kernel moves the missing
+ * experts from the host tier into their slots, and then the layer runs with
+ * each routed expert read from its slot.  All of it is enqueued on the
+ * stream with no host round trip.  The cache moves bytes, not arithmetic:
+ * outputs equal coli_moe_forward's on a fully resident layer.
+ *
+ * Replacement, per call: the experts the batch selects form the set R
+ * (entries -1 skipped).  The clock advances by one; each routed pair adds 1
+ * to use_count of its expert; each expert of R that is resident has its
+ * slot's last_use set to the clock (a hit).  The missing experts of R, in
+ * increasing expert order, take the unpinned slots not used by this call in
+ * increasing (last_use, slot) order, evicting what those slots held (an
+ * empty slot has last_use 0, so empty slots fill first).  A call needs
+ * min(E, T*k) <= S - n_pinned, checked on the host.
+ * ------------------------------------------------------------------------- */
+
+/* Pinned host memory for a host tier (library plumbing: hipHostMalloc with
+ * the default flags).  The returned address is valid on the host and on the
+ * device.  The library records the allocation: a cache's host tier must lie
+ * inside allocations made here, so a kernel never reads host memory the GPU
+ * cannot reach.  coli_host_free(NULL) does nothing. */
+coli_status coli_host_alloc(size_t bytes, void **ptr_out);
+coli_status coli_host_free(void *ptr);
+
+/* One layer's expert cache (host struct; E routed experts, S slots). */
+typedef struct {
+  int32_t n_experts; /* E, equal to the layer's router.n_experts */
+  int32_t n_slots;   /* S, 1 <= S <= E */
+  int32_t n_pinned;  /* slots pinned by the last coli_expert_cache_repin (0 after init) */
+  int32_t reserved;
+  /* host tier, inside coli_host_alloc allocations: w_gate/w_up [E][I][H*b/8],
+   * s_gate/s_up [E][I], w_down [E][H][I*b/8], s_down [E][H] */
+  const uint8_t *host_w_gate, *host_w_up, *host_w_down;
+  const float *host_s_gate, *host_s_up, *host_s_down;
+  void *state; /* device, coli_expert_cache_layout_of(E, S).total bytes, 256-byte aligned */
+} coli_expert_cache;
+
+/* Byte offsets inside a cache's device state, each 256-byte aligned:
+ *   ctl        uint32[64]: [0] clock, [1] misses copied by the last call,
+ *              [2] error bits (1: a call had more misses than free slots;
+ *              its outputs are undefined), [4..5] hits, [6..7] misses
+ *              (uint64, low word first; counted per unique expert per call)
+ *   slot_of    int32[E]: slot of expert e, or -1
+ *   expert_of  int32[S]: expert held by slot s, or -1
+ *   last_use   uint32[S]: clock of the slot's last use (0: never)
+ *   pinned     uint32[S]: 1 if the slot is pinned
+ *   use_count  uint32[E]: routed pairs that selected expert e since init (the
+ *              learned usage profile; a caller may save it and write it
+ *              back after init to restore what an earlier run learned)
+ *   copy_list  int32[S][2]: (expert, slot) of the last call's misses */
+typedef struct {
+  size_t ctl, slot_of, expert_of, last_use, pinned, use_count, copy_list, total;
+} coli_expert_cache_layout;
+coli_status coli_expert_cache_layout_of(int32_t n_experts, int32_t n_slots,
+                                        coli_expert_cache_layout *out);
+
+/* Empties the cache: every slot empty, usage, counters and clock zero.
+ * Enqueued on the stream (a fill kernel, no memset); n_pinned set to 0. */
+coli_status coli_expert_cache_init(coli_expert_cache *C, void *stream);
+
+/* Pins the n_pin experts with the largest use_count (ties: lower expert
+ * index) and unpins every other slot; pinned experts that are not resident
+ * are copied in, through the same replacement as a forward call (the clock
+ * advances; hits, misses and usage are not counted).  Sets C->n_pinned =
+ * n_pin.  0 <= n_pin < S.  L is the layer whose slots the cache fills. */
+coli_status coli_expert_cache_repin(coli_expert_cache *C,
+                                    const coli_moe_layer *L, int32_t n_pin,
+                                    void *stream);
+
+/* coli_moe_forward through the cache: the same arguments and results, with
+ * L's routed arrays stacked over C's S slots.  Routing runs first (logits
+ * from gate_w plus gate_offset unless logits_in is given), then the cache
+ * update and copies, then the layer.  T must satisfy min(E, T*k) <= S -
+ * C->n_pinned (else COLI_ERR_UNSUPPORTED).  Calls on one cache must be
+ * serialised (one stream). */
+coli_status coli_moe_forward_cached(const coli_moe_layer *L,
+                                    const coli_expert_cache *C, const float *x,
+                                    int32_t T, const float *logits_in,
+                                    float *y, int32_t *idx_out, float *w_out,
+                                    float *logits_out, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
 /* Status of the decode path's bounded waits (library plumbing, not a step
  * of the pages' layer; it reports when the outputs of coli_moe_forward are
  * undefined).  The workspace's status word (see coli_moe_workspace_bytes) copied to

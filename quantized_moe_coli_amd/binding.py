@@ -49,6 +49,20 @@ class MoeLayerC(ctypes.Structure):
                 ("mfma_min_tokens", ctypes.c_int32), ("gate_offset", _P)]
 
 
+class ExpertCacheC(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+                ("n_pinned", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("host_w_gate", _P), ("host_w_up", _P), ("host_w_down", _P),
+                ("host_s_gate", _P), ("host_s_up", _P), ("host_s_down", _P),
+                ("state", _P)]
+
+
+class CacheLayoutC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("ctl", "slot_of", "expert_of", "last_use", "pinned", "use_count", "copy_list",
+                 "total")]
+
+
 # The timeline build (decode kernel with timeline records compiled in), for
 # coli_debug_decode_trace only.
 TRACE_LIB_PATH = os.path.join(_PKG, "libcoli_moe_trace.so")
@@ -101,6 +115,14 @@ def _load(path: str) -> ctypes.CDLL:
         "coli_debug_stream_read": ([_P, sz, _P, ctypes.POINTER(i32), _P], ctypes.c_int),
         "coli_moe_forward_noalloc": ([ctypes.POINTER(MoeLayerC), _P, i32, _P, _P, _P, _P, _P,
                                       _P, _P], ctypes.c_int),
+        "coli_host_alloc": ([sz, ctypes.POINTER(_P)], ctypes.c_int),
+        "coli_host_free": ([_P], ctypes.c_int),
+        "coli_expert_cache_layout_of": ([i32, i32, ctypes.POINTER(CacheLayoutC)], ctypes.c_int),
+        "coli_expert_cache_init": ([ctypes.POINTER(ExpertCacheC), _P], ctypes.c_int),
+        "coli_expert_cache_repin": ([ctypes.POINTER(ExpertCacheC), ctypes.POINTER(MoeLayerC), i32,
+                                     _P], ctypes.c_int),
+        "coli_moe_forward_cached": ([ctypes.POINTER(MoeLayerC), ctypes.POINTER(ExpertCacheC), _P,
+                                     i32, _P, _P, _P, _P, _P, _P, sz, _P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -264,16 +286,20 @@ class MoeLayer:
                          _ptr(self.gate_offset, f32, "gate_offset"))
 
     @staticmethod
-    def empty(hidden, inter, qtype, cfg: RouterCfg, device="cuda", gate=True) -> "MoeLayer":
-        """Uninitialised device storage for a layer (filled by coli_quant_pack)."""
+    def empty(hidden, inter, qtype, cfg: RouterCfg, device="cuda", gate=True,
+              n_slots: int | None = None) -> "MoeLayer":
+        """Uninitialised device storage for a layer (filled by coli_quant_pack).
+        With ``n_slots`` the routed arrays hold that many expert-cache slots
+        instead of all E experts."""
         E, H, I = cfg.n_experts, hidden, inter
+        R = E if n_slots is None else n_slots  # routed entries: experts or slots
         gb, db = H * qtype // 8, I * qtype // 8
         u8, f32 = torch.uint8, torch.float32
         z = lambda *s, dt: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
         return MoeLayer(H, I, qtype, cfg,
                         z(E, H, dt=f32) if gate else None, z(E, dt=f32),
-                        z(E, I, gb, dt=u8), z(E, I, dt=f32), z(E, I, gb, dt=u8), z(E, I, dt=f32),
-                        z(E, H, db, dt=u8), z(E, H, dt=f32),
+                        z(R, I, gb, dt=u8), z(R, I, dt=f32), z(R, I, gb, dt=u8), z(R, I, dt=f32),
+                        z(R, H, db, dt=u8), z(R, H, dt=f32),
                         z(I, gb, dt=u8), z(I, dt=f32), z(I, gb, dt=u8), z(I, dt=f32),
                         z(H, db, dt=u8), z(H, dt=f32))
 
@@ -411,3 +437,160 @@ def coli_debug_qgemv_blocks(qtype: int, Wq: torch.Tensor, cols: int, xq: torch.T
     _check("coli_debug_qgemv_blocks", lib().coli_debug_qgemv_blocks(
         qtype, _ptr(Wq, torch.uint8, "Wq"), rows, cols, _ptr(xq, torch.int8, "xq"), T,
         _ptr(acc_out, torch.int32, "acc_out"), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Tiered expert residency: a host tier in pinned host memory, and per-layer
+# expert caches of HBM slots over it.
+# ---------------------------------------------------------------------------
+class HostBuffer:
+    """Pinned host memory from coli_host_alloc (valid on host and device);
+    freed by close() or when collected.  Views must not outlive it."""
+
+    def __init__(self, nbytes: int):
+        p = _P()
+        _check("coli_host_alloc", lib().coli_host_alloc(nbytes, ctypes.byref(p)))
+        self.ptr, self.nbytes = p.value, nbytes
+
+    def view(self, offset: int, shape, dtype) -> torch.Tensor:
+        """A CPU tensor over bytes [offset, offset + numel*itemsize)."""
+        import numpy as np
+        n = 1
+        for d in shape:
+            n *= d
+        nb = n * torch.empty((), dtype=dtype).element_size()
+        if offset < 0 or offset + nb > self.nbytes:
+            raise ValueError("view outside the buffer")
+        arr = np.ctypeslib.as_array((ctypes.c_uint8 * nb).from_address(self.ptr + offset))
+        return torch.from_numpy(arr).view(dtype).reshape(shape)
+
+    def close(self) -> None:
+        if self.ptr:
+            _check("coli_host_free", lib().coli_host_free(_P(self.ptr)))
+            self.ptr = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class HostTier:
+    """Every routed expert of one layer in pinned host memory, stacked over E
+    in the layer's layouts: w_gate/w_up uint8 [E, I, H*b/8], s_gate/s_up fp32
+    [E, I], w_down uint8 [E, H, I*b/8], s_down fp32 [E, H]."""
+
+    def __init__(self, n_experts: int, hidden: int, inter: int, qtype: int):
+        E, H, I, b = n_experts, hidden, inter, qtype
+        self.n_experts, self.hidden, self.inter, self.qtype = E, H, I, b
+        u8, f32 = torch.uint8, torch.float32
+        specs = [("w_gate", (E, I, H * b // 8), u8), ("w_up", (E, I, H * b // 8), u8),
+                 ("w_down", (E, H, I * b // 8), u8), ("s_gate", (E, I), f32),
+                 ("s_up", (E, I), f32), ("s_down", (E, H), f32)]
+        offs, off = [], 0
+        for _, shp, dt in specs:
+            offs.append(off)
+            n = torch.empty((), dtype=dt).element_size()
+            for d in shp:
+                n *= d
+            off = (off + n + 255) // 256 * 256
+        self.buf = HostBuffer(off)
+        for (name, shp, dt), o in zip(specs, offs):
+            setattr(self, name, self.buf.view(o, shp, dt))
+
+    def load_experts(self, layer: "MoeLayer", first: int = 0) -> None:
+        """Copy the routed experts of a device layer (stacked over its own
+        count n) into host-tier experts first .. first+n-1."""
+        n = layer.w_gate.shape[0]
+        for name in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down"):
+            getattr(self, name)[first:first + n].copy_(getattr(layer, name))
+
+    def close(self) -> None:
+        self.buf.close()
+
+
+class ExpertCache:
+    """One layer's expert cache: ``n_slots`` HBM slots (the routed arrays of
+    the layer it serves) over a HostTier, with its device state."""
+
+    def __init__(self, tier: HostTier, n_slots: int, device="cuda"):
+        E = tier.n_experts
+        self.tier, self.n_slots = tier, n_slots
+        lo = CacheLayoutC()
+        _check("coli_expert_cache_layout_of", lib().coli_expert_cache_layout_of(E, n_slots, ctypes.byref(lo)))
+        self.layout = lo
+        raw = torch.zeros(lo.total + 256, dtype=torch.uint8, device=device)
+        off = (-raw.data_ptr()) % 256
+        self._raw = raw
+        self.state = raw[off:off + lo.total]
+        h = lambda t: _P(t.data_ptr())  # noqa: E731 -- pinned host views
+        self.c = ExpertCacheC(E, n_slots, 0, 0, h(tier.w_gate), h(tier.w_up), h(tier.w_down),
+                              h(tier.s_gate), h(tier.s_up), h(tier.s_down), _P(self.state.data_ptr()))
+
+    def _words(self, off: int, n: int, dtype=torch.int32) -> torch.Tensor:
+        return self.state[off:off + 4 * n].view(dtype)
+
+    @property
+    def slot_of(self) -> torch.Tensor:
+        return self._words(self.layout.slot_of, self.c.n_experts)
+
+    @property
+    def expert_of(self) -> torch.Tensor:
+        return self._words(self.layout.expert_of, self.n_slots)
+
+    @property
+    def last_use(self) -> torch.Tensor:
+        return self._words(self.layout.last_use, self.n_slots)
+
+    @property
+    def pinned(self) -> torch.Tensor:
+        return self._words(self.layout.pinned, self.n_slots)
+
+    @property
+    def use_count(self) -> torch.Tensor:
+        return self._words(self.layout.use_count, self.c.n_experts)
+
+    def init(self, stream=None) -> None:
+        _check("coli_expert_cache_init", lib().coli_expert_cache_init(ctypes.byref(self.c), _stream(stream)))
+
+    def repin(self, layer: "MoeLayer", n_pin: int, stream=None, c_layer=None) -> None:
+        c = c_layer if c_layer is not None else layer.c_struct()
+        _check("coli_expert_cache_repin", lib().coli_expert_cache_repin(
+            ctypes.byref(self.c), ctypes.byref(c), n_pin, _stream(stream)))
+
+    def stats(self) -> dict:
+        """clock, last call's copies, error bits, hits and misses (host ints;
+        synchronises the device)."""
+        ctl = self.state[self.layout.ctl:self.layout.ctl + 64 * 4].view(torch.int64).cpu()
+        w = ctl.view(torch.int32)
+        return {"clock": int(w[0]) & 0xFFFFFFFF, "copied": int(w[1]), "error": int(w[2]),
+                "hits": int(ctl[2]), "misses": int(ctl[3])}
+
+    def save_usage(self, path: str) -> None:
+        """Write the learned usage profile (one count per expert)."""
+        with open(path, "w") as f:
+            f.write(" ".join(str(int(v)) for v in self.use_count.cpu().tolist()) + "\n")
+
+    def load_usage(self, path: str) -> None:
+        """Restore a usage profile written by save_usage (after init)."""
+        with open(path) as f:
+            vals = [int(v) for v in f.read().split()]
+        if len(vals) != self.c.n_experts:
+            raise ValueError("usage profile has the wrong expert count")
+        self.use_count.copy_(torch.tensor(vals, dtype=torch.int32))
+
+
+def coli_moe_forward_cached(layer: MoeLayer, cache: ExpertCache, x: torch.Tensor, y: torch.Tensor,
+                            ws: torch.Tensor, logits_in=None, idx_out=None, w_out=None,
+                            logits_out=None, stream=None, c_layer: MoeLayerC | None = None) -> None:
+    """coli_moe_forward with the layer's routed experts read from ``cache``'s
+    slots (``layer``'s routed arrays hold the slots)."""
+    T = x.shape[0]
+    c = c_layer if c_layer is not None else layer.c_struct()
+    _check("coli_moe_forward_cached", lib().coli_moe_forward_cached(
+        ctypes.byref(c), ctypes.byref(cache.c), _ptr(x, torch.float32, "x"), T,
+        _ptr(logits_in, torch.float32, "logits_in"), _ptr(y, torch.float32, "y"),
+        _ptr(idx_out, torch.int32, "idx_out"), _ptr(w_out, torch.float32, "w_out"),
+        _ptr(logits_out, torch.float32, "logits_out"), ctypes.c_void_p(ws.data_ptr()),
+        ws.numel(), _stream(stream)))

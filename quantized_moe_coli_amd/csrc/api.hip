@@ -5,6 +5,8 @@
 
 #include <atomic>
 #include <cstring>
+#include <algorithm>
+#include <map>
 #include <mutex>
 
 #include "coli_moe.h"
@@ -145,6 +147,103 @@ void *scratch_ptr(int dev, hipStream_t st) {
   }
   return g_scratch_ptr[dev];
 }
+
+// Pinned host allocations made by coli_host_alloc: base -> bytes.  A cache's
+// host tier must lie inside one of them, so the copy kernel only reads host
+// memory that is mapped for the GPU.
+std::mutex g_host_mu;
+std::map<uintptr_t, size_t> g_host_allocs;
+
+bool in_host_alloc(const void *p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  std::lock_guard<std::mutex> lock(g_host_mu);
+  auto it = g_host_allocs.upper_bound(a);
+  if (it == g_host_allocs.begin()) return false;
+  --it;
+  return a >= it->first && bytes <= it->second && a - it->first <= it->second - bytes;
+}
+
+bool cache_layout(int E, int S, coli_expert_cache_layout *o) {
+  if (E < 1 || E > 1024 || S < 1 || S > E) return false;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  o->ctl = take(coli::kCacheCtlWords * 4);
+  o->slot_of = take((size_t)E * 4);
+  o->expert_of = take((size_t)S * 4);
+  o->last_use = take((size_t)S * 4);
+  o->pinned = take((size_t)S * 4);
+  o->use_count = take((size_t)E * 4);
+  o->copy_list = take((size_t)S * 8);
+  o->total = off;
+  return true;
+}
+
+bool cache_state(const coli_expert_cache *C, coli::CacheState *st) {
+  coli_expert_cache_layout lo;
+  if (!C || !cache_layout(C->n_experts, C->n_slots, &lo) || !C->state || !aligned(C->state, 256))
+    return false;
+  if (C->n_pinned < 0 || C->n_pinned >= C->n_slots) return false;
+  char *b = static_cast<char *>(C->state);
+  st->ctl = reinterpret_cast<uint32_t *>(b + lo.ctl);
+  st->slot_of = reinterpret_cast<int32_t *>(b + lo.slot_of);
+  st->expert_of = reinterpret_cast<int32_t *>(b + lo.expert_of);
+  st->last_use = reinterpret_cast<uint32_t *>(b + lo.last_use);
+  st->pinned = reinterpret_cast<uint32_t *>(b + lo.pinned);
+  st->use_count = reinterpret_cast<uint32_t *>(b + lo.use_count);
+  st->copy_list = reinterpret_cast<int32_t *>(b + lo.copy_list);
+  st->E = C->n_experts;
+  st->S = C->n_slots;
+  return true;
+}
+
+// The copy description of a cache over layer L: the host tier (checked to
+// lie inside coli_host_alloc allocations) and L's routed arrays as slots.
+bool cache_tier(const coli_moe_layer *L, const coli_expert_cache *C, coli::CacheTier *t) {
+  if (!L || !C || C->n_experts != L->router.n_experts) return false;
+  const size_t E = C->n_experts, H = L->hidden, I = L->inter, b = L->qtype;
+  const size_t gu = I * (H * b / 8), d = H * (I * b / 8);
+  const void *hw[] = {C->host_w_gate, C->host_w_up, C->host_w_down};
+  const size_t hwb[] = {E * gu, E * gu, E * d};
+  const void *hs[] = {C->host_s_gate, C->host_s_up, C->host_s_down};
+  const size_t hsb[] = {E * I * 4, E * I * 4, E * H * 4};
+  for (int i = 0; i < 3; ++i) {
+    if (!hw[i] || !aligned(hw[i], 16) || !in_host_alloc(hw[i], hwb[i])) return false;
+    if (!hs[i] || !aligned(hs[i], 16) || !in_host_alloc(hs[i], hsb[i])) return false;
+  }
+  // the copies move 16-byte words: the slot arrays' scales must be 16-byte aligned too
+  if (!aligned(L->s_gate, 16) || !aligned(L->s_up, 16) || !aligned(L->s_down, 16)) return false;
+  t->hw_gate = C->host_w_gate;
+  t->hw_up = C->host_w_up;
+  t->hw_down = C->host_w_down;
+  t->hs_gate = C->host_s_gate;
+  t->hs_up = C->host_s_up;
+  t->hs_down = C->host_s_down;
+  t->dw_gate = const_cast<uint8_t *>(L->w_gate);
+  t->dw_up = const_cast<uint8_t *>(L->w_up);
+  t->dw_down = const_cast<uint8_t *>(L->w_down);
+  t->ds_gate = const_cast<float *>(L->s_gate);
+  t->ds_up = const_cast<float *>(L->s_up);
+  t->ds_down = const_cast<float *>(L->s_down);
+  t->gu_bytes = gu;
+  t->d_bytes = d;
+  t->I = (int)I;
+  t->H = (int)H;
+  return true;
+}
+
+struct CacheRun {
+  coli::CacheState st;
+  coli::CacheTier tier;
+};
+
+coli_status forward_impl(const coli_moe_layer *L, const CacheRun *cache, const float *x,
+                         int32_t T, const float *logits_in, float *y, int32_t *idx_out,
+                         float *w_out, float *logits_out, void *workspace, size_t workspace_bytes,
+                         void *stream, void *const *stage_events, int32_t n_stage_events);
 
 template <typename F>
 coli_status guarded(F &&f) {
@@ -289,6 +388,20 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
                                       float *w_out, float *logits_out, void *workspace,
                                       size_t workspace_bytes, void *stream,
                                       void *const *stage_events, int32_t n_stage_events) {
+  return forward_impl(L, nullptr, x, T, logits_in, y, idx_out, w_out, logits_out, workspace,
+                      workspace_bytes, stream, stage_events, n_stage_events);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The layer on T tokens; with `cache`, routing runs first, then the cache
+// update and copies, and routed experts are read from their slots.
+coli_status forward_impl(const coli_moe_layer *L, const CacheRun *cache, const float *x,
+                         int32_t T, const float *logits_in, float *y, int32_t *idx_out,
+                         float *w_out, float *logits_out, void *workspace, size_t workspace_bytes,
+                         void *stream, void *const *stage_events, int32_t n_stage_events) {
   return guarded([&] {
     if (n_stage_events < 0 || (n_stage_events > 0 && !stage_events)) return COLI_ERR_INVALID_ARG;
     if (!layer_ok(L) || T < 0 || T > kMaxTokens) return COLI_ERR_INVALID_ARG;
@@ -334,6 +447,10 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
     fa.L = coli::LayerPtrs{H, I, L->qtype, L->w_gate, L->w_up, L->w_down, L->s_gate, L->s_up,
                            L->s_down, L->sh_gate, L->sh_up, L->sh_down, L->sh_s_gate,
                            L->sh_s_up, L->sh_s_down};
+    if (cache) {
+      fa.L.slot_of = cache->st.slot_of;
+      fa.L.n_slots = cache->st.S;
+    }
     fa.T = T;
     fa.k = k;
     fa.E = E;
@@ -352,6 +469,33 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
     fa.obuf = reinterpret_cast<float *>(base + ws.obuf);
     fa.y = y;
     const int mfma_min = L->mfma_min_tokens;
+    // the cache update and copies, once the batch's routing is in idx
+    auto cache_step = [&]() {
+      hipError_t ce = coli::launch_cache_plan(cache->st, idx, T * k, -1, s);
+      if (ce == hipSuccess) ce = coli::launch_cache_fill(cache->st, cache->tier, s);
+      return ce;
+    };
+    if (cache && T == 1) {
+      // decode through the cache: logits (unless supplied), selection, cache
+      // update and copies, then the layer on the supplied logits
+      if (!logits_in) {
+        e = coli::launch_front(L->qtype, x, L->gate_w, L->gate_offset, T, E, H, lp_dst, nullptr,
+                               nullptr, s);
+        if (e != hipSuccess) return COLI_ERR_DEVICE;
+      }
+      e = coli::launch_route(to_cfg(L->router), lp, L->gate_bias, T, idx, wts, nullptr, nullptr, s);
+      if (e == hipSuccess) e = cache_step();
+      if (e != hipSuccess) return COLI_ERR_DEVICE;
+      fa.loff = nullptr;
+      e = coli::launch_decode_fused(fa, x, nullptr, lp, nullptr,
+                                    reinterpret_cast<uint32_t *>(base + ws.ctr),
+                                    reinterpret_cast<float *>(base + ws.hsh), s, kev(0));
+      if (e != hipErrorNotSupported) return from_hip(e);
+      e = coli::launch_front(L->qtype, x, nullptr, nullptr, T, E, H, nullptr, xq, xd, s, kev(0));
+      if (e == hipSuccess) e = coli::launch_gateup(fa, false, mfma_min, s, kev(1));
+      if (e == hipSuccess) e = coli::launch_down(fa, false, mfma_min, s, kev(2));
+      return from_hip(e);
+    }
     if (T == 1) {
       // decode: the whole layer in one kernel where that kernel is built for
       // the layer's row shapes
@@ -372,6 +516,7 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
     }
     e = coli::launch_route(to_cfg(L->router), lp, L->gate_bias, T, idx, wts, idx_out, w_out, s);
     if (e != hipSuccess) return COLI_ERR_DEVICE;
+    if (cache && cache_step() != hipSuccess) return COLI_ERR_DEVICE;
     int32_t *counts = reinterpret_cast<int32_t *>(base + ws.counts);
     int32_t *offs = reinterpret_cast<int32_t *>(base + ws.offs);
     int32_t *perm = reinterpret_cast<int32_t *>(base + ws.perm);
@@ -394,6 +539,10 @@ coli_status coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, i
     return from_hip(e);
   });
 }
+
+}  // namespace
+
+extern "C" {
 
 coli_status coli_moe_forward_noalloc(const coli_moe_layer *L, const float *x, int32_t T,
                                      const float *logits_in, float *y, int32_t *idx_out,
@@ -504,6 +653,99 @@ coli_status coli_debug_qgemv_blocks(int32_t qtype, const uint8_t *Wq, int32_t ro
     if (st != COLI_OK) return st;
     return from_hip(coli::launch_debug_blocks(qtype, Wq, rows, cols, xq, T, acc_out,
                                               static_cast<hipStream_t>(stream)));
+  });
+}
+
+coli_status coli_host_alloc(size_t bytes, void **ptr_out) {
+  return guarded([&] {
+    if (!ptr_out || bytes == 0) return COLI_ERR_INVALID_ARG;
+    *ptr_out = nullptr;
+    const coli_status st = check_device();
+    if (st != COLI_OK) return st;
+    void *p = nullptr;
+    if (hipHostMalloc(&p, bytes, hipHostMallocDefault) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return COLI_ERR_DEVICE;
+    }
+    // the copy kernel reads the host tier at its host address
+    void *d = nullptr;
+    if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess || d != p) {
+      (void)hipGetLastError();
+      (void)hipHostFree(p);
+      return COLI_ERR_DEVICE;
+    }
+    {
+      std::lock_guard<std::mutex> lock(g_host_mu);
+      g_host_allocs[reinterpret_cast<uintptr_t>(p)] = bytes;
+    }
+    *ptr_out = p;
+    return COLI_OK;
+  });
+}
+
+coli_status coli_host_free(void *ptr) {
+  return guarded([&] {
+    if (!ptr) return COLI_OK;
+    {
+      std::lock_guard<std::mutex> lock(g_host_mu);
+      auto it = g_host_allocs.find(reinterpret_cast<uintptr_t>(ptr));
+      if (it == g_host_allocs.end()) return COLI_ERR_INVALID_ARG;
+      g_host_allocs.erase(it);
+    }
+    return from_hip(hipHostFree(ptr));
+  });
+}
+
+coli_status coli_expert_cache_layout_of(int32_t n_experts, int32_t n_slots,
+                                        coli_expert_cache_layout *out) {
+  if (!out || !cache_layout(n_experts, n_slots, out)) return COLI_ERR_INVALID_ARG;
+  return COLI_OK;
+}
+
+coli_status coli_expert_cache_init(coli_expert_cache *C, void *stream) {
+  return guarded([&] {
+    coli::CacheState st;
+    if (!C) return COLI_ERR_INVALID_ARG;
+    C->n_pinned = 0;
+    if (!cache_state(C, &st)) return COLI_ERR_INVALID_ARG;
+    const coli_status ds = check_device();
+    if (ds != COLI_OK) return ds;
+    return from_hip(coli::launch_cache_init(st, static_cast<hipStream_t>(stream)));
+  });
+}
+
+coli_status coli_expert_cache_repin(coli_expert_cache *C, const coli_moe_layer *L, int32_t n_pin,
+                                    void *stream) {
+  return guarded([&] {
+    CacheRun run;
+    if (!C || !layer_ok(L) || !cache_state(C, &run.st) || !cache_tier(L, C, &run.tier))
+      return COLI_ERR_INVALID_ARG;
+    if (n_pin < 0 || n_pin >= C->n_slots) return COLI_ERR_INVALID_ARG;
+    const coli_status ds = check_device();
+    if (ds != COLI_OK) return ds;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = coli::launch_cache_plan(run.st, nullptr, 0, n_pin, s);
+    if (e == hipSuccess) e = coli::launch_cache_fill(run.st, run.tier, s);
+    if (e != hipSuccess) return COLI_ERR_DEVICE;
+    C->n_pinned = n_pin;
+    return COLI_OK;
+  });
+}
+
+coli_status coli_moe_forward_cached(const coli_moe_layer *L, const coli_expert_cache *C,
+                                    const float *x, int32_t T, const float *logits_in, float *y,
+                                    int32_t *idx_out, float *w_out, float *logits_out,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+  return guarded([&] {
+    CacheRun run;
+    if (!layer_ok(L) || !cache_state(C, &run.st) || !cache_tier(L, C, &run.tier))
+      return COLI_ERR_INVALID_ARG;
+    if (T < 0 || T > kMaxTokens) return COLI_ERR_INVALID_ARG;
+    // every expert the batch selects must find a slot
+    const int64_t need = std::min<int64_t>(C->n_experts, (int64_t)T * L->router.top_k);
+    if (need > C->n_slots - C->n_pinned) return COLI_ERR_UNSUPPORTED;
+    return forward_impl(L, &run, x, T, logits_in, y, idx_out, w_out, logits_out, workspace,
+                        workspace_bytes, stream, nullptr, 0);
   });
 }
 

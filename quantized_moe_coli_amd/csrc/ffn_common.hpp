@@ -105,6 +105,10 @@ __device__ __forceinline__ ExpertPtrs expert_ptrs(const LayerPtrs &L, int e) {
   } else {
     const size_t gu_stride = (size_t)L.I * (L.H * L.bits / 8);
     const size_t d_stride = (size_t)L.H * (L.I * L.bits / 8);
+    if (L.slot_of) {  // through the expert cache (an out-of-range slot reads slot 0)
+      const int s = L.slot_of[e];
+      e = (unsigned)s < (unsigned)L.n_slots ? s : 0;
+    }
     p.wg = L.w_gate + (size_t)e * gu_stride;
     p.wu = L.w_up + (size_t)e * gu_stride;
     p.wd = L.w_down + (size_t)e * d_stride;

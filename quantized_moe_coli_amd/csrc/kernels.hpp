@@ -49,7 +49,39 @@ struct LayerPtrs {
   const float *s_gate, *s_up, *s_down;
   const uint8_t *sh_gate, *sh_up, *sh_down;
   const float *sh_s_gate, *sh_s_up, *sh_s_down;
+  // expert cache: routed expert e lives in slot slot_of[e] of the routed
+  // arrays (n_slots of them); null = every expert resident at index e
+  const int32_t *slot_of;
+  int n_slots;
 };
+
+// A layer's expert-cache state in device memory (layout in coli_moe.h).
+constexpr int kCacheCtlWords = 64;
+struct CacheState {
+  uint32_t *ctl;
+  int32_t *slot_of, *expert_of;
+  uint32_t *last_use, *pinned, *use_count;
+  int32_t *copy_list;
+  int E, S;
+};
+
+// Where the cache copies from (host tier, device-visible) and to (the
+// layer's routed slot arrays), with one expert's byte counts.
+struct CacheTier {
+  const uint8_t *hw_gate, *hw_up, *hw_down;
+  const float *hs_gate, *hs_up, *hs_down;
+  uint8_t *dw_gate, *dw_up, *dw_down;
+  float *ds_gate, *ds_up, *ds_down;
+  size_t gu_bytes, d_bytes;
+  int I, H;
+};
+
+hipError_t launch_cache_init(const CacheState &c, hipStream_t st);
+// repin < 0: a forward call's update from idx[0..n_pairs-1]; repin >= 0: pin
+// the `repin` most-used experts.
+hipError_t launch_cache_plan(const CacheState &c, const int32_t *idx, int n_pairs, int repin,
+                             hipStream_t st);
+hipError_t launch_cache_fill(const CacheState &c, const CacheTier &t, hipStream_t st);
 
 // Union bookkeeping living in the workspace.
 struct Dispatch {

@@ -91,3 +91,68 @@ def step(st: Stack, h: torch.Tensor, ws: torch.Tensor, y: torch.Tensor,
                            w_out=None if w_rec is None else w_rec[li],
                            c_layer=st.c_layers[li])
         h.add_(y)
+
+
+@dataclass
+class TieredStack:
+    """The same stack with each layer's routed experts in a pinned host tier
+    and ``n_slots`` HBM slots per layer in front of it (per-layer expert
+    caches); gates, offsets and shared experts stay in HBM."""
+    s: inputs.Shape
+    layers: list
+    caches: list
+    offsets: list
+    n_slots: int
+    c_layers: list = field(default_factory=list)
+
+    @property
+    def n_layers(self) -> int:
+        return len(self.layers)
+
+
+def build_tiered(n_layers: int, n_slots: int, s: inputs.Shape = STACK_SHAPE,
+                 device="cuda", log=None) -> TieredStack:
+    """Draw and pack every layer as ``build`` does; each layer's routed
+    experts are packed into one reused HBM staging layer and copied to the
+    layer's host tier, and the layer keeps ``n_slots`` empty slots."""
+    cfg = B.router_cfg(s.n_experts, s.top_k, s.n_group, s.topk_group, 1, s.rsf, s.top_p, 1)
+    staging = B.MoeLayer.empty(s.hidden, s.inter, s.bits, cfg, device, gate=False)
+    layers, caches, offsets = [], [], []
+    for li in range(n_layers):
+        seed = layer_seed(li)
+        L = B.MoeLayer.empty(s.hidden, s.inter, s.bits, cfg, device, n_slots=n_slots)
+        L.gate_w.copy_(inputs.gate_weight(s, seed, device))
+        L.gate_bias.copy_(inputs.gate_bias(s, seed, device))
+        off = inputs.zipf_logit_offsets(0, li, s.n_experts, ZIPF_S, device)
+        L.gate_offset = off
+        for e in range(s.n_experts):
+            g, u, d = inputs.expert_weights(s, seed, e, device)
+            staging.pack_expert(e, g, u, d)
+        g, u, d = inputs.expert_weights(s, seed, s.n_experts, device)
+        L.pack_expert(s.n_experts, g, u, d)
+        del g, u, d
+        torch.cuda.synchronize()
+        tier = B.HostTier(s.n_experts, s.hidden, s.inter, s.bits)
+        tier.load_experts(staging)
+        cache = B.ExpertCache(tier, n_slots, device)
+        cache.init()
+        layers.append(L)
+        caches.append(cache)
+        offsets.append(off)
+        if log is not None and (li % 8 == 7 or li == n_layers - 1):
+            log(f"[stack] {li + 1}/{n_layers} layers to the host tier")
+    del staging
+    torch.cuda.synchronize()
+    st = TieredStack(s, layers, caches, offsets, n_slots)
+    st.c_layers = [L.c_struct() for L in layers]
+    return st
+
+
+def step_tiered(st: TieredStack, h: torch.Tensor, ws: torch.Tensor, y: torch.Tensor,
+                idx_rec: torch.Tensor | None = None) -> None:
+    """One token through every layer of a tiered stack, in place on h."""
+    for li, L in enumerate(st.layers):
+        B.coli_moe_forward_cached(L, st.caches[li], rmsnorm(h), y, ws,
+                                  idx_out=None if idx_rec is None else idx_rec[li],
+                                  c_layer=st.c_layers[li])
+        h.add_(y)

@@ -136,11 +136,49 @@ int main() {
   CHECK(coli_debug_stream_read(fake(0x300000), 15, fake<uint32_t>(16), nullptr, nullptr) == COLI_ERR_INVALID_ARG);
   CHECK(coli_debug_stream_read(nullptr, 16, fake<uint32_t>(16), nullptr, nullptr) == COLI_ERR_INVALID_ARG);
 
+  // expert cache: layouts over the whole size range, malformed descriptors,
+  // host tiers outside any coli_host_alloc allocation
+  for (int E : {1, 16, 256, 1024, 1025, 0, -5}) {
+    for (int S : {0, 1, 8, E, E + 1}) {
+      coli_expert_cache_layout lo;
+      const coli_status r = coli_expert_cache_layout_of(E, S, &lo);
+      if (E >= 1 && E <= 1024 && S >= 1 && S <= E) {
+        CHECK(r == COLI_OK && lo.total % 256 == 0 && lo.copy_list + (size_t)S * 8 <= lo.total);
+      } else {
+        CHECK(r == COLI_ERR_INVALID_ARG);
+      }
+    }
+  }
+  coli_expert_cache C;
+  memset(&C, 0, sizeof C);
+  C.n_experts = 256;
+  C.n_slots = 32;
+  C.host_w_gate = fake<const uint8_t>(0x800000);
+  C.host_w_up = fake<const uint8_t>(0x900000);
+  C.host_w_down = fake<const uint8_t>(0xA00000);
+  C.host_s_gate = fake<const float>(0xB00000);
+  C.host_s_up = fake<const float>(0xC00000);
+  C.host_s_down = fake<const float>(0xD00000);
+  C.state = fake(0x400010);
+  CHECK(coli_expert_cache_init(&C, nullptr) == COLI_ERR_INVALID_ARG);
+  CHECK(coli_expert_cache_init(nullptr, nullptr) == COLI_ERR_INVALID_ARG);
+  C.state = fake(0x400000);
+  CHECK(coli_moe_forward_cached(&good, &C, x, 1, nullptr, y, nullptr, nullptr, nullptr, wsp, ws, nullptr) == COLI_ERR_INVALID_ARG);
+  CHECK(coli_expert_cache_repin(&C, &good, 4, nullptr) == COLI_ERR_INVALID_ARG);
+  C.n_pinned = 32;
+  CHECK(coli_moe_forward_cached(&good, &C, x, 1, nullptr, y, nullptr, nullptr, nullptr, wsp, ws, nullptr) == COLI_ERR_INVALID_ARG);
+  CHECK(coli_moe_forward_cached(&good, nullptr, x, 1, nullptr, y, nullptr, nullptr, nullptr, wsp, ws, nullptr) == COLI_ERR_INVALID_ARG);
+  CHECK(coli_host_free(nullptr) == COLI_OK);
+  CHECK(coli_host_free(fake(0x12345000)) == COLI_ERR_INVALID_ARG);
+  void *hp = nullptr;
+  CHECK(coli_host_alloc(0, &hp) == COLI_ERR_INVALID_ARG);
+
   // with no device present, a well-formed call reports a device error
   const char *vis = getenv("COLI_EXPECT_NO_DEVICE");
   if (vis && vis[0] == '1') {
     CHECK(coli_moe_forward(&good, x, 1, nullptr, y, nullptr, nullptr, nullptr, wsp, ws, nullptr) == COLI_ERR_DEVICE);
     CHECK(coli_quant_pack(4, fake<float>(16), 4, 32, fake<uint8_t>(16), fake<float>(16), nullptr) == COLI_ERR_DEVICE);
+    CHECK(coli_host_alloc(4096, &hp) == COLI_ERR_DEVICE && hp == nullptr);
   }
   printf("host api checks ok\n");
   return 0;

@@ -172,3 +172,55 @@ def test_no_device_reports_device_error():
     cfg = B.router_cfg(16, 2)
     assert L.coli_moe_route(ctypes.byref(cfg), _fake(16), None, 1, _fake(16), _fake(16), None) \
         == B.COLI_ERR_DEVICE
+
+
+def _cache_struct(E=256, S=32, state=0x400000, host=0x800000):
+    h = [_fake(host + 0x100000 * i) for i in range(6)]
+    return B.ExpertCacheC(E, S, 0, 0, *h, _fake(state))
+
+
+def test_expert_cache_layout():
+    L = B.lib()
+    lo = B.CacheLayoutC()
+    assert L.coli_expert_cache_layout_of(256, 32, ctypes.byref(lo)) == B.COLI_OK
+    offs = [lo.ctl, lo.slot_of, lo.expert_of, lo.last_use, lo.pinned, lo.use_count, lo.copy_list]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and lo.total % 256 == 0
+    assert lo.slot_of - lo.ctl >= 64 * 4
+    assert lo.expert_of - lo.slot_of >= 256 * 4 and lo.total - lo.copy_list >= 32 * 8
+    for E, S in ((0, 1), (16, 0), (16, 17), (1025, 8), (-1, -1)):
+        assert L.coli_expert_cache_layout_of(E, S, ctypes.byref(lo)) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_expert_cache_layout_of(16, 8, None) == B.COLI_ERR_INVALID_ARG
+
+
+def test_expert_cache_calls_reject_bad_arguments_before_device():
+    L = B.lib()
+    c = _cache_struct()
+    good = _layer_struct()
+    ws = L.coli_moe_workspace_bytes(ctypes.byref(good), 1)
+    x, y, wsp = _fake(0x100000), _fake(0x200000), _fake(0x300000)
+    assert L.coli_expert_cache_init(None, None) == B.COLI_ERR_INVALID_ARG
+    bad = _cache_struct(state=0x400010)  # state not 256-byte aligned
+    assert L.coli_expert_cache_init(ctypes.byref(bad), None) == B.COLI_ERR_INVALID_ARG
+    bad = _cache_struct(S=300)  # more slots than experts
+    assert L.coli_expert_cache_init(ctypes.byref(bad), None) == B.COLI_ERR_INVALID_ARG
+    # host tier outside any coli_host_alloc allocation
+    assert L.coli_moe_forward_cached(ctypes.byref(good), ctypes.byref(c), x, 1, None, y, None,
+                                     None, None, wsp, ws, None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_expert_cache_repin(ctypes.byref(c), ctypes.byref(good), 2, None) \
+        == B.COLI_ERR_INVALID_ARG
+    # expert count differing from the layer's router
+    c16 = _cache_struct(E=16, S=8)
+    assert L.coli_moe_forward_cached(ctypes.byref(good), ctypes.byref(c16), x, 1, None, y, None,
+                                     None, None, wsp, ws, None) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_host_free(None) == B.COLI_OK
+    assert L.coli_host_free(_fake(0x12345000)) == B.COLI_ERR_INVALID_ARG
+    p = ctypes.c_void_p()
+    assert L.coli_host_alloc(0, ctypes.byref(p)) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_host_alloc(64, None) == B.COLI_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_host_alloc_without_device_reports_device_error():
+    p = ctypes.c_void_p(1)
+    assert B.lib().coli_host_alloc(4096, ctypes.byref(p)) == B.COLI_ERR_DEVICE
+    assert not p.value
