@@ -191,7 +191,10 @@ def main() -> int:
     ap.add_argument("--workload", choices=list(WORKLOADS) + ["stack", "tiered", "fp8convert",
                                                           "gemvf32", "timeline"],
                     default="decode")
-    ap.add_argument("--layers", type=int, default=40, help="stack workload: layers resident")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="stack workload: layers resident (default 40); tiered workload: "
+                         "layers whose experts sit in the pinned host tier (default 12: one "
+                         "process may pin 64 GiB on the measured host, 12 x 4.84 GB)")
     ap.add_argument("--slots", type=int, default=64,
                     help="tiered workload: HBM expert slots per layer")
     ap.add_argument("--pin", type=int, default=16,
@@ -761,7 +764,7 @@ def stack_main(args) -> int:
     from quantized_moe_coli_amd import inputs, stack
 
     dev = "cuda"
-    K, W, NL = args.steps, args.warmup, args.layers
+    K, W, NL = args.steps, args.warmup, args.layers or 40
     T = max(1, args.tokens)
     t0 = time.time()
     stk = stack.build(NL)
@@ -948,7 +951,7 @@ def tiered_main(args) -> int:
     from quantized_moe_coli_amd import inputs, stack
 
     dev = "cuda"
-    K, NL, S, NP = args.steps, args.layers, args.slots, args.pin
+    K, NL, S, NP = args.steps, args.layers or 12, args.slots, args.pin
     s = stack.STACK_SHAPE
     eb = expert_bytes(s)["total"]
     tier_bytes = NL * s.n_experts * eb

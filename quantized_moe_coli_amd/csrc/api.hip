@@ -483,8 +483,8 @@ coli_status forward_impl(const coli_moe_layer *L, const CacheRun *cache, const f
                                nullptr, s);
         if (e != hipSuccess) return COLI_ERR_DEVICE;
       }
-      e = coli::launch_route(to_cfg(L->router), lp, L->gate_bias, T, idx, wts, nullptr, nullptr, s);
-      if (e == hipSuccess) e = cache_step();
+      e = coli::launch_cache_route_plan(to_cfg(L->router), lp, L->gate_bias, cache->st, s);
+      if (e == hipSuccess) e = coli::launch_cache_fill(cache->st, cache->tier, s);
       if (e != hipSuccess) return COLI_ERR_DEVICE;
       fa.loff = nullptr;
       e = coli::launch_decode_fused(fa, x, nullptr, lp, nullptr,

@@ -9,14 +9,17 @@
 //   k_cache_init  -- empties a cache's state;
 //   k_cache_plan  -- one workgroup: marks hits, ranks the misses, picks the
 //                    LRU victims among unpinned slots, updates the state in
-//                    LDS and writes it back with the list of copies;
-//   k_cache_fill  -- every workgroup: copies the listed experts' bytes from
-//                    the host tier into their slots in 32 KiB chunks (the
-//                    host link bounds it; loads of host memory issued eight
-//                    per lane so that many requests are in flight).
+//                    LDS and writes it back with the list of copies (for one
+//                    token, k_cache_route_plan also selects the experts from
+//                    the logits in the same launch);
+//   k_cache_fill  -- one workgroup per CU: copies the listed experts' bytes
+//                    from the host tier into their slots in 64 KiB chunks
+//                    (the host link bounds it; sixteen 16-byte loads of host
+//                    memory per lane are in flight at once).
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace coli {
 
@@ -25,8 +28,8 @@ namespace {
 constexpr int kPlanThreads = 256;
 constexpr int kMaxCacheE = 1024;
 constexpr int kFillThreads = 256;
-constexpr int kFillPerLane = 8;  // uint4 per lane per chunk
-constexpr size_t kFillChunk = (size_t)kFillThreads * kFillPerLane * 16;  // 32 KiB
+constexpr int kFillPerLane = 16;  // uint4 per lane per chunk
+constexpr size_t kFillChunk = (size_t)kFillThreads * kFillPerLane * 16;  // 64 KiB
 
 __global__ __launch_bounds__(256) void k_cache_init(CacheState c) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -45,150 +48,208 @@ __global__ __launch_bounds__(256) void k_cache_init(CacheState c) {
 }
 
 // Exclusive prefix sum of v over the workgroup (kPlanThreads lanes); *total
-// receives the sum.  Hillis-Steele over LDS.
-__device__ int wg_exclusive_scan(int v, int *buf, int *total) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int d = 1; d < kPlanThreads; d <<= 1) {
-    const int add = t >= d ? buf[t - d] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+// receives the sum.  Shuffle scan inside each wave, then the wave totals.
+__device__ int wg_exclusive_scan(int v, int *wave_tot, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
   }
-  const int incl = buf[t];
-  *total = buf[kPlanThreads - 1];
+  if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
-  return incl - v;
+  int base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    const int t = wave_tot[w];
+    base += w < wave ? t : 0;
+    all += t;
+  }
+  *total = all;
+  return base + incl - v;
 }
 
-// repin < 0: a forward call's update from idx[0..n_pairs-1];
-// repin >= 0: pin the `repin` most-used experts.
-__global__ __launch_bounds__(kPlanThreads) void k_cache_plan(CacheState c, const int32_t *idx,
-                                                             int n_pairs, int repin) {
-  __shared__ int s_slot_of[kMaxCacheE], s_expert_of[kMaxCacheE], s_need[kMaxCacheE];
-  __shared__ int s_mrank[kMaxCacheE], s_victim[kMaxCacheE];
-  __shared__ uint32_t s_last[kMaxCacheE], s_pin[kMaxCacheE], s_use[kMaxCacheE];
-  __shared__ int s_scan[kPlanThreads];
-  __shared__ int s_hits, s_nelig;
+// LDS image of a cache's state plus the set one call needs.
+struct PlanLds {
+  int slot_of[kMaxCacheE], expert_of[kMaxCacheE], need[kMaxCacheE];
+  int mrank[kMaxCacheE], victim[kMaxCacheE];
+  uint32_t last[kMaxCacheE], pin[kMaxCacheE], use[kMaxCacheE];
+  int wave_tot[kPlanThreads / 64];
+  int hits, nelig;
+};
+
+// Loads the state into LDS (words outside their ranges -- a state never
+// initialised -- read as absent / empty, so every LDS index stays in bounds)
+// and clears the need set.  Ends with a barrier.
+__device__ void plan_load(const CacheState &c, PlanLds &p, bool repin) {
   const int t = threadIdx.x, E = c.E, S = c.S;
-  const uint32_t clock = c.ctl[0] + 1u;
-  // state words outside their ranges (a state never initialised) read as
-  // absent / empty, so every LDS index below stays in bounds
   for (int i = t; i < E; i += kPlanThreads) {
     const int sl = c.slot_of[i];
-    s_slot_of[i] = (sl >= 0 && sl < S) ? sl : -1;
-    s_need[i] = 0;
-    s_use[i] = c.use_count[i];
+    p.slot_of[i] = (sl >= 0 && sl < S) ? sl : -1;
+    p.need[i] = 0;
+    p.use[i] = c.use_count[i];
   }
   for (int i = t; i < S; i += kPlanThreads) {
     const int ex = c.expert_of[i];
-    s_expert_of[i] = (ex >= 0 && ex < E) ? ex : -1;
-    s_last[i] = c.last_use[i];
-    s_pin[i] = repin >= 0 ? 0u : c.pinned[i];
+    p.expert_of[i] = (ex >= 0 && ex < E) ? ex : -1;
+    p.last[i] = c.last_use[i];
+    p.pin[i] = repin ? 0u : c.pinned[i];
   }
   if (t == 0) {
-    s_hits = 0;
-    s_nelig = 0;
+    p.hits = 0;
+    p.nelig = 0;
   }
   __syncthreads();
+}
 
-  // the set this call needs: selected experts (with their pair counts), or
-  // the `repin` most-used ones, ranked by (use_count desc, expert asc)
-  if (repin < 0) {
-    for (int i = t; i < n_pairs; i += kPlanThreads) {
-      const int e = idx[i];
-      if (e >= 0 && e < E) atomicAdd(&s_need[e], 1);
-    }
-  } else {
-    for (int e = t; e < E; e += kPlanThreads) {
-      const uint32_t u = s_use[e];
-      int r = 0;
-      for (int e2 = 0; e2 < E; ++e2) {
-        const uint32_t u2 = s_use[e2];
-        r += (u2 > u) || (u2 == u && e2 < e);
-      }
-      s_need[e] = r < repin ? 1 : 0;
-    }
-  }
-  __syncthreads();
+// The replacement once p.need holds the call's set (pair counts, or 1 for
+// a repin's chosen experts): hits touch their slots, misses take the LRU
+// unpinned slots this call does not use, the state and the copy list are
+// written back.  Called by the whole workgroup after a barrier.
+__device__ void plan_core(const CacheState &c, PlanLds &p, bool repin) {
+  const int t = threadIdx.x, E = c.E, S = c.S;
+  const uint32_t clock = c.ctl[0] + 1u;
 
   // hits: touch their slots; usage learned from the routed pairs
   int hits = 0;
   for (int e = t; e < E; e += kPlanThreads) {
-    const int n = s_need[e];
+    const int n = p.need[e];
     if (!n) continue;
-    if (repin < 0) c.use_count[e] = s_use[e] + (uint32_t)n;
-    const int sl = s_slot_of[e];
+    if (!repin) c.use_count[e] = p.use[e] + (uint32_t)n;
+    const int sl = p.slot_of[e];
     if (sl >= 0) {
-      s_last[sl] = clock;
+      p.last[sl] = clock;
       ++hits;
     }
   }
-  if (hits) atomicAdd(&s_hits, hits);
+  if (hits) atomicAdd(&p.hits, hits);
   __syncthreads();
 
   // misses ranked in increasing expert order (each lane scans a contiguous run)
   const int per = (E + kPlanThreads - 1) / kPlanThreads;
   const int e0 = t * per, e1 = min(E, e0 + per);
   int local = 0;
-  for (int e = e0; e < e1; ++e) local += (s_need[e] && s_slot_of[e] < 0);
+  for (int e = e0; e < e1; ++e) local += (p.need[e] && p.slot_of[e] < 0);
   int n_miss = 0;
-  int r = wg_exclusive_scan(local, s_scan, &n_miss);
-  for (int e = e0; e < e1; ++e) s_mrank[e] = (s_need[e] && s_slot_of[e] < 0) ? r++ : -1;
+  int r = wg_exclusive_scan(local, p.wave_tot, &n_miss);
+  for (int e = e0; e < e1; ++e) p.mrank[e] = (p.need[e] && p.slot_of[e] < 0) ? r++ : -1;
 
   // victims: unpinned slots not used by this call, in (last_use, slot) order
-  for (int s = t; s < S; s += kPlanThreads) {
-    const bool el = !s_pin[s] && s_last[s] < clock;
-    if (!el) continue;
-    atomicAdd(&s_nelig, 1);
-    const uint32_t ls = s_last[s];
-    int rank = 0;
-    for (int s2 = 0; s2 < S; ++s2) {
-      const uint32_t l2 = s_last[s2];
-      rank += (!s_pin[s2] && l2 < clock) && (l2 < ls || (l2 == ls && s2 < s));
+  if (n_miss > 0) {
+    for (int s = t; s < S; s += kPlanThreads) {
+      const bool el = !p.pin[s] && p.last[s] < clock;
+      if (!el) continue;
+      atomicAdd(&p.nelig, 1);
+      const uint32_t ls = p.last[s];
+      int rank = 0;
+      for (int s2 = 0; s2 < S; ++s2) {
+        const uint32_t l2 = p.last[s2];
+        rank += (!p.pin[s2] && l2 < clock) && (l2 < ls || (l2 == ls && s2 < s));
+      }
+      if (rank < n_miss) p.victim[rank] = s;
     }
-    if (rank < n_miss) s_victim[rank] = s;
   }
   __syncthreads();
-  const int n_copy = min(n_miss, s_nelig);
+  const int n_copy = min(n_miss, p.nelig);
 
   // move the misses in; evicted experts become absent
   for (int e = t; e < E; e += kPlanThreads) {
-    const int m = s_mrank[e];
+    const int m = p.mrank[e];
     if (m < 0 || m >= n_copy) continue;
-    const int s = s_victim[m];
-    const int old = s_expert_of[s];
-    if (old >= 0) s_slot_of[old] = -1;
-    s_slot_of[e] = s;
-    s_expert_of[s] = e;
-    s_last[s] = clock;
+    const int s = p.victim[m];
+    const int old = p.expert_of[s];
+    if (old >= 0) p.slot_of[old] = -1;
+    p.slot_of[e] = s;
+    p.expert_of[s] = e;
+    p.last[s] = clock;
     c.copy_list[2 * m] = e;
     c.copy_list[2 * m + 1] = s;
   }
   __syncthreads();
-  if (repin >= 0) {
+  if (repin) {
     for (int e = t; e < E; e += kPlanThreads)
-      if (s_need[e] && s_slot_of[e] >= 0) s_pin[s_slot_of[e]] = 1u;
+      if (p.need[e] && p.slot_of[e] >= 0) p.pin[p.slot_of[e]] = 1u;
     __syncthreads();
   }
 
-  for (int i = t; i < E; i += kPlanThreads) c.slot_of[i] = s_slot_of[i];
+  for (int i = t; i < E; i += kPlanThreads) c.slot_of[i] = p.slot_of[i];
   for (int i = t; i < S; i += kPlanThreads) {
-    c.expert_of[i] = s_expert_of[i];
-    c.last_use[i] = s_last[i];
-    c.pinned[i] = s_pin[i];
+    c.expert_of[i] = p.expert_of[i];
+    c.last_use[i] = p.last[i];
+    c.pinned[i] = p.pin[i];
   }
   if (t == 0) {
     c.ctl[0] = clock;
     c.ctl[1] = (uint32_t)n_copy;
     if (n_miss > n_copy) c.ctl[2] |= 1u;
-    if (repin < 0) {
+    if (!repin) {
       unsigned long long *st = reinterpret_cast<unsigned long long *>(c.ctl + 4);
-      st[0] += (unsigned long long)s_hits;
+      st[0] += (unsigned long long)p.hits;
       st[1] += (unsigned long long)n_miss;
     }
   }
+}
+
+// repin < 0: a forward call's update from idx[0..n_pairs-1];
+// repin >= 0: pin the `repin` most-used experts, ranked by (use_count
+// desc, expert asc).
+__global__ __launch_bounds__(kPlanThreads) void k_cache_plan(CacheState c, const int32_t *idx,
+                                                             int n_pairs, int repin) {
+  __shared__ PlanLds p;
+  const int t = threadIdx.x, E = c.E;
+  plan_load(c, p, repin >= 0);
+  if (repin < 0) {
+    for (int i = t; i < n_pairs; i += kPlanThreads) {
+      const int e = idx[i];
+      if (e >= 0 && e < E) atomicAdd(&p.need[e], 1);
+    }
+  } else {
+    for (int e = t; e < E; e += kPlanThreads) {
+      const uint32_t u = p.use[e];
+      int r = 0;
+      for (int e2 = 0; e2 < E; ++e2) {
+        const uint32_t u2 = p.use[e2];
+        r += (u2 > u) || (u2 == u && e2 < e);
+      }
+      p.need[e] = r < repin ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  plan_core(c, p, repin >= 0);
+}
+
+// One token: its routing from the logits (the same selection, bit for bit,
+// as every other path of the library) and the cache update in one launch.
+__global__ __launch_bounds__(kPlanThreads) void k_cache_route_plan(RouterCfg cfg,
+                                                                   const float *__restrict__ logits,
+                                                                   const float *__restrict__ bias,
+                                                                   CacheState c) {
+  __shared__ PlanLds p;
+  __shared__ SelInput in;
+  __shared__ union {
+    SelFastScratch fast;
+    SelWgScratch wg;
+  } sel;
+  __shared__ int32_t sidx[kSelMaxK];
+  __shared__ float sw[kSelMaxK];
+  const int t = threadIdx.x, E = cfg.E;
+  for (int e = t; e < E; e += kPlanThreads) {
+    const float sg = sigmoid_f64(logits[e]);
+    in.sg[e] = sg;
+    in.c[e] = sg + (bias ? bias[e] : 0.f);
+  }
+  plan_load(c, p, false);  // ends with a barrier
+  if (select_fast_ok(E, cfg.n_group, cfg.topk_group, cfg.k, kPlanThreads))
+    select_fast<kPlanThreads>(cfg, in, sel.fast, sidx, sw);
+  else
+    select_wg<kPlanThreads>(cfg, in, sel.wg, sidx, sw);
+  if (t < cfg.k) {
+    const int e = sidx[t];
+    if (e >= 0 && e < E) atomicAdd(&p.need[e], 1);
+  }
+  __syncthreads();
+  plan_core(c, p, false);
 }
 
 // One expert's six tensors, in the order the chunks walk them.
@@ -269,13 +330,21 @@ hipError_t launch_cache_plan(const CacheState &c, const int32_t *idx, int n_pair
   return hipGetLastError();
 }
 
+hipError_t launch_cache_route_plan(const RouterCfg &cfg, const float *logits, const float *bias,
+                                   const CacheState &c, hipStream_t st) {
+  if (c.E < 1 || c.E > kMaxCacheE || c.S < 1 || c.S > c.E || cfg.E != c.E || cfg.k > kSelMaxK)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_cache_route_plan, dim3(1), dim3(kPlanThreads), 0, st, cfg, logits, bias, c);
+  return hipGetLastError();
+}
+
 hipError_t launch_cache_fill(const CacheState &c, const CacheTier &t, hipStream_t st) {
   int dev = 0, n_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       n_cu <= 0)
     n_cu = 256;
-  hipLaunchKernelGGL(k_cache_fill, dim3(n_cu * 4), dim3(kFillThreads), 0, st, c, t);
+  hipLaunchKernelGGL(k_cache_fill, dim3(n_cu), dim3(kFillThreads), 0, st, c, t);
   return hipGetLastError();
 }
 

@@ -81,6 +81,10 @@ hipError_t launch_cache_init(const CacheState &c, hipStream_t st);
 // the `repin` most-used experts.
 hipError_t launch_cache_plan(const CacheState &c, const int32_t *idx, int n_pairs, int repin,
                              hipStream_t st);
+// One token: selection from its logits (as every other path selects) and the
+// cache update, in one launch.
+hipError_t launch_cache_route_plan(const RouterCfg &cfg, const float *logits, const float *bias,
+                                   const CacheState &c, hipStream_t st);
 hipError_t launch_cache_fill(const CacheState &c, const CacheTier &t, hipStream_t st);
 
 // Union bookkeeping living in the workspace.

@@ -132,7 +132,13 @@ def build_tiered(n_layers: int, n_slots: int, s: inputs.Shape = STACK_SHAPE,
         L.pack_expert(s.n_experts, g, u, d)
         del g, u, d
         torch.cuda.synchronize()
-        tier = B.HostTier(s.n_experts, s.hidden, s.inter, s.bits)
+        try:
+            tier = B.HostTier(s.n_experts, s.hidden, s.inter, s.bits)
+        except B.ColiError as e:
+            pinned = sum(c.tier.buf.nbytes for c in caches)
+            raise RuntimeError(f"pinned host allocation failed after {li} layers "
+                               f"({pinned / 1e9:.1f} GB pinned): the host limits pinned "
+                               f"memory per process; build fewer layers") from e
         tier.load_experts(staging)
         cache = B.ExpertCache(tier, n_slots, device)
         cache.init()
