@@ -188,17 +188,21 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--instances", type=int, default=8)
-    ap.add_argument("--workload", choices=list(WORKLOADS) + ["stack", "tiered", "fp8convert",
-                                                          "gemvf32", "timeline"],
+    ap.add_argument("--workload", choices=list(WORKLOADS) + ["stack", "tiered", "guard",
+                                                          "fp8convert", "gemvf32", "timeline"],
                     default="decode")
     ap.add_argument("--layers", type=int, default=None,
                     help="stack workload: layers resident (default 40); tiered workload: "
                          "layers whose experts sit in the pinned host tier (default 12: one "
                          "process may pin 64 GiB on the measured host, 12 x 4.84 GB)")
-    ap.add_argument("--slots", type=int, default=64,
-                    help="tiered workload: HBM expert slots per layer")
+    ap.add_argument("--slots", type=int, default=None,
+                    help="tiered workload: HBM expert slots per layer (default 64); guard "
+                         "workload: run on the tiered stack with this many slots")
     ap.add_argument("--pin", type=int, default=16,
                     help="tiered workload: slots per layer pinned from the learned usage")
+    ap.add_argument("--accept", type=str, default="0.3,0.6,0.9",
+                    help="guard workload: per-draft acceptance rates to simulate")
+    ap.add_argument("--draft", type=int, default=2, help="guard workload: drafts per verify")
     ap.add_argument("--bits", type=int, choices=(8, 4, 2), default=None,
                     help="weight container of the GLM-5.2-shaped layer (default int4)")
     ap.add_argument("--mfma-min", type=int, default=0,
@@ -234,6 +238,8 @@ def main() -> int:
         return stack_main(args)
     if args.workload == "tiered":
         return tiered_main(args)
+    if args.workload == "guard":
+        return guard_main(args)
     if args.workload == "fp8convert":
         return fp8_main(args)
     if args.workload == "gemvf32":
@@ -951,7 +957,7 @@ def tiered_main(args) -> int:
     from quantized_moe_coli_amd import inputs, stack
 
     dev = "cuda"
-    K, NL, S, NP = args.steps, args.layers or 12, args.slots, args.pin
+    K, NL, S, NP = args.steps, args.layers or 12, args.slots or 64, args.pin
     s = stack.STACK_SHAPE
     eb = expert_bytes(s)["total"]
     tier_bytes = NL * s.n_experts * eb
@@ -1085,6 +1091,132 @@ def tiered_main(args) -> int:
             "bytes_per_launch": int((S - 1) * eb),
             "avg_launch_us": round(cal_ms * 1e3, 1),
         },
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def guard_main(args) -> int:
+    """The adaptive speculation guard on the stack decode.  A step either
+    decodes one token or verifies it with --draft drafts in one batch (one
+    batch union per layer); acceptance is simulated (seeded, per-draft rate
+    --accept, a draft counts only if every earlier one was accepted), since
+    the drafts' content needs the trained model.  Three policies per rate --
+    never draft, always draft, the guard fed each step's measured GPU time --
+    over the same --steps from the same start.  With --slots the stack is
+    the tiered one (12 layers over pinned host memory, caches emptied before
+    each policy: the cold start the guard exists for); else --layers resident
+    layers."""
+    import numpy as np
+    import torch
+
+    from quantized_moe_coli_amd import binding as B
+    from quantized_moe_coli_amd import inputs, stack
+
+    dev = "cuda"
+    K, D = args.steps, args.draft
+    tiered = args.slots is not None and args.slots > 0
+    rates = [float(v) for v in args.accept.split(",")]
+    t0 = time.time()
+    if tiered:
+        NL = args.layers or 12
+        st = stack.build_tiered(NL, args.slots, log=log)
+        step_fn = lambda h, ws, y, idx: stack.step_tiered(st, h, ws, y, idx)  # noqa: E731
+    else:
+        NL = args.layers or 40
+        st = stack.build(NL)
+        step_fn = lambda h, ws, y, idx: stack.step(st, h, ws, y, idx)  # noqa: E731
+    s = st.s
+    log(f"[bench] guard: {NL} layers {'tiered, ' + str(args.slots) + ' slots' if tiered else 'resident'}"
+        f", built in {time.time() - t0:.1f}s")
+    graphs, bufs = {}, {}
+    for T in (1, 1 + D):
+        ws = B.workspace(st.layers[0], T)
+        h = torch.empty(T, s.hidden, device=dev)
+        y = torch.empty(T, s.hidden, device=dev)
+        idx = torch.empty(NL, T, s.top_k, dtype=torch.int32, device=dev)
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                step_fn(h, ws, y, idx)
+        torch.cuda.synchronize()
+        # the graph reads and writes these: they live as long as it does
+        graphs[T], bufs[T] = g, (h, idx, ws, y)
+    xs = {T: torch.stack([inputs.tokens(s, stack.token_seed(), t, T, dev) for t in range(K)])
+          for T in (1, 1 + D)}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(policy, rate):
+        if tiered:
+            for c in st.caches:
+                c.init()
+            torch.cuda.synchronize()
+        rng = np.random.default_rng(1234)
+        guard = B.SpecGuard(D, probe_every=16, ema=0.25) if policy == "guard" else None
+        produced, total_ms, reads, drafted_steps, miss0 = 0, 0.0, 0, 0, 0
+        if tiered:
+            miss0 = sum(c.stats()["misses"] for c in st.caches)
+        for t in range(K):
+            d = D if policy == "always" else 0 if policy == "never" else guard.next_draft
+            T = 1 + d
+            h, idx = bufs[T][:2]
+            h.copy_(xs[T][t])
+            e0.record()
+            graphs[T].replay()
+            e1.record()
+            e1.synchronize()
+            ms = e0.elapsed_time(e1)
+            acc = 0
+            while acc < d and rng.random() < rate:
+                acc += 1
+            if guard is not None:
+                guard.step(d, acc, ms * 1e3)
+            produced += 1 + acc
+            total_ms += ms
+            drafted_steps += 1 if d else 0
+            ix = idx.cpu().numpy()
+            reads += sum(len(set(ix[li][ix[li] >= 0].tolist())) + 1 for li in range(NL))
+        out = {"tokens_per_s": round(produced / (total_ms / 1e3), 2),
+               "tokens_per_step": round(produced / K, 3),
+               "expert_reads_per_token": round(reads / produced, 2),
+               "draft_fraction": round(drafted_steps / K, 3)}
+        if tiered:
+            miss = sum(c.stats()["misses"] for c in st.caches) - miss0
+            out["host_link_gb_per_token"] = round(miss * expert_bytes(s)["total"] / produced / 1e9, 4)
+        return out
+
+    table = {}
+    for rate in rates:
+        table[str(rate)] = {p: run(p, rate) for p in ("never", "always", "guard")}
+        log(f"[bench] guard, acceptance {rate}: {table[str(rate)]}")
+    mid = table[str(rates[len(rates) // 2])]
+    result = {
+        "metric": ("MoE-stack tokens/s under the adaptive speculation guard "
+                   f"({NL} int4 layers, Zipf popularity, expert top-p 0.7, {D} drafts per verify)"),
+        "value": mid["guard"]["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": 0,
+        "ms_per_step": round(1e3 * mid["guard"]["tokens_per_step"] / mid["guard"]["tokens_per_s"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4xint8->int32,fp32-scale",
+        "data": "synthetic (acceptance simulated at the stated per-draft rates)",
+        "config": {
+            "workload": f"{NL} GLM-5.2-shaped routed-MoE layers ("
+                        + (f"tiered: {args.slots} HBM slots per layer over pinned host memory, "
+                           "caches emptied before each policy" if tiered else "resident")
+                        + "); each step decodes one token or verifies it with "
+                        f"{D} drafts as one {1 + D}-token batch union per layer; one HIP graph "
+                        "per batch size; policies never / always / guard (per-step GPU time "
+                        "as the cost, probe every 16 steps, weight 0.25)",
+            "value_rate": rates[len(rates) // 2],
+        },
+        "policies": table,
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -17,8 +17,10 @@
  * Memory: every data pointer is a DEVICE pointer on the current HIP device
  * unless marked "host".  The caller allocates and owns every buffer and keeps
  * it alive until the stream work that uses it has finished; the library
- * allocates nothing and keeps no per-call state, so calls on different
- * streams may run concurrently when their buffers are disjoint.
+ * allocates only when asked to (coli_host_alloc) and keeps no per-call
+ * state, so calls on different streams may run concurrently when their
+ * buffers are disjoint (an expert cache's calls excepted: they share the
+ * cache's state).
  *
  * Streams: `stream` is a hipStream_t passed as a plain pointer (NULL = the
  * null stream).  Every call only enqueues work on it and returns; outputs are
@@ -420,6 +422,48 @@ coli_status coli_moe_forward_cached(const coli_moe_layer *L,
                                     float *y, int32_t *idx_out, float *w_out,
                                     float *logits_out, void *workspace,
                                     size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Adaptive speculation guard.  Verifying the MTP head's drafts in one batch
+ * makes every draft route to more experts; on a cold cache the extra expert
+ * loads can cost more than the accepted drafts save, which is why the pages
+ * pair drafting with an adaptive guard and a DRAFT=0 switch (colibrì README,
+ * "Implemented features", native MTP item; "Quick start": DRAFT=n).
+ *
+ * A host-side controller (no device work).  After every step the caller
+ * reports the drafts it verified, how many were accepted and the step's
+ * cost (any additive measure: microseconds, expert bytes read, host-link
+ * bytes).  The guard keeps, per mode, exponentially weighted sums of the
+ * cost and of the tokens produced (1 + accepted per step); their ratio is
+ * that mode's cost per produced token (a ratio of averages: an average of
+ * per-step ratios would overrate drafting's cost when acceptance varies
+ * from step to step).  It answers
+ * the drafts for the next step: max_draft while the drafting estimate is at
+ * most (1 + margin) times the plain one, else 0.  Every probe_every steps it
+ * runs one step in the mode not in use, so both estimates stay current
+ * (the cache warming up makes drafting pay again).  Unknown estimates:
+ * drafting starts on and the first probe measures plain decode.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t max_draft;   /* drafts per step while drafting (DRAFT=n), >= 1 */
+  int32_t probe_every; /* steps between probes of the other mode, >= 2 */
+  float ema;           /* weight of the newest step in the estimates, (0, 1] */
+  float margin;        /* drafting kept while cost_draft <= cost_plain * (1 + margin) */
+  /* state, written by init and step */
+  double cost_draft, cost_plain; /* per produced token; negative: not yet measured */
+  double sum_cost[2], sum_tokens[2]; /* weighted sums, [0] plain, [1] drafting */
+  int32_t next_draft;            /* drafts the next step should verify */
+  int32_t since_probe;           /* steps since the last probe */
+  int64_t steps, draft_steps, tokens;
+} coli_spec_guard;
+
+coli_status coli_spec_guard_init(coli_spec_guard *g, int32_t max_draft,
+                                 int32_t probe_every, float ema, float margin);
+/* Records one step (drafted in 0..max_draft, accepted in 0..drafted, cost
+ * >= 0) and returns the drafts for the next step (also in g->next_draft);
+ * a malformed report returns -1 and changes nothing. */
+int32_t coli_spec_guard_step(coli_spec_guard *g, int32_t drafted,
+                             int32_t accepted, double cost);
 
 /* Status of the decode path's bounded waits (library plumbing, not a step
  * of the pages' layer; it reports when the outputs of coli_moe_forward are

@@ -57,6 +57,16 @@ class ExpertCacheC(ctypes.Structure):
                 ("state", _P)]
 
 
+class SpecGuardC(ctypes.Structure):
+    _fields_ = [("max_draft", ctypes.c_int32), ("probe_every", ctypes.c_int32),
+                ("ema", ctypes.c_float), ("margin", ctypes.c_float),
+                ("cost_draft", ctypes.c_double), ("cost_plain", ctypes.c_double),
+                ("sum_cost", ctypes.c_double * 2), ("sum_tokens", ctypes.c_double * 2),
+                ("next_draft", ctypes.c_int32), ("since_probe", ctypes.c_int32),
+                ("steps", ctypes.c_int64), ("draft_steps", ctypes.c_int64),
+                ("tokens", ctypes.c_int64)]
+
+
 class CacheLayoutC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("ctl", "slot_of", "expert_of", "last_use", "pinned", "use_count", "copy_list",
@@ -123,6 +133,9 @@ def _load(path: str) -> ctypes.CDLL:
                                      _P], ctypes.c_int),
         "coli_moe_forward_cached": ([ctypes.POINTER(MoeLayerC), ctypes.POINTER(ExpertCacheC), _P,
                                      i32, _P, _P, _P, _P, _P, _P, sz, _P], ctypes.c_int),
+        "coli_spec_guard_init": ([ctypes.POINTER(SpecGuardC), i32, i32, ctypes.c_float,
+                                  ctypes.c_float], ctypes.c_int),
+        "coli_spec_guard_step": ([ctypes.POINTER(SpecGuardC), i32, i32, ctypes.c_double], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -594,3 +607,24 @@ def coli_moe_forward_cached(layer: MoeLayer, cache: ExpertCache, x: torch.Tensor
         _ptr(idx_out, torch.int32, "idx_out"), _ptr(w_out, torch.float32, "w_out"),
         _ptr(logits_out, torch.float32, "logits_out"), ctypes.c_void_p(ws.data_ptr()),
         ws.numel(), _stream(stream)))
+
+
+class SpecGuard:
+    """The adaptive speculation guard (coli_spec_guard_*): report each step,
+    get the drafts for the next one."""
+
+    def __init__(self, max_draft: int, probe_every: int = 16, ema: float = 0.25,
+                 margin: float = 0.0):
+        self.c = SpecGuardC()
+        _check("coli_spec_guard_init", lib().coli_spec_guard_init(
+            ctypes.byref(self.c), max_draft, probe_every, ema, margin))
+
+    @property
+    def next_draft(self) -> int:
+        return self.c.next_draft
+
+    def step(self, drafted: int, accepted: int, cost: float) -> int:
+        r = lib().coli_spec_guard_step(ctypes.byref(self.c), drafted, accepted, float(cost))
+        if r < 0:
+            raise ValueError("malformed guard report")
+        return r

@@ -586,14 +586,18 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
   // later tickets come from the queue's counter, offset by nq.
   const int q = blockIdx.x % kQueues;
   const int nq = ((int)gridDim.x - q + kQueues - 1) / kQueues;
+  // A counter value past the queue's items (a header the caller did not
+  // zero) ends the loop: the item index is formed in 64 bits and clamped,
+  // so no value of the header can yield an index outside [0, total].
   auto next_ticket = [&]() -> int {
     if (threadIdx.x == 0)
       s_ticket = (int)__hip_atomic_fetch_add(d.ctr + kCtrTicket + q * kCtrStride, 1u,
                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const int t = q + kQueues * (nq + uniform_i32(s_ticket));
+    const uint32_t tk = (uint32_t)uniform_i32(s_ticket);
+    const long long tt = (long long)q + (long long)kQueues * ((long long)nq + (long long)tk);
     __syncthreads();
-    return t;
+    return tt < (long long)d.total ? (int)tt : d.total;
   };
 
   int trn = 0;

@@ -530,6 +530,31 @@ def test_decode_wait_giveup_is_reported(glm):
     assert _ws_status(ws) == 0
 
 
+def test_decode_garbage_ticket_counters_stay_in_bounds(glm):
+    """A workspace whose work-queue counters hold garbage (a caller that let
+    the memory be reused: nonzero words, values with the sign bit set, float
+    bit patterns) must not make the decode kernel index outside its items:
+    the call completes, its last workgroup clears the header, and the next
+    call is bit-identical to one on a fresh workspace.  Only the eight ticket
+    words are planted; the polling bound and status words stay zero."""
+    x = inputs.tokens(glm.s, 0, 9, 1, "cuda")
+    ref = glm.gpu_forward(x)
+    ws = B.workspace(glm.gpu, 1)
+    words = ws[:B.WORKSPACE_COUNTER_BYTES].view(torch.int32)
+    garbage = [0x3F800000, -0x40800000, 0x7FFFFFFF, -1, -0x80000000, 1, 0x40000000, -0x21524111]
+    for q, v in enumerate(garbage):
+        words[64 * q] = v  # queue q's ticket counter (one 256-byte line per counter)
+    torch.cuda.synchronize()
+    glm.gpu_forward(x, ws=ws)  # outputs undefined: items were skipped
+    torch.cuda.synchronize()
+    hdr = ws[:B.WORKSPACE_COUNTER_BYTES].cpu().numpy()
+    assert (hdr == 0).all()
+    b = glm.gpu_forward(x, ws=ws)
+    for u, v in zip(b, ref):
+        np.testing.assert_array_equal(u, v)
+    assert _ws_status(ws) == 0
+
+
 # The full-size layer (256 experts, computed logits) in the int8 and int2
 # containers at batch 1, 8 and 64 (the int4 container is covered above): the
 # precision-by-batch grid.  Routing of every token is checked; outputs for

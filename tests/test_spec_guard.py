@@ -1,0 +1,93 @@
+"""The adaptive speculation guard (host logic, coli_spec_guard_*), against
+the policy include/coli_moe.h states: per-mode moving estimates of the cost
+per produced token, the cheaper mode runs, the other is probed every
+probe_every steps."""
+import ctypes
+
+import pytest
+
+from quantized_moe_coli_amd import binding as B
+
+
+def drive(g, cost_of, accept_of, n):
+    """Run n steps; cost_of(step, drafted) and accept_of(step, drafted) give
+    the report; returns the drafts chosen before each step."""
+    chosen = []
+    for t in range(n):
+        d = g.next_draft
+        chosen.append(d)
+        g.step(d, accept_of(t, d), cost_of(t, d))
+    return chosen
+
+
+def test_drafting_that_does_not_pay_is_turned_off():
+    # verify of 1 + 2 drafts reads ~2.5x the experts of one token, and only
+    # one in five drafts is accepted: 2.5 / 1.2 > 1 per token
+    g = B.SpecGuard(2, probe_every=10, ema=0.3)
+    chosen = drive(g, lambda t, d: 2.5 if d else 1.0, lambda t, d: 1 if (d and t % 5 == 0) else 0, 200)
+    assert all(c == 2 for c in chosen[:9])  # drafting is on until the first probe
+    tail = chosen[20:]
+    assert sum(1 for c in tail if c) <= len(tail) // 10 + 1  # only the probes draft
+    assert g.c.cost_draft > g.c.cost_plain
+    assert g.c.steps == 200 and g.c.draft_steps == sum(1 for c in chosen if c)
+
+
+def test_drafting_that_pays_stays_on():
+    # every draft accepted: 2.5 / 3 < 1 per token
+    g = B.SpecGuard(2, probe_every=10, ema=0.3)
+    chosen = drive(g, lambda t, d: 2.5 if d else 1.0, lambda t, d: d, 200)
+    tail = chosen[20:]
+    assert sum(1 for c in tail if c == 0) <= len(tail) // 10 + 1  # only the probes are plain
+    assert g.c.tokens == sum(1 + c for c in chosen)
+
+
+def test_guard_turns_drafting_back_on_once_the_cache_warms():
+    # cold: a draft step costs 6 (misses), warm from step 80 on: 2
+    g = B.SpecGuard(2, probe_every=8, ema=0.5)
+    cost = lambda t, d: (6.0 if t < 80 else 2.0) if d else 2.0  # noqa: E731
+    chosen = drive(g, cost, lambda t, d: 1 if d else 0, 200)
+    assert sum(1 for c in chosen[30:80] if c) <= 50 // 8 + 1  # off while cold
+    assert sum(1 for c in chosen[110:200] if c == 0) <= 90 // 8 + 1  # back on; plain only as probes
+    first_on = next(t for t in range(80, 200) if all(chosen[t:t + 4]))
+    assert first_on <= 80 + 2 * 8
+
+
+def test_margin_keeps_drafting_when_slightly_dearer():
+    g = B.SpecGuard(1, probe_every=6, ema=1.0, margin=0.5)
+    chosen = drive(g, lambda t, d: 2.6 if d else 1.0, lambda t, d: d, 60)  # 1.3 per token
+    assert sum(1 for c in chosen[12:] if c == 0) <= 48 // 6 + 1
+    g = B.SpecGuard(1, probe_every=6, ema=1.0, margin=0.2)
+    chosen = drive(g, lambda t, d: 2.6 if d else 1.0, lambda t, d: d, 60)
+    assert sum(1 for c in chosen[12:] if c) <= 48 // 6 + 1
+
+
+def test_malformed_reports_and_arguments():
+    L = B.lib()
+    g = B.SpecGuardC()
+    assert L.coli_spec_guard_init(None, 2, 8, 0.5, 0.0) == B.COLI_ERR_INVALID_ARG
+    for args in ((0, 8, 0.5, 0.0), (2, 1, 0.5, 0.0), (2, 8, 0.0, 0.0), (2, 8, 1.5, 0.0),
+                 (2, 8, 0.5, -0.1), (2, 8, float("nan"), 0.0)):
+        assert L.coli_spec_guard_init(ctypes.byref(g), *args) == B.COLI_ERR_INVALID_ARG
+    assert L.coli_spec_guard_init(ctypes.byref(g), 2, 8, 0.5, 0.0) == B.COLI_OK
+    before = bytes(g)
+    for rep in ((3, 0, 1.0), (-1, 0, 1.0), (2, 3, 1.0), (1, -1, 1.0), (1, 0, -1.0),
+                (1, 0, float("inf")), (1, 0, float("nan"))):
+        assert L.coli_spec_guard_step(ctypes.byref(g), *rep) == -1
+    assert bytes(g) == before
+    assert L.coli_spec_guard_step(None, 0, 0, 1.0) == -1
+    with pytest.raises(ValueError):
+        B.SpecGuard(2).step(5, 0, 1.0)
+
+
+def test_cost_per_token_is_a_ratio_of_averages():
+    # acceptance varies from step to step: 0, 1 or 2 of 2 drafts; a verify
+    # step costs 4.4 and a plain one 2.05 (the resident stack's timings at
+    # 0.9 acceptance): 4.4 / E[1 + accepted] = 1.62 < 2.05, so drafting pays
+    # even though some single steps cost 4.4 per token
+    pattern = [2, 2, 2, 0, 2, 2, 1, 2, 2, 2]  # mean 1.7 accepted of 2
+    g = B.SpecGuard(2, probe_every=16, ema=0.25)
+    chosen = drive(g, lambda t, d: 4.4 if d else 2.05,
+                   lambda t, d: min(d, pattern[t % len(pattern)]), 320)
+    assert abs(g.c.cost_draft - 4.4 / 2.7) < 0.35
+    tail = chosen[40:]
+    assert sum(1 for c in tail if c == 0) <= len(tail) // 16 + 1
