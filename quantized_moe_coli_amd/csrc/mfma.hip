@@ -20,7 +20,7 @@
 // (the container ordering of coli_quant_act_q8_0's forward copy); the int32
 // results are shifted back exactly.
 //
-// Work items: a (union slot, token group of 64, 64-row block) each; the
+// Work items: a (union slot, token group of 64, 128-row block) each; the
 // item table (prefix of token groups over the slots that run here) is built
 // on the device after the dispatch tables, so the grid is a host-side upper
 // bound and surplus workgroups exit at once.
@@ -33,8 +33,11 @@ namespace coli {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaRows = 64;  // weight rows per workgroup (16 per wave)
+constexpr int kMfmaRows = 128;  // weight rows per workgroup (16 per wave)
 constexpr int kMfmaTiles = kMfmaTokens / 16;
+constexpr int kMfmaThreads = 512;  // threads per workgroup (8 waves)
+constexpr int kMfmaWaves = kMfmaThreads / 64;
+constexpr int kStages = 3;         // LDS ring: two stages in flight while one is multiplied
 
 // Tokens a union slot sends to the matrix cores (0: the dot-product path
 // takes it).
@@ -121,7 +124,16 @@ constexpr int wshift() {
   return BITS == 8 ? 0 : BITS == 4 ? 4 : 6;
 }
 
-// The work item of this workgroup: union slot, token group, and row block.
+// ---------------------------------------------------------------------------
+// Work items: (union slot, token group of up to 64, block of weight rows),
+// numbered G * n_rb + rb over the token groups G of the slots that run here
+// (mgofs), one per workgroup; the hardware hands each CU the next workgroup
+// as soon as one finishes, which balances items of unequal cost.  Workgroup
+// b takes item n_items - 1 - b: the shared expert's groups (the last slot,
+// a full 64 tokens each when it runs here) start first instead of forming
+// the tail.  Items of one (slot, row block) with several token groups are
+// n_rb apart, so their re-reads of the weights run at about the same time.
+// ---------------------------------------------------------------------------
 struct MfmaItem {
   int e;      // expert (-1: shared)
   TokList s;  // the slot's tokens
@@ -130,11 +142,13 @@ struct MfmaItem {
 };
 
 __device__ __forceinline__ bool mfma_item(const FfnArgs &a, int n_rb, MfmaItem &it) {
-  const int G = blockIdx.x / n_rb;
-  it.rb = blockIdx.x % n_rb;
   const int nu = *a.disp.n_uniq;
   const int32_t *gofs = a.disp.mgofs;
-  if (G >= gofs[nu + 1]) return false;
+  const int n_items = gofs[nu + 1] * n_rb;
+  if ((int)blockIdx.x >= n_items) return false;
+  const int i = n_items - 1 - (int)blockIdx.x;
+  const int G = i / n_rb;
+  it.rb = i % n_rb;
   int lo = 0, hi = nu;  // last slot whose first group is <= G
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -153,246 +167,356 @@ __device__ __forceinline__ bool mfma_item(const FfnArgs &a, int n_rb, MfmaItem &
 }
 
 // ---------------------------------------------------------------------------
-// The block-scaled int8 GEMM core shared by both kernels.  A workgroup of 4
-// waves multiplies NMAT weight matrices (16 rows per wave each) by up to 64
-// token rows of Q8_0 codes, over K in chunks of CH blocks of 32.  Each chunk
-// is loaded with 16-byte coalesced loads into registers one chunk ahead,
-// stored to LDS, then read back in the MFMA operand layout (a 16-byte load
-// per lane of a weight row holds whole blocks, while an operand holds a
-// quarter block of each of 16 rows, so the reshuffle goes through LDS).
-// acc[m][tt][r]: matrix m, token tile tt, row 4 g + r of the wave, token
-// 16 tt + li (lane = 16 g + li).
+// The block-scaled int8 GEMM core shared by both kernels.  A workgroup of 8
+// waves multiplies NMAT weight matrices (128 rows each, 16 per wave) by up
+// to 64 token rows of Q8_0 codes, over K in stages of CH blocks of 32.
+//
+// Stages go straight from memory into a ring of kStages LDS buffers with
+// global_load_lds (16-byte pieces for weights and codes, 4-byte ones for
+// the block scales), so two stages are in flight while a third is
+// multiplied, and no register holds them on the way.  Every wave issues the
+// same number of load instructions per stage, so one s_waitcnt vmcnt(N)
+// waits for exactly the oldest stage; a bare s_barrier (no fence, which
+// would wait for every load in flight) then makes it visible to all waves.
+//
+// LDS layouts are XOR-swizzled in 16-byte pieces (scales in 4-byte words):
+// the lanes of a wave read a 16 x 32 operand (16 rows or tokens at one k
+// offset) from 64 distinct banks, and the global reads behind each load
+// instruction stay contiguous per row.  Pieces past a row's end, rows past
+// the matrix and tokens past the item are clamped to valid addresses; what
+// they bring in is never used.
+//
+// The token tile count NTT is a template parameter (one loop per count), so
+// a full stage's eight blocks unroll with no runtime branch.
+// acc[m][tt][r]: matrix m, token tile tt, row 4 g + r of the wave's 16,
+// token 16 tt + li (lane = 16 g + li).
 // ---------------------------------------------------------------------------
 template <int BITS>
 struct MfmaGeo {
-  static constexpr int CH = BITS == 8 ? 8 : 16;           // blocks per chunk
-  static constexpr int RBC = CH * 32 * BITS / 8;          // weight bytes per row per chunk
-  static constexpr int WST = RBC + 16;                    // LDS stride of a weight row
-  static constexpr int XST = CH * 32 + 16;                // LDS stride of a token row
-  static constexpr int XPT = kMfmaTokens * CH * 2 / 256;  // 16-byte code loads per thread
-  static constexpr int DPT = kMfmaTokens * CH / 256;      // scales per thread
+  static constexpr int CH = BITS == 8 ? 4 : 8;          // blocks per stage
+  static constexpr int RB = CH * 32 * BITS / 8;         // weight bytes per row per stage
+  static constexpr int PPR = RB / 16;                   // 16-byte pieces per weight row
+  static constexpr int XR = CH * 32;                    // code bytes per token per stage
+  static constexpr int XPR = XR / 16;                   // pieces per token
+  static constexpr int KW = 256 / RB;                   // weight rows per 256 bytes of LDS
+  static constexpr int KX = 256 / XR;                   // token rows per 256 bytes
+};
+
+// Swizzled positions (pieces, or words for the scales).
+template <int BITS>
+__device__ __forceinline__ int wkey(int r) {
+  using G = MfmaGeo<BITS>;
+  return (r / G::KW) & (G::PPR - 1);
+}
+template <int BITS>
+__device__ __forceinline__ int xkey(int t) {
+  using G = MfmaGeo<BITS>;
+  return (t / G::KX) & (G::XPR - 1);
+}
+template <int BITS>
+__device__ __forceinline__ int dkey(int t) {
+  return MfmaGeo<BITS>::CH == 8 ? (t >> 3) & 7 : 0;
+}
+
+template <int BITS, int NMAT>
+struct MfmaStage {
+  using G = MfmaGeo<BITS>;
+  static constexpr int W = NMAT * kMfmaRows * G::RB;   // weight bytes
+  static constexpr int X = kMfmaTokens * G::XR;        // code bytes
+  static constexpr int D = kMfmaTokens * G::CH * 4;    // scale bytes
+  static constexpr int BYTES = W + X + D;
+  // load instructions per wave per stage
+  static constexpr int NW = W / 16 / kMfmaThreads;
+  static constexpr int NX = X / 16 / kMfmaThreads;
+  static constexpr int NL = NW + NX + 1;
+  static_assert(W % (16 * kMfmaThreads) == 0 && X % (16 * kMfmaThreads) == 0, "stage split");
+  static_assert(kMfmaTokens * G::CH <= 64 * kMfmaWaves && kMfmaTokens * G::CH % kMfmaWaves == 0,
+                "one scale instruction per wave");
 };
 
 template <int BITS, int NMAT>
 struct MfmaLds {
-  using G = MfmaGeo<BITS>;
-  int8_t xs[kMfmaTokens * G::XST];    // token codes of the chunk
-  float ds[kMfmaTokens][G::CH + 1];   // their block scales
-  uint8_t ws[4][NMAT * 16 * G::WST];  // each wave's weight rows of the chunk
-  int trow[kMfmaTokens];              // activation row of each token
+  __align__(16) unsigned char ring[kStages][MfmaStage<BITS, NMAT>::BYTES];
+  int trow[kMfmaTokens];  // activation row of each token slot (clamped past the item)
 };
 
-template <int BITS, int NMAT, typename Acc>
-__device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, size_t row_bytes,
-                                          const int8_t *act, const float *actd, int K, int nt,
-                                          MfmaLds<BITS, NMAT> &L, Acc (*acc)[kMfmaTiles][4]) {
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt untouched), gfx9 field layout.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// nrows[m]: rows of matrix m that exist (>= 1; rows past it load its last).
+template <int BITS, int NMAT, int NTT, typename Acc>
+__device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int *nrows,
+                                          size_t row_bytes, const int8_t *act, const float *actd,
+                                          int K, MfmaLds<BITS, NMAT> &L,
+                                          Acc (*acc)[kMfmaTiles][4]) {
   using G = MfmaGeo<BITS>;
+  using ST = MfmaStage<BITS, NMAT>;
   constexpr int SH = wshift<BITS>();
-  constexpr int PPR = G::RBC / 16;             // 16-byte pieces per weight row
-  constexpr int WPL = NMAT * 16 * PPR / 64;    // 16-byte weight loads per lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, g = lane >> 4;
-  const int nbk = K / 32, nch = (nbk + G::CH - 1) / G::CH;
-  const int ntt = (nt + 15) >> 4;
+  const int nbk = K / 32, nst = (nbk + G::CH - 1) / G::CH;
   const v4i zero = {0, 0, 0, 0};
-  uint4 xr[G::XPT], wr[WPL];
-  float dr[G::DPT];
+  // the accumulators live here, sized for the item, and go to acc at the end
+  Acc ac[NMAT][NTT][4];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ac[m][tt][r] = (Acc)0;
 
-  auto load_chunk = [&](int c) {
-    const int b0 = c * G::CH, cb = min(G::CH, nbk - b0);
+  // one stage's loads: every wave issues ST::NL instructions
+  auto issue = [&](int c) {
+    unsigned char *buf = L.ring[c % kStages];
+    const int valid_w = min(G::RB, (int)(row_bytes - (size_t)c * G::RB));  // bytes of this stage in a row
+    const int valid_x = min(G::XR, K - c * G::XR);
 #pragma unroll
-    for (int i = 0; i < G::XPT; ++i) {
-      const int p = threadIdx.x + 256 * i, tok = p / (2 * G::CH), pc = p % (2 * G::CH);
-      xr[i] = make_uint4(0, 0, 0, 0);
-      if (tok < nt && pc < 2 * cb)
-        xr[i] = *reinterpret_cast<const uint4 *>(act + (size_t)L.trow[tok] * K + b0 * 32 + 16 * pc);
+    for (int i = 0; i < ST::NW; ++i) {
+      const int q0 = (i * kMfmaWaves + wave) * 64, q = q0 + lane;
+      const int m = q / (kMfmaRows * G::PPR), r = (q / G::PPR) % kMfmaRows, pl = q % G::PPR;
+      const int gp = min(pl ^ wkey<BITS>(r), valid_w / 16 - 1);
+      const int rr = min(r, nrows[m] - 1);
+      const uint8_t *src = wbase[m] + (size_t)rr * row_bytes + (size_t)c * G::RB + 16 * gp;
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + (size_t)q0 * 16), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < G::DPT; ++i) {
-      const int p = threadIdx.x + 256 * i, tok = p / G::CH, bb = p % G::CH;
-      dr[i] = 0.f;
-      if (tok < nt && bb < cb) dr[i] = actd[(size_t)L.trow[tok] * nbk + b0 + bb];
+    for (int i = 0; i < ST::NX; ++i) {
+      const int q0 = (i * kMfmaWaves + wave) * 64, q = q0 + lane;
+      const int t = q / G::XPR, pl = q % G::XPR;
+      const int gp = min(pl ^ xkey<BITS>(t), valid_x / 16 - 1);
+      const int8_t *src = act + (size_t)L.trow[t] * K + (size_t)c * G::XR + 16 * gp;
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + (size_t)q0 * 16), 16, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < WPL; ++i) {
-      const int p = lane + 64 * i, r = p / PPR, pc = p % PPR;
-      wr[i] = make_uint4(0, 0, 0, 0);
-      if (pc * 16 < cb * 32 * BITS / 8)
-        wr[i] = ld_nt(reinterpret_cast<const uint4 *>(wbase[r / 16] + (size_t)(r % 16) * row_bytes +
-                                                      (size_t)b0 * 32 * BITS / 8) + pc);
+    {
+      // the scales: wave w loads words [w * per, (w + 1) * per) of the stage
+      constexpr int per = kMfmaTokens * G::CH / kMfmaWaves;
+      const int q = wave * per + lane;
+      if (lane < per) {
+        const int t = q / G::CH, bl = q % G::CH;
+        const int bg = min(c * G::CH + (bl ^ dkey<BITS>(t)), nbk - 1);
+        const float *src = actd + (size_t)L.trow[t] * nbk + bg;
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + ST::X + (size_t)wave * per * 4),
+                                         4, 0, 0);
+      }
     }
   };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int i = 0; i < G::XPT; ++i) {
-      const int p = threadIdx.x + 256 * i, tok = p / (2 * G::CH), pc = p % (2 * G::CH);
-      *reinterpret_cast<uint4 *>(L.xs + tok * G::XST + 16 * pc) = xr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < G::DPT; ++i) {
-      const int p = threadIdx.x + 256 * i;
-      L.ds[p / G::CH][p % G::CH] = dr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < WPL; ++i) {
-      const int p = lane + 64 * i, r = p / PPR, pc = p % PPR;
-      *reinterpret_cast<uint4 *>(L.ws[wave] + r * G::WST + 16 * pc) = wr[i];
-    }
-  };
 
-  load_chunk(0);
-  for (int c = 0; c < nch; ++c) {
-    __syncthreads();  // the previous chunk's operands are no longer read
-    store_chunk();
-    if (c + 1 < nch) load_chunk(c + 1);
-    __syncthreads();
-    const int cb = min(G::CH, nbk - c * G::CH);
-#pragma unroll 4
-    for (int b = 0; b < cb; ++b) {
-      long aw[NMAT];
+  auto block_step = [&](const unsigned char *buf, int b) {
+    long aw[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      const int r = 16 * wave + li;
+      const unsigned char *wrow = buf + (size_t)(m * kMfmaRows + r) * G::RB;
+      const int key = wkey<BITS>(r);
+      if constexpr (BITS == 8) {
+        const int pc = (2 * b + (g >> 1)) ^ key;
+        aw[m] = *reinterpret_cast<const long *>(wrow + 16 * pc + 8 * (g & 1));
+      } else if constexpr (BITS == 4) {
+        aw[m] = wop<4>(*reinterpret_cast<const uint32_t *>(wrow + 16 * (b ^ key) + 4 * g), g);
+      } else {
+        const int pc = (b >> 1) ^ key;
+        aw[m] = wop<2>(*reinterpret_cast<const uint32_t *>(wrow + 16 * pc + 8 * (b & 1) + 4 * (g >> 1)), g);
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      const int t = 16 * tt + li;
+      const int pc = (2 * b + (g >> 1)) ^ xkey<BITS>(t);
+      const long bx = *reinterpret_cast<const long *>(buf + ST::W + (size_t)t * G::XR + 16 * pc + 8 * (g & 1));
+      const float dj = *reinterpret_cast<const float *>(buf + ST::W + ST::X +
+                                                        ((size_t)t * G::CH + (b ^ dkey<BITS>(t))) * 4);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
-        const uint8_t *wrow = L.ws[wave] + (m * 16 + li) * G::WST;
-        if constexpr (BITS == 8) aw[m] = *reinterpret_cast<const long *>(wrow + 32 * b + 8 * g);
-        else if constexpr (BITS == 4)
-          aw[m] = wop<4>(*reinterpret_cast<const uint32_t *>(wrow + 16 * b + 4 * g), g);
-        else aw[m] = wop<2>(*reinterpret_cast<const uint32_t *>(wrow + 8 * b + 4 * (g >> 1)), g);
-      }
+        const v4i cm = __builtin_amdgcn_mfma_i32_16x16x32_i8(aw[m], bx, zero, 0, 0, 0);
+        // the block's exact int32 sum times the token's block scale
+        if constexpr (std::is_same<Acc, double>::value) {
+          // the x16 / x64 widening folded into the scale: exact in binary64
+          const double djs = (double)dj * (1.0 / (double)(1 << SH));
 #pragma unroll
-      for (int tt = 0; tt < kMfmaTiles; ++tt) {
-        if (tt < ntt) {
-          const long bx = *reinterpret_cast<const long *>(L.xs + (16 * tt + li) * G::XST + 32 * b + 8 * g);
-          const Acc dj = (Acc)L.ds[16 * tt + li][b];
+          for (int r = 0; r < 4; ++r) ac[m][tt][r] += (double)cm[r] * djs;
+        } else {
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m) {
-            const v4i cm = __builtin_amdgcn_mfma_i32_16x16x32_i8(aw[m], bx, zero, 0, 0, 0);
-            // the block's exact int32 sum times the token's block scale
-            // (exact in binary64; one rounding per step in binary32)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[m][tt][r] += (Acc)(cm[r] >> SH) * dj;
-          }
+          for (int r = 0; r < 4; ++r) ac[m][tt][r] += (Acc)(cm[r] >> SH) * dj;
         }
       }
     }
+  };
+
+#pragma unroll
+  for (int c = 0; c < kStages - 1; ++c)
+    if (c < nst) issue(c);
+  for (int c = 0; c < nst; ++c) {
+    // this wave's loads of stage c are done once at most the later stages'
+    // remain; the barrier makes every wave's visible and frees stage c - 1
+    if (c + 1 < nst) wait_vm_lgkm0<ST::NL * (kStages - 2)>();
+    else wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    if (c + kStages - 1 < nst) issue(c + kStages - 1);
+    const unsigned char *buf = L.ring[c % kStages];
+    const int cb = min(G::CH, nbk - c * G::CH);
+    if (cb == G::CH) {
+      // a full stage unrolled (one or two token tiles), or by two blocks
+      // (more tiles: their operands and accumulators leave no room for more)
+      if constexpr (NTT <= 2) {
+#pragma unroll
+        for (int b = 0; b < G::CH; ++b) block_step(buf, b);
+      } else {
+#pragma unroll 2
+        for (int b = 0; b < G::CH; ++b) block_step(buf, b);
+      }
+    } else {
+      for (int b = 0; b < cb; ++b) block_step(buf, b);
+    }
   }
-  __syncthreads();  // LDS free for the caller
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[m][tt][r] = ac[m][tt][r];
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();  // every wave is done with the ring (no load is in flight)
+}
+
+template <int BITS, int NMAT, typename Acc>
+__device__ __forceinline__ void mfma_core_ntt(int ntt, const uint8_t *const *wbase, const int *nrows,
+                                              size_t row_bytes, const int8_t *act, const float *actd,
+                                              int K, MfmaLds<BITS, NMAT> &L, Acc (*acc)[kMfmaTiles][4]) {
+  switch (ntt) {
+    case 1: mfma_core<BITS, NMAT, 1>(wbase, nrows, row_bytes, act, actd, K, L, acc); break;
+    case 2: mfma_core<BITS, NMAT, 2>(wbase, nrows, row_bytes, act, actd, K, L, acc); break;
+    case 3: mfma_core<BITS, NMAT, 3>(wbase, nrows, row_bytes, act, actd, K, L, acc); break;
+    default: mfma_core<BITS, NMAT, 4>(wbase, nrows, row_bytes, act, actd, K, L, acc); break;
+  }
+}
+
+// Token slots of an item: activation row of each (clamped past nt), into LDS.
+__device__ __forceinline__ void item_rows(const FfnArgs &a, const MfmaItem &it, bool hrows, int *trow) {
+  for (int n = threadIdx.x; n < kMfmaTokens; n += kMfmaThreads) {
+    int t = 0, hrow = 0, j;
+    tok_at(a, true, it.s, it.n0 + min(n, it.nt - 1), t, hrow, j);
+    trow[n] = hrows ? hrow : t;
+  }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up + SwiGLU + Q8_0(h): rows [64 rb, +64) of gate and up for up to 64
-// tokens of one expert.  Wave w owns rows 16 w .. 16 w + 15 of both.
+// Gate/up + SwiGLU + Q8_0(h): rows [128 rb, +128) of gate and up for up to
+// 64 tokens of one expert.  Wave w owns rows 16 w .. 16 w + 15 of both.
 // ---------------------------------------------------------------------------
 template <int BITS>
-__global__ __launch_bounds__(256) void k_gateup_mfma(FfnArgs a) {
-  __shared__ __align__(16) MfmaLds<BITS, 2> L;
+__global__ __launch_bounds__(kMfmaThreads) void k_gateup_mfma(FfnArgs a) {
+  __shared__ MfmaLds<BITS, 2> L;
   const int H = a.L.H, I = a.L.I;
   MfmaItem it;
-  if (!mfma_item(a, I / kMfmaRows, it)) return;
+  if (!mfma_item(a, (I + kMfmaRows - 1) / kMfmaRows, it)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, g = lane >> 4;
   const ExpertPtrs ep = expert_ptrs(a.L, it.e);
   const size_t row_bytes = (size_t)H * BITS / 8;
-  const int row0 = it.rb * kMfmaRows + wave * 16;
-  for (int n = threadIdx.x; n < kMfmaTokens; n += 256) {
-    int t = 0, hrow, j;
-    if (n < it.nt) tok_at(a, true, it.s, it.n0 + n, t, hrow, j);
-    L.trow[n] = t;
-  }
-  __syncthreads();
-  const uint8_t *wb[2] = {ep.wg + (size_t)row0 * row_bytes, ep.wu + (size_t)row0 * row_bytes};
+  const int rb0 = it.rb * kMfmaRows, nrows = min(kMfmaRows, I - rb0);
+  item_rows(a, it, false, L.trow);
+  const uint8_t *wb[2] = {ep.wg + (size_t)rb0 * row_bytes, ep.wu + (size_t)rb0 * row_bytes};
+  const int nr[2] = {nrows, nrows};
   // g and u accumulate in binary64 (the expert definition's sum, rounded
   // once), so h -- and its Q8_0 codes -- are those of that definition
   double acc[2][kMfmaTiles][4];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int tt = 0; tt < kMfmaTiles; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[m][tt][r] = 0.0;
-  mfma_core<BITS, 2>(wb, row_bytes, a.xq, a.xd, H, it.nt, L, acc);
+  const int ntt = (it.nt + 15) >> 4;
+  mfma_core_ntt<BITS, 2>(ntt, wb, nr, row_bytes, a.xq, a.xd, H, L, acc);
 
   // h = silu(g) * u for rows 4 g + r of the wave, token 16 tt + li, staged
-  // in LDS (over the operand tiles) for the Q8_0 step
-  static_assert(sizeof(float) * kMfmaTokens * (kMfmaRows + 1) <= sizeof(L.xs) + sizeof(L.ds),
-                "h tile exceeds the operand tiles");
-  float(*hs)[kMfmaRows + 1] = reinterpret_cast<float(*)[kMfmaRows + 1]>(L.xs);
-  const int ntt = (it.nt + 15) >> 4;
+  // in LDS (over the ring) for the Q8_0 step
+  static_assert(sizeof(float) * kMfmaTokens * (kMfmaRows + 1) <= sizeof(L.ring), "h tile");
+  float(*hs)[kMfmaRows + 1] = reinterpret_cast<float(*)[kMfmaRows + 1]>(&L.ring[0][0]);
+  const int rw = 16 * wave + 4 * g;  // the lane's first row in the block
   float sg[4], su[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    sg[r] = ep.sg[row0 + 4 * g + r];
-    su[r] = ep.su[row0 + 4 * g + r];
+    const int row = rb0 + min(rw + r, nrows - 1);
+    sg[r] = ep.sg[row];
+    su[r] = ep.su[row];
   }
 #pragma unroll
   for (int tt = 0; tt < kMfmaTiles; ++tt)
     if (tt < ntt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        hs[16 * tt + li][wave * 16 + 4 * g + r] =
-            swiglu_h(row_out(acc[0][tt][r], sg[r]), row_out(acc[1][tt][r], su[r]));
+        hs[16 * tt + li][rw + r] = swiglu_h(row_out(acc[0][tt][r], sg[r]), row_out(acc[1][tt][r], su[r]));
   __syncthreads();
-  // Q8_0 of each token's two 32-row blocks of h: 32 threads per block
-  for (int q = threadIdx.x; q < it.nt * kMfmaRows; q += 256) {
-    const int tl = q / kMfmaRows, bb = (q / 32) & 1, i = q & 31;
+  // Q8_0 of each token's 32-row blocks of h: 32 threads per block
+  const int nblk = nrows / 32;
+  for (int q = threadIdx.x; q < it.nt * kMfmaRows; q += kMfmaThreads) {
+    const int tl = q / kMfmaRows, bb = (q / 32) % (kMfmaRows / 32), i = q & 31;
     const float h = hs[tl][bb * 32 + i];
     float amax = group_max<32>(fabsf(h));
     amax = __shfl(amax, (lane & 32) | 31, 64);
-    int t, hrow, j;
-    tok_at(a, true, it.s, it.n0 + tl, t, hrow, j);
-    const float db = amax / 127.f;
-    float c = 0.f;
-    if (db != 0.f) c = fminf(fmaxf(rintf(h / db), -127.f), 127.f);
-    const int blk = it.rb * (kMfmaRows / 32) + bb;
-    a.hq[(size_t)hrow * I + blk * 32 + perm_dst<BITS>(i)] = (int8_t)c;
-    if (i == 0) a.hd[(size_t)hrow * (I / 32) + blk] = db;
+    if (bb < nblk) {
+      int t, hrow, j;
+      tok_at(a, true, it.s, it.n0 + tl, t, hrow, j);
+      const float db = amax / 127.f;
+      float c = 0.f;
+      if (db != 0.f) c = fminf(fmaxf(rintf(h / db), -127.f), 127.f);
+      const int blk = rb0 / 32 + bb;
+      a.hq[(size_t)hrow * I + blk * 32 + perm_dst<BITS>(i)] = (int8_t)c;
+      if (i == 0) a.hd[(size_t)hrow * (I / 32) + blk] = db;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Down projection: output rows [64 rb, +64) for up to 64 tokens of one
-// expert, o into the per-(token, slot) buffer the combine kernel reduces.
+// Down projection: output rows [256 rb, +256) for up to 64 tokens of one
+// expert (two 128-row halves, the core's two matrices), o into the
+// per-(token, slot) buffer the combine kernel reduces.
 // ---------------------------------------------------------------------------
+constexpr int kDownRows = 2 * kMfmaRows;
+
 template <int BITS>
-__global__ __launch_bounds__(256) void k_down_mfma(FfnArgs a) {
-  __shared__ __align__(16) MfmaLds<BITS, 1> L;
+__global__ __launch_bounds__(kMfmaThreads) void k_down_mfma(FfnArgs a) {
+  __shared__ MfmaLds<BITS, 2> L;
   const int H = a.L.H, I = a.L.I;
   MfmaItem it;
-  if (!mfma_item(a, H / kMfmaRows, it)) return;
+  if (!mfma_item(a, (H + kDownRows - 1) / kDownRows, it)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, g = lane >> 4;
   const ExpertPtrs ep = expert_ptrs(a.L, it.e);
   const size_t row_bytes = (size_t)I * BITS / 8;
-  const int row0 = it.rb * kMfmaRows + wave * 16;
-  for (int n = threadIdx.x; n < kMfmaTokens; n += 256) {
-    int t = 0, hrow = 0, j;
-    if (n < it.nt) tok_at(a, true, it.s, it.n0 + n, t, hrow, j);
-    L.trow[n] = hrow;
-  }
-  __syncthreads();
-  const uint8_t *wb[1] = {ep.wd + (size_t)row0 * row_bytes};
-  float acc[1][kMfmaTiles][4];
-#pragma unroll
-  for (int tt = 0; tt < kMfmaTiles; ++tt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[0][tt][r] = 0.f;
-  mfma_core<BITS, 1>(wb, row_bytes, a.hq, a.hd, I, it.nt, L, acc);
-
+  const int rb0 = it.rb * kDownRows, nrows = min(kDownRows, H - rb0);
+  item_rows(a, it, true, L.trow);
+  // half 1 may not exist at the matrix edge: its loads then read half 0's rows
+  const int nr[2] = {min(nrows, kMfmaRows), max(1, nrows - kMfmaRows)};
+  const uint8_t *wb[2] = {ep.wd + (size_t)rb0 * row_bytes,
+                          ep.wd + (size_t)(nrows > kMfmaRows ? rb0 + kMfmaRows : rb0) * row_bytes};
+  float acc[2][kMfmaTiles][4];
   const int ntt = (it.nt + 15) >> 4;
-  float sd[4];
+  mfma_core_ntt<BITS, 2>(ntt, wb, nr, row_bytes, a.hq, a.hd, I, L, acc);
+
+  const int rw = 16 * wave + 4 * g;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) sd[r] = ep.sd[row0 + 4 * g + r];
+  for (int m = 0; m < 2; ++m) {
+    const int row = m * kMfmaRows + rw;  // first of the lane's 4 rows in the block
+    if (row >= nrows) continue;          // rows past the matrix: whole quads
+    float sd[4];
 #pragma unroll
-  for (int tt = 0; tt < kMfmaTiles; ++tt) {
-    const int n = 16 * tt + li;
-    if (tt < ntt && n < it.nt) {
-      int t, hrow, j;
-      tok_at(a, true, it.s, it.n0 + n, t, hrow, j);
-      float4 o;
-      o.x = acc[0][tt][0] * sd[0];
-      o.y = acc[0][tt][1] * sd[1];
-      o.z = acc[0][tt][2] * sd[2];
-      o.w = acc[0][tt][3] * sd[3];
-      *reinterpret_cast<float4 *>(a.obuf + ((size_t)t * (a.k + 1) + j) * H + row0 + 4 * g) = o;
+    for (int r = 0; r < 4; ++r) sd[r] = ep.sd[rb0 + row + r];
+#pragma unroll
+    for (int tt = 0; tt < kMfmaTiles; ++tt) {
+      const int n = 16 * tt + li;
+      if (tt < ntt && n < it.nt) {
+        int t, hrow, j;
+        tok_at(a, true, it.s, it.n0 + n, t, hrow, j);
+        float4 o;
+        o.x = acc[m][tt][0] * sd[0];
+        o.y = acc[m][tt][1] * sd[1];
+        o.z = acc[m][tt][2] * sd[2];
+        o.w = acc[m][tt][3] * sd[3];
+        *reinterpret_cast<float4 *>(a.obuf + ((size_t)t * (a.k + 1) + j) * H + rb0 + row) = o;
+      }
     }
   }
 }
@@ -409,13 +533,16 @@ static int mfma_group_bound(const FfnArgs &a) {
   return (int)((pairs + kMfmaTokens - 1) / kMfmaTokens + cap + shared);
 }
 
+// Grid: one workgroup per item (an upper bound; surplus workgroups exit).
+static int mfma_grid(const FfnArgs &a, int n_rb) { return mfma_group_bound(a) * n_rb; }
+
 hipError_t launch_mfma_items(const FfnArgs &a, int32_t *mgofs, hipStream_t st) {
   hipLaunchKernelGGL(k_mfma_items, dim3(1), dim3(1024), 0, st, a, mgofs);
   return hipGetLastError();
 }
 
 hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t st, KEvents ev) {
-  const dim3 grid((unsigned)(mfma_group_bound(a) * (a.L.I / kMfmaRows))), block(256);
+  const dim3 grid((unsigned)mfma_grid(a, (a.L.I + kMfmaRows - 1) / kMfmaRows)), block(kMfmaThreads);
   switch (a.L.bits) {
     case 8: COLI_LAUNCH(ev, k_gateup_mfma<8>, grid, block, 0, st, a); break;
     case 4: COLI_LAUNCH(ev, k_gateup_mfma<4>, grid, block, 0, st, a); break;
@@ -426,7 +553,7 @@ hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t st, KEvents ev) {
 }
 
 hipError_t launch_down_mfma(const FfnArgs &a, hipStream_t st, KEvents ev) {
-  const dim3 grid((unsigned)(mfma_group_bound(a) * (a.L.H / kMfmaRows))), block(256);
+  const dim3 grid((unsigned)mfma_grid(a, (a.L.H + kDownRows - 1) / kDownRows)), block(kMfmaThreads);
   switch (a.L.bits) {
     case 8: COLI_LAUNCH(ev, k_down_mfma<8>, grid, block, 0, st, a); break;
     case 4: COLI_LAUNCH(ev, k_down_mfma<4>, grid, block, 0, st, a); break;
