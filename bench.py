@@ -49,7 +49,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
-MFMA_MIN_DEFAULT = 8  # the library's default mfma_min_tokens (routed experts)
+MFMA_MIN_DEFAULT = 8  # the library's default mfma_min_tokens (routed experts) ...
+MFMA_ALL_TOKENS = 64  # ... in batches below this size; from it on, every routed expert
 MFMA_MIN_SHARED_DEFAULT = 64  # and for the shared expert
 INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, published
 
@@ -97,6 +98,8 @@ def expert_bytes(s) -> dict:
 KERNEL_SOURCES = {
     "k_decode_fused": ["decode.hip", "actq.hpp", "device.hpp", "ffn_common.hpp", "kernels.hpp",
                        "select.hpp"],
+    "k_gateup_mfma": ["mfma.hip", "device.hpp", "ffn_common.hpp", "kernels.hpp"],
+    "k_down_mfma": ["mfma.hip", "device.hpp", "ffn_common.hpp", "kernels.hpp"],
 }
 
 
@@ -382,7 +385,7 @@ def main() -> int:
     # algorithmic bytes: the unique experts each step reads (+ the shared
     # one); in a union batch, experts with at least mfma_min tokens (and the
     # shared expert when T >= mfma_min) run on the matrix cores
-    mfma_min = layers[0].mfma_min_tokens or MFMA_MIN_DEFAULT
+    mfma_min = layers[0].mfma_min_tokens or (1 if T >= MFMA_ALL_TOKENS else MFMA_MIN_DEFAULT)
     shared_min = layers[0].mfma_min_tokens or MFMA_MIN_SHARED_DEFAULT
     if T == 1:
         uniq = np.full(K, s.top_k, dtype=np.float64)

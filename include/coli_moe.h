@@ -90,8 +90,9 @@ typedef struct {
  * mfma_min_tokens: in a
  * batch of T >= 2 tokens, a unique expert (or the shared expert) receiving at
  * least this many tokens runs on the int8 matrix cores, one with fewer on the
- * integer dot-product GEMV; 0 selects the library defaults (8 tokens for a
- * routed expert, 64 for the shared expert, which receives the whole batch).
+ * integer dot-product GEMV; 0 selects the library defaults (a routed expert
+ * with 8 tokens, or any routed expert in a batch of 64 tokens or more; the
+ * shared expert, which receives the whole batch, from 64 tokens).
  * Both give the same results up to fp32 summation order.
  * gate_offset: NOT a step of the pages' layer -- an extension for synthetic
  * workloads.  Optional [E] fp32 per-expert terms added (one binary32

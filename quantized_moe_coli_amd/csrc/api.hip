@@ -526,14 +526,17 @@ coli_status forward_impl(const coli_moe_layer *L, const CacheRun *cache, const f
     if (e != hipSuccess) return COLI_ERR_DEVICE;
     int32_t *mgofs = reinterpret_cast<int32_t *>(base + ws.mgofs);
     fa.disp = coli::Dispatch{counts, offs, perm, uniq, nuniq, mgofs};
-    fa.mfma_min = mfma_min > 0 ? mfma_min : coli::kMfmaMinDefault;
+    fa.mfma_min = mfma_min > 0 ? mfma_min : T >= coli::kMfmaAllTokens ? 1 : coli::kMfmaMinDefault;
     fa.mfma_min_shared = mfma_min > 0 ? mfma_min : coli::kMfmaMinSharedDefault;
     // no slot of a batch smaller than mfma_min tokens can reach the matrix cores
     const bool mfma = T >= fa.mfma_min;
+    // every slot on the matrix cores: the dot-product kernels would only
+    // launch workgroups that find nothing to do
+    const bool dot = !(mfma && fa.mfma_min <= 1 && T >= fa.mfma_min_shared);
     if (mfma) e = coli::launch_mfma_items(fa, mgofs, s);
-    if (e == hipSuccess) e = coli::launch_gateup(fa, true, mfma_min, s, kev(1));
+    if (e == hipSuccess && dot) e = coli::launch_gateup(fa, true, mfma_min, s, kev(1));
     if (e == hipSuccess && mfma) e = coli::launch_gateup_mfma(fa, s, kev(3));
-    if (e == hipSuccess) e = coli::launch_down(fa, true, mfma_min, s, kev(2));
+    if (e == hipSuccess && dot) e = coli::launch_down(fa, true, mfma_min, s, kev(2));
     if (e == hipSuccess && mfma) e = coli::launch_down_mfma(fa, s, kev(4));
     if (e == hipSuccess) e = coli::launch_combine(fa, s);
     return from_hip(e);

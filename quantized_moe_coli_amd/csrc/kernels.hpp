@@ -149,6 +149,11 @@ struct FfnArgs {
 
 constexpr int kMfmaTokens = 64;  // tokens per matrix-core work item
 constexpr int kMfmaMinDefault = 8;  // default token count from which an expert runs on MFMA
+// From this batch size on, the default sends every routed expert to the
+// matrix cores: at 64-128 tokens the few-token experts the dot-product path
+// would keep cost more there (measured at the GLM-5.2 shape: 64 tokens 1.33
+// vs 1.19 ms, 128 tokens 1.86 vs 1.35 ms) than one matrix-core tile does.
+constexpr int kMfmaAllTokens = 64;
 // default for the shared expert, which receives the whole batch: one full
 // 64-token group.  With fewer tokens it usually runs alone on the matrix
 // cores (I/64 + H/64 workgroups), slower than on the dot-product path.

@@ -250,10 +250,11 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 }
 
 // nrows[m]: rows of matrix m that exist (>= 1; rows past it load its last).
+// act_rows bounds the activation rows the item's tokens name (trow).
 template <int BITS, int NMAT, int NTT, typename Acc>
 __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int *nrows,
                                           size_t row_bytes, const int8_t *act, const float *actd,
-                                          int K, MfmaLds<BITS, NMAT> &L,
+                                          int K, int act_rows, MfmaLds<BITS, NMAT> &L,
                                           Acc (*acc)[kMfmaTiles][4]) {
   using G = MfmaGeo<BITS>;
   using ST = MfmaStage<BITS, NMAT>;
@@ -271,9 +272,61 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
 #pragma unroll
       for (int r = 0; r < 4; ++r) ac[m][tt][r] = (Acc)0;
 
+  // Each lane's byte offset for every load instruction, from a base that
+  // only the stage moves (so a full stage's loads need no address
+  // arithmetic per lane): weight row and swizzled piece, token row and
+  // piece, token row and swizzled scale word.  The matrix of weight
+  // instruction i is the same for every wave.
+  static_assert((kMfmaRows * G::PPR) % (kMfmaWaves * 64) == 0, "one matrix per weight instruction");
+  const bool lane_offs = (uint64_t)act_rows * (uint64_t)K < (1ull << 31);
+  uint32_t woff[ST::NW], xoff[ST::NX], doff = 0;
+#pragma unroll
+  for (int i = 0; i < ST::NW; ++i) {
+    const int q = (i * kMfmaWaves + wave) * 64 + lane;
+    const int m = (i * kMfmaWaves * 64) / (kMfmaRows * G::PPR);
+    const int r = (q / G::PPR) % kMfmaRows, pl = q % G::PPR;
+    woff[i] = (uint32_t)((size_t)min(r, nrows[m] - 1) * row_bytes) + 16u * (uint32_t)(pl ^ wkey<BITS>(r));
+  }
+#pragma unroll
+  for (int i = 0; i < ST::NX; ++i) {
+    const int q = (i * kMfmaWaves + wave) * 64 + lane;
+    const int t = q / G::XPR, pl = q % G::XPR;
+    xoff[i] = (uint32_t)L.trow[t] * (uint32_t)K + 16u * (uint32_t)(pl ^ xkey<BITS>(t));
+  }
+  {
+    constexpr int per = kMfmaTokens * G::CH / kMfmaWaves;
+    const int q = wave * per + lane;
+    const int t = min(q / G::CH, kMfmaTokens - 1), bl = q % G::CH;
+    doff = 4u * ((uint32_t)L.trow[t] * (uint32_t)nbk + (uint32_t)(bl ^ dkey<BITS>(t)));
+  }
+
   // one stage's loads: every wave issues ST::NL instructions
   auto issue = [&](int c) {
     unsigned char *buf = L.ring[c % kStages];
+    if (lane_offs && (c + 1) * G::CH <= nbk) {
+      // a full stage: wave-uniform bases plus the lanes' fixed offsets
+#pragma unroll
+      for (int i = 0; i < ST::NW; ++i) {
+        const int m = (i * kMfmaWaves * 64) / (kMfmaRows * G::PPR);
+        const uint8_t *src = wbase[m] + (size_t)c * G::RB + woff[i];
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + (size_t)(i * kMfmaWaves + wave) * 64 * 16),
+                                         16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < ST::NX; ++i) {
+        const int8_t *src = act + (size_t)c * G::XR + xoff[i];
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + (size_t)(i * kMfmaWaves + wave) * 64 * 16),
+                                         16, 0, 0);
+      }
+      constexpr int per = kMfmaTokens * G::CH / kMfmaWaves;
+      if (lane < per) {
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(actd + (size_t)c * G::CH) + doff;
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + ST::X + (size_t)wave * per * 4),
+                                         4, 0, 0);
+      }
+      return;
+    }
+    // the last, partial stage (or activation offsets past 31 bits): clamped
     const int valid_w = min(G::RB, (int)(row_bytes - (size_t)c * G::RB));  // bytes of this stage in a row
     const int valid_x = min(G::XR, K - c * G::XR);
 #pragma unroll
@@ -307,43 +360,99 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
     }
   };
 
+  // The A operand of block b, matrix m: the packed word(s) as stored, then
+  // widened to int8.
+  auto a_raw = [&](const unsigned char *buf, int b, int m) -> WRaw<BITS> {
+    const int r = 16 * wave + li;
+    const unsigned char *wrow = buf + (size_t)(m * kMfmaRows + r) * G::RB;
+    const int key = wkey<BITS>(r);
+    if constexpr (BITS == 8) {
+      const int pc = (2 * b + (g >> 1)) ^ key;
+      return *reinterpret_cast<const uint64_t *>(wrow + 16 * pc + 8 * (g & 1));
+    } else if constexpr (BITS == 4) {
+      return *reinterpret_cast<const uint32_t *>(wrow + 16 * (b ^ key) + 4 * g);
+    } else {
+      const int pc = (b >> 1) ^ key;
+      return *reinterpret_cast<const uint32_t *>(wrow + 16 * pc + 8 * (b & 1) + 4 * (g >> 1));
+    }
+  };
+  // B operand (token tile tt's codes) and the tokens' block scale
+  auto b_op = [&](const unsigned char *buf, int b, int tt) -> long {
+    const int t = 16 * tt + li;
+    const int pc = (2 * b + (g >> 1)) ^ xkey<BITS>(t);
+    return *reinterpret_cast<const long *>(buf + ST::W + (size_t)t * G::XR + 16 * pc + 8 * (g & 1));
+  };
+  auto b_scale = [&](const unsigned char *buf, int b, int tt) -> float {
+    const int t = 16 * tt + li;
+    return *reinterpret_cast<const float *>(buf + ST::W + ST::X +
+                                            ((size_t)t * G::CH + (b ^ dkey<BITS>(t))) * 4);
+  };
+  // the block's exact int32 sums times the token's block scale
+  auto scale_acc = [&](Acc *a4, const v4i &cm, float dj) {
+    if constexpr (std::is_same<Acc, double>::value) {
+      // the x16 / x64 widening folded into the scale: exact in binary64
+      const double djs = (double)dj * (1.0 / (double)(1 << SH));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a4[r] += (double)cm[r] * djs;
+    } else {
+      // the sums are multiples of 2^SH below 2^24 in magnitude, so taking
+      // 2^-SH into the scale gives the product of the unshifted sum (short
+      // of a subnormal scale)
+      const float djs = dj * (1.0f / (float)(1 << SH));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a4[r] += (float)cm[r] * djs;
+    }
+  };
+
   auto block_step = [&](const unsigned char *buf, int b) {
     long aw[NMAT];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      const int r = 16 * wave + li;
-      const unsigned char *wrow = buf + (size_t)(m * kMfmaRows + r) * G::RB;
-      const int key = wkey<BITS>(r);
-      if constexpr (BITS == 8) {
-        const int pc = (2 * b + (g >> 1)) ^ key;
-        aw[m] = *reinterpret_cast<const long *>(wrow + 16 * pc + 8 * (g & 1));
-      } else if constexpr (BITS == 4) {
-        aw[m] = wop<4>(*reinterpret_cast<const uint32_t *>(wrow + 16 * (b ^ key) + 4 * g), g);
-      } else {
-        const int pc = (b >> 1) ^ key;
-        aw[m] = wop<2>(*reinterpret_cast<const uint32_t *>(wrow + 16 * pc + 8 * (b & 1) + 4 * (g >> 1)), g);
-      }
-    }
+    for (int m = 0; m < NMAT; ++m) aw[m] = wop<BITS>(a_raw(buf, b, m), g);
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
-      const int t = 16 * tt + li;
-      const int pc = (2 * b + (g >> 1)) ^ xkey<BITS>(t);
-      const long bx = *reinterpret_cast<const long *>(buf + ST::W + (size_t)t * G::XR + 16 * pc + 8 * (g & 1));
-      const float dj = *reinterpret_cast<const float *>(buf + ST::W + ST::X +
-                                                        ((size_t)t * G::CH + (b ^ dkey<BITS>(t))) * 4);
+      const long bx = b_op(buf, b, tt);
+      const float dj = b_scale(buf, b, tt);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
         const v4i cm = __builtin_amdgcn_mfma_i32_16x16x32_i8(aw[m], bx, zero, 0, 0, 0);
-        // the block's exact int32 sum times the token's block scale
-        if constexpr (std::is_same<Acc, double>::value) {
-          // the x16 / x64 widening folded into the scale: exact in binary64
-          const double djs = (double)dj * (1.0 / (double)(1 << SH));
+        scale_acc(ac[m][tt], cm, dj);
+      }
+    }
+  };
+
+  // NB blocks from b0, software-pipelined: every LDS operand of the NB
+  // blocks is read first, then each MFMA is issued LAG products ahead of
+  // the scaling of its result, so neither the LDS latency nor the MFMA's
+  // is waited for product by product.
+  constexpr int LAG = 2;
+  auto blocks_piped = [&](auto nb_c, const unsigned char *buf, int b0) {
+    constexpr int NB = decltype(nb_c)::value;
+    constexpr int NM = NB * NTT * NMAT;
+    WRaw<BITS> raw[NB][NMAT];
+    long bx[NB][NTT];
+    float dj[NB][NTT];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ac[m][tt][r] += (double)cm[r] * djs;
-        } else {
+    for (int b = 0; b < NB; ++b) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ac[m][tt][r] += (Acc)(cm[r] >> SH) * dj;
-        }
+      for (int m = 0; m < NMAT; ++m) raw[b][m] = a_raw(buf, b0 + b, m);
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        bx[b][tt] = b_op(buf, b0 + b, tt);
+        dj[b][tt] = b_scale(buf, b0 + b, tt);
+      }
+    }
+    v4i cm[LAG + 1];
+#pragma unroll
+    for (int i = 0; i < NM + LAG; ++i) {
+      if (i < NM) {
+        const int b = i / (NTT * NMAT), tt = (i / NMAT) % NTT, m = i % NMAT;
+        cm[i % (LAG + 1)] =
+            __builtin_amdgcn_mfma_i32_16x16x32_i8(wop<BITS>(raw[b][m], g), bx[b][tt], zero, 0, 0, 0);
+      }
+      if (i >= LAG) {
+        const int j = i - LAG;
+        const int b = j / (NTT * NMAT), tt = (j / NMAT) % NTT, m = j % NMAT;
+        scale_acc(ac[m][tt], cm[j % (LAG + 1)], dj[b][tt]);
       }
     }
   };
@@ -361,14 +470,13 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
     const unsigned char *buf = L.ring[c % kStages];
     const int cb = min(G::CH, nbk - c * G::CH);
     if (cb == G::CH) {
-      // a full stage unrolled (one or two token tiles), or by two blocks
-      // (more tiles: their operands and accumulators leave no room for more)
+      // a full stage in one pipelined run (one or two token tiles), or in
+      // runs of two blocks (more tiles: operands and accumulators leave no
+      // room for more)
       if constexpr (NTT <= 2) {
-#pragma unroll
-        for (int b = 0; b < G::CH; ++b) block_step(buf, b);
+        blocks_piped(std::integral_constant<int, G::CH>(), buf, 0);
       } else {
-#pragma unroll 2
-        for (int b = 0; b < G::CH; ++b) block_step(buf, b);
+        for (int b0 = 0; b0 < G::CH; b0 += 2) blocks_piped(std::integral_constant<int, 2>(), buf, b0);
       }
     } else {
       for (int b = 0; b < cb; ++b) block_step(buf, b);
@@ -387,12 +495,13 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
 template <int BITS, int NMAT, typename Acc>
 __device__ __forceinline__ void mfma_core_ntt(int ntt, const uint8_t *const *wbase, const int *nrows,
                                               size_t row_bytes, const int8_t *act, const float *actd,
-                                              int K, MfmaLds<BITS, NMAT> &L, Acc (*acc)[kMfmaTiles][4]) {
+                                              int K, int act_rows, MfmaLds<BITS, NMAT> &L,
+                                              Acc (*acc)[kMfmaTiles][4]) {
   switch (ntt) {
-    case 1: mfma_core<BITS, NMAT, 1>(wbase, nrows, row_bytes, act, actd, K, L, acc); break;
-    case 2: mfma_core<BITS, NMAT, 2>(wbase, nrows, row_bytes, act, actd, K, L, acc); break;
-    case 3: mfma_core<BITS, NMAT, 3>(wbase, nrows, row_bytes, act, actd, K, L, acc); break;
-    default: mfma_core<BITS, NMAT, 4>(wbase, nrows, row_bytes, act, actd, K, L, acc); break;
+    case 1: mfma_core<BITS, NMAT, 1>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc); break;
+    case 2: mfma_core<BITS, NMAT, 2>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc); break;
+    case 3: mfma_core<BITS, NMAT, 3>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc); break;
+    default: mfma_core<BITS, NMAT, 4>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc); break;
   }
 }
 
@@ -428,7 +537,7 @@ __global__ __launch_bounds__(kMfmaThreads) void k_gateup_mfma(FfnArgs a) {
   // once), so h -- and its Q8_0 codes -- are those of that definition
   double acc[2][kMfmaTiles][4];
   const int ntt = (it.nt + 15) >> 4;
-  mfma_core_ntt<BITS, 2>(ntt, wb, nr, row_bytes, a.xq, a.xd, H, L, acc);
+  mfma_core_ntt<BITS, 2>(ntt, wb, nr, row_bytes, a.xq, a.xd, H, a.T, L, acc);
 
   // h = silu(g) * u for rows 4 g + r of the wave, token 16 tt + li, staged
   // in LDS (over the ring) for the Q8_0 step
@@ -494,7 +603,7 @@ __global__ __launch_bounds__(kMfmaThreads) void k_down_mfma(FfnArgs a) {
                           ep.wd + (size_t)(nrows > kMfmaRows ? rb0 + kMfmaRows : rb0) * row_bytes};
   float acc[2][kMfmaTiles][4];
   const int ntt = (it.nt + 15) >> 4;
-  mfma_core_ntt<BITS, 2>(ntt, wb, nr, row_bytes, a.hq, a.hd, I, L, acc);
+  mfma_core_ntt<BITS, 2>(ntt, wb, nr, row_bytes, a.hq, a.hd, I, a.T * (a.k + 1), L, acc);
 
   const int rw = 16 * wave + 4 * g;
 #pragma unroll
