@@ -94,7 +94,7 @@ struct Dispatch {
   const int32_t *perm;    // [T*k] entries t*k+j ordered by (expert, t, j)
   const int32_t *uniq;    // [E]
   const int32_t *n_uniq;  // [1]
-  const int32_t *mgofs;   // [n_uniq+2] first matrix-core token group of each union slot
+  const int32_t *mgofs;   // [2][E+2] first matrix-core token group (64, then 32 tokens) of each union slot
 };
 
 hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t cols, uint8_t *q,
@@ -147,7 +147,6 @@ struct FfnArgs {
   int mfma_min_shared;  // union: the same for the shared expert (its tokens: the whole batch)
 };
 
-constexpr int kMfmaTokens = 64;  // tokens per matrix-core work item
 constexpr int kMfmaMinDefault = 8;  // default token count from which an expert runs on MFMA
 // From this batch size on, the default sends every routed expert to the
 // matrix cores: at 64-128 tokens the few-token experts the dot-product path

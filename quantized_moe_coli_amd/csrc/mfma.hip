@@ -33,52 +33,72 @@ namespace coli {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaRows = 128;  // weight rows per workgroup (16 per wave)
-constexpr int kMfmaTiles = kMfmaTokens / 16;
+constexpr int kMfmaGroup = 64;   // tokens per group in the item table
+constexpr int kMfmaRows = 128;   // weight rows per workgroup (16 per wave)
 constexpr int kMfmaThreads = 512;  // threads per workgroup (8 waves)
 constexpr int kMfmaWaves = kMfmaThreads / 64;
-constexpr int kStages = 3;         // LDS ring: two stages in flight while one is multiplied
+constexpr int kMaxStages = 8;
 
-// Tokens a union slot sends to the matrix cores (0: the dot-product path
-// takes it).
-__device__ __forceinline__ int mfma_groups(int n_tok, int mfma_min) {
-  return n_tok >= mfma_min ? (n_tok + kMfmaTokens - 1) / kMfmaTokens : 0;
+// A kernel's geometry by the workgroups it keeps resident per CU (WG).  Two
+// halve each one's LDS ring, its tokens per item and its stage rows, and cap
+// it at 128 VGPRs, so four waves share a SIMD instead of two: the binary32
+// down projection gains from that, the binary64 gate/up does not.
+template <int WG>
+struct MfmaCfg {
+  static constexpr int TOK = kMfmaGroup / WG;             // tokens per work item (group)
+  static constexpr int TILES = TOK / 16;                  // 16-token tiles
+  static constexpr int ROWB = 128 / WG;                   // weight bytes per row per stage (at most)
+  static constexpr int RING = 160 * 1024 / WG - 1024;     // LDS for the stage ring
+};
+
+// Token groups of `tok` tokens a union slot sends to the matrix cores (0:
+// the dot-product path takes it).
+__device__ __forceinline__ int mfma_groups(int n_tok, int mfma_min, int tok) {
+  return n_tok >= mfma_min ? (n_tok + tok - 1) / tok : 0;
 }
 
-// mgofs[u] = first token group of union slot u (slots 0 .. n_uniq-1 are the
-// unique routed experts, slot n_uniq the shared expert); mgofs[n_uniq + 1]
-// is the total.  One workgroup; slots <= 1025.
+// Two item tables, one per token-group size: mgofs[u] = first 64-token
+// group of union slot u (slots 0 .. n_uniq-1 are the unique routed experts,
+// slot n_uniq the shared expert), mgofs[n_uniq + 1] the total; the same for
+// 32-token groups from mgofs + E + 2.  One workgroup; slots <= 1025; both
+// counts scanned at once as the halves of one 64-bit word.
 __global__ __launch_bounds__(1024) void k_mfma_items(FfnArgs a, int32_t *__restrict__ mgofs) {
-  __shared__ int sc[2][1024];
+  __shared__ uint64_t sc[2][1024];
   const int tid = threadIdx.x;
   const int nu = *a.disp.n_uniq;
   const int slots = nu + 1;
+  auto groups = [&](int u) -> uint64_t {
+    const int n = u < nu ? a.disp.counts[a.disp.uniq[u]] : a.T;
+    const int mn = u < nu ? a.mfma_min : a.mfma_min_shared;
+    return (uint64_t)mfma_groups(n, mn, kMfmaGroup) | ((uint64_t)mfma_groups(n, mn, kMfmaGroup / 2) << 32);
+  };
   // thread i sums slots 2i, 2i+1
-  int g0 = 0, g1 = 0;
-  if (2 * tid < slots) {
-    const int u = 2 * tid;
-    g0 = u < nu ? mfma_groups(a.disp.counts[a.disp.uniq[u]], a.mfma_min)
-               : mfma_groups(a.T, a.mfma_min_shared);
-  }
-  if (2 * tid + 1 < slots) {
-    const int u = 2 * tid + 1;
-    g1 = u < nu ? mfma_groups(a.disp.counts[a.disp.uniq[u]], a.mfma_min)
-               : mfma_groups(a.T, a.mfma_min_shared);
-  }
+  const uint64_t g0 = 2 * tid < slots ? groups(2 * tid) : 0;
+  const uint64_t g1 = 2 * tid + 1 < slots ? groups(2 * tid + 1) : 0;
   int cur = 0;
   sc[0][tid] = g0 + g1;
   __syncthreads();
   for (int d = 1; d < 1024; d <<= 1) {
-    const int v = sc[cur][tid] + (tid >= d ? sc[cur][tid - d] : 0);
+    const uint64_t v = sc[cur][tid] + (tid >= d ? sc[cur][tid - d] : 0);
     sc[cur ^ 1][tid] = v;
     cur ^= 1;
     __syncthreads();
   }
-  const int incl = sc[cur][tid];  // inclusive prefix of the pair sums
-  const int excl = incl - (g0 + g1);
-  if (2 * tid < slots) mgofs[2 * tid] = excl;
-  if (2 * tid + 1 < slots) mgofs[2 * tid + 1] = excl + g0;
-  if (tid == 1023) mgofs[slots] = incl;  // total (slots <= 2048)
+  const uint64_t incl = sc[cur][tid];  // inclusive prefix of the pair sums
+  const uint64_t excl = incl - (g0 + g1);
+  int32_t *m32 = mgofs + a.E + 2;
+  if (2 * tid < slots) {
+    mgofs[2 * tid] = (int32_t)(uint32_t)excl;
+    m32[2 * tid] = (int32_t)(excl >> 32);
+  }
+  if (2 * tid + 1 < slots) {
+    mgofs[2 * tid + 1] = (int32_t)(uint32_t)(excl + g0);
+    m32[2 * tid + 1] = (int32_t)((excl + g0) >> 32);
+  }
+  if (tid == 1023) {  // totals (slots <= 2048)
+    mgofs[slots] = (int32_t)(uint32_t)incl;
+    m32[slots] = (int32_t)(incl >> 32);
+  }
 }
 
 // A operand, in two steps so a block's raw loads can all be issued before
@@ -137,13 +157,15 @@ constexpr int wshift() {
 struct MfmaItem {
   int e;      // expert (-1: shared)
   TokList s;  // the slot's tokens
-  int n0, nt; // first token of the group, tokens in it
+  int n0, nt; // first token of the item, tokens in it
   int rb;     // row block
 };
 
+template <int WG>
 __device__ __forceinline__ bool mfma_item(const FfnArgs &a, int n_rb, MfmaItem &it) {
+  using C = MfmaCfg<WG>;
   const int nu = *a.disp.n_uniq;
-  const int32_t *gofs = a.disp.mgofs;
+  const int32_t *gofs = a.disp.mgofs + (C::TOK == kMfmaGroup ? 0 : a.E + 2);
   const int n_items = gofs[nu + 1] * n_rb;
   if ((int)blockIdx.x >= n_items) return false;
   const int i = n_items - 1 - (int)blockIdx.x;
@@ -161,8 +183,8 @@ __device__ __forceinline__ bool mfma_item(const FfnArgs &a, int n_rb, MfmaItem &
   it.s.shared = shared;
   it.s.n_tok = shared ? a.T : a.disp.counts[it.e];
   it.s.p0 = shared ? -1 : a.disp.offs[it.e];
-  it.n0 = (G - gofs[lo]) * kMfmaTokens;
-  it.nt = min(kMfmaTokens, it.s.n_tok - it.n0);
+  it.n0 = (G - gofs[lo]) * C::TOK;
+  it.nt = min(C::TOK, it.s.n_tok - it.n0);
   return it.nt > 0;
 }
 
@@ -171,9 +193,9 @@ __device__ __forceinline__ bool mfma_item(const FfnArgs &a, int n_rb, MfmaItem &
 // waves multiplies NMAT weight matrices (128 rows each, 16 per wave) by up
 // to 64 token rows of Q8_0 codes, over K in stages of CH blocks of 32.
 //
-// Stages go straight from memory into a ring of kStages LDS buffers with
+// Stages go straight from memory into a ring of as many LDS buffers as fit, with
 // global_load_lds (16-byte pieces for weights and codes, 4-byte ones for
-// the block scales), so two stages are in flight while a third is
+// the block scales), so all other stages are in flight while one is
 // multiplied, and no register holds them on the way.  Every wave issues the
 // same number of load instructions per stage, so one s_waitcnt vmcnt(N)
 // waits for exactly the oldest stage; a bare s_barrier (no fence, which
@@ -191,9 +213,10 @@ __device__ __forceinline__ bool mfma_item(const FfnArgs &a, int n_rb, MfmaItem &
 // acc[m][tt][r]: matrix m, token tile tt, row 4 g + r of the wave's 16,
 // token 16 tt + li (lane = 16 g + li).
 // ---------------------------------------------------------------------------
-template <int BITS>
+template <int BITS, int WG>
 struct MfmaGeo {
-  static constexpr int CH = BITS == 8 ? 4 : 8;          // blocks per stage
+  static constexpr int CH0 = MfmaCfg<WG>::ROWB * 8 / (32 * BITS);
+  static constexpr int CH = CH0 < 8 ? CH0 : 8;          // blocks per stage
   static constexpr int RB = CH * 32 * BITS / 8;         // weight bytes per row per stage
   static constexpr int PPR = RB / 16;                   // 16-byte pieces per weight row
   static constexpr int XR = CH * 32;                    // code bytes per token per stage
@@ -203,41 +226,49 @@ struct MfmaGeo {
 };
 
 // Swizzled positions (pieces, or words for the scales).
-template <int BITS>
+template <int BITS, int WG>
 __device__ __forceinline__ int wkey(int r) {
-  using G = MfmaGeo<BITS>;
+  using G = MfmaGeo<BITS, WG>;
   return (r / G::KW) & (G::PPR - 1);
 }
-template <int BITS>
+template <int BITS, int WG>
 __device__ __forceinline__ int xkey(int t) {
-  using G = MfmaGeo<BITS>;
+  using G = MfmaGeo<BITS, WG>;
   return (t / G::KX) & (G::XPR - 1);
 }
-template <int BITS>
+template <int BITS, int WG>
 __device__ __forceinline__ int dkey(int t) {
-  return MfmaGeo<BITS>::CH == 8 ? (t >> 3) & 7 : 0;
+  return MfmaGeo<BITS, WG>::CH == 8 ? (t >> 3) & 7 : 0;
 }
 
-template <int BITS, int NMAT>
+template <int BITS, int NMAT, int WG>
 struct MfmaStage {
-  using G = MfmaGeo<BITS>;
+  using G = MfmaGeo<BITS, WG>;
+  static constexpr int TOK = MfmaCfg<WG>::TOK;
   static constexpr int W = NMAT * kMfmaRows * G::RB;   // weight bytes
-  static constexpr int X = kMfmaTokens * G::XR;        // code bytes
-  static constexpr int D = kMfmaTokens * G::CH * 4;    // scale bytes
+  static constexpr int X = TOK * G::XR;                // code bytes
+  static constexpr int D = TOK * G::CH * 4;            // scale bytes
   static constexpr int BYTES = W + X + D;
+  // ring depth: as many stages as fit, all but one in flight
+  static constexpr int RING = MfmaCfg<WG>::RING;
+  static constexpr int STAGES = RING / BYTES < kMaxStages ? RING / BYTES : kMaxStages;
+  static_assert(STAGES >= 3, "ring depth");
   // load instructions per wave per stage
   static constexpr int NW = W / 16 / kMfmaThreads;
-  static constexpr int NX = X / 16 / kMfmaThreads;
+  // code pieces: NX instructions of XPW lanes each per wave
+  static constexpr int PX = X / 16;
+  static constexpr int NX = PX >= kMfmaThreads ? PX / kMfmaThreads : 1;
+  static constexpr int XPW = PX >= kMfmaThreads ? 64 : PX / kMfmaWaves;
   static constexpr int NL = NW + NX + 1;
-  static_assert(W % (16 * kMfmaThreads) == 0 && X % (16 * kMfmaThreads) == 0, "stage split");
-  static_assert(kMfmaTokens * G::CH <= 64 * kMfmaWaves && kMfmaTokens * G::CH % kMfmaWaves == 0,
+  static_assert(W % (16 * kMfmaThreads) == 0 && NX * kMfmaWaves * XPW == PX, "stage split");
+  static_assert(TOK * G::CH <= 64 * kMfmaWaves && TOK * G::CH % kMfmaWaves == 0,
                 "one scale instruction per wave");
 };
 
-template <int BITS, int NMAT>
+template <int BITS, int NMAT, int WG>
 struct MfmaLds {
-  __align__(16) unsigned char ring[kStages][MfmaStage<BITS, NMAT>::BYTES];
-  int trow[kMfmaTokens];  // activation row of each token slot (clamped past the item)
+  __align__(16) unsigned char ring[MfmaStage<BITS, NMAT, WG>::STAGES][MfmaStage<BITS, NMAT, WG>::BYTES];
+  int trow[MfmaCfg<WG>::TOK];  // activation row of each token slot (clamped past the item)
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -249,15 +280,27 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
+// Wait until at most `later` stages of NL loads each are in flight (later
+// <= L): the oldest stage has landed.
+template <int NL, int L>
+__device__ __forceinline__ void wait_stages_left(int later) {
+  if constexpr (L == 0) {
+    wait_vm_lgkm0<0>();
+  } else {
+    if (later >= L) wait_vm_lgkm0<NL * L>();
+    else wait_stages_left<NL, L - 1>(later);
+  }
+}
+
 // nrows[m]: rows of matrix m that exist (>= 1; rows past it load its last).
 // act_rows bounds the activation rows the item's tokens name (trow).
-template <int BITS, int NMAT, int NTT, typename Acc>
+template <int BITS, int NMAT, int NTT, int WG, typename Acc>
 __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int *nrows,
                                           size_t row_bytes, const int8_t *act, const float *actd,
-                                          int K, int act_rows, MfmaLds<BITS, NMAT> &L,
-                                          Acc (*acc)[kMfmaTiles][4]) {
-  using G = MfmaGeo<BITS>;
-  using ST = MfmaStage<BITS, NMAT>;
+                                          int K, int act_rows, MfmaLds<BITS, NMAT, WG> &L,
+                                          Acc (*acc)[MfmaCfg<WG>::TILES][4]) {
+  using G = MfmaGeo<BITS, WG>;
+  using ST = MfmaStage<BITS, NMAT, WG>;
   constexpr int SH = wshift<BITS>();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, g = lane >> 4;
@@ -285,24 +328,24 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
     const int q = (i * kMfmaWaves + wave) * 64 + lane;
     const int m = (i * kMfmaWaves * 64) / (kMfmaRows * G::PPR);
     const int r = (q / G::PPR) % kMfmaRows, pl = q % G::PPR;
-    woff[i] = (uint32_t)((size_t)min(r, nrows[m] - 1) * row_bytes) + 16u * (uint32_t)(pl ^ wkey<BITS>(r));
+    woff[i] = (uint32_t)((size_t)min(r, nrows[m] - 1) * row_bytes) + 16u * (uint32_t)(pl ^ wkey<BITS, WG>(r));
   }
 #pragma unroll
   for (int i = 0; i < ST::NX; ++i) {
-    const int q = (i * kMfmaWaves + wave) * 64 + lane;
+    const int q = min((i * kMfmaWaves + wave) * ST::XPW + lane, ST::PX - 1);
     const int t = q / G::XPR, pl = q % G::XPR;
-    xoff[i] = (uint32_t)L.trow[t] * (uint32_t)K + 16u * (uint32_t)(pl ^ xkey<BITS>(t));
+    xoff[i] = (uint32_t)L.trow[t] * (uint32_t)K + 16u * (uint32_t)(pl ^ xkey<BITS, WG>(t));
   }
   {
-    constexpr int per = kMfmaTokens * G::CH / kMfmaWaves;
+    constexpr int per = ST::TOK * G::CH / kMfmaWaves;
     const int q = wave * per + lane;
-    const int t = min(q / G::CH, kMfmaTokens - 1), bl = q % G::CH;
-    doff = 4u * ((uint32_t)L.trow[t] * (uint32_t)nbk + (uint32_t)(bl ^ dkey<BITS>(t)));
+    const int t = min(q / G::CH, ST::TOK - 1), bl = q % G::CH;
+    doff = 4u * ((uint32_t)L.trow[t] * (uint32_t)nbk + (uint32_t)(bl ^ dkey<BITS, WG>(t)));
   }
 
   // one stage's loads: every wave issues ST::NL instructions
   auto issue = [&](int c) {
-    unsigned char *buf = L.ring[c % kStages];
+    unsigned char *buf = L.ring[c % ST::STAGES];
     if (lane_offs && (c + 1) * G::CH <= nbk) {
       // a full stage: wave-uniform bases plus the lanes' fixed offsets
 #pragma unroll
@@ -315,10 +358,11 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
 #pragma unroll
       for (int i = 0; i < ST::NX; ++i) {
         const int8_t *src = act + (size_t)c * G::XR + xoff[i];
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + (size_t)(i * kMfmaWaves + wave) * 64 * 16),
-                                         16, 0, 0);
+        if (ST::XPW == 64 || lane < ST::XPW)
+          __builtin_amdgcn_global_load_lds(
+              src, (lds_void *)(buf + ST::W + (size_t)(i * kMfmaWaves + wave) * ST::XPW * 16), 16, 0, 0);
       }
-      constexpr int per = kMfmaTokens * G::CH / kMfmaWaves;
+      constexpr int per = ST::TOK * G::CH / kMfmaWaves;
       if (lane < per) {
         const uint8_t *src = reinterpret_cast<const uint8_t *>(actd + (size_t)c * G::CH) + doff;
         __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + ST::X + (size_t)wave * per * 4),
@@ -333,26 +377,27 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
     for (int i = 0; i < ST::NW; ++i) {
       const int q0 = (i * kMfmaWaves + wave) * 64, q = q0 + lane;
       const int m = q / (kMfmaRows * G::PPR), r = (q / G::PPR) % kMfmaRows, pl = q % G::PPR;
-      const int gp = min(pl ^ wkey<BITS>(r), valid_w / 16 - 1);
+      const int gp = min(pl ^ wkey<BITS, WG>(r), valid_w / 16 - 1);
       const int rr = min(r, nrows[m] - 1);
       const uint8_t *src = wbase[m] + (size_t)rr * row_bytes + (size_t)c * G::RB + 16 * gp;
       __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + (size_t)q0 * 16), 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < ST::NX; ++i) {
-      const int q0 = (i * kMfmaWaves + wave) * 64, q = q0 + lane;
+      const int q0 = (i * kMfmaWaves + wave) * ST::XPW, q = min(q0 + lane, ST::PX - 1);
       const int t = q / G::XPR, pl = q % G::XPR;
-      const int gp = min(pl ^ xkey<BITS>(t), valid_x / 16 - 1);
+      const int gp = min(pl ^ xkey<BITS, WG>(t), valid_x / 16 - 1);
       const int8_t *src = act + (size_t)L.trow[t] * K + (size_t)c * G::XR + 16 * gp;
-      __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + (size_t)q0 * 16), 16, 0, 0);
+      if (ST::XPW == 64 || lane < ST::XPW)
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + (size_t)q0 * 16), 16, 0, 0);
     }
     {
       // the scales: wave w loads words [w * per, (w + 1) * per) of the stage
-      constexpr int per = kMfmaTokens * G::CH / kMfmaWaves;
+      constexpr int per = ST::TOK * G::CH / kMfmaWaves;
       const int q = wave * per + lane;
       if (lane < per) {
         const int t = q / G::CH, bl = q % G::CH;
-        const int bg = min(c * G::CH + (bl ^ dkey<BITS>(t)), nbk - 1);
+        const int bg = min(c * G::CH + (bl ^ dkey<BITS, WG>(t)), nbk - 1);
         const float *src = actd + (size_t)L.trow[t] * nbk + bg;
         __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + ST::X + (size_t)wave * per * 4),
                                          4, 0, 0);
@@ -365,7 +410,7 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
   auto a_raw = [&](const unsigned char *buf, int b, int m) -> WRaw<BITS> {
     const int r = 16 * wave + li;
     const unsigned char *wrow = buf + (size_t)(m * kMfmaRows + r) * G::RB;
-    const int key = wkey<BITS>(r);
+    const int key = wkey<BITS, WG>(r);
     if constexpr (BITS == 8) {
       const int pc = (2 * b + (g >> 1)) ^ key;
       return *reinterpret_cast<const uint64_t *>(wrow + 16 * pc + 8 * (g & 1));
@@ -379,13 +424,13 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
   // B operand (token tile tt's codes) and the tokens' block scale
   auto b_op = [&](const unsigned char *buf, int b, int tt) -> long {
     const int t = 16 * tt + li;
-    const int pc = (2 * b + (g >> 1)) ^ xkey<BITS>(t);
+    const int pc = (2 * b + (g >> 1)) ^ xkey<BITS, WG>(t);
     return *reinterpret_cast<const long *>(buf + ST::W + (size_t)t * G::XR + 16 * pc + 8 * (g & 1));
   };
   auto b_scale = [&](const unsigned char *buf, int b, int tt) -> float {
     const int t = 16 * tt + li;
     return *reinterpret_cast<const float *>(buf + ST::W + ST::X +
-                                            ((size_t)t * G::CH + (b ^ dkey<BITS>(t))) * 4);
+                                            ((size_t)t * G::CH + (b ^ dkey<BITS, WG>(t))) * 4);
   };
   // the block's exact int32 sums times the token's block scale
   auto scale_acc = [&](Acc *a4, const v4i &cm, float dj) {
@@ -458,16 +503,15 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
   };
 
 #pragma unroll
-  for (int c = 0; c < kStages - 1; ++c)
+  for (int c = 0; c < ST::STAGES - 1; ++c)
     if (c < nst) issue(c);
   for (int c = 0; c < nst; ++c) {
     // this wave's loads of stage c are done once at most the later stages'
     // remain; the barrier makes every wave's visible and frees stage c - 1
-    if (c + 1 < nst) wait_vm_lgkm0<ST::NL * (kStages - 2)>();
-    else wait_vm_lgkm0<0>();
+    wait_stages_left<ST::NL, ST::STAGES - 2>(min(ST::STAGES - 2, nst - 1 - c));
     __builtin_amdgcn_s_barrier();
-    if (c + kStages - 1 < nst) issue(c + kStages - 1);
-    const unsigned char *buf = L.ring[c % kStages];
+    if (c + ST::STAGES - 1 < nst) issue(c + ST::STAGES - 1);
+    const unsigned char *buf = L.ring[c % ST::STAGES];
     const int cb = min(G::CH, nbk - c * G::CH);
     if (cb == G::CH) {
       // a full stage in one pipelined run (one or two token tiles), or in
@@ -492,22 +536,26 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
   __builtin_amdgcn_s_barrier();  // every wave is done with the ring (no load is in flight)
 }
 
-template <int BITS, int NMAT, typename Acc>
+template <int BITS, int NMAT, int WG, typename Acc>
 __device__ __forceinline__ void mfma_core_ntt(int ntt, const uint8_t *const *wbase, const int *nrows,
                                               size_t row_bytes, const int8_t *act, const float *actd,
-                                              int K, int act_rows, MfmaLds<BITS, NMAT> &L,
-                                              Acc (*acc)[kMfmaTiles][4]) {
-  switch (ntt) {
-    case 1: mfma_core<BITS, NMAT, 1>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc); break;
-    case 2: mfma_core<BITS, NMAT, 2>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc); break;
-    case 3: mfma_core<BITS, NMAT, 3>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc); break;
-    default: mfma_core<BITS, NMAT, 4>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc); break;
+                                              int K, int act_rows, MfmaLds<BITS, NMAT, WG> &L,
+                                              Acc (*acc)[MfmaCfg<WG>::TILES][4]) {
+  constexpr int TILES = MfmaCfg<WG>::TILES;
+  if (ntt <= 1) {
+    mfma_core<BITS, NMAT, 1, WG>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc);
+  } else if (ntt == 2 || TILES == 2) {
+    mfma_core<BITS, NMAT, 2, WG>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc);
+  } else if constexpr (TILES >= 4) {
+    if (ntt == 3) mfma_core<BITS, NMAT, 3, WG>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc);
+    else mfma_core<BITS, NMAT, 4, WG>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc);
   }
 }
 
 // Token slots of an item: activation row of each (clamped past nt), into LDS.
+template <int TOK>
 __device__ __forceinline__ void item_rows(const FfnArgs &a, const MfmaItem &it, bool hrows, int *trow) {
-  for (int n = threadIdx.x; n < kMfmaTokens; n += kMfmaThreads) {
+  for (int n = threadIdx.x; n < TOK; n += kMfmaThreads) {
     int t = 0, hrow = 0, j;
     tok_at(a, true, it.s, it.n0 + min(n, it.nt - 1), t, hrow, j);
     trow[n] = hrows ? hrow : t;
@@ -519,29 +567,33 @@ __device__ __forceinline__ void item_rows(const FfnArgs &a, const MfmaItem &it, 
 // Gate/up + SwiGLU + Q8_0(h): rows [128 rb, +128) of gate and up for up to
 // 64 tokens of one expert.  Wave w owns rows 16 w .. 16 w + 15 of both.
 // ---------------------------------------------------------------------------
+constexpr int kGateupWg = 1;
+
 template <int BITS>
-__global__ __launch_bounds__(kMfmaThreads) void k_gateup_mfma(FfnArgs a) {
-  __shared__ MfmaLds<BITS, 2> L;
+__global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 * kGateupWg))) void k_gateup_mfma(FfnArgs a) {
+  constexpr int WG = kGateupWg;
+  constexpr int TOK = MfmaCfg<WG>::TOK, TILES = MfmaCfg<WG>::TILES;
+  __shared__ MfmaLds<BITS, 2, WG> L;
   const int H = a.L.H, I = a.L.I;
   MfmaItem it;
-  if (!mfma_item(a, (I + kMfmaRows - 1) / kMfmaRows, it)) return;
+  if (!mfma_item<WG>(a, (I + kMfmaRows - 1) / kMfmaRows, it)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, g = lane >> 4;
   const ExpertPtrs ep = expert_ptrs(a.L, it.e);
   const size_t row_bytes = (size_t)H * BITS / 8;
   const int rb0 = it.rb * kMfmaRows, nrows = min(kMfmaRows, I - rb0);
-  item_rows(a, it, false, L.trow);
+  item_rows<TOK>(a, it, false, L.trow);
   const uint8_t *wb[2] = {ep.wg + (size_t)rb0 * row_bytes, ep.wu + (size_t)rb0 * row_bytes};
   const int nr[2] = {nrows, nrows};
   // g and u accumulate in binary64 (the expert definition's sum, rounded
   // once), so h -- and its Q8_0 codes -- are those of that definition
-  double acc[2][kMfmaTiles][4];
+  double acc[2][TILES][4];
   const int ntt = (it.nt + 15) >> 4;
-  mfma_core_ntt<BITS, 2>(ntt, wb, nr, row_bytes, a.xq, a.xd, H, a.T, L, acc);
+  mfma_core_ntt<BITS, 2, WG>(ntt, wb, nr, row_bytes, a.xq, a.xd, H, a.T, L, acc);
 
   // h = silu(g) * u for rows 4 g + r of the wave, token 16 tt + li, staged
   // in LDS (over the ring) for the Q8_0 step
-  static_assert(sizeof(float) * kMfmaTokens * (kMfmaRows + 1) <= sizeof(L.ring), "h tile");
+  static_assert(sizeof(float) * TOK * (kMfmaRows + 1) <= sizeof(L.ring), "h tile");
   float(*hs)[kMfmaRows + 1] = reinterpret_cast<float(*)[kMfmaRows + 1]>(&L.ring[0][0]);
   const int rw = 16 * wave + 4 * g;  // the lane's first row in the block
   float sg[4], su[4];
@@ -552,7 +604,7 @@ __global__ __launch_bounds__(kMfmaThreads) void k_gateup_mfma(FfnArgs a) {
     su[r] = ep.su[row];
   }
 #pragma unroll
-  for (int tt = 0; tt < kMfmaTiles; ++tt)
+  for (int tt = 0; tt < TILES; ++tt)
     if (tt < ntt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -585,25 +637,31 @@ __global__ __launch_bounds__(kMfmaThreads) void k_gateup_mfma(FfnArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kDownRows = 2 * kMfmaRows;
 
+// two resident workgroups, except for int2 (whose core would not fit 128 VGPRs)
 template <int BITS>
-__global__ __launch_bounds__(kMfmaThreads) void k_down_mfma(FfnArgs a) {
-  __shared__ MfmaLds<BITS, 2> L;
+constexpr int down_wg() { return BITS == 2 ? 1 : 2; }
+
+template <int BITS>
+__global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 * down_wg<BITS>()))) void k_down_mfma(FfnArgs a) {
+  constexpr int WG = down_wg<BITS>();
+  constexpr int TOK = MfmaCfg<WG>::TOK, TILES = MfmaCfg<WG>::TILES;
+  __shared__ MfmaLds<BITS, 2, WG> L;
   const int H = a.L.H, I = a.L.I;
   MfmaItem it;
-  if (!mfma_item(a, (H + kDownRows - 1) / kDownRows, it)) return;
+  if (!mfma_item<WG>(a, (H + kDownRows - 1) / kDownRows, it)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, g = lane >> 4;
   const ExpertPtrs ep = expert_ptrs(a.L, it.e);
   const size_t row_bytes = (size_t)I * BITS / 8;
   const int rb0 = it.rb * kDownRows, nrows = min(kDownRows, H - rb0);
-  item_rows(a, it, true, L.trow);
+  item_rows<TOK>(a, it, true, L.trow);
   // half 1 may not exist at the matrix edge: its loads then read half 0's rows
   const int nr[2] = {min(nrows, kMfmaRows), max(1, nrows - kMfmaRows)};
   const uint8_t *wb[2] = {ep.wd + (size_t)rb0 * row_bytes,
                           ep.wd + (size_t)(nrows > kMfmaRows ? rb0 + kMfmaRows : rb0) * row_bytes};
-  float acc[2][kMfmaTiles][4];
+  float acc[2][TILES][4];
   const int ntt = (it.nt + 15) >> 4;
-  mfma_core_ntt<BITS, 2>(ntt, wb, nr, row_bytes, a.hq, a.hd, I, a.T * (a.k + 1), L, acc);
+  mfma_core_ntt<BITS, 2, WG>(ntt, wb, nr, row_bytes, a.hq, a.hd, I, a.T * (a.k + 1), L, acc);
 
   const int rw = 16 * wave + 4 * g;
 #pragma unroll
@@ -614,7 +672,7 @@ __global__ __launch_bounds__(kMfmaThreads) void k_down_mfma(FfnArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) sd[r] = ep.sd[rb0 + row + r];
 #pragma unroll
-    for (int tt = 0; tt < kMfmaTiles; ++tt) {
+    for (int tt = 0; tt < TILES; ++tt) {
       const int n = 16 * tt + li;
       if (tt < ntt && n < it.nt) {
         int t, hrow, j;
@@ -631,19 +689,22 @@ __global__ __launch_bounds__(kMfmaThreads) void k_down_mfma(FfnArgs a) {
 }
 
 // Upper bound of the token groups a batch can send here: routed pairs in
-// groups of 64 plus one partial group per unique expert that can reach
+// groups of tok plus one partial group per unique expert that can reach
 // mfma_min tokens (at most pairs / mfma_min of them), plus the shared
 // expert's groups when the batch reaches its threshold.
-static int mfma_group_bound(const FfnArgs &a) {
+static int mfma_group_bound(const FfnArgs &a, int tok) {
   const long pairs = (long)a.T * a.k;
   long cap = pairs < a.E ? pairs : a.E;
   if (pairs / a.mfma_min < cap) cap = pairs / a.mfma_min;
-  const long shared = a.T >= a.mfma_min_shared ? (a.T + kMfmaTokens - 1) / kMfmaTokens : 0;
-  return (int)((pairs + kMfmaTokens - 1) / kMfmaTokens + cap + shared);
+  const long shared = a.T >= a.mfma_min_shared ? (a.T + tok - 1) / tok : 0;
+  return (int)((pairs + tok - 1) / tok + cap + shared);
 }
 
 // Grid: one workgroup per item (an upper bound; surplus workgroups exit).
-static int mfma_grid(const FfnArgs &a, int n_rb) { return mfma_group_bound(a) * n_rb; }
+template <int WG>
+static dim3 mfma_grid(const FfnArgs &a, int n_rb) {
+  return dim3((unsigned)(mfma_group_bound(a, MfmaCfg<WG>::TOK) * n_rb));
+}
 
 hipError_t launch_mfma_items(const FfnArgs &a, int32_t *mgofs, hipStream_t st) {
   hipLaunchKernelGGL(k_mfma_items, dim3(1), dim3(1024), 0, st, a, mgofs);
@@ -651,7 +712,7 @@ hipError_t launch_mfma_items(const FfnArgs &a, int32_t *mgofs, hipStream_t st) {
 }
 
 hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t st, KEvents ev) {
-  const dim3 grid((unsigned)mfma_grid(a, (a.L.I + kMfmaRows - 1) / kMfmaRows)), block(kMfmaThreads);
+  const dim3 grid = mfma_grid<kGateupWg>(a, (a.L.I + kMfmaRows - 1) / kMfmaRows), block(kMfmaThreads);
   switch (a.L.bits) {
     case 8: COLI_LAUNCH(ev, k_gateup_mfma<8>, grid, block, 0, st, a); break;
     case 4: COLI_LAUNCH(ev, k_gateup_mfma<4>, grid, block, 0, st, a); break;
@@ -662,11 +723,12 @@ hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t st, KEvents ev) {
 }
 
 hipError_t launch_down_mfma(const FfnArgs &a, hipStream_t st, KEvents ev) {
-  const dim3 grid((unsigned)mfma_grid(a, (a.L.H + kDownRows - 1) / kDownRows)), block(kMfmaThreads);
+  const int n_rb = (a.L.H + kDownRows - 1) / kDownRows;
+  const dim3 block(kMfmaThreads);
   switch (a.L.bits) {
-    case 8: COLI_LAUNCH(ev, k_down_mfma<8>, grid, block, 0, st, a); break;
-    case 4: COLI_LAUNCH(ev, k_down_mfma<4>, grid, block, 0, st, a); break;
-    case 2: COLI_LAUNCH(ev, k_down_mfma<2>, grid, block, 0, st, a); break;
+    case 8: COLI_LAUNCH(ev, k_down_mfma<8>, mfma_grid<down_wg<8>()>(a, n_rb), block, 0, st, a); break;
+    case 4: COLI_LAUNCH(ev, k_down_mfma<4>, mfma_grid<down_wg<4>()>(a, n_rb), block, 0, st, a); break;
+    case 2: COLI_LAUNCH(ev, k_down_mfma<2>, mfma_grid<down_wg<2>()>(a, n_rb), block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
