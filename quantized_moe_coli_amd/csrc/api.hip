@@ -81,7 +81,7 @@ coli::RouterCfg to_cfg(const coli_router_cfg &c) {
 }
 
 struct WsLayout {
-  size_t ctr, xq, xd, logits, idx, w, counts, offs, perm, uniq, nuniq, mgofs, hq, hd, hsh, obuf,
+  size_t ctr, xq, xd, xd64, logits, idx, w, counts, offs, perm, uniq, nuniq, mgofs, hq, hd, hsh, obuf,
       total;
 };
 
@@ -98,6 +98,7 @@ WsLayout ws_layout(const coli_moe_layer *L, int Tmax) {
   w.ctr = take(COLI_WORKSPACE_COUNTER_BYTES);  // decode counters: zero before first use, left zero
   w.xq = take(T * H);
   w.xd = take(T * (H / 32) * 4);
+  w.xd64 = take(Tmax >= 2 ? T * coli::xd64_ld(H) * 8 : 0);  // union batches only
   w.logits = take(T * E * 4);
   w.idx = take(T * k * 4);
   w.w = take(T * k * 4);
@@ -504,9 +505,12 @@ coli_status forward_impl(const coli_moe_layer *L, const CacheRun *cache, const f
                                     reinterpret_cast<float *>(base + ws.hsh), s, kev(0));
       if (e != hipErrorNotSupported) return from_hip(e);
     }
-    // activations -> Q8_0 codes, and the router logits unless supplied
+    // activations -> Q8_0 codes (union batches: their scales in binary64
+    // too, for the matrix cores), and the router logits unless supplied
+    double *xd64 = T >= 2 ? reinterpret_cast<double *>(base + ws.xd64) : nullptr;
+    fa.xd64 = xd64;
     e = coli::launch_front(L->qtype, x, logits_in ? nullptr : L->gate_w, fa.loff, T, E, H, lp_dst,
-                           xq, xd, s, kev(0));
+                           xq, xd, s, kev(0), xd64);
     if (e != hipSuccess) return COLI_ERR_DEVICE;
     if (T == 1) {
       // decode on other shapes: each gate/up workgroup selects the experts itself

@@ -103,17 +103,21 @@ hipError_t launch_quant_pack_fp8(int bits, const uint8_t *w8, const float *bscal
                                  int64_t cols, uint8_t *q, float *scale, hipStream_t st);
 hipError_t launch_gemv_f32act(int bits, const uint8_t *W, const float *scale, int64_t rows,
                               int64_t cols, const float *x, float *y, hipStream_t st);
+// Row stride of the binary64 copy of the Q8_0 block scales (d64, for the
+// matrix-core gate/up): the blocks of a row rounded up to a multiple of 8.
+__host__ __device__ inline int xd64_ld(int64_t n) { return (int)(((n / 32 + 7) / 8) * 8); }
 hipError_t launch_act_quant(int layout_bits, const float *x, int64_t T, int64_t n, int8_t *q,
-                            float *d, hipStream_t st, KEvents ev = {});
+                            float *d, hipStream_t st, KEvents ev = {}, double *d64 = nullptr);
 
 hipError_t launch_logits(const float *x, const float *gate_w, int T, int E, int H, float *logits,
                          hipStream_t st);
 // Router logits (if gate_w) and Q8_0 activations in container BITS ordering
 // (if xq), in as few launches as the batch allows.
 // loff: optional [E] terms added to each computed logit.
+// xd64: optional binary64 copy of xd (row stride xd64_ld(H)).
 hipError_t launch_front(int bits, const float *x, const float *gate_w, const float *loff, int T,
                         int E, int H, float *logits, int8_t *xq, float *xd, hipStream_t st,
-                        KEvents ev = {});
+                        KEvents ev = {}, double *xd64 = nullptr);
 hipError_t launch_route(const RouterCfg &cfg, const float *logits, const float *bias, int T,
                         int32_t *idx, float *w, int32_t *idx_copy, float *w_copy, hipStream_t st);
 hipError_t launch_dispatch(const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offs,
@@ -129,6 +133,7 @@ struct FfnArgs {
   int T, k, E;
   const int8_t *xq;     // [T][H], ordering of L.bits
   const float *xd;      // [T][H/32]
+  const double *xd64;   // union: xd in binary64, [T][xd64_ld(H)]
   int32_t *idx;         // [T][k] (decode: written by the gate/up kernel)
   float *w;             // [T][k]
   // decode mode: the gate/up kernel selects the experts itself

@@ -236,18 +236,35 @@ __device__ __forceinline__ int xkey(int t) {
   using G = MfmaGeo<BITS, WG>;
   return (t / G::KX) & (G::XPR - 1);
 }
-template <int BITS, int WG>
-__device__ __forceinline__ int dkey(int t) {
-  return MfmaGeo<BITS, WG>::CH == 8 ? (t >> 3) & 7 : 0;
-}
+// The block scales of a stage, binary32 (4-byte words) or binary64 (16-byte
+// pieces of two): per token CH scales in SPT pieces of PB bytes; the lanes
+// reading one block's scale for 16 tokens hit distinct banks.
+template <int CH, typename SC>
+struct ScaleGeo {
+  static constexpr bool F64 = sizeof(SC) == 8;
+  static constexpr int PB = F64 ? 16 : 4;               // bytes per load piece
+  static constexpr int SPT = CH * (int)sizeof(SC) / PB;  // pieces per token
+  static constexpr int KD = F64 ? 256 / (CH * 8) : 8;   // tokens per key step
+  __device__ static int key(int t) {
+    if constexpr (F64) return (t / KD) & (SPT - 1);
+    else return CH == 8 ? (t >> 3) & 7 : 0;
+  }
+  // LDS byte offset of token t's scale of block b within the stage's scales
+  __device__ static int at(int t, int b) {
+    if constexpr (F64) return t * CH * 8 + 16 * ((b >> 1) ^ key(t)) + 8 * (b & 1);
+    else return (t * CH + (b ^ key(t))) * 4;
+  }
+};
 
-template <int BITS, int NMAT, int WG>
+template <int BITS, int NMAT, int WG, typename SC>
 struct MfmaStage {
   using G = MfmaGeo<BITS, WG>;
+  using SG = ScaleGeo<G::CH, SC>;
   static constexpr int TOK = MfmaCfg<WG>::TOK;
   static constexpr int W = NMAT * kMfmaRows * G::RB;   // weight bytes
   static constexpr int X = TOK * G::XR;                // code bytes
-  static constexpr int D = TOK * G::CH * 4;            // scale bytes
+  static constexpr int D = TOK * G::CH * (int)sizeof(SC);  // scale bytes
+  static constexpr int DPW = D / SG::PB / kMfmaWaves;  // scale pieces per wave (one instruction)
   static constexpr int BYTES = W + X + D;
   // ring depth: as many stages as fit, all but one in flight
   static constexpr int RING = MfmaCfg<WG>::RING;
@@ -261,13 +278,13 @@ struct MfmaStage {
   static constexpr int XPW = PX >= kMfmaThreads ? 64 : PX / kMfmaWaves;
   static constexpr int NL = NW + NX + 1;
   static_assert(W % (16 * kMfmaThreads) == 0 && NX * kMfmaWaves * XPW == PX, "stage split");
-  static_assert(TOK * G::CH <= 64 * kMfmaWaves && TOK * G::CH % kMfmaWaves == 0,
-                "one scale instruction per wave");
+  static_assert(DPW <= 64 && DPW * kMfmaWaves * SG::PB == D, "one scale instruction per wave");
 };
 
-template <int BITS, int NMAT, int WG>
+template <int BITS, int NMAT, int WG, typename SC>
 struct MfmaLds {
-  __align__(16) unsigned char ring[MfmaStage<BITS, NMAT, WG>::STAGES][MfmaStage<BITS, NMAT, WG>::BYTES];
+  using ST = MfmaStage<BITS, NMAT, WG, SC>;
+  __align__(16) unsigned char ring[ST::STAGES][ST::BYTES];
   int trow[MfmaCfg<WG>::TOK];  // activation row of each token slot (clamped past the item)
 };
 
@@ -293,15 +310,18 @@ __device__ __forceinline__ void wait_stages_left(int later) {
 }
 
 // nrows[m]: rows of matrix m that exist (>= 1; rows past it load its last).
-// act_rows bounds the activation rows the item's tokens name (trow).
-template <int BITS, int NMAT, int NTT, int WG, typename Acc>
+// act_rows bounds the activation rows the item's tokens name (trow); actd
+// holds each row's block scales at a stride of sld.  The results are the
+// sums of the widened (x 2^wshift) codes: the caller scales them back.
+template <int BITS, int NMAT, int NTT, int WG, typename Acc, typename SC>
 __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int *nrows,
-                                          size_t row_bytes, const int8_t *act, const float *actd,
-                                          int K, int act_rows, MfmaLds<BITS, NMAT, WG> &L,
+                                          size_t row_bytes, const int8_t *act, const SC *actd,
+                                          int sld, int K, int act_rows,
+                                          MfmaLds<BITS, NMAT, WG, SC> &L,
                                           Acc (*acc)[MfmaCfg<WG>::TILES][4]) {
   using G = MfmaGeo<BITS, WG>;
-  using ST = MfmaStage<BITS, NMAT, WG>;
-  constexpr int SH = wshift<BITS>();
+  using ST = MfmaStage<BITS, NMAT, WG, SC>;
+  using SG = typename ST::SG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, g = lane >> 4;
   const int nbk = K / 32, nst = (nbk + G::CH - 1) / G::CH;
@@ -337,10 +357,9 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
     xoff[i] = (uint32_t)L.trow[t] * (uint32_t)K + 16u * (uint32_t)(pl ^ xkey<BITS, WG>(t));
   }
   {
-    constexpr int per = ST::TOK * G::CH / kMfmaWaves;
-    const int q = wave * per + lane;
-    const int t = min(q / G::CH, ST::TOK - 1), bl = q % G::CH;
-    doff = 4u * ((uint32_t)L.trow[t] * (uint32_t)nbk + (uint32_t)(bl ^ dkey<BITS, WG>(t)));
+    const int q = wave * ST::DPW + lane;
+    const int t = min(q / SG::SPT, ST::TOK - 1), p = q % SG::SPT;
+    doff = (uint32_t)L.trow[t] * (uint32_t)(sld * sizeof(SC)) + (uint32_t)(SG::PB * (p ^ SG::key(t)));
   }
 
   // one stage's loads: every wave issues ST::NL instructions
@@ -362,11 +381,10 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
           __builtin_amdgcn_global_load_lds(
               src, (lds_void *)(buf + ST::W + (size_t)(i * kMfmaWaves + wave) * ST::XPW * 16), 16, 0, 0);
       }
-      constexpr int per = ST::TOK * G::CH / kMfmaWaves;
-      if (lane < per) {
+      if (lane < ST::DPW) {
         const uint8_t *src = reinterpret_cast<const uint8_t *>(actd + (size_t)c * G::CH) + doff;
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + ST::X + (size_t)wave * per * 4),
-                                         4, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + ST::X + (size_t)wave * ST::DPW * SG::PB),
+                                         SG::PB, 0, 0);
       }
       return;
     }
@@ -392,15 +410,20 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
         __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + (size_t)q0 * 16), 16, 0, 0);
     }
     {
-      // the scales: wave w loads words [w * per, (w + 1) * per) of the stage
-      constexpr int per = ST::TOK * G::CH / kMfmaWaves;
-      const int q = wave * per + lane;
-      if (lane < per) {
-        const int t = q / G::CH, bl = q % G::CH;
-        const int bg = min(c * G::CH + (bl ^ dkey<BITS, WG>(t)), nbk - 1);
-        const float *src = actd + (size_t)L.trow[t] * nbk + bg;
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + ST::X + (size_t)wave * per * 4),
-                                         4, 0, 0);
+      // the scales: wave w loads pieces [w * DPW, (w + 1) * DPW) of the
+      // stage (binary64 rows are padded to whole stages: no clamp)
+      const int q = wave * ST::DPW + lane;
+      if (lane < ST::DPW) {
+        const int t = q / SG::SPT, p = q % SG::SPT;
+        size_t off;
+        if constexpr (SG::F64) {
+          off = (size_t)L.trow[t] * sld * 8 + (size_t)c * G::CH * 8 + SG::PB * (p ^ SG::key(t));
+        } else {
+          off = ((size_t)L.trow[t] * sld + min(c * G::CH + (p ^ SG::key(t)), nbk - 1)) * 4;
+        }
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(actd) + off;
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + ST::W + ST::X + (size_t)wave * ST::DPW * SG::PB),
+                                         SG::PB, 0, 0);
       }
     }
   };
@@ -427,26 +450,14 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
     const int pc = (2 * b + (g >> 1)) ^ xkey<BITS, WG>(t);
     return *reinterpret_cast<const long *>(buf + ST::W + (size_t)t * G::XR + 16 * pc + 8 * (g & 1));
   };
-  auto b_scale = [&](const unsigned char *buf, int b, int tt) -> float {
-    const int t = 16 * tt + li;
-    return *reinterpret_cast<const float *>(buf + ST::W + ST::X +
-                                            ((size_t)t * G::CH + (b ^ dkey<BITS, WG>(t))) * 4);
+  auto b_scale = [&](const unsigned char *buf, int b, int tt) -> SC {
+    return *reinterpret_cast<const SC *>(buf + ST::W + ST::X + SG::at(16 * tt + li, b));
   };
-  // the block's exact int32 sums times the token's block scale
-  auto scale_acc = [&](Acc *a4, const v4i &cm, float dj) {
-    if constexpr (std::is_same<Acc, double>::value) {
-      // the x16 / x64 widening folded into the scale: exact in binary64
-      const double djs = (double)dj * (1.0 / (double)(1 << SH));
+  // the block's exact int32 sums (of the widened codes, below 2^24 in
+  // magnitude, so exact in either type) times the token's block scale
+  auto scale_acc = [&](Acc *a4, const v4i &cm, SC dj) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a4[r] += (double)cm[r] * djs;
-    } else {
-      // the sums are multiples of 2^SH below 2^24 in magnitude, so taking
-      // 2^-SH into the scale gives the product of the unshifted sum (short
-      // of a subnormal scale)
-      const float djs = dj * (1.0f / (float)(1 << SH));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) a4[r] += (float)cm[r] * djs;
-    }
+    for (int r = 0; r < 4; ++r) a4[r] += (Acc)cm[r] * (Acc)dj;
   };
 
   auto block_step = [&](const unsigned char *buf, int b) {
@@ -456,7 +467,7 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
       const long bx = b_op(buf, b, tt);
-      const float dj = b_scale(buf, b, tt);
+      const SC dj = b_scale(buf, b, tt);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
         const v4i cm = __builtin_amdgcn_mfma_i32_16x16x32_i8(aw[m], bx, zero, 0, 0, 0);
@@ -475,7 +486,7 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
     constexpr int NM = NB * NTT * NMAT;
     WRaw<BITS> raw[NB][NMAT];
     long bx[NB][NTT];
-    float dj[NB][NTT];
+    SC dj[NB][NTT];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
@@ -536,19 +547,20 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
   __builtin_amdgcn_s_barrier();  // every wave is done with the ring (no load is in flight)
 }
 
-template <int BITS, int NMAT, int WG, typename Acc>
+template <int BITS, int NMAT, int WG, typename Acc, typename SC>
 __device__ __forceinline__ void mfma_core_ntt(int ntt, const uint8_t *const *wbase, const int *nrows,
-                                              size_t row_bytes, const int8_t *act, const float *actd,
-                                              int K, int act_rows, MfmaLds<BITS, NMAT, WG> &L,
+                                              size_t row_bytes, const int8_t *act, const SC *actd,
+                                              int sld, int K, int act_rows,
+                                              MfmaLds<BITS, NMAT, WG, SC> &L,
                                               Acc (*acc)[MfmaCfg<WG>::TILES][4]) {
   constexpr int TILES = MfmaCfg<WG>::TILES;
   if (ntt <= 1) {
-    mfma_core<BITS, NMAT, 1, WG>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc);
+    mfma_core<BITS, NMAT, 1, WG>(wbase, nrows, row_bytes, act, actd, sld, K, act_rows, L, acc);
   } else if (ntt == 2 || TILES == 2) {
-    mfma_core<BITS, NMAT, 2, WG>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc);
+    mfma_core<BITS, NMAT, 2, WG>(wbase, nrows, row_bytes, act, actd, sld, K, act_rows, L, acc);
   } else if constexpr (TILES >= 4) {
-    if (ntt == 3) mfma_core<BITS, NMAT, 3, WG>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc);
-    else mfma_core<BITS, NMAT, 4, WG>(wbase, nrows, row_bytes, act, actd, K, act_rows, L, acc);
+    if (ntt == 3) mfma_core<BITS, NMAT, 3, WG>(wbase, nrows, row_bytes, act, actd, sld, K, act_rows, L, acc);
+    else mfma_core<BITS, NMAT, 4, WG>(wbase, nrows, row_bytes, act, actd, sld, K, act_rows, L, acc);
   }
 }
 
@@ -573,7 +585,7 @@ template <int BITS>
 __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 * kGateupWg))) void k_gateup_mfma(FfnArgs a) {
   constexpr int WG = kGateupWg;
   constexpr int TOK = MfmaCfg<WG>::TOK, TILES = MfmaCfg<WG>::TILES;
-  __shared__ MfmaLds<BITS, 2, WG> L;
+  __shared__ MfmaLds<BITS, 2, WG, double> L;
   const int H = a.L.H, I = a.L.I;
   MfmaItem it;
   if (!mfma_item<WG>(a, (I + kMfmaRows - 1) / kMfmaRows, it)) return;
@@ -589,13 +601,15 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
   // once), so h -- and its Q8_0 codes -- are those of that definition
   double acc[2][TILES][4];
   const int ntt = (it.nt + 15) >> 4;
-  mfma_core_ntt<BITS, 2, WG>(ntt, wb, nr, row_bytes, a.xq, a.xd, H, a.T, L, acc);
+  mfma_core_ntt<BITS, 2, WG>(ntt, wb, nr, row_bytes, a.xq, a.xd64, xd64_ld(H), H, a.T, L, acc);
 
   // h = silu(g) * u for rows 4 g + r of the wave, token 16 tt + li, staged
   // in LDS (over the ring) for the Q8_0 step
   static_assert(sizeof(float) * TOK * (kMfmaRows + 1) <= sizeof(L.ring), "h tile");
   float(*hs)[kMfmaRows + 1] = reinterpret_cast<float(*)[kMfmaRows + 1]>(&L.ring[0][0]);
   const int rw = 16 * wave + 4 * g;  // the lane's first row in the block
+  // the sums are of codes widened by 2^wshift: a power of two, undone exactly
+  constexpr double unw = 1.0 / (double)(1 << wshift<BITS>());
   float sg[4], su[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -608,7 +622,7 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
     if (tt < ntt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        hs[16 * tt + li][rw + r] = swiglu_h(row_out(acc[0][tt][r], sg[r]), row_out(acc[1][tt][r], su[r]));
+        hs[16 * tt + li][rw + r] = swiglu_h(row_out(acc[0][tt][r] * unw, sg[r]), row_out(acc[1][tt][r] * unw, su[r]));
   __syncthreads();
   // Q8_0 of each token's 32-row blocks of h: 32 threads per block
   const int nblk = nrows / 32;
@@ -645,7 +659,7 @@ template <int BITS>
 __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 * down_wg<BITS>()))) void k_down_mfma(FfnArgs a) {
   constexpr int WG = down_wg<BITS>();
   constexpr int TOK = MfmaCfg<WG>::TOK, TILES = MfmaCfg<WG>::TILES;
-  __shared__ MfmaLds<BITS, 2, WG> L;
+  __shared__ MfmaLds<BITS, 2, WG, float> L;
   const int H = a.L.H, I = a.L.I;
   MfmaItem it;
   if (!mfma_item<WG>(a, (H + kDownRows - 1) / kDownRows, it)) return;
@@ -661,13 +675,14 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
                           ep.wd + (size_t)(nrows > kMfmaRows ? rb0 + kMfmaRows : rb0) * row_bytes};
   float acc[2][TILES][4];
   const int ntt = (it.nt + 15) >> 4;
-  mfma_core_ntt<BITS, 2, WG>(ntt, wb, nr, row_bytes, a.hq, a.hd, I, a.T * (a.k + 1), L, acc);
+  mfma_core_ntt<BITS, 2, WG>(ntt, wb, nr, row_bytes, a.hq, a.hd, I / 32, I, a.T * (a.k + 1), L, acc);
 
   const int rw = 16 * wave + 4 * g;
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int row = m * kMfmaRows + rw;  // first of the lane's 4 rows in the block
     if (row >= nrows) continue;          // rows past the matrix: whole quads
+    constexpr float unw = 1.0f / (float)(1 << wshift<BITS>());
     float sd[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) sd[r] = ep.sd[rb0 + row + r];
@@ -678,10 +693,10 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
         int t, hrow, j;
         tok_at(a, true, it.s, it.n0 + n, t, hrow, j);
         float4 o;
-        o.x = acc[m][tt][0] * sd[0];
-        o.y = acc[m][tt][1] * sd[1];
-        o.z = acc[m][tt][2] * sd[2];
-        o.w = acc[m][tt][3] * sd[3];
+        o.x = acc[m][tt][0] * unw * sd[0];
+        o.y = acc[m][tt][1] * unw * sd[1];
+        o.z = acc[m][tt][2] * unw * sd[2];
+        o.w = acc[m][tt][3] * unw * sd[3];
         *reinterpret_cast<float4 *>(a.obuf + ((size_t)t * (a.k + 1) + j) * H + rb0 + row) = o;
       }
     }

@@ -226,16 +226,18 @@ __global__ __launch_bounds__(256) void k_quant_pack_fp8(const uint8_t *__restric
   }
 }
 
-// One thread per Q8_0 block of 32 values (act_quant_block, actq.hpp).
+// One thread per Q8_0 block of 32 values (act_quant_block, actq.hpp); with
+// d64, each block scale also in binary64 (row stride xd64_ld(n)).
 template <int BITS>
 __global__ __launch_bounds__(256) void k_act_quant(const float *__restrict__ x, int64_t T,
                                                    int64_t n, int8_t *__restrict__ q,
-                                                   float *__restrict__ d) {
+                                                   float *__restrict__ d, double *__restrict__ d64) {
   const int64_t nb = n / 32;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * nb) return;
   const int64_t t = i / nb, b = i % nb;
   act_quant_block<BITS>(x + t * n + b * 32, q + t * n + b * 32, d + i);
+  if (d64) d64[t * xd64_ld(n) + b] = (double)d[i];
 }
 
 hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t cols, uint8_t *q,
@@ -398,14 +400,14 @@ hipError_t launch_quant_pack_fp8(int bits, const uint8_t *w8, const float *bscal
 }
 
 hipError_t launch_act_quant(int layout_bits, const float *x, int64_t T, int64_t n, int8_t *q,
-                            float *d, hipStream_t st, KEvents ev) {
+                            float *d, hipStream_t st, KEvents ev, double *d64) {
   const int64_t blocks = T * (n / 32);
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)((blocks + 255) / 256)), block(256);
   switch (layout_bits) {
-    case 8: COLI_LAUNCH(ev, k_act_quant<8>, grid, block, 0, st, x, T, n, q, d); break;
-    case 4: COLI_LAUNCH(ev, k_act_quant<4>, grid, block, 0, st, x, T, n, q, d); break;
-    case 2: COLI_LAUNCH(ev, k_act_quant<2>, grid, block, 0, st, x, T, n, q, d); break;
+    case 8: COLI_LAUNCH(ev, k_act_quant<8>, grid, block, 0, st, x, T, n, q, d, d64); break;
+    case 4: COLI_LAUNCH(ev, k_act_quant<4>, grid, block, 0, st, x, T, n, q, d, d64); break;
+    case 2: COLI_LAUNCH(ev, k_act_quant<2>, grid, block, 0, st, x, T, n, q, d, d64); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -34,7 +34,8 @@ __global__ __launch_bounds__(256) void k_front_small(const float *__restrict__ x
                                                      const float *__restrict__ loff, int T, int E,
                                                      int H, float *__restrict__ out, int nlog,
                                                      int8_t *__restrict__ xq,
-                                                     float *__restrict__ xd) {
+                                                     float *__restrict__ xd,
+                                                     double *__restrict__ xd64) {
   __shared__ double red[4][MAXT];
   const int b = blockIdx.x;
   if (b >= nlog) {
@@ -43,6 +44,7 @@ __global__ __launch_bounds__(256) void k_front_small(const float *__restrict__ x
     if (i >= (int64_t)T * nb) return;
     const int64_t t = i / nb, blk = i % nb;
     act_quant_block<BITS>(x + t * H + blk * 32, xq + t * H + blk * 32, xd + i);
+    if (xd64) xd64[t * xd64_ld(H) + blk] = (double)xd[i];
     return;
   }
   const int e = b;
@@ -162,22 +164,23 @@ __global__ __launch_bounds__(64 * kLogWaves) void k_logits_mfma(const float *__r
 
 template <int BITS>
 static void front_small(const float *x, const float *gate_w, const float *loff, int T, int E,
-                        int H, float *logits, int8_t *xq, float *xd, hipStream_t st, KEvents ev) {
+                        int H, float *logits, int8_t *xq, float *xd, double *xd64, hipStream_t st,
+                        KEvents ev) {
   const int nlog = gate_w ? E : 0;
   const int naq = xq ? (int)(((int64_t)T * (H / 32) + 255) / 256) : 0;
   COLI_LAUNCH(ev, (k_front_small<BITS, 4>), dim3(nlog + naq), dim3(256), 0, st, x, gate_w, loff, T,
-              E, H, logits, nlog, xq, xd);
+              E, H, logits, nlog, xq, xd, xd64);
 }
 
 hipError_t launch_front(int bits, const float *x, const float *gate_w, const float *loff, int T,
                         int E, int H, float *logits, int8_t *xq, float *xd, hipStream_t st,
-                        KEvents ev) {
+                        KEvents ev, double *xd64) {
   if (T == 0 || (!gate_w && !xq)) return hipSuccess;
   if (T <= 4) {
     switch (bits) {
-      case 8: front_small<8>(x, gate_w, loff, T, E, H, logits, xq, xd, st, ev); break;
-      case 4: front_small<4>(x, gate_w, loff, T, E, H, logits, xq, xd, st, ev); break;
-      case 2: front_small<2>(x, gate_w, loff, T, E, H, logits, xq, xd, st, ev); break;
+      case 8: front_small<8>(x, gate_w, loff, T, E, H, logits, xq, xd, xd64, st, ev); break;
+      case 4: front_small<4>(x, gate_w, loff, T, E, H, logits, xq, xd, xd64, st, ev); break;
+      case 2: front_small<2>(x, gate_w, loff, T, E, H, logits, xq, xd, xd64, st, ev); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -190,7 +193,7 @@ hipError_t launch_front(int bits, const float *x, const float *gate_w, const flo
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (xq) return launch_act_quant(bits, x, T, H, xq, xd, st, gate_w ? KEvents{} : ev);
+  if (xq) return launch_act_quant(bits, x, T, H, xq, xd, st, gate_w ? KEvents{} : ev, xd64);
   return hipSuccess;
 }
 
