@@ -529,7 +529,7 @@ def timed_samples(run_one, budget_s, n_samples=3):
     done) until its share is spent, at least once.  Returns the per-sample
     (units, seconds)."""
     out = []
-    for _ in range(n_samples):
+    for i in range(n_samples):
         units, spent = 0, 0.0
         while True:
             dt, du = run_one()
@@ -538,6 +538,7 @@ def timed_samples(run_one, budget_s, n_samples=3):
             if spent >= budget_s / n_samples:
                 break
         out.append((units, spent))
+        log(f"[bench] cpu baseline sample {i + 1}/{n_samples}: {units:g} units in {spent:.2f} s")
     return out
 
 

@@ -94,7 +94,9 @@ struct Dispatch {
   const int32_t *perm;    // [T*k] entries t*k+j ordered by (expert, t, j)
   const int32_t *uniq;    // [E]
   const int32_t *n_uniq;  // [1]
-  const int32_t *mgofs;   // [2][E+2] first matrix-core token group (64, then 32 tokens) of each union slot
+  // matrix-core item tables: [2][E+2] first token group (64, then 32
+  // tokens) of each union slot, then [2][mfma_gmax] union slot of each group
+  const int32_t *mgofs;
 };
 
 hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t cols, uint8_t *q,
@@ -103,6 +105,11 @@ hipError_t launch_quant_pack_fp8(int bits, const uint8_t *w8, const float *bscal
                                  int64_t cols, uint8_t *q, float *scale, hipStream_t st);
 hipError_t launch_gemv_f32act(int bits, const uint8_t *W, const float *scale, int64_t rows,
                               int64_t cols, const float *x, float *y, hipStream_t st);
+// Bound of the matrix-core token groups of one batch (32-token groups: the
+// routed pairs, one partial group per unique expert, the shared expert's).
+__host__ __device__ inline int mfma_gmax(int T, int k, int E) {
+  return (int)(((int64_t)T * k + 31) / 32 + E + (T + 31) / 32 + 1);
+}
 // Row stride of the binary64 copy of the Q8_0 block scales (d64, for the
 // matrix-core gate/up): the blocks of a row rounded up to a multiple of 8.
 __host__ __device__ inline int xd64_ld(int64_t n) { return (int)(((n / 32 + 7) / 8) * 8); }

@@ -60,8 +60,10 @@ __device__ __forceinline__ int mfma_groups(int n_tok, int mfma_min, int tok) {
 // Two item tables, one per token-group size: mgofs[u] = first 64-token
 // group of union slot u (slots 0 .. n_uniq-1 are the unique routed experts,
 // slot n_uniq the shared expert), mgofs[n_uniq + 1] the total; the same for
-// 32-token groups from mgofs + E + 2.  One workgroup; slots <= 1025; both
-// counts scanned at once as the halves of one 64-bit word.
+// 32-token groups from mgofs + E + 2.  Then, from mgofs + 2 (E + 2), the
+// slot of each 64-token group, and mfma_gmax entries on, of each 32-token
+// group.  One workgroup; slots <= 1025; both counts scanned at once as the
+// halves of one 64-bit word.
 __global__ __launch_bounds__(1024) void k_mfma_items(FfnArgs a, int32_t *__restrict__ mgofs) {
   __shared__ uint64_t sc[2][1024];
   const int tid = threadIdx.x;
@@ -99,6 +101,15 @@ __global__ __launch_bounds__(1024) void k_mfma_items(FfnArgs a, int32_t *__restr
     mgofs[slots] = (int32_t)(uint32_t)incl;
     m32[slots] = (int32_t)(incl >> 32);
   }
+  // group -> slot
+  int32_t *s64 = mgofs + 2 * (a.E + 2), *s32 = s64 + mfma_gmax(a.T, a.k, a.E);
+  const uint32_t e64 = (uint32_t)excl, e32 = (uint32_t)(excl >> 32);
+  const uint32_t a64 = (uint32_t)g0, a32 = (uint32_t)(g0 >> 32);
+  const uint32_t b64 = (uint32_t)g1, b32 = (uint32_t)(g1 >> 32);
+  for (uint32_t j = 0; j < a64; ++j) s64[e64 + j] = 2 * tid;
+  for (uint32_t j = 0; j < b64; ++j) s64[e64 + a64 + j] = 2 * tid + 1;
+  for (uint32_t j = 0; j < a32; ++j) s32[e32 + j] = 2 * tid;
+  for (uint32_t j = 0; j < b32; ++j) s32[e32 + a32 + j] = 2 * tid + 1;
 }
 
 // A operand, in two steps so a block's raw loads can all be issued before
@@ -153,6 +164,14 @@ constexpr int wshift() {
 // a full 64 tokens each when it runs here) start first instead of forming
 // the tail.  Items of one (slot, row block) with several token groups are
 // n_rb apart, so their re-reads of the weights run at about the same time.
+//
+// Workgroup b runs on XCD b mod 8, each XCD with its own L2.  In plain order
+// an XCD takes the same row blocks of every group (n_rb a multiple of 8):
+// each weight row block is fetched once, but every group's activations by
+// all eight XCDs.  Runs of 8 groups of 8 different slots (experts with one
+// group each, most of a prefill's) are taken transposed instead: XCD x
+// runs every row block of one group, so its activations are fetched once
+// too, and so are the weights, which no other group uses.
 // ---------------------------------------------------------------------------
 struct MfmaItem {
   int e;      // expert (-1: shared)
@@ -166,17 +185,18 @@ __device__ __forceinline__ bool mfma_item(const FfnArgs &a, int n_rb, MfmaItem &
   using C = MfmaCfg<WG>;
   const int nu = *a.disp.n_uniq;
   const int32_t *gofs = a.disp.mgofs + (C::TOK == kMfmaGroup ? 0 : a.E + 2);
+  const int32_t *gslot = a.disp.mgofs + 2 * (a.E + 2) + (C::TOK == kMfmaGroup ? 0 : mfma_gmax(a.T, a.k, a.E));
   const int n_items = gofs[nu + 1] * n_rb;
   if ((int)blockIdx.x >= n_items) return false;
   const int i = n_items - 1 - (int)blockIdx.x;
-  const int G = i / n_rb;
+  int G = i / n_rb;
   it.rb = i % n_rb;
-  int lo = 0, hi = nu;  // last slot whose first group is <= G
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (gofs[mid] <= G) lo = mid;
-    else hi = mid - 1;
+  const int run = 8 * n_rb, r0 = i / run;
+  if ((r0 + 1) * run <= n_items && gslot[8 * r0 + 7] - gslot[8 * r0] == 7) {
+    G = 8 * r0 + i % 8;
+    it.rb = (i % run) / 8;
   }
+  const int lo = gslot[G];
   const bool shared = lo == nu;
   it.e = shared ? -1 : a.disp.uniq[lo];
   it.s.slot = -1;
