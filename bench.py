@@ -363,11 +363,17 @@ def main() -> int:
             return float("nan")
         return v.value
 
-    # decode: one fused kernel; union: front, gate/up and down on the
-    # dot-product path, gate/up and down on the matrix cores
+    # decode and batches of 2-4 tokens: one fused kernel; larger unions:
+    # front, gate/up and down on the dot-product path, gate/up and down on
+    # the matrix cores
     n_k = 1 if T == 1 else 5
     stage = np.array([[el(evs[st * n_ev + 2 * i], evs[st * n_ev + 2 * i + 1]) for i in range(n_k)]
                       for st in range(K)])  # ms
+    # a small batch that ran as one kernel records only the first events
+    single = T == 1 or (T <= 4 and not np.isfinite(stage[:, 1:]).any())
+    if single:
+        stage = stage[:, :1]
+        n_k = 1
     # the last kernel that ran (the matrix-core kernels are skipped for
     # batches below mfma_min tokens)
     last = n_k - 1 if np.isfinite(stage[:, n_k - 1]).all() else min(n_k - 1, 2)
@@ -409,8 +415,9 @@ def main() -> int:
     layer_bytes = (uniq + 1) * eb["total"] + gate_bytes + act_bytes
     avg = stage.mean(axis=0)
     layer_gbps = float(np.mean(layer_bytes)) / (ms_per_step * 1e-3) / 1e9
-    if T == 1:  # the dominant (only) kernel is the fused decode kernel
-        dom_name = "k_decode_fused (the whole layer for one token)"
+    if single:  # the dominant (only) kernel is the fused kernel
+        dom_name = ("k_decode_fused (the whole layer for one token)" if T == 1 else
+                    f"k_small_fused (the whole layer for the {T}-token batch)")
         dom_ms = float(avg[0])
         dom_bytes = float(np.mean(layer_bytes))
     else:
@@ -433,8 +440,9 @@ def main() -> int:
     log(f"[bench] eager pass with kernel events: {eager_ms / K * 1e3:.2f} us/step (host wall "
         f"{eager_wall / K * 1e6:.2f} us/step), first-kernel start to last-kernel end "
         f"{np.mean(span) * 1e3:.2f} us")
-    if T == 1:
-        log(f"[bench] kernel mean (us): k_decode_fused {avg[0] * 1e3:.2f}")
+    if single:
+        log(f"[bench] kernel mean (us): {'k_decode_fused' if T == 1 else 'k_small_fused'} "
+            f"{avg[0] * 1e3:.2f}")
     else:
         gbs = {i: float(np.mean(kbytes[i])) / (avg[i] * 1e-3) / 1e9 for i in (1, 2, 3, 4)}
         log(f"[bench] kernel means (us): front {avg[0] * 1e3:.2f}; dot-product path gate/up "
@@ -463,7 +471,8 @@ def main() -> int:
         "config": {
             "workload": (("GLM-5.2 routed-MoE layer" if s is not inputs.TINY and args.workload != "tiny"
                           else "small routed-MoE layer") +
-                         (" batch-1 decode" if T == 1 else f" {T}-token union batch") +
+                         (" batch-1 decode" if T == 1 else f" {T}-token union batch"
+                          + (" in one kernel" if single else "")) +
                          f": H {s.hidden}, I {s.inter}, {s.n_experts} experts top-{s.top_k} "
                          + (f"({s.n_group} groups keep {s.topk_group}, rsf {s.rsf}) " if s.n_group > 1
                             else f"(rsf {s.rsf}) ")
@@ -476,7 +485,8 @@ def main() -> int:
             "unique_experts_per_step": {"mean": round(float(uniq.mean()), 2),
                                         "min": int(uniq.min()), "max": int(uniq.max())},
             "launch": "one HIP graph of the K timed steps",
-            "kernel_us": ({"k_decode_fused": round(float(avg[0]) * 1e3, 3)} if T == 1 else
+            "kernel_us": ({("k_decode_fused" if T == 1 else "k_small_fused"): round(float(avg[0]) * 1e3, 3)}
+                          if single else
                           {"front": round(float(avg[0]) * 1e3, 3),
                            "gate_up_dot": round(float(avg[1]) * 1e3, 3),
                            "down_dot": round(float(avg[2]) * 1e3, 3),

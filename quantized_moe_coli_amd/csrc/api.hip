@@ -111,7 +111,7 @@ WsLayout ws_layout(const coli_moe_layer *L, int Tmax) {
   w.mgofs = take((2 * (E + 2) + 2 * (size_t)coli::mfma_gmax((int)T, (int)k, (int)E)) * 4);
   w.hq = take((T * k + T) * I);
   w.hd = take((T * k + T) * (I / 32) * 4);
-  w.hsh = take(I * 4);  // decode: the shared expert's h in binary32
+  w.hsh = take(4 * I * 4);  // decode and batches up to 4: the shared expert's h in binary32
   w.obuf = take(Tmax >= 2 ? T * (k + 1) * H * 4 : 0);
   w.total = off;
   return w;
@@ -504,6 +504,14 @@ coli_status forward_impl(const coli_moe_layer *L, const CacheRun *cache, const f
       e = coli::launch_decode_fused(fa, x, logits_in ? nullptr : L->gate_w, logits_in, logits_out,
                                     reinterpret_cast<uint32_t *>(base + ws.ctr),
                                     reinterpret_cast<float *>(base + ws.hsh), s, kev(0));
+      if (e != hipErrorNotSupported) return from_hip(e);
+    }
+    if (!cache && T >= 2 && T <= 4) {
+      // a small batch (an MTP verify): the whole layer in one kernel where
+      // that kernel is built for the layer's shapes
+      e = coli::launch_small_fused(fa, x, logits_in ? nullptr : L->gate_w, logits_in, logits_out,
+                                   reinterpret_cast<uint32_t *>(base + ws.ctr),
+                                   reinterpret_cast<float *>(base + ws.hsh), s, kev(0));
       if (e != hipErrorNotSupported) return from_hip(e);
     }
     // activations -> Q8_0 codes (union batches: their scales in binary64

@@ -235,30 +235,32 @@ struct SliceGate {
 // requests every partial of the thread's expert once (threads that call
 // it); finish() requests the rest, polls what was absent, computes the
 // scores, and ends with a barrier.  `lsave` (or null) keeps the logits for
-// the caller.  Threads cover experts e, e + NT, ....
+// the caller.  Threads cover experts e, e + NT, ....  Token `tok` of a
+// small batch: its logits row of the supplied ones, its partial words after
+// those of the tokens before it.
 struct ScorePoll {
   uint64_t v[kMaxPartsPerRow];
 
   bool have = false;  // the first round's words were requested by issue()
 
-  __device__ __forceinline__ void issue(const DecodeArgs &d) {
+  __device__ __forceinline__ void issue(const DecodeArgs &d, int tok = 0) {
     const int e = threadIdx.x, P = d.n_part;
     if (d.logits_in || e >= d.f.cfg.E) return;
     have = true;
-    const uint64_t *w = reinterpret_cast<const uint64_t *>(d.ctr + kScoreWords) + e * P;
+    const uint64_t *w = reinterpret_cast<const uint64_t *>(d.ctr + kScoreWords) + ((size_t)tok * d.f.cfg.E + e) * P;
 #pragma unroll
     for (int p = 0; p < kMaxPartsPerRow; ++p)
       if (p < P) v[p] = __hip_atomic_load(w + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __device__ __forceinline__ void finish(const DecodeArgs &d, SelInput &in, float *lsave) {
+  __device__ __forceinline__ void finish(const DecodeArgs &d, SelInput &in, float *lsave, int tok = 0) {
     const RouterCfg &cfg = d.f.cfg;
     const int P = d.n_part;
     for (int e = threadIdx.x; e < cfg.E; e += kDecThreads) {
       float l;
       if (d.logits_in) {
-        l = d.logits_in[e];
+        l = d.logits_in[(size_t)tok * cfg.E + e];
       } else {
-        const uint64_t *w = reinterpret_cast<const uint64_t *>(d.ctr + kScoreWords) + e * P;
+        const uint64_t *w = reinterpret_cast<const uint64_t *>(d.ctr + kScoreWords) + ((size_t)tok * cfg.E + e) * P;
         if (e >= kDecThreads || !have) {  // words not requested by issue(): requested now
 #pragma unroll
           for (int p = 0; p < kMaxPartsPerRow; ++p)
@@ -691,6 +693,571 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
   }
 }
 
+// ===========================================================================
+// Small batches (2 to 4 tokens: an MTP verify of the current token and its
+// drafts) as ONE kernel, the batch union of the decode kernel's design.
+//
+// colibrì README, "Implemented features", native MTP item: the drafts are
+// verified in one batched forward, where each unique expert of the batch is
+// read once for every token that picked it (batch-union item).
+//
+// Per call, in order:
+//   logit slices (computed logits): one gate row per slice for every token
+//     (P = 1), each token's binary64 partial in its own header word;
+//   every workgroup: the tokens' Q8_0 codes into LDS;
+//   workgroup t < T: token t's scores and experts (select_local), written to
+//     the workspace's idx / w rows and counted in the selection counter;
+//   every workgroup: its rows of the shared expert's gate/up for all tokens
+//     (h in binary32; the workgroup completing a 32-row block quantises it
+//     for every token), then, once T selections are counted, the batch's
+//     union in LDS: the (token, slot) pairs sorted by (expert, pair), so the
+//     experts' runs are consecutive and each pair's h row is its position;
+//   tickets: GR items (unique expert u, 32-row block) for the tokens of u,
+//     then D items (a block of output rows for every token: the shared
+//     expert first, then the unique experts in order, each token's
+//     contributions weighted and summed in that fixed order).
+// Slot counters: unique expert u on line u, the shared expert on line
+// kSelMaxK; the waits, give-ups, status word and header reset are the
+// decode kernel's.
+// ===========================================================================
+constexpr int kSmallMaxT = 4;
+constexpr int kSmallPipe = 1;  // gate/up row passes in flight per wave
+constexpr int kCtrSel = kCtrSpin + 16;  // selections published (a word of the polling-bound line)
+constexpr int kShLine = kSelMaxK;       // the shared expert's slot counter line
+
+// The batch union, built by every workgroup from the published selections.
+struct SmallUnion {
+  int n_pairs, n_valid, U;
+  int pidx[kSelMaxK];    // expert of pair l = t * k + j (-1: none)
+  float pw[kSelMaxK];    // weight of pair l
+  int sorted[kSelMaxK];  // pair at h row r
+  int ue[kSelMaxK + 1];  // expert of unique u
+  int ufirst[kSelMaxK + 1];  // first h row of unique u (ufirst[U] = n_valid)
+};
+
+template <int T>
+__device__ __forceinline__ void small_union(const DecodeArgs &d, SmallUnion &su) {
+  const FfnArgs &a = d.f;
+  const int n = T * a.k, E = a.E;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < n) {
+    const int e = (int)ld_dev(reinterpret_cast<const uint32_t *>(a.idx) + tid);
+    su.pidx[tid] = (e >= 0 && e < E) ? e : -1;
+    su.pw[tid] = __uint_as_float(ld_dev(reinterpret_cast<const uint32_t *>(a.w) + tid));
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // rank of pair l among keys (expert, l), invalid pairs last
+    const bool in = lane < n;
+    const int e = in ? su.pidx[lane] : -1;
+    const int key = in ? (e >= 0 ? e * 64 + lane : E * 64 + lane) : 0x7FFFFFFF;
+    int rank = 0;
+    for (int m = 0; m < n; ++m) {
+      const int em = su.pidx[m];
+      const int km = em >= 0 ? em * 64 + m : E * 64 + m;
+      rank += km < key ? 1 : 0;
+    }
+    if (in) su.sorted[rank] = lane;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const bool in = lane < n;
+    const int e = in ? su.pidx[su.sorted[lane]] : -1;
+    const int ep = (in && lane > 0) ? su.pidx[su.sorted[lane - 1]] : -2;
+    const bool valid = e >= 0;
+    const bool first = valid && e != ep;
+    const uint64_t bf = __ballot(first), bv = __ballot(valid);
+    const int u = __popcll(bf & ((1ull << lane) - 1ull));
+    if (first) {
+      su.ue[u] = e;
+      su.ufirst[u] = lane;
+    }
+    if (lane == 0) {
+      su.U = __popcll(bf);
+      su.n_valid = __popcll(bv);
+      su.n_pairs = n;
+      su.ufirst[__popcll(bf)] = __popcll(bv);
+    }
+  }
+  __syncthreads();
+}
+
+// Logit slice e (P = 1): the binary64 sums x_t . gate_w[e] of every token,
+// split over the waves as SliceGate does.
+template <int T>
+__device__ __forceinline__ void small_slice(const DecodeArgs &d, int e, double (*part)[kDecWaves]) {
+  constexpr int kMaxPer = SliceGate::kMaxPer;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = d.f.L.H, E = d.f.cfg.E;
+  const int q4 = H / 4, qw = (q4 + kDecWaves - 1) / kDecWaves;
+  const int c0 = wave * qw, cn = min(qw, q4 - wave * qw);
+  const float4 *wr = reinterpret_cast<const float4 *>(d.gate_w + (size_t)e * H);
+  float4 wv[kMaxPer], xv[T][kMaxPer];
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    if (lane + 64 * i < cn) {
+      wv[i] = wr[c0 + lane + 64 * i];
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        xv[t][i] = reinterpret_cast<const float4 *>(d.x + (size_t)t * H)[c0 + lane + 64 * i];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      if (lane + 64 * i < cn) {
+        acc = fma((double)xv[t][i].x, (double)wv[i].x, acc);
+        acc = fma((double)xv[t][i].y, (double)wv[i].y, acc);
+        acc = fma((double)xv[t][i].z, (double)wv[i].z, acc);
+        acc = fma((double)xv[t][i].w, (double)wv[i].w, acc);
+      }
+    }
+    const double ws = wave_sum_f64(acc);
+    if (lane == 0) part[t][wave] = ws;
+  }
+  __syncthreads();
+  if (threadIdx.x < T) {
+    const int t = threadIdx.x;
+    double sum = part[t][0];
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w) sum += part[t][w];
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(d.ctr + kScoreWords) + (size_t)t * E + e,
+                       ~(uint64_t)__double_as_longlong(sum), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+}
+
+// The shared expert's gate/up rows [r0, r0 + nr) for every token (shared_rows
+// with T activations per row); h rows k*T + t.
+template <int BITS, int LPR, int CPL, int T>
+__device__ __forceinline__ void small_shared_rows(const DecodeArgs &d, int r0, int nr,
+                                                  const int8_t *xq, const float *xd, int *s_last) {
+  constexpr int RPP = 64 / LPR;
+  const FfnArgs &a = d.f;
+  const int H = a.L.H, I = a.L.I, hr0 = a.k * T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gl = lane % LPR, rsub = lane / LPR;
+  const int nchunks = H * BITS / 128;
+  const size_t row_bytes = (size_t)H * BITS / 8;
+  const ExpertPtrs ep = expert_ptrs(a.L, -1);
+  for (int rp = wave * RPP; rp < nr; rp += kDecWaves * RPP) {
+    const int row = min(r0 + rp + rsub, I - 1);
+    const uint4 *gp = reinterpret_cast<const uint4 *>(ep.wg + (size_t)row * row_bytes);
+    const uint4 *up = reinterpret_cast<const uint4 *>(ep.wu + (size_t)row * row_bytes);
+    uint4 wg[CPL], wu[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = min(gl + LPR * i, nchunks - 1);
+      wg[i] = ld_nt(gp + c);
+      wu[i] = ld_nt(up + c);
+    }
+    // each token's activation chunks from LDS, one token at a time (few
+    // registers: the rows' weights stay, the activations are re-read)
+    for (int t = 0; t < T; ++t) {
+      double pg = 0.0, pu = 0.0;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = gl + LPR * i;
+        Act<BITS> act;
+        if (c < nchunks) load_act<BITS>(act, xq + (size_t)t * H, xd + (size_t)t * (H / 32), c);
+        else zero_act<BITS>(act);
+        pg += chunk_part_f64<BITS>(wg[i], act);
+        pu += chunk_part_f64<BITS>(wu[i], act);
+      }
+      pg = group_sum_f64<LPR>(pg);
+      pu = group_sum_f64<LPR>(pu);
+      if (lane == group_sum_lane<LPR>(lane) && rp + rsub < nr) {
+        const float h = swiglu_h(row_out(pg, ep.sg[row]), row_out(pu, ep.su[row]));
+        st_dev(reinterpret_cast<uint32_t *>(d.hsh) + (size_t)t * I + row, __float_as_uint(h));
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int b_lo = r0 / 32, b_hi = (r0 + nr - 1) / 32;
+  for (int b = b_lo; b <= b_hi; ++b) {
+    if (threadIdx.x == 0) {
+      const int n_in = min(r0 + nr, 32 * b + 32) - max(r0, 32 * b);
+      const uint32_t old = __hip_atomic_fetch_add(d.ctr + kCtrShBlk + b, (uint32_t)n_in,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_last = (int)(old + (uint32_t)n_in) == 32;
+    }
+    __syncthreads();
+    if (*s_last) {
+      // this workgroup completed block b: Q8_0 of its 32 values of h for
+      // every token, wave t for token t
+      if (wave < T && lane < 32) {
+        const int t = wave, i = lane;
+        const float h = __uint_as_float(ld_dev(reinterpret_cast<const uint32_t *>(d.hsh) + (size_t)t * I + 32 * b + i));
+        const float amax = __shfl(group_max<32>(fabsf(h)), 31, 64);
+        const float db = amax / 127.f;
+        float c = 0.f;
+        if (db != 0.f) c = fminf(fmaxf(rintf(h / db), -127.f), 127.f);
+        const int code = (int)c & 0xFF;
+        uint32_t word = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          word |= ((uint32_t)__shfl(code, perm_src<BITS>((4 * i + m) & 31), 64) & 0xFFu) << (8 * m);
+        if (i < 8) st_dev(reinterpret_cast<uint32_t *>(a.hq + (size_t)(hr0 + t) * I + 32 * b) + i, word);
+        if (i == 0)
+          st_dev(reinterpret_cast<uint32_t *>(a.hd) + (size_t)(hr0 + t) * (I / 32) + b, __float_as_uint(db));
+      }
+      publish(d.ctr + kCtrSlot0 + kShLine * kCtrStride, 1u);
+    }
+    __syncthreads();
+  }
+}
+
+// D item: output rows [r0, r0 + down_rows) for every token.  "Experts" in
+// order: q = 0 the shared one (its T rows at k*T), then unique u = q - 1
+// (its pairs' rows ufirst[u] .. ufirst[u+1]-1), SG at a time; wave w owns
+// rows r0 + w*PR .. for every expert and token, so each token's y is
+// summed in this fixed order.
+template <int BITS, int LPR, int CPL, int NPASS, int SG, int T>
+__device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const SmallUnion &su, int r0,
+                                                int8_t *lds_q, float *lds_d, int *srow) {
+  constexpr int RPP = 64 / LPR;
+  const FfnArgs &a = d.f;
+  const int I = a.L.I, H = a.L.H, k = a.k, hr0 = k * T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gl = lane % LPR, rsub = lane / LPR;
+  const int nchunks = I * BITS / 128;
+  const size_t row_bytes = (size_t)I * BITS / 8;
+  const int nx = su.U + 1;
+  const int wrow0 = r0 + wave * NPASS * RPP;
+  float y[T][NPASS];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) y[t][p] = 0.f;
+
+  for (int g0 = 0; g0 < nx; g0 += SG) {
+    const int gn = min(SG, nx - g0);
+    uint4 wv[SG][NPASS][CPL];
+    float sdv[SG][NPASS];
+#pragma unroll
+    for (int q = 0; q < SG; ++q) {
+      if (q < gn) {
+        const int x = g0 + q;
+        const ExpertPtrs ep = expert_ptrs(a.L, x == 0 ? -1 : su.ue[x - 1]);
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+          const int row = wrow0 + p * RPP + rsub;
+          const uint4 *wp = reinterpret_cast<const uint4 *>(ep.wd + (size_t)row * row_bytes);
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) wv[q][p][i] = ld_nt(wp + min(gl + LPR * i, nchunks - 1));
+          sdv[q][p] = ep.sd[row];
+        }
+      }
+    }
+    // the group's h rows: first row and count of each of its experts
+    int rbeg[SG], rcnt[SG], nrows = 0;
+#pragma unroll
+    for (int q = 0; q < SG; ++q) {
+      const int x = g0 + q;
+      rbeg[q] = q >= gn ? 0 : x == 0 ? hr0 : su.ufirst[x - 1];
+      rcnt[q] = q >= gn ? 0 : x == 0 ? T : su.ufirst[x] - su.ufirst[x - 1];
+      nrows += rcnt[q];
+    }
+    if ((int)threadIdx.x < gn) {
+      const int x = g0 + threadIdx.x;
+      const uint32_t *c = d.ctr + kCtrSlot0 + (x == 0 ? kShLine : x - 1) * kCtrStride;
+      const uint32_t target = (uint32_t)(I / kGuRows);
+      const uint32_t sb = spin_bound(d, 8u * kSpinLimit);
+      const uint32_t spin = sb & ~kSpinForced;
+      const bool forced = (sb & kSpinForced) != 0u;
+      uint32_t it = 0, v;
+      while (((v = ld_ctr(c)) < target || forced) && it < spin) {
+        __builtin_amdgcn_s_sleep(8);
+        ++it;
+      }
+      if (v < target || forced) gave_up(d, COLI_WAIT_SLOTS);
+    }
+    if (threadIdx.x == 0) {
+      int n = 0;
+#pragma unroll
+      for (int q = 0; q < SG; ++q)
+        for (int r = 0; r < rcnt[q]; ++r) srow[n++] = rbeg[q] + r;
+    }
+    __syncthreads();
+    {
+      // staged rows g = 0 .. nrows-1: codes then scales, 16-byte pieces
+      // straight into LDS with the device-scope loads' cache policy
+      const int cq = I / 16, cd = I / 128;
+      const int nA = nrows * cq, nB = nrows * cd;
+      const int nwA = (nA + 63) / 64, nwB = (nB + 63) / 64;
+      for (int ii = wave; ii < nwA + nwB; ii += kDecWaves) {
+        const bool codes = ii < nwA;
+        const int base = (codes ? ii : ii - nwA) * 64;
+        const int c = base + lane, per = codes ? cq : cd;
+        unsigned char *dst = (codes ? reinterpret_cast<unsigned char *>(lds_q)
+                                    : reinterpret_cast<unsigned char *>(lds_d)) + (size_t)base * 16;
+        if (c < (codes ? nA : nB)) {
+          const int g = c / per, r = c - g * per;
+          const int hrow = srow[g];
+          const unsigned char *src =
+              codes ? reinterpret_cast<const unsigned char *>(a.hq) + (size_t)hrow * I + r * 16
+                    : reinterpret_cast<const unsigned char *>(a.hd) + (size_t)hrow * (I / 8) + r * 16;
+          __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0,
+                                           kLoadSc1);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    int g = 0;
+#pragma unroll
+    for (int q = 0; q < SG; ++q) {
+      for (int r = 0; r < rcnt[q]; ++r, ++g) {
+        // the pair's token and weight (the shared expert: token r, weight 1)
+        const int x = g0 + q;
+        const int pair = x == 0 ? -1 : su.sorted[rbeg[q] + r];
+        const int tok = x == 0 ? r : pair / k;
+        const float wgt = x == 0 ? 1.f : su.pw[pair];
+        Act<BITS> act[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const int c = gl + LPR * i;
+          if (c < nchunks) load_act<BITS>(act[i], lds_q + (size_t)g * I, lds_d + g * (I / 32), c);
+          else zero_act<BITS>(act[i]);
+        }
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+          float acc = 0.f;
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) acc += chunk_part<BITS>(wv[q][p][i], act[i]);
+          const float contrib = (x == 0 ? sdv[q][p] : wgt * sdv[q][p]) * acc;
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+            if (t == tok) y[t][p] += contrib;
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const float yr = group_sum<LPR>(y[t][p]);
+      if (lane == group_sum_lane<LPR>(lane)) a.y[(size_t)t * H + wrow0 + p * RPP + rsub] = yr;
+    }
+}
+
+// GR item: unique expert u's gate/up rows [32 rb, +32) for its n tokens
+// (h rows ufirst[u] ..): the gate/up body with the tokens in a runtime loop
+// whose activations are re-read from LDS per row pass, so a pass holds only
+// its rows' weights (PIPE passes in flight) -- few registers at any n.
+template <int BITS, int LPR, int CPL, int PIPE>
+__device__ __forceinline__ void small_gateup(const DecodeArgs &d, const SmallUnion &su, int u, int rb,
+                                             float (*hs)[kGuRows], float (*hu)[kGuRows],
+                                             int8_t (*hcode)[kGuRows], const int8_t *xq,
+                                             const float *xd) {
+  static_assert(kGuRows == 32, "one Q8_0 block of h per item");
+  constexpr int RPP = 64 / LPR;
+  constexpr int ROWS_PER_WAVE = kGuRows / kDecWaves;
+  constexpr int PASSES = ROWS_PER_WAVE / RPP;
+  const FfnArgs &a = d.f;
+  const int H = a.L.H, I = a.L.I;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gl = lane % LPR, rsub = lane / LPR;
+  const int nchunks = H * BITS / 128;
+  const size_t row_bytes = (size_t)H * BITS / 8;
+  const int xblocks = H / 32;
+  const int h0 = su.ufirst[u], n_tok = su.ufirst[u + 1] - h0;
+  const ExpertPtrs ep = expert_ptrs(a.L, su.ue[u]);
+  const int srow = rb * 32 + wave * ROWS_PER_WAVE + min(lane, ROWS_PER_WAVE - 1);
+  const float sgv = ep.sg[srow], suv = ep.su[srow];
+  uint4 wg[PIPE][CPL], wu[PIPE][CPL];
+  auto load_rows = [&](int p, int buf) {
+    const int row = rb * 32 + wave * ROWS_PER_WAVE + p * RPP + rsub;
+    const uint4 *gp = reinterpret_cast<const uint4 *>(ep.wg + (size_t)row * row_bytes);
+    const uint4 *up = reinterpret_cast<const uint4 *>(ep.wu + (size_t)row * row_bytes);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = min(gl + LPR * i, nchunks - 1);
+      wg[buf][i] = ld_nt(gp + c);
+      wu[buf][i] = ld_nt(up + c);
+    }
+  };
+  load_rows(0, 0);
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    if (PIPE == 2 && p + 1 < PASSES) load_rows(p + 1, (p + 1) & 1);
+    const int buf = PIPE == 2 ? (p & 1) : 0;
+    const int rl = wave * ROWS_PER_WAVE + p * RPP + rsub;
+    const float sg = row_scale<RPP>(sgv, p, rsub), su_ = row_scale<RPP>(suv, p, rsub);
+    for (int n = 0; n < n_tok; ++n) {
+      const int t = su.sorted[h0 + n] / a.k;
+      const int8_t *xqt = xq + (size_t)t * H;
+      const float *xdt = xd + (size_t)t * xblocks;
+      double pg = 0.0, pu = 0.0;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = gl + LPR * i;
+        Act<BITS> act;
+        if (c < nchunks) load_act<BITS>(act, xqt, xdt, c);
+        else zero_act<BITS>(act);
+        pg += chunk_part_f64<BITS>(wg[buf][i], act);
+        pu += chunk_part_f64<BITS>(wu[buf][i], act);
+      }
+      pg = group_sum_f64<LPR>(pg);
+      pu = group_sum_f64<LPR>(pu);
+      if (lane == group_sum_lane<LPR>(lane)) {
+        hs[n][rl] = row_out(pg, sg);
+        hu[n][rl] = row_out(pu, su_);
+      }
+    }
+    if (PIPE == 1 && p + 1 < PASSES) load_rows(p + 1, 0);
+  }
+  __syncthreads();
+  // SwiGLU and Q8_0 of each token's 32 values of h: 32 threads per token
+  {
+    const int n = threadIdx.x >> 5, i = threadIdx.x & 31;
+    if (n < n_tok) {
+      const float h = swiglu_h(hs[n][i], hu[n][i]);
+      float amax = group_max<32>(fabsf(h));
+      amax = __shfl(amax, (lane & 32) | 31, 64);
+      const float db = amax / 127.f;
+      float c = 0.f;
+      if (db != 0.f) c = fminf(fmaxf(rintf(h / db), -127.f), 127.f);
+      hcode[n][perm_dst<BITS>(i)] = (int8_t)c;
+      if (i == 0)
+        st_dev(reinterpret_cast<uint32_t *>(a.hd) + (size_t)(h0 + n) * (I / 32) + rb, __float_as_uint(db));
+    }
+  }
+  __syncthreads();
+  {
+    const int n = threadIdx.x >> 3, i = threadIdx.x & 7;
+    if (n < n_tok)
+      st_dev(reinterpret_cast<uint32_t *>(a.hq + (size_t)(h0 + n) * I + rb * 32) + i,
+             reinterpret_cast<const uint32_t *>(hcode[n])[i]);
+  }
+}
+
+template <int BITS, int GLPR, int GCPL, int DLPR, int DCPL, int T>
+__global__ __launch_bounds__(kDecThreads)
+__attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 2))) void k_small_fused(DecodeArgs d) {
+  constexpr int DNPASS = DCPL == 1 ? 2 : 1;
+  constexpr int DSG = DCPL == 1 ? 3 : 2;
+  __shared__ SmallUnion su;
+  __shared__ float hs[kSmallMaxT][kGuRows], hu[kSmallMaxT][kGuRows];
+  __shared__ __align__(16) int8_t hcode[kSmallMaxT][kGuRows];
+  __shared__ double lpart[kSmallMaxT][kDecWaves];
+  __shared__ int s_ticket;
+  __shared__ int srow[DSG * kSmallMaxT];
+  __shared__ int32_t sidx[kSelMaxK];
+  __shared__ float sw[kSelMaxK];
+  // dynamic LDS: [selection scratch, later a D item's staged h | the tokens'
+  // Q8_0 codes and scales | one token's logits kept for the caller]
+  extern __shared__ __align__(16) unsigned char dyn[];
+  const FfnArgs &a = d.f;
+  const int k = a.k, I = a.L.I, H = a.L.H, E = a.E;
+  const int n_rb = I / kGuRows;
+  int8_t *xq_lds = reinterpret_cast<int8_t *>(dyn + d.lds_x);
+  float *xd_lds = reinterpret_cast<float *>(dyn + d.lds_x + T * H);
+  float *lsave = d.lds_l >= 0 ? reinterpret_cast<float *>(dyn + d.lds_l) : nullptr;
+
+  // logit slices: gate row e for every token
+  for (int e = (int)blockIdx.x; e < d.n_slice; e += gridDim.x) small_slice<T>(d, e, lpart);
+  {
+    ActRow<BITS, kDecThreads> xr;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      xr.load(d.x + (size_t)t * H, H);
+      xr.quantize(H, xq_lds + (size_t)t * H, xd_lds + (size_t)t * (H / 32));
+    }
+  }
+  __syncthreads();
+  if ((int)blockIdx.x < T) {
+    // token blockIdx.x: scores, experts, weights, published
+    const int t = blockIdx.x;
+    SelInput &in = *reinterpret_cast<SelInput *>(dyn);
+    ScorePoll sp;
+    sp.issue(d, t);
+    sp.finish(d, in, lsave, t);
+    select_local(d, in, dyn + sizeof(SelInput), sidx, sw);
+    for (int j = threadIdx.x; j < k; j += kDecThreads) {
+      st_dev(reinterpret_cast<uint32_t *>(a.idx) + t * k + j, (uint32_t)sidx[j]);
+      st_dev(reinterpret_cast<uint32_t *>(a.w) + t * k + j, __float_as_uint(sw[j]));
+      if (a.idx_user) a.idx_user[t * k + j] = sidx[j];
+      if (a.w_user) a.w_user[t * k + j] = sw[j];
+    }
+    if (lsave && d.logits_out)
+      for (int e = threadIdx.x; e < E; e += kDecThreads) d.logits_out[(size_t)t * E + e] = lsave[e];
+    publish(d.ctr + kCtrSel, 1u);
+    __syncthreads();
+  }
+  {
+    const int r0 = (int)blockIdx.x * d.sh_rows;
+    const int nr = min(d.sh_rows, I - r0);
+    if (nr > 0) small_shared_rows<BITS, GLPR, GCPL, T>(d, r0, nr, xq_lds, xd_lds, &s_ticket);
+  }
+  // every token's selection, then the union
+  if (threadIdx.x == 0) {
+    const uint32_t sb = spin_bound(d, kSpinLimit);
+    const uint32_t spin = sb & ~kSpinForced;
+    const bool forced = (sb & kSpinForced) != 0u;
+    uint32_t it = 0, v;
+    while (((v = ld_ctr(d.ctr + kCtrSel)) < (uint32_t)T || forced) && it < spin) {
+      __builtin_amdgcn_s_sleep(2);
+      ++it;
+    }
+    if (v < (uint32_t)T || forced) gave_up(d, COLI_WAIT_SCORES);
+  }
+  __syncthreads();
+  small_union<T>(d, su);
+  const int n_gr = su.U * n_rb;
+  const int total = n_gr + d.n_down;
+
+  const int q = blockIdx.x % kQueues;
+  const int nq = ((int)gridDim.x - q + kQueues - 1) / kQueues;
+  auto next_ticket = [&]() -> int {
+    if (threadIdx.x == 0)
+      s_ticket = (int)__hip_atomic_fetch_add(d.ctr + kCtrTicket + q * kCtrStride, 1u,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint32_t tk = (uint32_t)uniform_i32(s_ticket);
+    const long long tt = (long long)q + (long long)kQueues * ((long long)nq + (long long)tk);
+    __syncthreads();
+    return tt < (long long)total ? (int)tt : total;
+  };
+
+  int t = (int)blockIdx.x < total ? (int)blockIdx.x : total;
+  for (; t < n_gr; t = next_ticket()) {
+    const int u = t / n_rb, rb = t % n_rb;
+    small_gateup<BITS, GLPR, GCPL, kSmallPipe>(d, su, u, rb, hs, hu, hcode, xq_lds, xd_lds);
+    publish(d.ctr + kCtrSlot0 + u * kCtrStride, 1u);
+  }
+  int8_t *lds_q = reinterpret_cast<int8_t *>(dyn);
+  float *lds_d = reinterpret_cast<float *>(dyn + (size_t)DSG * T * I);
+  for (; t < total; t = next_ticket())
+    small_down_rows<BITS, DLPR, DCPL, DNPASS, DSG, T>(d, su, (t - n_gr) * d.down_rows, lds_q, lds_d, srow);
+
+  // the last workgroup out clears the header for the next call
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_ticket = (int)__hip_atomic_fetch_add(d.ctr + kCtrExit, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (uniform_i32(s_ticket) == (int)gridDim.x - 1) {
+    const int nc = kCtrSlot0 / kCtrStride + kSelMaxK + 1;
+    for (int i = threadIdx.x; i < nc; i += kDecThreads)
+      __hip_atomic_store(d.ctr + i * kCtrStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(d.ctr + kCtrSpin, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(d.ctr + kCtrSel, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int sl = threadIdx.x; sl < T * d.n_slice; sl += kDecThreads)
+      __hip_atomic_store(reinterpret_cast<uint64_t *>(d.ctr + kScoreWords) + sl, (uint64_t)0,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int b = threadIdx.x; b < I / 32; b += kDecThreads)
+      __hip_atomic_store(d.ctr + kCtrShBlk + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 static int dec_lpr(int nchunks) { return (nchunks % 64 != 0 && nchunks % 32 == 0) ? 32 : 64; }
 
 static int dec_cpl(int nchunks, int lpr) {
@@ -771,6 +1338,95 @@ static hipError_t launch_fused_bits(DecodeArgs d, hipStream_t st, KEvents ev) {
   if constexpr (BITS == 2) { COLI_DEC_CASE(32, 3, 32, 1) }
 #undef COLI_DEC_CASE
   return hipErrorNotSupported;
+}
+
+template <int BITS, int GLPR, int GCPL, int DLPR, int DCPL, int T>
+static hipError_t launch_small_t(DecodeArgs d, hipStream_t st, KEvents ev) {
+  constexpr int DNPASS = DCPL == 1 ? 2 : 1;
+  constexpr int DSG = DCPL == 1 ? 3 : 2;
+  const int I = d.f.L.I, H = d.f.L.H, E = d.f.E, k = d.f.k;
+  d.down_rows = kDecWaves * DNPASS * (64 / DLPR);
+  if (H % d.down_rows || I % kGuRows || T * k > kSelMaxK || (d.gate_w && T * E > kMaxSlices) ||
+      (H / 4 + kDecWaves - 1) / kDecWaves > 64 * SliceGate::kMaxPer || H > 8192)
+    return hipErrorNotSupported;
+  d.n_down = H / d.down_rows;
+  // dynamic LDS: [max(selection scratch, staged h of DSG experts' rows) |
+  // the tokens' codes and scales | one token's logits kept for the caller]
+  const size_t per_row = (size_t)I + (size_t)(I / 32) * 4;
+  const size_t sel =
+      (sizeof(SelInput) + std::max(sizeof(SelWgScratch), sizeof(SelFastScratch)) + 15) / 16 * 16;
+  const size_t reg_a = (std::max(sel, (size_t)DSG * T * per_row) + 15) / 16 * 16;
+  d.lds_x = (int)reg_a;
+  const size_t reg_x = ((size_t)T * H + (size_t)T * (H / 32) * 4 + 15) / 16 * 16;
+  d.lds_l = d.logits_out ? (int)(reg_a + reg_x) : -1;
+  const size_t shmem = reg_a + reg_x + (d.logits_out ? (size_t)E * 4 : 0);
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void *>(&k_small_fused<BITS, GLPR, GCPL, DLPR, DCPL, T>),
+          kDecThreads, shmem) != hipSuccess ||
+      per_cu <= 0)
+    return hipErrorNotSupported;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n_cu <= 0)
+    n_cu = 256;
+  const int cap = std::max(per_cu * n_cu, kQueues);
+  d.total = T * k * (I / kGuRows) + d.n_down;  // items at most (every pair its own expert)
+  const int grid = std::min(d.total, cap);
+  d.sh_rows = (I + grid - 1) / grid;
+  d.n_part = 1;
+  d.n_slice = d.gate_w ? E : 0;
+  if (d.grid_out) *d.grid_out = grid;
+  COLI_LAUNCH(ev, (k_small_fused<BITS, GLPR, GCPL, DLPR, DCPL, T>), dim3(grid), dim3(kDecThreads),
+              shmem, st, d);
+  return hipGetLastError();
+}
+
+template <int BITS, int GL, int GC, int DL, int DC>
+static hipError_t launch_small_shape(DecodeArgs d, int T, hipStream_t st, KEvents ev) {
+  switch (T) {
+    case 2: return launch_small_t<BITS, GL, GC, DL, DC, 2>(d, st, ev);
+    case 3: return launch_small_t<BITS, GL, GC, DL, DC, 3>(d, st, ev);
+    case 4: return launch_small_t<BITS, GL, GC, DL, DC, 4>(d, st, ev);
+    default: return hipErrorNotSupported;
+  }
+}
+
+// The single-kernel small batch is built for the decode kernel's row shapes.
+template <int BITS>
+static hipError_t launch_small_bits(DecodeArgs d, int T, hipStream_t st, KEvents ev) {
+  const int gn = d.f.L.H * BITS / 128, dn = d.f.L.I * BITS / 128;
+  const int gl = dec_lpr(gn), gc = dec_cpl(gn, gl), dl = dec_lpr(dn), dc = dec_cpl(dn, dl);
+#define COLI_SMALL_CASE(GL, GC, DL, DC) \
+  if (gl == GL && gc == GC && dl == DL && dc == DC) return launch_small_shape<BITS, GL, GC, DL, DC>(d, T, st, ev);
+  COLI_SMALL_CASE(64, 1, 64, 1)
+  if constexpr (BITS == 8) { COLI_SMALL_CASE(64, 6, 64, 2) }
+  if constexpr (BITS == 4) { COLI_SMALL_CASE(64, 3, 64, 1) }
+  if constexpr (BITS == 2) { COLI_SMALL_CASE(32, 3, 32, 1) }
+#undef COLI_SMALL_CASE
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_small_fused(const FfnArgs &f, const float *x, const float *gate_w,
+                              const float *logits_in, float *logits_out, uint32_t *ctr, float *hsh,
+                              hipStream_t st, KEvents ev, int *grid_out) {
+  if (f.T < 2 || f.T > kSmallMaxT) return hipErrorNotSupported;
+  DecodeArgs d{};
+  d.grid_out = grid_out;
+  d.f = f;
+  d.x = x;
+  d.gate_w = gate_w;
+  d.logits_in = gate_w ? nullptr : logits_in;
+  d.logits_out = gate_w ? logits_out : nullptr;
+  d.ctr = ctr;
+  d.hsh = hsh;
+  switch (f.L.bits) {
+    case 8: return launch_small_bits<8>(d, f.T, st, ev);
+    case 4: return launch_small_bits<4>(d, f.T, st, ev);
+    case 2: return launch_small_bits<2>(d, f.T, st, ev);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // The header's status word into *out, cleared afterwards when `clear`.

@@ -120,17 +120,25 @@ __device__ __forceinline__ ExpertPtrs expert_ptrs(const LayerPtrs &L, int e) {
 }
 
 // The tokens of one work item: decode -> token 0 at h row `slot`; union ->
-// the expert's perm range (routed) or every token (shared).
+// the expert's perm range (routed) or every token (shared); a small fused
+// batch (slot kTokPacked) -> up to four tokens named in `tok` (8 bits each)
+// at h rows p0, p0 + 1, ....
+constexpr int kTokPacked = -2;
 struct TokList {
   int n_tok;
-  int p0;      // union routed: first perm position; -1 otherwise
-  int slot;    // decode: slot index
+  int p0;      // union routed: first perm position; packed: first h row; -1 otherwise
+  int slot;    // decode: slot index; kTokPacked: packed list
   bool shared;
+  int tok;     // packed list: token n in bits 8n .. 8n + 7
 };
 
 __device__ __forceinline__ void tok_at(const FfnArgs &a, bool union_mode, const TokList &s, int n,
                                        int &t, int &hrow, int &j) {
-  if (!union_mode) {
+  if (s.slot == kTokPacked) {
+    t = (s.tok >> (8 * n)) & 0xFF;
+    hrow = s.p0 + n;
+    j = 0;
+  } else if (!union_mode) {
     t = 0;
     hrow = s.slot;
     j = s.slot;

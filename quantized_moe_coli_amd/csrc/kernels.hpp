@@ -197,6 +197,16 @@ hipError_t launch_decode_fused(const FfnArgs &f, const float *x, const float *ga
                                uint64_t *trace = nullptr, int trace_wgs = 0,
                                int *grid_out = nullptr);
 
+// A batch of 2 to 4 tokens (f.T) in one kernel: logits (or supplied ones),
+// selection, the batch union, the combine (decode.hip).  The same header,
+// waits and outputs as launch_decode_fused; idx/w: the workspace's [T][k]
+// rows, through which the selections pass; hsh: [4][I] binary32; h rows of
+// f.hq / f.hd: [T*k + T][...].  hipErrorNotSupported for other batch sizes
+// and shapes.
+hipError_t launch_small_fused(const FfnArgs &f, const float *x, const float *gate_w,
+                              const float *logits_in, float *logits_out, uint32_t *ctr, float *hsh,
+                              hipStream_t st, KEvents ev = {}, int *grid_out = nullptr);
+
 // Plain streaming read of `bytes` (a multiple of 16, 16-byte aligned) with
 // 16-byte non-temporal loads, one sum word per workgroup into out[grid]
 // (keeps the loads live); *grid_out receives the grid size.
