@@ -722,6 +722,10 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
 // ===========================================================================
 constexpr int kSmallMaxT = 4;
 constexpr int kSmallPipe = 1;  // gate/up row passes in flight per wave
+// D items: row passes per wave, experts whose weights are in flight together
+constexpr int small_dpass(int dcpl) { return dcpl == 1 ? 2 : 1; }
+// (at most 12 staged h rows, so two workgroups still fit a CU's LDS)
+constexpr int small_dsg(int dcpl, int t) { return dcpl == 1 ? 12 / t : 2; }
 constexpr int kCtrSel = kCtrSpin + 16;  // selections published (a word of the polling-bound line)
 constexpr int kShLine = kSelMaxK;       // the shared expert's slot counter line
 
@@ -911,13 +915,20 @@ __device__ __forceinline__ void small_shared_rows(const DecodeArgs &d, int r0, i
 }
 
 // D item: output rows [r0, r0 + down_rows) for every token.  "Experts" in
-// order: q = 0 the shared one (its T rows at k*T), then unique u = q - 1
-// (its pairs' rows ufirst[u] .. ufirst[u+1]-1), SG at a time; wave w owns
-// rows r0 + w*PR .. for every expert and token, so each token's y is
-// summed in this fixed order.
+// order: x = 0 the shared one (its T rows at k*T), then unique u = x - 1
+// (its pairs' rows ufirst[u] .. ufirst[u+1]-1).  They are taken in groups
+// of at most SG units of at most SG*T staged h rows in all (a unit: some
+// consecutive rows of one expert; an expert normally has at most T pairs,
+// but a token may repeat an expert); wave w owns rows r0 + w*PR .. for
+// every expert and token.  Each (token, slot) output
+// row is the union path's: its lanes' chunk products summed, times the row
+// scale; they are kept in LDS (ob) and combined per token in slot order as
+// the union path's combine does, so both paths give the same bits.
+constexpr int kSmallObRows = 32;  // output rows per D item, at most
 template <int BITS, int LPR, int CPL, int NPASS, int SG, int T>
 __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const SmallUnion &su, int r0,
-                                                int8_t *lds_q, float *lds_d, int *srow) {
+                                                int8_t *lds_q, float *lds_d, int *srow,
+                                                float (*ob)[kSmallObRows]) {
   constexpr int RPP = 64 / LPR;
   const FfnArgs &a = d.f;
   const int I = a.L.I, H = a.L.H, k = a.k, hr0 = k * T;
@@ -927,20 +938,39 @@ __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const Small
   const size_t row_bytes = (size_t)I * BITS / 8;
   const int nx = su.U + 1;
   const int wrow0 = r0 + wave * NPASS * RPP;
-  float y[T][NPASS];
-#pragma unroll
-  for (int t = 0; t < T; ++t)
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) y[t][p] = 0.f;
+  static_assert(kDecWaves * NPASS * RPP <= kSmallObRows, "output rows per D item");
 
-  for (int g0 = 0; g0 < nx; g0 += SG) {
-    const int gn = min(SG, nx - g0);
+  constexpr int R = SG * T;  // staged rows per group
+  int nxt = 0, nxr = 0;      // next expert and its next row
+  while (nxt < nx) {
+    // the next group: units (expert ux[q], its rows [rbeg[q], + rcnt[q]))
+    int ux[SG], rbeg[SG], rcnt[SG], nrows = 0, gn = 0;
+#pragma unroll
+    for (int q = 0; q < SG; ++q) {
+      ux[q] = 0;
+      rbeg[q] = 0;
+      rcnt[q] = 0;
+      if (nxt < nx && nrows < R) {
+        const int cnt = nxt == 0 ? T : su.ufirst[nxt] - su.ufirst[nxt - 1];
+        const int take = min(cnt - nxr, R - nrows);
+        ux[q] = nxt;
+        rbeg[q] = (nxt == 0 ? hr0 : su.ufirst[nxt - 1]) + nxr;
+        rcnt[q] = take;
+        nrows += take;
+        gn = q + 1;
+        nxr += take;
+        if (nxr == cnt) {
+          ++nxt;
+          nxr = 0;
+        }
+      }
+    }
     uint4 wv[SG][NPASS][CPL];
     float sdv[SG][NPASS];
 #pragma unroll
     for (int q = 0; q < SG; ++q) {
       if (q < gn) {
-        const int x = g0 + q;
+        const int x = ux[q];
         const ExpertPtrs ep = expert_ptrs(a.L, x == 0 ? -1 : su.ue[x - 1]);
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
@@ -952,17 +982,11 @@ __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const Small
         }
       }
     }
-    // the group's h rows: first row and count of each of its experts
-    int rbeg[SG], rcnt[SG], nrows = 0;
-#pragma unroll
-    for (int q = 0; q < SG; ++q) {
-      const int x = g0 + q;
-      rbeg[q] = q >= gn ? 0 : x == 0 ? hr0 : su.ufirst[x - 1];
-      rcnt[q] = q >= gn ? 0 : x == 0 ? T : su.ufirst[x] - su.ufirst[x - 1];
-      nrows += rcnt[q];
-    }
     if ((int)threadIdx.x < gn) {
-      const int x = g0 + threadIdx.x;
+      int x = 0;
+#pragma unroll
+      for (int q = 0; q < SG; ++q)
+        if (q == (int)threadIdx.x) x = ux[q];
       const uint32_t *c = d.ctr + kCtrSlot0 + (x == 0 ? kShLine : x - 1) * kCtrStride;
       const uint32_t target = (uint32_t)(I / kGuRows);
       const uint32_t sb = spin_bound(d, 8u * kSpinLimit);
@@ -1011,11 +1035,11 @@ __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const Small
 #pragma unroll
     for (int q = 0; q < SG; ++q) {
       for (int r = 0; r < rcnt[q]; ++r, ++g) {
-        // the pair's token and weight (the shared expert: token r, weight 1)
-        const int x = g0 + q;
+        // the pair's token and slot (the shared expert: token r, slot k)
+        const int x = ux[q];
         const int pair = x == 0 ? -1 : su.sorted[rbeg[q] + r];
-        const int tok = x == 0 ? r : pair / k;
-        const float wgt = x == 0 ? 1.f : su.pw[pair];
+        const int tok = x == 0 ? rbeg[q] - hr0 + r : pair / k;
+        const int slot = x == 0 ? k : pair % k;
         Act<BITS> act[CPL];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
@@ -1028,22 +1052,27 @@ __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const Small
           float acc = 0.f;
 #pragma unroll
           for (int i = 0; i < CPL; ++i) acc += chunk_part<BITS>(wv[q][p][i], act[i]);
-          const float contrib = (x == 0 ? sdv[q][p] : wgt * sdv[q][p]) * acc;
-#pragma unroll
-          for (int t = 0; t < T; ++t)
-            if (t == tok) y[t][p] += contrib;
+          acc = group_sum<LPR>(acc);
+          if (lane == group_sum_lane<LPR>(lane))
+            ob[tok * (k + 1) + slot][wrow0 - r0 + p * RPP + rsub] = acc * sdv[q][p];
         }
       }
     }
     __syncthreads();
   }
-#pragma unroll
-  for (int t = 0; t < T; ++t)
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-      const float yr = group_sum<LPR>(y[t][p]);
-      if (lane == group_sum_lane<LPR>(lane)) a.y[(size_t)t * H + wrow0 + p * RPP + rsub] = yr;
+  // y = o_shared + the kept slots' w * o in slot order, one thread per
+  // (token, row)
+  const int rows = kDecWaves * NPASS * RPP;
+  for (int i = threadIdx.x; i < T * rows; i += kDecThreads) {
+    const int t = i / rows, rl = i % rows;
+    float y = ob[t * (k + 1) + k][rl];
+    for (int j = 0; j < k; ++j) {
+      if (su.pidx[t * k + j] < 0) continue;
+      y += su.pw[t * k + j] * ob[t * (k + 1) + j][rl];
     }
+    a.y[(size_t)t * H + r0 + rl] = y;
+  }
+  __syncthreads();
 }
 
 // GR item: unique expert u's gate/up rows [32 rb, +32) for its n tokens
@@ -1114,8 +1143,8 @@ __device__ __forceinline__ void small_gateup(const DecodeArgs &d, const SmallUni
   }
   __syncthreads();
   // SwiGLU and Q8_0 of each token's 32 values of h: 32 threads per token
-  {
-    const int n = threadIdx.x >> 5, i = threadIdx.x & 31;
+  for (int n0 = 0; n0 < n_tok; n0 += kDecThreads / 32) {
+    const int n = n0 + (threadIdx.x >> 5), i = threadIdx.x & 31;
     if (n < n_tok) {
       const float h = swiglu_h(hs[n][i], hu[n][i]);
       float amax = group_max<32>(fabsf(h));
@@ -1140,14 +1169,17 @@ __device__ __forceinline__ void small_gateup(const DecodeArgs &d, const SmallUni
 template <int BITS, int GLPR, int GCPL, int DLPR, int DCPL, int T>
 __global__ __launch_bounds__(kDecThreads)
 __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 2))) void k_small_fused(DecodeArgs d) {
-  constexpr int DNPASS = DCPL == 1 ? 2 : 1;
-  constexpr int DSG = DCPL == 1 ? 3 : 2;
+  constexpr int DNPASS = small_dpass(DCPL);
+  constexpr int DSG = small_dsg(DCPL, T);
   __shared__ SmallUnion su;
-  __shared__ float hs[kSmallMaxT][kGuRows], hu[kSmallMaxT][kGuRows];
-  __shared__ __align__(16) int8_t hcode[kSmallMaxT][kGuRows];
+  // a GR item's g, u and h codes: one row per pair of its expert (at most
+  // every pair of the batch, if the tokens repeat an expert)
+  __shared__ float hs[kSelMaxK][kGuRows], hu[kSelMaxK][kGuRows];
+  __shared__ __align__(16) int8_t hcode[kSelMaxK][kGuRows];
   __shared__ double lpart[kSmallMaxT][kDecWaves];
   __shared__ int s_ticket;
   __shared__ int srow[DSG * kSmallMaxT];
+  __shared__ float ob[kSelMaxK + kSmallMaxT][kSmallObRows];  // a D item's (token, slot) rows
   __shared__ int32_t sidx[kSelMaxK];
   __shared__ float sw[kSelMaxK];
   // dynamic LDS: [selection scratch, later a D item's staged h | the tokens'
@@ -1234,7 +1266,7 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 2))) void k_small_fused(Decod
   int8_t *lds_q = reinterpret_cast<int8_t *>(dyn);
   float *lds_d = reinterpret_cast<float *>(dyn + (size_t)DSG * T * I);
   for (; t < total; t = next_ticket())
-    small_down_rows<BITS, DLPR, DCPL, DNPASS, DSG, T>(d, su, (t - n_gr) * d.down_rows, lds_q, lds_d, srow);
+    small_down_rows<BITS, DLPR, DCPL, DNPASS, DSG, T>(d, su, (t - n_gr) * d.down_rows, lds_q, lds_d, srow, ob);
 
   // the last workgroup out clears the header for the next call
   __syncthreads();
@@ -1342,8 +1374,8 @@ static hipError_t launch_fused_bits(DecodeArgs d, hipStream_t st, KEvents ev) {
 
 template <int BITS, int GLPR, int GCPL, int DLPR, int DCPL, int T>
 static hipError_t launch_small_t(DecodeArgs d, hipStream_t st, KEvents ev) {
-  constexpr int DNPASS = DCPL == 1 ? 2 : 1;
-  constexpr int DSG = DCPL == 1 ? 3 : 2;
+  constexpr int DNPASS = small_dpass(DCPL);
+  constexpr int DSG = small_dsg(DCPL, T);
   const int I = d.f.L.I, H = d.f.L.H, E = d.f.E, k = d.f.k;
   d.down_rows = kDecWaves * DNPASS * (64 / DLPR);
   if (H % d.down_rows || I % kGuRows || T * k > kSelMaxK || (d.gate_w && T * E > kMaxSlices) ||

@@ -476,6 +476,43 @@ def test_glm_mtp_verify_union(glm):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("T", [2, 4])
+def test_glm_small_batch_computed_logits(glm, T):
+    """Batches of 2 and 4 tokens (one kernel: logit slices for every token,
+    per-token selection, the batch union, the combine), computed logits."""
+    x = inputs.tokens(glm.s, 0, 2000 + T, T, "cuda")
+    y, idx, w, lg = glm.gpu_forward(x)
+    y_r, idx_r, w_r, lg_r = glm.oracle_forward(x.cpu().numpy())
+    assert ulp_diff(lg, lg_r).max() <= 1
+    np.testing.assert_array_equal(idx, idx_r)
+    np.testing.assert_array_equal(w, w_r)
+    assert_close_layer(y, y_r)
+
+
+@pytest.mark.slow
+def test_small_batch_wait_giveup_is_reported(glm):
+    """The small-batch kernel's bounded waits (scores, selections, slots)
+    forced to give up from the host, as for the decode kernel: the call
+    completes, the status word records it, the header is left clear and the
+    next call is bit-identical to one on a fresh workspace."""
+    T = 3
+    x = inputs.tokens(glm.s, 0, 7, T, "cuda")
+    ref = glm.gpu_forward(x)
+    ws = B.workspace(glm.gpu, T)
+    off = B.WORKSPACE_SPIN_LIMIT_OFFSET
+    ws[off:off + 4].copy_(torch.tensor([1, 0, 0, 0x80], dtype=torch.uint8))  # 0x80000001
+    glm.gpu_forward(x, ws=ws)  # outputs undefined
+    st = _ws_status(ws, clear=True)
+    assert st == B.WAIT_SCORES | B.WAIT_SLOTS, st
+    hdr = ws[:B.WORKSPACE_COUNTER_BYTES].cpu().numpy()
+    assert (hdr == 0).all()
+    b = glm.gpu_forward(x, ws=ws)
+    for u, v in zip(b, ref):
+        np.testing.assert_array_equal(u, v)
+    assert _ws_status(ws) == 0
+
+
+@pytest.mark.slow
 @pytest.mark.parametrize("T", [8, 64])
 def test_glm_union_sampled(glm, T):
     """Computed logits; a union batch of T tokens, 3 sampled tokens checked
