@@ -98,6 +98,8 @@ def expert_bytes(s) -> dict:
 KERNEL_SOURCES = {
     "k_decode_fused": ["decode.hip", "actq.hpp", "device.hpp", "ffn_common.hpp", "kernels.hpp",
                        "select.hpp"],
+    "k_small_fused": ["decode.hip", "actq.hpp", "device.hpp", "ffn_common.hpp", "kernels.hpp",
+                      "select.hpp"],
     "k_gateup_mfma": ["mfma.hip", "device.hpp", "ffn_common.hpp", "kernels.hpp"],
     "k_down_mfma": ["mfma.hip", "device.hpp", "ffn_common.hpp", "kernels.hpp"],
 }
