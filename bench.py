@@ -222,6 +222,9 @@ def main() -> int:
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one untimed device-to-device copy of this many MiB after the "
                          "warm-up (the known-size reference for hardware byte counters)")
+    ap.add_argument("--stacked", action="store_true",
+                    help="gemvf32 workload: one launch over the 16 experts' gate-shaped rows "
+                         "stacked (32768 x 6144) and one over their down-shaped rows (98304 x 2048)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's timed CPU sample (0 disables it)")
     args = ap.parse_args()
@@ -1374,7 +1377,10 @@ def gemv_f32_main(args) -> int:
     s = inputs.GLM if args.bits is None else inputs.GLM.with_(bits=args.bits)
     H, I, b = s.hidden, s.inter, s.bits
     K, W, NE = args.steps, args.warmup, 16
-    shapes = [(I, H), (H, I)]
+    # stacked: the 16 experts' matrices as one tall matrix of each shape
+    shapes = [(NE * I, H), (NE * H, I)] if args.stacked else [(I, H), (H, I)]
+    if args.stacked:
+        NE = 1
     mats = []
     for e in range(NE):
         row = []
@@ -1438,12 +1444,16 @@ def gemv_f32_main(args) -> int:
         "vs_baseline": None,
         "dtype": f"int{b}xf32->f32",
         "data": "synthetic",
-        "config": {"workload": f"one token through a GLM-5.2 expert's gate-shaped (2048 x 6144) "
-                               f"and down-shaped (6144 x 2048) int{b} matrices with per-row "
-                               f"fp32 scales, binary32 activations; {NE} experts resident"},
+        "config": {"workload": (f"one token through 16 GLM-5.2 experts' rows stacked: a "
+                                f"{shapes[0][0]} x {shapes[0][1]} and a {shapes[1][0]} x {shapes[1][1]} "
+                                f"int{b} matrix with per-row fp32 scales, binary32 activations"
+                                if args.stacked else
+                                f"one token through a GLM-5.2 expert's gate-shaped (2048 x 6144) "
+                                f"and down-shaped (6144 x 2048) int{b} matrices with per-row "
+                                f"fp32 scales, binary32 activations; {NE} experts resident")},
         "roofline": {
             "bound": "hbm",
-            "kernel": f"k_gemv_f32act<{b}> (gate-shaped matrix)",
+            "kernel": f"k_gemv_f32act<{b}> ({shapes[0][0]} x {shapes[0][1]} matrix)",
             "achieved": round(gbps[0], 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -257,21 +257,39 @@ hipError_t launch_quant_pack(int bits, const float *w, int64_t rows, int64_t col
 // f32-activation variant of the quantised product (colibrì README,
 // "Implemented features": for a single row the int4 kernel keeps its
 // activations in f32, measured faster than the integer path there):
-// y[r] = s_r * sum_c code[r][c] * x[c] for one token, the codes
-// sign-extended in registers and multiplied with the binary32 activations.
-// x is staged in LDS once per workgroup; the four float4 groups of a
-// 16-byte weight chunk's activations are stored rotated by the chunk index,
-// so the lanes of a wave (one chunk each) read different banks.  A wave owns
-// RW rows; a lane takes chunks lane, lane + 64, ... of each, all loaded at
-// once, and reuses each chunk's activations for its RW rows.  fp32 sums,
-// wave-reduced with DPP.
+// y[r] = s_r * sum_c code[r][c] * x[c] for one token.  The codes are taken
+// in offset binary, u = code + B (B = 2^(BITS-1)): flipping each field's
+// sign bit turns a two's complement field into u, masking spreads a word's
+// fields over the bytes of NS words (byte b of group s: field s + NS*b of
+// the word), and v_cvt_f32_ubyte converts each byte; so a weight costs a
+// byte conversion, an FMA and a fraction of an integer op.  The sum of
+// u * x then loses B * sum(x), one correction per row (sum(x) is the same
+// for every row).  x is staged in LDS once per workgroup in the order the
+// bytes consume it, the float4 groups of a chunk rotated by the chunk
+// index so the lanes of a wave (one chunk each) read different banks.  A
+// wave owns RW rows; a lane takes chunks lane, lane + 64, ... of each, all
+// loaded at once.  fp32 sums, wave-reduced with DPP.
+template <int BITS>
+struct F32Act {
+  static constexpr int NS = BITS == 8 ? 1 : BITS == 4 ? 2 : 4;  // byte groups per word
+  static constexpr int G = 4 * NS;                               // float4 groups per chunk
+  static constexpr int FPW = 32 / BITS;                          // fields per word
+  static constexpr uint32_t FLIP = BITS == 8 ? 0x80808080u : BITS == 4 ? 0x88888888u : 0xAAAAAAAAu;
+  static constexpr uint32_t MASK = BITS == 8 ? 0xFFFFFFFFu : BITS == 4 ? 0x0F0F0F0Fu : 0x03030303u;
+  static constexpr float BIAS = (float)(1 << (BITS - 1));
+  // element (within the chunk) of byte b of group s of word w
+  __host__ __device__ static int elem(int w, int s, int b) { return w * FPW + s + NS * b; }
+};
+
 template <int BITS, int CPL, int RW>
 __global__ __launch_bounds__(256) void k_gemv_f32act(const uint8_t *__restrict__ W,
                                                      const float *__restrict__ scale, int64_t rows,
                                                      int64_t cols, const float *__restrict__ x,
                                                      float *__restrict__ y) {
-  constexpr int kElems = 128 / BITS, kPerWord = 32 / BITS, kN4 = kElems / 4;
+  using F = F32Act<BITS>;
+  constexpr int kElems = 128 / BITS;
   extern __shared__ __align__(16) float xs[];
+  __shared__ float xsum_w[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nchunks = cols * BITS / 128;
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RW;
@@ -284,16 +302,30 @@ __global__ __launch_bounds__(256) void k_gemv_f32act(const uint8_t *__restrict__
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int64_t c = lane + 64 * i;
-      wv[rr][i] = c < nchunks ? ld_nt(wr + c) : make_uint4(0, 0, 0, 0);
+      wv[rr][i] = c < nchunks ? ld_nt(wr + c) : make_uint4(F::FLIP, F::FLIP, F::FLIP, F::FLIP);
     }
   }
-  // float4 group m of chunk c at position c*kN4 + (m + c) % kN4
-  for (int64_t q = threadIdx.x; q < nchunks * kN4; q += 256) {
-    const int64_t c = q / kN4;
-    const int m = (int)(q - c * kN4);
-    reinterpret_cast<float4 *>(xs)[c * kN4 + (m + c) % kN4] = reinterpret_cast<const float4 *>(x)[q];
+  // x into LDS, read as float4 and each value written to its place (byte b
+  // of group g = NS * w + s of chunk c at float4 c*G + (g + c) % G), and
+  // sum(x): each thread's values in order, then the waves' in order
+  float part = 0.f;
+  for (int64_t q = threadIdx.x; q < nchunks * (kElems / 4); q += 256) {
+    const float4 v = reinterpret_cast<const float4 *>(x)[q];
+    const int64_t c = q / (kElems / 4);
+    const int e0 = (int)(q - c * (kElems / 4)) * 4;  // first element (within the chunk)
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = e0 + m, w = e / F::FPW, j = e % F::FPW, s = j % F::NS, b = j / F::NS;
+      const int g = F::NS * w + s;
+      xs[(c * F::G + (g + c) % F::G) * 4 + b] = vv[m];
+    }
+    part += ((v.x + v.y) + (v.z + v.w));
   }
+  part = wave_sum(part);
+  if (lane == 0) xsum_w[wave] = part;
   __syncthreads();
+  const float xsum = (xsum_w[0] + xsum_w[1]) + (xsum_w[2] + xsum_w[3]);
   float acc[RW];
 #pragma unroll
   for (int rr = 0; rr < RW; ++rr) acc[rr] = 0.f;
@@ -301,20 +333,24 @@ __global__ __launch_bounds__(256) void k_gemv_f32act(const uint8_t *__restrict__
   for (int i = 0; i < CPL; ++i) {
     const int64_t c = lane + 64 * i;
     if (c < nchunks) {
-      const float4 *xc = reinterpret_cast<const float4 *>(xs) + c * kN4;
+      const float4 *xc = reinterpret_cast<const float4 *>(xs) + c * F::G;
 #pragma unroll
-      for (int m = 0; m < kN4; ++m) {
-        const float4 v = xc[(m + c) % kN4];
-        const float xv[4] = {v.x, v.y, v.z, v.w};
+      for (int w = 0; w < 4; ++w) {
 #pragma unroll
-        for (int rr = 0; rr < RW; ++rr) {
-          const uint32_t ws[4] = {wv[rr][i].x, wv[rr][i].y, wv[rr][i].z, wv[rr][i].w};
+        for (int s = 0; s < F::NS; ++s) {
+          const int g = F::NS * w + s;
+          const float4 v = xc[(g + c) % F::G];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int k = 4 * m + j;
-            const int sh = 32 - BITS * (k % kPerWord + 1);
-            const int code = (int)(ws[k / kPerWord] << sh) >> (32 - BITS);  // sign-extended field
-            acc[rr] = fmaf((float)code, xv[j], acc[rr]);
+          for (int rr = 0; rr < RW; ++rr) {
+            const uint32_t word = w == 0 ? wv[rr][i].x : w == 1 ? wv[rr][i].y : w == 2 ? wv[rr][i].z : wv[rr][i].w;
+            uint32_t u = ((word ^ F::FLIP) >> (BITS * s)) & F::MASK;
+            // keep the masked word whole, so each byte converts straight
+            // from it (v_cvt_f32_ubyte0..3) instead of a field extract first
+            asm volatile("" : "+v"(u));
+            acc[rr] = fmaf((float)(u & 0xFFu), v.x, acc[rr]);
+            acc[rr] = fmaf((float)((u >> 8) & 0xFFu), v.y, acc[rr]);
+            acc[rr] = fmaf((float)((u >> 16) & 0xFFu), v.z, acc[rr]);
+            acc[rr] = fmaf((float)(u >> 24), v.w, acc[rr]);
           }
         }
       }
@@ -323,7 +359,7 @@ __global__ __launch_bounds__(256) void k_gemv_f32act(const uint8_t *__restrict__
 #pragma unroll
   for (int rr = 0; rr < RW; ++rr) {
     const float sum = wave_sum(acc[rr]);
-    if (lane == 0 && row0 + rr < rows) y[row0 + rr] = scale[row0 + rr] * sum;
+    if (lane == 0 && row0 + rr < rows) y[row0 + rr] = scale[row0 + rr] * fmaf(-F::BIAS, xsum, sum);
   }
 }
 
