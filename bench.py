@@ -837,8 +837,8 @@ def stack_main(args) -> int:
 
     # kernel durations: an eager pass over the first steps, every layer's
     # launches recording start and stop events (T = 1: the fused decode
-    # kernel; T > 1: front, gate/up and down on the dot-product path, gate/up
-    # and down on the matrix cores)
+    # kernel; T = 2-4: the fused small-batch kernel; larger T: front, gate/up
+    # and down on the dot-product path, gate/up and down on the matrix cores)
     hip = _hip()
     KP = min(K, 32)
     n_ev = 2 if T == 1 else 10
@@ -851,13 +851,16 @@ def stack_main(args) -> int:
             B.coli_moe_forward_profiled(L, stack.rmsnorm(h), y, ws, e, c_layer=stk.c_layers[li])
             h.add_(y)
     torch.cuda.synchronize()
-    kms = []
-    dom_k = 0 if T == 1 else 1  # the fused kernel / the dot-product gate/up kernel
-    for i in range(KP * NL):
+    def ev_ms(i, k):
         v = ctypes.c_float()
-        rc = hip.hipEventElapsedTime(ctypes.byref(v), ctypes.c_void_p(evs[i * n_ev + 2 * dom_k]),
-                                     ctypes.c_void_p(evs[i * n_ev + 2 * dom_k + 1]))
-        kms.append(v.value if rc == 0 else float("nan"))
+        rc = hip.hipEventElapsedTime(ctypes.byref(v), ctypes.c_void_p(evs[i * n_ev + 2 * k]),
+                                     ctypes.c_void_p(evs[i * n_ev + 2 * k + 1]))
+        return v.value if rc == 0 else float("nan")
+
+    # a small batch that ran as one kernel records only the first events
+    single = T == 1 or (T <= 4 and all(np.isnan(ev_ms(i, 1)) for i in range(KP * NL)))
+    dom_k = 0 if single else 1  # the fused kernel / the dot-product gate/up kernel
+    kms = [ev_ms(i, dom_k) for i in range(KP * NL)]
     for e in evs:
         hip.hipEventDestroy(ctypes.c_void_p(e))
     hip.hipGetLastError()
@@ -877,9 +880,10 @@ def stack_main(args) -> int:
     tokens_per_s = T * K / (total_ms / 1e3)
     gbps = float(step_bytes.mean()) / (ms_per_step * 1e-3) / 1e9
     k_avg_ms = float(np.nanmean(kms))
-    if T == 1:
+    if single:
         k_bytes = float(launch_bytes[:KP].mean())
-        k_name = "k_decode_fused (one layer for one token)"
+        k_name = ("k_decode_fused (one layer for one token)" if T == 1 else
+                  f"k_small_fused (one layer for the {T}-token batch)")
     else:  # T < 8: every slot on the dot-product path
         k_bytes = float(((uniq[:KP] + 1) * ebd["gate_up"]).mean())
         k_name = "k_gateup_union (one layer's gate/up for the batch union)"
@@ -914,7 +918,8 @@ def stack_main(args) -> int:
                         "expert top-p 0.7 renormalised; "
                         + ("batch-1 decode" if T == 1 else
                            f"{T}-token MTP verify batches (the current token and {T - 1} "
-                           "drafts) run as one batch union per layer")
+                           "drafts) run as one batch union per layer"
+                           + (" in one kernel" if single else ""))
                         + ", h <- h + MoE(rmsnorm(h)) between layers",
             "tokens_per_step": T,
             "layers": NL,
