@@ -434,11 +434,13 @@ coli_status coli_moe_forward_cached(const coli_moe_layer *L,
  * A host-side controller (no device work).  After every step the caller
  * reports the drafts it verified, how many were accepted and the step's
  * cost (any additive measure: microseconds, expert bytes read, host-link
- * bytes).  The guard keeps, per mode, exponentially weighted sums of the
- * cost and of the tokens produced (1 + accepted per step); their ratio is
- * that mode's cost per produced token (a ratio of averages: an average of
- * per-step ratios would overrate drafting's cost when acceptance varies
- * from step to step).  It answers
+ * bytes).  The guard keeps, per mode, an exponentially weighted average of
+ * the step cost (weight ema for the newest step) and a slower one of the
+ * tokens each step produces, 1 + accepted (weight 0.4 * ema: the accepted
+ * count varies from step to step around a slowly moving rate, while the step
+ * cost follows the cache); their ratio is that mode's cost per produced
+ * token (a ratio of averages: an average of per-step ratios would overrate
+ * drafting's cost when acceptance varies from step to step).  It answers
  * the drafts for the next step: max_draft while the drafting estimate is at
  * most (1 + margin) times the plain one, else 0.  Every probe_every steps it
  * runs one step in the mode not in use, so both estimates stay current
@@ -452,7 +454,7 @@ typedef struct {
   float margin;        /* drafting kept while cost_draft <= cost_plain * (1 + margin) */
   /* state, written by init and step */
   double cost_draft, cost_plain; /* per produced token; negative: not yet measured */
-  double sum_cost[2], sum_tokens[2]; /* weighted sums, [0] plain, [1] drafting */
+  double sum_cost[2], sum_tokens[2]; /* averages per step of the cost and of the tokens, [0] plain, [1] drafting */
   int32_t next_draft;            /* drafts the next step should verify */
   int32_t since_probe;           /* steps since the last probe */
   int64_t steps, draft_steps, tokens;

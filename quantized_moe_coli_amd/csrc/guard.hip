@@ -2,9 +2,10 @@
 // pays only while the accepted drafts save more than their verification's
 // extra expert loads cost; the pages turn drafting off adaptively for the
 // cold-cache case (colibrì README, "Implemented features", native MTP item;
-// "Quick start": DRAFT=n).  Per mode, exponentially weighted sums of cost
-// and of produced tokens, whose ratio estimates the cost per token; the
-// cheaper mode runs, the other is probed periodically.
+// "Quick start": DRAFT=n).  Per mode, an exponentially weighted average of
+// the step cost and a slower one of the tokens per step, whose ratio
+// estimates the cost per token; the cheaper mode runs, the other is probed
+// periodically.
 #include <cmath>
 
 #include "coli_moe.h"
@@ -42,9 +43,12 @@ int32_t coli_spec_guard_step(coli_spec_guard *g, int32_t drafted, int32_t accept
     return -1;
   const int produced = 1 + accepted;
   const int m = drafted > 0 ? 1 : 0;
-  const double w = g->sum_tokens[m] > 0.0 ? (double)g->ema : 1.0;  // the first sample sets the sums
+  // the first sample sets both averages; the tokens' average moves slower
+  const bool first = !(g->sum_tokens[m] > 0.0);
+  const double w = first ? 1.0 : (double)g->ema;
+  const double wn = first ? 1.0 : 0.4 * (double)g->ema;
   g->sum_cost[m] = (1.0 - w) * g->sum_cost[m] + w * cost;
-  g->sum_tokens[m] = (1.0 - w) * g->sum_tokens[m] + w * produced;
+  g->sum_tokens[m] = (1.0 - wn) * g->sum_tokens[m] + wn * produced;
   (m ? g->cost_draft : g->cost_plain) = g->sum_cost[m] / g->sum_tokens[m];
   g->steps += 1;
   g->tokens += produced;

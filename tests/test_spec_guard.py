@@ -91,3 +91,27 @@ def test_cost_per_token_is_a_ratio_of_averages():
     assert abs(g.c.cost_draft - 4.4 / 2.7) < 0.35
     tail = chosen[40:]
     assert sum(1 for c in tail if c == 0) <= len(tail) // 16 + 1
+
+
+def test_noisy_acceptance_does_not_switch_paying_drafts_off():
+    # a verify step costs 3.22 and a plain one 2.06 (the resident stack's
+    # timings with verify batches in one kernel); each of 2 drafts is
+    # accepted with probability 0.6 after the previous one: 1.96 tokens per
+    # verify on average, 1.64 per token < 2.06, though a step that accepts
+    # nothing costs 3.22 for one token.  Over seeds, drafting stays the
+    # choice outside the probes.
+    import numpy as np
+    fracs = []
+    for seed in range(20):
+        rng = np.random.default_rng(seed)
+        g = B.SpecGuard(2, probe_every=16, ema=0.25)
+
+        def accept(t, d):
+            a = 0
+            while a < d and rng.random() < 0.6:
+                a += 1
+            return a
+
+        chosen = drive(g, lambda t, d: 3.22 if d else 2.06, accept, 200)
+        fracs.append(sum(1 for c in chosen if c) / len(chosen))
+    assert np.mean(fracs) >= 0.65, fracs  # equal-weight averages: ~0.43
