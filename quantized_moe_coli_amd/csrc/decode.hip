@@ -10,10 +10,11 @@
 // down phases each pay a launch, ramp-up and drain that one streaming kernel
 // pays once.
 //
-// Work items, in ticket order:
-//   L   router logits, four expert rows per item (two waves per row, each
-//       summing half of the row in binary64; skipped if logits are given)
-//   GS  shared-expert gate/up + SwiGLU + Q8_0(h), kGuRows rows per item
+// Every workgroup first computes its router logit slices (binary64 partial
+// sums of gate rows; skipped if logits are given), quantises x into its LDS
+// and requests its rows of the shared expert's gate/up, then selects the
+// token's experts and finishes those rows.  Then work items, in ticket
+// order:
 //   GR  routed-expert gate/up, one (slot, kGuRows-row block) per item
 //   D   down projection + combine for a block of output rows, all slots in
 //       the combine order (shared, then routed 0 .. k-1).
@@ -53,13 +54,14 @@ namespace coli {
 // Workspace header (uint32 words, zero between calls except the status):
 //   counters, each on its own 256-byte line so polls and atomic adds on one
 //   do not contend with the others: one ticket per work queue, the finished
-//   workgroups, and per slot (routed 0 .. k-1, shared k) the finished
-//   gate/up items;
+//   workgroups, and per slot the finished gate/up items (routed 0 .. k-1)
+//   or rows (shared, k);
 //   the status word (sticky: give-ups of bounded waits, never cleared by the
 //   kernel) and the polling bound override (test hook: if nonzero at the
 //   start of a call, the bound on every wait's polling rounds; cleared by
 //   the call);
-//   one word per 32-row block of the shared expert: its rows done so far;
+//   one word per 32-row block of the shared expert: its rows done so far
+//   (the small-batch kernel's);
 //   then up to 1024 64-bit words of router logit partials: slice s = e * P + p
 //   holds the complemented bits of the binary64 sum of x . gate_w[e] over the
 //   p-th of P equal column ranges.  Zero means "not written yet" (no finite
@@ -314,89 +316,99 @@ __device__ __forceinline__ void select_local(const DecodeArgs &d, const SelInput
 
 // The shared expert's gate/up rows [r0, r0 + nr) of this workgroup, in
 // passes of RPP rows per wave: g and u summed in binary64 and rounded once,
-// h = SwiGLU, stored in binary32 to hsh with device-scope stores.  Every
-// 32-row block then counts the rows it received; the workgroup whose rows
-// complete a block quantises it to Q8_0 (codes in the container ordering,
-// into the shared slot's h row; its scale) and bumps the shared slot's
-// counter.  The shared expert needs no routing, so this runs while the
-// router's scores are still on their way, spread over every workgroup.
+// h = SwiGLU, stored in binary32 to hsh with device-scope stores.  The
+// shared expert needs no routing, so issue() requests the first pass's
+// weights before the router's scores are polled and the experts selected,
+// and finish() computes (and loads any further pass) once the selection is
+// done: the rows stream while the selection's latency runs.  The workgroup
+// counts its rows in the shared slot's counter once its stores have
+// completed (with its first gate/up item's counter, or on its own), and
+// every D item quantises the shared h to Q8_0 itself.
 template <int BITS, int LPR, int CPL>
-__device__ __forceinline__ void shared_rows(const DecodeArgs &d, int r0, int nr, const int8_t *xq,
-                                            const float *xd, int *s_last) {
-  constexpr int RPP = 64 / LPR;
-  const FfnArgs &a = d.f;
-  const int H = a.L.H, I = a.L.I, k = a.k;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int gl = lane % LPR, rsub = lane / LPR;
-  const int nchunks = H * BITS / 128;
-  const size_t row_bytes = (size_t)H * BITS / 8;
-  const ExpertPtrs ep = expert_ptrs(a.L, -1);
-  Act<BITS> act[CPL];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = gl + LPR * i;
-    if (c < nchunks) load_act<BITS>(act[i], xq, xd, c);
-    else zero_act<BITS>(act[i]);
-  }
-  for (int rp = wave * RPP; rp < nr; rp += kDecWaves * RPP) {
-    const int row = min(r0 + rp + rsub, I - 1);  // a row past the range recomputes the last, unused
+struct SharedRows {
+  static constexpr int RPP = 64 / LPR;
+  uint4 wg[CPL], wu[CPL];
+
+  __device__ __forceinline__ void load(const DecodeArgs &d, int row) {
+    const int H = d.f.L.H, gl = (threadIdx.x & 63) % LPR;
+    const int nchunks = H * BITS / 128;
+    const size_t row_bytes = (size_t)H * BITS / 8;
+    const ExpertPtrs ep = expert_ptrs(d.f.L, -1);
     const uint4 *gp = reinterpret_cast<const uint4 *>(ep.wg + (size_t)row * row_bytes);
     const uint4 *up = reinterpret_cast<const uint4 *>(ep.wu + (size_t)row * row_bytes);
-    uint4 wg[CPL], wu[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = min(gl + LPR * i, nchunks - 1);
       wg[i] = ld_nt(gp + c);
       wu[i] = ld_nt(up + c);
     }
-    double pg = 0.0, pu = 0.0;
+  }
+  // a row past the range recomputes the last, unused
+  __device__ __forceinline__ int row_of(const DecodeArgs &d, int r0, int rp) const {
+    return min(r0 + rp + (int)(threadIdx.x & 63) / LPR, d.f.L.I - 1);
+  }
+  __device__ __forceinline__ void issue(const DecodeArgs &d, int r0, int nr) {
+    const int rp = (int)(threadIdx.x >> 6) * RPP;
+    if (rp < nr) load(d, row_of(d, r0, rp));
+  }
+  __device__ __forceinline__ void finish(const DecodeArgs &d, int r0, int nr, const int8_t *xq,
+                                         const float *xd) {
+    const int H = d.f.L.H;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gl = lane % LPR, rsub = lane / LPR;
+    const int nchunks = H * BITS / 128;
+    const ExpertPtrs ep = expert_ptrs(d.f.L, -1);
+    Act<BITS> act[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      pg += chunk_part_f64<BITS>(wg[i], act[i]);
-      pu += chunk_part_f64<BITS>(wu[i], act[i]);
+      const int c = gl + LPR * i;
+      if (c < nchunks) load_act<BITS>(act[i], xq, xd, c);
+      else zero_act<BITS>(act[i]);
     }
-    pg = group_sum_f64<LPR>(pg);
-    pu = group_sum_f64<LPR>(pu);
-    if (lane == group_sum_lane<LPR>(lane) && rp + rsub < nr) {
-      const float h = swiglu_h(row_out(pg, ep.sg[row]), row_out(pu, ep.su[row]));
-      st_dev(reinterpret_cast<uint32_t *>(d.hsh) + row, __float_as_uint(h));
+    for (int rp = wave * RPP; rp < nr; rp += kDecWaves * RPP) {
+      const int row = row_of(d, r0, rp);
+      if (rp != wave * RPP) load(d, row);
+      double pg = 0.0, pu = 0.0;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        pg += chunk_part_f64<BITS>(wg[i], act[i]);
+        pu += chunk_part_f64<BITS>(wu[i], act[i]);
+      }
+      pg = group_sum_f64<LPR>(pg);
+      pu = group_sum_f64<LPR>(pu);
+      if (lane == group_sum_lane<LPR>(lane) && rp + rsub < nr) {
+        const float h = swiglu_h(row_out(pg, ep.sg[row]), row_out(pu, ep.su[row]));
+        st_dev(reinterpret_cast<uint32_t *>(d.hsh) + row, __float_as_uint(h));
+      }
     }
   }
-  // the rows' stores complete before any block counts them
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  const int b_lo = r0 / 32, b_hi = (r0 + nr - 1) / 32;
-  for (int b = b_lo; b <= b_hi; ++b) {
-    if (threadIdx.x == 0) {
-      const int n_in = min(r0 + nr, 32 * b + 32) - max(r0, 32 * b);
-      const uint32_t old = __hip_atomic_fetch_add(d.ctr + kCtrShBlk + b, (uint32_t)n_in,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *s_last = (int)(old + (uint32_t)n_in) == 32;
-    }
-    __syncthreads();
-    if (*s_last) {
-      // this workgroup completed block b: Q8_0 of its 32 values of h
-      if (threadIdx.x < 32) {
-        const int i = threadIdx.x;
-        const float h = __uint_as_float(ld_dev(reinterpret_cast<const uint32_t *>(d.hsh) + 32 * b + i));
-        const float amax = __shfl(group_max<32>(fabsf(h)), 31, 64);
-        const float db = amax / 127.f;
-        float c = 0.f;
-        if (db != 0.f) c = fminf(fmaxf(rintf(h / db), -127.f), 127.f);
-        // lane j < 8 gathers bytes 4j .. 4j+3 of the block in the container
-        // ordering (byte s holds element perm_src(s))
-        const int code = (int)c & 0xFF;
-        uint32_t word = 0;
+};
+
+// The shared expert's h (binary32, hsh, complete) as Q8_0 codes in the
+// container ordering and block scales, into LDS: 4 values per thread, the 8
+// threads of a 32-value block together (amax, then amax / 127 and the codes
+// rounded to nearest even, as every other Q8_0 step of the layer).
+template <int BITS>
+__device__ __forceinline__ void quantize_shared_h(const DecodeArgs &d, int8_t *q, float *dsc) {
+  const int I = d.f.L.I;
+  const int part = threadIdx.x & 7;
+  for (int i0 = 4 * (int)threadIdx.x; i0 < I; i0 += 4 * kDecThreads) {
+    const uint64_t *src = reinterpret_cast<const uint64_t *>(d.hsh + i0);
+    const uint64_t lo = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float e[4] = {__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                        __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
+    float m = fmaxf(fmaxf(fabsf(e[0]), fabsf(e[1])), fmaxf(fabsf(e[2]), fabsf(e[3])));
+    m = group_max<8>(m);
+    const float db = m / 127.f;
+    const int blk = i0 / 32;
+    if (part == 0) dsc[blk] = db;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          word |= ((uint32_t)__shfl(code, perm_src<BITS>((4 * i + m) & 31), 64) & 0xFFu) << (8 * m);
-        if (i < 8) st_dev(reinterpret_cast<uint32_t *>(a.hq + (size_t)k * I + 32 * b) + i, word);
-        if (i == 0)
-          st_dev(reinterpret_cast<uint32_t *>(a.hd) + (size_t)k * (I / 32) + b, __float_as_uint(db));
-      }
-      publish(d.ctr + kCtrSlot0 + k * kCtrStride, 1u);
+    for (int j = 0; j < 4; ++j) {
+      float c = 0.f;
+      if (db != 0.f) c = fminf(fmaxf(rintf(e[j] / db), -127.f), 127.f);
+      q[(size_t)blk * 32 + perm_dst<BITS>(4 * part + j)] = (int8_t)c;
     }
-    __syncthreads();
   }
 }
 
@@ -443,13 +455,15 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
         }
       }
     }
-    // once every gate/up item of the group's slots is done, stage their h
-    // codes and scales in LDS (device-scope loads, all in flight together)
+    // once every gate/up item of the group's slots is done (the shared
+    // slot: every row of h), stage their h codes and scales in LDS
+    // (device-scope loads, all in flight together); the shared h is
+    // quantised here from binary32
     if ((int)threadIdx.x < gn) {
       const int q = threadIdx.x;
       const int sl = g0 + q == 0 ? k : g0 + q - 1;
       const uint32_t *c = d.ctr + kCtrSlot0 + sl * kCtrStride;
-      const uint32_t target = (uint32_t)(I / kGuRows);
+      const uint32_t target = (uint32_t)(sl == k ? I : I / kGuRows);
       const uint32_t sb = spin_bound(d, 8u * kSpinLimit);
       const uint32_t spin = sb & ~kSpinForced;
       const bool forced = (sb & kSpinForced) != 0u;
@@ -462,21 +476,25 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
     }
     __syncthreads();
     if (g0 == 0) trace_rec(d, trn, kTrDReady, r0);
+    // the staged slots: [q_lo, gn) (slot 0 of the first group is the shared
+    // expert's, quantised below)
+    const int q_lo = g0 == 0 ? 1 : 0;
     if (I % 128 == 0) {
       // straight into LDS: 16-byte loads with the cache policy of the
       // device-scope loads (sc1), all in flight at once and no registers.
       // One wave instruction fills 64 consecutive 16-byte LDS chunks.
       const int cq = I / 16, cd = I / 128;  // chunks of codes / of scales per slot
-      const int nA = gn * cq, nB = gn * cd;
+      const int nA = (gn - q_lo) * cq, nB = (gn - q_lo) * cd;
       const int nwA = (nA + 63) / 64, nwB = (nB + 63) / 64;
       for (int ii = wave; ii < nwA + nwB; ii += kDecWaves) {
         const bool codes = ii < nwA;
         const int base = (codes ? ii : ii - nwA) * 64;
         const int c = base + lane, per = codes ? cq : cd;
         unsigned char *dst = (codes ? reinterpret_cast<unsigned char *>(lds_q)
-                                    : reinterpret_cast<unsigned char *>(lds_d)) + (size_t)base * 16;
+                                    : reinterpret_cast<unsigned char *>(lds_d)) +
+                             ((size_t)q_lo * per + base) * 16;
         if (c < (codes ? nA : nB)) {
-          const int q = c / per, r = c - q * per;
+          const int q = q_lo + c / per, r = c - (q - q_lo) * per;
           const int sl = g0 + q == 0 ? k : g0 + q - 1;
           const unsigned char *src =
               codes ? reinterpret_cast<const unsigned char *>(a.hq) + (size_t)sl * I + r * 16
@@ -485,13 +503,15 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
                                            kLoadSc1);
         }
       }
+      if (q_lo) quantize_shared_h<BITS>(d, lds_q, lds_d);
       __builtin_amdgcn_s_waitcnt(0);
     } else {
+      if (q_lo) quantize_shared_h<BITS>(d, lds_q, lds_d);
       // 64-bit device-scope loads, kStage per thread issued before any is
       // written to LDS
       constexpr int kStage = 2;
       const int wq = I / 8, wd = I / 64;  // 8-byte words of codes and scales per slot
-      const int n = gn * (wq + wd);
+      const int n = (gn - q_lo) * (wq + wd);
       for (int i0 = 0; i0 < n; i0 += kStage * kDecThreads) {
         uint64_t v[kStage];
 #pragma unroll
@@ -499,7 +519,7 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
           const int i = i0 + j * kDecThreads + threadIdx.x;
           v[j] = 0;
           if (i < n) {
-            const int q = i / (wq + wd), r = i - q * (wq + wd);
+            const int q = q_lo + i / (wq + wd), r = i - (q - q_lo) * (wq + wd);
             const int sl = g0 + q == 0 ? k : g0 + q - 1;
             const uint64_t *src = r < wq ? reinterpret_cast<const uint64_t *>(a.hq + (size_t)sl * I) + r
                                          : reinterpret_cast<const uint64_t *>(a.hd + (size_t)sl * (I / 32)) + (r - wq);
@@ -510,7 +530,7 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
         for (int j = 0; j < kStage; ++j) {
           const int i = i0 + j * kDecThreads + threadIdx.x;
           if (i < n) {
-            const int q = i / (wq + wd), r = i - q * (wq + wd);
+            const int q = q_lo + i / (wq + wd), r = i - (q - q_lo) * (wq + wd);
             uint64_t *dst = r < wq ? reinterpret_cast<uint64_t *>(lds_q + (size_t)q * I) + r
                                    : reinterpret_cast<uint64_t *>(lds_d + q * (I / 32)) + (r - wq);
             *dst = v[j];
@@ -554,10 +574,11 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
 
 // Persistent: the grid is at most the workgroups the GPU holds at once.
 // Every workgroup first computes its logit slices, quantises x into its LDS
-// and computes its share of the shared expert's gate/up rows (none of which
-// needs the routing), then selects the token's experts itself and takes
-// tickets: GR items (with a full grid, exactly one per workgroup), then D
-// items.  A D item stages h in the region the selection scratch used.
+// and requests its share of the shared expert's gate/up rows (none of which
+// needs the routing), then selects the token's experts itself, finishes the
+// shared rows and takes tickets: GR items (with a full grid, exactly one
+// per workgroup), then D items.  A D item stages h in the region the
+// selection scratch used.
 template <int BITS, int GLPR, int GCPL, int DLPR, int DCPL>
 __global__ __launch_bounds__(kDecThreads)
 __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(DecodeArgs d) {
@@ -624,12 +645,12 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
   }
   __syncthreads();
   trace_rec(d, trn, kTrXq, 0);
-  {
-    const int r0 = (int)blockIdx.x * d.sh_rows;
-    const int nr = min(d.sh_rows, I - r0);
-    if (nr > 0) shared_rows<BITS, GLPR, GCPL>(d, r0, nr, xq_lds, xd_lds, &s_ticket);
-  }
-  trace_rec(d, trn, kTrShDone, 0);
+  // this workgroup's rows of the shared expert stream while the scores are
+  // polled and the experts selected
+  const int sh_r0 = (int)blockIdx.x * d.sh_rows;
+  const int sh_nr = max(0, min(d.sh_rows, I - sh_r0));
+  SharedRows<BITS, GLPR, GCPL> shr;
+  shr.issue(d, sh_r0, sh_nr);
   trace_rec(d, trn, kTrSelBegin, 0);
   {
     ScorePoll sp;
@@ -639,7 +660,12 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
   trace_rec(d, trn, kTrPollDone, 0);
   select_local(d, in, dyn + sizeof(SelInput), sidx, sw);
   trace_rec(d, trn, kTrSelEnd, 0);
+  shr.finish(d, sh_r0, sh_nr, xq_lds, xd_lds);
+  trace_rec(d, trn, kTrShDone, 0);
 
+  // the shared rows are counted once their stores have completed: with the
+  // first gate/up item's counter, else on their own before the D items
+  bool sh_counted = sh_nr == 0;
   int t = (int)blockIdx.x;
   // GR: routed slot u, rows [kGuRows rb, +kGuRows)
   for (; t < b_d; t = next_ticket()) {
@@ -658,9 +684,19 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
       gateup_body<BITS, GLPR, GCPL, 1, kDecWaves, true, BLK, kGuPipe>(a, false, expert_ptrs(a.L, e), s,
                                                                      BLK * rb, hs, xq_lds, xd_lds);
     }
-    publish(d.ctr + kCtrSlot0 + u * kCtrStride, 1u);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __hip_atomic_fetch_add(d.ctr + kCtrSlot0 + u * kCtrStride, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      if (!sh_counted)
+        __hip_atomic_fetch_add(d.ctr + kCtrSlot0 + k * kCtrStride, (uint32_t)sh_nr,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    sh_counted = true;
     trace_rec(d, trn, kTrGrEnd, t);
   }
+  if (!sh_counted) publish(d.ctr + kCtrSlot0 + k * kCtrStride, (uint32_t)sh_nr);
   // D: output rows of D item t - b_d; the staged h overlays the selection
   // scratch, which is no longer needed by then
   int8_t *lds_q = reinterpret_cast<int8_t *>(dyn);
@@ -688,8 +724,6 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
     for (int sl = threadIdx.x; sl < d.n_slice; sl += kDecThreads)
       __hip_atomic_store(reinterpret_cast<uint64_t *>(d.ctr + kScoreWords) + sl, (uint64_t)0,
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int b = threadIdx.x; b < I / 32; b += kDecThreads)
-      __hip_atomic_store(d.ctr + kCtrShBlk + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
