@@ -535,8 +535,6 @@ coli_status forward_impl(const coli_moe_layer *L, const CacheRun *cache, const f
     int32_t *perm = reinterpret_cast<int32_t *>(base + ws.perm);
     int32_t *uniq = reinterpret_cast<int32_t *>(base + ws.uniq);
     int32_t *nuniq = reinterpret_cast<int32_t *>(base + ws.nuniq);
-    e = coli::launch_dispatch(idx, T, k, E, counts, offs, perm, uniq, nuniq, s);
-    if (e != hipSuccess) return COLI_ERR_DEVICE;
     int32_t *mgofs = reinterpret_cast<int32_t *>(base + ws.mgofs);
     fa.disp = coli::Dispatch{counts, offs, perm, uniq, nuniq, mgofs};
     fa.mfma_min = mfma_min > 0 ? mfma_min : T >= coli::kMfmaAllTokens ? 1 : coli::kMfmaMinDefault;
@@ -546,8 +544,11 @@ coli_status forward_impl(const coli_moe_layer *L, const CacheRun *cache, const f
     // every slot on the matrix cores: the dot-product kernels would only
     // launch workgroups that find nothing to do
     const bool dot = !(mfma && fa.mfma_min <= 1 && T >= fa.mfma_min_shared);
-    if (mfma) e = coli::launch_mfma_items(fa, mgofs, s);
-    if (e == hipSuccess && dot) e = coli::launch_gateup(fa, true, mfma_min, s, kev(1));
+    // the union tables, and the matrix-core item tables in the same launch
+    e = coli::launch_dispatch(idx, T, k, E, counts, offs, perm, uniq, nuniq, s,
+                              mfma ? mgofs : nullptr, fa.mfma_min, fa.mfma_min_shared);
+    if (e != hipSuccess) return COLI_ERR_DEVICE;
+    if (dot) e = coli::launch_gateup(fa, true, mfma_min, s, kev(1));
     if (e == hipSuccess && mfma) e = coli::launch_gateup_mfma(fa, s, kev(3));
     if (e == hipSuccess && dot) e = coli::launch_down(fa, true, mfma_min, s, kev(2));
     if (e == hipSuccess && mfma) e = coli::launch_down_mfma(fa, s, kev(4));

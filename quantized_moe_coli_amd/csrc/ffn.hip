@@ -233,21 +233,40 @@ __global__ __launch_bounds__(256) void k_down_union(FfnArgs a, int n_items) {
 }
 
 // y[t][r] = o_shared + sum over kept slots j (in order) of w_tj * o_tj.
+// The rows of 8 slots at a time are requested before any is added (every
+// slot's row exists in obuf; a dropped slot's is read and not used).
 __global__ __launch_bounds__(256) void k_combine(FfnArgs a) {
+  constexpr int kGroup = 8;
   const int H = a.L.H, k = a.k;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
   if (i >= (int64_t)a.T * (H / 4)) return;
   const int t = (int)(i / (H / 4)), r4 = (int)(i % (H / 4));
   const float4 *ob = reinterpret_cast<const float4 *>(a.obuf + (size_t)t * (k + 1) * H);
+  const int32_t *ti = a.idx + (size_t)t * k;
+  const float *tw = a.w + (size_t)t * k;
   float4 y = ob[(size_t)k * (H / 4) + r4];
-  for (int j = 0; j < k; ++j) {
-    if (a.idx[(size_t)t * k + j] < 0) continue;
-    const float w = a.w[(size_t)t * k + j];
-    const float4 o = ob[(size_t)j * (H / 4) + r4];
-    y.x += w * o.x;
-    y.y += w * o.y;
-    y.z += w * o.z;
-    y.w += w * o.w;
+  for (int j0 = 0; j0 < k; j0 += kGroup) {
+    float4 o[kGroup];
+    int id[kGroup];
+    float wj[kGroup];
+#pragma unroll
+    for (int jj = 0; jj < kGroup; ++jj) {
+      const int j = j0 + jj;
+      if (j < k) {
+        id[jj] = ti[j];
+        wj[jj] = tw[j];
+        o[jj] = ob[(size_t)j * (H / 4) + r4];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < kGroup; ++jj) {
+      if (j0 + jj >= k || id[jj] < 0) continue;
+      const float w = wj[jj];
+      y.x += w * o[jj].x;
+      y.y += w * o[jj].y;
+      y.z += w * o[jj].z;
+      y.w += w * o[jj].w;
+    }
   }
   reinterpret_cast<float4 *>(a.y + (size_t)t * H)[r4] = y;
 }

@@ -105,6 +105,12 @@ hipError_t launch_quant_pack_fp8(int bits, const uint8_t *w8, const float *bscal
                                  int64_t cols, uint8_t *q, float *scale, hipStream_t st);
 hipError_t launch_gemv_f32act(int bits, const uint8_t *W, const float *scale, int64_t rows,
                               int64_t cols, const float *x, float *y, hipStream_t st);
+constexpr int kMfmaGroup = 64;  // tokens per group in the matrix-core item table
+// Token groups of `tok` tokens a union slot sends to the matrix cores (0:
+// the dot-product path takes it).
+__host__ __device__ inline int mfma_groups(int n_tok, int mfma_min, int tok) {
+  return n_tok >= mfma_min ? (n_tok + tok - 1) / tok : 0;
+}
 // Bound of the matrix-core token groups of one batch (32-token groups: the
 // routed pairs, one partial group per unique expert, the shared expert's).
 __host__ __device__ inline int mfma_gmax(int T, int k, int E) {
@@ -127,8 +133,13 @@ hipError_t launch_front(int bits, const float *x, const float *gate_w, const flo
                         KEvents ev = {}, double *xd64 = nullptr);
 hipError_t launch_route(const RouterCfg &cfg, const float *logits, const float *bias, int T,
                         int32_t *idx, float *w, int32_t *idx_copy, float *w_copy, hipStream_t st);
+// Union tables (counts, offs, perm, uniq, n_uniq) from idx [T][k].  With
+// mgofs, the same launch also writes the matrix-core item tables of the
+// batch (layout at Dispatch::mgofs) for the slots with at least mfma_min
+// tokens (the shared expert: mfma_min_shared).
 hipError_t launch_dispatch(const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offs,
-                           int32_t *perm, int32_t *uniq, int32_t *n_uniq, hipStream_t st);
+                           int32_t *perm, int32_t *uniq, int32_t *n_uniq, hipStream_t st,
+                           int32_t *mgofs = nullptr, int mfma_min = 0, int mfma_min_shared = 0);
 
 // Expert FFN stages.  Slot lists: decode mode (T == 1) runs the k routed
 // slots of token 0 (idx[0..k-1], -1 skipped) plus the shared expert as slot
@@ -177,9 +188,8 @@ hipError_t launch_down(const FfnArgs &a, bool union_mode, int mfma_min, hipStrea
 hipError_t launch_combine(const FfnArgs &a, hipStream_t st);
 
 // Union slots with at least a.mfma_min tokens run on the int8 matrix cores
-// (mfma.hip): the item table after the dispatch tables, then gate/up and
-// down; the dot-product kernels skip those slots.
-hipError_t launch_mfma_items(const FfnArgs &a, int32_t *mgofs, hipStream_t st);
+// (mfma.hip), from the item tables launch_dispatch writes; the dot-product
+// kernels skip those slots.
 hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t st, KEvents ev = {});
 hipError_t launch_down_mfma(const FfnArgs &a, hipStream_t st, KEvents ev = {});
 

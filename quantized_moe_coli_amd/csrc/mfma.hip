@@ -8,8 +8,8 @@
 // expert is read once for all of its tokens.  With many tokens per expert
 // the dot-product GEMV (ffn.hip) turns ALU-bound; here the products run on
 // v_mfma_i32_16x16x32_i8, whose K = 32 is exactly one Q8_0 block, so every
-// MFMA result is one block's exact int32 sum, scaled in fp32 by the token's
-// block scale before it is accumulated.
+// MFMA result is one block's exact int32 sum, scaled by the token's block
+// scale before it is accumulated (binary64 for gate/up, binary32 for down).
 //
 // Operands (16 x 16 x 32): lane l holds 8 int8 values of row l % 16 of A
 // and of column l % 16 of B, at k = 8 (l / 16) .. 8 (l / 16) + 7; the
@@ -22,8 +22,8 @@
 //
 // Work items: a (union slot, token group of 64, 128-row block) each; the
 // item table (prefix of token groups over the slots that run here) is built
-// on the device after the dispatch tables, so the grid is a host-side upper
-// bound and surplus workgroups exit at once.
+// on the device with the dispatch tables (k_dispatch), so the grid is a
+// host-side upper bound and surplus workgroups exit at once.
 #include <type_traits>
 
 #include "ffn_common.hpp"
@@ -33,7 +33,6 @@ namespace coli {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaGroup = 64;   // tokens per group in the item table
 constexpr int kMfmaRows = 128;   // weight rows per workgroup (16 per wave)
 constexpr int kMfmaThreads = 512;  // threads per workgroup (8 waves)
 constexpr int kMfmaWaves = kMfmaThreads / 64;
@@ -50,67 +49,6 @@ struct MfmaCfg {
   static constexpr int ROWB = 128 / WG;                   // weight bytes per row per stage (at most)
   static constexpr int RING = 160 * 1024 / WG - 1024;     // LDS for the stage ring
 };
-
-// Token groups of `tok` tokens a union slot sends to the matrix cores (0:
-// the dot-product path takes it).
-__device__ __forceinline__ int mfma_groups(int n_tok, int mfma_min, int tok) {
-  return n_tok >= mfma_min ? (n_tok + tok - 1) / tok : 0;
-}
-
-// Two item tables, one per token-group size: mgofs[u] = first 64-token
-// group of union slot u (slots 0 .. n_uniq-1 are the unique routed experts,
-// slot n_uniq the shared expert), mgofs[n_uniq + 1] the total; the same for
-// 32-token groups from mgofs + E + 2.  Then, from mgofs + 2 (E + 2), the
-// slot of each 64-token group, and mfma_gmax entries on, of each 32-token
-// group.  One workgroup; slots <= 1025; both counts scanned at once as the
-// halves of one 64-bit word.
-__global__ __launch_bounds__(1024) void k_mfma_items(FfnArgs a, int32_t *__restrict__ mgofs) {
-  __shared__ uint64_t sc[2][1024];
-  const int tid = threadIdx.x;
-  const int nu = *a.disp.n_uniq;
-  const int slots = nu + 1;
-  auto groups = [&](int u) -> uint64_t {
-    const int n = u < nu ? a.disp.counts[a.disp.uniq[u]] : a.T;
-    const int mn = u < nu ? a.mfma_min : a.mfma_min_shared;
-    return (uint64_t)mfma_groups(n, mn, kMfmaGroup) | ((uint64_t)mfma_groups(n, mn, kMfmaGroup / 2) << 32);
-  };
-  // thread i sums slots 2i, 2i+1
-  const uint64_t g0 = 2 * tid < slots ? groups(2 * tid) : 0;
-  const uint64_t g1 = 2 * tid + 1 < slots ? groups(2 * tid + 1) : 0;
-  int cur = 0;
-  sc[0][tid] = g0 + g1;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const uint64_t v = sc[cur][tid] + (tid >= d ? sc[cur][tid - d] : 0);
-    sc[cur ^ 1][tid] = v;
-    cur ^= 1;
-    __syncthreads();
-  }
-  const uint64_t incl = sc[cur][tid];  // inclusive prefix of the pair sums
-  const uint64_t excl = incl - (g0 + g1);
-  int32_t *m32 = mgofs + a.E + 2;
-  if (2 * tid < slots) {
-    mgofs[2 * tid] = (int32_t)(uint32_t)excl;
-    m32[2 * tid] = (int32_t)(excl >> 32);
-  }
-  if (2 * tid + 1 < slots) {
-    mgofs[2 * tid + 1] = (int32_t)(uint32_t)(excl + g0);
-    m32[2 * tid + 1] = (int32_t)((excl + g0) >> 32);
-  }
-  if (tid == 1023) {  // totals (slots <= 2048)
-    mgofs[slots] = (int32_t)(uint32_t)incl;
-    m32[slots] = (int32_t)(incl >> 32);
-  }
-  // group -> slot
-  int32_t *s64 = mgofs + 2 * (a.E + 2), *s32 = s64 + mfma_gmax(a.T, a.k, a.E);
-  const uint32_t e64 = (uint32_t)excl, e32 = (uint32_t)(excl >> 32);
-  const uint32_t a64 = (uint32_t)g0, a32 = (uint32_t)(g0 >> 32);
-  const uint32_t b64 = (uint32_t)g1, b32 = (uint32_t)(g1 >> 32);
-  for (uint32_t j = 0; j < a64; ++j) s64[e64 + j] = 2 * tid;
-  for (uint32_t j = 0; j < b64; ++j) s64[e64 + a64 + j] = 2 * tid + 1;
-  for (uint32_t j = 0; j < a32; ++j) s32[e32 + j] = 2 * tid;
-  for (uint32_t j = 0; j < b32; ++j) s32[e32 + a32 + j] = 2 * tid + 1;
-}
 
 // A operand, in two steps so a block's raw loads can all be issued before
 // any is used: wraw loads the packed bytes of k-group g of block b of a
@@ -741,10 +679,6 @@ static dim3 mfma_grid(const FfnArgs &a, int n_rb) {
   return dim3((unsigned)(mfma_group_bound(a, MfmaCfg<WG>::TOK) * n_rb));
 }
 
-hipError_t launch_mfma_items(const FfnArgs &a, int32_t *mgofs, hipStream_t st) {
-  hipLaunchKernelGGL(k_mfma_items, dim3(1), dim3(1024), 0, st, a, mgofs);
-  return hipGetLastError();
-}
 
 hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t st, KEvents ev) {
   const dim3 grid = mfma_grid<kGateupWg>(a, (a.L.I + kMfmaRows - 1) / kMfmaRows), block(kMfmaThreads);

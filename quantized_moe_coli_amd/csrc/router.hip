@@ -12,6 +12,8 @@
 // order as the definition (no contraction), so indices and weights are
 // reproducible bit for bit; the sigmoid is evaluated in binary64 and rounded
 // once.
+#include <algorithm>
+
 #include "actq.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
@@ -227,122 +229,286 @@ __global__ __launch_bounds__(256) void k_route(RouterCfg cfg, const float *__res
   }
 }
 
+// One workgroup per token: the scores in LDS (one expert per thread), then
+// the workgroup-parallel selection (select_fast: the same order and binary32
+// operations as select_token, so the same experts and weights), for layers
+// whose expert count and groups it covers.  Shorter per token than one wave
+// running the k rounds of arg-max.
+constexpr int kRouteWgThreads = 256;
+__global__ __launch_bounds__(kRouteWgThreads) void k_route_wg(RouterCfg cfg,
+                                                              const float *__restrict__ logits,
+                                                              const float *__restrict__ bias,
+                                                              int32_t *__restrict__ idx,
+                                                              float *__restrict__ wout,
+                                                              int32_t *__restrict__ idx2,
+                                                              float *__restrict__ w2) {
+  __shared__ SelInput in;
+  __shared__ SelFastScratch sc;
+  __shared__ int32_t sidx[kSelMaxK];
+  __shared__ float sw[kSelMaxK];
+  const int t = blockIdx.x, e = threadIdx.x, k = cfg.k;
+  if (e < cfg.E) {
+    const float l = logits[(size_t)t * cfg.E + e];
+    const float bv = bias ? bias[e] : 0.f;
+    const float sg = sigmoid_f64(l);
+    in.sg[e] = sg;
+    in.c[e] = sg + bv;
+  }
+  __syncthreads();
+  select_fast<kRouteWgThreads>(cfg, in, sc, sidx, sw);
+  if (e < k) {
+    const int32_t i = (unsigned)sidx[e] < (unsigned)cfg.E ? sidx[e] : -1;
+    idx[(size_t)t * k + e] = i;
+    wout[(size_t)t * k + e] = sw[e];
+    if (idx2) idx2[(size_t)t * k + e] = i;
+    if (w2) w2[(size_t)t * k + e] = sw[e];
+  }
+}
+
 hipError_t launch_route(const RouterCfg &cfg, const float *logits, const float *bias, int T,
                         int32_t *idx, float *w, int32_t *idx_copy, float *w_copy, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, st, cfg, logits, bias, T, idx, w,
-                     idx_copy, w_copy);
+  if (select_fast_ok(cfg.E, cfg.n_group, cfg.topk_group, cfg.k, kRouteWgThreads))
+    hipLaunchKernelGGL(k_route_wg, dim3(T), dim3(kRouteWgThreads), 0, st, cfg, logits, bias, idx, w,
+                       idx_copy, w_copy);
+  else
+    hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, st, cfg, logits, bias, T, idx, w,
+                       idx_copy, w_copy);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Union tables: one workgroup.  counts by LDS atomics (order-free), an
-// exclusive scan, then a stable placement: entries are taken in chunks of
-// 32*W consecutive (token, slot) pairs; each expert gets a W-word bitmask of
-// its entries in the chunk, and an entry's position is the expert's running
-// base + the popcount of its earlier bits.  Deterministic, and ordered by
-// (expert, token, slot) even if a token repeats an expert.
+// Union tables: one workgroup of 1024 threads.  Counts by LDS atomics
+// (order-free); one scan of (count, nonzero) pairs gives offs, uniq and
+// n_uniq.  Placement is a stable counting sort in rounds of up to 64 * C
+// pairs: wave w takes chunks w, w + 16, ... of 64 consecutive pairs; in each
+// chunk a pair's rank among the chunk's pairs of its expert comes from the
+// lanes holding the same expert id (one ballot per bit of the id), and the
+// expert's first lane writes the chunk's count of it into an LDS matrix
+// [C][E].  A scan of each expert's column over the chunks then gives every
+// chunk's first position for the expert, so pair i of expert e goes to
+// base[e] + column prefix + rank.  Ordered by (expert, token, slot) even if
+// a token repeats an expert; deterministic.
+//
+// With mgofs, the matrix-core item tables too, one per token-group size:
+// mgofs[u] = first 64-token group of union slot u (slots 0 .. n_uniq-1 are
+// the unique routed experts, slot n_uniq the shared expert), mgofs[n_uniq +
+// 1] the total; the same for 32-token groups from mgofs + E + 2.  Then, from
+// mgofs + 2 (E + 2), the slot of each 64-token group, and mfma_gmax entries
+// on, of each 32-token group.  Both group counts are scanned at once as the
+// halves of one 64-bit word.
 // ---------------------------------------------------------------------------
 constexpr int kDispThreads = 1024;
-constexpr int kDispWords = 4096;  // E * W <= this
+constexpr int kDispWaves = kDispThreads / 64;
+constexpr int kDispCells = 16384;    // chunk x expert count matrix in LDS (64 KB)
+constexpr int kDispMaxChunks = 256;  // chunks per round (16 per wave)
 
+__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
+  const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, d, 64);
+  const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), d, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// C chunks per round (a multiple of 16 and of P), P threads per expert
+// column in the column scan (a power of two dividing 64).
 __global__ __launch_bounds__(kDispThreads) void k_dispatch(const int32_t *__restrict__ idx, int T,
-                                                           int k, int E, int W,
+                                                           int k, int E, int C, int P,
                                                            int32_t *__restrict__ counts,
                                                            int32_t *__restrict__ offs,
                                                            int32_t *__restrict__ perm,
                                                            int32_t *__restrict__ uniq,
-                                                           int32_t *__restrict__ n_uniq) {
+                                                           int32_t *__restrict__ n_uniq,
+                                                           int32_t *__restrict__ mgofs,
+                                                           int mfma_min, int mfma_min_shared) {
+  __shared__ int cm[kDispCells];
   __shared__ int cnt[kSelMaxE];
-  __shared__ int scan_a[kSelMaxE];
-  __shared__ int scan_b[kSelMaxE];
   __shared__ int base[kSelMaxE];
-  __shared__ uint32_t mask[kDispWords];
-  __shared__ int pref[kDispWords];
-  const int tid = threadIdx.x;
+  __shared__ int ucnt[kSelMaxE];  // count of the u-th unique expert
+  __shared__ uint64_t wtot[kDispWaves];
+  __shared__ int s_nu;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n = (int64_t)T * k;
 
+  constexpr int kJ = kDispMaxChunks / kDispWaves;
+  // this thread's pairs of the round starting at r0 (chunk wave + 16 j,
+  // lane): the expert ids, E for none; every load issued before any use
+  int ky[kJ];
+  auto load_keys = [&](int64_t r0) {
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int c = wave + kDispWaves * j;
+      const int64_t i = r0 + 64 * c + lane;
+      const int e = (c < C && i < n) ? idx[i] : -1;
+      ky[j] = (e >= 0 && e < E) ? e : E;
+    }
+  };
+  // a single round: the keys are loaded once and counted from registers
+  const bool one_round = n <= (int64_t)64 * C;
+  if (one_round) load_keys(0);
   for (int e = tid; e < E; e += kDispThreads) cnt[e] = 0;
   __syncthreads();
-  for (int64_t i = tid; i < n; i += kDispThreads) {
-    const int e = idx[i];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  if (one_round) {
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+      if (ky[j] < E) atomicAdd(&cnt[ky[j]], 1);
+  } else {
+    for (int64_t i0 = tid; i0 < n; i0 += 4 * kDispThreads) {
+      int ev[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t i = i0 + (int64_t)u * kDispThreads;
+        ev[u] = i < n ? idx[i] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (ev[u] >= 0 && ev[u] < E) atomicAdd(&cnt[ev[u]], 1);
+    }
   }
   __syncthreads();
 
-  // inclusive scans (Hillis-Steele) of counts and of nonzero flags
-  for (int e = tid; e < E; e += kDispThreads) {
-    scan_a[e] = cnt[e];
-    scan_b[e] = cnt[e] > 0 ? 1 : 0;
+  // inclusive scan over the experts (thread e holds expert e) of the count
+  // and the nonzero flag, as the halves of one 64-bit word
+  const int c0 = tid < E ? cnt[tid] : 0;
+  const uint64_t v = (uint64_t)(uint32_t)c0 | ((uint64_t)(c0 > 0 ? 1 : 0) << 32);
+  uint64_t inc = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t o = shfl_up_u64(inc, d);
+    if (lane >= d) inc += o;
   }
+  if (lane == 63) wtot[wave] = inc;
   __syncthreads();
-  for (int d = 1; d < E; d <<= 1) {
-    int va[(kSelMaxE + kDispThreads - 1) / kDispThreads], vb[(kSelMaxE + kDispThreads - 1) / kDispThreads];
-    int q = 0;
-    for (int e = tid; e < E; e += kDispThreads, ++q) {
-      va[q] = scan_a[e] + (e >= d ? scan_a[e - d] : 0);
-      vb[q] = scan_b[e] + (e >= d ? scan_b[e - d] : 0);
+  for (int w = 0; w < wave; ++w) inc += wtot[w];
+  const uint64_t exc = inc - v;
+  if (tid < E) {
+    counts[tid] = c0;
+    offs[tid] = (int32_t)(uint32_t)exc;
+    base[tid] = (int)(uint32_t)exc;
+    if (c0 > 0) {
+      uniq[(int)(exc >> 32)] = tid;
+      ucnt[(int)(exc >> 32)] = c0;
     }
-    __syncthreads();
-    q = 0;
-    for (int e = tid; e < E; e += kDispThreads, ++q) {
-      scan_a[e] = va[q];
-      scan_b[e] = vb[q];
-    }
-    __syncthreads();
   }
-  for (int e = tid; e < E; e += kDispThreads) {
-    const int excl = scan_a[e] - cnt[e];
-    counts[e] = cnt[e];
-    offs[e] = excl;
-    base[e] = excl;
-    if (cnt[e] > 0) uniq[scan_b[e] - 1] = e;
-  }
-  if (tid == 0) {
-    offs[E] = scan_a[E - 1];
-    n_uniq[0] = scan_b[E - 1];
+  if (tid == kDispThreads - 1) {
+    offs[E] = (int32_t)(uint32_t)inc;
+    n_uniq[0] = (int32_t)(inc >> 32);
+    s_nu = (int)(inc >> 32);
   }
   __syncthreads();
 
-  const int chunk = 32 * W;
-  for (int64_t c0 = 0; c0 < n; c0 += chunk) {
-    for (int m = tid; m < E * W; m += kDispThreads) mask[m] = 0u;
-    __syncthreads();
-    for (int i = tid; i < chunk && c0 + i < n; i += kDispThreads) {
-      const int e = idx[c0 + i];
-      if (e >= 0 && e < E) atomicOr(&mask[e * W + (i >> 5)], 1u << (i & 31));
+  if (mgofs) {
+    // thread i: union slots 2i, 2i + 1 (at most 1025 slots)
+    const int nu = s_nu, slots = nu + 1;
+    auto groups = [&](int u) -> uint64_t {
+      const int nt = u < nu ? ucnt[u] : T;
+      const int mn = u < nu ? mfma_min : mfma_min_shared;
+      return (uint64_t)mfma_groups(nt, mn, kMfmaGroup) |
+             ((uint64_t)mfma_groups(nt, mn, kMfmaGroup / 2) << 32);
+    };
+    const uint64_t g0 = 2 * tid < slots ? groups(2 * tid) : 0;
+    const uint64_t g1 = 2 * tid + 1 < slots ? groups(2 * tid + 1) : 0;
+    uint64_t gi = g0 + g1;
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint64_t o = shfl_up_u64(gi, d);
+      if (lane >= d) gi += o;
     }
+    if (lane == 63) wtot[wave] = gi;
     __syncthreads();
-    for (int e = tid; e < E; e += kDispThreads) {
-      int run = 0;
-      for (int w = 0; w < W; ++w) {
-        pref[e * W + w] = run;
-        run += __popc(mask[e * W + w]);
+    for (int w = 0; w < wave; ++w) gi += wtot[w];
+    const uint64_t ge = gi - (g0 + g1);
+    int32_t *m32 = mgofs + E + 2;
+    if (2 * tid < slots) {
+      mgofs[2 * tid] = (int32_t)(uint32_t)ge;
+      m32[2 * tid] = (int32_t)(ge >> 32);
+    }
+    if (2 * tid + 1 < slots) {
+      mgofs[2 * tid + 1] = (int32_t)(uint32_t)(ge + g0);
+      m32[2 * tid + 1] = (int32_t)((ge + g0) >> 32);
+    }
+    if (tid == kDispThreads - 1) {  // totals
+      mgofs[slots] = (int32_t)(uint32_t)gi;
+      m32[slots] = (int32_t)(gi >> 32);
+    }
+    // group -> slot
+    int32_t *s64 = mgofs + 2 * (E + 2), *s32 = s64 + mfma_gmax(T, k, E);
+    const uint32_t e64 = (uint32_t)ge, e32 = (uint32_t)(ge >> 32);
+    const uint32_t a64 = (uint32_t)g0, a32 = (uint32_t)(g0 >> 32);
+    const uint32_t b64 = (uint32_t)g1, b32 = (uint32_t)(g1 >> 32);
+    for (uint32_t j = 0; j < a64; ++j) s64[e64 + j] = 2 * tid;
+    for (uint32_t j = 0; j < b64; ++j) s64[e64 + a64 + j] = 2 * tid + 1;
+    for (uint32_t j = 0; j < a32; ++j) s32[e32 + j] = 2 * tid;
+    for (uint32_t j = 0; j < b32; ++j) s32[e32 + a32 + j] = 2 * tid + 1;
+  }
+
+  const int nb = 32 - __clz(E);  // bits of the ids 0 .. E (E: no expert)
+  const int rows = C / P;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int64_t r0 = 0; r0 < n; r0 += (int64_t)64 * C) {
+    if (!one_round) load_keys(r0);
+    for (int m = tid; m < C * E; m += kDispThreads) cm[m] = 0;
+    __syncthreads();
+    int rk[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int c = wave + kDispWaves * j;
+      rk[j] = 0;
+      if (c < C) {  // uniform: every lane of the wave
+        const int key = ky[j];
+        uint64_t same = ~0ull;
+        for (int b = 0; b < nb; ++b) {
+          const bool bit = (key >> b) & 1;
+          const uint64_t bal = __ballot(bit);
+          same &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(same & below);
+        if (key < E && rank == 0) cm[c * E + key] = __popcll(same);
+        rk[j] = rank;
       }
     }
     __syncthreads();
-    for (int i = tid; i < chunk && c0 + i < n; i += kDispThreads) {
-      const int e = idx[c0 + i];
-      if (e >= 0 && e < E) {
-        const int w = i >> 5;
-        const uint32_t below = mask[e * W + w] & ((1u << (i & 31)) - 1u);
-        perm[base[e] + pref[e * W + w] + __popc(below)] = (int32_t)(c0 + i);
+    // each expert's column: P consecutive lanes of one wave, rows apiece,
+    // turned into first positions: base + exclusive prefix over the chunks
+    if (tid < E * P) {
+      const int e = tid / P, p = tid % P;
+      int s = 0;
+      for (int c = p * rows; c < (p + 1) * rows; ++c) {
+        const int x = cm[c * E + e];
+        cm[c * E + e] = s;
+        s += x;
       }
+      int ip = s;
+      for (int d = 1; d < P; d <<= 1) {
+        const int o = __shfl_up(ip, d, 64);
+        if (p >= d) ip += o;
+      }
+      const int add = base[e] + ip - s;
+      for (int c = p * rows; c < (p + 1) * rows; ++c) cm[c * E + e] += add;
+      // the column's lanes are one wave's, whose reads of base[e] above
+      // precede this write
+      if (p == P - 1) base[e] += ip;
     }
     __syncthreads();
-    for (int e = tid; e < E; e += kDispThreads)
-      base[e] += pref[e * W + W - 1] + __popc(mask[e * W + W - 1]);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int c = wave + kDispWaves * j;
+      if (c < C && ky[j] < E) {
+        const int64_t i = r0 + 64 * c + lane;
+        perm[cm[c * E + ky[j]] + rk[j]] = (int32_t)i;
+      }
+    }
     __syncthreads();
   }
 }
 
 hipError_t launch_dispatch(const int32_t *idx, int T, int k, int E, int32_t *counts, int32_t *offs,
-                           int32_t *perm, int32_t *uniq, int32_t *n_uniq, hipStream_t st) {
-  int W = kDispWords / E;
-  if (W > 32) W = 32;
-  if (W < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(kDispThreads), 0, st, idx, T, k, E, W, counts, offs,
-                     perm, uniq, n_uniq);
+                           int32_t *perm, int32_t *uniq, int32_t *n_uniq, hipStream_t st,
+                           int32_t *mgofs, int mfma_min, int mfma_min_shared) {
+  if (E < 1 || E > kSelMaxE) return hipErrorInvalidValue;
+  int P = 1;
+  while (P * 2 <= 64 && P * 2 * E <= kDispThreads) P *= 2;
+  int C = std::min(kDispMaxChunks, kDispCells / E / 16 * 16);
+  if (C < 16 || C % P) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(kDispThreads), 0, st, idx, T, k, E, C, P, counts,
+                     offs, perm, uniq, n_uniq, mgofs, mfma_min, mfma_min_shared);
   return hipGetLastError();
 }
 

@@ -91,17 +91,18 @@ __device__ __forceinline__ void select_core(const RouterCfg &cfg, const float *c
                                             int32_t *idx_out, float *w_out);
 
 // Selects a token's experts.  Lane j < k writes slot j of `idx_out`/`w_out`
-// (any address space).
-__device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *__restrict__ lrow,
-                                             const float *__restrict__ bias, SelScratch &sc,
-                                             int32_t *idx_out, float *w_out) {
+// (any address space).  EPL >= (E + 63) / 64 candidates per lane.
+template <int EPL>
+__device__ __forceinline__ void select_token_t(const RouterCfg &cfg, const float *__restrict__ lrow,
+                                               const float *__restrict__ bias, SelScratch &sc,
+                                               int32_t *idx_out, float *w_out) {
   const int lane = threadIdx.x & 63;
   const int E = cfg.E;
   const int epl = (E + 63) / 64;  // candidates per lane (uniform)
-  float c[kSelEPL], lv[kSelEPL], bv[kSelEPL];
+  float c[EPL], lv[EPL], bv[EPL];
   // all loads first (clamped addresses), so they are in flight together
 #pragma unroll
-  for (int m = 0; m < kSelEPL; ++m) {
+  for (int m = 0; m < EPL; ++m) {
     if (m < epl) {
       const int ec = min(lane + 64 * m, E - 1);
       lv[m] = lrow[ec];
@@ -109,7 +110,7 @@ __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *
     }
   }
 #pragma unroll
-  for (int m = 0; m < kSelEPL; ++m) {
+  for (int m = 0; m < EPL; ++m) {
     const int e = lane + 64 * m;
     c[m] = 0.f;
     if (m < epl) {
@@ -121,7 +122,17 @@ __device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *
 
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  select_core(cfg, c, sc.sig, sc, idx_out, w_out);
+  select_core<EPL>(cfg, c, sc.sig, sc, idx_out, w_out);
+}
+
+// The instance with as few candidates per lane as the expert count allows
+// (the same selection: lanes' candidates past E are never eligible).
+__device__ __forceinline__ void select_token(const RouterCfg &cfg, const float *__restrict__ lrow,
+                                             const float *__restrict__ bias, SelScratch &sc,
+                                             int32_t *idx_out, float *w_out) {
+  if (cfg.E <= 64) select_token_t<1>(cfg, lrow, bias, sc, idx_out, w_out);
+  else if (cfg.E <= 256) select_token_t<4>(cfg, lrow, bias, sc, idx_out, w_out);
+  else select_token_t<kSelEPL>(cfg, lrow, bias, sc, idx_out, w_out);
 }
 
 // The selection itself from the biased scores c[m] of experts lane + 64 m

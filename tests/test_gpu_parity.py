@@ -262,7 +262,9 @@ def test_route_bit_exact(orc, name, T, rho):
 
 @pytest.mark.parametrize("T,k,E,drop,dup", [(1, 8, 256, 0.0, False), (3, 8, 256, 0.0, False),
                                             (512, 8, 256, 0.0, False), (77, 4, 16, 0.3, False),
-                                            (300, 8, 1024, 0.1, True), (2, 32, 64, 0.0, False)])
+                                            (300, 8, 1024, 0.1, True), (2, 32, 64, 0.0, False),
+                                            (600, 8, 256, 0.05, True), (50, 6, 100, 0.2, True),
+                                            (4096, 8, 256, 0.0, False)])
 def test_dispatch_tables_bit_exact(orc, T, k, E, drop, dup):
     rng = np.random.default_rng(T * 31 + E)
     idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
