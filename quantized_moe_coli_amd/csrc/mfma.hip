@@ -214,11 +214,13 @@ struct ScaleGeo {
   }
 };
 
-template <int BITS, int NMAT, int WG, typename SC>
+// A stage of the ring for TS staged tokens (the item's token tiles; fewer
+// tokens leave room for more stages in flight).
+template <int BITS, int NMAT, int WG, typename SC, int TS = MfmaCfg<WG>::TOK>
 struct MfmaStage {
   using G = MfmaGeo<BITS, WG>;
   using SG = ScaleGeo<G::CH, SC>;
-  static constexpr int TOK = MfmaCfg<WG>::TOK;
+  static constexpr int TOK = TS;
   static constexpr int W = NMAT * kMfmaRows * G::RB;   // weight bytes
   static constexpr int X = TOK * G::XR;                // code bytes
   static constexpr int D = TOK * G::CH * (int)sizeof(SC);  // scale bytes
@@ -239,10 +241,29 @@ struct MfmaStage {
   static_assert(DPW <= 64 && DPW * kMfmaWaves * SG::PB == D, "one scale instruction per wave");
 };
 
+// Whether a stage of TS tokens splits into whole load instructions per wave.
+template <int BITS, int NMAT, int WG, typename SC, int TS>
+constexpr bool stage_fits() {
+  using G = MfmaGeo<BITS, WG>;
+  constexpr int PX = TS * G::XR / 16;
+  constexpr int NX = PX >= kMfmaThreads ? PX / kMfmaThreads : 1;
+  constexpr int XPW = PX >= kMfmaThreads ? 64 : PX / kMfmaWaves;
+  constexpr int D = TS * G::CH * (int)sizeof(SC);
+  constexpr int PB = sizeof(SC) == 8 ? 16 : 4;
+  constexpr int DPW = D / PB / kMfmaWaves;
+  return NX * kMfmaWaves * XPW == PX && XPW >= 1 && DPW >= 1 && DPW <= 64 &&
+         DPW * kMfmaWaves * PB == D;
+}
+// Tokens staged per stage for NTT token tiles: the tiles' tokens where that
+// splits evenly, else the full group.
+template <int BITS, int NMAT, int WG, typename SC, int NTT>
+constexpr int stage_tokens() {
+  return stage_fits<BITS, NMAT, WG, SC, 16 * NTT>() ? 16 * NTT : MfmaCfg<WG>::TOK;
+}
+
 template <int BITS, int NMAT, int WG, typename SC>
 struct MfmaLds {
-  using ST = MfmaStage<BITS, NMAT, WG, SC>;
-  __align__(16) unsigned char ring[ST::STAGES][ST::BYTES];
+  __align__(16) unsigned char ring[MfmaCfg<WG>::RING];  // stages of any token count
   int trow[MfmaCfg<WG>::TOK];  // activation row of each token slot (clamped past the item)
 };
 
@@ -278,8 +299,9 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
                                           MfmaLds<BITS, NMAT, WG, SC> &L,
                                           Acc (*acc)[MfmaCfg<WG>::TILES][4]) {
   using G = MfmaGeo<BITS, WG>;
-  using ST = MfmaStage<BITS, NMAT, WG, SC>;
+  using ST = MfmaStage<BITS, NMAT, WG, SC, stage_tokens<BITS, NMAT, WG, SC, NTT>()>;
   using SG = typename ST::SG;
+  static_assert(ST::STAGES * ST::BYTES <= (int)sizeof(L.ring) && 16 * NTT <= ST::TOK, "ring");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, g = lane >> 4;
   const int nbk = K / 32, nst = (nbk + G::CH - 1) / G::CH;
@@ -322,7 +344,7 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
 
   // one stage's loads: every wave issues ST::NL instructions
   auto issue = [&](int c) {
-    unsigned char *buf = L.ring[c % ST::STAGES];
+    unsigned char *buf = L.ring + (size_t)(c % ST::STAGES) * ST::BYTES;
     if (lane_offs && (c + 1) * G::CH <= nbk) {
       // a full stage: wave-uniform bases plus the lanes' fixed offsets
 #pragma unroll
@@ -474,26 +496,31 @@ __device__ __forceinline__ void mfma_core(const uint8_t *const *wbase, const int
 #pragma unroll
   for (int c = 0; c < ST::STAGES - 1; ++c)
     if (c < nst) issue(c);
-  for (int c = 0; c < nst; ++c) {
-    // this wave's loads of stage c are done once at most the later stages'
-    // remain; the barrier makes every wave's visible and frees stage c - 1
+  // stage c's data: this wave's loads of it are done once at most the later
+  // stages' remain; the barrier makes every wave's visible and frees stage
+  // c - 1, whose buffer then takes stage c + STAGES - 1
+  auto stage_ready = [&](int c) -> const unsigned char * {
     wait_stages_left<ST::NL, ST::STAGES - 2>(min(ST::STAGES - 2, nst - 1 - c));
     __builtin_amdgcn_s_barrier();
     if (c + ST::STAGES - 1 < nst) issue(c + ST::STAGES - 1);
-    const unsigned char *buf = L.ring[c % ST::STAGES];
-    const int cb = min(G::CH, nbk - c * G::CH);
-    if (cb == G::CH) {
-      // a full stage in one pipelined run (one or two token tiles), or in
-      // runs of two blocks (more tiles: operands and accumulators leave no
-      // room for more)
-      if constexpr (NTT <= 2) {
-        blocks_piped(std::integral_constant<int, G::CH>(), buf, 0);
-      } else {
-        for (int b0 = 0; b0 < G::CH; b0 += 2) blocks_piped(std::integral_constant<int, 2>(), buf, b0);
-      }
+    return L.ring + (size_t)(c % ST::STAGES) * ST::BYTES;
+  };
+  // the full stages, each in one pipelined run (one or two token tiles) or
+  // in runs of two blocks (more tiles: operands and accumulators leave no
+  // room for more); the partial last stage, if any, after the loop, so the
+  // loop body has one path and the accumulators stay in place across it
+  const int nfull = nbk / G::CH;
+  for (int c = 0; c < nfull; ++c) {
+    const unsigned char *buf = stage_ready(c);
+    if constexpr (NTT <= 2) {
+      blocks_piped(std::integral_constant<int, G::CH>(), buf, 0);
     } else {
-      for (int b = 0; b < cb; ++b) block_step(buf, b);
+      for (int b0 = 0; b0 < G::CH; b0 += 2) blocks_piped(std::integral_constant<int, 2>(), buf, b0);
     }
+  }
+  if (nfull < nst) {
+    const unsigned char *buf = stage_ready(nfull);
+    for (int b = 0; b < nbk - nfull * G::CH; ++b) block_step(buf, b);
   }
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
@@ -564,7 +591,7 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
   // h = silu(g) * u for rows 4 g + r of the wave, token 16 tt + li, staged
   // in LDS (over the ring) for the Q8_0 step
   static_assert(sizeof(float) * TOK * (kMfmaRows + 1) <= sizeof(L.ring), "h tile");
-  float(*hs)[kMfmaRows + 1] = reinterpret_cast<float(*)[kMfmaRows + 1]>(&L.ring[0][0]);
+  float(*hs)[kMfmaRows + 1] = reinterpret_cast<float(*)[kMfmaRows + 1]>(L.ring);
   const int rw = 16 * wave + 4 * g;  // the lane's first row in the block
   // the sums are of codes widened by 2^wshift: a power of two, undone exactly
   constexpr double unw = 1.0 / (double)(1 << wshift<BITS>());
