@@ -94,12 +94,13 @@ constexpr int wshift() {
 }
 
 // ---------------------------------------------------------------------------
-// Work items: (union slot, token group of up to 64, block of weight rows),
+// Work items: (union slot, token group of up to 64 or 32 tokens, block of
+// weight rows),
 // numbered G * n_rb + rb over the token groups G of the slots that run here
 // (mgofs), one per workgroup; the hardware hands each CU the next workgroup
 // as soon as one finishes, which balances items of unequal cost.  Workgroup
 // b takes item n_items - 1 - b: the shared expert's groups (the last slot,
-// a full 64 tokens each when it runs here) start first instead of forming
+// full groups when it runs here) start first instead of forming
 // the tail.  Items of one (slot, row block) with several token groups are
 // n_rb apart, so their re-reads of the weights run at about the same time.
 //
@@ -562,13 +563,18 @@ __device__ __forceinline__ void item_rows(const FfnArgs &a, const MfmaItem &it, 
 
 // ---------------------------------------------------------------------------
 // Gate/up + SwiGLU + Q8_0(h): rows [128 rb, +128) of gate and up for up to
-// 64 tokens of one expert.  Wave w owns rows 16 w .. 16 w + 15 of both.
+// 32 tokens (64 at int2) of one expert.  Wave w owns rows 16 w .. 16 w + 15
+// of both.
 // ---------------------------------------------------------------------------
-constexpr int kGateupWg = 1;
+// Workgroups resident per CU: two (each with half the LDS ring and 32-token
+// items), so one's item start and h epilogue overlap the other's stages;
+// int2's core would not fit the 128 VGPRs that leaves, so it keeps one.
+template <int BITS>
+constexpr int gateup_wg() { return BITS == 2 ? 1 : 2; }
 
 template <int BITS>
-__global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 * kGateupWg))) void k_gateup_mfma(FfnArgs a) {
-  constexpr int WG = kGateupWg;
+__global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 * gateup_wg<BITS>()))) void k_gateup_mfma(FfnArgs a) {
+  constexpr int WG = gateup_wg<BITS>();
   constexpr int TOK = MfmaCfg<WG>::TOK, TILES = MfmaCfg<WG>::TILES;
   __shared__ MfmaLds<BITS, 2, WG, double> L;
   const int H = a.L.H, I = a.L.I;
@@ -630,8 +636,8 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
 }
 
 // ---------------------------------------------------------------------------
-// Down projection: output rows [256 rb, +256) for up to 64 tokens of one
-// expert (two 128-row halves, the core's two matrices), o into the
+// Down projection: output rows [256 rb, +256) for up to 32 tokens (64 at
+// int2) of one expert (two 128-row halves, the core's two matrices), o into the
 // per-(token, slot) buffer the combine kernel reduces.
 // ---------------------------------------------------------------------------
 constexpr int kDownRows = 2 * kMfmaRows;
@@ -708,11 +714,12 @@ static dim3 mfma_grid(const FfnArgs &a, int n_rb) {
 
 
 hipError_t launch_gateup_mfma(const FfnArgs &a, hipStream_t st, KEvents ev) {
-  const dim3 grid = mfma_grid<kGateupWg>(a, (a.L.I + kMfmaRows - 1) / kMfmaRows), block(kMfmaThreads);
+  const int n_rb = (a.L.I + kMfmaRows - 1) / kMfmaRows;
+  const dim3 block(kMfmaThreads);
   switch (a.L.bits) {
-    case 8: COLI_LAUNCH(ev, k_gateup_mfma<8>, grid, block, 0, st, a); break;
-    case 4: COLI_LAUNCH(ev, k_gateup_mfma<4>, grid, block, 0, st, a); break;
-    case 2: COLI_LAUNCH(ev, k_gateup_mfma<2>, grid, block, 0, st, a); break;
+    case 8: COLI_LAUNCH(ev, k_gateup_mfma<8>, mfma_grid<gateup_wg<8>()>(a, n_rb), block, 0, st, a); break;
+    case 4: COLI_LAUNCH(ev, k_gateup_mfma<4>, mfma_grid<gateup_wg<4>()>(a, n_rb), block, 0, st, a); break;
+    case 2: COLI_LAUNCH(ev, k_gateup_mfma<2>, mfma_grid<gateup_wg<2>()>(a, n_rb), block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
