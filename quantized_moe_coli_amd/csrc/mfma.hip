@@ -95,14 +95,14 @@ constexpr int wshift() {
 
 // ---------------------------------------------------------------------------
 // Work items: (union slot, token group of up to 64 or 32 tokens, block of
-// weight rows),
-// numbered G * n_rb + rb over the token groups G of the slots that run here
-// (mgofs), one per workgroup; the hardware hands each CU the next workgroup
-// as soon as one finishes, which balances items of unequal cost.  Workgroup
-// b takes item n_items - 1 - b: the shared expert's groups (the last slot,
-// full groups when it runs here) start first instead of forming
-// the tail.  Items of one (slot, row block) with several token groups are
-// n_rb apart, so their re-reads of the weights run at about the same time.
+// weight rows), numbered G * n_rb + rb over the token groups G of the slots
+// that run here (mgofs), one per workgroup; the hardware hands each CU the
+// next workgroup as soon as one finishes, which balances items of unequal
+// cost.  Workgroup b takes item n_items - 1 - b: the shared expert's groups
+// (the last slot, full groups when it runs here) start first instead of
+// forming the tail.  Items of one (slot, row block) with several token
+// groups are n_rb apart, so their re-reads of the weights run at about the
+// same time.
 //
 // Workgroup b runs on XCD b mod 8, each XCD with its own L2.  In plain order
 // an XCD takes the same row blocks of every group (n_rb a multiple of 8):
