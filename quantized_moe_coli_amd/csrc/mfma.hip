@@ -266,6 +266,7 @@ template <int BITS, int NMAT, int WG, typename SC>
 struct MfmaLds {
   __align__(16) unsigned char ring[MfmaCfg<WG>::RING];  // stages of any token count
   int trow[MfmaCfg<WG>::TOK];  // activation row of each token slot (clamped past the item)
+  int orow[MfmaCfg<WG>::TOK];  // output row of each token slot (h row, or obuf row)
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -552,11 +553,13 @@ __device__ __forceinline__ void mfma_core_ntt(int ntt, const uint8_t *const *wba
 
 // Token slots of an item: activation row of each (clamped past nt), into LDS.
 template <int TOK>
-__device__ __forceinline__ void item_rows(const FfnArgs &a, const MfmaItem &it, bool hrows, int *trow) {
+__device__ __forceinline__ void item_rows(const FfnArgs &a, const MfmaItem &it, bool hrows, int *trow,
+                                          int *orow) {
   for (int n = threadIdx.x; n < TOK; n += kMfmaThreads) {
-    int t = 0, hrow = 0, j;
+    int t = 0, hrow = 0, j = 0;
     tok_at(a, true, it.s, it.n0 + min(n, it.nt - 1), t, hrow, j);
     trow[n] = hrows ? hrow : t;
+    orow[n] = hrows ? t * (a.k + 1) + j : hrow;
   }
   __syncthreads();
 }
@@ -585,7 +588,7 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
   const ExpertPtrs ep = expert_ptrs(a.L, it.e);
   const size_t row_bytes = (size_t)H * BITS / 8;
   const int rb0 = it.rb * kMfmaRows, nrows = min(kMfmaRows, I - rb0);
-  item_rows<TOK>(a, it, false, L.trow);
+  item_rows<TOK>(a, it, false, L.trow, L.orow);
   const uint8_t *wb[2] = {ep.wg + (size_t)rb0 * row_bytes, ep.wu + (size_t)rb0 * row_bytes};
   const int nr[2] = {nrows, nrows};
   // g and u accumulate in binary64 (the expert definition's sum, rounded
@@ -623,8 +626,7 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
     float amax = group_max<32>(fabsf(h));
     amax = __shfl(amax, (lane & 32) | 31, 64);
     if (bb < nblk) {
-      int t, hrow, j;
-      tok_at(a, true, it.s, it.n0 + tl, t, hrow, j);
+      const int hrow = L.orow[tl];
       const float db = amax / 127.f;
       float c = 0.f;
       if (db != 0.f) c = fminf(fmaxf(rintf(h / db), -127.f), 127.f);
@@ -659,7 +661,7 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
   const ExpertPtrs ep = expert_ptrs(a.L, it.e);
   const size_t row_bytes = (size_t)I * BITS / 8;
   const int rb0 = it.rb * kDownRows, nrows = min(kDownRows, H - rb0);
-  item_rows<TOK>(a, it, true, L.trow);
+  item_rows<TOK>(a, it, true, L.trow, L.orow);
   // half 1 may not exist at the matrix edge: its loads then read half 0's rows
   const int nr[2] = {min(nrows, kMfmaRows), max(1, nrows - kMfmaRows)};
   const uint8_t *wb[2] = {ep.wd + (size_t)rb0 * row_bytes,
@@ -681,14 +683,12 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
     for (int tt = 0; tt < TILES; ++tt) {
       const int n = 16 * tt + li;
       if (tt < ntt && n < it.nt) {
-        int t, hrow, j;
-        tok_at(a, true, it.s, it.n0 + n, t, hrow, j);
         float4 o;
         o.x = acc[m][tt][0] * unw * sd[0];
         o.y = acc[m][tt][1] * unw * sd[1];
         o.z = acc[m][tt][2] * unw * sd[2];
         o.w = acc[m][tt][3] * unw * sd[3];
-        *reinterpret_cast<float4 *>(a.obuf + ((size_t)t * (a.k + 1) + j) * H + rb0 + row) = o;
+        *reinterpret_cast<float4 *>(a.obuf + (size_t)L.orow[n] * H + rb0 + row) = o;
       }
     }
   }
