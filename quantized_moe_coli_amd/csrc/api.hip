@@ -108,7 +108,7 @@ WsLayout ws_layout(const coli_moe_layer *L, int Tmax) {
   w.uniq = take(E * 4);
   w.nuniq = take(4);
   // matrix-core item tables of 64- and 32-token groups
-  w.mgofs = take((2 * (E + 2) + 2 * (size_t)coli::mfma_gmax((int)T, (int)k, (int)E)) * 4);
+  w.mgofs = take(coli::mfma_table_words((int)T, (int)k, (int)E) * 4);
   w.hq = take((T * k + T) * I);
   w.hd = take((T * k + T) * (I / 32) * 4);
   w.hsh = take(4 * I * 4);  // decode and batches up to 4: the shared expert's h in binary32

@@ -95,7 +95,10 @@ struct Dispatch {
   const int32_t *uniq;    // [E]
   const int32_t *n_uniq;  // [1]
   // matrix-core item tables: [2][E+2] first token group (64, then 32
-  // tokens) of each union slot, then [2][mfma_gmax] union slot of each group
+  // tokens) of each union slot, then [2][mfma_gmax] union slot of each
+  // group, then (from mfma_desc_off) the group counts {64, 32, n_uniq, 0}
+  // and [2][mfma_gmax] group descriptors {expert (-1: shared), first pair
+  // (-1: shared), first token, tokens}
   const int32_t *mgofs;
 };
 
@@ -115,6 +118,14 @@ __host__ __device__ inline int mfma_groups(int n_tok, int mfma_min, int tok) {
 // routed pairs, one partial group per unique expert, the shared expert's).
 __host__ __device__ inline int mfma_gmax(int T, int k, int E) {
   return (int)(((int64_t)T * k + 31) / 32 + E + (T + 31) / 32 + 1);
+}
+// Offset (int32 words, 16-byte aligned) of the group counts and descriptors
+// in the matrix-core tables, and the tables' total size in words.
+__host__ __device__ inline size_t mfma_desc_off(int T, int k, int E) {
+  return ((2 * (size_t)(E + 2) + 2 * (size_t)mfma_gmax(T, k, E) + 3) / 4) * 4;
+}
+__host__ __device__ inline size_t mfma_table_words(int T, int k, int E) {
+  return mfma_desc_off(T, k, E) + 4 + 8 * (size_t)mfma_gmax(T, k, E);
 }
 // Row stride of the binary64 copy of the Q8_0 block scales (d64, for the
 // matrix-core gate/up): the blocks of a row rounded up to a multiple of 8.

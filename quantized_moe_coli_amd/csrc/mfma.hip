@@ -47,7 +47,7 @@ struct MfmaCfg {
   static constexpr int TOK = kMfmaGroup / WG;             // tokens per work item (group)
   static constexpr int TILES = TOK / 16;                  // 16-token tiles
   static constexpr int ROWB = 128 / WG;                   // weight bytes per row per stage (at most)
-  static constexpr int RING = 160 * 1024 / WG - 1024;     // LDS for the stage ring
+  static constexpr int RING = 160 * 1024 / WG - 2048;     // LDS for the stage ring
 };
 
 // A operand, in two steps so a block's raw loads can all be issued before
@@ -111,6 +111,10 @@ constexpr int wshift() {
 // group each, most of a prefill's) are taken transposed instead: XCD x
 // runs every row block of one group, so its activations are fetched once
 // too, and so are the weights, which no other group uses.
+//
+// A workgroup finds its item in two dependent loads: the group counts, then
+// the group descriptors (expert, first pair, first token, tokens) and the
+// run's end slots together, all written by the dispatch kernel.
 // ---------------------------------------------------------------------------
 struct MfmaItem {
   int e;      // expert (-1: shared)
@@ -122,28 +126,36 @@ struct MfmaItem {
 template <int WG>
 __device__ __forceinline__ bool mfma_item(const FfnArgs &a, int n_rb, MfmaItem &it) {
   using C = MfmaCfg<WG>;
-  const int nu = *a.disp.n_uniq;
-  const int32_t *gofs = a.disp.mgofs + (C::TOK == kMfmaGroup ? 0 : a.E + 2);
-  const int32_t *gslot = a.disp.mgofs + 2 * (a.E + 2) + (C::TOK == kMfmaGroup ? 0 : mfma_gmax(a.T, a.k, a.E));
-  const int n_items = gofs[nu + 1] * n_rb;
+  const int gmax = mfma_gmax(a.T, a.k, a.E);
+  const bool g64 = C::TOK == kMfmaGroup;
+  const int32_t *gslot = a.disp.mgofs + 2 * (a.E + 2) + (g64 ? 0 : gmax);
+  const int4 *hdr = reinterpret_cast<const int4 *>(a.disp.mgofs + mfma_desc_off(a.T, a.k, a.E));
+  const int4 *desc = hdr + 1 + (g64 ? 0 : gmax);
+  const int4 h = *hdr;
+  const int n_items = (g64 ? h.x : h.y) * n_rb;
   if ((int)blockIdx.x >= n_items) return false;
   const int i = n_items - 1 - (int)blockIdx.x;
-  int G = i / n_rb;
-  it.rb = i % n_rb;
   const int run = 8 * n_rb, r0 = i / run;
-  if ((r0 + 1) * run <= n_items && gslot[8 * r0 + 7] - gslot[8 * r0] == 7) {
-    G = 8 * r0 + i % 8;
-    it.rb = (i % run) / 8;
+  // both candidate groups' descriptors and the run's end slots, loaded together
+  const bool full = (r0 + 1) * run <= n_items;
+  const int4 dp = desc[i / n_rb];
+  int4 dt = dp;
+  int s0 = 0, s7 = 0;
+  if (full) {
+    s0 = gslot[8 * r0];
+    s7 = gslot[8 * r0 + 7];
+    dt = desc[8 * r0 + i % 8];
   }
-  const int lo = gslot[G];
-  const bool shared = lo == nu;
-  it.e = shared ? -1 : a.disp.uniq[lo];
+  const bool transposed = full && s7 - s0 == 7;
+  const int4 d = transposed ? dt : dp;
+  it.rb = transposed ? (i % run) / 8 : i % n_rb;
+  it.e = d.x;
   it.s.slot = -1;
-  it.s.shared = shared;
-  it.s.n_tok = shared ? a.T : a.disp.counts[it.e];
-  it.s.p0 = shared ? -1 : a.disp.offs[it.e];
-  it.n0 = (G - gofs[lo]) * C::TOK;
-  it.nt = min(C::TOK, it.s.n_tok - it.n0);
+  it.s.shared = d.x < 0;
+  it.s.p0 = d.y;
+  it.n0 = d.z;
+  it.nt = d.w;
+  it.s.n_tok = d.z + d.w;
   return it.nt > 0;
 }
 
@@ -267,6 +279,7 @@ struct MfmaLds {
   __align__(16) unsigned char ring[MfmaCfg<WG>::RING];  // stages of any token count
   int trow[MfmaCfg<WG>::TOK];  // activation row of each token slot (clamped past the item)
   int orow[MfmaCfg<WG>::TOK];  // output row of each token slot (h row, or obuf row)
+  float rsc[2 * kMfmaRows];    // the scales of the item's rows (two 128-row matrices)
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -552,15 +565,21 @@ __device__ __forceinline__ void mfma_core_ntt(int ntt, const uint8_t *const *wba
 }
 
 // Token slots of an item: activation row of each (clamped past nt), into LDS.
+// The item's token rows (activations in, outputs out) and the scales of its
+// weight rows (s0[0 .. c0), s1[0 .. c1), clamped), into LDS at the start, so
+// the epilogue needs no further round trip to memory.
 template <int TOK>
 __device__ __forceinline__ void item_rows(const FfnArgs &a, const MfmaItem &it, bool hrows, int *trow,
-                                          int *orow) {
+                                          int *orow, float *rsc, const float *s0, int c0,
+                                          const float *s1, int c1) {
   for (int n = threadIdx.x; n < TOK; n += kMfmaThreads) {
     int t = 0, hrow = 0, j = 0;
     tok_at(a, true, it.s, it.n0 + min(n, it.nt - 1), t, hrow, j);
     trow[n] = hrows ? hrow : t;
     orow[n] = hrows ? t * (a.k + 1) + j : hrow;
   }
+  for (int i = threadIdx.x; i < 2 * kMfmaRows; i += kMfmaThreads)
+    rsc[i] = i < kMfmaRows ? s0[min(i, c0 - 1)] : s1[min(i - kMfmaRows, c1 - 1)];
   __syncthreads();
 }
 
@@ -588,7 +607,7 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
   const ExpertPtrs ep = expert_ptrs(a.L, it.e);
   const size_t row_bytes = (size_t)H * BITS / 8;
   const int rb0 = it.rb * kMfmaRows, nrows = min(kMfmaRows, I - rb0);
-  item_rows<TOK>(a, it, false, L.trow, L.orow);
+  item_rows<TOK>(a, it, false, L.trow, L.orow, L.rsc, ep.sg + rb0, nrows, ep.su + rb0, nrows);
   const uint8_t *wb[2] = {ep.wg + (size_t)rb0 * row_bytes, ep.wu + (size_t)rb0 * row_bytes};
   const int nr[2] = {nrows, nrows};
   // g and u accumulate in binary64 (the expert definition's sum, rounded
@@ -607,9 +626,9 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
   float sg[4], su[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int row = rb0 + min(rw + r, nrows - 1);
-    sg[r] = ep.sg[row];
-    su[r] = ep.su[row];
+    const int row = min(rw + r, nrows - 1);
+    sg[r] = L.rsc[row];
+    su[r] = L.rsc[kMfmaRows + row];
   }
 #pragma unroll
   for (int tt = 0; tt < TILES; ++tt)
@@ -661,7 +680,8 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
   const ExpertPtrs ep = expert_ptrs(a.L, it.e);
   const size_t row_bytes = (size_t)I * BITS / 8;
   const int rb0 = it.rb * kDownRows, nrows = min(kDownRows, H - rb0);
-  item_rows<TOK>(a, it, true, L.trow, L.orow);
+  item_rows<TOK>(a, it, true, L.trow, L.orow, L.rsc, ep.sd + rb0, min(nrows, kMfmaRows),
+                 ep.sd + rb0 + (nrows > kMfmaRows ? kMfmaRows : 0), max(1, nrows - kMfmaRows));
   // half 1 may not exist at the matrix edge: its loads then read half 0's rows
   const int nr[2] = {min(nrows, kMfmaRows), max(1, nrows - kMfmaRows)};
   const uint8_t *wb[2] = {ep.wd + (size_t)rb0 * row_bytes,
@@ -678,7 +698,7 @@ __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2 
     constexpr float unw = 1.0f / (float)(1 << wshift<BITS>());
     float sd[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sd[r] = ep.sd[rb0 + row + r];
+    for (int r = 0; r < 4; ++r) sd[r] = L.rsc[row + r];
 #pragma unroll
     for (int tt = 0; tt < TILES; ++tt) {
       const int n = 16 * tt + li;

@@ -324,6 +324,8 @@ __global__ __launch_bounds__(kDispThreads) void k_dispatch(const int32_t *__rest
   __shared__ int cnt[kSelMaxE];
   __shared__ int base[kSelMaxE];
   __shared__ int ucnt[kSelMaxE];  // count of the u-th unique expert
+  __shared__ int uexp[kSelMaxE];  // its expert id
+  __shared__ int uoff[kSelMaxE];  // its first pair
   __shared__ uint64_t wtot[kDispWaves];
   __shared__ int s_nu;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -386,6 +388,8 @@ __global__ __launch_bounds__(kDispThreads) void k_dispatch(const int32_t *__rest
     if (c0 > 0) {
       uniq[(int)(exc >> 32)] = tid;
       ucnt[(int)(exc >> 32)] = c0;
+      uexp[(int)(exc >> 32)] = tid;
+      uoff[(int)(exc >> 32)] = (int)(uint32_t)exc;
     }
   }
   if (tid == kDispThreads - 1) {
@@ -437,6 +441,24 @@ __global__ __launch_bounds__(kDispThreads) void k_dispatch(const int32_t *__rest
     for (uint32_t j = 0; j < b64; ++j) s64[e64 + a64 + j] = 2 * tid + 1;
     for (uint32_t j = 0; j < a32; ++j) s32[e32 + j] = 2 * tid;
     for (uint32_t j = 0; j < b32; ++j) s32[e32 + a32 + j] = 2 * tid + 1;
+    // group counts and descriptors: {expert, first pair, first token, tokens}
+    int4 *hdr = reinterpret_cast<int4 *>(mgofs + mfma_desc_off(T, k, E));
+    int4 *d64 = hdr + 1, *d32 = d64 + mfma_gmax(T, k, E);
+    if (tid == kDispThreads - 1) hdr[0] = make_int4((int)(uint32_t)gi, (int)(gi >> 32), nu, 0);
+    auto descs = [&](int u, uint32_t first, uint32_t ng, int tok, int4 *d) {
+      const bool sh = u == nu;
+      const int e = sh ? -1 : uexp[u], p0 = sh ? -1 : uoff[u], nt = sh ? T : ucnt[u];
+      for (uint32_t j = 0; j < ng; ++j)
+        d[first + j] = make_int4(e, p0, (int)j * tok, min(tok, nt - (int)j * tok));
+    };
+    if (2 * tid < slots) {
+      descs(2 * tid, e64, a64, kMfmaGroup, d64);
+      descs(2 * tid, e32, a32, kMfmaGroup / 2, d32);
+    }
+    if (2 * tid + 1 < slots) {
+      descs(2 * tid + 1, e64 + a64, b64, kMfmaGroup, d64);
+      descs(2 * tid + 1, e32 + a32, b32, kMfmaGroup / 2, d32);
+    }
   }
 
   const int nb = 32 - __clz(E);  // bits of the ids 0 .. E (E: no expert)
