@@ -388,11 +388,16 @@ struct SharedRows {
 // container ordering and block scales, into LDS: 4 values per thread, the 8
 // threads of a 32-value block together (amax, then amax / 127 and the codes
 // rounded to nearest even, as every other Q8_0 step of the layer).
+// (The thread index passes through an empty asm statement so the address
+// arithmetic stays here instead of being hoisted to the kernel's start,
+// where its registers would be spilled for the whole kernel.)
 template <int BITS>
 __device__ __forceinline__ void quantize_shared_h(const DecodeArgs &d, int8_t *q, float *dsc) {
   const int I = d.f.L.I;
-  const int part = threadIdx.x & 7;
-  for (int i0 = 4 * (int)threadIdx.x; i0 < I; i0 += 4 * kDecThreads) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int part = tid & 7;
+  for (int i0 = 4 * tid; i0 < I; i0 += 4 * kDecThreads) {
     const uint64_t *src = reinterpret_cast<const uint64_t *>(d.hsh + i0);
     const uint64_t lo = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t hi = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -512,11 +517,13 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
       constexpr int kStage = 2;
       const int wq = I / 8, wd = I / 64;  // 8-byte words of codes and scales per slot
       const int n = (gn - q_lo) * (wq + wd);
+      int tid = threadIdx.x;  // kept here, as in quantize_shared_h
+      asm volatile("" : "+v"(tid));
       for (int i0 = 0; i0 < n; i0 += kStage * kDecThreads) {
         uint64_t v[kStage];
 #pragma unroll
         for (int j = 0; j < kStage; ++j) {
-          const int i = i0 + j * kDecThreads + threadIdx.x;
+          const int i = i0 + j * kDecThreads + tid;
           v[j] = 0;
           if (i < n) {
             const int q = q_lo + i / (wq + wd), r = i - (q - q_lo) * (wq + wd);
@@ -528,7 +535,7 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
         }
 #pragma unroll
         for (int j = 0; j < kStage; ++j) {
-          const int i = i0 + j * kDecThreads + threadIdx.x;
+          const int i = i0 + j * kDecThreads + tid;
           if (i < n) {
             const int q = q_lo + i / (wq + wd), r = i - (q - q_lo) * (wq + wd);
             uint64_t *dst = r < wq ? reinterpret_cast<uint64_t *>(lds_q + (size_t)q * I) + r
