@@ -143,6 +143,15 @@ __device__ __forceinline__ uint32_t ld_ctr(const uint32_t *c) {
   return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The thread index through an empty asm statement: address arithmetic on it
+// stays inside the loop that uses it instead of being hoisted to the
+// kernel's start, where its registers would be spilled for the whole kernel.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Every wave waits until its device-scope stores have completed, then one
 // thread adds to the counter.
 __device__ __forceinline__ void publish(uint32_t *c, uint32_t v) {
@@ -388,14 +397,10 @@ struct SharedRows {
 // container ordering and block scales, into LDS: 4 values per thread, the 8
 // threads of a 32-value block together (amax, then amax / 127 and the codes
 // rounded to nearest even, as every other Q8_0 step of the layer).
-// (The thread index passes through an empty asm statement so the address
-// arithmetic stays here instead of being hoisted to the kernel's start,
-// where its registers would be spilled for the whole kernel.)
 template <int BITS>
 __device__ __forceinline__ void quantize_shared_h(const DecodeArgs &d, int8_t *q, float *dsc) {
   const int I = d.f.L.I;
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
+  const int tid = opaque_tid();
   const int part = tid & 7;
   for (int i0 = 4 * tid; i0 < I; i0 += 4 * kDecThreads) {
     const uint64_t *src = reinterpret_cast<const uint64_t *>(d.hsh + i0);
@@ -517,8 +522,7 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &d, int r0, int8_t *l
       constexpr int kStage = 2;
       const int wq = I / 8, wd = I / 64;  // 8-byte words of codes and scales per slot
       const int n = (gn - q_lo) * (wq + wd);
-      int tid = threadIdx.x;  // kept here, as in quantize_shared_h
-      asm volatile("" : "+v"(tid));
+      const int tid = opaque_tid();
       for (int i0 = 0; i0 < n; i0 += kStage * kDecThreads) {
         uint64_t v[kStage];
 #pragma unroll
@@ -970,10 +974,11 @@ template <int BITS, int LPR, int CPL, int NPASS, int SG, int T>
 __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const SmallUnion &su, int r0,
                                                 int8_t *lds_q, float *lds_d, int *srow,
                                                 float (*ob)[kSmallObRows]) {
+  const int tid = opaque_tid();
   constexpr int RPP = 64 / LPR;
   const FfnArgs &a = d.f;
   const int I = a.L.I, H = a.L.H, k = a.k, hr0 = k * T;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int gl = lane % LPR, rsub = lane / LPR;
   const int nchunks = I * BITS / 128;
   const size_t row_bytes = (size_t)I * BITS / 8;
@@ -1023,11 +1028,11 @@ __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const Small
         }
       }
     }
-    if ((int)threadIdx.x < gn) {
+    if (tid < gn) {
       int x = 0;
 #pragma unroll
       for (int q = 0; q < SG; ++q)
-        if (q == (int)threadIdx.x) x = ux[q];
+        if (q == tid) x = ux[q];
       const uint32_t *c = d.ctr + kCtrSlot0 + (x == 0 ? kShLine : x - 1) * kCtrStride;
       const uint32_t target = (uint32_t)(I / kGuRows);
       const uint32_t sb = spin_bound(d, 8u * kSpinLimit);
@@ -1040,7 +1045,7 @@ __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const Small
       }
       if (v < target || forced) gave_up(d, COLI_WAIT_SLOTS);
     }
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
       int n = 0;
 #pragma unroll
       for (int q = 0; q < SG; ++q)
@@ -1104,7 +1109,7 @@ __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const Small
   // y = o_shared + the kept slots' w * o in slot order, one thread per
   // (token, row)
   const int rows = kDecWaves * NPASS * RPP;
-  for (int i = threadIdx.x; i < T * rows; i += kDecThreads) {
+  for (int i = tid; i < T * rows; i += kDecThreads) {
     const int t = i / rows, rl = i % rows;
     float y = ob[t * (k + 1) + k][rl];
     for (int j = 0; j < k; ++j) {
@@ -1125,13 +1130,14 @@ __device__ __forceinline__ void small_gateup(const DecodeArgs &d, const SmallUni
                                              float (*hs)[kGuRows], float (*hu)[kGuRows],
                                              int8_t (*hcode)[kGuRows], const int8_t *xq,
                                              const float *xd) {
+  const int tid = opaque_tid();
   static_assert(kGuRows == 32, "one Q8_0 block of h per item");
   constexpr int RPP = 64 / LPR;
   constexpr int ROWS_PER_WAVE = kGuRows / kDecWaves;
   constexpr int PASSES = ROWS_PER_WAVE / RPP;
   const FfnArgs &a = d.f;
   const int H = a.L.H, I = a.L.I;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int gl = lane % LPR, rsub = lane / LPR;
   const int nchunks = H * BITS / 128;
   const size_t row_bytes = (size_t)H * BITS / 8;
@@ -1185,7 +1191,7 @@ __device__ __forceinline__ void small_gateup(const DecodeArgs &d, const SmallUni
   __syncthreads();
   // SwiGLU and Q8_0 of each token's 32 values of h: 32 threads per token
   for (int n0 = 0; n0 < n_tok; n0 += kDecThreads / 32) {
-    const int n = n0 + (threadIdx.x >> 5), i = threadIdx.x & 31;
+    const int n = n0 + (tid >> 5), i = tid & 31;
     if (n < n_tok) {
       const float h = swiglu_h(hs[n][i], hu[n][i]);
       float amax = group_max<32>(fabsf(h));
@@ -1200,7 +1206,7 @@ __device__ __forceinline__ void small_gateup(const DecodeArgs &d, const SmallUni
   }
   __syncthreads();
   {
-    const int n = threadIdx.x >> 3, i = threadIdx.x & 7;
+    const int n = tid >> 3, i = tid & 7;
     if (n < n_tok)
       st_dev(reinterpret_cast<uint32_t *>(a.hq + (size_t)(h0 + n) * I + rb * 32) + i,
              reinterpret_cast<const uint32_t *>(hcode[n])[i]);
