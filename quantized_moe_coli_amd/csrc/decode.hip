@@ -780,7 +780,7 @@ struct SmallUnion {
   int pidx[kSelMaxK];    // expert of pair l = t * k + j (-1: none)
   float pw[kSelMaxK];    // weight of pair l
   int sorted[kSelMaxK];  // pair at h row r
-  int ue[kSelMaxK + 1];  // expert of unique u
+  int ue[kSelMaxK + 1];  // where unique u's weights are stored (expert_store)
   int ufirst[kSelMaxK + 1];  // first h row of unique u (ufirst[U] = n_valid)
 };
 
@@ -818,7 +818,7 @@ __device__ __forceinline__ void small_union(const DecodeArgs &d, SmallUnion &su)
     const uint64_t bf = __ballot(first), bv = __ballot(valid);
     const int u = __popcll(bf & ((1ull << lane) - 1ull));
     if (first) {
-      su.ue[u] = e;
+      su.ue[u] = expert_store(a.L, e);
       su.ufirst[u] = lane;
     }
     if (lane == 0) {
@@ -890,7 +890,7 @@ __device__ __forceinline__ void small_shared_rows(const DecodeArgs &d, int r0, i
   const int gl = lane % LPR, rsub = lane / LPR;
   const int nchunks = H * BITS / 128;
   const size_t row_bytes = (size_t)H * BITS / 8;
-  const ExpertPtrs ep = expert_ptrs(a.L, -1);
+  const ExpertPtrs ep = expert_ptrs_at(a.L, -1);
   for (int rp = wave * RPP; rp < nr; rp += kDecWaves * RPP) {
     const int row = min(r0 + rp + rsub, I - 1);
     const uint4 *gp = reinterpret_cast<const uint4 *>(ep.wg + (size_t)row * row_bytes);
@@ -901,6 +901,13 @@ __device__ __forceinline__ void small_shared_rows(const DecodeArgs &d, int r0, i
       const int c = min(gl + LPR * i, nchunks - 1);
       wg[i] = ld_nt(gp + c);
       wu[i] = ld_nt(up + c);
+    }
+    // the row scales with the weights, one round trip for both (at four
+    // tokens they would not fit the registers beside the rest: read at use)
+    float sgv = 0.f, suv = 0.f;
+    if constexpr (T < 4) {
+      sgv = ep.sg[row];
+      suv = ep.su[row];
     }
     // each token's activation chunks from LDS, one token at a time (few
     // registers: the rows' weights stay, the activations are re-read)
@@ -918,7 +925,11 @@ __device__ __forceinline__ void small_shared_rows(const DecodeArgs &d, int r0, i
       pg = group_sum_f64<LPR>(pg);
       pu = group_sum_f64<LPR>(pu);
       if (lane == group_sum_lane<LPR>(lane) && rp + rsub < nr) {
-        const float h = swiglu_h(row_out(pg, ep.sg[row]), row_out(pu, ep.su[row]));
+        if constexpr (T >= 4) {
+          sgv = ep.sg[row];
+          suv = ep.su[row];
+        }
+        const float h = swiglu_h(row_out(pg, sgv), row_out(pu, suv));
         st_dev(reinterpret_cast<uint32_t *>(d.hsh) + (size_t)t * I + row, __float_as_uint(h));
       }
     }
@@ -1017,7 +1028,7 @@ __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const Small
     for (int q = 0; q < SG; ++q) {
       if (q < gn) {
         const int x = ux[q];
-        const ExpertPtrs ep = expert_ptrs(a.L, x == 0 ? -1 : su.ue[x - 1]);
+        const ExpertPtrs ep = expert_ptrs_at(a.L, x == 0 ? -1 : su.ue[x - 1]);
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
           const int row = wrow0 + p * RPP + rsub;
@@ -1143,7 +1154,7 @@ __device__ __forceinline__ void small_gateup(const DecodeArgs &d, const SmallUni
   const size_t row_bytes = (size_t)H * BITS / 8;
   const int xblocks = H / 32;
   const int h0 = su.ufirst[u], n_tok = su.ufirst[u + 1] - h0;
-  const ExpertPtrs ep = expert_ptrs(a.L, su.ue[u]);
+  const ExpertPtrs ep = expert_ptrs_at(a.L, su.ue[u]);
   const int srow = rb * 32 + wave * ROWS_PER_WAVE + min(lane, ROWS_PER_WAVE - 1);
   const float sgv = ep.sg[srow], suv = ep.su[srow];
   uint4 wg[PIPE][CPL], wu[PIPE][CPL];
@@ -1239,14 +1250,19 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 2))) void k_small_fused(Decod
   float *xd_lds = reinterpret_cast<float *>(dyn + d.lds_x + T * H);
   float *lsave = d.lds_l >= 0 ? reinterpret_cast<float *>(dyn + d.lds_l) : nullptr;
 
-  // logit slices: gate row e for every token
+  // logit slices: gate row e for every token; then the tokens' Q8_0 codes,
+  // the loads of up to three tokens in flight together
   for (int e = (int)blockIdx.x; e < d.n_slice; e += gridDim.x) small_slice<T>(d, e, lpart);
   {
-    ActRow<BITS, kDecThreads> xr;
+    constexpr int XB = T == 4 ? 2 : T;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      xr.load(d.x + (size_t)t * H, H);
-      xr.quantize(H, xq_lds + (size_t)t * H, xd_lds + (size_t)t * (H / 32));
+    for (int t0 = 0; t0 < T; t0 += XB) {
+      ActRow<BITS, kDecThreads> xr[XB];
+#pragma unroll
+      for (int t = 0; t < XB; ++t) xr[t].load(d.x + (size_t)(t0 + t) * H, H);
+#pragma unroll
+      for (int t = 0; t < XB; ++t)
+        xr[t].quantize(H, xq_lds + (size_t)(t0 + t) * H, xd_lds + (size_t)(t0 + t) * (H / 32));
     }
   }
   __syncthreads();

@@ -97,7 +97,16 @@ struct ExpertPtrs {
   const float *sg, *su, *sd;
 };
 
-__device__ __forceinline__ ExpertPtrs expert_ptrs(const LayerPtrs &L, int e) {
+// Where expert e's weights are stored: its own index, or through the expert
+// cache its slot (an out-of-range slot reads slot 0).
+__device__ __forceinline__ int expert_store(const LayerPtrs &L, int e) {
+  if (e < 0 || !L.slot_of) return e;
+  const int s = L.slot_of[e];
+  return (unsigned)s < (unsigned)L.n_slots ? s : 0;
+}
+
+// Pointers of the expert stored at index e (-1: the shared expert).
+__device__ __forceinline__ ExpertPtrs expert_ptrs_at(const LayerPtrs &L, int e) {
   ExpertPtrs p;
   if (e < 0) {
     p.wg = L.sh_gate; p.wu = L.sh_up; p.wd = L.sh_down;
@@ -105,10 +114,6 @@ __device__ __forceinline__ ExpertPtrs expert_ptrs(const LayerPtrs &L, int e) {
   } else {
     const size_t gu_stride = (size_t)L.I * (L.H * L.bits / 8);
     const size_t d_stride = (size_t)L.H * (L.I * L.bits / 8);
-    if (L.slot_of) {  // through the expert cache (an out-of-range slot reads slot 0)
-      const int s = L.slot_of[e];
-      e = (unsigned)s < (unsigned)L.n_slots ? s : 0;
-    }
     p.wg = L.w_gate + (size_t)e * gu_stride;
     p.wu = L.w_up + (size_t)e * gu_stride;
     p.wd = L.w_down + (size_t)e * d_stride;
@@ -117,6 +122,10 @@ __device__ __forceinline__ ExpertPtrs expert_ptrs(const LayerPtrs &L, int e) {
     p.sd = L.s_down + (size_t)e * L.H;
   }
   return p;
+}
+
+__device__ __forceinline__ ExpertPtrs expert_ptrs(const LayerPtrs &L, int e) {
+  return expert_ptrs_at(L, expert_store(L, e));
 }
 
 // The tokens of one work item: decode -> token 0 at h row `slot`; union ->
