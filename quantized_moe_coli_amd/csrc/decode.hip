@@ -60,8 +60,6 @@ namespace coli {
 //   kernel) and the polling bound override (test hook: if nonzero at the
 //   start of a call, the bound on every wait's polling rounds; cleared by
 //   the call);
-//   one word per 32-row block of the shared expert: its rows done so far
-//   (the small-batch kernel's);
 //   then up to 1024 64-bit words of router logit partials: slice s = e * P + p
 //   holds the complemented bits of the binary64 sum of x . gate_w[e] over the
 //   p-th of P equal column ranges.  Zero means "not written yet" (no finite
@@ -75,10 +73,9 @@ enum : int {
   kCtrSlot0 = kCtrExit + kCtrStride,
   kCtrStatus = kCtrSlot0 + (kSelMaxK + 1) * kCtrStride,
   kCtrSpin = kCtrStatus + kCtrStride,
-  kCtrShBlk = kCtrSpin + kCtrStride,  // one word per 32-row block of the shared expert
   kScoreWords = 3072
 };
-static_assert(kCtrShBlk + 8192 / 32 <= kScoreWords, "counters overlap scores");
+static_assert(kCtrSpin + kCtrStride <= kScoreWords, "counters overlap scores");
 constexpr int kMaxSlices = 1024;  // logit partial words in the header
 static_assert((kScoreWords + 2 * kMaxSlices) * 4 <= kDecodeCounterBytes,
               "decode state exceeds the workspace header");
@@ -749,18 +746,18 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 1))) void k_decode_fused(Deco
 // Per call, in order:
 //   logit slices (computed logits): one gate row per slice for every token
 //     (P = 1), each token's binary64 partial in its own header word;
-//   every workgroup: the tokens' Q8_0 codes into LDS;
 //   workgroup t < T: token t's scores and experts (select_local), written to
-//     the workspace's idx / w rows and counted in the selection counter;
-//   every workgroup: its rows of the shared expert's gate/up for all tokens
-//     (h in binary32; the workgroup completing a 32-row block quantises it
-//     for every token), then, once T selections are counted, the batch's
-//     union in LDS: the (token, slot) pairs sorted by (expert, pair), so the
-//     experts' runs are consecutive and each pair's h row is its position;
-//   tickets: GR items (unique expert u, 32-row block) for the tokens of u,
-//     then D items (a block of output rows for every token: the shared
-//     expert first, then the unique experts in order, each token's
-//     contributions weighted and summed in that fixed order).
+//     the workspace's idx / w rows and counted in the selection counter
+//     (first, so the union waits as little as possible for it);
+//   every workgroup: the tokens' Q8_0 codes into LDS, then, once T
+//     selections are counted, the batch's union in LDS: the (token, slot)
+//     pairs sorted by (expert, pair), so the experts' runs are consecutive
+//     and each pair's h row is its position;
+//   tickets: GR items (a 32-row block of the shared expert for every token,
+//     then of each unique expert u for the tokens of u), then D items (a
+//     block of output rows for every token: the shared expert first, then
+//     the unique experts in order, each token's contributions weighted and
+//     summed in that fixed order).
 // Slot counters: unique expert u on line u, the shared expert on line
 // kSelMaxK; the waits, give-ups, status word and header reset are the
 // decode kernel's.
@@ -876,98 +873,6 @@ __device__ __forceinline__ void small_slice(const DecodeArgs &d, int e, double (
                        ~(uint64_t)__double_as_longlong(sum), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-}
-
-// The shared expert's gate/up rows [r0, r0 + nr) for every token (shared_rows
-// with T activations per row); h rows k*T + t.
-template <int BITS, int LPR, int CPL, int T>
-__device__ __forceinline__ void small_shared_rows(const DecodeArgs &d, int r0, int nr,
-                                                  const int8_t *xq, const float *xd, int *s_last) {
-  constexpr int RPP = 64 / LPR;
-  const FfnArgs &a = d.f;
-  const int H = a.L.H, I = a.L.I, hr0 = a.k * T;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int gl = lane % LPR, rsub = lane / LPR;
-  const int nchunks = H * BITS / 128;
-  const size_t row_bytes = (size_t)H * BITS / 8;
-  const ExpertPtrs ep = expert_ptrs_at(a.L, -1);
-  for (int rp = wave * RPP; rp < nr; rp += kDecWaves * RPP) {
-    const int row = min(r0 + rp + rsub, I - 1);
-    const uint4 *gp = reinterpret_cast<const uint4 *>(ep.wg + (size_t)row * row_bytes);
-    const uint4 *up = reinterpret_cast<const uint4 *>(ep.wu + (size_t)row * row_bytes);
-    uint4 wg[CPL], wu[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = min(gl + LPR * i, nchunks - 1);
-      wg[i] = ld_nt(gp + c);
-      wu[i] = ld_nt(up + c);
-    }
-    // the row scales with the weights, one round trip for both (at four
-    // tokens they would not fit the registers beside the rest: read at use)
-    float sgv = 0.f, suv = 0.f;
-    if constexpr (T < 4) {
-      sgv = ep.sg[row];
-      suv = ep.su[row];
-    }
-    // each token's activation chunks from LDS, one token at a time (few
-    // registers: the rows' weights stay, the activations are re-read)
-    for (int t = 0; t < T; ++t) {
-      double pg = 0.0, pu = 0.0;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = gl + LPR * i;
-        Act<BITS> act;
-        if (c < nchunks) load_act<BITS>(act, xq + (size_t)t * H, xd + (size_t)t * (H / 32), c);
-        else zero_act<BITS>(act);
-        pg += chunk_part_f64<BITS>(wg[i], act);
-        pu += chunk_part_f64<BITS>(wu[i], act);
-      }
-      pg = group_sum_f64<LPR>(pg);
-      pu = group_sum_f64<LPR>(pu);
-      if (lane == group_sum_lane<LPR>(lane) && rp + rsub < nr) {
-        if constexpr (T >= 4) {
-          sgv = ep.sg[row];
-          suv = ep.su[row];
-        }
-        const float h = swiglu_h(row_out(pg, sgv), row_out(pu, suv));
-        st_dev(reinterpret_cast<uint32_t *>(d.hsh) + (size_t)t * I + row, __float_as_uint(h));
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  const int b_lo = r0 / 32, b_hi = (r0 + nr - 1) / 32;
-  for (int b = b_lo; b <= b_hi; ++b) {
-    if (threadIdx.x == 0) {
-      const int n_in = min(r0 + nr, 32 * b + 32) - max(r0, 32 * b);
-      const uint32_t old = __hip_atomic_fetch_add(d.ctr + kCtrShBlk + b, (uint32_t)n_in,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *s_last = (int)(old + (uint32_t)n_in) == 32;
-    }
-    __syncthreads();
-    if (*s_last) {
-      // this workgroup completed block b: Q8_0 of its 32 values of h for
-      // every token, wave t for token t
-      if (wave < T && lane < 32) {
-        const int t = wave, i = lane;
-        const float h = __uint_as_float(ld_dev(reinterpret_cast<const uint32_t *>(d.hsh) + (size_t)t * I + 32 * b + i));
-        const float amax = __shfl(group_max<32>(fabsf(h)), 31, 64);
-        const float db = amax / 127.f;
-        float c = 0.f;
-        if (db != 0.f) c = fminf(fmaxf(rintf(h / db), -127.f), 127.f);
-        const int code = (int)c & 0xFF;
-        uint32_t word = 0;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          word |= ((uint32_t)__shfl(code, perm_src<BITS>((4 * i + m) & 31), 64) & 0xFFu) << (8 * m);
-        if (i < 8) st_dev(reinterpret_cast<uint32_t *>(a.hq + (size_t)(hr0 + t) * I + 32 * b) + i, word);
-        if (i == 0)
-          st_dev(reinterpret_cast<uint32_t *>(a.hd) + (size_t)(hr0 + t) * (I / 32) + b, __float_as_uint(db));
-      }
-      publish(d.ctr + kCtrSlot0 + kShLine * kCtrStride, 1u);
-    }
-    __syncthreads();
-  }
 }
 
 // D item: output rows [r0, r0 + down_rows) for every token.  "Experts" in
@@ -1133,14 +1038,15 @@ __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const Small
 }
 
 // GR item: unique expert u's gate/up rows [32 rb, +32) for its n tokens
-// (h rows ufirst[u] ..): the gate/up body with the tokens in a runtime loop
+// (h rows ufirst[u] ..), or with u < 0 the shared expert's for all n_sh
+// tokens (h rows k * n_sh + t): the gate/up body with the tokens in a runtime loop
 // whose activations are re-read from LDS per row pass, so a pass holds only
 // its rows' weights (PIPE passes in flight) -- few registers at any n.
 template <int BITS, int LPR, int CPL, int PIPE>
 __device__ __forceinline__ void small_gateup(const DecodeArgs &d, const SmallUnion &su, int u, int rb,
                                              float (*hs)[kGuRows], float (*hu)[kGuRows],
                                              int8_t (*hcode)[kGuRows], const int8_t *xq,
-                                             const float *xd) {
+                                             const float *xd, int n_sh) {
   const int tid = opaque_tid();
   static_assert(kGuRows == 32, "one Q8_0 block of h per item");
   constexpr int RPP = 64 / LPR;
@@ -1153,8 +1059,10 @@ __device__ __forceinline__ void small_gateup(const DecodeArgs &d, const SmallUni
   const int nchunks = H * BITS / 128;
   const size_t row_bytes = (size_t)H * BITS / 8;
   const int xblocks = H / 32;
-  const int h0 = su.ufirst[u], n_tok = su.ufirst[u + 1] - h0;
-  const ExpertPtrs ep = expert_ptrs_at(a.L, su.ue[u]);
+  const bool shared = u < 0;
+  const int h0 = shared ? a.k * n_sh : su.ufirst[u];
+  const int n_tok = shared ? n_sh : su.ufirst[u + 1] - h0;
+  const ExpertPtrs ep = expert_ptrs_at(a.L, shared ? -1 : su.ue[u]);
   const int srow = rb * 32 + wave * ROWS_PER_WAVE + min(lane, ROWS_PER_WAVE - 1);
   const float sgv = ep.sg[srow], suv = ep.su[srow];
   uint4 wg[PIPE][CPL], wu[PIPE][CPL];
@@ -1177,7 +1085,7 @@ __device__ __forceinline__ void small_gateup(const DecodeArgs &d, const SmallUni
     const int rl = wave * ROWS_PER_WAVE + p * RPP + rsub;
     const float sg = row_scale<RPP>(sgv, p, rsub), su_ = row_scale<RPP>(suv, p, rsub);
     for (int n = 0; n < n_tok; ++n) {
-      const int t = su.sorted[h0 + n] / a.k;
+      const int t = shared ? n : su.sorted[h0 + n] / a.k;
       const int8_t *xqt = xq + (size_t)t * H;
       const float *xdt = xd + (size_t)t * xblocks;
       double pg = 0.0, pu = 0.0;
@@ -1250,22 +1158,10 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 2))) void k_small_fused(Decod
   float *xd_lds = reinterpret_cast<float *>(dyn + d.lds_x + T * H);
   float *lsave = d.lds_l >= 0 ? reinterpret_cast<float *>(dyn + d.lds_l) : nullptr;
 
-  // logit slices: gate row e for every token; then the tokens' Q8_0 codes,
-  // the loads of up to three tokens in flight together
+  // logit slices: gate row e for every token; workgroup t < T then selects
+  // token t's experts; then the tokens' Q8_0 codes, the loads of up to three
+  // tokens in flight together
   for (int e = (int)blockIdx.x; e < d.n_slice; e += gridDim.x) small_slice<T>(d, e, lpart);
-  {
-    constexpr int XB = T == 4 ? 2 : T;
-#pragma unroll
-    for (int t0 = 0; t0 < T; t0 += XB) {
-      ActRow<BITS, kDecThreads> xr[XB];
-#pragma unroll
-      for (int t = 0; t < XB; ++t) xr[t].load(d.x + (size_t)(t0 + t) * H, H);
-#pragma unroll
-      for (int t = 0; t < XB; ++t)
-        xr[t].quantize(H, xq_lds + (size_t)(t0 + t) * H, xd_lds + (size_t)(t0 + t) * (H / 32));
-    }
-  }
-  __syncthreads();
   if ((int)blockIdx.x < T) {
     // token blockIdx.x: scores, experts, weights, published
     const int t = blockIdx.x;
@@ -1286,10 +1182,18 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 2))) void k_small_fused(Decod
     __syncthreads();
   }
   {
-    const int r0 = (int)blockIdx.x * d.sh_rows;
-    const int nr = min(d.sh_rows, I - r0);
-    if (nr > 0) small_shared_rows<BITS, GLPR, GCPL, T>(d, r0, nr, xq_lds, xd_lds, &s_ticket);
+    constexpr int XB = T == 4 ? 2 : T;
+#pragma unroll
+    for (int t0 = 0; t0 < T; t0 += XB) {
+      ActRow<BITS, kDecThreads> xr[XB];
+#pragma unroll
+      for (int t = 0; t < XB; ++t) xr[t].load(d.x + (size_t)(t0 + t) * H, H);
+#pragma unroll
+      for (int t = 0; t < XB; ++t)
+        xr[t].quantize(H, xq_lds + (size_t)(t0 + t) * H, xd_lds + (size_t)(t0 + t) * (H / 32));
+    }
   }
+  __syncthreads();
   // every token's selection, then the union
   if (threadIdx.x == 0) {
     const uint32_t sb = spin_bound(d, kSpinLimit);
@@ -1304,7 +1208,9 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 2))) void k_small_fused(Decod
   }
   __syncthreads();
   small_union<T>(d, su);
-  const int n_gr = su.U * n_rb;
+  // GR items: the shared expert's row blocks (x = 0), then each unique
+  // expert's (x = u + 1)
+  const int n_gr = (su.U + 1) * n_rb;
   const int total = n_gr + d.n_down;
 
   const int q = blockIdx.x % kQueues;
@@ -1322,9 +1228,9 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 2))) void k_small_fused(Decod
 
   int t = (int)blockIdx.x < total ? (int)blockIdx.x : total;
   for (; t < n_gr; t = next_ticket()) {
-    const int u = t / n_rb, rb = t % n_rb;
-    small_gateup<BITS, GLPR, GCPL, kSmallPipe>(d, su, u, rb, hs, hu, hcode, xq_lds, xd_lds);
-    publish(d.ctr + kCtrSlot0 + u * kCtrStride, 1u);
+    const int u = t / n_rb - 1, rb = t % n_rb;
+    small_gateup<BITS, GLPR, GCPL, kSmallPipe>(d, su, u, rb, hs, hu, hcode, xq_lds, xd_lds, T);
+    publish(d.ctr + kCtrSlot0 + (u < 0 ? kShLine : u) * kCtrStride, 1u);
   }
   int8_t *lds_q = reinterpret_cast<int8_t *>(dyn);
   float *lds_d = reinterpret_cast<float *>(dyn + (size_t)DSG * T * I);
@@ -1348,8 +1254,6 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 2))) void k_small_fused(Decod
     for (int sl = threadIdx.x; sl < T * d.n_slice; sl += kDecThreads)
       __hip_atomic_store(reinterpret_cast<uint64_t *>(d.ctr + kScoreWords) + sl, (uint64_t)0,
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int b = threadIdx.x; b < I / 32; b += kDecThreads)
-      __hip_atomic_store(d.ctr + kCtrShBlk + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1467,9 +1371,8 @@ static hipError_t launch_small_t(DecodeArgs d, hipStream_t st, KEvents ev) {
       n_cu <= 0)
     n_cu = 256;
   const int cap = std::max(per_cu * n_cu, kQueues);
-  d.total = T * k * (I / kGuRows) + d.n_down;  // items at most (every pair its own expert)
+  d.total = (T * k + 1) * (I / kGuRows) + d.n_down;  // items at most (every pair its own expert)
   const int grid = std::min(d.total, cap);
-  d.sh_rows = (I + grid - 1) / grid;
   d.n_part = 1;
   d.n_slice = d.gate_w ? E : 0;
   if (d.grid_out) *d.grid_out = grid;
