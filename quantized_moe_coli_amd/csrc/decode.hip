@@ -766,8 +766,11 @@ constexpr int kSmallMaxT = 4;
 constexpr int kSmallPipe = 1;  // gate/up row passes in flight per wave
 // D items: row passes per wave, experts whose weights are in flight together
 constexpr int small_dpass(int dcpl) { return dcpl == 1 ? 2 : 1; }
-// (at most 12 staged h rows, so two workgroups still fit a CU's LDS)
-constexpr int small_dsg(int dcpl, int t) { return dcpl == 1 ? 12 / t : 2; }
+// D items: units (an expert's rows) per group, whose weights are in flight
+// together, and the h rows staged for them (at most 12, so two workgroups
+// still fit a CU's LDS)
+constexpr int small_dsg(int dcpl, int t) { return dcpl == 1 ? 6 : 2; }
+constexpr int small_drows(int dcpl, int t) { return dcpl == 1 ? 12 : 2 * t; }
 constexpr int kCtrSel = kCtrSpin + 16;  // selections published (a word of the polling-bound line)
 constexpr int kShLine = kSelMaxK;       // the shared expert's slot counter line
 
@@ -886,7 +889,7 @@ __device__ __forceinline__ void small_slice(const DecodeArgs &d, int e, double (
 // scale; they are kept in LDS (ob) and combined per token in slot order as
 // the union path's combine does, so both paths give the same bits.
 constexpr int kSmallObRows = 32;  // output rows per D item, at most
-template <int BITS, int LPR, int CPL, int NPASS, int SG, int T>
+template <int BITS, int LPR, int CPL, int NPASS, int SG, int RW, int T>
 __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const SmallUnion &su, int r0,
                                                 int8_t *lds_q, float *lds_d, int *srow,
                                                 float (*ob)[kSmallObRows]) {
@@ -902,7 +905,7 @@ __device__ __forceinline__ void small_down_rows(const DecodeArgs &d, const Small
   const int wrow0 = r0 + wave * NPASS * RPP;
   static_assert(kDecWaves * NPASS * RPP <= kSmallObRows, "output rows per D item");
 
-  constexpr int R = SG * T;  // staged rows per group
+  constexpr int R = RW;  // staged rows per group
   int nxt = 0, nxr = 0;      // next expert and its next row
   while (nxt < nx) {
     // the next group: units (expert ux[q], its rows [rbeg[q], + rcnt[q]))
@@ -1144,7 +1147,8 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 2))) void k_small_fused(Decod
   __shared__ __align__(16) int8_t hcode[kSelMaxK][kGuRows];
   __shared__ double lpart[kSmallMaxT][kDecWaves];
   __shared__ int s_ticket;
-  __shared__ int srow[DSG * kSmallMaxT];
+  constexpr int DRW = small_drows(DCPL, T);
+  __shared__ int srow[DRW];
   __shared__ float ob[kSelMaxK + kSmallMaxT][kSmallObRows];  // a D item's (token, slot) rows
   __shared__ int32_t sidx[kSelMaxK];
   __shared__ float sw[kSelMaxK];
@@ -1233,9 +1237,9 @@ __attribute__((amdgpu_waves_per_eu(BITS == 4 ? 4 : 2))) void k_small_fused(Decod
     publish(d.ctr + kCtrSlot0 + (u < 0 ? kShLine : u) * kCtrStride, 1u);
   }
   int8_t *lds_q = reinterpret_cast<int8_t *>(dyn);
-  float *lds_d = reinterpret_cast<float *>(dyn + (size_t)DSG * T * I);
+  float *lds_d = reinterpret_cast<float *>(dyn + (size_t)DRW * I);
   for (; t < total; t = next_ticket())
-    small_down_rows<BITS, DLPR, DCPL, DNPASS, DSG, T>(d, su, (t - n_gr) * d.down_rows, lds_q, lds_d, srow, ob);
+    small_down_rows<BITS, DLPR, DCPL, DNPASS, DSG, DRW, T>(d, su, (t - n_gr) * d.down_rows, lds_q, lds_d, srow, ob);
 
   // the last workgroup out clears the header for the next call
   __syncthreads();
@@ -1342,7 +1346,6 @@ static hipError_t launch_fused_bits(DecodeArgs d, hipStream_t st, KEvents ev) {
 template <int BITS, int GLPR, int GCPL, int DLPR, int DCPL, int T>
 static hipError_t launch_small_t(DecodeArgs d, hipStream_t st, KEvents ev) {
   constexpr int DNPASS = small_dpass(DCPL);
-  constexpr int DSG = small_dsg(DCPL, T);
   const int I = d.f.L.I, H = d.f.L.H, E = d.f.E, k = d.f.k;
   d.down_rows = kDecWaves * DNPASS * (64 / DLPR);
   if (H % d.down_rows || I % kGuRows || T * k > kSelMaxK || (d.gate_w && T * E > kMaxSlices) ||
@@ -1354,7 +1357,7 @@ static hipError_t launch_small_t(DecodeArgs d, hipStream_t st, KEvents ev) {
   const size_t per_row = (size_t)I + (size_t)(I / 32) * 4;
   const size_t sel =
       (sizeof(SelInput) + std::max(sizeof(SelWgScratch), sizeof(SelFastScratch)) + 15) / 16 * 16;
-  const size_t reg_a = (std::max(sel, (size_t)DSG * T * per_row) + 15) / 16 * 16;
+  const size_t reg_a = (std::max(sel, (size_t)small_drows(DCPL, T) * per_row) + 15) / 16 * 16;
   d.lds_x = (int)reg_a;
   const size_t reg_x = ((size_t)T * H + (size_t)T * (H / 32) * 4 + 15) / 16 * 16;
   d.lds_l = d.logits_out ? (int)(reg_a + reg_x) : -1;
